@@ -1,0 +1,75 @@
+"""Pins for the oracle's MoE token sort and grouped GEMM: the hand case H5, invariants of the
+sort, and reduction of the grouped GEMM to per-token dense GEMMs."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def test_h5_moe_align():
+    c = GOLD["H5_moe_align"]
+    r = oracle.ref_moe_align(np.array(c["topk_ids"]), c["E"], c["block_m"])
+    assert r["counts"].tolist() == c["counts"]
+    assert r["expert_offsets"].tolist() == c["expert_offsets"]
+    assert r["num_padded"] == c["num_padded"]
+    assert r["sorted_ids"].tolist() == c["sorted_ids"]
+    assert r["block_expert"].tolist() == c["block_expert"]
+
+
+@pytest.mark.parametrize("T,topk,E,bm", [(1, 8, 256, 16), (37, 8, 16, 4), (200, 2, 7, 64)])
+def test_moe_align_invariants(T, topk, E, bm):
+    ids = np.random.default_rng(T).integers(0, E, (T, topk)).astype(np.int32)
+    r = oracle.ref_moe_align(ids, E, bm)
+    flat = ids.reshape(-1)
+    S = T * topk
+    assert r["counts"].sum() == S
+    off = r["expert_offsets"]
+    assert off[0] == 0 and np.all(np.diff(off) % bm == 0) and off[-1] == r["num_padded"]
+    real = r["sorted_ids"][r["sorted_ids"] != S]
+    assert sorted(real.tolist()) == list(range(S))
+    for e in range(E):
+        seg = r["sorted_ids"][off[e]:off[e + 1]]
+        members = seg[seg != S]
+        assert np.all(flat[members] == e)
+        assert np.all(np.diff(members) > 0)                     # stable ascending order
+        assert np.all(seg[len(members):] == S)                  # padding at the end only
+        assert len(seg) - len(members) < bm                      # minimal padding
+    for b, e in enumerate(r["block_expert"]):
+        assert off[e] <= b * bm < off[e + 1]
+
+
+def test_moe_align_skips_out_of_range_ids():
+    ids = np.array([[0, 5], [-1, 1]], np.int32)
+    r = oracle.ref_moe_align(ids, 2, 2)
+    assert r["counts"].tolist() == [1, 1]
+    assert r["sorted_ids"].tolist() == [0, 4, 3, 4]
+
+
+def test_moe_gemm_equals_per_token_dense():
+    T, topk, E, N, K = 5, 2, 4, 8, 256
+    x = synth.normal_bf16(np.random.default_rng(0), (T, K))
+    ids = np.array([[0, 3], [1, 0], [3, 3], [2, 1], [0, 2]], np.int32)
+    ws = {e: synth.make_moe_weights_expert(950, e, N, K) for e in range(E)}
+    tw = np.random.default_rng(1).random((T, topk)).astype(np.float32)
+    y, _, valid = oracle.ref_moe_gemm(x, ids, lambda e: ws[e], N, E, 128, topk_weights=tw)
+    assert valid.all()
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            yd, _ = oracle.ref_wna16(x[t:t + 1], ws[e]["wq"], ws[e]["scales"], None, 128)
+            assert np.array_equal(y[t * topk + j], yd[0] * float(tw[t, j]))
+
+
+def test_moe_gemm_invalid_rows_masked():
+    T, topk, E, N, K = 2, 2, 2, 4, 128
+    x = synth.normal_bf16(np.random.default_rng(0), (T, K))
+    ids = np.array([[0, 7], [1, -1]], np.int32)
+    ws = {e: synth.make_moe_weights_expert(951, e, N, K) for e in range(E)}
+    _, _, valid = oracle.ref_moe_gemm(x, ids, lambda e: ws[e], N, E, 128)
+    assert valid.tolist() == [True, False, True, False]
