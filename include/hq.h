@@ -1,0 +1,194 @@
+/*
+ * hq.h -- C ABI of the MI355X (gfx950) fused-dequantization quantized GEMM library (libhq.so).
+ *
+ * Computes Y = X . dequant(Wq, scales, zero-points)^T for dense layers and for the MoE grouped
+ * GEMM, with three weight/activation pairs:
+ *   WNA16  : group-wise INT4 weights (symmetric, or unsigned with a zero-point) x bf16 activations
+ *   W8A8   : per-channel INT8 weights x per-token INT8 activations
+ *   W4A8   : MXFP4 weights (e2m1 + e8m0 block scales) x per-token FP8 e4m3 activations
+ *
+ * Source of the method: "Humming: vLLM and Ant Group Open-Source a General-Purpose Kernel
+ * Library for Quantized Inference" (English announcement page). Its section "A unified
+ * quantization representation" describes one standard quantization description in which
+ * weight format, scale granularity, scale dtype and zero-points are separate parameters and
+ * activations have their own format; `hq_quant_desc` is that description. Section "Tuning and
+ * JIT compilation per workload" describes preprocessing that validates parameters and repacks
+ * tensors into the target kernel's layout (`hq_prepack_weights`), and inference that combines
+ * the preprocessed weights with runtime activations (`hq_gemm`, `hq_moe_grouped_gemm`). The
+ * MoE token sort (`hq_moe_align`) is not described by the page; it is the step that feeds the
+ * "Indexed" MoE path of section "Results: kernel microbenchmarks" (rows gathered through a
+ * sorted index).
+ *
+ * General conventions
+ *   - Ownership: the caller allocates every buffer. Host buffers for the prepack; device
+ *     buffers (e.g. from PyTorch) for everything else. The library keeps no pointer after a
+ *     call returns and allocates no device memory.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream). Device calls only enqueue
+ *     work and never synchronize. `hq_moe_grouped_gemm` reads the padded row count on the
+ *     device, so no host round trip is needed between the two MoE calls.
+ *   - Errors: every argument is checked on the host before any launch. A non-HQ_OK status
+ *     leaves outputs untouched and sets a thread-local message (`hq_last_error`). A failed
+ *     launch returns HQ_ERR_HIP.
+ *   - Device pointers must be 16-byte aligned. Shapes: N % 16 == 0 and K a multiple of the
+ *     format's K unit (128 for WNA16 and W4A8, 64 for W8A8); other shapes are rejected with
+ *     HQ_ERR_UNSUPPORTED (the caller pads).
+ */
+#ifndef HQ_H_
+#define HQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* hq_stream_t; /* a hipStream_t */
+
+typedef enum {
+  HQ_OK = 0,
+  HQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, misaligned pointer      */
+  HQ_ERR_UNSUPPORTED = 2,      /* valid description, but a combination/shape not provided  */
+  HQ_ERR_WORKSPACE = 3,        /* workspace or output buffer smaller than required          */
+  HQ_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed                */
+} hq_status;
+
+typedef enum {
+  HQ_W_INT4_SYM = 0,   /* two's-complement INT4 in [-8, 7], packed 2 per byte, low nibble = even k */
+  HQ_W_UINT4_ASYM = 1, /* unsigned INT4 in [0, 15] with a uint4 zero-point per (n, group)          */
+  HQ_W_INT8_SYM = 2,   /* two's-complement INT8 (codes in [-127, 127])                              */
+  HQ_W_FP4_E2M1 = 3    /* OCP MX e2m1, packed 2 per byte, low nibble = even k                      */
+} hq_weight_fmt;
+
+typedef enum {
+  HQ_SCALE_BF16 = 0, /* one bf16 scale per (n, group)                         */
+  HQ_SCALE_FP32 = 1, /* one fp32 scale per output channel n (group = whole K) */
+  HQ_SCALE_E8M0 = 2  /* one e8m0 byte per (n, 32-element block): 2^(b - 127)  */
+} hq_scale_dtype;
+
+typedef enum {
+  HQ_ACT_BF16 = 0,             /* bf16 [M, K] row-major, no activation scale          */
+  HQ_ACT_INT8_PER_TOKEN = 1,   /* int8 [M, K] row-major + fp32 scale per row [M]      */
+  HQ_ACT_FP8E4M3_PER_TOKEN = 2 /* OCP e4m3 [M, K] row-major + fp32 scale per row [M]  */
+} hq_act_fmt;
+
+typedef enum {
+  HQ_OUT_BF16 = 0,     /* bf16 [M, N] row-major                                           */
+  HQ_OUT_INT32_ACC = 1 /* W8A8 only: the raw int32 accumulator sum_k xq*wq, [M, N] (test) */
+} hq_out_fmt;
+
+/* The standard quantization description (one per layer). Fields are int32 for a stable ABI. */
+typedef struct {
+  uint32_t struct_size;   /* = sizeof(hq_quant_desc)                                         */
+  int32_t weight_fmt;     /* hq_weight_fmt                                                   */
+  int32_t group_size;     /* along K: 128 (INT4), 32 (FP4/MX), 0 = per channel (INT8)        */
+  int32_t scale_dtype;    /* hq_scale_dtype                                                  */
+  int32_t has_zero_point; /* 1 for HQ_W_UINT4_ASYM, else 0                                   */
+  int32_t act_fmt;        /* hq_act_fmt                                                      */
+  int32_t out_fmt;        /* hq_out_fmt                                                      */
+} hq_quant_desc;
+
+/*
+ * Supported combinations (others return HQ_ERR_UNSUPPORTED):
+ *   INT4_SYM   + BF16 scale, group 128, no zero-point + ACT_BF16              -> OUT_BF16
+ *   UINT4_ASYM + BF16 scale, group 128, zero-point    + ACT_BF16              -> OUT_BF16
+ *   INT8_SYM   + FP32 scale, group 0                  + ACT_INT8_PER_TOKEN    -> OUT_BF16 | OUT_INT32_ACC
+ *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_FP8E4M3_PER_TOKEN -> OUT_BF16
+ * MoE grouped GEMM: the two WNA16 combinations.
+ */
+
+/* ---------------------------------------------------------------------------------------------
+ * Weight prepack (host).  Standard-format inputs, all host memory, row-major:
+ *   wq      INT4/FP4: uint8 [E, N, K/2] (two codes per byte, low nibble = even k)
+ *           INT8    : int8  [E, N, K]
+ *   scales  BF16: uint16 bf16 bits [E, N, K/group];  FP32: float [E, N];  E8M0: uint8 [E, N, K/32]
+ *   zeros   UINT4_ASYM only: uint8 [E, N, K/group], values 0..15; NULL otherwise
+ * E = 1 for a dense layer, E = number of experts for MoE (experts stacked).
+ * Output: `out` (host, `hq_prepacked_bytes` bytes) receives the weights rearranged into the
+ * MFMA operand order of the kernels. The layout is private to this library version; the caller
+ * only copies it to the device unchanged. A bijective rearrangement: no value is rounded.
+ * Returns HQ_ERR_WORKSPACE if out_bytes is too small. Codes outside a format's range are not
+ * checked (INT8 -128 is accepted and used as is).
+ * ------------------------------------------------------------------------------------------- */
+size_t hq_prepacked_bytes(const hq_quant_desc* desc, int64_t E, int64_t N, int64_t K);
+hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, int64_t K,
+                             const void* wq, const void* scales, const void* zeros,
+                             void* out, size_t out_bytes);
+
+/* ---------------------------------------------------------------------------------------------
+ * Dense GEMM (device):  y[m, n] = epilogue( sum_k a[m, k] * w[n, k] ),  0 <= m < M, 0 <= n < N
+ *   a        activations, format desc->act_fmt, [M, K] row-major (device)
+ *   a_scale  fp32 [M] per-token scales for INT8/FP8 activations (device); NULL for BF16
+ *   w_packed the prepacked weights of ONE layer (E = 1) (device)
+ *   y        [M, N] row-major, bf16 or int32 per desc->out_fmt (device)
+ *   ws       scratch of at least hq_gemm_workspace_bytes(desc, M, N, K) bytes (device); may be
+ *            NULL when that size is 0. Contents on entry do not matter.
+ * Epilogues:  WNA16: bf16( sum_g s[n,g] * sum_{k in g} a*(q - z) )  (fp32 accumulation)
+ *             W8A8 : bf16( float(acc) * a_scale[m] * s_ch[n] ),  acc exact int32
+ *             W4A8 : bf16( a_scale[m] * sum_k e4m3(a) * e2m1(q) * 2^(e - 127) ) (fp32 accumulation)
+ * All bf16 results use round-to-nearest-even. M = 0 is a no-op returning HQ_OK.
+ * ------------------------------------------------------------------------------------------- */
+size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K);
+hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K,
+                  const void* a, const float* a_scale, const void* w_packed,
+                  void* y, void* ws, size_t ws_bytes, hq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * MoE token sort / expert offsets (device).
+ *   topk_ids       int32 [T, topk] expert of each (token, slot); ids outside [0, E) are routed
+ *                  nowhere (no row is produced for them)
+ *   block_m        rows per GEMM block, a multiple of 16 in [16, 256]
+ * Outputs (device, caller-allocated):
+ *   sorted_ids     int32 [hq_moe_align_capacity(T, topk, E, block_m)]: for each expert e in
+ *                  order, the flat indices f = t*topk + j routed to e in ascending order, then
+ *                  sentinel T*topk up to the next multiple of block_m. Entries past num_padded
+ *                  are unspecified.
+ *   block_expert   int32 [capacity / block_m]: expert of each block of block_m sorted rows
+ *   expert_offsets int32 [E + 1]: exclusive prefix sum of the padded per-expert counts
+ *   num_padded     int32 [1]: total padded rows (= expert_offsets[E])
+ *   ws             scratch of hq_moe_align_workspace_bytes(...) bytes (contents irrelevant)
+ * The result is deterministic (stable order), independent of thread scheduling.
+ * ------------------------------------------------------------------------------------------- */
+size_t hq_moe_align_capacity(int64_t T, int32_t topk, int32_t E, int32_t block_m);
+size_t hq_moe_align_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t block_m);
+hq_status hq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                       int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                       int32_t* expert_offsets, int32_t* num_padded,
+                       void* ws, size_t ws_bytes, hq_stream_t stream);
+
+/* Recommended block_m for a grouped GEMM over T tokens (the tuning table's choice). */
+int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E,
+                       int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------------------------------------
+ * MoE grouped GEMM (device), WNA16 only:
+ *   y[f, :] = (topk_weights ? topk_weights[f] : 1) * a[f / topk, :] . dequant(W_{e(f)})^T
+ * for every flat index f = t*topk + j that hq_moe_align routed to a valid expert e(f). Rows of
+ * y for unrouted f are not written.
+ *   a             bf16 [T, K] row-major (device);  a_scale must be NULL
+ *   w_packed      prepacked weights of all E experts (hq_prepack_weights with E experts)
+ *   sorted_ids, block_expert, num_padded: outputs of hq_moe_align with the same T, topk, E,
+ *                 block_m (device)
+ *   topk_weights  fp32 [T*topk] or NULL (device)
+ *   y             bf16 [T*topk, N] row-major (device)
+ *   ws            hq_moe_gemm_workspace_bytes(...) bytes (may be 0 / NULL)
+ * ------------------------------------------------------------------------------------------- */
+size_t hq_moe_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t T, int32_t topk,
+                                   int32_t E, int64_t N, int64_t K, int32_t block_m);
+hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E,
+                              int64_t N, int64_t K, const void* a, const float* a_scale,
+                              const void* w_packed, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              int32_t block_m, const float* topk_weights, void* y,
+                              void* ws, size_t ws_bytes, hq_stream_t stream);
+
+/* Thread-local message describing the last non-HQ_OK status of this thread ("" if none). */
+const char* hq_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t hq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HQ_H_ */

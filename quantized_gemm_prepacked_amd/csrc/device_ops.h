@@ -1,0 +1,85 @@
+// device_ops.h -- gfx950 device building blocks of the fused-dequantization GEMM: operand
+// fragments, in-register dequantization, MFMA wrappers and the output epilogue.
+//
+// MFMA operand convention (16x16xK, wave64): for A (activations, 16 rows) lane l supplies row
+// (l & 15); for B (weights, 16 output channels) lane l supplies channel (l & 15); the K slice a
+// lane supplies is selected by (l >> 4) and is the SAME for A and B, which is all a contraction
+// needs. The fp32/int32 result tile D[16x16] leaves row 4*(l>>4)+i, column (l & 15) in element
+// i of lane l.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace hq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Weights are read exactly once per workgroup: stream them past the caches.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// ---- WNA16 dequantization -------------------------------------------------------------------
+// One dword holds 8 unsigned 4-bit codes u of consecutive k in the slot order k0 k2 k4 k6 k1 k3
+// k5 k7 (layout.h). Returns the 8 values (u - z), exactly representable in bf16 since
+// |u - z| <= 15, as the MFMA's 8-element bf16 operand in k order.
+__device__ __forceinline__ bf16x8 dequant_int4x8(uint32_t v, float z) {
+  const uint32_t lo = v & 0x0F0F0F0Fu;          // bytes: k0 k4 k1 k5
+  const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;   // bytes: k2 k6 k3 k7
+  f32x2 p0 = {float(lo & 0xFFu) - z, float((lo >> 16) & 0xFFu) - z};
+  f32x2 p1 = {float(hi & 0xFFu) - z, float((hi >> 16) & 0xFFu) - z};
+  f32x2 p2 = {float((lo >> 8) & 0xFFu) - z, float(lo >> 24) - z};
+  f32x2 p3 = {float((hi >> 8) & 0xFFu) - z, float(hi >> 24) - z};
+  bf16x2 b0 = __builtin_convertvector(p0, bf16x2);
+  bf16x2 b1 = __builtin_convertvector(p1, bf16x2);
+  bf16x2 b2 = __builtin_convertvector(p2, bf16x2);
+  bf16x2 b3 = __builtin_convertvector(p3, bf16x2);
+  bf16x8 r = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+  return r;
+}
+
+// ---- MFMA wrappers ------------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// A: 32 fp8 e4m3 per lane (format 0), unscaled (e8m0 127 = 1.0).
+// B: 32 fp4 e2m1 per lane (format 4) in the low 4 dwords, scaled by the lane's e8m0 byte.
+__device__ __forceinline__ f32x4 mfma_fp8_fp4(u32x4 a_lo, u32x4 a_hi, u32x4 b, int b_scale,
+                                              f32x4 c) {
+  i32x8 av = {int(a_lo[0]), int(a_lo[1]), int(a_lo[2]), int(a_lo[3]),
+              int(a_hi[0]), int(a_hi[1]), int(a_hi[2]), int(a_hi[3])};
+  i32x8 bv = {int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, 127, 0, b_scale);
+}
+
+}  // namespace hq

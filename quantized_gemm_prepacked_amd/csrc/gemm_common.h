@@ -1,0 +1,96 @@
+// gemm_common.h -- kernel parameters and the output epilogue shared by the GEMM kernels.
+//
+// The epilogue is where the Humming announcement (section "Shared CUDA components across
+// formats and architectures") fuses scaling into the output stage: per-token and per-channel
+// scales, the MoE router weight, bf16 rounding and the MoE row scatter happen here, once per
+// output element.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_ops.h"
+#include "layout.h"
+
+namespace hq {
+
+struct KParams {
+  const uint8_t* a;         // activations [rows, K] (bf16 / int8 / e4m3)
+  const float* a_scale;     // per-token scale [rows] (INT8 / FP8 activations)
+  const uint8_t* w;         // prepacked weights, expert 0
+  void* y;                  // output [M, N] bf16 or int32
+  void* ws;                 // split-K partials [split][M][N] (fp32 or int32)
+  int M;                    // dense: rows of A and y; MoE: T * topk (flat routed rows)
+  int N, K;
+  int k_units;              // K / K unit
+  int units_per_split;
+  int split;
+  int asym, out_i32;
+  size_t expert_stride, scales_off, zeros_off;
+  const int32_t* sorted_ids;    // MoE only
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  const float* topk_weights;
+  int topk;
+};
+
+template <int FAM>
+struct AccType {
+  typedef f32x4 type;
+  typedef float elem;
+};
+template <>
+struct AccType<FAM_W8A8> {
+  typedef i32x4 type;
+  typedef int elem;
+};
+
+// Final value of output (orow, n): `v` is the full K sum; srow indexes the per-token scale.
+template <int FAM>
+__device__ __forceinline__ void epilogue(const KParams& p, int orow, int srow, int n,
+                                         typename AccType<FAM>::elem v, float tw) {
+  const size_t o = size_t(orow) * p.N + n;
+  if constexpr (FAM == FAM_WNA16) {
+    reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * tw);
+  } else if constexpr (FAM == FAM_W8A8) {
+    if (p.out_i32) {
+      reinterpret_cast<int*>(p.y)[o] = v;
+    } else {
+      const float sch = reinterpret_cast<const float*>(p.w + p.scales_off)[n];
+      reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(float(v) * p.a_scale[srow] * sch);
+    }
+  } else {
+    reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * p.a_scale[srow] * tw);
+  }
+}
+
+// Row `row` of the workgroup's row space (dense: m; MoE: position in sorted_ids).
+template <int FAM, bool MOE>
+__device__ __forceinline__ void store_result(const KParams& p, int row, int n,
+                                             typename AccType<FAM>::elem v, int z) {
+  if constexpr (MOE) {
+    const int id = p.sorted_ids[row];
+    if (id >= p.M) return;
+    const float tw = p.topk_weights ? p.topk_weights[id] : 1.0f;
+    epilogue<FAM>(p, id, id / p.topk, n, v, tw);
+  } else {
+    if (row >= p.M) return;
+    if (p.split > 1) {
+      typedef typename AccType<FAM>::elem E;
+      reinterpret_cast<E*>(p.ws)[(size_t(z) * p.M + row) * p.N + n] = v;
+      return;
+    }
+    epilogue<FAM>(p, row, row, n, v, 1.0f);
+  }
+}
+
+// A skinny-kernel instantiation: MB row blocks of 16, NTW channel tiles of 16, NW waves that
+// split K, UNR units in flight per wave.
+struct SkinnyCfg {
+  int mb, ntw, nw, unr;
+};
+const SkinnyCfg* skinny_configs(int* count);
+
+hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid, hipStream_t s);
+hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s);
+
+}  // namespace hq

@@ -1,0 +1,139 @@
+// gemm_dispatch.hip -- per-M-range kernel choice and launches (the tuning table), plus the
+// split-K reduction kernel.
+//
+// The Humming announcement (section "Tuning and JIT compilation per workload") prepares
+// different kernel configurations for ranges of input sizes and dispatches at runtime. Here the
+// configurations are compiled ahead of time for gfx950 and chosen by M (or tokens per expert
+// for MoE) and by the shape.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace hq {
+
+namespace {
+
+constexpr int kCUs = 256;
+
+int k_unit(const Combo& c) { return family_k_unit(c.fam); }
+
+// Pick the skinny configuration for a row block of `rows` rows and N channels.
+int pick_skinny(int64_t rows, int64_t N) {
+  const int64_t nt = N / 16;
+  if (rows <= 16) return nt % 4 == 0 ? 0 : (nt % 2 == 0 ? 1 : 2);
+  if (rows <= 32) return nt % 4 == 0 ? 3 : (nt % 2 == 0 ? 7 : 8);
+  return nt % 4 == 0 ? 4 : (nt % 2 == 0 ? 5 : 6);
+}
+
+size_t acc_elem_bytes() { return 4; }
+
+template <int FAM>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(KParams p) {
+  typedef typename AccType<FAM>::elem E;
+  const size_t total = size_t(p.M) * p.N;
+  const size_t idx = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const E* ws = reinterpret_cast<const E*>(p.ws);
+  E s = ws[idx];
+  for (int z = 1; z < p.split; ++z) s += ws[size_t(z) * total + idx];
+  const int m = int(idx / p.N);
+  const int n = int(idx % p.N);
+  epilogue<FAM>(p, m, m, n, s, 1.0f);
+}
+
+}  // namespace
+
+hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
+  const size_t total = size_t(p.M) * p.N;
+  dim3 grid(unsigned((total + 255) / 256));
+  if (fam == FAM_WNA16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_WNA16>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_W8A8)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W8A8>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
+  Plan pl{};
+  pl.kind = 0;
+  pl.cfg = pick_skinny(M, N);
+  int n_cfg = 0;
+  const SkinnyCfg& sc = skinny_configs(&n_cfg)[pl.cfg];
+  const int64_t units = K / k_unit(c);
+  const int64_t wgs = (N / 16 / sc.ntw) * ((M + 16 * sc.mb - 1) / (16 * sc.mb));
+  int split = 1;
+  // Too few workgroups to cover the chip: split K across workgroups as long as every wave
+  // keeps at least two units.
+  while (wgs * split < kCUs && units / (int64_t(split) * 2 * sc.nw) >= 2) split *= 2;
+  pl.split = split;
+  pl.ws_bytes = split > 1 ? size_t(split) * M * N * acc_elem_bytes() : 0;
+  return pl;
+}
+
+Plan plan_moe(const Combo&, int64_t, int32_t, int32_t, int64_t N, int64_t, int32_t block_m) {
+  Plan pl{};
+  pl.kind = 0;
+  pl.cfg = pick_skinny(block_m, N);
+  pl.split = 1;
+  pl.ws_bytes = 0;
+  return pl;
+}
+
+bool moe_block_m_supported(int32_t block_m) { return block_m == 16 || block_m == 32 || block_m == 64; }
+
+int32_t moe_block_m(const Combo&, int64_t T, int32_t topk, int32_t E, int64_t, int64_t) {
+  const double rows_per_expert = double(T) * topk / std::max(1, E);
+  if (rows_per_expert <= 16) return 16;
+  if (rows_per_expert <= 64) return 32;
+  return 64;
+}
+
+hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
+  const Combo& c = call.c;
+  const PackedLayout L = make_layout(c.fam, c.asym, call.N, call.K);
+  KParams p{};
+  p.a = static_cast<const uint8_t*>(call.a);
+  p.a_scale = call.a_scale;
+  p.w = call.w;
+  p.y = call.y;
+  p.ws = call.ws;
+  p.N = int(call.N);
+  p.K = int(call.K);
+  p.k_units = int(L.k_units);
+  p.asym = c.asym ? 1 : 0;
+  p.out_i32 = c.out_i32 ? 1 : 0;
+  p.expert_stride = L.expert_stride;
+  p.scales_off = L.scales_off;
+  p.zeros_off = L.zeros_off;
+  const bool moe = call.sorted_ids != nullptr;
+  int n_cfg = 0;
+  const SkinnyCfg& sc = skinny_configs(&n_cfg)[plan.cfg];
+  const int rows_per_block = 16 * sc.mb;
+  if (moe) {
+    p.M = int(call.T * call.topk);
+    p.sorted_ids = call.sorted_ids;
+    p.block_expert = call.block_expert;
+    p.num_padded = call.num_padded;
+    p.topk_weights = call.topk_weights;
+    p.topk = call.topk;
+    p.split = 1;
+    p.units_per_split = p.k_units;
+    dim3 grid(unsigned(call.N / 16 / sc.ntw), unsigned(call.max_blocks), 1);
+    return launch_skinny(p, c.fam, true, plan.cfg, grid, call.stream);
+  }
+  p.M = int(call.M);
+  p.split = plan.split;
+  p.units_per_split = (p.k_units + plan.split - 1) / plan.split;
+  dim3 grid(unsigned(call.N / 16 / sc.ntw), unsigned((call.M + rows_per_block - 1) / rows_per_block),
+            unsigned(plan.split));
+  hipError_t e = launch_skinny(p, c.fam, false, plan.cfg, grid, call.stream);
+  if (e != hipSuccess || plan.split == 1) return e;
+  return launch_splitk_reduce(p, c.fam, call.stream);
+}
+
+}  // namespace hq

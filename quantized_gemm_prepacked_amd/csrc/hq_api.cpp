@@ -1,0 +1,271 @@
+// hq_api.cpp -- the C ABI (include/hq.h): argument validation, then prepack or kernel launch.
+//
+// Validation follows the preprocessing contract of the Humming announcement (section "Tuning and
+// JIT compilation per workload": parameters are validated before anything runs). Every check
+// here happens on the host before any HIP call, so a rejected call has no device side effect.
+#include "hq.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+#include "layout.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hq_status fail(hq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hq_status ok() {
+  g_last_error.clear();
+  return HQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+// Map a description onto a supported combination.
+hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
+  if (!d) return fail(HQ_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->struct_size != sizeof(hq_quant_desc))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "desc->struct_size %u != %zu", d->struct_size,
+                sizeof(hq_quant_desc));
+  if (d->out_fmt != HQ_OUT_BF16 && d->out_fmt != HQ_OUT_INT32_ACC)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "unknown out_fmt %d", d->out_fmt);
+  c->out_i32 = d->out_fmt == HQ_OUT_INT32_ACC;
+  c->asym = false;
+  switch (d->weight_fmt) {
+    case HQ_W_INT4_SYM:
+    case HQ_W_UINT4_ASYM: {
+      const bool asym = d->weight_fmt == HQ_W_UINT4_ASYM;
+      if (d->group_size != 128 || d->scale_dtype != HQ_SCALE_BF16 ||
+          d->has_zero_point != (asym ? 1 : 0) || d->act_fmt != HQ_ACT_BF16 || c->out_i32)
+        return fail(HQ_ERR_UNSUPPORTED,
+                    "INT4 weights need group_size 128, BF16 scales, has_zero_point %d, BF16 "
+                    "activations and bf16 output",
+                    asym ? 1 : 0);
+      c->fam = hq::FAM_WNA16;
+      c->asym = asym;
+      return HQ_OK;
+    }
+    case HQ_W_INT8_SYM:
+      if (d->group_size != 0 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 ||
+          d->act_fmt != HQ_ACT_INT8_PER_TOKEN)
+        return fail(HQ_ERR_UNSUPPORTED,
+                    "INT8 weights need group_size 0 (per channel), FP32 scales, no zero-point "
+                    "and per-token INT8 activations");
+      c->fam = hq::FAM_W8A8;
+      return HQ_OK;
+    case HQ_W_FP4_E2M1:
+      if (d->group_size != 32 || d->scale_dtype != HQ_SCALE_E8M0 || d->has_zero_point != 0 ||
+          d->act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN || c->out_i32)
+        return fail(HQ_ERR_UNSUPPORTED,
+                    "FP4 weights need group_size 32, E8M0 scales, no zero-point, per-token FP8 "
+                    "e4m3 activations and bf16 output");
+      c->fam = hq::FAM_W4A8;
+      return HQ_OK;
+    default:
+      return fail(HQ_ERR_INVALID_ARGUMENT, "unknown weight_fmt %d", d->weight_fmt);
+  }
+}
+
+hq_status check_shape(const hq::Combo& c, int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "N=%lld K=%lld out of range", (long long)N, (long long)K);
+  const int ku = hq::family_k_unit(c.fam);
+  if (N % 16 != 0 || K % ku != 0)
+    return fail(HQ_ERR_UNSUPPORTED, "N must be a multiple of 16 and K of %d (N=%lld K=%lld)", ku,
+                (long long)N, (long long)K);
+  return HQ_OK;
+}
+
+hq_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hq_last_error(void) { return g_last_error.c_str(); }
+
+int32_t hq_version(void) { return 100; }
+
+size_t hq_prepacked_bytes(const hq_quant_desc* desc, int64_t E, int64_t N, int64_t K) {
+  hq::Combo c{};
+  if (resolve(desc, &c) != HQ_OK || E <= 0 || check_shape(c, N, K) != HQ_OK) return 0;
+  return hq::prepacked_bytes(c, E, N, K);
+}
+
+hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, int64_t K,
+                             const void* wq, const void* scales, const void* zeros, void* out,
+                             size_t out_bytes) {
+  hq::Combo c{};
+  hq_status s = resolve(desc, &c);
+  if (s != HQ_OK) return s;
+  if (E <= 0 || E > 65536) return fail(HQ_ERR_INVALID_ARGUMENT, "E=%lld out of range", (long long)E);
+  if ((s = check_shape(c, N, K)) != HQ_OK) return s;
+  if (!wq || !scales || !out) return fail(HQ_ERR_INVALID_ARGUMENT, "wq, scales and out must be non-NULL");
+  if (c.asym && !zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for UINT4_ASYM");
+  if (!c.asym && zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be NULL without zero-points");
+  const size_t need = hq::prepacked_bytes(c, E, N, K);
+  if (out_bytes < need)
+    return fail(HQ_ERR_WORKSPACE, "out_bytes %zu < required %zu", out_bytes, need);
+  hq::prepack(c, E, N, K, wq, scales, zeros, out);
+  return ok();
+}
+
+size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K) {
+  hq::Combo c{};
+  if (resolve(desc, &c) != HQ_OK || M <= 0 || M > kMaxDim || check_shape(c, N, K) != HQ_OK) return 0;
+  return hq::plan_dense(c, M, N, K).ws_bytes;
+}
+
+hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, const void* a,
+                  const float* a_scale, const void* w_packed, void* y, void* ws, size_t ws_bytes,
+                  hq_stream_t stream) {
+  hq::Combo c{};
+  hq_status s = resolve(desc, &c);
+  if (s != HQ_OK) return s;
+  if ((s = check_shape(c, N, K)) != HQ_OK) return s;
+  if (M < 0 || M > kMaxDim) return fail(HQ_ERR_INVALID_ARGUMENT, "M=%lld out of range", (long long)M);
+  if (M * N >= (int64_t(1) << 31) || M * K >= (int64_t(1) << 40))
+    return fail(HQ_ERR_UNSUPPORTED, "M*N must stay below 2^31 (M=%lld N=%lld)", (long long)M, (long long)N);
+  if (!a || !w_packed || !y) return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be non-NULL");
+  if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
+  const bool needs_scale = c.fam != hq::FAM_WNA16;
+  if (needs_scale && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale is required for INT8/FP8 activations");
+  if (!needs_scale && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
+  if (a_scale && (reinterpret_cast<uintptr_t>(a_scale) & 3u))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be 4-byte aligned");
+  if (M == 0) return ok();
+  const hq::Plan plan = hq::plan_dense(c, M, N, K);
+  if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
+    return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
+  if (ws && !aligned16(ws)) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 16-byte aligned");
+  hq::GemmCall call{};
+  call.c = c;
+  call.M = M;
+  call.N = N;
+  call.K = K;
+  call.a = a;
+  call.a_scale = a_scale;
+  call.w = static_cast<const uint8_t*>(w_packed);
+  call.y = y;
+  call.ws = ws;
+  call.ws_bytes = ws_bytes;
+  call.stream = static_cast<hipStream_t>(stream);
+  return check_hip(hq::launch_gemm(call, plan), "hq_gemm launch");
+}
+
+size_t hq_moe_align_capacity(int64_t T, int32_t topk, int32_t E, int32_t block_m) {
+  if (T < 0 || topk <= 0 || E <= 0 || block_m <= 0) return 0;
+  const int64_t n_flat = T * topk;
+  const int64_t active = std::min<int64_t>(E, n_flat);
+  const int64_t cap = n_flat + active * (block_m - 1);
+  return size_t((cap + block_m - 1) / block_m * block_m);
+}
+
+size_t hq_moe_align_workspace_bytes(int64_t T, int32_t topk, int32_t E, int32_t block_m) {
+  return hq::moe_align_ws_bytes(T, topk, E, block_m);
+}
+
+hq_status hq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                       int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                       int32_t* expert_offsets, int32_t* num_padded, void* ws, size_t ws_bytes,
+                       hq_stream_t stream) {
+  if (T < 0 || T * int64_t(topk) > (int64_t(1) << 30))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld out of range", (long long)T);
+  if (topk <= 0 || topk > 64) return fail(HQ_ERR_INVALID_ARGUMENT, "topk=%d out of range", topk);
+  if (E <= 0 || E > 512) return fail(HQ_ERR_UNSUPPORTED, "E=%d: 1..512 experts supported", E);
+  if (block_m < 16 || block_m > 256 || block_m % 16 != 0)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "block_m=%d must be a multiple of 16 in [16, 256]", block_m);
+  if (!sorted_ids || !block_expert || !expert_offsets || !num_padded || (T > 0 && !topk_ids))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "output pointers and topk_ids must be non-NULL");
+  const size_t need = hq::moe_align_ws_bytes(T, topk, E, block_m);
+  if (ws_bytes < need) return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, need);
+  return check_hip(hq::launch_moe_align(topk_ids, T, topk, E, block_m, sorted_ids, block_expert,
+                                        expert_offsets, num_padded, ws,
+                                        static_cast<hipStream_t>(stream)),
+                   "hq_moe_align launch");
+}
+
+int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E, int64_t N,
+                       int64_t K) {
+  hq::Combo c{};
+  if (resolve(desc, &c) != HQ_OK || T < 0 || topk <= 0 || E <= 0) return 0;
+  return hq::moe_block_m(c, T, topk, E, N, K);
+}
+
+size_t hq_moe_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E,
+                                   int64_t N, int64_t K, int32_t block_m) {
+  hq::Combo c{};
+  if (resolve(desc, &c) != HQ_OK || check_shape(c, N, K) != HQ_OK) return 0;
+  return hq::plan_moe(c, T, topk, E, N, K, block_m).ws_bytes;
+}
+
+hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E,
+                              int64_t N, int64_t K, const void* a, const float* a_scale,
+                              const void* w_packed, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              int32_t block_m, const float* topk_weights, void* y, void* ws,
+                              size_t ws_bytes, hq_stream_t stream) {
+  hq::Combo c{};
+  hq_status s = resolve(desc, &c);
+  if (s != HQ_OK) return s;
+  if (c.fam != hq::FAM_WNA16) return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM supports WNA16 only");
+  if ((s = check_shape(c, N, K)) != HQ_OK) return s;
+  if (T < 0 || topk <= 0 || topk > 64 || E <= 0 || E > 512)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld topk=%d E=%d out of range", (long long)T, topk, E);
+  if (T * topk * N >= (int64_t(1) << 31))
+    return fail(HQ_ERR_UNSUPPORTED, "T*topk*N must stay below 2^31");
+  if (!hq::moe_block_m_supported(block_m))
+    return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: supported values are 16, 32, 64", block_m);
+  if (a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
+  if (!a || !w_packed || !sorted_ids || !block_expert || !num_padded || !y)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, sorted_ids, block_expert, num_padded and y must be non-NULL");
+  if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
+  if (T == 0) return ok();
+  const hq::Plan plan = hq::plan_moe(c, T, topk, E, N, K, block_m);
+  if (ws_bytes < plan.ws_bytes) return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
+  hq::GemmCall call{};
+  call.c = c;
+  call.M = T * topk;
+  call.N = N;
+  call.K = K;
+  call.a = a;
+  call.w = static_cast<const uint8_t*>(w_packed);
+  call.y = y;
+  call.ws = ws;
+  call.ws_bytes = ws_bytes;
+  call.stream = static_cast<hipStream_t>(stream);
+  call.sorted_ids = sorted_ids;
+  call.block_expert = block_expert;
+  call.num_padded = num_padded;
+  call.topk_weights = topk_weights;
+  call.T = T;
+  call.topk = topk;
+  call.E = E;
+  call.block_m = block_m;
+  call.max_blocks = int64_t(hq_moe_align_capacity(T, topk, E, block_m)) / block_m;
+  return check_hip(hq::launch_gemm(call, plan), "hq_moe_grouped_gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// internal.h -- declarations shared by the C ABI (hq_api.cpp), the host prepack and the HIP
+// launchers. Not part of the public interface.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "layout.h"
+
+namespace hq {
+
+// A validated weight/activation/output combination.
+struct Combo {
+  Family fam;
+  bool asym;     // WNA16 with zero-points
+  bool out_i32;  // W8A8 raw accumulator output
+};
+
+size_t prepacked_bytes(const Combo& c, int64_t E, int64_t N, int64_t K);
+void prepack(const Combo& c, int64_t E, int64_t N, int64_t K, const void* wq, const void* scales,
+             const void* zeros, void* out);
+
+// Kernel choice for one call (see dispatch in gemm_kernels.hip).
+struct Plan {
+  int kind;    // 0 = skinny (waves split K), 1 = tiled (LDS-staged activations)
+  int cfg;     // index into the kind's instantiation table
+  int split;   // K splits across workgroups (partials in the workspace, then a reduction)
+  size_t ws_bytes;
+};
+
+struct GemmCall {
+  Combo c;
+  int64_t M, N, K;
+  const void* a;
+  const float* a_scale;
+  const uint8_t* w;
+  void* y;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+  // MoE (sorted_ids != nullptr)
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  const float* topk_weights;
+  int64_t T;
+  int32_t topk;
+  int32_t E;
+  int32_t block_m;
+  int64_t max_blocks;
+};
+
+Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K);
+Plan plan_moe(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K,
+              int32_t block_m);
+int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K);
+bool moe_block_m_supported(int32_t block_m);
+hipError_t launch_gemm(const GemmCall& call, const Plan& plan);
+
+size_t moe_align_ws_bytes(int64_t T, int32_t topk, int32_t E, int32_t block_m);
+hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                            int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                            int32_t* expert_offsets, int32_t* num_padded, void* ws,
+                            hipStream_t stream);
+
+}  // namespace hq

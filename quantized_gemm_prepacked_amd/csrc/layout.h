@@ -1,0 +1,78 @@
+// layout.h -- the prepacked weight layout shared by the host prepack and the gfx950 kernels.
+//
+// The weights are split into "units": 16 output channels (one MFMA column tile) by one K unit.
+// A unit's codes are exactly 1 KiB, laid out as the B operand of a wave-wide MFMA: 64 lanes x
+// 16 bytes, so one coalesced 128-bit load per lane fetches the whole unit. Lane l owns output
+// channel n = 16*nt + (l & 15) and a contiguous K slice selected by (l >> 4):
+//
+//   WNA16 (INT4, K unit 128 = one quantization group, v_mfma_f32_16x16x32_bf16 x 4):
+//     lane l holds k = 128*kt + 32*(l>>4) + 8*d + j  in dword d (0..3), j = 0..7.
+//     Inside a dword, nibble slot p (bits 4p..4p+3) holds j = 2*(p & 3) + (p >> 2), i.e. the
+//     order k0 k2 k4 k6 k1 k3 k5 k7, so (dword >> 4i) & 0x000F000F yields the pair (k 2i, 2i+1)
+//     as two 16-bit lanes. Codes are stored as unsigned u in [0, 15]: u = q (asymmetric) or
+//     u = q + 8 (symmetric, i.e. the two's-complement nibble with bit 3 flipped); the kernel
+//     always computes u - z with z = 8 for symmetric weights.
+//   W8A8 (INT8, K unit 64, v_mfma_i32_16x16x64_i8):
+//     lane l holds k = 64*kt + 16*(l>>4) + j in byte j (0..15).
+//   W4A8 (FP4, K unit 128 = four MX blocks, v_mfma_scale_f32_16x16x128_f8f6f4):
+//     lane l holds k = 128*kt + 32*(l>>4) + j in nibble j (0..31, low nibble first): exactly one
+//     32-element MX block, so the lane's e8m0 byte is that block's scale.
+//
+// Regions per expert (each starts at a 256-byte aligned offset; experts are stacked with a
+// 256-byte aligned stride):
+//   codes : [N/16][K/KU] units of 1024 bytes (K units of one channel tile are contiguous)
+//   WNA16 scales: [N/16][K/128][16] bf16;  zeros (asym): [N/16][K/128][8] bytes, byte i holds
+//                 the zero of channel 2i (low nibble) and 2i+1 (high nibble)
+//   W8A8  scales: [N] fp32 per channel
+//   W4A8  scales: [N/16][K/128][64] e8m0 bytes, byte l = scale of lane l's block
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+
+namespace hq {
+
+enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2 };
+
+constexpr int kUnitBytes = 1024;
+constexpr int kTileN = 16;
+
+inline int family_k_unit(Family f) { return f == FAM_W8A8 ? 64 : 128; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct PackedLayout {
+  Family fam;
+  bool asym;
+  int64_t N, K;
+  int64_t n_tiles, k_units;
+  size_t codes_off, codes_bytes;
+  size_t scales_off, scales_bytes;
+  size_t zeros_off, zeros_bytes;
+  size_t expert_stride;
+};
+
+inline PackedLayout make_layout(Family fam, bool asym, int64_t N, int64_t K) {
+  PackedLayout L{};
+  L.fam = fam;
+  L.asym = asym;
+  L.N = N;
+  L.K = K;
+  L.n_tiles = N / kTileN;
+  L.k_units = K / family_k_unit(fam);
+  L.codes_off = 0;
+  L.codes_bytes = size_t(L.n_tiles) * size_t(L.k_units) * kUnitBytes;
+  L.scales_off = align256(L.codes_bytes);
+  if (fam == FAM_WNA16) {
+    L.scales_bytes = size_t(L.n_tiles) * L.k_units * 16 * 2;
+  } else if (fam == FAM_W8A8) {
+    L.scales_bytes = size_t(N) * 4;
+  } else {
+    L.scales_bytes = size_t(L.n_tiles) * L.k_units * 64;
+  }
+  L.zeros_off = align256(L.scales_off + L.scales_bytes);
+  L.zeros_bytes = (fam == FAM_WNA16 && asym) ? size_t(L.n_tiles) * L.k_units * 8 : 0;
+  L.expert_stride = align256(L.zeros_off + L.zeros_bytes);
+  return L;
+}
+
+}  // namespace hq

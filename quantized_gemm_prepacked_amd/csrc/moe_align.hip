@@ -1,0 +1,131 @@
+// moe_align.hip -- MoE token sort / expert offsets on the device, one workgroup, no host sync.
+//
+// Feeds the "Indexed" MoE path (rows gathered through a sorted index) of the Humming
+// announcement's section "Results: kernel microbenchmarks". The token sort itself is not
+// described there; the contract (stable ascending order per expert, per-expert padding to a
+// multiple of block_m with sentinel T*topk) is the library's (hq.h).
+//
+// One workgroup of 1024 threads: (1) per-expert histogram with LDS atomics (order-free),
+// (2) block-wide scan of the padded counts, (3) stable scatter in tiles of 1024 entries: inside a
+// wave, entries of the same expert are found with ballots over the expert id bits and ranked by
+// lane; across the 16 waves of a tile, per-wave counts are prefix-summed in wave order; across
+// tiles a running count per expert carries on. Every position is therefore a pure function of
+// the input, independent of scheduling.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace hq {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kIdBits = 11;  // expert ids < 2048; id E marks an unrouted entry
+
+__global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __restrict__ ids,
+                                                             int n_flat, int E, int bm,
+                                                             int32_t* __restrict__ sorted,
+                                                             int32_t* __restrict__ block_expert,
+                                                             int32_t* __restrict__ offsets_out,
+                                                             int32_t* __restrict__ num_padded) {
+  extern __shared__ int sm[];
+  int* cnt = sm;               // [E]
+  int* offs = cnt + E;         // [E + 1]
+  int* run = offs + E + 1;     // [E]
+  int* scan = run + E;         // [kThreads]
+  int* wc = scan + kThreads;   // [kWaves][E]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  for (int e = tid; e < E; e += kThreads) {
+    cnt[e] = 0;
+    run[e] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_flat; i += kThreads) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // Exclusive scan of padded counts; E <= kThreads is checked on the host, E may be < kThreads.
+  const int padded = tid < E ? (cnt[tid] + bm - 1) / bm * bm : 0;
+  scan[tid] = padded;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int t = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += t;
+    __syncthreads();
+  }
+  if (tid < E) offs[tid] = scan[tid] - padded;
+  if (tid == E - 1) offs[E] = scan[tid];
+  __syncthreads();
+  const int total = offs[E];
+  for (int e = tid; e <= E; e += kThreads) offsets_out[e] = offs[e];
+  if (tid == 0) *num_padded = total;
+
+  // Padding slots and the block -> expert table.
+  for (int e = tid; e < E; e += kThreads)
+    for (int s = offs[e] + cnt[e]; s < offs[e + 1]; ++s) sorted[s] = n_flat;
+  for (int b = tid; b * bm < total; b += kThreads) {
+    const int row = b * bm;
+    int lo = 0, hi = E - 1;  // last e with offs[e] <= row (offs is non-decreasing)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offs[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    block_expert[b] = lo;
+  }
+
+  // Stable scatter.
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int t0 = 0; t0 < n_flat; t0 += kThreads) {
+    for (int j = tid; j < kWaves * E; j += kThreads) wc[j] = 0;
+    __syncthreads();
+    const int i = t0 + tid;
+    int e = i < n_flat ? ids[i] : -1;
+    const bool valid = e >= 0 && e < E;
+    const int key = valid ? e : E;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    if (valid && rank == 0) wc[wave * E + e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int base = run[e];
+      for (int w = 0; w < wave; ++w) base += wc[w * E + e];
+      sorted[offs[e] + base + rank] = i;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kThreads) {
+      int s = 0;
+      for (int w = 0; w < kWaves; ++w) s += wc[w * E + x];
+      run[x] += s;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+size_t moe_align_ws_bytes(int64_t, int32_t, int32_t, int32_t) { return 0; }
+
+hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                            int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                            int32_t* expert_offsets, int32_t* num_padded, void*,
+                            hipStream_t stream) {
+  const size_t smem = sizeof(int) * (size_t(E) * 3 + 1 + kThreads + size_t(kWaves) * E);
+  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kThreads), smem, stream, topk_ids,
+                     int(T * topk), int(E), int(block_m), sorted_ids, block_expert,
+                     expert_offsets, num_padded);
+  return hipGetLastError();
+}
+
+}  // namespace hq

@@ -1,0 +1,75 @@
+"""Shared plumbing for the GPU parity tests: upload standard-format inputs, prepack, call the
+library through its C ABI, and compare with the CPU oracle under the stated tolerances."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import quantized_gemm_prepacked_amd as hq
+
+DEV = "cuda:0"
+
+# Float paths: relative L2 <= 2e-3 and max-abs <= 2e-2 * max|ref| against the unrounded fp64
+# oracle. W8A8: int32 accumulator bit-exact, bf16 output within 1 ulp of bf16(oracle).
+REL_L2_TOL = 2e-3
+MAX_ABS_FRAC = 2e-2
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def prepack(desc, E, N, K, wq, scales, zeros=None) -> torch.Tensor:
+    out = np.zeros(hq.hq_prepacked_bytes(desc, E, N, K), np.uint8)
+    hq.hq_prepack_weights(desc, E, N, K, wq, scales, zeros, out)
+    return to_dev(out)
+
+
+def workspace(nbytes: int):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=DEV), nbytes
+
+
+def gemm(desc, M, N, K, a, a_scale, w_dev, out_dtype=torch.int16):
+    y = torch.empty((max(M, 1), N), dtype=out_dtype, device=DEV)
+    ws, wsb = workspace(hq.hq_gemm_workspace_bytes(desc, M, N, K))
+    hq.hq_gemm(desc, M, N, K, a, a_scale, w_dev, y, ws, wsb)
+    torch.cuda.synchronize()
+    return y[:M].cpu().numpy()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_float(y_bits: np.ndarray, ref64: np.ndarray, what: str):
+    y = bf16_to_f64(y_bits.view(np.uint16))
+    assert np.isfinite(y).all(), f"{what}: non-finite output"
+    err = y - ref64
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref64), 1e-300)
+    mx = np.abs(err).max() / max(np.abs(ref64).max(), 1e-300)
+    say(f"  {what}: rel_l2={rel:.3e} max_abs/max_ref={mx:.3e}")
+    assert rel <= REL_L2_TOL, f"{what}: relative L2 {rel:.3e} > {REL_L2_TOL}"
+    assert mx <= MAX_ABS_FRAC, f"{what}: max abs err {mx:.3e} x max|ref| > {MAX_ABS_FRAC}"
+    return rel, mx
+
+
+def bf16_ordered(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> integers whose order is the numeric order (+0 and -0 -> 0)."""
+    b = bits.astype(np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def check_ulp(y_bits: np.ndarray, ref_bits: np.ndarray, what: str, max_ulp: int = 1):
+    d = np.abs(bf16_ordered(y_bits.view(np.uint16)) - bf16_ordered(ref_bits))
+    say(f"  {what}: max ulp {d.max()}, exact {np.mean(d == 0) * 100:.2f}%")
+    assert d.max() <= max_ulp, f"{what}: bf16 differs by {d.max()} ulp"

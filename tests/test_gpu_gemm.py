@@ -1,0 +1,152 @@
+"""GPU parity of the dense fused-dequantization GEMM against the CPU oracle, through the C ABI.
+
+Small and ragged shapes compare every output; the full benchmark shapes compare a sampled set of
+rows and columns (the oracle computes just those) in the launch configuration the benchmark
+uses. Tolerances: float paths relative L2 <= 2e-3 and max-abs <= 2e-2 * max|ref| against the
+unrounded fp64 oracle; W8A8 int32 accumulator bit-exact and bf16 output within 1 ulp."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_prepacked_amd as hq
+import synth
+
+from gpu_harness import check_float, check_ulp, gemm, prepack, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(M, N, rng, nr=48, nc=96):
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, nr)])) if M > nr else np.arange(M)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, nc)]))
+    return rows, cols
+
+
+# ---- WNA16 -------------------------------------------------------------------------------------
+WNA16_SMALL = [
+    # (M, N, K, asym)
+    (16, 256, 512, False),    # the tiny dense W4A16 workload
+    (1, 256, 512, False),
+    (37, 272, 384, False),    # ragged M, odd number of channel tiles
+    (5, 48, 128, False),      # a single K unit
+    (64, 512, 1024, False),
+    (100, 1024, 2048, False),
+    (1, 2048, 1024, True),
+    (16, 1024, 4096, True),
+    (33, 304, 512, True),
+    (128, 512, 512, True),
+    (300, 256, 1024, True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,asym", WNA16_SMALL)
+def test_wna16_small(M, N, K, asym):
+    say(f"[wna16] M={M} N={N} K={K} asym={asym}")
+    d = synth.make_wna16(100 + asym, M, N, K, asym=asym)
+    desc = hq.DESC_W4A16_ASYM if asym else hq.DESC_W4A16_SYM
+    w = prepack(desc, 1, N, K, d["wq"], d["scales"], d.get("zeros"))
+    y = gemm(desc, M, N, K, to_dev(d["x"]), None, w)
+    ref, _ = oracle.ref_wna16(d["x"], d["wq"], d["scales"], d.get("zeros"), 128)
+    check_float(y, ref, "wna16")
+
+
+def test_wna16_deterministic():
+    M, N, K = 3, 512, 4096
+    d = synth.make_wna16(7, M, N, K, asym=True)
+    w = prepack(hq.DESC_W4A16_ASYM, 1, N, K, d["wq"], d["scales"], d["zeros"])
+    x = to_dev(d["x"])
+    y1 = gemm(hq.DESC_W4A16_ASYM, M, N, K, x, None, w)
+    y2 = gemm(hq.DESC_W4A16_ASYM, M, N, K, x, None, w)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.fixture(scope="module")
+def cfg2_weights():
+    N, K = 14336, 4096
+    d = synth.make_wna16(2, 1, N, K, asym=True)
+    w = prepack(hq.DESC_W4A16_ASYM, 1, N, K, d["wq"], d["scales"], d["zeros"])
+    return d, w
+
+
+@pytest.mark.parametrize("M", [1, 16, 128, 1024, 8192])
+def test_wna16_full_size_sampled(cfg2_weights, M):
+    N, K = 14336, 4096
+    d, w = cfg2_weights
+    say(f"[wna16 full] M={M} N={N} K={K}")
+    x = synth.normal_bf16(synth.rng(2, M), (M, K))
+    y = gemm(hq.DESC_W4A16_ASYM, M, N, K, to_dev(x), None, w)
+    rows, cols = _sample(M, N, np.random.default_rng(M))
+    ref, _ = oracle.ref_wna16(x, d["wq"], d["scales"], d["zeros"], 128, rows=rows, cols=cols)
+    check_float(y[np.ix_(rows, cols)], ref, f"wna16 M={M}")
+
+
+# ---- W8A8 -------------------------------------------------------------------------------------
+W8A8_SMALL = [(1, 256, 8192), (64, 512, 1024), (7, 272, 320), (16, 256, 64), (200, 512, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", W8A8_SMALL)
+def test_w8a8_small(M, N, K):
+    say(f"[w8a8] M={M} N={N} K={K}")
+    d = synth.make_w8a8(300, M, N, K)
+    w = prepack(hq.DESC_W8A8, 1, N, K, d["wq"], d["s_ch"])
+    xq, st = to_dev(d["xq"]), to_dev(d["s_tok"])
+    acc = gemm(hq.DESC_W8A8_I32, M, N, K, xq, st, w, out_dtype=torch.int32)
+    y = gemm(hq.DESC_W8A8, M, N, K, xq, st, w)
+    ref_acc, _, ref_bits = oracle.ref_w8a8(d["xq"], d["s_tok"], d["wq"], d["s_ch"])
+    assert np.array_equal(acc.astype(np.int64), ref_acc), "int32 accumulator not bit-exact"
+    check_ulp(y, ref_bits, "w8a8 bf16")
+
+
+@pytest.mark.parametrize("M", [1, 64, 512, 4096])
+def test_w8a8_full_size_sampled(M):
+    N = K = 8192
+    say(f"[w8a8 full] M={M}")
+    d = synth.make_w8a8(3, M, N, K)
+    w = prepack(hq.DESC_W8A8, 1, N, K, d["wq"], d["s_ch"])
+    xq, st = to_dev(d["xq"]), to_dev(d["s_tok"])
+    acc = gemm(hq.DESC_W8A8_I32, M, N, K, xq, st, w, out_dtype=torch.int32)
+    y = gemm(hq.DESC_W8A8, M, N, K, xq, st, w)
+    rows, cols = _sample(M, N, np.random.default_rng(M))
+    ref_acc, _, ref_bits = oracle.ref_w8a8(d["xq"], d["s_tok"], d["wq"], d["s_ch"], rows=rows, cols=cols)
+    assert np.array_equal(acc[np.ix_(rows, cols)].astype(np.int64), ref_acc)
+    check_ulp(y[np.ix_(rows, cols)], ref_bits, f"w8a8 M={M}")
+
+
+# ---- W4A8-MXFP4 -------------------------------------------------------------------------------
+W4A8_SMALL = [(1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", W4A8_SMALL)
+def test_w4a8_small(M, N, K):
+    say(f"[w4a8] M={M} N={N} K={K}")
+    d = synth.make_w4a8(400, M, N, K)
+    w = prepack(hq.DESC_W4A8_MXFP4, 1, N, K, d["wq"], d["scales"])
+    y = gemm(hq.DESC_W4A8_MXFP4, M, N, K, to_dev(d["xq"]), to_dev(d["s_tok"]), w)
+    ref, _ = oracle.ref_w4a8(d["xq"], d["s_tok"], d["wq"], d["scales"])
+    check_float(y, ref, "w4a8")
+
+
+@pytest.mark.parametrize("M", [1, 32, 256, 2048, 8192])
+def test_w4a8_full_size_sampled(M):
+    N, K = 4096, 7168
+    say(f"[w4a8 full] M={M}")
+    d = synth.make_w4a8(4, M, N, K)
+    w = prepack(hq.DESC_W4A8_MXFP4, 1, N, K, d["wq"], d["scales"])
+    y = gemm(hq.DESC_W4A8_MXFP4, M, N, K, to_dev(d["xq"]), to_dev(d["s_tok"]), w)
+    rows, cols = _sample(M, N, np.random.default_rng(M))
+    ref, _ = oracle.ref_w4a8(d["xq"], d["s_tok"], d["wq"], d["scales"], rows=rows, cols=cols)
+    check_float(y[np.ix_(rows, cols)], ref, f"w4a8 M={M}")
+
+
+def test_w4a8_block_scale_extremes():
+    """Block exponents far from 127 (the e8m0 operand path) and a zero block."""
+    M, N, K = 4, 32, 256
+    d = synth.make_w4a8(401, M, N, K)
+    g = np.random.default_rng(0)
+    d["scales"] = g.integers(100, 150, d["scales"].shape).astype(np.uint8)
+    d["scales"][0, 0] = 0
+    w = prepack(hq.DESC_W4A8_MXFP4, 1, N, K, d["wq"], d["scales"])
+    y = gemm(hq.DESC_W4A8_MXFP4, M, N, K, to_dev(d["xq"]), to_dev(d["s_tok"]), w)
+    ref, _ = oracle.ref_w4a8(d["xq"], d["s_tok"], d["wq"], d["scales"])
+    check_float(y, ref, "w4a8 scale extremes")

@@ -1,0 +1,111 @@
+"""GPU parity of the MoE token sort (exact) and the grouped WNA16 GEMM (oracle tolerance)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_prepacked_amd as hq
+import synth
+
+from gpu_harness import DEV, check_float, prepack, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def align(ids: np.ndarray, E: int, bm: int):
+    T, topk = ids.shape
+    cap = hq.hq_moe_align_capacity(T, topk, E, bm)
+    sorted_ids = torch.full((max(cap, 1),), -7, dtype=torch.int32, device=DEV)
+    block_expert = torch.full((max(cap // bm, 1),), -7, dtype=torch.int32, device=DEV)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    npad = torch.empty(1, dtype=torch.int32, device=DEV)
+    hq.hq_moe_align(to_dev(ids.astype(np.int32)), T, topk, E, bm, sorted_ids, block_expert, offs, npad)
+    torch.cuda.synchronize()
+    n = int(npad.item())
+    return {
+        "num_padded": n, "expert_offsets": offs.cpu().numpy(),
+        "sorted_ids": sorted_ids.cpu().numpy()[:n], "block_expert": block_expert.cpu().numpy()[:n // bm],
+        "dev": (sorted_ids, block_expert, npad),
+    }
+
+
+def _check_align(ids, E, bm):
+    got = align(ids, E, bm)
+    ref = oracle.ref_moe_align(ids, E, bm)
+    assert got["num_padded"] == ref["num_padded"]
+    assert np.array_equal(got["expert_offsets"], ref["expert_offsets"])
+    assert np.array_equal(got["sorted_ids"], ref["sorted_ids"])
+    assert np.array_equal(got["block_expert"], ref["block_expert"])
+    return got
+
+
+def test_moe_align_hand_case():
+    c = GOLD["H5_moe_align"]
+    say("[moe_align] hand case")
+    got = _check_align(np.array(c["topk_ids"], np.int32), c["E"], c["block_m"])
+    assert got["sorted_ids"].tolist() == c["sorted_ids"]
+
+
+@pytest.mark.parametrize("T", [1, 3, 32, 512, 4096])
+@pytest.mark.parametrize("bm", [16, 64])
+def test_moe_align_skewed_routing(T, bm):
+    say(f"[moe_align] T={T} bm={bm}")
+    ids = synth.make_moe_inputs(5, T, 64)["topk_ids"]
+    _check_align(ids, 256, bm)
+
+
+def test_moe_align_out_of_range_ids_and_small_E():
+    ids = np.random.default_rng(3).integers(-2, 9, (700, 4)).astype(np.int32)
+    say("[moe_align] invalid ids")
+    _check_align(ids, 7, 32)
+
+
+def _moe_case(T, topk, E, N, K, bm, with_weights, seed):
+    inp = synth.make_moe_inputs(seed, T, K, E, topk)
+    ids = inp["topk_ids"]
+    active = np.unique(ids)
+    experts = {int(e): synth.make_moe_weights_expert(seed, int(e), N, K) for e in active}
+    desc = hq.DESC_W4A16_SYM
+    stride = hq.hq_prepacked_bytes(desc, 1, N, K)
+    w = torch.zeros(stride * E, dtype=torch.uint8, device=DEV)
+    for e, wd in experts.items():
+        w[e * stride:(e + 1) * stride] = prepack(desc, 1, N, K, wd["wq"], wd["scales"])
+    al = _check_align(ids, E, bm)
+    sorted_ids, block_expert, npad = al["dev"]
+    y = torch.full((T * topk, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    tw = to_dev(inp["topk_weights"].reshape(-1)) if with_weights else None
+    say(f"[moe gemm] T={T} topk={topk} E={E} N={N} K={K} bm={bm} weights={with_weights}")
+    hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, to_dev(inp["x"]), None, w, sorted_ids,
+                           block_expert, npad, bm, tw, y)
+    torch.cuda.synchronize()
+    return inp, experts, y.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,topk,E,N,K,bm,tw", [
+    (5, 2, 4, 64, 256, 16, False),
+    (64, 8, 16, 512, 1024, 16, True),
+    (300, 4, 8, 256, 512, 32, False),
+    (200, 8, 32, 272, 384, 64, True),     # odd channel tiles
+])
+def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
+    inp, experts, y = _moe_case(T, topk, E, N, K, bm, tw, 500 + T)
+    ref, _, valid = oracle.ref_moe_gemm(inp["x"], inp["topk_ids"], lambda e: experts[e], N, E, 128,
+                                        topk_weights=inp["topk_weights"] if tw else None)
+    assert valid.all()
+    check_float(y, ref, "moe gemm")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_moe_gemm_full_size_sampled(T):
+    """DeepSeek-V3-shaped layer: 256 experts, top-8, K=7168, fused gate_up N=4096."""
+    E, topk, N, K = 256, 8, 4096, 7168
+    bm = hq.hq_moe_block_m(hq.DESC_W4A16_SYM, T, topk, E, N, K)
+    inp, experts, y = _moe_case(T, topk, E, N, K, bm, False, 5)
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(T).integers(0, N, 128)]))
+    ref, _, _ = oracle.ref_moe_gemm(inp["x"], inp["topk_ids"], lambda e: experts[e], N, E, 128, cols=cols)
+    check_float(y[:, cols], ref, f"moe full T={T}")
