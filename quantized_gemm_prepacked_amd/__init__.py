@@ -13,6 +13,9 @@ import ctypes
 import os
 
 import numpy as np
+# PyTorch's HIP runtime must be the one loaded before libhq.so: the library then binds to that
+# same runtime (device memory and streams come from PyTorch).
+import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhq.so")

@@ -22,6 +22,29 @@ BUILD = os.path.join(PKG, "_build")
 SOURCES = ["hq_api.cpp", "prepack.cpp", "gemm_dispatch.hip", "gemm_skinny.hip", "moe_align.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def _hip_runtime_dir() -> str:
+    """Directory of the HIP runtime to link against.
+
+    PyTorch-ROCm ships its own libamdhip64/libhsa-runtime64. Device memory and streams come from
+    PyTorch, so the kernels must be registered with that same runtime: a second HIP runtime in
+    the process opens its own HSA instance and sees no device. The library records the
+    runtime's SONAME, so when PyTorch is loaded first (the binding imports it before opening
+    libhq.so) the loader reuses PyTorch's copy; loaded on its own, it resolves to ROCm's.
+    """
+    try:
+        import importlib.util
+        spec = importlib.util.find_spec("torch")
+        if spec and spec.origin:
+            d = os.path.join(os.path.dirname(spec.origin), "lib")
+            if os.path.exists(os.path.join(d, "libamdhip64.so")):
+                return d
+    except Exception:
+        pass
+    return "/opt/rocm/lib"
+
+
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 # Device code: gfx950 only; keep the compiler from forming packed-fp32 instructions.
 DEVICE = ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -54,7 +77,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs]
+    rt = _hip_runtime_dir()
+    cmd = ["g++", "-shared", "-fPIC", "-o", tmp, *objs, f"-L{rt}", "-l:libamdhip64.so",
+           f"-Wl,-rpath,{rt}", "-Wl,--no-undefined"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
