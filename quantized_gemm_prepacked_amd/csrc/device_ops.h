@@ -72,8 +72,13 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
                                                __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
 }
 
-// A: 32 fp8 e4m3 per lane (format 0), unscaled (e8m0 127 = 1.0).
-// B: 32 fp4 e2m1 per lane (format 4) in the low 4 dwords, scaled by the lane's e8m0 byte.
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = fp8 e4m3 (format 0) and B = fp4 e2m1 (format 4).
+// Operand K layouts (established with an on-device probe of single-element products):
+//   A, 8-bit: lane group g = l>>4 holds k = 16g + j in byte j (j < 16) and k = 64 + 16g + (j-16)
+//             in byte j (j >= 16), i.e. two 16-byte halves;
+//   B, 4-bit: lane group g holds k = 32g + j in nibble j (low nibble first), one contiguous block.
+// The e8m0 scale of K block b (k in [32b, 32b+32)) is taken from lane group b's scale register,
+// for A and for B alike. A is passed unscaled (127 = 2^0); B's scale is the weight block's.
 __device__ __forceinline__ f32x4 mfma_fp8_fp4(u32x4 a_lo, u32x4 a_hi, u32x4 b, int b_scale,
                                               f32x4 c) {
   i32x8 av = {int(a_lo[0]), int(a_lo[1]), int(a_lo[2]), int(a_lo[3]),

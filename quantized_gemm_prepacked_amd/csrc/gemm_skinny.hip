@@ -116,9 +116,11 @@ struct SkinnyFrag<FAM_W4A8, MB, NTW> {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (arow[mb]) {
-        const uint8_t* src = arow[mb] + size_t(u) * 128 + 32 * (lane >> 4);
+        // 8-bit A operand of the scaled MFMA: lane group g holds k = 16g..16g+15 in bytes 0..15
+        // and k = 64+16g..64+16g+15 in bytes 16..31.
+        const uint8_t* src = arow[mb] + size_t(u) * 128 + 16 * (lane >> 4);
         a[mb][0] = ldg16(src);
-        a[mb][1] = ldg16(src + 16);
+        a[mb][1] = ldg16(src + 64);
       } else {
         a[mb][0] = u32x4{0, 0, 0, 0};
         a[mb][1] = u32x4{0, 0, 0, 0};

@@ -16,7 +16,9 @@
 //     lane l holds k = 64*kt + 16*(l>>4) + j in byte j (0..15).
 //   W4A8 (FP4, K unit 128 = four MX blocks, v_mfma_scale_f32_16x16x128_f8f6f4):
 //     lane l holds k = 128*kt + 32*(l>>4) + j in nibble j (0..31, low nibble first): exactly one
-//     32-element MX block, so the lane's e8m0 byte is that block's scale.
+//     32-element MX block, so the lane's e8m0 byte is that block's scale (the MFMA takes block b's
+//     scale from lane group b). The fp8 activations are fed in the instruction's own 8-bit A
+//     layout (two 16-byte halves per lane, see device_ops.h).
 //
 // Regions per expert (each starts at a 256-byte aligned offset; experts are stacked with a
 // 256-byte aligned stride):

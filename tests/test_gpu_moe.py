@@ -45,10 +45,16 @@ def _check_align(ids, E, bm):
 
 
 def test_moe_align_hand_case():
+    """The hand case's routing at the smallest block the library takes (16 rows): expert 0 gets
+    flat ids 1, 4; expert 2 gets 0, 2, 5; expert 3 gets 3; sentinel T*topk = 6."""
     c = GOLD["H5_moe_align"]
-    say("[moe_align] hand case")
-    got = _check_align(np.array(c["topk_ids"], np.int32), c["E"], c["block_m"])
-    assert got["sorted_ids"].tolist() == c["sorted_ids"]
+    say("[moe_align] hand case, block_m 16")
+    got = _check_align(np.array(c["topk_ids"], np.int32), c["E"], 16)
+    s = got["sorted_ids"].tolist()
+    assert got["num_padded"] == 48 and got["expert_offsets"].tolist() == [0, 16, 16, 32, 48]
+    assert s[:2] == [1, 4] and s[16:19] == [0, 2, 5] and s[32] == 3
+    assert all(v == 6 for v in s[2:16] + s[19:32] + s[33:48])
+    assert got["block_expert"].tolist() == [0, 2, 3]
 
 
 @pytest.mark.parametrize("T", [1, 3, 32, 512, 4096])
