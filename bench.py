@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Throughput of the fused-dequantization quantized GEMM on one MI355X.
+
+Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
+scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
+M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
+--config w8a8 | w4a8 | moe.
+
+Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
+microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
+caches): every launch reads a different copy of the weights, cycled through more than 3x the
+MI355X's 256 MB Infinity Cache, so weight bytes come from HBM; each launch is bracketed by
+HIP events on the stream it runs on. `value` = total flops of a step / total kernel time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized GEMM TFLOPS and HBM GB/s vs roofline over M=1..8192; MoE tokens/s"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "int8": 5000.0, "fp8": 5000.0}
+
+WORKLOADS = {
+    "w4a16": dict(name="dense W4A16 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
+                  dtype="bf16", peak="bf16"),
+    "w8a8": dict(name="dense W8A8 INT8", N=8192, K=8192, Ms=[1, 64, 512, 4096], cfg=3,
+                 dtype="int8", peak="int8"),
+    "w4a8": dict(name="dense W4A8-MXFP4", N=4096, K=7168, Ms=[1, 32, 256, 2048, 8192], cfg=4,
+                 dtype="fp8", peak="fp8"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
+    """Bytes the method must move once: packed weights with scales/zeros, activations (+ per-token
+    scales), output."""
+    if wl == "w4a16":
+        w = N * K // 2 + N * (K // 128) * 2 + N * (K // 128) // 2
+        return w + M * K * 2 + M * N * 2
+    if wl == "w8a8":
+        return N * K + N * 4 + M * K + M * 4 + M * N * 2
+    return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
+
+
+def make_inputs(wl: str, spec: dict):
+    import numpy as np
+
+    import synth
+    N, K, cfg = spec["N"], spec["K"], spec["cfg"]
+    import quantized_gemm_prepacked_amd as hq
+    if wl == "w4a16":
+        d = synth.make_wna16(cfg, 1, N, K, asym=True)
+        desc = hq.DESC_W4A16_ASYM
+        std = (d["wq"], d["scales"], d["zeros"])
+        acts = {M: (synth.normal_bf16(synth.rng(cfg, M), (M, K)), None) for M in spec["Ms"]}
+    elif wl == "w8a8":
+        d = synth.make_w8a8(cfg, 1, N, K)
+        desc = hq.DESC_W8A8
+        std = (d["wq"], d["s_ch"], None)
+        acts = {}
+        for M in spec["Ms"]:
+            a = synth.make_w8a8_activations(cfg, M, K)
+            acts[M] = (a["xq"], a["s_tok"])
+    else:
+        d = synth.make_w4a8(cfg, 1, N, K)
+        desc = hq.DESC_W4A8_MXFP4
+        std = (d["wq"], d["scales"], None)
+        acts = {}
+        for M in spec["Ms"]:
+            a = synth.make_w4a8_activations(cfg, M, K)
+            acts[M] = (a["xq"], a["s_tok"])
+    packed = np.zeros(hq.hq_prepacked_bytes(desc, 1, N, K), np.uint8)
+    hq.hq_prepack_weights(desc, 1, N, K, *std, packed)
+    return desc, std, packed, acts
+
+
+def cpu_baseline(wl: str, spec: dict, std, acts):
+    """The CPU oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    N, K = spec["N"], spec["K"]
+    flops = 0.0
+    secs = 0.0
+    parts = []
+    for M in spec["Ms"]:
+        x, s = acts[M]
+        rows = None if M <= 1024 else np.arange(1024)
+        m_eff = M if rows is None else len(rows)
+        t0 = time.perf_counter()
+        if wl == "w4a16":
+            oracle.ref_wna16(x, std[0], std[1], std[2], 128, rows=rows)
+        elif wl == "w8a8":
+            oracle.ref_w8a8(x, s, std[0], std[1], rows=rows)
+        else:
+            oracle.ref_w4a8(x, s, std[0], std[1], rows=rows)
+        dt = time.perf_counter() - t0
+        secs += dt
+        flops += 2.0 * m_eff * N * K
+        parts.append(f"M={M}" + ("" if rows is None else f" (first {m_eff} rows)"))
+    return {
+        "value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{spec['name']}: " + ", ".join(parts) + f"; fp64 dequantize + matmul, {secs:.1f} s",
+    }
+
+
+def run_dense(args, wl: str):
+    import numpy as np
+    import torch
+
+    import quantized_gemm_prepacked_amd as hq
+
+    spec = WORKLOADS[wl]
+    N, K, Ms = spec["N"], spec["K"], spec["Ms"]
+    dev = torch.device("cuda:0")
+    log(f"[bench] {spec['name']} N={N} K={K} M={Ms}: generating inputs")
+    desc, std, packed, acts = make_inputs(wl, spec)
+    w0 = torch.from_numpy(packed).to(dev)
+    n_copies = max(2, int(np.ceil(768e6 / packed.nbytes)))
+    weights = [w0] + [w0.clone() for _ in range(n_copies - 1)]
+    dev_acts, outs, wss = {}, {}, {}
+    for M in Ms:
+        x, s = acts[M]
+        xt = torch.from_numpy(np.ascontiguousarray(x).view(np.uint8)).to(dev)
+        st = None if s is None else torch.from_numpy(s).to(dev)
+        dev_acts[M] = (xt, st)
+        outs[M] = torch.empty((M, N), dtype=torch.int16, device=dev)
+        nb = hq.hq_gemm_workspace_bytes(desc, M, N, K)
+        wss[M] = (torch.empty(max(nb, 16), dtype=torch.uint8, device=dev), nb)
+    order = sorted(Ms, reverse=True)  # the long launch first keeps the queue ahead of the GPU
+    stream = torch.cuda.current_stream()
+    ctr = [0]
+
+    def launch(M):
+        w = weights[ctr[0] % n_copies]
+        ctr[0] += 1
+        xt, st = dev_acts[M]
+        ws, nb = wss[M]
+        hq.hq_gemm(desc, M, N, K, xt, st, w, outs[M], ws, nb, stream)
+
+    log(f"[bench] warmup {args.warmup} steps ({n_copies} weight copies rotate)")
+    for _ in range(args.warmup):
+        for M in order:
+            launch(M)
+    torch.cuda.synchronize()
+    evs = {M: [] for M in Ms}
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for M in order:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(M)
+            b.record(stream)
+            evs[M].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sweep = []
+    tot_flops = 0.0
+    tot_s = 0.0
+    for M in Ms:
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs[M]])) * 1e3
+        fl = 2.0 * M * N * K
+        by = alg_bytes(wl, M, N, K)
+        tf = fl / (us * 1e-6) / 1e12
+        gbs = by / (us * 1e-6) / 1e9
+        peak = PEAK_TFLOPS[spec["peak"]]
+        frac_c, frac_m = tf / peak, gbs / HBM_PEAK_GBS
+        sweep.append({"M": M, "us": round(us, 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
+                      "bound": "hbm" if frac_m >= frac_c else "mfma",
+                      "frac": round(max(frac_c, frac_m), 4), "bytes": by, "flops": fl})
+        tot_flops += fl
+        tot_s += us * 1e-6
+    dom = max(sweep, key=lambda r: r["us"])
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS[spec["peak"]],
+                "unit": "TFLOP/s", "frac": round(dom["tflops"] / PEAK_TFLOPS[spec["peak"]], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = f"M={dom['M']}"
+    line = {
+        "metric": METRIC, "value": round(tot_flops / tot_s / 1e12, 4), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
+        "config": {"workload": spec["name"], "N": N, "K": K, "M": Ms,
+                   "weights": {"w4a16": "uint4 asym g128 bf16 scale + uint4 zero",
+                               "w8a8": "int8 per-channel fp32 scale, int8 per-token act",
+                               "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act"}[wl]},
+        "roofline": roof,
+        "sweep": sweep,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (bounded sample)")
+        line["cpu_baseline"] = cpu_baseline(wl, spec, std, acts)
+    else:
+        line["cpu_baseline"] = None
+    return line
+
+
+MOE = dict(name="MoE grouped GEMM W4A16 (DeepSeek-V3-shaped gate_up)", E=256, topk=8, N=4096,
+           K=7168, Ts=[1, 32, 512, 4096], cfg=5)
+
+
+def run_moe(args):
+    """Token sort + grouped GEMM per T. tokens/s = T / (t_align + t_gemm)."""
+    import numpy as np
+    import torch
+
+    import quantized_gemm_prepacked_amd as hq
+    import synth
+
+    E, topk, N, K, Ts, cfg = (MOE[k] for k in ("E", "topk", "N", "K", "Ts", "cfg"))
+    dev = torch.device("cuda:0")
+    desc = hq.DESC_W4A16_SYM
+    stride = hq.hq_prepacked_bytes(desc, 1, N, K)
+    log(f"[bench] {MOE['name']}: {E} experts x {stride / 1e6:.1f} MB prepacked (random INT4 codes)")
+    w0 = torch.empty(stride * E, dtype=torch.uint8, device=dev)
+    g = synth.rng(cfg, 0)
+    std = {}
+    host = np.zeros(stride, np.uint8)
+    for e in range(E):
+        d = synth.random_int4_sym_expert(g, N, K)
+        if e < 16:
+            std[e] = d
+        hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, host)
+        w0[e * stride:(e + 1) * stride].copy_(torch.from_numpy(host))
+    n_copies = 4                      # > 256 MB Infinity Cache between reuses even at T = 1
+    weights = [w0] + [w0.clone() for _ in range(n_copies - 1)]
+    state = {}
+    for T in Ts:
+        inp = synth.make_moe_inputs(cfg, T, K, E, topk)
+        bm = hq.hq_moe_block_m(desc, T, topk, E, N, K)
+        cap = hq.hq_moe_align_capacity(T, topk, E, bm)
+        hist = np.bincount(inp["topk_ids"].reshape(-1), minlength=E)
+        state[T] = dict(
+            x=torch.from_numpy(inp["x"].view(np.int16)).to(dev),
+            ids=torch.from_numpy(inp["topk_ids"]).to(dev), bm=bm,
+            sorted=torch.empty(cap, dtype=torch.int32, device=dev),
+            bexp=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
+            offs=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            npad=torch.empty(1, dtype=torch.int32, device=dev),
+            y=torch.empty((T * topk, N), dtype=torch.int16, device=dev),
+            active=int((hist > 0).sum()), top=int(hist.max()), inp=inp)
+    stream = torch.cuda.current_stream()
+    ctr = [0]
+
+    def launch(T, evs=None):
+        s = state[T]
+        w = weights[ctr[0] % n_copies]
+        ctr[0] += 1
+        if evs is not None:
+            evs[0].record(stream)
+        hq.hq_moe_align(s["ids"], T, topk, E, s["bm"], s["sorted"], s["bexp"], s["offs"], s["npad"],
+                        None, 0, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, s["x"], None, w, s["sorted"], s["bexp"],
+                               s["npad"], s["bm"], None, s["y"], None, 0, stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    order = sorted(Ts, reverse=True)
+    for _ in range(args.warmup):
+        for T in order:
+            launch(T)
+    torch.cuda.synchronize()
+    rec = {T: [] for T in Ts}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for T in order:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            launch(T, evs)
+            rec[T].append(evs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sweep = []
+    tot_t = 0.0
+    tot_tok = 0
+    for T in Ts:
+        ta = float(np.mean([e[0].elapsed_time(e[1]) for e in rec[T]])) * 1e3
+        tg = float(np.mean([e[1].elapsed_time(e[2]) for e in rec[T]])) * 1e3
+        s = state[T]
+        fl = 2.0 * T * topk * N * K
+        by = s["active"] * stride + T * K * 2 + T * topk * N * 2
+        tf = fl / (tg * 1e-6) / 1e12
+        gbs = by / (tg * 1e-6) / 1e9
+        fc, fm = tf / PEAK_TFLOPS["bf16"], gbs / HBM_PEAK_GBS
+        sweep.append({"T": T, "block_m": s["bm"], "active_experts": s["active"], "top_expert_rows": s["top"],
+                      "align_us": round(ta, 3), "gemm_us": round(tg, 3),
+                      "tokens_per_s": round(T / ((ta + tg) * 1e-6), 1), "tflops": round(tf, 3),
+                      "gbps": round(gbs, 1), "bound": "hbm" if fm >= fc else "mfma",
+                      "frac": round(max(fc, fm), 4)})
+        tot_t += (ta + tg) * 1e-6
+        tot_tok += T
+    dom = max(sweep, key=lambda r: r["gemm_us"])
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / PEAK_TFLOPS["bf16"], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
+    roof.update(traffic=None, kernel=f"grouped GEMM T={dom['T']}")
+    line = {
+        "metric": METRIC, "value": round(tot_tok / tot_t, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": MOE["name"], "E": E, "topk": topk, "N": N, "K": K, "T": Ts,
+                   "routing": "N(0,1) logits + Zipf(1.1) log-prior, softmax top-8"},
+        "roofline": roof, "sweep": sweep, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        inp = state[1]["inp"]
+        ids = inp["topk_ids"]
+        need = [int(e) for e in np.unique(ids)]
+        rg = synth.rng(cfg, 0)
+        ws = {}
+        for e in range(max(need) + 1):      # regenerate the same random experts in order
+            d = synth.random_int4_sym_expert(rg, N, K)
+            if e in need:
+                ws[e] = d
+        t0 = time.perf_counter()
+        oracle.ref_moe_gemm(inp["x"], ids, lambda e: ws[e], N, E, 128)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(),
+                                "kind": "oracle", "sample": f"T=1 ({len(need)} experts), {dt:.1f} s"}
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path: every box here has a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.config == "moe":
+        line = run_moe(args)
+    else:
+        line = run_dense(args, args.config)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -90,6 +90,15 @@ struct SkinnyCfg {
 };
 const SkinnyCfg* skinny_configs(int* count);
 
+// A tiled-kernel instantiation: waves own (16*MW) x (16*NTW) sub-tiles, WM x WN waves per
+// workgroup; the workgroup tile is (16*MW*WM) x (16*NTW*WN).
+struct TiledCfg {
+  int mw, ntw, wm, wn;
+};
+const TiledCfg* tiled_configs(int* count);
+hipError_t launch_tiled(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
+                        int tiles_n, hipStream_t s);
+
 hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid, hipStream_t s);
 hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s);
 

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -29,6 +31,24 @@ int pick_skinny(int64_t rows, int64_t N) {
 }
 
 size_t acc_elem_bytes() { return 4; }
+
+// Sweep override for tuning runs: HQ_TUNE="cfg=<i>,split=<s>" forces a skinny configuration
+// and K split for every dense call (ignored when it does not fit the shape).
+struct TuneOverride {
+  int cfg = -1, split = -1;
+};
+
+const TuneOverride& tune_override() {
+  static TuneOverride t = [] {
+    TuneOverride o;
+    if (const char* e = std::getenv("HQ_TUNE")) {
+      std::sscanf(e, "cfg=%d,split=%d", &o.cfg, &o.split);
+    }
+    return o;
+  }();
+  return t;
+}
+
 
 template <int FAM>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(KParams p) {
@@ -58,29 +78,61 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+
+// Tiled configuration for a dense call, or -1 when the shape does not fit one.
+int pick_tiled(const Combo&, int64_t N, int64_t K) {
+  if (K % 128 != 0) return -1;
+  if (N % 128 == 0) return 0;
+  if (N % 64 == 0) return 1;
+  if (N % 32 == 0) return 2;
+  return -1;
+}
+
+constexpr int64_t kTiledMinM = 128;
+
+}  // namespace
+
 Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   Plan pl{};
+  const TuneOverride& tov = tune_override();
+  const int tcfg = pick_tiled(c, N, K);
+  if (tcfg >= 0 && M >= kTiledMinM && tov.cfg < 0) {
+    pl.kind = 1;
+    pl.cfg = tcfg;
+    pl.split = 1;
+    pl.ws_bytes = 0;
+    return pl;
+  }
   pl.kind = 0;
   pl.cfg = pick_skinny(M, N);
   int n_cfg = 0;
-  const SkinnyCfg& sc = skinny_configs(&n_cfg)[pl.cfg];
+  const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
+  if (tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0) pl.cfg = tov.cfg;
+  const SkinnyCfg& sc = cfgs[pl.cfg];
   const int64_t units = K / k_unit(c);
   const int64_t wgs = (N / 16 / sc.ntw) * ((M + 16 * sc.mb - 1) / (16 * sc.mb));
   int split = 1;
   // Too few workgroups to cover the chip: split K across workgroups as long as every wave
   // keeps at least two units.
   while (wgs * split < kCUs && units / (int64_t(split) * 2 * sc.nw) >= 2) split *= 2;
+  if (tov.split >= 1 && tov.split <= units) split = tov.split;
   pl.split = split;
   pl.ws_bytes = split > 1 ? size_t(split) * M * N * acc_elem_bytes() : 0;
   return pl;
 }
 
-Plan plan_moe(const Combo&, int64_t, int32_t, int32_t, int64_t N, int64_t, int32_t block_m) {
+Plan plan_moe(const Combo&, int64_t, int32_t, int32_t, int64_t N, int64_t K, int32_t block_m) {
   Plan pl{};
-  pl.kind = 0;
-  pl.cfg = pick_skinny(block_m, N);
   pl.split = 1;
   pl.ws_bytes = 0;
+  if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
+    pl.kind = 1;
+    pl.cfg = 3;
+    return pl;
+  }
+  pl.kind = 0;
+  pl.cfg = pick_skinny(block_m, N);
   return pl;
 }
 
@@ -111,6 +163,29 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   p.scales_off = L.scales_off;
   p.zeros_off = L.zeros_off;
   const bool moe = call.sorted_ids != nullptr;
+  if (plan.kind == 1) {
+    int n_cfg = 0;
+    const TiledCfg& tc = tiled_configs(&n_cfg)[plan.cfg];
+    const int bm = 16 * tc.mw * tc.wm;
+    const int bn = 16 * tc.ntw * tc.wn;
+    p.split = 1;
+    p.units_per_split = p.k_units;
+    const int tiles_n = int(call.N / bn);
+    if (moe) {
+      p.M = int(call.T * call.topk);
+      p.sorted_ids = call.sorted_ids;
+      p.block_expert = call.block_expert;
+      p.num_padded = call.num_padded;
+      p.topk_weights = call.topk_weights;
+      p.topk = call.topk;
+      return launch_tiled(p, c.fam, true, plan.cfg, dim3(unsigned(tiles_n), unsigned(call.max_blocks)),
+                          int(call.max_blocks), tiles_n, call.stream);
+    }
+    p.M = int(call.M);
+    const int tiles_m = int((call.M + bm - 1) / bm);
+    return launch_tiled(p, c.fam, false, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n,
+                        call.stream);
+  }
   int n_cfg = 0;
   const SkinnyCfg& sc = skinny_configs(&n_cfg)[plan.cfg];
   const int rows_per_block = 16 * sc.mb;

@@ -35,7 +35,8 @@ __all__ = [
     "rng", "bf16_bits", "bf16_bits_to_f32", "normal_bf16",
     "quantize_int4_sym", "quantize_uint4_asym", "quantize_int8_rows",
     "quantize_mxfp4", "quantize_fp8_rows", "moe_routing",
-    "make_wna16", "make_w8a8", "make_w4a8", "make_moe_weights_expert", "make_moe_inputs",
+    "make_wna16", "make_w8a8", "make_w4a8", "make_w8a8_activations", "make_w4a8_activations",
+    "make_moe_weights_expert", "make_moe_inputs", "random_int4_sym_expert",
     "E2M1_MAGNITUDES",
 ]
 
@@ -198,22 +199,41 @@ def make_wna16(config_id: int, M: int, N: int, K: int, asym: bool, g: int = 128)
     return {"x": x, **qw}
 
 
+def make_w8a8_activations(config_id: int, M: int, K: int):
+    """Per-token INT8 activations quantized from bf16 N(0,1)."""
+    x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))
+    xq, s_tok = quantize_int8_rows(x)
+    return {"xq": xq, "s_tok": s_tok}
+
+
 def make_w8a8(config_id: int, M: int, N: int, K: int):
     """Dense W8A8: per-channel INT8 weights, per-token INT8 activations from bf16 N(0,1)."""
     w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
     wq, s_ch = quantize_int8_rows(w)
+    return {**make_w8a8_activations(config_id, M, K), "wq": wq, "s_ch": s_ch}
+
+
+def make_w4a8_activations(config_id: int, M: int, K: int):
+    """Per-token FP8 e4m3 activations quantized from bf16 N(0,1)."""
     x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))
-    xq, s_tok = quantize_int8_rows(x)
-    return {"xq": xq, "s_tok": s_tok, "wq": wq, "s_ch": s_ch}
+    xq, s_tok = quantize_fp8_rows(x)
+    return {"xq": xq, "s_tok": s_tok}
 
 
 def make_w4a8(config_id: int, M: int, N: int, K: int):
     """Dense W4A8-MXFP4: MXFP4 weights, per-token FP8 e4m3 activations from bf16 N(0,1)."""
     w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
     qw = quantize_mxfp4(w)
-    x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))
-    xq, s_tok = quantize_fp8_rows(x)
-    return {"xq": xq, "s_tok": s_tok, **qw}
+    return {**make_w4a8_activations(config_id, M, K), **qw}
+
+
+def random_int4_sym_expert(g: np.random.Generator, N: int, K: int, gs: int = 128):
+    """Standard-format symmetric INT4 weights with uniformly random codes and bf16 scales near
+    absmax/7 of N(0, 0.02) groups. Used where only the data volume matters (throughput runs
+    over hundreds of experts), since drawing and quantizing billions of normals is slow."""
+    wq = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    s = (0.0094 * (1.0 + 0.1 * g.standard_normal((N, K // gs)))).astype(np.float32)
+    return {"wq": wq, "scales": bf16_bits(s)}
 
 
 def make_moe_weights_expert(config_id: int, e: int, N: int, K: int, g: int = 128):

@@ -97,6 +97,8 @@ def _moe_case(T, topk, E, N, K, bm, with_weights, seed):
     (64, 8, 16, 512, 1024, 16, True),
     (300, 4, 8, 256, 512, 32, False),
     (200, 8, 32, 272, 384, 64, True),     # odd channel tiles
+    (512, 8, 16, 256, 512, 64, True),     # 64-row blocks on the LDS-tiled kernel
+    (700, 8, 64, 384, 1024, 64, False),   # skewed, ragged expert counts, tiled kernel
 ])
 def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
     inp, experts, y = _moe_case(T, topk, E, N, K, bm, tw, 500 + T)
