@@ -261,7 +261,10 @@ def run_moe(args):
             offs=torch.empty(E + 1, dtype=torch.int32, device=dev),
             npad=torch.empty(1, dtype=torch.int32, device=dev),
             y=torch.empty((T * topk, N), dtype=torch.int16, device=dev),
+            wsb=hq.hq_moe_gemm_workspace_bytes(desc, T, topk, E, N, K, bm),
             active=int((hist > 0).sum()), top=int(hist.max()), inp=inp)
+    for T in Ts:
+        state[T]["ws"] = torch.empty(max(state[T]["wsb"], 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ctr = [0]
 
@@ -276,7 +279,7 @@ def run_moe(args):
         if evs is not None:
             evs[1].record(stream)
         hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, s["x"], None, w, s["sorted"], s["bexp"],
-                               s["npad"], s["bm"], None, s["y"], None, 0, stream)
+                               s["npad"], s["bm"], None, s["y"], s["ws"], s["wsb"], stream)
         if evs is not None:
             evs[2].record(stream)
 

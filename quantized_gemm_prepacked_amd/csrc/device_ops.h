@@ -62,9 +62,36 @@ __device__ __forceinline__ bf16x8 dequant_int4x8(uint32_t v, float z) {
   return r;
 }
 
+// Cheaper form for kernels that remove the offset separately: returns (128 + u) for the 8 codes,
+// exact in bf16 (0x4300 is 128.0 and its last mantissa bit weighs 1, so OR-ing a 4-bit u into the
+// low bits adds u). One bit-select per pair of weights.
+__device__ __forceinline__ bf16x8 dequant_int4x8_offset128(uint32_t v) {
+  const uint32_t m = 0x000F000Fu, c = 0x43004300u;
+  const uint32_t p0 = (v & m) | c;
+  const uint32_t p1 = ((v >> 4) & m) | c;
+  const uint32_t p2 = ((v >> 8) & m) | c;
+  const uint32_t p3 = ((v >> 12) & m) | c;
+  const u32x4 r = {p0, p1, p2, p3};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// -(128 + z) in all 8 bf16 slots (z in [0, 15]): the constant operand that removes the offset of
+// dequant_int4x8_offset128 inside an MFMA chain.
+__device__ __forceinline__ bf16x8 neg_offset_bf16x8(uint32_t z) {
+  const uint32_t h = 0xC300u | z;
+  const uint32_t pr = h | (h << 16);
+  const u32x4 r = {pr, pr, pr, pr};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // ---- MFMA wrappers ------------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 x fp32 16x16x4: lane l supplies A[l & 15][l >> 4] and B[l >> 4][l & 15].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {

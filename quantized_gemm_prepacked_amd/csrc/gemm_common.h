@@ -31,6 +31,7 @@ struct KParams {
   const int32_t* num_padded;
   const float* topk_weights;
   int topk;
+  int s_rows;               // rows of the per-group activation sums in the workspace (WNA16 tiled)
 };
 
 template <int FAM>
@@ -98,6 +99,8 @@ struct TiledCfg {
 const TiledCfg* tiled_configs(int* count);
 hipError_t launch_tiled(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
                         int tiles_n, hipStream_t s);
+
+hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStream_t s);
 
 hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid, hipStream_t s);
 hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s);

@@ -101,7 +101,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
     pl.kind = 1;
     pl.cfg = tcfg;
     pl.split = 1;
-    pl.ws_bytes = 0;
+    pl.ws_bytes = c.fam == FAM_WNA16 ? size_t(M) * (K / 128) * 4 : 0;  // activation group sums
     return pl;
   }
   pl.kind = 0;
@@ -122,13 +122,14 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   return pl;
 }
 
-Plan plan_moe(const Combo&, int64_t, int32_t, int32_t, int64_t N, int64_t K, int32_t block_m) {
+Plan plan_moe(const Combo&, int64_t T, int32_t, int32_t, int64_t N, int64_t K, int32_t block_m) {
   Plan pl{};
   pl.split = 1;
   pl.ws_bytes = 0;
   if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
     pl.kind = 1;
     pl.cfg = 3;
+    pl.ws_bytes = size_t(T) * (K / 128) * 4;  // per-token activation group sums
     return pl;
   }
   pl.kind = 0;
@@ -171,6 +172,11 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.split = 1;
     p.units_per_split = p.k_units;
     const int tiles_n = int(call.N / bn);
+    if (c.fam == FAM_WNA16) {
+      p.s_rows = int(moe ? call.T : call.M);
+      hipError_t e = launch_group_sums(p.a, p.s_rows, p.K, static_cast<float*>(call.ws), call.stream);
+      if (e != hipSuccess) return e;
+    }
     if (moe) {
       p.M = int(call.T * call.topk);
       p.sorted_ids = call.sorted_ids;

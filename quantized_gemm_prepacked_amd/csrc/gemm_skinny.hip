@@ -51,19 +51,24 @@ struct SkinnyFrag<FAM_WNA16, MB, NTW> {
     }
   }
 
+  // The group's partial sum_k x*(u - z) is formed on the MFMA as sum_k x*(128 + u) plus
+  // sum_k x*(-(128 + z)): the first operand costs one bit-select per weight pair, the second is
+  // a per-channel constant. At small M the MFMA has cycles to spare; the VALU does not.
   __device__ __forceinline__ void compute(const KParams& p, int lane, f32x4 (*acc)[NTW]) const {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const float z = p.asym ? float((lane & 1) ? (zb[t] >> 4) : (zb[t] & 0xFu)) : 8.0f;
+      const uint32_t z = p.asym ? ((lane & 1) ? (zb[t] >> 4) : (zb[t] & 0xFu)) : 8u;
       const float s = bf16_bits_to_f32(s_bits[t]);
+      const bf16x8 bneg = neg_offset_bf16x8(z);
       f32x4 part[MB];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16x8 bw = dequant_int4x8(b[t][d], z);
+        const bf16x8 bw = dequant_int4x8_offset128(b[t][d]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const bf16x8 av = __builtin_bit_cast(bf16x8, a[mb][d]);
           part[mb] = mfma_bf16(av, bw, d == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : part[mb]);
+          part[mb] = mfma_bf16(av, bneg, part[mb]);
         }
       }
 #pragma unroll

@@ -10,8 +10,10 @@
 //   - each wave streams the packed weight units of its own channel tiles straight from HBM into
 //     registers one step ahead (1 KiB per unit, one 128-bit load per lane), dequantizes them in
 //     registers and feeds the MFMA;
-//   - WNA16 keeps the integer (q - z) exact in bf16, forms each 128-k group's fp32 partial with
-//     four MFMAs and applies the group scale with one fp32 FMA per accumulator.
+//   - WNA16 feeds the MFMA the exact bf16 value 128 + u of each code (one bit-select per pair of
+//     weights), forms each 128-k group's fp32 partial with four MFMAs and applies the group scale
+//     with one fp32 FMA per accumulator; the offset term sum_g s*(128 + z)*rowsum_g(x) is removed
+//     once at the end by a K/128-deep fp32 MFMA contraction (exact enough: fp32 throughout).
 // Workgroups are ordered so that each XCD (workgroup id mod 8) gets a contiguous band of tiles
 // grouped along M, which keeps the shared weight and activation tiles in that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -188,12 +190,10 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_gemm_kernel(KParams p, int
           af[mb][d] = __builtin_bit_cast(bf16x8, read_frag(stage, mb, 4 * (lane >> 4) + d));
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        const uint32_t zb = bcur.z[t];
-        const float z = p.asym ? float((lane & 1) ? (zb >> 4) : (zb & 0xFu)) : 8.0f;
         const float s = bf16_bits_to_f32(bcur.s[t]);
         bf16x8 bw[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) bw[d] = dequant_int4x8(bcur.b[t][0][d], z);
+        for (int d = 0; d < 4; ++d) bw[d] = dequant_int4x8_offset128(bcur.b[t][0][d]);
 #pragma unroll
         for (int mb = 0; mb < MW; ++mb) {
           f32x4 part = mfma_bf16(af[mb][0], bw[0], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -233,6 +233,48 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_gemm_kernel(KParams p, int
     __syncthreads();
   }
 
+  if constexpr (FAM == FAM_WNA16) {
+    // The MFMA summed x*(128 + u); remove sum_g s[n,g]*(128 + z[n,g]) * S[g][row], S = the
+    // group sums of the activation row (computed by group_sums_kernel into the workspace), as a
+    // K' = K/128 fp32 contraction on the MFMA: lane l supplies S[g][row l&15] and
+    // -s*(128+z) for channel l&15, g = 4*gq + (l >> 4).
+    const float* S = reinterpret_cast<const float*>(p.ws);
+    const int G = p.K / 128;
+    int srow[MW];
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      const int r = row0 + wm * 16 * MW + 16 * mb + (lane & 15);
+      if constexpr (MOE) {
+        const int id = p.sorted_ids[r];
+        srow[mb] = id < p.M ? id / p.topk : -1;
+      } else {
+        srow[mb] = r < p.M ? r : -1;
+      }
+    }
+    for (int gq = 0; gq < G / 4; ++gq) {
+      const int g = 4 * gq + (lane >> 4);
+      float bneg[NTW];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const size_t unit = size_t(nt0 + t) * p.k_units + g;
+        const float sc = bf16_bits_to_f32(
+            *reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
+        uint32_t z = 8;
+        if (p.asym) {
+          const uint32_t zb = w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)];
+          z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
+        }
+        bneg[t] = -sc * float(128u + z);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        const float sv = srow[mb] >= 0 ? S[size_t(g) * p.s_rows + srow[mb]] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[mb][t] = mfma_f32(sv, bneg[t], acc[mb][t]);
+      }
+    }
+  }
+
   // ---- epilogue: lane holds rows 4*(lane>>4)+i, column lane&15 of each 16x16 tile ----
 #pragma unroll
   for (int mb = 0; mb < MW; ++mb)
@@ -246,7 +288,33 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_gemm_kernel(KParams p, int
       }
 }
 
+// S[g][r] = sum of the bf16 activations of row r over k in [128g, 128g + 128), fp32.
+__global__ __launch_bounds__(256) void group_sums_kernel(const uint8_t* __restrict__ a, int rows,
+                                                         int K, float* __restrict__ S) {
+  const int G = K / 128;
+  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= long(rows) * G) return;
+  const int r = int(idx % rows);
+  const int g = int(idx / rows);
+  const u32x4* src = reinterpret_cast<const u32x4*>(a + (size_t(r) * K + size_t(g) * 128) * 2);
+  float sum = 0.0f;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const u32x4 v = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xFFFF0000u);
+  }
+  S[size_t(g) * rows + r] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStream_t s) {
+  const long total = long(rows) * (K / 128);
+  hipLaunchKernelGGL(group_sums_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a,
+                     rows, K, S);
+  return hipGetLastError();
+}
 
 static constexpr TiledCfg kTiled[] = {
     {4, 4, 2, 2},  // 0: 128 x 128 tile, 64 x 64 per wave

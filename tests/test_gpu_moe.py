@@ -86,8 +86,10 @@ def _moe_case(T, topk, E, N, K, bm, with_weights, seed):
     y = torch.full((T * topk, N), 0x7FC0, dtype=torch.int16, device=DEV)
     tw = to_dev(inp["topk_weights"].reshape(-1)) if with_weights else None
     say(f"[moe gemm] T={T} topk={topk} E={E} N={N} K={K} bm={bm} weights={with_weights}")
+    wsb = hq.hq_moe_gemm_workspace_bytes(desc, T, topk, E, N, K, bm)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
     hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, to_dev(inp["x"]), None, w, sorted_ids,
-                           block_expert, npad, bm, tw, y)
+                           block_expert, npad, bm, tw, y, ws, wsb)
     torch.cuda.synchronize()
     return inp, experts, y.cpu().numpy()
 
