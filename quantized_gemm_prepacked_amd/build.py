@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libhq.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["hq_api.cpp", "prepack.cpp", "gemm_dispatch.hip", "gemm_skinny.hip", "gemm_tiled.hip", "moe_align.hip"]
+SOURCES = ["hq_api.cpp", "prepack.cpp", "gemm_dispatch.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gemm_pipe.hip", "moe_align.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -47,8 +47,10 @@ def _hip_runtime_dir() -> str:
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 # Device code: gfx950 only; keep the compiler from forming packed-fp32 instructions.
+# MFMA results stay in ordinary VGPRs: the WNA16 group scale is applied to the accumulators with
+# VALU FMAs, which would otherwise shuttle every value between AGPRs and VGPRs.
 DEVICE = ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-gpu-rdc", "-munsafe-fp-atomics"]
+          "-fno-gpu-rdc", "-munsafe-fp-atomics", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def _compile(src: str) -> str:

@@ -94,11 +94,20 @@ const SkinnyCfg* skinny_configs(int* count);
 // A tiled-kernel instantiation: waves own (16*MW) x (16*NTW) sub-tiles, WM x WN waves per
 // workgroup; the workgroup tile is (16*MW*WM) x (16*NTW*WN).
 struct TiledCfg {
-  int mw, ntw, wm, wn;
+  int mw, ntw, wm, wn, occ;  // occ: waves per SIMD the register allocation must allow
 };
 const TiledCfg* tiled_configs(int* count);
 hipError_t launch_tiled(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
                         int tiles_n, hipStream_t s);
+
+// A pipelined-kernel instantiation: WM x WN waves of (16*MW) x (16*NTW), STAGES K steps in flight.
+struct PipeCfg {
+  int mw, ntw, wm, wn, stages;
+};
+const PipeCfg* pipe_configs(int* count);
+int pipe_lds_bytes(int fam, int cfg);
+hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
+                       int tiles_n, hipStream_t s);
 
 hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStream_t s);
 

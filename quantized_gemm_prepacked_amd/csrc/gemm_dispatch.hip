@@ -32,23 +32,20 @@ int pick_skinny(int64_t rows, int64_t N) {
 
 size_t acc_elem_bytes() { return 4; }
 
-// Sweep override for tuning runs: HQ_TUNE="cfg=<i>,split=<s>" forces a skinny configuration
-// and K split for every dense call (ignored when it does not fit the shape).
+// Sweep override for tuning runs: HQ_TUNE="kind=<0|1>,cfg=<i>,split=<s>" forces the kernel
+// family (0 skinny, 1 tiled), its configuration and (skinny) the K split for every dense call;
+// entries that do not fit the shape are ignored. Read on every call so one process can sweep.
 struct TuneOverride {
-  int cfg = -1, split = -1;
+  int kind = -1, cfg = -1, split = -1;
 };
 
-const TuneOverride& tune_override() {
-  static TuneOverride t = [] {
-    TuneOverride o;
-    if (const char* e = std::getenv("HQ_TUNE")) {
-      std::sscanf(e, "cfg=%d,split=%d", &o.cfg, &o.split);
-    }
-    return o;
-  }();
-  return t;
+TuneOverride tune_override() {
+  TuneOverride o;
+  if (const char* e = std::getenv("HQ_TUNE")) {
+    std::sscanf(e, "kind=%d,cfg=%d,split=%d", &o.kind, &o.cfg, &o.split);
+  }
+  return o;
 }
-
 
 template <int FAM>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(KParams p) {
@@ -89,17 +86,81 @@ int pick_tiled(const Combo&, int64_t N, int64_t K) {
   return -1;
 }
 
-constexpr int64_t kTiledMinM = 128;
+// The per-M-range table for large M (kinds: 1 = LDS-tiled, 2 = async-pipelined), measured on
+// MI355X at the benchmark shapes: the first entry whose max_m covers M and whose tile divides N
+// is used; below the first entry (and when no tile fits) the skinny kernel runs.
+struct RangeEntry {
+  int64_t max_m;
+  int kind, cfg;
+};
+constexpr int64_t kInf = int64_t(1) << 40;
+constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {192, 2, 2}, {384, 1, 9}, {kInf, 2, 7}};
+constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {512, 2, 3}, {1536, 2, 10}, {kInf, 2, 8}};
+constexpr RangeEntry kW4a8Table[] = {{256, 0, 0}, {768, 2, 3}, {1536, 2, 2}, {kInf, 2, 11}};
+
+int tile_n_of(int kind, int cfg) {
+  int n = 0;
+  if (kind == 1) {
+    const TiledCfg& t = tiled_configs(&n)[cfg];
+    return 16 * t.ntw * t.wn;
+  }
+  const PipeCfg& t = pipe_configs(&n)[cfg];
+  return 16 * t.ntw * t.wn;
+}
+
+// (kind, cfg) from the table, or kind 0 for the skinny kernel.
+RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
+  if (K % 128 != 0) return {0, 0, 0};
+  const RangeEntry* t;
+  int n;
+  if (c.fam == FAM_WNA16) {
+    t = kWna16Table;
+    n = int(sizeof(kWna16Table) / sizeof(kWna16Table[0]));
+  } else if (c.fam == FAM_W8A8) {
+    t = kW8a8Table;
+    n = int(sizeof(kW8a8Table) / sizeof(kW8a8Table[0]));
+  } else {
+    t = kW4a8Table;
+    n = int(sizeof(kW4a8Table) / sizeof(kW4a8Table[0]));
+  }
+  for (int i = 0; i < n; ++i) {
+    if (M > t[i].max_m) continue;
+    if (t[i].kind == 0) return t[i];
+    if (N % tile_n_of(t[i].kind, t[i].cfg) != 0) break;
+    if (t[i].kind == 2 && pipe_lds_bytes(c.fam, t[i].cfg) > 160 * 1024) break;
+    return t[i];
+  }
+  // Fallbacks when the preferred tile does not divide N.
+  const int tc = pick_tiled(c, N, K);
+  if (M > 64 && tc >= 0) return {kInf, 1, tc};
+  return {0, 0, 0};
+}
 
 }  // namespace
 
 Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   Plan pl{};
-  const TuneOverride& tov = tune_override();
-  const int tcfg = pick_tiled(c, N, K);
-  if (tcfg >= 0 && M >= kTiledMinM && tov.cfg < 0) {
-    pl.kind = 1;
-    pl.cfg = tcfg;
+  const TuneOverride tov = tune_override();
+  RangeEntry pick = pick_range(c, M, N, K);
+  // Sweep overrides (HQ_TUNE), honoured only where the shape fits.
+  if (tov.kind == 0) pick = {0, 0, 0};
+  if (tov.kind == 1 && pick_tiled(c, N, K) >= 0) {
+    int n_t = 0;
+    const TiledCfg* tc = tiled_configs(&n_t);
+    const int cfg = (tov.cfg >= 0 && tov.cfg < n_t && N % (16 * tc[tov.cfg].ntw * tc[tov.cfg].wn) == 0)
+                        ? tov.cfg : pick_tiled(c, N, K);
+    pick = {kInf, 1, cfg};
+  }
+  if (tov.kind == 2 && K % 128 == 0) {
+    int n_p = 0;
+    const PipeCfg* pc = pipe_configs(&n_p);
+    if (tov.cfg >= 0 && tov.cfg < n_p && N % (16 * pc[tov.cfg].ntw * pc[tov.cfg].wn) == 0 &&
+        pipe_lds_bytes(c.fam, tov.cfg) <= 160 * 1024)
+      pick = {kInf, 2, tov.cfg};
+  }
+  if (pick.kind != 0) {
+    pl.kind = pick.kind;
+    pl.cfg = pick.cfg;
     pl.split = 1;
     pl.ws_bytes = c.fam == FAM_WNA16 ? size_t(M) * (K / 128) * 4 : 0;  // activation group sums
     return pl;
@@ -108,7 +169,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   pl.cfg = pick_skinny(M, N);
   int n_cfg = 0;
   const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
-  if (tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0) pl.cfg = tov.cfg;
+  if (tov.kind == 0 && tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0) pl.cfg = tov.cfg;
   const SkinnyCfg& sc = cfgs[pl.cfg];
   const int64_t units = K / k_unit(c);
   const int64_t wgs = (N / 16 / sc.ntw) * ((M + 16 * sc.mb - 1) / (16 * sc.mb));
@@ -116,7 +177,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   // Too few workgroups to cover the chip: split K across workgroups as long as every wave
   // keeps at least two units.
   while (wgs * split < kCUs && units / (int64_t(split) * 2 * sc.nw) >= 2) split *= 2;
-  if (tov.split >= 1 && tov.split <= units) split = tov.split;
+  if (tov.kind == 0 && tov.split >= 1 && tov.split <= units) split = tov.split;
   pl.split = split;
   pl.ws_bytes = split > 1 ? size_t(split) * M * N * acc_elem_bytes() : 0;
   return pl;
@@ -127,8 +188,8 @@ Plan plan_moe(const Combo&, int64_t T, int32_t, int32_t, int64_t N, int64_t K, i
   pl.split = 1;
   pl.ws_bytes = 0;
   if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
-    pl.kind = 1;
-    pl.cfg = 3;
+    pl.kind = 2;       // async-pipelined, 64 x 128 tiles: one expert block per tile row
+    pl.cfg = 2;
     pl.ws_bytes = size_t(T) * (K / 128) * 4;  // per-token activation group sums
     return pl;
   }
@@ -164,11 +225,22 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   p.scales_off = L.scales_off;
   p.zeros_off = L.zeros_off;
   const bool moe = call.sorted_ids != nullptr;
-  if (plan.kind == 1) {
+  if (plan.kind == 1 || plan.kind == 2) {
     int n_cfg = 0;
-    const TiledCfg& tc = tiled_configs(&n_cfg)[plan.cfg];
-    const int bm = 16 * tc.mw * tc.wm;
-    const int bn = 16 * tc.ntw * tc.wn;
+    int bm, bn;
+    if (plan.kind == 1) {
+      const TiledCfg& tc = tiled_configs(&n_cfg)[plan.cfg];
+      bm = 16 * tc.mw * tc.wm;
+      bn = 16 * tc.ntw * tc.wn;
+    } else {
+      const PipeCfg& pc = pipe_configs(&n_cfg)[plan.cfg];
+      bm = 16 * pc.mw * pc.wm;
+      bn = 16 * pc.ntw * pc.wn;
+    }
+    auto launch = [&](dim3 grid, int tm, int tn) {
+      return plan.kind == 1 ? launch_tiled(p, c.fam, moe, plan.cfg, grid, tm, tn, call.stream)
+                            : launch_pipe(p, c.fam, moe, plan.cfg, grid, tm, tn, call.stream);
+    };
     p.split = 1;
     p.units_per_split = p.k_units;
     const int tiles_n = int(call.N / bn);
@@ -184,13 +256,11 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
       p.num_padded = call.num_padded;
       p.topk_weights = call.topk_weights;
       p.topk = call.topk;
-      return launch_tiled(p, c.fam, true, plan.cfg, dim3(unsigned(tiles_n), unsigned(call.max_blocks)),
-                          int(call.max_blocks), tiles_n, call.stream);
+      return launch(dim3(unsigned(tiles_n), unsigned(call.max_blocks)), int(call.max_blocks), tiles_n);
     }
     p.M = int(call.M);
     const int tiles_m = int((call.M + bm - 1) / bm);
-    return launch_tiled(p, c.fam, false, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n,
-                        call.stream);
+    return launch(dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n);
   }
   int n_cfg = 0;
   const SkinnyCfg& sc = skinny_configs(&n_cfg)[plan.cfg];

@@ -75,9 +75,9 @@ __device__ __forceinline__ int swz(int row, int chunk, int cpr) {
   return (chunk ^ (row & (cpr - 1)));
 }
 
-template <int FAM, int MW, int NTW, int WM, int WN, bool MOE>
-__global__ __launch_bounds__(64 * WM * WN) void tiled_gemm_kernel(KParams p, int tiles_m,
-                                                                  int tiles_n) {
+template <int FAM, int MW, int NTW, int WM, int WN, int OCC, bool MOE>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void tiled_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
   using Acc = typename AccType<FAM>::type;
   constexpr int kThreads = 64 * WM * WN;
   constexpr int BM = 16 * MW * WM;
@@ -251,8 +251,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_gemm_kernel(KParams p, int
         srow[mb] = r < p.M ? r : -1;
       }
     }
-    for (int gq = 0; gq < G / 4; ++gq) {
-      const int g = 4 * gq + (lane >> 4);
+    for (int gq = 0; gq < (G + 3) / 4; ++gq) {
+      // groups past G (when G is not a multiple of 4) contribute zero
+      const int g_raw = 4 * gq + (lane >> 4);
+      const bool gv = g_raw < G;
+      const int g = gv ? g_raw : G - 1;
       float bneg[NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_gemm_kernel(KParams p, int
           const uint32_t zb = w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)];
           z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
         }
-        bneg[t] = -sc * float(128u + z);
+        bneg[t] = gv ? -sc * float(128u + z) : 0.0f;
       }
 #pragma unroll
       for (int mb = 0; mb < MW; ++mb) {
@@ -317,10 +320,16 @@ hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStr
 }
 
 static constexpr TiledCfg kTiled[] = {
-    {4, 4, 2, 2},  // 0: 128 x 128 tile, 64 x 64 per wave
-    {4, 2, 2, 2},  // 1: 128 x 64 (N/16 even)
-    {4, 1, 2, 2},  // 2: 128 x 32 (any N)
-    {2, 4, 2, 2},  // 3: 64 x 128 (MoE block 64)
+    {4, 4, 2, 2, 1},  // 0: 128 x 128 tile, 64 x 64 per wave
+    {4, 2, 2, 2, 1},  // 1: 128 x 64 (N/16 even)
+    {4, 1, 2, 2, 2},  // 2: 128 x 32 (any N)
+    {2, 4, 2, 2, 2},  // 3: 64 x 128 (MoE block 64)
+    {4, 4, 2, 2, 2},  // 4: as 0, two waves per SIMD
+    {8, 4, 2, 2, 1},  // 5: 256 x 128, 128 x 64 per wave
+    {8, 4, 2, 2, 2},  // 6: as 5, two waves per SIMD
+    {4, 4, 4, 2, 1},  // 7: 256 x 128, 8 waves
+    {2, 4, 2, 2, 1},  // 8: 64 x 128
+    {4, 2, 2, 4, 2},  // 9: 128 x 128, 8 waves of 64 x 32
 };
 
 const TiledCfg* tiled_configs(int* count) {
@@ -335,14 +344,14 @@ static hipError_t launch_tiled_fam(const KParams& p, int cfg, dim3 grid, int til
   case I: {                                                                                         \
     constexpr TiledCfg C = kTiled[I];                                                               \
     constexpr int kSmem = 2 * 16 * C.mw * C.wm * 128 * TiledTraits<FAM>::kABytes;                   \
-    auto kern = tiled_gemm_kernel<FAM, C.mw, C.ntw, C.wm, C.wn, MOE>;                               \
+    auto kern = tiled_gemm_kernel<FAM, C.mw, C.ntw, C.wm, C.wn, C.occ, MOE>;                               \
     if (kSmem > 65536) (void)hipFuncSetAttribute((const void*)kern,                                     \
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);     \
     hipLaunchKernelGGL(kern, grid, dim3(64 * C.wm * C.wn), kSmem, s, p, tiles_m, tiles_n);          \
     break;                                                                                          \
   }
   switch (cfg) {
-    HQ_TL(0) HQ_TL(1) HQ_TL(2) HQ_TL(3)
+    HQ_TL(0) HQ_TL(1) HQ_TL(2) HQ_TL(3) HQ_TL(4) HQ_TL(5) HQ_TL(6) HQ_TL(7) HQ_TL(8) HQ_TL(9)
     default:
       return hipErrorInvalidValue;
   }

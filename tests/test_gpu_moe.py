@@ -101,6 +101,7 @@ def _moe_case(T, topk, E, N, K, bm, with_weights, seed):
     (200, 8, 32, 272, 384, 64, True),     # odd channel tiles
     (512, 8, 16, 256, 512, 64, True),     # 64-row blocks on the LDS-tiled kernel
     (700, 8, 64, 384, 1024, 64, False),   # skewed, ragged expert counts, tiled kernel
+    (300, 8, 16, 256, 640, 64, True),     # K/128 = 5 groups (not a multiple of 4)
 ])
 def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
     inp, experts, y = _moe_case(T, topk, E, N, K, bm, tw, 500 + T)
