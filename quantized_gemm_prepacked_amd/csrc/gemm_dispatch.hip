@@ -188,8 +188,8 @@ Plan plan_moe(const Combo&, int64_t T, int32_t, int32_t, int64_t N, int64_t K, i
   pl.split = 1;
   pl.ws_bytes = 0;
   if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
-    pl.kind = 2;       // async-pipelined, 64 x 128 tiles: one expert block per tile row
-    pl.cfg = 2;
+    pl.kind = 1;       // LDS-tiled, 64 x 128 tiles: one expert block per tile row
+    pl.cfg = 3;
     pl.ws_bytes = size_t(T) * (K / 128) * 4;  // per-token activation group sums
     return pl;
   }
