@@ -9,8 +9,11 @@ M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Othe
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
 caches): every launch reads a different copy of the weights, cycled through more than 3x the
-MI355X's 256 MB Infinity Cache, so weight bytes come from HBM; each launch is bracketed by
-HIP events on the stream it runs on. `value` = total flops of a step / total kernel time.
+MI355X's 256 MB Infinity Cache, so weight bytes come from HBM. Each M point is a HIP graph of R
+back-to-back launches (so small launches are not separated by host gaps), replayed between HIP
+events on the stream it runs on; per-launch time = event time / R. One step replays every M
+point's graph; `value` = (sum over the M points of one launch's flops) / (sum of the per-launch
+times), i.e. the sweep's throughput with each M point counted once.
 """
 from __future__ import annotations
 
@@ -143,32 +146,52 @@ def run_dense(args, wl: str):
         outs[M] = torch.empty((M, N), dtype=torch.int16, device=dev)
         nb = hq.hq_gemm_workspace_bytes(desc, M, N, K)
         wss[M] = (torch.empty(max(nb, 16), dtype=torch.uint8, device=dev), nb)
-    order = sorted(Ms, reverse=True)  # the long launch first keeps the queue ahead of the GPU
     stream = torch.cuda.current_stream()
     ctr = [0]
 
-    def launch(M):
+    def launch(M, strm=None):
         w = weights[ctr[0] % n_copies]
         ctr[0] += 1
         xt, st = dev_acts[M]
         ws, nb = wss[M]
-        hq.hq_gemm(desc, M, N, K, xt, st, w, outs[M], ws, nb, stream)
+        hq.hq_gemm(desc, M, N, K, xt, st, w, outs[M], ws, nb, strm)
 
-    log(f"[bench] warmup {args.warmup} steps ({n_copies} weight copies rotate)")
+    # Launch-bound small calls would be timed with host gaps in between; so each M point is a HIP
+    # graph of R back-to-back launches (consecutive launches read different weight copies), and
+    # the graph replay is bracketed by events on the capturing stream.
+    reps = {M: max(1, min(32, int(2e6 // max(M * N * K // 4096, 1)))) for M in Ms}
+    eager = {}
+    for M in Ms:
+        launch(M, stream)
+        torch.cuda.synchronize()
+        eager[M] = outs[M].clone()
+    graphs = {}
+    for M in Ms:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps[M]):
+                launch(M)           # current stream = the capture stream
+        graphs[M] = g
+    for M in Ms:                     # a replay must reproduce the eager result bit for bit
+        graphs[M].replay()
+        torch.cuda.synchronize()
+        if not torch.equal(outs[M], eager[M]):
+            raise RuntimeError(f"graph replay differs from the eager result at M={M}")
+    log(f"[bench] warmup {args.warmup} steps ({n_copies} weight copies rotate; launches per graph {reps})")
     for _ in range(args.warmup):
-        for M in order:
-            launch(M)
+        for M in Ms:
+            graphs[M].replay()
     torch.cuda.synchronize()
     evs = {M: [] for M in Ms}
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for M in order:
+        for M in Ms:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            launch(M)
+            graphs[M].replay()
             b.record(stream)
             evs[M].append((a, b))
     torch.cuda.synchronize()
@@ -177,14 +200,14 @@ def run_dense(args, wl: str):
     tot_flops = 0.0
     tot_s = 0.0
     for M in Ms:
-        us = float(np.mean([a.elapsed_time(b) for a, b in evs[M]])) * 1e3
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs[M]])) * 1e3 / reps[M]
         fl = 2.0 * M * N * K
         by = alg_bytes(wl, M, N, K)
         tf = fl / (us * 1e-6) / 1e12
         gbs = by / (us * 1e-6) / 1e9
         peak = PEAK_TFLOPS[spec["peak"]]
         frac_c, frac_m = tf / peak, gbs / HBM_PEAK_GBS
-        sweep.append({"M": M, "us": round(us, 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
+        sweep.append({"M": M, "launches_per_graph": reps[M], "us": round(us, 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
                       "bound": "hbm" if frac_m >= frac_c else "mfma",
                       "frac": round(max(frac_c, frac_m), 4), "bytes": by, "flops": fl})
         tot_flops += fl
@@ -268,32 +291,50 @@ def run_moe(args):
     stream = torch.cuda.current_stream()
     ctr = [0]
 
-    def launch(T, evs=None):
+    def align(T):
+        s = state[T]
+        hq.hq_moe_align(s["ids"], T, topk, E, s["bm"], s["sorted"], s["bexp"], s["offs"], s["npad"],
+                        None, 0, None)
+
+    def gemm(T):
         s = state[T]
         w = weights[ctr[0] % n_copies]
         ctr[0] += 1
-        if evs is not None:
-            evs[0].record(stream)
-        hq.hq_moe_align(s["ids"], T, topk, E, s["bm"], s["sorted"], s["bexp"], s["offs"], s["npad"],
-                        None, 0, stream)
-        if evs is not None:
-            evs[1].record(stream)
         hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, s["x"], None, w, s["sorted"], s["bexp"],
-                               s["npad"], s["bm"], None, s["y"], s["ws"], s["wsb"], stream)
-        if evs is not None:
-            evs[2].record(stream)
+                               s["npad"], s["bm"], None, s["y"], s["ws"], s["wsb"], None)
 
-    order = sorted(Ts, reverse=True)
+    # One HIP graph of R back-to-back launches per (T, stage); the sort's outputs persist, so R
+    # sorts then R grouped GEMMs over rotating weight copies time each stage without host gaps.
+    reps = {T: max(1, min(16, int(4e5 // max(T, 1)))) for T in Ts}
+    for T in Ts:
+        align(T)
+        gemm(T)
+    torch.cuda.synchronize()
+    ga, gg = {}, {}
+    for T in Ts:
+        ga[T] = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ga[T]):
+            for _ in range(reps[T]):
+                align(T)
+        gg[T] = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gg[T]):
+            for _ in range(reps[T]):
+                gemm(T)
     for _ in range(args.warmup):
-        for T in order:
-            launch(T)
+        for T in Ts:
+            ga[T].replay()
+            gg[T].replay()
     torch.cuda.synchronize()
     rec = {T: [] for T in Ts}
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for T in order:
+        for T in Ts:
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            launch(T, evs)
+            evs[0].record(stream)
+            ga[T].replay()
+            evs[1].record(stream)
+            gg[T].replay()
+            evs[2].record(stream)
             rec[T].append(evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -301,21 +342,21 @@ def run_moe(args):
     tot_t = 0.0
     tot_tok = 0
     for T in Ts:
-        ta = float(np.mean([e[0].elapsed_time(e[1]) for e in rec[T]])) * 1e3
-        tg = float(np.mean([e[1].elapsed_time(e[2]) for e in rec[T]])) * 1e3
+        ta = float(np.mean([e[0].elapsed_time(e[1]) for e in rec[T]])) * 1e3 / reps[T]
+        tg = float(np.mean([e[1].elapsed_time(e[2]) for e in rec[T]])) * 1e3 / reps[T]
         s = state[T]
         fl = 2.0 * T * topk * N * K
         by = s["active"] * stride + T * K * 2 + T * topk * N * 2
         tf = fl / (tg * 1e-6) / 1e12
         gbs = by / (tg * 1e-6) / 1e9
         fc, fm = tf / PEAK_TFLOPS["bf16"], gbs / HBM_PEAK_GBS
-        sweep.append({"T": T, "block_m": s["bm"], "active_experts": s["active"], "top_expert_rows": s["top"],
+        sweep.append({"T": T, "launches_per_graph": reps[T], "block_m": s["bm"], "active_experts": s["active"], "top_expert_rows": s["top"],
                       "align_us": round(ta, 3), "gemm_us": round(tg, 3),
                       "tokens_per_s": round(T / ((ta + tg) * 1e-6), 1), "tflops": round(tf, 3),
                       "gbps": round(gbs, 1), "bound": "hbm" if fm >= fc else "mfma",
                       "frac": round(max(fc, fm), 4)})
-        tot_t += (ta + tg) * 1e-6
-        tot_tok += T
+        tot_t += (ta + tg) * 1e-6 * reps[T]
+        tot_tok += T * reps[T]
     dom = max(sweep, key=lambda r: r["gemm_us"])
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",

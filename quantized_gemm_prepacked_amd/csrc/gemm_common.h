@@ -85,9 +85,10 @@ __device__ __forceinline__ void store_result(const KParams& p, int row, int n,
 }
 
 // A skinny-kernel instantiation: MB row blocks of 16, NTW channel tiles of 16, NW waves that
-// split K, UNR units in flight per wave.
+// split K, UNR units per batch; pp = 1 double-buffers batches (next batch in flight while the
+// current one is computed).
 struct SkinnyCfg {
-  int mb, ntw, nw, unr;
+  int mb, ntw, nw, unr, pp;
 };
 const SkinnyCfg* skinny_configs(int* count);
 

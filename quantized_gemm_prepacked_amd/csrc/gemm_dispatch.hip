@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <cstdio>
 #include <cstdlib>
 
@@ -22,12 +23,27 @@ constexpr int kCUs = 256;
 
 int k_unit(const Combo& c) { return family_k_unit(c.fam); }
 
-// Pick the skinny configuration for a row block of `rows` rows and N channels.
-int pick_skinny(int64_t rows, int64_t N) {
+// Pick the skinny configuration for a row block of `rows` rows and N channels (measured on
+// MI355X at the benchmark shapes; the first candidate whose channel-tile count divides N/16).
+int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   const int64_t nt = N / 16;
-  if (rows <= 16) return nt % 4 == 0 ? 0 : (nt % 2 == 0 ? 1 : 2);
-  if (rows <= 32) return nt % 4 == 0 ? 3 : (nt % 2 == 0 ? 7 : 8);
-  return nt % 4 == 0 ? 4 : (nt % 2 == 0 ? 5 : 6);
+  int n_cfg = 0;
+  const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
+  auto first_fit = [&](std::initializer_list<int> cands) {
+    for (int i : cands)
+      if (nt % cfgs[i].ntw == 0) return i;
+    return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
+  };
+  if (rows <= 16) {
+    if (c.fam == FAM_W8A8) return first_fit({10, 2});
+    if (c.fam == FAM_W4A8) return first_fit({11, 2});
+    return first_fit({0, 1, 2});
+  }
+  if (rows <= 32) {
+    if (c.fam == FAM_W4A8) return first_fit({16, 8});
+    return first_fit({3, 7, 8});
+  }
+  return first_fit({4, 5, 6});
 }
 
 size_t acc_elem_bytes() { return 4; }
@@ -95,7 +111,7 @@ struct RangeEntry {
 };
 constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {192, 2, 2}, {384, 1, 9}, {kInf, 2, 7}};
-constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {512, 2, 3}, {1536, 2, 10}, {kInf, 2, 8}};
+constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {512, 2, 3}, {1536, 2, 10}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{256, 0, 0}, {768, 2, 3}, {1536, 2, 2}, {kInf, 2, 11}};
 
 int tile_n_of(int kind, int cfg) {
@@ -166,7 +182,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
     return pl;
   }
   pl.kind = 0;
-  pl.cfg = pick_skinny(M, N);
+  pl.cfg = pick_skinny(c, M, N);
   int n_cfg = 0;
   const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
   if (tov.kind == 0 && tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0) pl.cfg = tov.cfg;
@@ -174,16 +190,17 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   const int64_t units = K / k_unit(c);
   const int64_t wgs = (N / 16 / sc.ntw) * ((M + 16 * sc.mb - 1) / (16 * sc.mb));
   int split = 1;
-  // Too few workgroups to cover the chip: split K across workgroups as long as every wave
-  // keeps at least two units.
-  while (wgs * split < kCUs && units / (int64_t(split) * 2 * sc.nw) >= 2) split *= 2;
+  // Far too few workgroups to cover the chip: split K across workgroups (partials + a reduction
+  // launch) as long as every wave keeps at least two units. Measured: with a few hundred
+  // workgroups the extra launch costs more than the idle CUs.
+  while (wgs * split < kCUs / 2 && units / (int64_t(split) * 2 * sc.nw) >= 2) split *= 2;
   if (tov.kind == 0 && tov.split >= 1 && tov.split <= units) split = tov.split;
   pl.split = split;
   pl.ws_bytes = split > 1 ? size_t(split) * M * N * acc_elem_bytes() : 0;
   return pl;
 }
 
-Plan plan_moe(const Combo&, int64_t T, int32_t, int32_t, int64_t N, int64_t K, int32_t block_m) {
+Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K, int32_t block_m) {
   Plan pl{};
   pl.split = 1;
   pl.ws_bytes = 0;
@@ -194,7 +211,7 @@ Plan plan_moe(const Combo&, int64_t T, int32_t, int32_t, int64_t N, int64_t K, i
     return pl;
   }
   pl.kind = 0;
-  pl.cfg = pick_skinny(block_m, N);
+  pl.cfg = block_m <= 16 ? pick_skinny(c, 16, N) : pick_skinny(c, block_m, N);
   return pl;
 }
 

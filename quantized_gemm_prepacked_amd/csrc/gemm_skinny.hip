@@ -142,7 +142,7 @@ struct SkinnyFrag<FAM_W4A8, MB, NTW> {
   }
 };
 
-template <int FAM, int MB, int NTW, int NW, int UNR, bool MOE>
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE>
 __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   using Acc = typename AccType<FAM>::type;
   using Elem = typename AccType<FAM>::elem;
@@ -177,19 +177,42 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[mb][t] = Acc{0, 0, 0, 0};
 
+  // This wave's units are u0, u0 + NW, ... < uend, taken in batches of UNR. Two register
+  // buffers alternate so that batch b+1 is in flight while batch b is dequantized and
+  // multiplied (written as an explicit ping-pong: no register copies between the buffers).
   const int ubeg = blockIdx.z * p.units_per_split;
   const int uend = min(p.k_units, ubeg + p.units_per_split);
-  int u = ubeg + wave;
-  for (; u + (UNR - 1) * NW < uend; u += UNR * NW) {
-    SkinnyFrag<FAM, MB, NTW> f[UNR];
+  const int u0 = ubeg + wave;
+  const int nunits = u0 < uend ? (uend - u0 + NW - 1) / NW : 0;
+  const int nbatch = nunits / UNR;
+  using Frag = SkinnyFrag<FAM, MB, NTW>;
+  Frag fa[UNR];
+  [[maybe_unused]] Frag fb[PP ? UNR : 1];
+  auto load_batch = [&](Frag* f, int b) {
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) f[r].load(p, w, nt0, u + r * NW, lane, arow);
+    for (int r = 0; r < UNR; ++r) f[r].load(p, w, nt0, u0 + (b * UNR + r) * NW, lane, arow);
+  };
+  auto compute_batch = [&](const Frag* f) {
 #pragma unroll
     for (int r = 0; r < UNR; ++r) f[r].compute(p, lane, acc);
+  };
+  if constexpr (PP) {
+    if (nbatch > 0) load_batch(fa, 0);
+    for (int b = 0; b < nbatch; b += 2) {
+      if (b + 1 < nbatch) load_batch(fb, b + 1);
+      compute_batch(fa);
+      if (b + 2 < nbatch) load_batch(fa, b + 2);
+      if (b + 1 < nbatch) compute_batch(fb);
+    }
+  } else {
+    for (int b = 0; b < nbatch; ++b) {
+      load_batch(fa, b);
+      compute_batch(fa);
+    }
   }
-  for (; u < uend; u += NW) {
-    SkinnyFrag<FAM, MB, NTW> f;
-    f.load(p, w, nt0, u, lane, arow);
+  for (int i = nbatch * UNR; i < nunits; ++i) {
+    Frag f;
+    f.load(p, w, nt0, u0 + i * NW, lane, arow);
     f.compute(p, lane, acc);
   }
 
@@ -223,15 +246,31 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 
 // Index = plan.cfg. Keep in sync with skinny_configs() below.
 static constexpr SkinnyCfg kSkinny[] = {
-    {1, 4, 8, 2},  // 0: M <= 16, wide N
-    {1, 2, 8, 2},  // 1: M <= 16, N/16 not a multiple of 4
-    {1, 1, 8, 2},  // 2: M <= 16, odd channel tiles
-    {2, 4, 4, 2},  // 3: M <= 32
-    {4, 4, 4, 1},  // 4: M <= 64
-    {4, 2, 4, 1},  // 5: M <= 64, N/16 even only
-    {4, 1, 4, 1},  // 6: M <= 64, any N
-    {2, 2, 4, 2},  // 7: M <= 32, N/16 even only
-    {2, 1, 4, 2},  // 8: M <= 32, any N
+    // mb ntw nw unr pp
+    {1, 4, 8, 2, 0},   // 0: M <= 16, wide N
+    {1, 2, 8, 2, 0},   // 1: M <= 16, N/16 not a multiple of 4
+    {1, 1, 8, 2, 0},   // 2: M <= 16, odd channel tiles
+    {2, 4, 4, 2, 0},   // 3: M <= 32
+    {4, 4, 4, 1, 0},   // 4: M <= 64
+    {4, 2, 4, 1, 0},   // 5: M <= 64, N/16 even only
+    {4, 1, 4, 1, 0},   // 6: M <= 64, any N
+    {2, 2, 4, 2, 0},   // 7: M <= 32, N/16 even only
+    {2, 1, 4, 2, 0},   // 8: M <= 32, any N
+    {1, 2, 8, 4, 0},   // 9: M <= 16, 4 units in flight per wave
+    {1, 1, 8, 4, 0},   // 10
+    {1, 1, 16, 2, 0},  // 11
+    {1, 2, 16, 2, 0},  // 12
+    {1, 4, 8, 1, 1},   // 13: ping-pong, one unit per buffer
+    {1, 1, 4, 4, 0},   // 14
+    {2, 2, 8, 2, 0},   // 15: M <= 32
+    {2, 1, 8, 4, 0},   // 16
+    {1, 4, 8, 2, 1},   // 17: ping-pong
+    {1, 2, 8, 2, 1},   // 18
+    {1, 1, 8, 2, 1},   // 19
+    {1, 2, 16, 1, 1},  // 20
+    {1, 1, 16, 1, 1},  // 21
+    {2, 4, 4, 1, 1},   // 22: M <= 32, ping-pong
+    {2, 2, 8, 1, 1},   // 23
 };
 
 const SkinnyCfg* skinny_configs(int* count) {
@@ -244,11 +283,13 @@ static hipError_t launch_skinny_fam(const KParams& p, int cfg, dim3 grid, hipStr
 #define HQ_SK(I)                                                                           \
   case I:                                                                                  \
     hipLaunchKernelGGL((skinny_gemm_kernel<FAM, kSkinny[I].mb, kSkinny[I].ntw, kSkinny[I].nw, \
-                                           kSkinny[I].unr, MOE>),                          \
+                                           kSkinny[I].unr, kSkinny[I].pp != 0, MOE>),      \
                        grid, dim3(kSkinny[I].nw * 64), 0, s, p);                           \
     break;
   switch (cfg) {
-    HQ_SK(0) HQ_SK(1) HQ_SK(2) HQ_SK(3) HQ_SK(4) HQ_SK(5) HQ_SK(6) HQ_SK(7) HQ_SK(8)
+    HQ_SK(0) HQ_SK(1) HQ_SK(2) HQ_SK(3) HQ_SK(4) HQ_SK(5) HQ_SK(6) HQ_SK(7) HQ_SK(8) HQ_SK(9)
+    HQ_SK(10) HQ_SK(11) HQ_SK(12) HQ_SK(13) HQ_SK(14) HQ_SK(15) HQ_SK(16) HQ_SK(17) HQ_SK(18)
+    HQ_SK(19) HQ_SK(20) HQ_SK(21) HQ_SK(22) HQ_SK(23)
     default:
       return hipErrorInvalidValue;
   }
