@@ -65,8 +65,13 @@ __device__ __forceinline__ bf16x8 dequant_int4x8(uint32_t v, float z) {
 // Cheaper form for kernels that remove the offset separately: returns (128 + u) for the 8 codes,
 // exact in bf16 (0x4300 is 128.0 and its last mantissa bit weighs 1, so OR-ing a 4-bit u into the
 // low bits adds u). One bit-select per pair of weights.
+// Each output dword is (v >> 4j) & 0x000F000F | 0x43004300. gfx9 VOP3 encodings take no literal
+// operand, so with both constants as literals the compiler emits v_and + v_or; holding them in
+// registers (empty asm statements make them opaque) lets it select one v_and_or_b32 per dword.
 __device__ __forceinline__ bf16x8 dequant_int4x8_offset128(uint32_t v) {
-  const uint32_t m = 0x000F000Fu, c = 0x43004300u;
+  uint32_t m = 0x000F000Fu, c = 0x43004300u;
+  asm("" : "+s"(m));
+  asm("" : "+v"(c));
   const uint32_t p0 = (v & m) | c;
   const uint32_t p1 = ((v >> 4) & m) | c;
   const uint32_t p2 = ((v >> 8) & m) | c;
@@ -113,5 +118,37 @@ __device__ __forceinline__ f32x4 mfma_fp8_fp4(u32x4 a_lo, u32x4 a_hi, u32x4 b, i
   i32x8 bv = {int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, 127, 0, b_scale);
 }
+
+// Position of 16-byte chunk `chunk` of activation row `row` in an LDS tile with `cpr` chunks per
+// row (an XOR swizzle, so each row's chunks stay a permutation of its own slots). For 128-byte
+// rows the key is the row's low three bits. For 256-byte rows the plain key (row & 15) leaves the
+// chunks that one ds_read_b128 fetches for lane groups 0 and 1 (chunks d and 4 + d) in the same
+// bank group, which measures as a two-way conflict on gfx950; rotating the four key bits left by
+// one measures conflict-free.
+__device__ __forceinline__ int lds_chunk_swizzle(int row, int chunk, int cpr) {
+  const int key = cpr == 16 ? (((row & 7) << 1) | ((row >> 3) & 1)) : (row & (cpr - 1));
+  return chunk ^ key;
+}
+
+// ---- direct-to-LDS copies and wait counters ---------------------------------------------------
+// One global -> LDS copy per lane: lane i's `bytes` (4 or 16) land at lds + bytes * i, where lds
+// must be wave-uniform. The copy counts in the wave's vmcnt like any vector load, once per
+// instruction whatever the lane mask.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters unconstrained (gfx9 encoding; n < 64).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads (and scalar loads) have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 }  // namespace hq

@@ -110,6 +110,20 @@ int pipe_lds_bytes(int fam, int cfg);
 hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
                        int tiles_n, hipStream_t s);
 
+// A ping-pong-kernel instantiation: eight waves (WM x WN) of (16*MW) x (16*NTW), three K steps
+// in flight; the workgroup tile is (16*MW*WM) x (16*NTW*WN).
+struct PPCfg {
+  int mw, ntw, wm, wn;
+};
+const PPCfg* pp_configs(int* count);
+int pp_lds_bytes(int fam, int cfg);
+hipError_t launch_pingpong(const KParams& p, int fam, int cfg, dim3 grid, int tiles_m, int tiles_n,
+                           hipStream_t s);
+// WNA16 group sums for the ping-pong kernel: per row, Gp = ceil(K/128 / 32) * 32 bf16 high
+// halves then Gp low halves.
+size_t group_sums_split_bytes(int64_t rows, int64_t K);
+hipError_t launch_group_sums_split(const uint8_t* a, int rows, int K, void* ws, hipStream_t s);
+
 hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStream_t s);
 
 hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid, hipStream_t s);

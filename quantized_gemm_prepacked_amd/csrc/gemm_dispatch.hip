@@ -48,8 +48,8 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
 
 size_t acc_elem_bytes() { return 4; }
 
-// Sweep override for tuning runs: HQ_TUNE="kind=<0|1>,cfg=<i>,split=<s>" forces the kernel
-// family (0 skinny, 1 tiled), its configuration and (skinny) the K split for every dense call;
+// Sweep override for tuning runs: HQ_TUNE="kind=<k>,cfg=<i>,split=<s>" forces the kernel
+// family (0 skinny, 1 LDS-tiled, 2 async-pipelined, 3 ping-pong), its configuration and (skinny) the K split for every dense call;
 // entries that do not fit the shape are ignored. Read on every call so one process can sweep.
 struct TuneOverride {
   int kind = -1, cfg = -1, split = -1;
@@ -120,6 +120,10 @@ int tile_n_of(int kind, int cfg) {
     const TiledCfg& t = tiled_configs(&n)[cfg];
     return 16 * t.ntw * t.wn;
   }
+  if (kind == 3) {
+    const PPCfg& t = pp_configs(&n)[cfg];
+    return 16 * t.ntw * t.wn;
+  }
   const PipeCfg& t = pipe_configs(&n)[cfg];
   return 16 * t.ntw * t.wn;
 }
@@ -144,6 +148,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
     if (t[i].kind == 0) return t[i];
     if (N % tile_n_of(t[i].kind, t[i].cfg) != 0) break;
     if (t[i].kind == 2 && pipe_lds_bytes(c.fam, t[i].cfg) > 160 * 1024) break;
+    if (t[i].kind == 3 && (K % 128 != 0 || pp_lds_bytes(c.fam, t[i].cfg) > 160 * 1024)) break;
     return t[i];
   }
   // Fallbacks when the preferred tile does not divide N.
@@ -174,11 +179,27 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
         pipe_lds_bytes(c.fam, tov.cfg) <= 160 * 1024)
       pick = {kInf, 2, tov.cfg};
   }
+  if (tov.kind == 3 && K % 128 == 0) {
+    int n_p = 0;
+    const PPCfg* pc = pp_configs(&n_p);
+    if (tov.cfg >= 0 && tov.cfg < n_p && N % (16 * pc[tov.cfg].ntw * pc[tov.cfg].wn) == 0 &&
+        pp_lds_bytes(c.fam, tov.cfg) <= 160 * 1024)
+      pick = {kInf, 3, tov.cfg};
+  }
+  // The direct-to-LDS kernels address activations with 32-bit offsets.
+  if ((pick.kind == 2 || pick.kind == 3) &&
+      uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) >= (uint64_t(1) << 32)) {
+    const int tc = pick_tiled(c, N, K);
+    pick = tc >= 0 ? RangeEntry{kInf, 1, tc} : RangeEntry{0, 0, 0};
+  }
   if (pick.kind != 0) {
     pl.kind = pick.kind;
     pl.cfg = pick.cfg;
     pl.split = 1;
-    pl.ws_bytes = c.fam == FAM_WNA16 ? size_t(M) * (K / 128) * 4 : 0;  // activation group sums
+    // activation group sums (fp32 [G][M], or split bf16 [M][2][Gp] for the ping-pong kernel)
+    pl.ws_bytes = c.fam != FAM_WNA16 ? 0
+                  : pick.kind == 3   ? group_sums_split_bytes(M, K)
+                                     : size_t(M) * (K / 128) * 4;
     return pl;
   }
   pl.kind = 0;
@@ -242,6 +263,22 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   p.scales_off = L.scales_off;
   p.zeros_off = L.zeros_off;
   const bool moe = call.sorted_ids != nullptr;
+  if (plan.kind == 3 && !moe) {
+    int n_cfg = 0;
+    const PPCfg& pc = pp_configs(&n_cfg)[plan.cfg];
+    const int bm = 16 * pc.mw * pc.wm, bn = 16 * pc.ntw * pc.wn;
+    p.split = 1;
+    p.units_per_split = p.k_units;
+    p.M = int(call.M);
+    p.s_rows = int(call.M);
+    if (c.fam == FAM_WNA16) {
+      hipError_t e = launch_group_sums_split(p.a, p.M, p.K, call.ws, call.stream);
+      if (e != hipSuccess) return e;
+    }
+    const int tiles_n = int(call.N / bn);
+    const int tiles_m = int((call.M + bm - 1) / bm);
+    return launch_pingpong(p, c.fam, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n, call.stream);
+  }
   if (plan.kind == 1 || plan.kind == 2) {
     int n_cfg = 0;
     int bm, bn;

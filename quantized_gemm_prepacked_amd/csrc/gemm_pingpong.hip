@@ -1,0 +1,461 @@
+// gemm_pingpong.hip -- the large-M fused-dequantization GEMM with eight waves in two ping-pong
+// groups.
+//
+// Same computation as gemm_pipe.hip (the Humming announcement's larger-batch pipeline, section
+// "Tuning and JIT compilation per workload"), scheduled so the matrix cores never wait for the
+// memory work of their own SIMD:
+//   - the workgroup's eight waves form two groups of four, one wave of each group per SIMD;
+//   - every K step (128 k) a wave runs a memory phase (issue the direct-to-LDS copies of a step
+//     two ahead, read its operand fragments of this step from LDS into registers) and then a
+//     compute phase (dequantization, MFMAs and the group scaling, registers only);
+//   - group 1 runs one phase behind group 0, and a workgroup barrier separates the phases, so
+//     on each SIMD one wave computes while the other loads;
+//   - three LDS slots hold steps s (being read), s + 1 (landed or landing) and s + 2 (in
+//     flight); a wave waits only for its own copies of step s + 1 before the barrier that ends
+//     its memory phase of step s, so a copy has about three phases to land.
+// WNA16 keeps the offset-128 operand of the other kernels. The offset term
+//   -sum_g s[n,g] * (128 + z[n,g]) * S[m,g]   (S: group sums of the activation row)
+// is one more contraction over the K/128 groups, run at the end on the bf16 MFMA with both
+// operands split into bf16 high and low halves (hi*hi + hi*lo + lo*hi, about 16 significant
+// bits each) instead of the fp32 MFMA, which takes four times as many instructions.
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "device_ops.h"
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace hq {
+
+namespace {
+
+template <int FAM>
+struct PPTraits;
+template <>
+struct PPTraits<FAM_WNA16> {
+  static constexpr int kABytes = 2;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 32;   // 16 bf16 group scales
+};
+template <>
+struct PPTraits<FAM_W8A8> {
+  static constexpr int kABytes = 1;
+  static constexpr int kUnitsPerStep = 2;
+  static constexpr int kMetaPerTile = 0;
+};
+template <>
+struct PPTraits<FAM_W4A8> {
+  static constexpr int kABytes = 1;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 64;   // one e8m0 byte per lane
+};
+
+// Workgroup barrier that the instruction scheduler may not move work across: the phases around
+// it must stay where they are for the two groups to alternate.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FAM, int MW, int NTW, int WM, int WN>
+struct PPShape {
+  static_assert(WM * WN == 8, "eight waves");
+  static constexpr int kStages = 3;
+  static constexpr int BM = 16 * MW * WM;
+  static constexpr int BN = 16 * NTW * WN;
+  static constexpr int AB = PPTraits<FAM>::kABytes;
+  static constexpr int RB = 128 * AB;                 // activation bytes per row per step
+  static constexpr int CPR = RB / 16;
+  static constexpr int A_BYTES = BM * RB;
+  static constexpr int NT = BN / 16;
+  static constexpr int UPS = PPTraits<FAM>::kUnitsPerStep;
+  static constexpr int B_BYTES = NT * UPS * kUnitBytes;
+  static constexpr int MPT = PPTraits<FAM>::kMetaPerTile;
+  static constexpr int META_BYTES = NT * MPT;
+  static constexpr int META_PER_WAVE = META_BYTES / 8;
+  static constexpr int META_LANES = META_PER_WAVE / 16;
+  static constexpr int STAGE = (A_BYTES + B_BYTES + META_BYTES + 1023) / 1024 * 1024;
+  static constexpr int LDS = kStages * STAGE;
+  static constexpr int A_INSTR = A_BYTES / 1024 / 8;
+  static constexpr int B_INSTR = NT * UPS / 8;
+  static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0);
+  static_assert(A_BYTES % (1024 * 8) == 0, "activation tile must split into wave loads");
+  static_assert((NT * UPS) % 8 == 0, "weight units must split over the waves");
+  static_assert(META_BYTES % (16 * 8) == 0 && META_LANES <= 64, "metadata split over the waves");
+};
+
+template <int FAM, int MW, int NTW, int WM, int WN>
+__global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
+  using Sh = PPShape<FAM, MW, NTW, WM, WN>;
+  using Acc = typename AccType<FAM>::type;
+  constexpr int BM = Sh::BM, RB = Sh::RB, CPR = Sh::CPR, NT = Sh::NT, UPS = Sh::UPS;
+  constexpr int S = Sh::kStages;
+  extern __shared__ __align__(1024) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int group = wave >> 2;   // waves w and w + 4 share a SIMD
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // XCD-aware tile order (blocks are dealt to the eight XCDs round robin), then groups of eight
+  // M tiles per N tile so that concurrently running workgroups share operands in L2.
+  const int nwg = gridDim.x;
+  const int pid = blockIdx.x;
+  const int lid = (nwg % 8 == 0) ? (pid % 8) * (nwg / 8) + pid / 8 : pid;
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int first_m = (lid / per_group) * GM;
+  const int gm = min(GM, tiles_m - first_m);
+  const int in_group = lid % per_group;
+  const int mt = first_m + in_group % gm;
+  const int ntile = in_group / gm;
+  const int row0 = mt * BM;
+  const int nt_wg = ntile * NT;
+  const int nt0 = nt_wg + wn * NTW;
+  const uint8_t* w = p.w;
+
+  // ---- per-lane sources of the stage copies (constant over K) ----
+  uint32_t a_off[Sh::A_INSTR];
+#pragma unroll
+  for (int j = 0; j < Sh::A_INSTR; ++j) {
+    const int q = (wave * Sh::A_INSTR + j) * 64 + lane;
+    const int r = q / CPR;
+    const int c = lds_chunk_swizzle(r, q % CPR, CPR);
+    const int src_row = min(row0 + r, p.M - 1);   // rows past M are computed, never stored
+    a_off[j] = uint32_t(src_row) * uint32_t(p.K * Sh::AB) + uint32_t(c * 16);
+  }
+  // metadata: this wave copies bytes [wave * META_PER_WAVE, +META_PER_WAVE) of the stage's
+  // [tile][MPT] block, 16 per lane
+  int meta_tile = 0, meta_byte = 0;
+  if constexpr (Sh::META_BYTES > 0) {
+    const int b = wave * Sh::META_PER_WAVE + 16 * min(lane, Sh::META_LANES - 1);
+    meta_tile = b / Sh::MPT;
+    meta_byte = b % Sh::MPT;
+  }
+
+  auto issue_stage = [&](int ks) {
+    uint8_t* st = smem + (ks % S) * Sh::STAGE;
+#pragma unroll
+    for (int j = 0; j < Sh::A_INSTR; ++j)
+      lds_dma16(p.a + a_off[j] + size_t(ks) * RB, st + (wave * Sh::A_INSTR + j) * 1024);
+    uint8_t* sb = st + Sh::A_BYTES;
+#pragma unroll
+    for (int j = 0; j < Sh::B_INSTR; ++j) {
+      const int u = wave * Sh::B_INSTR + j;
+      const size_t unit = size_t(nt_wg + u / UPS) * p.k_units + size_t(ks) * UPS + (u % UPS);
+      lds_dma16(w + unit * kUnitBytes + 16 * lane, sb + u * 1024);
+    }
+    if constexpr (Sh::META_BYTES > 0) {
+      // lanes past META_LANES skip the copy (a direct-to-LDS load writes lane i at base + 16 i);
+      // the instruction still counts once in this wave's vmcnt
+      const size_t unit = size_t(nt_wg + meta_tile) * p.k_units + ks;
+      if (lane < Sh::META_LANES)
+        lds_dma16(w + p.scales_off + unit * Sh::MPT + meta_byte, sb + Sh::B_BYTES + wave * Sh::META_PER_WAVE);
+    }
+  };
+
+  auto read_a = [&](const uint8_t* st, int mb, int chunk) -> u32x4 {
+    const int r = wm * 16 * MW + 16 * mb + (lane & 15);
+    return *reinterpret_cast<const u32x4*>(st + r * RB + lds_chunk_swizzle(r, chunk, CPR) * 16);
+  };
+  auto read_b = [&](const uint8_t* st, int t, int q) -> u32x4 {
+    const int u = (wn * NTW + t) * UPS + q;
+    return *reinterpret_cast<const u32x4*>(st + Sh::A_BYTES + u * 1024 + 16 * lane);
+  };
+
+  Acc acc[MW][NTW];
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) acc[mb][t] = Acc{0, 0, 0, 0};
+
+  // Operand fragments of one step, filled by the memory phase and used by the compute phase.
+  constexpr int NA = FAM == FAM_WNA16 ? 4 : 2;   // activation fragments per row block
+  constexpr int NB = FAM == FAM_W8A8 ? 2 : 1;    // packed weight fragments per channel tile
+  u32x4 af[MW][NA];
+  u32x4 bq[NTW][NB];
+  uint32_t meta[NTW];
+
+  auto memory_phase = [&](int ks) {
+    const uint8_t* st = smem + (ks % S) * Sh::STAGE;
+    const uint8_t* sm = st + Sh::A_BYTES + Sh::B_BYTES;
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+      for (int d = 0; d < NA; ++d) {
+        // WNA16: lane group g holds k 32g..32g+31 of the step (chunks 4g..4g+3); 8-bit
+        // activations: MFMA d takes chunk 4d + g (W8A8: k 64d + 16g..; W4A8: the two halves)
+        const int chunk = FAM == FAM_WNA16 ? 4 * (lane >> 4) + d : 4 * d + (lane >> 4);
+        af[mb][d] = read_a(st, mb, chunk);
+      }
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+#pragma unroll
+      for (int q = 0; q < NB; ++q) bq[t][q] = read_b(st, t, q);
+      const int tw = wn * NTW + t;
+      if constexpr (FAM == FAM_WNA16)
+        meta[t] = *reinterpret_cast<const uint16_t*>(sm + tw * 32 + 2 * (lane & 15));
+      else if constexpr (FAM == FAM_W4A8)
+        meta[t] = sm[tw * 64 + lane];
+    }
+  };
+
+  auto compute_phase = [&]() {
+    if constexpr (FAM == FAM_WNA16) {
+      // Software-pipelined over the channel tiles: while the MFMAs of tile t run, the VALU
+      // dequantizes tile t + 1 and applies the group scale to tile t - 1's partial sums.
+      bf16x8 bw[2][4];
+      f32x4 part[2][MW];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) bw[0][d] = dequant_int4x8_offset128(bq[0][0][d]);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int cur = t & 1;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb)
+            part[cur][mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bw[cur][d],
+                                      d == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : part[cur][mb]);
+        if (t + 1 < NTW) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) bw[cur ^ 1][d] = dequant_int4x8_offset128(bq[t + 1][0][d]);
+        }
+        if (t > 0) {
+          const float s = __uint_as_float(meta[t - 1] << 16);
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb) acc[mb][t - 1] += part[cur ^ 1][mb] * s;
+        }
+      }
+      {
+        const float s = __uint_as_float(meta[NTW - 1] << 16);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) acc[mb][NTW - 1] += part[(NTW - 1) & 1][mb] * s;
+      }
+      // issue order: one MFMA, then up to three VALU instructions
+#pragma unroll
+      for (int i = 0; i < 4 * MW * NTW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    } else if constexpr (FAM == FAM_W8A8) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_i8(af[mb][q], bq[t][q], acc[mb][t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb)
+          acc[mb][t] = mfma_fp8_fp4(af[mb][0], af[mb][1], bq[t][0], int(meta[t]), acc[mb][t]);
+    }
+  };
+
+  const int nks = p.K / 128;
+  issue_stage(0);
+  if (nks > 1) issue_stage(1);
+  if (nks > 1) wait_vmcnt<Sh::INSTR>();
+  else wait_vmcnt<0>();
+  phase_barrier();
+  if (group == 1) phase_barrier();   // group 1 runs one phase behind
+
+  for (int ks = 0; ks < nks; ++ks) {
+    // memory phase of step ks: the slot of step ks + 2 held step ks - 1, which both groups
+    // finished reading before the barrier that opened this phase
+    if (ks + 2 < nks) issue_stage(ks + 2);
+    memory_phase(ks);
+    if (ks + 2 < nks) wait_vmcnt<Sh::INSTR>();   // own copies of step ks + 1 have landed
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    phase_barrier();
+    compute_phase();
+    // group 1's last compute phase needs no closing barrier; the counts of the groups match
+    if (!(group == 1 && ks == nks - 1)) phase_barrier();
+  }
+
+  if constexpr (FAM == FAM_WNA16) {
+    // Offset term as a contraction over the groups (K' = Gp = G rounded up to 32): A = group sums
+    // of the activation row (workspace: per row Gp bf16 high halves then Gp low halves), B =
+    // -s * (128 + z) of the channel, both split hi + lo. Lane l: row / channel l & 15, groups
+    // 32 gb + 8 (l >> 4) .. + 7.
+    const int G = p.K / 128;
+    const int Gp = (G + 31) / 32 * 32;
+    const uint16_t* Ssplit = reinterpret_cast<const uint16_t*>(p.ws);
+    const int h = lane >> 4;
+    for (int gb = 0; gb < Gp / 32; ++gb) {
+      u32x4 sh[MW], sl[MW];
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        const int r = min(row0 + wm * 16 * MW + 16 * mb + (lane & 15), p.M - 1);
+        const uint16_t* src = Ssplit + size_t(r) * 2 * Gp + 32 * gb + 8 * h;
+        sh[mb] = *reinterpret_cast<const u32x4*>(src);
+        sl[mb] = *reinterpret_cast<const u32x4*>(src + Gp);
+      }
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        uint32_t bh[4], bl[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int g = 32 * gb + 8 * h + j;
+          float b = 0.0f;
+          if (g < G) {
+            const size_t unit = size_t(nt0 + t) * p.k_units + g;
+            const float sc = bf16_bits_to_f32(
+                *reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
+            uint32_t z = 8;
+            if (p.asym) {
+              const uint32_t zb = w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)];
+              z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
+            }
+            b = -sc * float(128u + z);
+          }
+          const uint32_t hi = f32_to_bf16_rne(b);
+          const uint32_t lo = f32_to_bf16_rne(b - __uint_as_float(hi << 16));
+          if (j & 1) {
+            bh[j >> 1] |= hi << 16;
+            bl[j >> 1] |= lo << 16;
+          } else {
+            bh[j >> 1] = hi;
+            bl[j >> 1] = lo;
+          }
+        }
+        const bf16x8 bhv = __builtin_bit_cast(bf16x8, u32x4{bh[0], bh[1], bh[2], bh[3]});
+        const bf16x8 blv = __builtin_bit_cast(bf16x8, u32x4{bl[0], bl[1], bl[2], bl[3]});
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) {
+          const bf16x8 shv = __builtin_bit_cast(bf16x8, sh[mb]);
+          acc[mb][t] = mfma_bf16(shv, bhv, acc[mb][t]);
+          acc[mb][t] = mfma_bf16(shv, blv, acc[mb][t]);
+          acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, sl[mb]), bhv, acc[mb][t]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i;
+        const int n = (nt0 + t) * 16 + (lane & 15);
+        store_result<FAM, false>(p, row0 + r, n, acc[mb][t][i], 0);
+      }
+}
+
+// Group sums of bf16 activation rows over 128-k groups, split into bf16 high and low halves:
+// ws[row][0][g] = hi, ws[row][1][g] = lo with hi + lo = the fp32 sum to about 16 bits; groups
+// G..Gp-1 are zero. One thread per (row, group), groups fastest.
+__global__ __launch_bounds__(256) void group_sums_split_kernel(const uint8_t* __restrict__ a, int rows,
+                                                               int K, uint16_t* __restrict__ ws) {
+  const int G = K / 128;
+  const int Gp = (G + 31) / 32 * 32;
+  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= long(rows) * Gp) return;
+  const int g = int(idx % Gp);
+  const long r = idx / Gp;
+  float sum = 0.0f;
+  if (g < G) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a + (size_t(r) * K + size_t(g) * 128) * 2);
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const u32x4 v = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xFFFF0000u);
+    }
+  }
+  const uint16_t hi = f32_to_bf16_rne(sum);
+  const uint16_t lo = f32_to_bf16_rne(sum - __uint_as_float(uint32_t(hi) << 16));
+  ws[size_t(r) * 2 * Gp + g] = hi;
+  ws[size_t(r) * 2 * Gp + Gp + g] = lo;
+}
+
+}  // namespace
+
+static constexpr PPCfg kPP[] = {
+    {4, 4, 2, 4},  // 0: 128 x 256, waves of 64 x 64
+    {4, 4, 4, 2},  // 1: 256 x 128, waves of 64 x 64
+    {2, 4, 4, 2},  // 2: 128 x 128, waves of 32 x 64
+    {4, 2, 2, 4},  // 3: 128 x 128, waves of 64 x 32
+};
+
+const PPCfg* pp_configs(int* count) {
+  *count = int(sizeof(kPP) / sizeof(kPP[0]));
+  return kPP;
+}
+
+template <int FAM, int I>
+constexpr int pp_lds_of() {
+  return PPShape<FAM, kPP[I].mw, kPP[I].ntw, kPP[I].wm, kPP[I].wn>::LDS;
+}
+
+template <int FAM, int... I>
+int pp_lds_table(int cfg, std::integer_sequence<int, I...>) {
+  static const int t[] = {pp_lds_of<FAM, I>()...};
+  return t[cfg];
+}
+
+int pp_lds_bytes(int fam, int cfg) {
+  constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
+  if (cfg < 0 || cfg >= n) return 1 << 30;
+  auto seq = std::make_integer_sequence<int, n>{};
+  if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
+  if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);
+  return pp_lds_table<FAM_W4A8>(cfg, seq);
+}
+
+template <int FAM, int I>
+static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
+  constexpr PPCfg C = kPP[I];
+  using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn>;
+  if constexpr (Sh::LDS <= 160 * 1024) {
+    auto kern = pp_gemm_kernel<FAM, C.mw, C.ntw, C.wm, C.wn>;
+    if (Sh::LDS > 65536)
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
+    hipLaunchKernelGGL(kern, grid, dim3(512), Sh::LDS, s, p, tiles_m, tiles_n);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int FAM, int... I>
+static hipError_t launch_pp_fam(const KParams& p, int cfg, dim3 grid, int tiles_m, int tiles_n,
+                                hipStream_t s, std::integer_sequence<int, I...>) {
+  using Fn = hipError_t (*)(const KParams&, dim3, int, int, hipStream_t);
+  static const Fn table[] = {&launch_pp_one<FAM, I>...};
+  return table[cfg](p, grid, tiles_m, tiles_n, s);
+}
+
+hipError_t launch_pingpong(const KParams& p, int fam, int cfg, dim3 grid, int tiles_m, int tiles_n,
+                           hipStream_t s) {
+  constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
+  if (cfg < 0 || cfg >= n) return hipErrorInvalidValue;
+  auto seq = std::make_integer_sequence<int, n>{};
+  if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  return launch_pp_fam<FAM_W4A8>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+}
+
+size_t group_sums_split_bytes(int64_t rows, int64_t K) {
+  const int64_t G = K / 128;
+  return size_t(rows) * size_t((G + 31) / 32 * 32) * 4;
+}
+
+hipError_t launch_group_sums_split(const uint8_t* a, int rows, int K, void* ws, hipStream_t s) {
+  const int G = K / 128;
+  const long total = long(rows) * ((G + 31) / 32 * 32);
+  hipLaunchKernelGGL(group_sums_split_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a,
+                     rows, K, static_cast<uint16_t*>(ws));
+  return hipGetLastError();
+}
+
+}  // namespace hq

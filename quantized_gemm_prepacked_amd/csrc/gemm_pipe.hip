@@ -10,8 +10,8 @@
 //     and, in the same place, retires the slot that the next loads overwrite;
 //   - the weight units of a step are loaded once per workgroup and read by every wave that
 //     needs them (no duplicate HBM/L2 traffic between waves along M).
-// The activation tile is stored with the 16-byte chunk XOR swizzle (chunk ^ row) so MFMA operand
-// reads are bank-conflict free; a direct-to-LDS load writes lane-contiguous chunks, so each lane
+// The activation tile is stored with a 16-byte chunk XOR swizzle (lds_chunk_swizzle) so MFMA
+// operand reads are bank-conflict free; a direct-to-LDS load writes lane-contiguous chunks, so each lane
 // fetches the global chunk that belongs at its swizzled position.
 #include <hip/hip_runtime.h>
 
@@ -45,21 +45,6 @@ struct PipeTraits<FAM_W4A8> {
   static constexpr int kUnitsPerStep = 1;
   static constexpr int kMetaPerTile = 64;      // 64 e8m0 bytes (one per lane)
 };
-
-// One direct-to-LDS load of 16 bytes per lane: lane i's bytes land at lds + 16*i.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding; n < 64).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_s_barrier();
@@ -138,7 +123,7 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
   for (int j = 0; j < Sh::A_INSTR; ++j) {
     const int q = (wave * Sh::A_INSTR + j) * 64 + lane;
     const int r = q / CPR;
-    const int c = (q % CPR) ^ (r & (CPR - 1));
+    const int c = lds_chunk_swizzle(r, q % CPR, CPR);
     int src_row;
     if constexpr (MOE) {
       const int id = p.sorted_ids[row0 + r];
@@ -153,13 +138,13 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
     uint8_t* st = smem + (ks % STAGES) * Sh::STAGE;
 #pragma unroll
     for (int j = 0; j < Sh::A_INSTR; ++j)
-      dma16(p.a + a_off[j] + size_t(ks) * RB, st + (wave * Sh::A_INSTR + j) * 1024);
+      lds_dma16(p.a + a_off[j] + size_t(ks) * RB, st + (wave * Sh::A_INSTR + j) * 1024);
     uint8_t* sb = st + Sh::A_BYTES;
 #pragma unroll
     for (int j = 0; j < Sh::B_INSTR; ++j) {
       const int u = wave * Sh::B_INSTR + j;        // unit index within the stage: tile u/UPS
       const size_t unit = size_t(nt_wg + u / UPS) * p.k_units + size_t(ks) * UPS + (u % UPS);
-      dma16(w + unit * kUnitBytes + 16 * lane, sb + u * 1024);
+      lds_dma16(w + unit * kUnitBytes + 16 * lane, sb + u * 1024);
     }
     uint8_t* sm = sb + Sh::B_BYTES;
     // Metadata: only the lanes that carry bytes run the load (a direct-to-LDS load writes lane
@@ -169,20 +154,20 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
       // scales: NT tiles x 32 bytes = 2 lanes x 16 per tile; zeros: NT x 8 bytes = 2 lanes x 4
       const int t = lane >> 1;
       const size_t unit = size_t(nt_wg + min(t, NT - 1)) * p.k_units + ks;
-      if (lane < 2 * NT) dma16(w + p.scales_off + unit * 32 + 16 * (lane & 1), sm);
+      if (lane < 2 * NT) lds_dma16(w + p.scales_off + unit * 32 + 16 * (lane & 1), sm);
       const uint8_t* zsrc = p.asym ? w + p.zeros_off + unit * 8 + 4 * (lane & 1)
                                    : w + p.scales_off + unit * 32;   // unused for symmetric weights
-      if (lane < 2 * NT) dma4(zsrc, sm + 1024);
+      if (lane < 2 * NT) lds_dma4(zsrc, sm + 1024);
     } else if constexpr (FAM == FAM_W4A8) {
       const int t = lane >> 2;
       const size_t unit = size_t(nt_wg + min(t, NT - 1)) * p.k_units + ks;
-      if (lane < 4 * NT) dma16(w + p.scales_off + unit * 64 + 16 * (lane & 3), sm);
+      if (lane < 4 * NT) lds_dma16(w + p.scales_off + unit * 64 + 16 * (lane & 3), sm);
     }
   };
 
   auto read_a = [&](const uint8_t* st, int mb, int chunk) -> u32x4 {
     const int r = wm * 16 * MW + 16 * mb + (lane & 15);
-    return *reinterpret_cast<const u32x4*>(st + r * RB + ((chunk ^ (r & (CPR - 1))) * 16));
+    return *reinterpret_cast<const u32x4*>(st + r * RB + (lds_chunk_swizzle(r, chunk, CPR) * 16));
   };
   auto read_b = [&](const uint8_t* st, int t, int q) -> u32x4 {
     const int u = (wn * NTW + t) * UPS + q;
@@ -206,7 +191,7 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
     if (newer >= 2) wait_vmcnt<2 * Sh::INSTR>();
     else if (newer == 1) wait_vmcnt<Sh::INSTR>();
     else wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of the old slot done
+    wait_lgkm0();  // this wave's LDS reads of the old slot are done
     block_barrier();
     if (ks + STAGES - 1 < nks) issue_stage(ks + STAGES - 1);
     const uint8_t* st = smem + (ks % STAGES) * Sh::STAGE;

@@ -4,12 +4,19 @@
 // section "Tuning and JIT compilation per workload", picks a different pipeline per input-size
 // range; at small batch the winner is the one that keeps many asynchronous loads in flight).
 // Here a workgroup owns NTW channel tiles (16 channels each) and one block of 16*MB rows, and
-// its NW waves split the K units between them: each wave streams whole 1 KiB weight units with
-// one 128-bit load per lane (no LDS staging: every weight byte is used by exactly one wave),
-// dequantizes them in registers and feeds the MFMA. The waves' partial tiles are summed through
-// LDS in a fixed order, so the result is deterministic. Optionally the K units are also split
-// across workgroups (grid.z); then fp32/int32 partials go to the workspace and a second kernel
-// sums them in split order and applies the epilogue.
+// its NW waves split the K units between them. Per unit a wave
+//   - loads the packed weights of its NTW tiles with one 128-bit load per lane (registers;
+//     every weight byte is used by exactly one wave),
+//   - copies the unit's activation rows and the tiles' scales (and zero points) into its own LDS
+//     slot with direct-to-LDS copies: whole rows per instruction, so a copy touches the fewest
+//     cache lines (the MFMA operand layout read straight from global memory would touch four
+//     times as many), rows XOR-swizzled for conflict-free operand reads,
+//   - dequantizes in registers and feeds the MFMA.
+// Units go in batches of UNR; with PP two batch buffers alternate so the next batch is in
+// flight while the current one is computed. The waves' partial tiles are summed through LDS in a
+// fixed order, so the result is deterministic. Optionally the K units are also split across
+// workgroups (grid.z); then fp32/int32 partials go to the workspace and a second kernel sums
+// them in split order and applies the epilogue.
 #include <hip/hip_runtime.h>
 
 #include "device_ops.h"
@@ -18,135 +25,53 @@
 
 namespace hq {
 
-template <int FAM, int MB, int NTW>
-struct SkinnyFrag;
+namespace {
 
-// WNA16: one unit = 16 channels x 128 k (one group) = 4 MFMA k-steps of 32.
-template <int MB, int NTW>
-struct SkinnyFrag<FAM_WNA16, MB, NTW> {
-  u32x4 b[NTW];
-  uint32_t s_bits[NTW];
-  uint32_t zb[NTW];
-  u32x4 a[MB][4];
-
-  __device__ __forceinline__ void load(const KParams& p, const uint8_t* w, int nt0, int u,
-                                       int lane, const uint8_t* const* arow) {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const size_t unit = size_t(nt0 + t) * p.k_units + u;
-      b[t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
-      s_bits[t] = *reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15));
-      zb[t] = p.asym ? uint32_t(w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)]) : 0u;
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (arow[mb]) {
-        const uint8_t* src = arow[mb] + (size_t(u) * 128 + 32 * (lane >> 4)) * 2;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) a[mb][d] = ldg16(src + 16 * d);
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) a[mb][d] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-
-  // The group's partial sum_k x*(u - z) is formed on the MFMA as sum_k x*(128 + u) plus
-  // sum_k x*(-(128 + z)): the first operand costs one bit-select per weight pair, the second is
-  // a per-channel constant. At small M the MFMA has cycles to spare; the VALU does not.
-  __device__ __forceinline__ void compute(const KParams& p, int lane, f32x4 (*acc)[NTW]) const {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const uint32_t z = p.asym ? ((lane & 1) ? (zb[t] >> 4) : (zb[t] & 0xFu)) : 8u;
-      const float s = bf16_bits_to_f32(s_bits[t]);
-      const bf16x8 bneg = neg_offset_bf16x8(z);
-      f32x4 part[MB];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const bf16x8 bw = dequant_int4x8_offset128(b[t][d]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const bf16x8 av = __builtin_bit_cast(bf16x8, a[mb][d]);
-          part[mb] = mfma_bf16(av, bw, d == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : part[mb]);
-          part[mb] = mfma_bf16(av, bneg, part[mb]);
-        }
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb][t] += part[mb] * s;
-    }
-  }
+template <int FAM>
+struct SkTraits;
+template <>
+struct SkTraits<FAM_WNA16> {
+  static constexpr int kABytes = 2, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8;
+};
+template <>
+struct SkTraits<FAM_W8A8> {
+  static constexpr int kABytes = 1, kUnitK = 64, kScaleBytes = 0, kZeroBytes = 0;
+};
+template <>
+struct SkTraits<FAM_W4A8> {
+  static constexpr int kABytes = 1, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0;
 };
 
-// W8A8: one unit = 16 channels x 64 k = one int8 MFMA.
-template <int MB, int NTW>
-struct SkinnyFrag<FAM_W8A8, MB, NTW> {
-  u32x4 b[NTW];
-  u32x4 a[MB];
-
-  __device__ __forceinline__ void load(const KParams& p, const uint8_t* w, int nt0, int u,
-                                       int lane, const uint8_t* const* arow) {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const size_t unit = size_t(nt0 + t) * p.k_units + u;
-      b[t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      a[mb] = arow[mb] ? ldg16(arow[mb] + size_t(u) * 64 + 16 * (lane >> 4)) : u32x4{0, 0, 0, 0};
-  }
-
-  __device__ __forceinline__ void compute(const KParams&, int, i32x4 (*acc)[NTW]) const {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb][t] = mfma_i8(a[mb], b[t], acc[mb][t]);
-  }
-};
-
-// W4A8: one unit = 16 channels x 128 k = four MX blocks = one scaled fp8 x fp4 MFMA.
-template <int MB, int NTW>
-struct SkinnyFrag<FAM_W4A8, MB, NTW> {
-  u32x4 b[NTW];
-  uint32_t sc[NTW];
-  u32x4 a[MB][2];
-
-  __device__ __forceinline__ void load(const KParams& p, const uint8_t* w, int nt0, int u,
-                                       int lane, const uint8_t* const* arow) {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const size_t unit = size_t(nt0 + t) * p.k_units + u;
-      b[t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
-      sc[t] = w[p.scales_off + unit * 64 + lane];
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (arow[mb]) {
-        // 8-bit A operand of the scaled MFMA: lane group g holds k = 16g..16g+15 in bytes 0..15
-        // and k = 64+16g..64+16g+15 in bytes 16..31.
-        const uint8_t* src = arow[mb] + size_t(u) * 128 + 16 * (lane >> 4);
-        a[mb][0] = ldg16(src);
-        a[mb][1] = ldg16(src + 64);
-      } else {
-        a[mb][0] = u32x4{0, 0, 0, 0};
-        a[mb][1] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-
-  __device__ __forceinline__ void compute(const KParams&, int, f32x4 (*acc)[NTW]) const {
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        acc[mb][t] = mfma_fp8_fp4(a[mb][0], a[mb][1], b[t], int(sc[t]), acc[mb][t]);
-  }
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP>
+struct SkShape {
+  using T = SkTraits<FAM>;
+  static constexpr int ROWB = T::kUnitK * T::kABytes;    // activation bytes per row per unit
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int A_UNIT = 16 * MB * ROWB;
+  static constexpr int A_INSTR = A_UNIT / 1024;         // copies of a unit's activation rows
+  static constexpr int SC = NTW * T::kScaleBytes;       // per unit, all tiles
+  static constexpr int ZB = NTW * T::kZeroBytes;
+  static constexpr int META_INSTR = (SC ? 1 : 0) + (ZB ? 1 : 0);
+  static constexpr int UNIT_LDS = (A_UNIT + SC + ZB + 15) / 16 * 16;
+  static constexpr int NBUF = PP ? 2 : 1;
+  static constexpr int WAVE_LDS = NBUF * UNR * UNIT_LDS;
+  static constexpr int RED = NW * MB * NTW * 4 * 64 * 4; // epilogue reduction (aliases the slots)
+  static constexpr int LDS = (NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED);
+  static constexpr int UNIT_INSTR = A_INSTR + NTW + META_INSTR;   // vector-memory ops per unit
+  static_assert(A_UNIT % 1024 == 0, "whole-wave activation copies");
+  static_assert(SC / 16 <= 64 && ZB / 4 <= 64, "metadata copies fit one instruction each");
+  static_assert(UNR * UNIT_INSTR < 64, "vmcnt range");
 };
 
 template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE>
 __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
+  using Sh = SkShape<FAM, MB, NTW, NW, UNR, PP>;
   using Acc = typename AccType<FAM>::type;
   using Elem = typename AccType<FAM>::elem;
-  constexpr int ABYTES = FAM == FAM_WNA16 ? 2 : 1;
+  using T = SkTraits<FAM>;
+  constexpr int ROWB = Sh::ROWB, CPR = Sh::CPR;
+  extern __shared__ __align__(16) uint8_t smem[];
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nt0 = blockIdx.x * NTW;
@@ -159,16 +84,23 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     w += size_t(p.block_expert[rb]) * p.expert_stride;
   }
 
-  const uint8_t* arow[MB];
+  // Activation copy sources: copy j of a unit moves LDS positions q = 64 j + lane of the unit's
+  // [16*MB rows][CPR chunks] block; position (r, slot) holds source chunk swizzle(r, slot). Rows
+  // past M (MoE: padding) read a valid row and are never stored, so every lane copies.
+  const uint8_t* asrc[Sh::A_INSTR];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int i = row0 + 16 * mb + (lane & 15);
+  for (int j = 0; j < Sh::A_INSTR; ++j) {
+    const int q = 64 * j + lane;
+    const int r = q / CPR;
+    const int c = lds_chunk_swizzle(r, q % CPR, CPR);
+    int src_row;
     if constexpr (MOE) {
-      const int id = p.sorted_ids[i];
-      arow[mb] = id < p.M ? p.a + size_t(id / p.topk) * p.K * ABYTES : nullptr;
+      const int id = p.sorted_ids[row0 + r];
+      src_row = id < p.M ? id / p.topk : 0;
     } else {
-      arow[mb] = i < p.M ? p.a + size_t(i) * p.K * ABYTES : nullptr;
+      src_row = min(row0 + r, p.M - 1);
     }
+    asrc[j] = p.a + size_t(src_row) * p.K * T::kABytes + 16 * c;
   }
 
   Acc acc[MB][NTW];
@@ -177,48 +109,165 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[mb][t] = Acc{0, 0, 0, 0};
 
-  // This wave's units are u0, u0 + NW, ... < uend, taken in batches of UNR. Two register
-  // buffers alternate so that batch b+1 is in flight while batch b is dequantized and
-  // multiplied (written as an explicit ping-pong: no register copies between the buffers).
+  uint8_t* wlds = smem + wave * Sh::WAVE_LDS;
+  u32x4 bw[Sh::NBUF][UNR][NTW];   // packed weights of the batches in flight
+
+  // Issue every copy and load of unit u into slot (buf, r).
+  auto issue_unit = [&](int buf, int r, int u) __attribute__((always_inline)) {
+    uint8_t* slot = wlds + (buf * UNR + r) * Sh::UNIT_LDS;
+#pragma unroll
+    for (int j = 0; j < Sh::A_INSTR; ++j) lds_dma16(asrc[j] + size_t(u) * ROWB, slot + 1024 * j);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const size_t unit = size_t(nt0 + t) * p.k_units + u;
+      bw[buf][r][t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
+    }
+    if constexpr (Sh::SC > 0) {
+      // the NTW tiles' scale blocks of this unit, T::kScaleBytes each, 16 bytes per lane
+      constexpr int per_tile = T::kScaleBytes / 16;
+      const int t = min(lane / per_tile, NTW - 1);
+      const size_t unit = size_t(nt0 + t) * p.k_units + u;
+      if (lane < Sh::SC / 16)
+        lds_dma16(w + p.scales_off + unit * T::kScaleBytes + 16 * (lane % per_tile), slot + Sh::A_UNIT);
+    }
+    if constexpr (Sh::ZB > 0) {
+      // zero points (8 bytes per tile), 4 bytes per lane; symmetric weights have none and copy
+      // scale bytes instead, which are never read
+      const int t = min(lane >> 1, NTW - 1);
+      const size_t unit = size_t(nt0 + t) * p.k_units + u;
+      const uint8_t* src = p.asym ? w + p.zeros_off + unit * 8 + 4 * (lane & 1)
+                                  : w + p.scales_off + unit * T::kScaleBytes;
+      if (lane < Sh::ZB / 4) lds_dma4(src, slot + Sh::A_UNIT + Sh::SC);
+    }
+  };
+
+  // Operand reads from the slot and the MFMAs of one unit.
+  auto compute_unit = [&](int buf, int r) __attribute__((always_inline)) {
+    const uint8_t* slot = wlds + (buf * UNR + r) * Sh::UNIT_LDS;
+    auto read_a = [&](int mb, int chunk) __attribute__((always_inline)) -> u32x4 {
+      const int row = 16 * mb + (lane & 15);
+      return *reinterpret_cast<const u32x4*>(slot + row * ROWB + 16 * lds_chunk_swizzle(row, chunk, CPR));
+    };
+    if constexpr (FAM == FAM_WNA16) {
+      // The group's partial sum_k x*(u - z) is formed as sum_k x*(128 + u) (the offset-128
+      // operand costs one bit-select per weight pair) minus (128 + z) * sum_k x; the row sums
+      // come from one MFMA against an all-ones operand, shared by the NTW tiles.
+      u32x4 af[MB][4];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) af[mb][d] = read_a(mb, 4 * (lane >> 4) + d);
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      f32x4 rsum[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        rsum[mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][0]), ones, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int d = 1; d < 4; ++d) rsum[mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), ones, rsum[mb]);
+      }
+      const uint8_t* sc = slot + Sh::A_UNIT;
+      const uint8_t* zp = sc + Sh::SC;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc + t * 32 + 2 * (lane & 15)));
+        uint32_t z = 8;
+        if (p.asym) {
+          const uint32_t zb = zp[t * 8 + ((lane & 15) >> 1)];
+          z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
+        }
+        const float c = -s * float(128u + z);
+        f32x4 part[MB];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_int4x8_offset128(bw[buf][r][t][d]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            part[mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv,
+                                 d == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : part[mb]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb][t] += part[mb] * s + rsum[mb] * c;
+      }
+    } else if constexpr (FAM == FAM_W8A8) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 av = read_a(mb, lane >> 4);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[mb][t] = mfma_i8(av, bw[buf][r][t], acc[mb][t]);
+      }
+    } else {
+      // 8-bit A operand of the scaled MFMA: lane group g holds chunks g and 4 + g
+      const uint8_t* sc = slot + Sh::A_UNIT;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 alo = read_a(mb, lane >> 4);
+        const u32x4 ahi = read_a(mb, 4 + (lane >> 4));
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          acc[mb][t] = mfma_fp8_fp4(alo, ahi, bw[buf][r][t], int(sc[t * 64 + lane]), acc[mb][t]);
+      }
+    }
+  };
+
+  // This wave's units are u0, u0 + NW, ... < uend, in batches of UNR; a remainder below UNR is
+  // taken one unit at a time.
   const int ubeg = blockIdx.z * p.units_per_split;
   const int uend = min(p.k_units, ubeg + p.units_per_split);
   const int u0 = ubeg + wave;
   const int nunits = u0 < uend ? (uend - u0 + NW - 1) / NW : 0;
   const int nbatch = nunits / UNR;
-  using Frag = SkinnyFrag<FAM, MB, NTW>;
-  Frag fa[UNR];
-  [[maybe_unused]] Frag fb[PP ? UNR : 1];
-  auto load_batch = [&](Frag* f, int b) {
+  auto issue_batch = [&](int buf, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) f[r].load(p, w, nt0, u0 + (b * UNR + r) * NW, lane, arow);
+    for (int r = 0; r < UNR; ++r) issue_unit(buf, r, u0 + (b * UNR + r) * NW);
   };
-  auto compute_batch = [&](const Frag* f) {
+  auto compute_batch = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) f[r].compute(p, lane, acc);
+    for (int r = 0; r < UNR; ++r) compute_unit(buf, r);
   };
   if constexpr (PP) {
-    if (nbatch > 0) load_batch(fa, 0);
+    // Written out for both buffers so that every register index is a constant. Before a buffer
+    // is refilled, the operand reads of the batch that used it last have completed.
+    if (nbatch > 0) issue_batch(0, 0);
     for (int b = 0; b < nbatch; b += 2) {
-      if (b + 1 < nbatch) load_batch(fb, b + 1);
-      compute_batch(fa);
-      if (b + 2 < nbatch) load_batch(fa, b + 2);
-      if (b + 1 < nbatch) compute_batch(fb);
+      wait_lgkm0();
+      if (b + 1 < nbatch) {
+        issue_batch(1, b + 1);
+        wait_vmcnt<UNR * Sh::UNIT_INSTR>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      compute_batch(0);
+      if (b + 1 < nbatch) {
+        wait_lgkm0();
+        if (b + 2 < nbatch) {
+          issue_batch(0, b + 2);
+          wait_vmcnt<UNR * Sh::UNIT_INSTR>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        compute_batch(1);
+      }
     }
   } else {
     for (int b = 0; b < nbatch; ++b) {
-      load_batch(fa, b);
-      compute_batch(fa);
+      wait_lgkm0();
+      issue_batch(0, b);
+      wait_vmcnt<0>();
+      compute_batch(0);
     }
   }
   for (int i = nbatch * UNR; i < nunits; ++i) {
-    Frag f;
-    f.load(p, w, nt0, u0 + i * NW, lane, arow);
-    f.compute(p, lane, acc);
+    wait_lgkm0();
+    issue_unit(0, 0, u0 + i * NW);
+    wait_vmcnt<0>();
+    compute_unit(0, 0);
   }
 
-  // Sum the waves' tiles through LDS (fixed order: wave 0, 1, ...), then the epilogue.
+  // Sum the waves' tiles through LDS (fixed order: wave 0, 1, ...), then the epilogue. The
+  // reduction buffer aliases the unit slots: every wave has finished with its slot first.
   constexpr int kVals = MB * NTW * 4;
-  __shared__ Elem red[NW][kVals][64];
+  Elem(*red)[kVals][64] = reinterpret_cast<Elem(*)[kVals][64]>(smem);
+  __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -241,6 +290,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     store_result<FAM, MOE>(p, row0 + ib, n, sum, blockIdx.z);
   }
 }
+
+}  // namespace
 
 // ---- launch table --------------------------------------------------------------------------
 
@@ -271,6 +322,9 @@ static constexpr SkinnyCfg kSkinny[] = {
     {1, 1, 16, 1, 1},  // 21
     {2, 4, 4, 1, 1},   // 22: M <= 32, ping-pong
     {2, 2, 8, 1, 1},   // 23
+    {1, 4, 8, 4, 0},   // 24: M <= 16, all of a wave's units in flight at once (K = 4096)
+    {1, 4, 4, 4, 0},   // 25
+    {1, 2, 8, 4, 1},   // 26
 };
 
 const SkinnyCfg* skinny_configs(int* count) {
@@ -278,23 +332,34 @@ const SkinnyCfg* skinny_configs(int* count) {
   return kSkinny;
 }
 
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE>
+static hipError_t launch_skinny_one(const KParams& p, dim3 grid, hipStream_t s) {
+  constexpr int lds = SkShape<FAM, MB, NTW, NW, UNR, PP>::LDS;
+  if constexpr (lds > 160 * 1024) {
+    return hipErrorInvalidValue;
+  } else {
+    auto kern = skinny_gemm_kernel<FAM, MB, NTW, NW, UNR, PP, MOE>;
+    if (lds > 65536)
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, p);
+    return hipGetLastError();
+  }
+}
+
 template <int FAM, bool MOE>
 static hipError_t launch_skinny_fam(const KParams& p, int cfg, dim3 grid, hipStream_t s) {
 #define HQ_SK(I)                                                                           \
   case I:                                                                                  \
-    hipLaunchKernelGGL((skinny_gemm_kernel<FAM, kSkinny[I].mb, kSkinny[I].ntw, kSkinny[I].nw, \
-                                           kSkinny[I].unr, kSkinny[I].pp != 0, MOE>),      \
-                       grid, dim3(kSkinny[I].nw * 64), 0, s, p);                           \
-    break;
+    return launch_skinny_one<FAM, kSkinny[I].mb, kSkinny[I].ntw, kSkinny[I].nw,            \
+                             kSkinny[I].unr, kSkinny[I].pp != 0, MOE>(p, grid, s);
   switch (cfg) {
     HQ_SK(0) HQ_SK(1) HQ_SK(2) HQ_SK(3) HQ_SK(4) HQ_SK(5) HQ_SK(6) HQ_SK(7) HQ_SK(8) HQ_SK(9)
     HQ_SK(10) HQ_SK(11) HQ_SK(12) HQ_SK(13) HQ_SK(14) HQ_SK(15) HQ_SK(16) HQ_SK(17) HQ_SK(18)
-    HQ_SK(19) HQ_SK(20) HQ_SK(21) HQ_SK(22) HQ_SK(23)
+    HQ_SK(19) HQ_SK(20) HQ_SK(21) HQ_SK(22) HQ_SK(23) HQ_SK(24) HQ_SK(25) HQ_SK(26)
     default:
       return hipErrorInvalidValue;
   }
 #undef HQ_SK
-  return hipGetLastError();
 }
 
 hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid,

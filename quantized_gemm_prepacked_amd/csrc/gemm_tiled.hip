@@ -71,10 +71,6 @@ struct BStep {
   }
 };
 
-__device__ __forceinline__ int swz(int row, int chunk, int cpr) {
-  return (chunk ^ (row & (cpr - 1)));
-}
-
 template <int FAM, int MW, int NTW, int WM, int WN, int OCC, bool MOE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void tiled_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
@@ -152,12 +148,12 @@ void tiled_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
       const int ci = tid + j * kThreads;
       const int r = ci / CPR;
       const int c = ci % CPR;
-      *reinterpret_cast<u32x4*>(sbase + r * RB + swz(r, c, CPR) * 16) = regs[j];
+      *reinterpret_cast<u32x4*>(sbase + r * RB + lds_chunk_swizzle(r, c, CPR) * 16) = regs[j];
     }
   };
   auto read_frag = [&](int stage, int mb, int chunk) -> u32x4 {
     const int r = wm * 16 * MW + 16 * mb + (lane & 15);
-    return *reinterpret_cast<const u32x4*>(smem + stage * (BM * RB) + r * RB + swz(r, chunk, CPR) * 16);
+    return *reinterpret_cast<const u32x4*>(smem + stage * (BM * RB) + r * RB + lds_chunk_swizzle(r, chunk, CPR) * 16);
   };
 
   Acc acc[MW][NTW];
