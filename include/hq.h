@@ -143,7 +143,9 @@ hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K,
  *                  order, the flat indices f = t*topk + j routed to e in ascending order, then
  *                  sentinel T*topk up to the next multiple of block_m. Entries past num_padded
  *                  are unspecified.
- *   block_expert   int32 [capacity / block_m]: expert of each block of block_m sorted rows
+ *   block_expert   int32 [capacity / block_m]: expert of each block of block_m sorted rows;
+ *                  blocks past num_padded / block_m hold -1 (no expert; the grouped GEMM
+ *                  skips them)
  *   expert_offsets int32 [E + 1]: exclusive prefix sum of the padded per-expert counts
  *   num_padded     int32 [1]: total padded rows (= expert_offsets[E])
  *   ws             scratch of hq_moe_align_workspace_bytes(...) bytes (contents irrelevant)

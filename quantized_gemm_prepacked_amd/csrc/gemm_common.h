@@ -31,6 +31,7 @@ struct KParams {
   const int32_t* num_padded;
   const float* topk_weights;
   int topk;
+  int E;                    // MoE experts (block_expert entries outside [0, E) are skipped)
   int s_rows;               // rows of the per-group activation sums in the workspace (WNA16 tiled)
 };
 
@@ -91,6 +92,7 @@ struct SkinnyCfg {
   int mb, ntw, nw, unr, pp;
 };
 const SkinnyCfg* skinny_configs(int* count);
+int skinny_lds_bytes(int fam, int cfg);
 
 // A tiled-kernel instantiation: waves own (16*MW) x (16*NTW) sub-tiles, WM x WN waves per
 // workgroup; the workgroup tile is (16*MW*WM) x (16*NTW*WN).

@@ -31,18 +31,20 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
   auto first_fit = [&](std::initializer_list<int> cands) {
     for (int i : cands)
-      if (nt % cfgs[i].ntw == 0) return i;
+      if (nt % cfgs[i].ntw == 0 && skinny_lds_bytes(c.fam, i) <= 160 * 1024) return i;
     return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
   };
   if (rows <= 16) {
-    if (c.fam == FAM_W8A8) return first_fit({10, 2});
-    if (c.fam == FAM_W4A8) return first_fit({11, 2});
-    return first_fit({0, 1, 2});
+    if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
+    if (c.fam == FAM_W4A8) return first_fit({21, 2});
+    return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
     if (c.fam == FAM_W4A8) return first_fit({16, 8});
-    return first_fit({3, 7, 8});
+    if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
+    return first_fit({29, 22, 3, 7, 8});
   }
+  if (c.fam == FAM_WNA16) return first_fit({5, 4, 6});
   return first_fit({4, 5, 6});
 }
 
@@ -102,17 +104,17 @@ int pick_tiled(const Combo&, int64_t N, int64_t K) {
   return -1;
 }
 
-// The per-M-range table for large M (kinds: 1 = LDS-tiled, 2 = async-pipelined), measured on
-// MI355X at the benchmark shapes: the first entry whose max_m covers M and whose tile divides N
-// is used; below the first entry (and when no tile fits) the skinny kernel runs.
+// The per-M-range table for large M (kinds: 1 = LDS-tiled, 2 = async-pipelined, 3 = ping-pong),
+// measured on MI355X at the benchmark shapes: the first entry whose max_m covers M and whose
+// tile divides N is used; below the first entry (and when no tile fits) the skinny kernel runs.
 struct RangeEntry {
   int64_t max_m;
   int kind, cfg;
 };
 constexpr int64_t kInf = int64_t(1) << 40;
-constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {192, 2, 2}, {384, 1, 9}, {kInf, 2, 7}};
-constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {512, 2, 3}, {1536, 2, 10}, {kInf, 2, 8}};
-constexpr RangeEntry kW4a8Table[] = {{256, 0, 0}, {768, 2, 3}, {1536, 2, 2}, {kInf, 2, 11}};
+constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 10}, {256, 3, 3}, {kInf, 3, 0}};
+constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 9}};
+constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -206,7 +208,9 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   pl.cfg = pick_skinny(c, M, N);
   int n_cfg = 0;
   const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
-  if (tov.kind == 0 && tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0) pl.cfg = tov.cfg;
+  if (tov.kind == 0 && tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0 &&
+      skinny_lds_bytes(c.fam, tov.cfg) <= 160 * 1024)
+    pl.cfg = tov.cfg;
   const SkinnyCfg& sc = cfgs[pl.cfg];
   const int64_t units = K / k_unit(c);
   const int64_t wgs = (N / 16 / sc.ntw) * ((M + 16 * sc.mb - 1) / (16 * sc.mb));
@@ -231,8 +235,21 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
     pl.ws_bytes = size_t(T) * (K / 128) * 4;  // per-token activation group sums
     return pl;
   }
+  // MoE row blocks: many small workgroups share the GPU, so keep the per-workgroup LDS small
   pl.kind = 0;
-  pl.cfg = block_m <= 16 ? pick_skinny(c, 16, N) : pick_skinny(c, block_m, N);
+  const int64_t nt = N / 16;
+  int n_cfg = 0;
+  const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
+  // the kernel's row block (16 * mb rows) is the alignment's block of block_m rows; the last
+  // candidate of each list has one channel tile per workgroup and always fits
+  static const int c16[3] = {0, 1, 2}, c32[3] = {3, 7, 8}, c64[3] = {4, 5, 6};
+  const int* cands = block_m <= 16 ? c16 : block_m <= 32 ? c32 : c64;
+  pl.cfg = cands[2];
+  for (int j = 0; j < 3; ++j)
+    if (nt % cfgs[cands[j]].ntw == 0) {
+      pl.cfg = cands[j];
+      break;
+    }
   return pl;
 }
 
@@ -304,12 +321,14 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
       if (e != hipSuccess) return e;
     }
     if (moe) {
+      if (bm != call.block_m) return hipErrorInvalidValue;   // one workgroup row = one block
       p.M = int(call.T * call.topk);
       p.sorted_ids = call.sorted_ids;
       p.block_expert = call.block_expert;
       p.num_padded = call.num_padded;
       p.topk_weights = call.topk_weights;
       p.topk = call.topk;
+      p.E = call.E;
       return launch(dim3(unsigned(tiles_n), unsigned(call.max_blocks)), int(call.max_blocks), tiles_n);
     }
     p.M = int(call.M);
@@ -320,12 +339,14 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   const SkinnyCfg& sc = skinny_configs(&n_cfg)[plan.cfg];
   const int rows_per_block = 16 * sc.mb;
   if (moe) {
+    if (rows_per_block != call.block_m) return hipErrorInvalidValue;   // one row block = one block
     p.M = int(call.T * call.topk);
     p.sorted_ids = call.sorted_ids;
     p.block_expert = call.block_expert;
     p.num_padded = call.num_padded;
     p.topk_weights = call.topk_weights;
     p.topk = call.topk;
+    p.E = call.E;
     p.split = 1;
     p.units_per_split = p.k_units;
     dim3 grid(unsigned(call.N / 16 / sc.ntw), unsigned(call.max_blocks), 1);

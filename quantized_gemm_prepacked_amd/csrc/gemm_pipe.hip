@@ -98,7 +98,9 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
     ntile = blockIdx.x;
     row0 = mt * BM;
     if (row0 >= *p.num_padded) return;
-    w += size_t(p.block_expert[mt]) * p.expert_stride;
+    const int expert = p.block_expert[mt];
+    if (expert < 0 || expert >= p.E) return;   // a block past the sorted rows
+    w += size_t(expert) * p.expert_stride;
   } else {
     const int nwg = gridDim.x;
     const int pid = blockIdx.x;

@@ -19,6 +19,8 @@
 // them in split order and applies the epilogue.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "device_ops.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -81,7 +83,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   const uint8_t* w = p.w;
   if constexpr (MOE) {
     if (row0 >= *p.num_padded) return;
-    w += size_t(p.block_expert[rb]) * p.expert_stride;
+    const int expert = p.block_expert[rb];
+    if (expert < 0 || expert >= p.E) return;   // a block past the sorted rows
+    w += size_t(expert) * p.expert_stride;
   }
 
   // Activation copy sources: copy j of a unit moves LDS positions q = 64 j + lane of the unit's
@@ -325,11 +329,30 @@ static constexpr SkinnyCfg kSkinny[] = {
     {1, 4, 8, 4, 0},   // 24: M <= 16, all of a wave's units in flight at once (K = 4096)
     {1, 4, 4, 4, 0},   // 25
     {1, 2, 8, 4, 1},   // 26
+    {1, 4, 16, 2, 0},  // 27: M <= 16, 16 waves
+    {1, 4, 16, 1, 1},  // 28
+    {2, 4, 8, 2, 0},   // 29: M <= 32, 8 waves
 };
 
 const SkinnyCfg* skinny_configs(int* count) {
   *count = int(sizeof(kSkinny) / sizeof(kSkinny[0]));
   return kSkinny;
+}
+
+template <int FAM, int... I>
+static int skinny_lds_table(int cfg, std::integer_sequence<int, I...>) {
+  static const int t[] = {SkShape<FAM, kSkinny[I].mb, kSkinny[I].ntw, kSkinny[I].nw, kSkinny[I].unr,
+                                  kSkinny[I].pp != 0>::LDS...};
+  return t[cfg];
+}
+
+int skinny_lds_bytes(int fam, int cfg) {
+  constexpr int n = int(sizeof(kSkinny) / sizeof(kSkinny[0]));
+  if (cfg < 0 || cfg >= n) return 1 << 30;
+  auto seq = std::make_integer_sequence<int, n>{};
+  if (fam == FAM_WNA16) return skinny_lds_table<FAM_WNA16>(cfg, seq);
+  if (fam == FAM_W8A8) return skinny_lds_table<FAM_W8A8>(cfg, seq);
+  return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
 template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE>
@@ -355,7 +378,7 @@ static hipError_t launch_skinny_fam(const KParams& p, int cfg, dim3 grid, hipStr
   switch (cfg) {
     HQ_SK(0) HQ_SK(1) HQ_SK(2) HQ_SK(3) HQ_SK(4) HQ_SK(5) HQ_SK(6) HQ_SK(7) HQ_SK(8) HQ_SK(9)
     HQ_SK(10) HQ_SK(11) HQ_SK(12) HQ_SK(13) HQ_SK(14) HQ_SK(15) HQ_SK(16) HQ_SK(17) HQ_SK(18)
-    HQ_SK(19) HQ_SK(20) HQ_SK(21) HQ_SK(22) HQ_SK(23) HQ_SK(24) HQ_SK(25) HQ_SK(26)
+    HQ_SK(19) HQ_SK(20) HQ_SK(21) HQ_SK(22) HQ_SK(23) HQ_SK(24) HQ_SK(25) HQ_SK(26) HQ_SK(27) HQ_SK(28) HQ_SK(29)
     default:
       return hipErrorInvalidValue;
   }

@@ -13,6 +13,7 @@
 // the input, independent of scheduling.
 #include <hip/hip_runtime.h>
 
+#include "hq.h"
 #include "internal.h"
 
 namespace hq {
@@ -27,7 +28,8 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
                                                              int32_t* __restrict__ sorted,
                                                              int32_t* __restrict__ block_expert,
                                                              int32_t* __restrict__ offsets_out,
-                                                             int32_t* __restrict__ num_padded) {
+                                                             int32_t* __restrict__ num_padded,
+                                                             int max_blocks) {
   extern __shared__ int sm[];
   int* cnt = sm;               // [E]
   int* offs = cnt + E;         // [E + 1]
@@ -78,6 +80,8 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
     }
     block_expert[b] = lo;
   }
+  // blocks past the sorted rows (up to the capacity) get no expert
+  for (int b = (total + bm - 1) / bm + tid; b < max_blocks; b += kThreads) block_expert[b] = -1;
 
   // Stable scatter.
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -124,7 +128,8 @@ hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, in
   const size_t smem = sizeof(int) * (size_t(E) * 3 + 1 + kThreads + size_t(kWaves) * E);
   hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kThreads), smem, stream, topk_ids,
                      int(T * topk), int(E), int(block_m), sorted_ids, block_expert,
-                     expert_offsets, num_padded);
+                     expert_offsets, num_padded,
+                     int(hq_moe_align_capacity(T, topk, E, block_m) / size_t(block_m)));
   return hipGetLastError();
 }
 

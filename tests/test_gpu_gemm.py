@@ -37,10 +37,12 @@ WNA16_SMALL = [
     (33, 304, 512, True),
     (128, 512, 512, True),
     (300, 256, 1024, True),
-    (600, 512, 640, True),    # 256 x 128 pipelined tiles, ragged M
+    (600, 512, 640, True),    # 128 x 256 ping-pong tiles, ragged M
     (600, 480, 512, False),   # no pipelined tile divides N: LDS-tiled fallback
     (600, 480, 384, True),    # LDS-tiled fallback with K/128 = 3 groups
-    (150, 256, 896, True),    # 64 x 128 pipelined tiles, K/128 = 7 groups
+    (150, 256, 896, True),    # 128 x 128 ping-pong tiles, K/128 = 7 groups
+    (24, 512, 1024, True),    # two 16-row blocks per skinny workgroup
+    (300, 512, 4224, True),   # 128 x 256 ping-pong tiles, K/128 = 33 groups (two 32-group blocks)
 ]
 
 
@@ -87,7 +89,10 @@ def test_wna16_full_size_sampled(cfg2_weights, M):
 
 # ---- W8A8 -------------------------------------------------------------------------------------
 W8A8_SMALL = [(1, 256, 8192), (64, 512, 1024), (7, 272, 320), (16, 256, 64), (200, 512, 2048),
-              (1100, 512, 1024),   # 256 x 128 pipelined tiles, ragged M
+              (20, 512, 1024),     # two 16-row blocks per skinny workgroup
+              (700, 384, 1024),    # 256 x 128 ping-pong tiles
+              (400, 256, 640),     # 128 x 128 ping-pong tiles
+              (1100, 512, 1024),   # 256 x 256 pipelined tiles, ragged M
               (2100, 640, 512),    # 256 x 256 tiles do not divide N: LDS-tiled fallback
               (2050, 512, 640)]    # 256 x 256 pipelined tiles, ragged M
 
@@ -122,9 +127,11 @@ def test_w8a8_full_size_sampled(M):
 
 # ---- W4A8-MXFP4 -------------------------------------------------------------------------------
 W4A8_SMALL = [(1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024),
-              (700, 256, 1024),    # 64 x 64 pipelined tiles
+              (600, 256, 1024),    # skinny, four 16-row blocks per workgroup
+              (700, 256, 1024),    # 64 x 128 pipelined tiles
               (1200, 512, 768),    # 64 x 128 pipelined tiles
-              (1600, 512, 384)]    # 256 x 256 pipelined tiles, ragged M
+              (1600, 512, 384),    # 128 x 128 pipelined tiles, ragged M
+              (3200, 256, 384)]    # 256 x 256 pipelined tiles, ragged M
 
 
 @pytest.mark.parametrize("M,N,K", W4A8_SMALL)

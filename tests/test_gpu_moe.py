@@ -27,9 +27,13 @@ def align(ids: np.ndarray, E: int, bm: int):
     hq.hq_moe_align(to_dev(ids.astype(np.int32)), T, topk, E, bm, sorted_ids, block_expert, offs, npad)
     torch.cuda.synchronize()
     n = int(npad.item())
+    be = block_expert.cpu().numpy()
+    # blocks past the sorted rows, up to the capacity, are marked as having no expert (-1), so a
+    # grouped GEMM launched over the capacity skips them
+    assert (be[n // bm: cap // bm] == -1).all()
     return {
         "num_padded": n, "expert_offsets": offs.cpu().numpy(),
-        "sorted_ids": sorted_ids.cpu().numpy()[:n], "block_expert": block_expert.cpu().numpy()[:n // bm],
+        "sorted_ids": sorted_ids.cpu().numpy()[:n], "block_expert": be[:n // bm],
         "dev": (sorted_ids, block_expert, npad),
     }
 
