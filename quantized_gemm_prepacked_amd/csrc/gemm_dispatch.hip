@@ -112,8 +112,8 @@ struct RangeEntry {
   int kind, cfg;
 };
 constexpr int64_t kInf = int64_t(1) << 40;
-constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 10}, {256, 3, 3}, {kInf, 3, 0}};
-constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 9}};
+constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
+constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
 
 int tile_n_of(int kind, int cfg) {
@@ -161,11 +161,45 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
+namespace {
+
+bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, int64_t K) {
+  int n = 0;
+  if (o.kind == 0) {
+    const SkinnyCfg* cfgs = skinny_configs(&n);
+    return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
+                         skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
+  }
+  if (o.kind == 1) {
+    const TiledCfg* cfgs = tiled_configs(&n);
+    return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
+  }
+  const bool a32 = uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) < (uint64_t(1) << 32);
+  if (o.kind == 2) {
+    const PipeCfg* cfgs = pipe_configs(&n);
+    return a32 && K % 128 == 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0 &&
+           pipe_lds_bytes(c.fam, o.cfg) <= 160 * 1024;
+  }
+  if (o.kind == 3) {
+    const PPCfg* cfgs = pp_configs(&n);
+    return a32 && K % 128 == 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0 &&
+           pp_lds_bytes(c.fam, o.cfg) <= 160 * 1024;
+  }
+  return false;
+}
+
+}  // namespace
+
 Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   Plan pl{};
   const TuneOverride tov = tune_override();
   RangeEntry pick = pick_range(c, M, N, K);
-  // Sweep overrides (HQ_TUNE), honoured only where the shape fits.
+  // Sweep overrides (HQ_TUNE): an override that does not fit the shape (tile, LDS, K) is
+  // refused (kind -1, the call fails) rather than silently replaced.
+  if (tov.kind >= 0 && !override_fits(c, tov, M, N, K)) {
+    pl.kind = -1;
+    return pl;
+  }
   if (tov.kind == 0) pick = {0, 0, 0};
   if (tov.kind == 1 && pick_tiled(c, N, K) >= 0) {
     int n_t = 0;

@@ -156,6 +156,7 @@ hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, co
     return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be 4-byte aligned");
   if (M == 0) return ok();
   const hq::Plan plan = hq::plan_dense(c, M, N, K);
+  if (plan.kind < 0) return fail(HQ_ERR_INVALID_ARGUMENT, "the HQ_TUNE override does not fit this shape");
   if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
     return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
   if (ws && !aligned16(ws)) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 16-byte aligned");
