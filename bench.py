@@ -44,6 +44,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_sources_sha() -> str:
+    """sha256 over the HIP/C++ sources of the library (file names and contents, sorted)."""
+    import hashlib
+    d = os.path.join(ROOT, "quantized_gemm_prepacked_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, point: str):
+    """HBM bytes per launch of the dominant kernel from the FETCH_SIZE / WRITE_SIZE counter passes
+    recorded in profiles/traffic_<workload>.json (each counter scaled by what it reads for a copy of
+    known size). None when there is no record for this point or the kernel sources have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("point") != point or rec.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
 def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
     """Bytes the method must move once: packed weights with scales/zeros, activations (+ per-token
     scales), output."""
@@ -219,7 +248,7 @@ def run_dense(args, wl: str):
     else:
         roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl, f"M={dom['M']}")
     roof["kernel"] = f"M={dom['M']}"
     line = {
         "metric": METRIC, "value": round(tot_flops / tot_s / 1e12, 4), "unit": "TFLOP/s",
@@ -364,7 +393,7 @@ def run_moe(args):
     else:
         roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
-    roof.update(traffic=None, kernel=f"grouped GEMM T={dom['T']}")
+    roof.update(traffic=measured_traffic("moe", f"T={dom['T']}"), kernel=f"grouped GEMM T={dom['T']}")
     line = {
         "metric": METRIC, "value": round(tot_tok / tot_t, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),

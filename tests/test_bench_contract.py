@@ -1,0 +1,36 @@
+"""Host-side pieces of bench.py: the multi-GPU refusal and the counter-derived traffic record."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_traffic_records_are_well_formed():
+    for wl in ("w4a16", "w8a8", "w4a8", "moe"):
+        path = os.path.join(ROOT, "profiles", f"traffic_{wl}.json")
+        rec = json.load(open(path))
+        cal = rec["copy_calibration"]
+        fetch = rec["fetch_size_kib_per_dispatch"] * 1024 * cal["fetch_factor"]
+        write = rec["write_size_kib_per_dispatch"] * 1024 * cal["write_factor"]
+        assert abs(fetch + write - rec["hbm_bytes_per_launch"]) <= 1e-4 * rec["hbm_bytes_per_launch"]
+        assert len(rec["kernel_sources_sha256"]) == 64
+
+
+def test_traffic_is_dropped_when_sources_change(monkeypatch):
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_w4a16.json")))
+    monkeypatch.setattr(bench, "kernel_sources_sha", lambda: rec["kernel_sources_sha256"])
+    assert bench.measured_traffic("w4a16", rec["point"]) == rec["hbm_bytes_per_launch"]
+    assert bench.measured_traffic("w4a16", "M=0") is None
+    monkeypatch.setattr(bench, "kernel_sources_sha", lambda: "0" * 64)
+    assert bench.measured_traffic("w4a16", rec["point"]) is None
