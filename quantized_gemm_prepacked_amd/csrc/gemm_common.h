@@ -32,7 +32,6 @@ struct KParams {
   const float* topk_weights;
   int topk;
   int E;                    // MoE experts (block_expert entries outside [0, E) are skipped)
-  int s_rows;               // rows of the per-group activation sums in the workspace (WNA16 tiled)
 };
 
 template <int FAM>
@@ -121,12 +120,11 @@ const PPCfg* pp_configs(int* count);
 int pp_lds_bytes(int fam, int cfg);
 hipError_t launch_pingpong(const KParams& p, int fam, int cfg, dim3 grid, int tiles_m, int tiles_n,
                            hipStream_t s);
-// WNA16 group sums for the ping-pong kernel: per row, Gp = ceil(K/128 / 32) * 32 bf16 high
-// halves then Gp low halves.
+// WNA16 group sums for the LDS-staged kernels' offset term: per row, Gp = ceil(K/128 / 32) * 32
+// bf16 high halves then Gp low halves.
 size_t group_sums_split_bytes(int64_t rows, int64_t K);
 hipError_t launch_group_sums_split(const uint8_t* a, int rows, int K, void* ws, hipStream_t s);
 
-hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStream_t s);
 
 hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid, hipStream_t s);
 hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s);

@@ -232,10 +232,8 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
     pl.kind = pick.kind;
     pl.cfg = pick.cfg;
     pl.split = 1;
-    // activation group sums (fp32 [G][M], or split bf16 [M][2][Gp] for the ping-pong kernel)
-    pl.ws_bytes = c.fam != FAM_WNA16 ? 0
-                  : pick.kind == 3   ? group_sums_split_bytes(M, K)
-                                     : size_t(M) * (K / 128) * 4;
+    // WNA16: the activation group sums of the offset term
+    pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(M, K) : 0;
     return pl;
   }
   pl.kind = 0;
@@ -266,7 +264,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
     pl.kind = 1;       // LDS-tiled, 64 x 128 tiles: one expert block per tile row
     pl.cfg = 3;
-    pl.ws_bytes = size_t(T) * (K / 128) * 4;  // per-token activation group sums
+    pl.ws_bytes = group_sums_split_bytes(T, K);  // per-token activation group sums
     return pl;
   }
   // MoE row blocks: many small workgroups share the GPU, so keep the per-workgroup LDS small
@@ -321,7 +319,6 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.split = 1;
     p.units_per_split = p.k_units;
     p.M = int(call.M);
-    p.s_rows = int(call.M);
     if (c.fam == FAM_WNA16) {
       hipError_t e = launch_group_sums_split(p.a, p.M, p.K, call.ws, call.stream);
       if (e != hipSuccess) return e;
@@ -350,8 +347,7 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.units_per_split = p.k_units;
     const int tiles_n = int(call.N / bn);
     if (c.fam == FAM_WNA16) {
-      p.s_rows = int(moe ? call.T : call.M);
-      hipError_t e = launch_group_sums(p.a, p.s_rows, p.K, static_cast<float*>(call.ws), call.stream);
+      hipError_t e = launch_group_sums_split(p.a, int(moe ? call.T : call.M), p.K, call.ws, call.stream);
       if (e != hipSuccess) return e;
     }
     if (moe) {

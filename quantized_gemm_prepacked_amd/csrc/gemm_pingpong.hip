@@ -13,11 +13,8 @@
 //   - three LDS slots hold steps s (being read), s + 1 (landed or landing) and s + 2 (in
 //     flight); a wave waits only for its own copies of step s + 1 before the barrier that ends
 //     its memory phase of step s, so a copy has about three phases to land.
-// WNA16 keeps the offset-128 operand of the other kernels. The offset term
-//   -sum_g s[n,g] * (128 + z[n,g]) * S[m,g]   (S: group sums of the activation row)
-// is one more contraction over the K/128 groups, run at the end on the bf16 MFMA with both
-// operands split into bf16 high and low halves (hi*hi + hi*lo + lo*hi, about 16 significant
-// bits each) instead of the fp32 MFMA, which takes four times as many instructions.
+// WNA16 keeps the offset-128 operand of the other kernels; the offset term is removed at the end
+// (tile_epilogue.h).
 #include <hip/hip_runtime.h>
 
 #include <utility>
@@ -25,6 +22,7 @@
 #include "device_ops.h"
 #include "gemm_common.h"
 #include "internal.h"
+#include "tile_epilogue.h"
 
 namespace hq {
 
@@ -280,75 +278,9 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     if (!(group == 1 && ks == nks - 1)) phase_barrier();
   }
 
-  if constexpr (FAM == FAM_WNA16) {
-    // Offset term as a contraction over the groups (K' = Gp = G rounded up to 32): A = group sums
-    // of the activation row (workspace: per row Gp bf16 high halves then Gp low halves), B =
-    // -s * (128 + z) of the channel, both split hi + lo. Lane l: row / channel l & 15, groups
-    // 32 gb + 8 (l >> 4) .. + 7.
-    const int G = p.K / 128;
-    const int Gp = (G + 31) / 32 * 32;
-    const uint16_t* Ssplit = reinterpret_cast<const uint16_t*>(p.ws);
-    const int h = lane >> 4;
-    for (int gb = 0; gb < Gp / 32; ++gb) {
-      u32x4 sh[MW], sl[MW];
-#pragma unroll
-      for (int mb = 0; mb < MW; ++mb) {
-        const int r = min(row0 + wm * 16 * MW + 16 * mb + (lane & 15), p.M - 1);
-        const uint16_t* src = Ssplit + size_t(r) * 2 * Gp + 32 * gb + 8 * h;
-        sh[mb] = *reinterpret_cast<const u32x4*>(src);
-        sl[mb] = *reinterpret_cast<const u32x4*>(src + Gp);
-      }
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        uint32_t bh[4], bl[4];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int g = 32 * gb + 8 * h + j;
-          float b = 0.0f;
-          if (g < G) {
-            const size_t unit = size_t(nt0 + t) * p.k_units + g;
-            const float sc = bf16_bits_to_f32(
-                *reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
-            uint32_t z = 8;
-            if (p.asym) {
-              const uint32_t zb = w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)];
-              z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
-            }
-            b = -sc * float(128u + z);
-          }
-          const uint32_t hi = f32_to_bf16_rne(b);
-          const uint32_t lo = f32_to_bf16_rne(b - __uint_as_float(hi << 16));
-          if (j & 1) {
-            bh[j >> 1] |= hi << 16;
-            bl[j >> 1] |= lo << 16;
-          } else {
-            bh[j >> 1] = hi;
-            bl[j >> 1] = lo;
-          }
-        }
-        const bf16x8 bhv = __builtin_bit_cast(bf16x8, u32x4{bh[0], bh[1], bh[2], bh[3]});
-        const bf16x8 blv = __builtin_bit_cast(bf16x8, u32x4{bl[0], bl[1], bl[2], bl[3]});
-#pragma unroll
-        for (int mb = 0; mb < MW; ++mb) {
-          const bf16x8 shv = __builtin_bit_cast(bf16x8, sh[mb]);
-          acc[mb][t] = mfma_bf16(shv, bhv, acc[mb][t]);
-          acc[mb][t] = mfma_bf16(shv, blv, acc[mb][t]);
-          acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, sl[mb]), bhv, acc[mb][t]);
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int mb = 0; mb < MW; ++mb)
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i;
-        const int n = (nt0 + t) * 16 + (lane & 15);
-        store_result<FAM, false>(p, row0 + r, n, acc[mb][t][i], 0);
-      }
+  const int row_base = row0 + wm * 16 * MW;
+  if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, false>(p, w, acc, row_base, nt0, lane);
+  store_tile<FAM, false, MW, NTW>(p, acc, row_base, nt0, lane);
 }
 
 // Group sums of bf16 activation rows over 128-k groups, split into bf16 high and low halves:

@@ -20,6 +20,7 @@
 #include "device_ops.h"
 #include "gemm_common.h"
 #include "internal.h"
+#include "tile_epilogue.h"
 
 namespace hq {
 
@@ -255,58 +256,9 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
     }
   }
 
-  if constexpr (FAM == FAM_WNA16) {
-    // Remove the offset term sum_g s*(128 + z) * rowsum_g(x) (see gemm_tiled.hip).
-    const float* S = reinterpret_cast<const float*>(p.ws);
-    const int G = p.K / 128;
-    int srow[MW];
-#pragma unroll
-    for (int mb = 0; mb < MW; ++mb) {
-      const int r = row0 + wm * 16 * MW + 16 * mb + (lane & 15);
-      if constexpr (MOE) {
-        const int id = p.sorted_ids[r];
-        srow[mb] = id < p.M ? id / p.topk : -1;
-      } else {
-        srow[mb] = r < p.M ? r : -1;
-      }
-    }
-    for (int gq = 0; gq < (G + 3) / 4; ++gq) {
-      // groups past G (when G is not a multiple of 4) contribute zero
-      const int g_raw = 4 * gq + (lane >> 4);
-      const bool gv = g_raw < G;
-      const int g = gv ? g_raw : G - 1;
-      float bneg[NTW];
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const size_t unit = size_t(nt0 + t) * p.k_units + g;
-        const float sc = bf16_bits_to_f32(
-            *reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
-        uint32_t z = 8;
-        if (p.asym) {
-          const uint32_t zb = w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)];
-          z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
-        }
-        bneg[t] = gv ? -sc * float(128u + z) : 0.0f;
-      }
-#pragma unroll
-      for (int mb = 0; mb < MW; ++mb) {
-        const float sv = srow[mb] >= 0 ? S[size_t(g) * p.s_rows + srow[mb]] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) acc[mb][t] = mfma_f32(sv, bneg[t], acc[mb][t]);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int mb = 0; mb < MW; ++mb)
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i;
-        const int n = (nt0 + t) * 16 + (lane & 15);
-        store_result<FAM, MOE>(p, row0 + r, n, acc[mb][t][i], 0);
-      }
+  const int row_base = row0 + wm * 16 * MW;
+  if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
+  store_tile<FAM, MOE, MW, NTW>(p, acc, row_base, nt0, lane);
 }
 
 }  // namespace

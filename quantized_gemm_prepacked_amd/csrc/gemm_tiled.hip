@@ -21,6 +21,7 @@
 #include "device_ops.h"
 #include "gemm_common.h"
 #include "internal.h"
+#include "tile_epilogue.h"
 
 namespace hq {
 
@@ -231,103 +232,21 @@ void tiled_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
     __syncthreads();
   }
 
-  if constexpr (FAM == FAM_WNA16) {
-    // The MFMA summed x*(128 + u); remove sum_g s[n,g]*(128 + z[n,g]) * S[g][row], S = the
-    // group sums of the activation row (computed by group_sums_kernel into the workspace), as a
-    // K' = K/128 fp32 contraction on the MFMA: lane l supplies S[g][row l&15] and
-    // -s*(128+z) for channel l&15, g = 4*gq + (l >> 4).
-    const float* S = reinterpret_cast<const float*>(p.ws);
-    const int G = p.K / 128;
-    int srow[MW];
-#pragma unroll
-    for (int mb = 0; mb < MW; ++mb) {
-      const int r = row0 + wm * 16 * MW + 16 * mb + (lane & 15);
-      if constexpr (MOE) {
-        const int id = p.sorted_ids[r];
-        srow[mb] = id < p.M ? id / p.topk : -1;
-      } else {
-        srow[mb] = r < p.M ? r : -1;
-      }
-    }
-    for (int gq = 0; gq < (G + 3) / 4; ++gq) {
-      // groups past G (when G is not a multiple of 4) contribute zero
-      const int g_raw = 4 * gq + (lane >> 4);
-      const bool gv = g_raw < G;
-      const int g = gv ? g_raw : G - 1;
-      float bneg[NTW];
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const size_t unit = size_t(nt0 + t) * p.k_units + g;
-        const float sc = bf16_bits_to_f32(
-            *reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
-        uint32_t z = 8;
-        if (p.asym) {
-          const uint32_t zb = w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)];
-          z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
-        }
-        bneg[t] = gv ? -sc * float(128u + z) : 0.0f;
-      }
-#pragma unroll
-      for (int mb = 0; mb < MW; ++mb) {
-        const float sv = srow[mb] >= 0 ? S[size_t(g) * p.s_rows + srow[mb]] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) acc[mb][t] = mfma_f32(sv, bneg[t], acc[mb][t]);
-      }
-    }
-  }
-
-  // ---- epilogue: lane holds rows 4*(lane>>4)+i, column lane&15 of each 16x16 tile ----
-#pragma unroll
-  for (int mb = 0; mb < MW; ++mb)
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i;
-        const int n = (nt0 + t) * 16 + (lane & 15);
-        store_result<FAM, MOE>(p, row0 + r, n, acc[mb][t][i], 0);
-      }
-}
-
-// S[g][r] = sum of the bf16 activations of row r over k in [128g, 128g + 128), fp32.
-__global__ __launch_bounds__(256) void group_sums_kernel(const uint8_t* __restrict__ a, int rows,
-                                                         int K, float* __restrict__ S) {
-  const int G = K / 128;
-  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= long(rows) * G) return;
-  const int r = int(idx % rows);
-  const int g = int(idx / rows);
-  const u32x4* src = reinterpret_cast<const u32x4*>(a + (size_t(r) * K + size_t(g) * 128) * 2);
-  float sum = 0.0f;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const u32x4 v = src[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sum += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xFFFF0000u);
-  }
-  S[size_t(g) * rows + r] = sum;
+  const int row_base = row0 + wm * 16 * MW;
+  if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
+  store_tile<FAM, MOE, MW, NTW>(p, acc, row_base, nt0, lane);
 }
 
 }  // namespace
 
-hipError_t launch_group_sums(const uint8_t* a, int rows, int K, float* S, hipStream_t s) {
-  const long total = long(rows) * (K / 128);
-  hipLaunchKernelGGL(group_sums_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a,
-                     rows, K, S);
-  return hipGetLastError();
-}
 
 static constexpr TiledCfg kTiled[] = {
     {4, 4, 2, 2, 1},  // 0: 128 x 128 tile, 64 x 64 per wave
     {4, 2, 2, 2, 1},  // 1: 128 x 64 (N/16 even)
     {4, 1, 2, 2, 2},  // 2: 128 x 32 (any N)
     {2, 4, 2, 2, 2},  // 3: 64 x 128 (MoE block 64)
-    {4, 4, 2, 2, 2},  // 4: as 0, two waves per SIMD
-    {8, 4, 2, 2, 1},  // 5: 256 x 128, 128 x 64 per wave
-    {8, 4, 2, 2, 2},  // 6: as 5, two waves per SIMD
-    {4, 4, 4, 2, 1},  // 7: 256 x 128, 8 waves
-    {2, 4, 2, 2, 1},  // 8: 64 x 128
-    {4, 2, 2, 4, 2},  // 9: 128 x 128, 8 waves of 64 x 32
+    {2, 4, 2, 2, 1},  // 4: 64 x 128
+    {4, 2, 2, 4, 2},  // 5: 128 x 128, 8 waves of 64 x 32
 };
 
 const TiledCfg* tiled_configs(int* count) {
@@ -349,7 +268,7 @@ static hipError_t launch_tiled_fam(const KParams& p, int cfg, dim3 grid, int til
     break;                                                                                          \
   }
   switch (cfg) {
-    HQ_TL(0) HQ_TL(1) HQ_TL(2) HQ_TL(3) HQ_TL(4) HQ_TL(5) HQ_TL(6) HQ_TL(7) HQ_TL(8) HQ_TL(9)
+    HQ_TL(0) HQ_TL(1) HQ_TL(2) HQ_TL(3) HQ_TL(4) HQ_TL(5)
     default:
       return hipErrorInvalidValue;
   }

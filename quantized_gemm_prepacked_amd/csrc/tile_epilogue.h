@@ -1,0 +1,147 @@
+// tile_epilogue.h -- the end of a wave's output tile in the LDS-staged GEMM kernels (tiled,
+// pipelined, ping-pong): WNA16's offset-term contraction and the scaled bf16 / int32 stores.
+//
+// A wave owns (16*MW) x (16*NTW) outputs as MW x NTW MFMA tiles; lane l holds rows
+// 4*(l>>4)+i (i = 0..3) of each 16-row block and column l&15 of each 16-channel tile. Every
+// per-row and per-column factor the stores need (MoE row index, token scale, router weight,
+// channel scale) is loaded once per tile, all loads issued together, before any store; the
+// per-element arithmetic is the one of `epilogue` in gemm_common.h, in the same order.
+#pragma once
+#include "gemm_common.h"
+
+namespace hq {
+
+// ---- WNA16 offset term ---------------------------------------------------------------------
+// The main loop summed x * (128 + u) per group. What remains is
+//   acc[m][n] -= sum_g s[n,g] * (128 + z[n,g]) * S[m][g]      (S: group sums of row m of X)
+// a K' = K/128 contraction, run on the bf16 MFMA over operands split into high and low bf16
+// halves: hi*hi + hi*lo + lo*hi keeps ~16 significant bits of each product (the fp32 sums in the
+// workspace and the fp32 -s*(128+z) are each exact to ~2^-17 relative). Lane l supplies
+// row / channel l&15 and groups 32*gb + 8*(l>>4) .. +7 of block gb; groups past G are zero.
+// Workspace: per activation row, Gp = ceil(G/32)*32 bf16 high halves then Gp low halves
+// (group_sums_split_kernel).
+template <int MW, int NTW, bool MOE>
+__device__ __forceinline__ void wna16_offset_contraction(const KParams& p, const uint8_t* w,
+                                                         f32x4 (&acc)[MW][NTW], int row_base,
+                                                         int nt0, int lane) {
+  const int G = p.K / 128;
+  const int Gp = (G + 31) / 32 * 32;
+  const uint16_t* ssplit = reinterpret_cast<const uint16_t*>(p.ws);
+  const int h = lane >> 4;
+  int srow[MW];
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb) {
+    const int r = row_base + 16 * mb + (lane & 15);
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[r];
+      srow[mb] = id < p.M ? id / p.topk : 0;      // padding rows: any valid row, never stored
+    } else {
+      srow[mb] = min(r, p.M - 1);
+    }
+  }
+  for (int gb = 0; gb < Gp / 32; ++gb) {
+    u32x4 sh[MW], sl[MW];
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      const uint16_t* src = ssplit + size_t(srow[mb]) * 2 * Gp + 32 * gb + 8 * h;
+      sh[mb] = *reinterpret_cast<const u32x4*>(src);
+      sl[mb] = *reinterpret_cast<const u32x4*>(src + Gp);
+    }
+    float sc[NTW][8];
+    uint32_t zc[NTW][8];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int g = min(32 * gb + 8 * h + j, G - 1);
+        const size_t unit = size_t(nt0 + t) * p.k_units + g;
+        sc[t][j] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
+        zc[t][j] = p.asym ? uint32_t(w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)]) : 0x88u;
+      }
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t z = (lane & 1) ? (zc[t][j] >> 4) : (zc[t][j] & 0xFu);
+        const float b = (32 * gb + 8 * h + j < G) ? -sc[t][j] * float(128u + z) : 0.0f;
+        const uint32_t hi = f32_to_bf16_rne(b);
+        const uint32_t lo = f32_to_bf16_rne(b - __uint_as_float(hi << 16));
+        if (j & 1) {
+          bh[j >> 1] |= hi << 16;
+          bl[j >> 1] |= lo << 16;
+        } else {
+          bh[j >> 1] = hi;
+          bl[j >> 1] = lo;
+        }
+      }
+      const bf16x8 bhv = __builtin_bit_cast(bf16x8, u32x4{bh[0], bh[1], bh[2], bh[3]});
+      const bf16x8 blv = __builtin_bit_cast(bf16x8, u32x4{bl[0], bl[1], bl[2], bl[3]});
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        const bf16x8 shv = __builtin_bit_cast(bf16x8, sh[mb]);
+        acc[mb][t] = mfma_bf16(shv, bhv, acc[mb][t]);
+        acc[mb][t] = mfma_bf16(shv, blv, acc[mb][t]);
+        acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, sl[mb]), bhv, acc[mb][t]);
+      }
+    }
+  }
+}
+
+// ---- stores ------------------------------------------------------------------------------------
+// row_base: the wave's first row in the workgroup's row space (dense: m; MoE: position in
+// sorted_ids). No K split here (p.split == 1).
+template <int FAM, bool MOE, int MW, int NTW>
+__device__ __forceinline__ void store_tile(const KParams& p, const typename AccType<FAM>::type (&acc)[MW][NTW],
+                                           int row_base, int nt0, int lane) {
+  int orow[MW][4];     // output row, or -1 (not stored)
+  float rs[MW][4];     // per-token activation scale (1 for bf16 activations)
+  float tw[MW][4];     // router weight (1 for dense)
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row_base + 16 * mb + 4 * (lane >> 4) + i;
+      int o, s;
+      float wgt = 1.0f;
+      if constexpr (MOE) {
+        const int id = p.sorted_ids[r];
+        o = id < p.M ? id : -1;
+        s = id < p.M ? id / p.topk : 0;
+        if (p.topk_weights && o >= 0) wgt = p.topk_weights[id];
+      } else {
+        o = r < p.M ? r : -1;
+        s = r < p.M ? r : 0;
+      }
+      orow[mb][i] = o;
+      tw[mb][i] = wgt;
+      rs[mb][i] = (FAM != FAM_WNA16 && o >= 0) ? p.a_scale[s] : 1.0f;
+    }
+  float cs[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int n = (nt0 + t) * 16 + (lane & 15);
+    cs[t] = (FAM == FAM_W8A8 && !p.out_i32) ? reinterpret_cast<const float*>(p.w + p.scales_off)[n] : 1.0f;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = orow[mb][i];
+        if (o < 0) continue;
+        const size_t idx = size_t(o) * p.N + (nt0 + t) * 16 + (lane & 15);
+        const auto v = acc[mb][t][i];
+        if constexpr (FAM == FAM_WNA16) {
+          reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * tw[mb][i]);
+        } else if constexpr (FAM == FAM_W8A8) {
+          if (p.out_i32) reinterpret_cast<int*>(p.y)[idx] = v;
+          else reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(float(v) * rs[mb][i] * cs[t]);
+        } else {
+          reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * rs[mb][i] * tw[mb][i]);
+        }
+      }
+}
+
+}  // namespace hq
