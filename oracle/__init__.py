@@ -16,6 +16,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench
 import this package. It shares no code, table or helper with the HIP library and never imports
 it; both consume the seeded inputs of ``synth``.
 
+``actquant`` defines the per-token dynamic quantization of bf16 activations that precedes the
+W8A8 and W4A8 GEMMs.
+
 Pins (in ``tests/test_oracle_*.py``, CPU only): format decode tables against hand values and
 torch's own dtype casts, the zero-exponent/symmetric-integer equivalence stated in the section
 "Results: quantization support", hand-computed cases under ``tests/golden/``, a brute-force
@@ -29,3 +32,4 @@ from .gemm import (  # noqa: F401
     dequant_wna16, dequant_mxfp4, ref_wna16, ref_w8a8, ref_w4a8,
 )
 from .moe import ref_moe_align, ref_moe_gemm  # noqa: F401
+from .actquant import encode_e4m3, quantize_per_token  # noqa: F401

@@ -1,0 +1,69 @@
+"""Per-token dynamic activation quantization for the oracle (test infrastructure).
+
+The step just before the W8A8 and W4A8 GEMMs: bf16 activations become 8-bit codes plus one fp32
+scale per row (token). The Humming announcement lists per-token activation scales among the
+"input scale layout" compute options (section "Tuning and JIT compilation per workload") and
+credits tokenwise FP8 activations for its end-to-end gain (section "End-to-end performance")
+but fixes no rule; the plain reading used here is symmetric absmax scaling per row:
+
+    amax   = max_k |x[m, k]|                         (exact: bf16 values)
+    s[m]   = fp32(amax / Q), Q = 127 (INT8) or 448 (largest finite e4m3); s = 1 for an all-zero row
+    v      = fp32(x[m, k] / s[m])                   (one IEEE binary32 division, round to nearest even)
+    INT8   : q = clamp(round_half_even(v), -127, 127)
+    e4m3   : q = nearest finite e4m3 ("fn") code to clamp(v, -448, 448), ties to the even code;
+             a negative value that rounds to zero gives -0 (0x80)
+
+Both divisions are binary32 on purpose: the codes are integers decided by floating point, and
+the kernel takes that decision in binary32, so the reference takes it in the same precision
+(numpy float32 division is IEEE correctly rounded).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import decode_bf16, decode_e4m3
+
+_E4M3_FINITE = np.array([c for c in range(0x80) if not (c & 0x7F) == 0x7F], dtype=np.int64)
+_E4M3_VALUES = decode_e4m3(_E4M3_FINITE)          # non-negative finite magnitudes, ascending
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """Nearest finite OCP e4m3 code (uint8), ties to the even code, saturating at +-448.
+
+    Brute force over the 127 non-negative finite magnitudes: the lowest code at minimum distance
+    unless two codes tie, then the even one. The sign bit is copied from v (so -0.0 and negative
+    values that round to zero give 0x80).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 448.0)
+    d = np.abs(a[..., None] - _E4M3_VALUES)                     # [..., 127]
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    idx_lo = np.argmax(cand, axis=-1)                          # first (smaller) minimiser
+    two = cand.sum(axis=-1) > 1                                # a tie: two neighbours
+    lo_code = _E4M3_FINITE[idx_lo]
+    code = np.where(two & (lo_code % 2 == 1), _E4M3_FINITE[np.minimum(idx_lo + 1, len(_E4M3_FINITE) - 1)], lo_code)
+    sign = np.signbit(v).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def _row_scale(x: np.ndarray, q: float) -> np.ndarray:
+    amax = np.abs(x).max(axis=1).astype(np.float32)
+    s = (amax / np.float32(q)).astype(np.float32)
+    return np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_per_token(x_bf16: np.ndarray, act: str):
+    """x_bf16: uint16 bf16 bits [M, K]; act: "int8" or "e4m3". Returns (codes uint8/int8 [M, K],
+    scales float32 [M])."""
+    x = decode_bf16(x_bf16).astype(np.float32)                 # exact
+    if act == "int8":
+        s = _row_scale(x, 127.0)
+        v = (x / s[:, None]).astype(np.float32)                # binary32 division
+        q = np.clip(np.rint(v), -127, 127).astype(np.int8)     # rint = half to even
+        return q, s
+    if act == "e4m3":
+        s = _row_scale(x, 448.0)
+        v = (x / s[:, None]).astype(np.float32)
+        return encode_e4m3(np.clip(v, np.float32(-448.0), np.float32(448.0))), s
+    raise ValueError(act)
