@@ -10,8 +10,9 @@ Timing follows the Humming announcement's microbenchmark protocol (section "Resu
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
 caches): every launch reads a different copy of the weights, cycled through more than 3x the
 MI355X's 256 MB Infinity Cache, so weight bytes come from HBM. Each M point is a HIP graph of R
-back-to-back launches (so small launches are not separated by host gaps), replayed between HIP
-events on the stream it runs on; per-launch time = event time / R. One step replays every M
+back-to-back launches (so small launches are not separated by host gaps; R gives a replay of about
+0.5 ms, at most 32 launches), replayed between HIP events on the stream it runs on; per-launch
+time = event time / R. One step replays every M
 point's graph; `value` = (sum over the M points of one launch's flops) / (sum of the per-launch
 times), i.e. the sweep's throughput with each M point counted once.
 """
@@ -187,13 +188,24 @@ def run_dense(args, wl: str):
 
     # Launch-bound small calls would be timed with host gaps in between; so each M point is a HIP
     # graph of R back-to-back launches (consecutive launches read different weight copies), and
-    # the graph replay is bracketed by events on the capturing stream.
-    reps = {M: max(1, min(32, int(2e6 // max(M * N * K // 4096, 1)))) for M in Ms}
+    # the graph replay is bracketed by events on the capturing stream. R is chosen so that one
+    # replay holds about 0.5 ms of launches (from an eager estimate, an upper bound), which
+    # amortizes the replay's own start-up cost, between 1 and 32 launches.
     eager = {}
+    est = {}
     for M in Ms:
         launch(M, stream)
         torch.cuda.synchronize()
         eager[M] = outs[M].clone()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(3):
+            launch(M, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        est[M] = a.elapsed_time(b) * 1e3 / 3
+    reps = {M: max(1, min(32, int(np.ceil(500.0 / max(est[M], 1e-3))))) for M in Ms}
     graphs = {}
     for M in Ms:
         g = torch.cuda.CUDAGraph()
@@ -241,6 +253,32 @@ def run_dense(args, wl: str):
                       "frac": round(max(frac_c, frac_m), 4), "bytes": by, "flops": fl})
         tot_flops += fl
         tot_s += us * 1e-6
+    if wl in ("w8a8", "w4a8"):
+        # The step before these GEMMs (per-token quantization of bf16 activations), timed the same
+        # way for context; it is not part of `value`.
+        act = hq.HQ_ACT_INT8_PER_TOKEN if wl == "w8a8" else hq.HQ_ACT_FP8E4M3_PER_TOKEN
+        for row in sweep:
+            M = row["M"]
+            xb = torch.randn(M, K, device=dev).to(torch.bfloat16)
+            xq = torch.empty(M, K, dtype=torch.uint8, device=dev)
+            sq = torch.empty(M, dtype=torch.float32, device=dev)
+            r = 32
+            gq = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gq):
+                for _ in range(r):
+                    hq.hq_quantize_activations(act, M, K, xb, xq, sq)
+            gq.replay()
+            torch.cuda.synchronize()
+            qe = []
+            for _ in range(max(3, args.steps)):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                gq.replay()
+                b.record(stream)
+                qe.append((a, b))
+            torch.cuda.synchronize()
+            row["act_quant_us"] = round(float(np.mean([a.elapsed_time(b) for a, b in qe])) * 1e3 / r, 3)
     dom = max(sweep, key=lambda r: r["us"])
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS[spec["peak"]],

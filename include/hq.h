@@ -98,6 +98,25 @@ typedef struct {
  */
 
 /* ---------------------------------------------------------------------------------------------
+ * Per-token dynamic activation quantization (device), the step before the W8A8 and W4A8 GEMMs.
+ * The announcement's section "Tuning and JIT compilation per workload" lists per-token input
+ * scales among the compute options, and its section "End-to-end performance" credits tokenwise
+ * FP8 activations; the rule implemented is symmetric absmax scaling per row:
+ *   s_tok[m] = fp32(max_k |x[m,k]| / Q), Q = 127 (INT8) or 448 (e4m3); 1 for an all-zero row
+ *   v        = fp32(x[m,k] / s_tok[m])            (IEEE binary32 division)
+ *   INT8     : xq = clamp(round_half_even(v), -127, 127)
+ *   e4m3     : xq = nearest OCP e4m3 code to clamp(v, -448, 448), ties to the even code
+ *              (negative values that round to zero give -0, 0x80)
+ * act_fmt  HQ_ACT_INT8_PER_TOKEN or HQ_ACT_FP8E4M3_PER_TOKEN (the desc act_fmt of the GEMM)
+ * x        bf16 [M, K] row-major (device, 16-byte aligned); K % 8 == 0
+ * xq       int8 / e4m3 bytes [M, K] row-major (device, 16-byte aligned), the GEMM's `a`
+ * s_tok    fp32 [M] (device), the GEMM's `a_scale`
+ * Inputs with NaN or infinity give unspecified codes. M == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const void* x, void* xq,
+                                  float* s_tok, hq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Weight prepack (host).  Standard-format inputs, all host memory, row-major:
  *   wq      INT4/FP4: uint8 [E, N, K/2] (two codes per byte, low nibble = even k)
  *           INT8    : int8  [E, N, K]

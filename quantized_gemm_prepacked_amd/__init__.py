@@ -35,7 +35,8 @@ HQ_OUT_BF16, HQ_OUT_INT32_ACC = range(2)
 EXPORTED = (
     "hq_prepacked_bytes", "hq_prepack_weights", "hq_gemm_workspace_bytes", "hq_gemm",
     "hq_moe_align_capacity", "hq_moe_align_workspace_bytes", "hq_moe_align", "hq_moe_block_m",
-    "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_last_error", "hq_version",
+    "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_quantize_activations",
+    "hq_last_error", "hq_version",
 )
 
 
@@ -89,6 +90,7 @@ _c = {
     "hq_moe_gemm_workspace_bytes": _sig("hq_moe_gemm_workspace_bytes", _SZ, _D, _I64, _I32, _I32, _I64, _I64, _I32),
     "hq_moe_grouped_gemm": _sig("hq_moe_grouped_gemm", ctypes.c_int, _D, _I64, _I32, _I32, _I64, _I64, _P, _P, _P,
                                 _P, _P, _P, _I32, _P, _P, _P, _SZ, _P),
+    "hq_quantize_activations": _sig("hq_quantize_activations", ctypes.c_int, _I32, _I64, _I64, _P, _P, _P, _P),
     "hq_last_error": _sig("hq_last_error", ctypes.c_char_p),
     "hq_version": _sig("hq_version", _I32),
 }
@@ -189,3 +191,7 @@ def hq_moe_grouped_gemm(desc, T, topk, E, N, K, a, a_scale, w_packed, sorted_ids
                                      _ptr(w_packed), _ptr(sorted_ids), _ptr(block_expert),
                                      _ptr(num_padded), block_m, _ptr(topk_weights), _ptr(y),
                                      _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def hq_quantize_activations(act_fmt, M, K, x, xq, s_tok, stream=None):
+    _check(_c["hq_quantize_activations"](act_fmt, M, K, _ptr(x), _ptr(xq), _ptr(s_tok), _stream(stream)))

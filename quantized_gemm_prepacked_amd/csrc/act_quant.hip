@@ -1,0 +1,109 @@
+// act_quant.hip -- per-token dynamic quantization of bf16 activations for the W8A8 and W4A8
+// GEMMs: one fp32 scale per row and INT8 or OCP e4m3 codes.
+//
+// The Humming announcement lists per-token input scales among the compute options (section
+// "Tuning and JIT compilation per workload") and attributes its end-to-end gain to tokenwise FP8
+// activations (section "End-to-end performance"); the rule here is symmetric absmax scaling:
+//   s = fp32(max_k |x| / Q) (Q = 127 or 448; 1 for an all-zero row), v = fp32(x / s) (IEEE
+//   binary32 division), INT8 q = clamp(rne(v), -127, 127), e4m3 q = rne_e4m3(clamp(v, +-448)).
+// One workgroup per row: a pass for the row maximum (wave then LDS reduction), a pass that
+// re-reads the row (from cache) and writes 8 codes per lane per step.
+#include <hip/hip_runtime.h>
+
+#include "device_ops.h"
+#include "internal.h"
+
+namespace hq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// fp32 -> OCP e4m3 ("fn") code, round to nearest even, for |v| <= 448 (the caller clamps). The
+// sign is kept, so values that round to zero give +-0 (0x00 / 0x80).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {
+    // below 2^-6: subnormal codes m * 2^-9 (m = 8 is the smallest normal, code 0x08); the
+    // scaling by 2^9 is exact
+    code = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  } else {
+    // normal: exponent field (fp32 exponent + 7, 1..15) and the top three mantissa bits,
+    // rounded on the 20 dropped bits (a carry moves into the exponent)
+    const uint32_t e = (a >> 23) - 120u;
+    const uint32_t m = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    code = (e << 3) | m;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) code += 1u;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ xq,
+                                                             float* __restrict__ s_tok, int K) {
+  const int row = blockIdx.x;
+  const uint16_t* xr = x + size_t(row) * K;
+  uint8_t* qr = xq + size_t(row) * K;
+
+  float amax = 0.0f;
+  for (int i = threadIdx.x * 8; i < K; i += kThreads * 8) {
+    const u32x4 v = ldg16(xr + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  __shared__ float wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+
+  float s = amax / (ACT == HQ_ACT_INT8_PER_TOKEN ? 127.0f : 448.0f);
+  if (s == 0.0f) s = 1.0f;
+  if (threadIdx.x == 0) s_tok[row] = s;
+
+  for (int i = threadIdx.x * 8; i < K; i += kThreads * 8) {
+    const u32x4 v = ldg16(xr + i);
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t bits = (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
+      const float q = __uint_as_float(bits) / s;
+      uint32_t code;
+      if constexpr (ACT == HQ_ACT_INT8_PER_TOKEN) {
+        code = uint32_t(int(fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f))) & 0xFFu;
+      } else {
+        code = e4m3_rne(fminf(fmaxf(q, -448.0f), 448.0f));
+      }
+      out[j >> 2] |= code << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint2*>(qr + i) = make_uint2(out[0], out[1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, void* xq, float* s_tok,
+                            hipStream_t stream) {
+  const dim3 grid{static_cast<unsigned>(M)};
+  const auto* xin = static_cast<const uint16_t*>(x);
+  auto* out = static_cast<uint8_t*>(xq);
+  if (act_fmt == HQ_ACT_INT8_PER_TOKEN)
+    hipLaunchKernelGGL(act_quant_kernel<HQ_ACT_INT8_PER_TOKEN>, grid, dim3(kThreads), 0, stream, xin, out, s_tok, int(K));
+  else
+    hipLaunchKernelGGL(act_quant_kernel<HQ_ACT_FP8E4M3_PER_TOKEN>, grid, dim3(kThreads), 0, stream, xin, out, s_tok, int(K));
+  return hipGetLastError();
+}
+
+}  // namespace hq

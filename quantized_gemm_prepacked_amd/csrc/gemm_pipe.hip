@@ -32,19 +32,16 @@ template <>
 struct PipeTraits<FAM_WNA16> {
   static constexpr int kABytes = 2;
   static constexpr int kUnitsPerStep = 1;
-  static constexpr int kMetaPerTile = 32 + 8;  // 16 bf16 scales + 8 bytes of packed zeros
 };
 template <>
 struct PipeTraits<FAM_W8A8> {
   static constexpr int kABytes = 1;
   static constexpr int kUnitsPerStep = 2;
-  static constexpr int kMetaPerTile = 0;
 };
 template <>
 struct PipeTraits<FAM_W4A8> {
   static constexpr int kABytes = 1;
   static constexpr int kUnitsPerStep = 1;
-  static constexpr int kMetaPerTile = 64;      // 64 e8m0 bytes (one per lane)
 };
 
 __device__ __forceinline__ void block_barrier() {

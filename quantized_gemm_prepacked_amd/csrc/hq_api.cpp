@@ -207,6 +207,21 @@ hq_status hq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t
                    "hq_moe_align launch");
 }
 
+hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const void* x, void* xq,
+                                  float* s_tok, hq_stream_t stream) {
+  if (act_fmt != HQ_ACT_INT8_PER_TOKEN && act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN)
+    return fail(HQ_ERR_UNSUPPORTED, "act_fmt=%d: INT8 or FP8 e4m3 per-token only", act_fmt);
+  if (M < 0 || M > kMaxDim || K <= 0 || K > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "M=%lld K=%lld out of range", (long long)M, (long long)K);
+  if (K % 8 != 0) return fail(HQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 8", (long long)K);
+  if (M == 0) return ok();
+  if (!x || !xq || !s_tok) return fail(HQ_ERR_INVALID_ARGUMENT, "x, xq and s_tok must be non-NULL");
+  if (!aligned16(x) || !aligned16(xq) || (reinterpret_cast<uintptr_t>(s_tok) & 3u))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "x and xq must be 16-byte aligned, s_tok 4-byte aligned");
+  return check_hip(hq::launch_act_quant(act_fmt, M, K, x, xq, s_tok, static_cast<hipStream_t>(stream)),
+                   "hq_quantize_activations launch");
+}
+
 int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E, int64_t N,
                        int64_t K) {
   hq::Combo c{};

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "hq.h"
 #include "layout.h"
 
 namespace hq {
@@ -59,6 +60,8 @@ bool moe_block_m_supported(int32_t block_m);
 hipError_t launch_gemm(const GemmCall& call, const Plan& plan);
 
 size_t moe_align_ws_bytes(int64_t T, int32_t topk, int32_t E, int32_t block_m);
+hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, void* xq, float* s_tok,
+                            hipStream_t stream);
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
                             int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                             int32_t* expert_offsets, int32_t* num_padded, void* ws,
