@@ -75,3 +75,48 @@ def ref_moe_gemm(x_bf16: np.ndarray, topk_ids: np.ndarray, expert_weights, N: in
     valid = ~np.isnan(y[:, 0]) if n_cols else np.ones(flat.size, dtype=bool)
     bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
     return y, bits, valid
+
+
+def ref_silu_mul(gate_up_bf16: np.ndarray):
+    """Gated activation of the MoE expert MLP: for each routed row, the first half of the
+    gate_up output is the gate g, the second half the up projection u, and
+    act = silu(g) * u = g / (1 + exp(-g)) * u, evaluated in float64 on the bf16 inputs and
+    rounded once to bf16. Returns (act float64 [R, I], act bf16 bits)."""
+    gu = decode_bf16(gate_up_bf16)
+    I = gu.shape[1] // 2
+    g, u = gu[:, :I], gu[:, I:]
+    act = g / (1.0 + np.exp(-g)) * u
+    return act, round_to_bf16(act)
+
+
+def ref_moe_combine(y_bf16: np.ndarray, topk_ids: np.ndarray, E: int):
+    """Top-k combine: out[t, :] = sum over k of y[t*topk + k, :] for the k routed to an expert in
+    [0, E) (a row routed elsewhere has no output and is left out), float64 sum of the bf16 rows,
+    rounded once to bf16. The router weights were applied by the Down GEMM. Returns
+    (out float64 [T, N], out bf16 bits)."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, topk = ids.shape
+    y = decode_bf16(y_bf16).reshape(T, topk, -1)
+    valid = ((ids >= 0) & (ids < E))[:, :, None]
+    out = np.where(valid, y, 0.0).sum(axis=1)
+    return out, round_to_bf16(out)
+
+
+def ref_moe_layer(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
+                  gate_up_weights, down_weights, I: int, H: int, E: int, g: int):
+    """One MoE layer: per routed row (t, k) with expert e = topk_ids[t, k],
+        gu  = bf16(x[t] . Wgu_e^T)          (gate_up GEMM, N = 2I)
+        a   = bf16(silu(gu[:I]) * gu[I:])    (gated activation)
+        d   = bf16(w[t, k] * a . Wd_e^T)      (Down GEMM, N = H, router weight in its epilogue)
+        out[t] = bf16(sum_k d)                (top-k combine)
+    Each stage is exact float64 arithmetic on its bf16 inputs, rounded once to bf16 at the stage
+    boundary -- the tensors a layer hands on are bf16. Returns the bf16 bits of every stage
+    (gate_up [T*topk, 2I], act [T*topk, I], down [T*topk, H], out [T, H])."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, topk = ids.shape
+    _, gu_bits, _ = ref_moe_gemm(x_bf16, ids, gate_up_weights, 2 * I, E, g)
+    _, act_bits = ref_silu_mul(gu_bits)
+    _, d_bits, _ = ref_moe_gemm(act_bits, ids.reshape(-1, 1), down_weights, H, E, g,
+                                topk_weights=np.asarray(topk_weights).reshape(-1, 1))
+    _, out_bits = ref_moe_combine(d_bits, ids, E)
+    return {"gate_up": gu_bits, "act": act_bits, "down": d_bits, "out": out_bits}

@@ -1,0 +1,78 @@
+"""Pins of the oracle's MoE layer stages (gated activation, top-k combine, full layer), CPU only."""
+import math
+
+import numpy as np
+from scipy.special import expit
+
+import oracle
+from oracle.codecs import decode_bf16, round_to_bf16
+
+import synth
+
+
+def _bf16(v):
+    return synth.bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def test_silu_mul_hand_values():
+    # gate = [0, 1, -2, 4], up = [5, 2, 1, -0.5]
+    gu = _bf16([[0.0, 1.0, -2.0, 4.0, 5.0, 2.0, 1.0, -0.5]])
+    act, bits = oracle.ref_silu_mul(gu)
+    want = [0.0, 2.0 / (1 + math.exp(-1.0)), -2.0 / (1 + math.exp(2.0)), -0.5 * 4.0 / (1 + math.exp(-4.0))]
+    assert np.allclose(act[0], want, rtol=0, atol=1e-15)
+    assert bits.tolist() == [round_to_bf16(np.array(want)).tolist()]
+
+
+def test_silu_mul_against_expit():
+    g = synth.normal_bf16(synth.rng(5), (16, 64), std=3.0)
+    u = synth.normal_bf16(synth.rng(6), (16, 64))
+    act, _ = oracle.ref_silu_mul(np.concatenate([g, u], axis=1))
+    gv, uv = decode_bf16(g), decode_bf16(u)
+    assert np.allclose(act, gv * expit(gv) * uv, rtol=1e-14, atol=1e-300)
+
+
+def test_combine_hand_case_and_skipped_rows():
+    ids = np.array([[0, 3], [7, 1]])          # E = 4: expert 7 is out of range
+    y = _bf16([[1.0, 2.0], [0.5, -4.0], [100.0, 100.0], [0.25, 0.25]])
+    out, bits = oracle.ref_moe_combine(y, ids, 4)
+    assert out.tolist() == [[1.5, -2.0], [0.25, 0.25]]
+    assert bits.tolist() == _bf16([[1.5, -2.0], [0.25, 0.25]]).tolist()
+
+
+def _layer_brute(x_bits, ids, tw, gu_w, dn_w, I, H, E):
+    """Scalar loops over one routed row at a time, straight from the layer's definition."""
+    T, topk = ids.shape
+    x = decode_bf16(x_bits)
+    out = np.zeros((T, H))
+    for t in range(T):
+        acc = [0.0] * H
+        for k in range(topk):
+            e = int(ids[t, k])
+            if not 0 <= e < E:
+                continue
+            Wgu = oracle.dequant_wna16(gu_w[e]["wq"], gu_w[e]["scales"], None, 128)
+            Wd = oracle.dequant_wna16(dn_w[e]["wq"], dn_w[e]["scales"], None, 128)
+            gu = [sum(float(x[t, j]) * float(Wgu[n, j]) for j in range(x.shape[1])) for n in range(2 * I)]
+            gu = decode_bf16(round_to_bf16(np.array(gu)))
+            a = [gu[i] / (1.0 + math.exp(-gu[i])) * gu[I + i] for i in range(I)]
+            a = decode_bf16(round_to_bf16(np.array(a)))
+            w = float(np.float32(tw[t, k]))
+            d = [w * sum(a[i] * float(Wd[h, i]) for i in range(I)) for h in range(H)]
+            d = decode_bf16(round_to_bf16(np.array(d)))
+            acc = [acc[h] + d[h] for h in range(H)]
+        out[t] = acc
+    return round_to_bf16(out)
+
+
+def test_layer_matches_scalar_loops():
+    T, topk, E, H, I = 3, 2, 3, 128, 128
+    g = synth.rng(77)
+    gu_w = [synth.quantize_int4_sym(g.standard_normal((2 * I, H)).astype(np.float32) * np.float32(0.05), 128)
+            for _ in range(E)]
+    dn_w = [synth.quantize_int4_sym(g.standard_normal((H, I)).astype(np.float32) * np.float32(0.05), 128)
+            for _ in range(E)]
+    x = synth.normal_bf16(g, (T, H))
+    ids = np.array([[0, 2], [1, 5], [2, 2]])  # expert 5 is out of range; token 2 routes twice to 2
+    tw = np.array([[0.7, 0.3], [0.6, 0.4], [0.5, 0.5]], dtype=np.float32)
+    ref = oracle.ref_moe_layer(x, ids, tw, lambda e: gu_w[e], lambda e: dn_w[e], I, H, E, 128)
+    assert np.array_equal(ref["out"], _layer_brute(x, ids, tw, gu_w, dn_w, I, H, E))
