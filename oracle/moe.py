@@ -49,6 +49,12 @@ def ref_moe_align(topk_ids: np.ndarray, E: int, block_m: int):
     }
 
 
+def _values(a: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) decoded, or float64 values taken as they are (the exact chain)."""
+    a = np.asarray(a)
+    return decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
 def ref_moe_gemm(x_bf16: np.ndarray, topk_ids: np.ndarray, expert_weights, N: int, E: int,
                  g: int, topk_weights: np.ndarray | None = None, rows=None, cols=None):
     """Grouped WNA16 GEMM over routed rows. ``expert_weights(e)`` returns the standard-format
@@ -58,7 +64,7 @@ def ref_moe_gemm(x_bf16: np.ndarray, topk_ids: np.ndarray, expert_weights, N: in
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, topk = ids.shape
     flat = np.arange(T * topk) if rows is None else np.asarray(rows, dtype=np.int64)
-    x = decode_bf16(x_bf16)
+    x = _values(x_bf16)
     n_cols = N if cols is None else len(cols)
     y = np.full((flat.size, n_cols), np.nan, dtype=np.float64)
     experts = ids.reshape(-1)[flat]
@@ -82,7 +88,7 @@ def ref_silu_mul(gate_up_bf16: np.ndarray):
     gate_up output is the gate g, the second half the up projection u, and
     act = silu(g) * u = g / (1 + exp(-g)) * u, evaluated in float64 on the bf16 inputs and
     rounded once to bf16. Returns (act float64 [R, I], act bf16 bits)."""
-    gu = decode_bf16(gate_up_bf16)
+    gu = _values(gate_up_bf16)
     I = gu.shape[1] // 2
     g, u = gu[:, :I], gu[:, I:]
     act = g / (1.0 + np.exp(-g)) * u
@@ -96,14 +102,14 @@ def ref_moe_combine(y_bf16: np.ndarray, topk_ids: np.ndarray, E: int):
     (out float64 [T, N], out bf16 bits)."""
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, topk = ids.shape
-    y = decode_bf16(y_bf16).reshape(T, topk, -1)
+    y = _values(y_bf16).reshape(T, topk, -1)
     valid = ((ids >= 0) & (ids < E))[:, :, None]
     out = np.where(valid, y, 0.0).sum(axis=1)
     return out, round_to_bf16(out)
 
 
 def ref_moe_layer(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
-                  gate_up_weights, down_weights, I: int, H: int, E: int, g: int):
+                  gate_up_weights, down_weights, I: int, H: int, E: int, g: int, exact: bool = False):
     """One MoE layer: per routed row (t, k) with expert e = topk_ids[t, k],
         gu  = bf16(x[t] . Wgu_e^T)          (gate_up GEMM, N = 2I)
         a   = bf16(silu(gu[:I]) * gu[I:])    (gated activation)
@@ -111,12 +117,17 @@ def ref_moe_layer(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_weights: np.nda
         out[t] = bf16(sum_k d)                (top-k combine)
     Each stage is exact float64 arithmetic on its bf16 inputs, rounded once to bf16 at the stage
     boundary -- the tensors a layer hands on are bf16. Returns the bf16 bits of every stage
-    (gate_up [T*topk, 2I], act [T*topk, I], down [T*topk, H], out [T, H])."""
+    (gate_up [T*topk, 2I], act [T*topk, I], down [T*topk, H], out [T, H]).
+
+    exact=True keeps every stage boundary in float64 instead (the same chain with no rounding;
+    rows routed nowhere are 0) and returns float64 values: the distance between the two chains
+    is the rounding noise that the bf16 boundaries alone put into the layer."""
     ids = np.asarray(topk_ids, dtype=np.int64)
     T, topk = ids.shape
-    _, gu_bits, _ = ref_moe_gemm(x_bf16, ids, gate_up_weights, 2 * I, E, g)
-    _, act_bits = ref_silu_mul(gu_bits)
-    _, d_bits, _ = ref_moe_gemm(act_bits, ids.reshape(-1, 1), down_weights, H, E, g,
-                                topk_weights=np.asarray(topk_weights).reshape(-1, 1))
-    _, out_bits = ref_moe_combine(d_bits, ids, E)
-    return {"gate_up": gu_bits, "act": act_bits, "down": d_bits, "out": out_bits}
+    pick = (lambda r: np.nan_to_num(r[0], nan=0.0)) if exact else (lambda r: r[1])
+    gu = pick(ref_moe_gemm(x_bf16, ids, gate_up_weights, 2 * I, E, g))
+    act = pick(ref_silu_mul(gu))
+    d = pick(ref_moe_gemm(act, ids.reshape(-1, 1), down_weights, H, E, g,
+                          topk_weights=np.asarray(topk_weights).reshape(-1, 1)))
+    out = pick(ref_moe_combine(d, ids, E))
+    return {"gate_up": gu, "act": act, "down": d, "out": out}

@@ -39,8 +39,10 @@ def test_combine_hand_case_and_skipped_rows():
     assert bits.tolist() == _bf16([[1.5, -2.0], [0.25, 0.25]]).tolist()
 
 
-def _layer_brute(x_bits, ids, tw, gu_w, dn_w, I, H, E):
-    """Scalar loops over one routed row at a time, straight from the layer's definition."""
+def _layer_brute(x_bits, ids, tw, gu_w, dn_w, I, H, E, rounded=True):
+    """Scalar loops over one routed row at a time, straight from the layer's definition
+    (rounded=False: no bf16 rounding between the stages)."""
+    rnd = (lambda v: decode_bf16(round_to_bf16(np.array(v)))) if rounded else (lambda v: np.array(v))
     T, topk = ids.shape
     x = decode_bf16(x_bits)
     out = np.zeros((T, H))
@@ -53,15 +55,15 @@ def _layer_brute(x_bits, ids, tw, gu_w, dn_w, I, H, E):
             Wgu = oracle.dequant_wna16(gu_w[e]["wq"], gu_w[e]["scales"], None, 128)
             Wd = oracle.dequant_wna16(dn_w[e]["wq"], dn_w[e]["scales"], None, 128)
             gu = [sum(float(x[t, j]) * float(Wgu[n, j]) for j in range(x.shape[1])) for n in range(2 * I)]
-            gu = decode_bf16(round_to_bf16(np.array(gu)))
+            gu = rnd(gu)
             a = [gu[i] / (1.0 + math.exp(-gu[i])) * gu[I + i] for i in range(I)]
-            a = decode_bf16(round_to_bf16(np.array(a)))
+            a = rnd(a)
             w = float(np.float32(tw[t, k]))
             d = [w * sum(a[i] * float(Wd[h, i]) for i in range(I)) for h in range(H)]
-            d = decode_bf16(round_to_bf16(np.array(d)))
+            d = rnd(d)
             acc = [acc[h] + d[h] for h in range(H)]
         out[t] = acc
-    return round_to_bf16(out)
+    return round_to_bf16(out) if rounded else out
 
 
 def test_layer_matches_scalar_loops():
@@ -76,3 +78,8 @@ def test_layer_matches_scalar_loops():
     tw = np.array([[0.7, 0.3], [0.6, 0.4], [0.5, 0.5]], dtype=np.float32)
     ref = oracle.ref_moe_layer(x, ids, tw, lambda e: gu_w[e], lambda e: dn_w[e], I, H, E, 128)
     assert np.array_equal(ref["out"], _layer_brute(x, ids, tw, gu_w, dn_w, I, H, E))
+    exact = oracle.ref_moe_layer(x, ids, tw, lambda e: gu_w[e], lambda e: dn_w[e], I, H, E, 128, exact=True)
+    brute = _layer_brute(x, ids, tw, gu_w, dn_w, I, H, E, rounded=False)
+    assert np.allclose(exact["out"], brute, rtol=1e-12, atol=1e-12 * np.abs(brute).max())
+    # the bf16 boundaries move the result by rounding noise only: a few bf16 ulps at most
+    assert np.abs(decode_bf16(ref["out"]) - exact["out"]).max() <= 2.0 ** -5 * np.abs(exact["out"]).max()
