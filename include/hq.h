@@ -209,6 +209,31 @@ const char* hq_last_error(void);
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int32_t hq_version(void);
 
+/* ---------------------------------------------------------------------------------------------
+ * MoE layer stages around the two grouped GEMMs (device). The announcement's section "Results:
+ * kernel microbenchmarks" times MoE as gate_up plus Down; a full layer for T tokens is
+ *   hq_moe_align(topk_ids, T, topk, E, block_m, ...)
+ *   hq_moe_grouped_gemm(desc, T, topk, E, 2I, H, x [T, H], ...)           -> gate_up [T*topk, 2I]
+ *   hq_moe_silu_mul(T*topk, I, gate_up, act)                              -> act     [T*topk, I]
+ *   hq_moe_grouped_gemm(desc, T*topk, 1, E, H, I, act, ..., same sorted_ids / block_expert /
+ *                       num_padded / block_m, topk_weights [T*topk])      -> down    [T*topk, H]
+ *   hq_moe_combine(T, topk, E, H, topk_ids, down, out)                    -> out     [T, H]
+ * The Down call treats every routed row as its own token (topk = 1): the alignment's flat ids
+ * t*topk + k then index `act` rows directly, and the router weight of each row is applied in the
+ * Down GEMM's epilogue.
+ *
+ * hq_moe_silu_mul: act[r, i] = bf16(silu(g) * u), g = gate_up[r, i], u = gate_up[r, I + i],
+ *   silu(g) = g / (1 + exp(-g)) = g * e / (1 + e) with e = exp(g) for g < 0, fp32 arithmetic. gate_up bf16 [R, 2I], act bf16 [R, I], both
+ *   16-byte aligned; I % 8 == 0. Rows that no GEMM wrote (ids outside [0, E)) give unspecified
+ *   values that the later stages never read.
+ * hq_moe_combine: out[t, n] = bf16(sum_k y[t*topk + k, n]) over the k with topk_ids[t, k] in
+ *   [0, E), summed in fp32 in k order; a token with no valid k gets zeros. y bf16 [T*topk, N],
+ *   out bf16 [T, N], 16-byte aligned; N % 8 == 0; topk_ids int32 [T, topk] (device).
+ * ------------------------------------------------------------------------------------------- */
+hq_status hq_moe_silu_mul(int64_t R, int64_t I, const void* gate_up, void* act, hq_stream_t stream);
+hq_status hq_moe_combine(int64_t T, int32_t topk, int32_t E, int64_t N, const int32_t* topk_ids,
+                         const void* y, void* out, hq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ EXPORTED = (
     "hq_prepacked_bytes", "hq_prepack_weights", "hq_gemm_workspace_bytes", "hq_gemm",
     "hq_moe_align_capacity", "hq_moe_align_workspace_bytes", "hq_moe_align", "hq_moe_block_m",
     "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_quantize_activations",
-    "hq_last_error", "hq_version",
+    "hq_moe_silu_mul", "hq_moe_combine", "hq_last_error", "hq_version",
 )
 
 
@@ -91,6 +91,8 @@ _c = {
     "hq_moe_grouped_gemm": _sig("hq_moe_grouped_gemm", ctypes.c_int, _D, _I64, _I32, _I32, _I64, _I64, _P, _P, _P,
                                 _P, _P, _P, _I32, _P, _P, _P, _SZ, _P),
     "hq_quantize_activations": _sig("hq_quantize_activations", ctypes.c_int, _I32, _I64, _I64, _P, _P, _P, _P),
+    "hq_moe_silu_mul": _sig("hq_moe_silu_mul", ctypes.c_int, _I64, _I64, _P, _P, _P),
+    "hq_moe_combine": _sig("hq_moe_combine", ctypes.c_int, _I64, _I32, _I32, _I64, _P, _P, _P, _P),
     "hq_last_error": _sig("hq_last_error", ctypes.c_char_p),
     "hq_version": _sig("hq_version", _I32),
 }
@@ -195,3 +197,11 @@ def hq_moe_grouped_gemm(desc, T, topk, E, N, K, a, a_scale, w_packed, sorted_ids
 
 def hq_quantize_activations(act_fmt, M, K, x, xq, s_tok, stream=None):
     _check(_c["hq_quantize_activations"](act_fmt, M, K, _ptr(x), _ptr(xq), _ptr(s_tok), _stream(stream)))
+
+
+def hq_moe_silu_mul(R, I, gate_up, act, stream=None):
+    _check(_c["hq_moe_silu_mul"](R, I, _ptr(gate_up), _ptr(act), _stream(stream)))
+
+
+def hq_moe_combine(T, topk, E, N, topk_ids, y, out, stream=None):
+    _check(_c["hq_moe_combine"](T, topk, E, N, _ptr(topk_ids), _ptr(y), _ptr(out), _stream(stream)))

@@ -222,6 +222,33 @@ hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const v
                    "hq_quantize_activations launch");
 }
 
+hq_status hq_moe_silu_mul(int64_t R, int64_t I, const void* gate_up, void* act, hq_stream_t stream) {
+  if (R < 0 || R > kMaxDim || I <= 0 || I > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld I=%lld out of range", (long long)R, (long long)I);
+  if (I % 8 != 0) return fail(HQ_ERR_UNSUPPORTED, "I=%lld must be a multiple of 8", (long long)I);
+  if (R * I > (int64_t(1) << 40)) return fail(HQ_ERR_UNSUPPORTED, "R*I must stay below 2^40");
+  if (R == 0) return ok();
+  if (!gate_up || !act) return fail(HQ_ERR_INVALID_ARGUMENT, "gate_up and act must be non-NULL");
+  if (!aligned16(gate_up) || !aligned16(act))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "gate_up and act must be 16-byte aligned");
+  return check_hip(hq::launch_silu_mul(R, I, gate_up, act, static_cast<hipStream_t>(stream)),
+                   "hq_moe_silu_mul launch");
+}
+
+hq_status hq_moe_combine(int64_t T, int32_t topk, int32_t E, int64_t N, const int32_t* topk_ids,
+                         const void* y, void* out, hq_stream_t stream) {
+  if (T < 0 || T > kMaxDim || topk <= 0 || topk > 64 || E <= 0 || N <= 0 || N > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld topk=%d E=%d N=%lld out of range", (long long)T, topk, E,
+                (long long)N);
+  if (N % 8 != 0) return fail(HQ_ERR_UNSUPPORTED, "N=%lld must be a multiple of 8", (long long)N);
+  if (T * N > (int64_t(1) << 40)) return fail(HQ_ERR_UNSUPPORTED, "T*N must stay below 2^40");
+  if (T == 0) return ok();
+  if (!topk_ids || !y || !out) return fail(HQ_ERR_INVALID_ARGUMENT, "topk_ids, y and out must be non-NULL");
+  if (!aligned16(y) || !aligned16(out)) return fail(HQ_ERR_INVALID_ARGUMENT, "y and out must be 16-byte aligned");
+  return check_hip(hq::launch_moe_combine(T, topk, E, N, topk_ids, y, out, static_cast<hipStream_t>(stream)),
+                   "hq_moe_combine launch");
+}
+
 int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32_t E, int64_t N,
                        int64_t K) {
   hq::Combo c{};
