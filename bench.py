@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | moe.
+--config w8a8 | w4a8 | moe | moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -460,12 +460,199 @@ def run_moe(args):
     return line
 
 
+MOE_LAYER = dict(name="MoE layer W4A16 (DeepSeek-V3-shaped: gate_up, SiLU*mul, Down, top-k combine)",
+                 E=256, topk=8, H=7168, I=2048, Ts=[1, 32, 512, 4096], cfg=5)
+
+
+def run_moe_layer(args):
+    """One MoE layer per T: token sort -> gate_up grouped GEMM [T*8, 4096] -> SiLU*mul ->
+    Down grouped GEMM [T*8, 7168] with router weights -> top-k combine. The Humming
+    announcement times MoE as gate_up plus Down (section "Results: kernel microbenchmarks").
+    tokens/s = T / (one layer's time); each stage is also timed on its own."""
+    import numpy as np
+    import torch
+
+    import quantized_gemm_prepacked_amd as hq
+    import synth
+
+    E, topk, H, I, Ts, cfg = (MOE_LAYER[k] for k in ("E", "topk", "H", "I", "Ts", "cfg"))
+    dev = torch.device("cuda:0")
+    desc = hq.DESC_W4A16_SYM
+    n_copies = 4                      # > 256 MB Infinity Cache between reuses even at T = 1
+    g = synth.rng(cfg, 0)
+    std = {}
+
+    def experts(N, K, tag):
+        stride = hq.hq_prepacked_bytes(desc, 1, N, K)
+        w0 = torch.empty(stride * E, dtype=torch.uint8, device=dev)
+        host = np.zeros(stride, np.uint8)
+        for e in range(E):
+            d = synth.random_int4_sym_expert(g, N, K)
+            if e < 16:
+                std[(tag, e)] = d
+            hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, host)
+            w0[e * stride:(e + 1) * stride].copy_(torch.from_numpy(host))
+        return [w0] + [w0.clone() for _ in range(n_copies - 1)], stride
+
+    log(f"[bench] {MOE_LAYER['name']}: preparing {E} gate_up and {E} Down experts (random INT4 codes)")
+    w_gu, st_gu = experts(2 * I, H, "gu")
+    log("[bench] gate_up experts ready")
+    w_dn, st_dn = experts(H, I, "dn")
+    log("[bench] Down experts ready")
+    state = {}
+    for T in Ts:
+        inp = synth.make_moe_inputs(cfg, T, H, E, topk)
+        R = T * topk
+        bm = hq.hq_moe_block_m(desc, T, topk, E, 2 * I, H)
+        cap = hq.hq_moe_align_capacity(T, topk, E, bm)
+        hist = np.bincount(inp["topk_ids"].reshape(-1), minlength=E)
+        ws1 = hq.hq_moe_gemm_workspace_bytes(desc, T, topk, E, 2 * I, H, bm)
+        ws2 = hq.hq_moe_gemm_workspace_bytes(desc, R, 1, E, H, I, bm)
+        state[T] = dict(
+            x=torch.from_numpy(inp["x"].view(np.int16)).to(dev),
+            ids=torch.from_numpy(inp["topk_ids"]).to(dev),
+            tw=torch.from_numpy(inp["topk_weights"].reshape(-1).astype(np.float32)).to(dev), bm=bm,
+            sorted=torch.empty(cap, dtype=torch.int32, device=dev),
+            bexp=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
+            offs=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            npad=torch.empty(1, dtype=torch.int32, device=dev),
+            gu=torch.empty((R, 2 * I), dtype=torch.int16, device=dev),
+            act=torch.empty((R, I), dtype=torch.int16, device=dev),
+            dn=torch.empty((R, H), dtype=torch.int16, device=dev),
+            out=torch.empty((T, H), dtype=torch.int16, device=dev),
+            ws1=ws1, ws2=ws2, ws=torch.empty(max(ws1, ws2, 16), dtype=torch.uint8, device=dev),
+            active=int((hist > 0).sum()), inp=inp)
+    stream = torch.cuda.current_stream()
+    ctr = [0, 0]
+
+    def align(T):
+        s = state[T]
+        hq.hq_moe_align(s["ids"], T, topk, E, s["bm"], s["sorted"], s["bexp"], s["offs"], s["npad"],
+                        None, 0, None)
+
+    def gate_up(T):
+        s = state[T]
+        w = w_gu[ctr[0] % n_copies]
+        ctr[0] += 1
+        hq.hq_moe_grouped_gemm(desc, T, topk, E, 2 * I, H, s["x"], None, w, s["sorted"], s["bexp"],
+                               s["npad"], s["bm"], None, s["gu"], s["ws"], s["ws1"], None)
+
+    def silu(T):
+        s = state[T]
+        hq.hq_moe_silu_mul(T * topk, I, s["gu"], s["act"], None)
+
+    def down(T):
+        s = state[T]
+        w = w_dn[ctr[1] % n_copies]
+        ctr[1] += 1
+        hq.hq_moe_grouped_gemm(desc, T * topk, 1, E, H, I, s["act"], None, w, s["sorted"], s["bexp"],
+                               s["npad"], s["bm"], s["tw"], s["dn"], s["ws"], s["ws2"], None)
+
+    def combine(T):
+        s = state[T]
+        hq.hq_moe_combine(T, topk, E, H, s["ids"], s["dn"], s["out"], None)
+
+    stages = {"align": align, "gate_up": gate_up, "silu_mul": silu, "down": down, "combine": combine}
+
+    def layer(T):
+        for f in stages.values():
+            f(T)
+
+    # HIP graphs of R back-to-back layers per T (the whole layer), and of R launches per stage
+    reps = {T: max(1, min(16, int(4e5 // max(T, 1)))) for T in Ts}
+    for T in Ts:
+        layer(T)
+    torch.cuda.synchronize()
+    graphs = {}
+    for T in Ts:
+        for name, f in [("layer", layer)] + list(stages.items()):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(reps[T]):
+                    f(T)
+            graphs[(T, name)] = gr
+    names = ["layer"] + list(stages)
+    for _ in range(args.warmup):
+        for gr in graphs.values():
+            gr.replay()
+    torch.cuda.synchronize()
+    rec = {k: [] for k in graphs}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for T in Ts:
+            for name in names:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                graphs[(T, name)].replay()
+                b.record(stream)
+                rec[(T, name)].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sweep, tot_t, tot_tok = [], 0.0, 0
+    for T in Ts:
+        us = {n: float(np.mean([a.elapsed_time(b) for a, b in rec[(T, n)]])) * 1e3 / reps[T] for n in names}
+        s = state[T]
+        R = T * topk
+        pt = {}
+        for n, (N, K, st) in (("gate_up", (2 * I, H, st_gu)), ("down", (H, I, st_dn))):
+            fl = 2.0 * R * N * K
+            by = s["active"] * st + R * K * 2 + R * N * 2
+            tf, gbs = fl / (us[n] * 1e-6) / 1e12, by / (us[n] * 1e-6) / 1e9
+            fc, fm = tf / PEAK_TFLOPS["bf16"], gbs / HBM_PEAK_GBS
+            pt[n] = {"us": round(us[n], 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
+                     "bound": "hbm" if fm >= fc else "mfma", "frac": round(max(fc, fm), 4)}
+        sweep.append({"T": T, "launches_per_graph": reps[T], "block_m": s["bm"], "active_experts": s["active"],
+                      "layer_us": round(us["layer"], 3),
+                      "stage_us": {n: round(us[n], 3) for n in stages},
+                      "tokens_per_s": round(T / (us["layer"] * 1e-6), 1), "gemms": pt})
+        tot_t += us["layer"] * 1e-6
+        tot_tok += T
+    dom_T, dom_n = max(((r["T"], n) for r in sweep for n in ("gate_up", "down")),
+                       key=lambda k: next(r for r in sweep if r["T"] == k[0])["gemms"][k[1]]["us"])
+    d = next(r for r in sweep if r["T"] == dom_T)["gemms"][dom_n]
+    if d["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(d["tflops"] / PEAK_TFLOPS["bf16"], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(d["gbps"] / HBM_PEAK_GBS, 4)}
+    roof.update(traffic=measured_traffic("moe_layer", f"{dom_n} T={dom_T}"), kernel=f"{dom_n} grouped GEMM T={dom_T}")
+    line = {
+        "metric": METRIC, "value": round(tot_tok / tot_t, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": MOE_LAYER["name"], "E": E, "topk": topk, "H": H, "I": I, "T": Ts,
+                   "routing": "N(0,1) logits + Zipf(1.1) log-prior, softmax top-8"},
+        "roofline": roof, "sweep": sweep, "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        inp = state[1]["inp"]
+        ids = inp["topk_ids"]
+        need = sorted(int(e) for e in np.unique(ids))
+        rg = synth.rng(cfg, 0)
+        gu_w, dn_w = {}, {}
+        for tag, (N, K), dst in (("gu", (2 * I, H), gu_w), ("dn", (H, I), dn_w)):
+            for e in range(E):           # regenerate the same random experts in order
+                dd = synth.random_int4_sym_expert(rg, N, K)
+                if e in need:
+                    dst[e] = dd
+        t0 = time.perf_counter()
+        oracle.ref_moe_layer(inp["x"], ids, inp["topk_weights"], lambda e: gu_w[e], lambda e: dn_w[e],
+                             I, H, E, 128)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(),
+                                "kind": "oracle", "sample": f"T=1 ({len(need)} experts), {dt:.1f} s"}
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe"])
+    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -474,6 +661,8 @@ def main():
         sys.exit(2)
     if args.config == "moe":
         line = run_moe(args)
+    elif args.config == "moe_layer":
+        line = run_moe_layer(args)
     else:
         line = run_dense(args, args.config)
     print(json.dumps(line), flush=True)

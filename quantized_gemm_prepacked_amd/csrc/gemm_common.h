@@ -118,8 +118,8 @@ struct PPCfg {
 };
 const PPCfg* pp_configs(int* count);
 int pp_lds_bytes(int fam, int cfg);
-hipError_t launch_pingpong(const KParams& p, int fam, int cfg, dim3 grid, int tiles_m, int tiles_n,
-                           hipStream_t s);
+hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
+                           int tiles_n, hipStream_t s);
 // WNA16 group sums for the LDS-staged kernels' offset term: per row, Gp = ceil(K/128 / 32) * 32
 // bf16 high halves then Gp low halves.
 size_t group_sums_split_bytes(int64_t rows, int64_t K);

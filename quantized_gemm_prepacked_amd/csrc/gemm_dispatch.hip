@@ -261,6 +261,41 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   Plan pl{};
   pl.split = 1;
   pl.ws_bytes = 0;
+  // Sweep override (HQ_TUNE="kind=3,cfg=<i>"): a ping-pong configuration whose tile rows equal
+  // block_m; one that does not fit is refused (kind -1).
+  const TuneOverride tov = tune_override();
+  if (tov.kind == 3) {
+    int n_p = 0;
+    const PPCfg* pc = pp_configs(&n_p);
+    const bool fits = tov.cfg >= 0 && tov.cfg < n_p && 16 * pc[tov.cfg].mw * pc[tov.cfg].wm == block_m &&
+                      K % 128 == 0 && N % (16 * pc[tov.cfg].ntw * pc[tov.cfg].wn) == 0 &&
+                      pp_lds_bytes(c.fam, tov.cfg) <= 160 * 1024 && uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);
+    pl.kind = fits ? 3 : -1;
+    pl.cfg = tov.cfg;
+    pl.ws_bytes = group_sums_split_bytes(T, K);
+    return pl;
+  }
+  // Blocks of 32 and 64 rows: the ping-pong kernel with one expert block per tile row, its
+  // widest tile that divides N (measured on MI355X at the DeepSeek-V3 gate_up and Down shapes,
+  // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
+  // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
+  const bool a32 = uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);   // 32-bit row offsets
+  if (c.fam == FAM_WNA16 && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+    static const int pp32[1] = {7}, pp64[2] = {5, 4};
+    const int* cands = block_m == 32 ? pp32 : pp64;
+    const int n_c = block_m == 32 ? 1 : 2;
+    int n_p = 0;
+    const PPCfg* pc = pp_configs(&n_p);
+    for (int j = 0; j < n_c; ++j) {
+      const PPCfg& t = pc[cands[j]];
+      if (N % (16 * t.ntw * t.wn) == 0 && pp_lds_bytes(c.fam, cands[j]) <= 160 * 1024) {
+        pl.kind = 3;
+        pl.cfg = cands[j];
+        pl.ws_bytes = group_sums_split_bytes(T, K);  // per-token activation group sums
+        return pl;
+      }
+    }
+  }
   if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
     pl.kind = 1;       // LDS-tiled, 64 x 128 tiles: one expert block per tile row
     pl.cfg = 3;
@@ -287,10 +322,14 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
 
 bool moe_block_m_supported(int32_t block_m) { return block_m == 16 || block_m == 32 || block_m == 64; }
 
+// Measured on MI355X (gate_up 4096 x 7168 and Down 7168 x 2048, 256 experts, top-8, skewed
+// routing): 16-row blocks below 2 routed rows per expert, 32-row blocks (ping-pong 32 x 256)
+// from 2, 64-row blocks (ping-pong 64 x 512) from 32 -- the two tie at 16 rows per expert and the
+// wider tile wins by ~11% at 64, where the padding of the small experts costs less than it gains.
 int32_t moe_block_m(const Combo&, int64_t T, int32_t topk, int32_t E, int64_t, int64_t) {
   const double rows_per_expert = double(T) * topk / std::max(1, E);
-  if (rows_per_expert <= 16) return 16;
-  if (rows_per_expert <= 64) return 32;
+  if (rows_per_expert < 2) return 16;
+  if (rows_per_expert < 32) return 32;
   return 64;
 }
 
@@ -325,7 +364,29 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     }
     const int tiles_n = int(call.N / bn);
     const int tiles_m = int((call.M + bm - 1) / bm);
-    return launch_pingpong(p, c.fam, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n, call.stream);
+    return launch_pingpong(p, c.fam, false, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n,
+                           call.stream);
+  }
+  if (plan.kind == 3) {   // MoE: one workgroup row of tiles per block of the token sort
+    int n_cfg = 0;
+    const PPCfg& pc = pp_configs(&n_cfg)[plan.cfg];
+    const int bm = 16 * pc.mw * pc.wm, bn = 16 * pc.ntw * pc.wn;
+    if (bm != call.block_m) return hipErrorInvalidValue;
+    p.split = 1;
+    p.units_per_split = p.k_units;
+    p.M = int(call.T * call.topk);
+    p.sorted_ids = call.sorted_ids;
+    p.block_expert = call.block_expert;
+    p.num_padded = call.num_padded;
+    p.topk_weights = call.topk_weights;
+    p.topk = call.topk;
+    p.E = call.E;
+    hipError_t e = launch_group_sums_split(p.a, int(call.T), p.K, call.ws, call.stream);
+    if (e != hipSuccess) return e;
+    const int tiles_n = int(call.N / bn);
+    const int tiles_m = int(call.max_blocks);
+    return launch_pingpong(p, c.fam, true, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n,
+                           call.stream);
   }
   if (plan.kind == 1 || plan.kind == 2) {
     int n_cfg = 0;

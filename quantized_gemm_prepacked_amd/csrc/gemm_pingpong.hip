@@ -15,6 +15,11 @@
 //     its memory phase of step s, so a copy has about three phases to land.
 // WNA16 keeps the offset-128 operand of the other kernels; the offset term is removed at the end
 // (tile_epilogue.h).
+//
+// MoE grouped GEMM (WNA16): a workgroup's BM rows are one block of the token sort's output, all
+// routed to one expert (block_m == BM); the rows are gathered through sorted_ids (token =
+// id / topk), the expert's weights are read at its stride, and the stores scatter to the flat ids
+// with the router weight. Blocks past the sorted rows carry expert -1 and exit at once.
 #include <hip/hip_runtime.h>
 
 #include <utility>
@@ -79,14 +84,16 @@ struct PPShape {
   static constexpr int A_INSTR = A_BYTES / 1024 / 8;
   static constexpr int B_INSTR = NT * UPS / 8;
   static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0);
-  static_assert(A_BYTES % (1024 * 8) == 0, "activation tile must split into wave loads");
-  static_assert((NT * UPS) % 8 == 0, "weight units must split over the waves");
-  static_assert(META_BYTES % (16 * 8) == 0 && META_LANES <= 64, "metadata split over the waves");
+  // the copies split evenly over the eight waves (shapes that do not are never launched)
+  static constexpr bool kValid = A_BYTES % (1024 * 8) == 0 && (NT * UPS) % 8 == 0 &&
+                                 META_BYTES % (16 * 8) == 0 && META_LANES <= 64;
+  static constexpr int LDS_OR_NONE = kValid ? LDS : 1 << 30;
 };
 
-template <int FAM, int MW, int NTW, int WM, int WN>
+template <int FAM, bool MOE, int MW, int NTW, int WM, int WN>
 __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
   using Sh = PPShape<FAM, MW, NTW, WM, WN>;
+  static_assert(Sh::kValid, "copies must split over the eight waves");
   using Acc = typename AccType<FAM>::type;
   constexpr int BM = Sh::BM, RB = Sh::RB, CPR = Sh::CPR, NT = Sh::NT, UPS = Sh::UPS;
   constexpr int S = Sh::kStages;
@@ -99,22 +106,37 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   const int wm = wave / WN;
   const int wn = wave % WN;
 
-  // XCD-aware tile order (blocks are dealt to the eight XCDs round robin), then groups of eight
-  // M tiles per N tile so that concurrently running workgroups share operands in L2.
+  // Dense: XCD-aware tile order (blocks are dealt to the eight XCDs round robin), then groups
+  // of eight M tiles per N tile so that concurrently running workgroups share operands in L2.
+  // MoE: block-major order. Only the first num_padded / BM blocks have work and the rest exit at
+  // once, so the live tiles must be the first ones dealt, spread over every XCD; with tiles_n a
+  // multiple of 8, an N tile then always lands on the same XCD, whose L2 keeps its slice of the
+  // expert's weights for all of the expert's blocks.
   const int nwg = gridDim.x;
   const int pid = blockIdx.x;
-  const int lid = (nwg % 8 == 0) ? (pid % 8) * (nwg / 8) + pid / 8 : pid;
-  constexpr int GM = 8;
-  const int per_group = GM * tiles_n;
-  const int first_m = (lid / per_group) * GM;
-  const int gm = min(GM, tiles_m - first_m);
-  const int in_group = lid % per_group;
-  const int mt = first_m + in_group % gm;
-  const int ntile = in_group / gm;
+  int mt, ntile;
+  if constexpr (MOE) {
+    mt = pid / tiles_n;
+    ntile = pid % tiles_n;
+  } else {
+    const int lid = (nwg % 8 == 0) ? (pid % 8) * (nwg / 8) + pid / 8 : pid;
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (lid / per_group) * GM;
+    const int gm = min(GM, tiles_m - first_m);
+    const int in_group = lid % per_group;
+    mt = first_m + in_group % gm;
+    ntile = in_group / gm;
+  }
   const int row0 = mt * BM;
   const int nt_wg = ntile * NT;
   const int nt0 = nt_wg + wn * NTW;
   const uint8_t* w = p.w;
+  if constexpr (MOE) {
+    const int e = p.block_expert[mt];
+    if (e < 0 || e >= p.E) return;     // the whole workgroup, before any barrier
+    w += size_t(e) * p.expert_stride;
+  }
 
   // ---- per-lane sources of the stage copies (constant over K) ----
   uint32_t a_off[Sh::A_INSTR];
@@ -123,7 +145,13 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     const int q = (wave * Sh::A_INSTR + j) * 64 + lane;
     const int r = q / CPR;
     const int c = lds_chunk_swizzle(r, q % CPR, CPR);
-    const int src_row = min(row0 + r, p.M - 1);   // rows past M are computed, never stored
+    int src_row;   // rows past M (dense) and padding rows (MoE) are computed, never stored
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[row0 + r];
+      src_row = id < p.M ? id / p.topk : 0;
+    } else {
+      src_row = min(row0 + r, p.M - 1);
+    }
     a_off[j] = uint32_t(src_row) * uint32_t(p.K * Sh::AB) + uint32_t(c * 16);
   }
   // metadata: this wave copies bytes [wave * META_PER_WAVE, +META_PER_WAVE) of the stage's
@@ -279,8 +307,8 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   }
 
   const int row_base = row0 + wm * 16 * MW;
-  if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, false>(p, w, acc, row_base, nt0, lane);
-  store_tile<FAM, false, MW, NTW>(p, acc, row_base, nt0, lane);
+  if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
+  store_tile<FAM, MOE, MW, NTW>(p, acc, row_base, nt0, lane);
 }
 
 // Group sums of bf16 activation rows over 128-k groups, split into bf16 high and low halves:
@@ -317,6 +345,10 @@ static constexpr PPCfg kPP[] = {
     {4, 4, 4, 2},  // 1: 256 x 128, waves of 64 x 64
     {2, 4, 4, 2},  // 2: 128 x 128, waves of 32 x 64
     {4, 2, 2, 4},  // 3: 128 x 128, waves of 64 x 32
+    {2, 4, 2, 4},  // 4: 64 x 256, waves of 32 x 64 (MoE blocks of 64 rows)
+    {2, 8, 2, 4},  // 5: 64 x 512, waves of 32 x 128
+    {1, 8, 2, 4},  // 6: 32 x 512, waves of 16 x 128 (MoE blocks of 32 rows)
+    {1, 4, 2, 4},  // 7: 32 x 256, waves of 16 x 64
 };
 
 const PPCfg* pp_configs(int* count) {
@@ -326,7 +358,7 @@ const PPCfg* pp_configs(int* count) {
 
 template <int FAM, int I>
 constexpr int pp_lds_of() {
-  return PPShape<FAM, kPP[I].mw, kPP[I].ntw, kPP[I].wm, kPP[I].wn>::LDS;
+  return PPShape<FAM, kPP[I].mw, kPP[I].ntw, kPP[I].wm, kPP[I].wn>::LDS_OR_NONE;
 }
 
 template <int FAM, int... I>
@@ -344,12 +376,12 @@ int pp_lds_bytes(int fam, int cfg) {
   return pp_lds_table<FAM_W4A8>(cfg, seq);
 }
 
-template <int FAM, int I>
+template <int FAM, bool MOE, int I>
 static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PPCfg C = kPP[I];
   using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn>;
-  if constexpr (Sh::LDS <= 160 * 1024) {
-    auto kern = pp_gemm_kernel<FAM, C.mw, C.ntw, C.wm, C.wn>;
+  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || FAM == FAM_WNA16)) {
+    auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     hipLaunchKernelGGL(kern, grid, dim3(512), Sh::LDS, s, p, tiles_m, tiles_n);
@@ -359,22 +391,26 @@ static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int ti
   }
 }
 
-template <int FAM, int... I>
+template <int FAM, bool MOE, int... I>
 static hipError_t launch_pp_fam(const KParams& p, int cfg, dim3 grid, int tiles_m, int tiles_n,
                                 hipStream_t s, std::integer_sequence<int, I...>) {
   using Fn = hipError_t (*)(const KParams&, dim3, int, int, hipStream_t);
-  static const Fn table[] = {&launch_pp_one<FAM, I>...};
+  static const Fn table[] = {&launch_pp_one<FAM, MOE, I>...};
   return table[cfg](p, grid, tiles_m, tiles_n, s);
 }
 
-hipError_t launch_pingpong(const KParams& p, int fam, int cfg, dim3 grid, int tiles_m, int tiles_n,
-                           hipStream_t s) {
+hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
+                           int tiles_n, hipStream_t s) {
   constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
   if (cfg < 0 || cfg >= n) return hipErrorInvalidValue;
   auto seq = std::make_integer_sequence<int, n>{};
-  if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16>(p, cfg, grid, tiles_m, tiles_n, s, seq);
-  if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8>(p, cfg, grid, tiles_m, tiles_n, s, seq);
-  return launch_pp_fam<FAM_W4A8>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (moe) {
+    if (fam != FAM_WNA16) return hipErrorInvalidValue;
+    return launch_pp_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  }
+  if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  return launch_pp_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
 }
 
 size_t group_sums_split_bytes(int64_t rows, int64_t K) {

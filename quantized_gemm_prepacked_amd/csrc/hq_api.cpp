@@ -287,6 +287,7 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
   if (T == 0) return ok();
   const hq::Plan plan = hq::plan_moe(c, T, topk, E, N, K, block_m);
+  if (plan.kind < 0) return fail(HQ_ERR_INVALID_ARGUMENT, "the HQ_TUNE override does not fit this shape");
   if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
     return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
   if (ws && !aligned16(ws)) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 16-byte aligned");

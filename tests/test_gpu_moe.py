@@ -75,11 +75,14 @@ def test_moe_align_out_of_range_ids_and_small_E():
     _check_align(ids, 7, 32)
 
 
-def _moe_case(T, topk, E, N, K, bm, with_weights, seed):
+def _moe_case(T, topk, E, N, K, bm, with_weights, seed, random_codes=False):
     inp = synth.make_moe_inputs(seed, T, K, E, topk)
     ids = inp["topk_ids"]
     active = np.unique(ids)
-    experts = {int(e): synth.make_moe_weights_expert(seed, int(e), N, K) for e in active}
+    if random_codes:   # uniformly random INT4 codes: fast to draw for hundreds of full-size experts
+        experts = {int(e): synth.random_int4_sym_expert(synth.rng(seed, 7, int(e)), N, K) for e in active}
+    else:
+        experts = {int(e): synth.make_moe_weights_expert(seed, int(e), N, K) for e in active}
     desc = hq.DESC_W4A16_SYM
     stride = hq.hq_prepacked_bytes(desc, 1, N, K)
     w = torch.zeros(stride * E, dtype=torch.uint8, device=DEV)
@@ -106,6 +109,9 @@ def _moe_case(T, topk, E, N, K, bm, with_weights, seed):
     (512, 8, 16, 256, 512, 64, True),     # 64-row blocks on the LDS-tiled kernel
     (700, 8, 64, 384, 1024, 64, False),   # skewed, ragged expert counts, tiled kernel
     (300, 8, 16, 256, 640, 64, True),     # K/128 = 5 groups (not a multiple of 4)
+    (400, 8, 16, 1024, 768, 64, True),    # ping-pong 64 x 512 tiles
+    (150, 8, 8, 512, 384, 32, True),      # ping-pong 32 x 256 tiles
+    (90, 8, 24, 768, 1152, 32, False),    # 32 x 256 tiles, 9 groups, sparse experts
 ])
 def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
     inp, experts, y = _moe_case(T, topk, E, N, K, bm, tw, 500 + T)
@@ -115,12 +121,12 @@ def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
     check_float(y, ref, "moe gemm")
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 8, 512, 2048])
 def test_moe_gemm_full_size_sampled(T):
     """DeepSeek-V3-shaped layer: 256 experts, top-8, K=7168, fused gate_up N=4096."""
     E, topk, N, K = 256, 8, 4096, 7168
     bm = hq.hq_moe_block_m(hq.DESC_W4A16_SYM, T, topk, E, N, K)
-    inp, experts, y = _moe_case(T, topk, E, N, K, bm, False, 5)
+    inp, experts, y = _moe_case(T, topk, E, N, K, bm, False, 5, random_codes=T > 8)
     cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(T).integers(0, N, 128)]))
     ref, _, _ = oracle.ref_moe_gemm(inp["x"], inp["topk_ids"], lambda e: experts[e], N, E, 128, cols=cols)
     check_float(y[:, cols], ref, f"moe full T={T}")
