@@ -31,5 +31,7 @@ from .codecs import (  # noqa: F401
 from .gemm import (  # noqa: F401
     dequant_wna16, dequant_mxfp4, ref_wna16, ref_w8a8, ref_w4a8,
 )
-from .moe import ref_moe_align, ref_moe_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer  # noqa: F401
+from .moe import (  # noqa: F401
+    ref_moe_align, ref_moe_gemm, ref_grouped_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer,
+)
 from .actquant import encode_e4m3, quantize_per_token  # noqa: F401

@@ -83,6 +83,31 @@ def ref_moe_gemm(x_bf16: np.ndarray, topk_ids: np.ndarray, expert_weights, N: in
     return y, bits, valid
 
 
+def ref_grouped_gemm(x_bf16: np.ndarray, expert_offsets: np.ndarray, expert_weights, N: int, E: int,
+                     g: int, cols=None):
+    """Grouped GEMM over activation rows already grouped by expert (the "Grouped" MoE path of the
+    announcement's section "Results: kernel microbenchmarks"): rows [offsets[e], offsets[e+1])
+    of X belong to expert e, and Y[r, :] = X[r, :] . dequant(W_e)^T for each of them. The
+    offsets are meant to be non-decreasing; a range is read as its intersection with [0, R), so
+    a decreasing pair or a bound past R gives fewer rows. Rows in no range have no defined output
+    (NaN in y, False in ``valid``). Returns (y float64 [R, N'], y bf16 bits, valid)."""
+    x = _values(x_bf16)
+    R = x.shape[0]
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    n_cols = N if cols is None else len(cols)
+    y = np.full((R, n_cols), np.nan, dtype=np.float64)
+    for e in range(E):
+        lo, hi = min(max(int(offs[e]), 0), R), min(max(int(offs[e + 1]), 0), R)
+        if hi <= lo:
+            continue
+        wd = expert_weights(e)
+        w = dequant_wna16(wd["wq"], wd["scales"], wd.get("zeros"), g, cols)
+        y[lo:hi] = x[lo:hi] @ w.T
+    valid = ~np.isnan(y[:, 0]) if n_cols else np.ones(R, dtype=bool)
+    bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
+    return y, bits, valid
+
+
 def ref_silu_mul(gate_up_bf16: np.ndarray):
     """Gated activation of the MoE expert MLP: for each routed row, the first half of the
     gate_up output is the gate g, the second half the up projection u, and

@@ -73,3 +73,43 @@ def test_moe_gemm_invalid_rows_masked():
     ws = {e: synth.make_moe_weights_expert(951, e, N, K) for e in range(E)}
     _, _, valid = oracle.ref_moe_gemm(x, ids, lambda e: ws[e], N, E, 128)
     assert valid.tolist() == [True, False, True, False]
+
+
+def test_grouped_gemm_equals_per_row_dense_and_masks_uncovered_rows():
+    """Each row equals the dense WNA16 GEMM of its own expert (a special case that reduces to the
+    dense oracle); empty, decreasing and out-of-range bounds cover no rows."""
+    R, E, N, K = 11, 5, 16, 256
+    x = synth.normal_bf16(np.random.default_rng(2), (R, K))
+    ws = {e: synth.make_moe_weights_expert(952, e, N, K) for e in range(E)}
+    # expert 0: rows 0-2; 1: empty; 2: rows 3-6; 3: [7, 14) clipped to [7, 11); 4: the
+    # decreasing pair [14, 9), no rows
+    offs = np.array([0, 3, 3, 7, 14, 9])
+    y, bits, valid = oracle.ref_grouped_gemm(x, offs, lambda e: ws[e], N, E, 128)
+    owner = {r: 0 for r in range(0, 3)} | {r: 2 for r in range(3, 7)} | {r: 3 for r in range(7, 11)}
+    for r in range(R):
+        e = owner[r]
+        yd, _ = oracle.ref_wna16(x[r:r + 1], ws[e]["wq"], ws[e]["scales"], None, 128)
+        assert np.array_equal(y[r], yd[0]), r
+    assert valid.all()
+
+
+def test_grouped_gemm_brute_force_and_gaps():
+    """Scalar triple loop on a tiny case with a gap between ranges; E = 1 is the dense GEMM."""
+    R, E, N, K = 6, 3, 4, 128
+    x = synth.normal_bf16(np.random.default_rng(3), (R, K))
+    ws = {e: synth.make_moe_weights_expert(953, e, N, K) for e in range(E)}
+    offs = np.array([0, 2, 2, 5])          # rows 0-1 expert 0, 2-4 expert 2, row 5 in no range
+    y, _, valid = oracle.ref_grouped_gemm(x, offs, lambda e: ws[e], N, E, 128)
+    assert valid.tolist() == [True] * 5 + [False]
+    xv = oracle.decode_bf16(x)
+    for r, e in [(0, 0), (1, 0), (2, 2), (3, 2), (4, 2)]:
+        codes = oracle.decode_int4_sym(oracle.unpack_nibbles(ws[e]["wq"]))
+        s = oracle.decode_bf16(ws[e]["scales"])
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(xv[r, k]) * float(codes[n, k]) * float(s[n, k // 128])
+            assert abs(y[r, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+    yd, _ = oracle.ref_wna16(x, ws[0]["wq"], ws[0]["scales"], None, 128)
+    y1, _, _ = oracle.ref_grouped_gemm(x, np.array([0, R]), lambda e: ws[0], N, 1, 128)
+    assert np.array_equal(y1, yd)
