@@ -203,6 +203,28 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
                               int32_t block_m, const float* topk_weights, void* y,
                               void* ws, size_t ws_bytes, hq_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Grouped GEMM (device), WNA16 only: the "Grouped" MoE path of the announcement's section
+ * "Results: kernel microbenchmarks", for activations that arrive already grouped by expert.
+ *   y[r, :] = a[r, :] . dequant(W_e)^T   for r in [expert_offsets[e], expert_offsets[e+1])
+ *   a               bf16 [R, K] row-major (device); a_scale must be NULL
+ *   w_packed        prepacked weights of all E experts (hq_prepack_weights with E experts)
+ *   expert_offsets  int32 [E + 1] (device): non-decreasing, 0 <= offsets[0], offsets[E] <= R.
+ *                   Each range is clipped to [0, R); rows in no range are not written. Offsets
+ *                   that overlap break the contract: the rows concerned get unspecified values,
+ *                   and no access leaves the buffers.
+ *   y               bf16 [R, N] row-major (device), same row order as a
+ *   ws              hq_grouped_gemm_workspace_bytes(...) bytes, 256-byte aligned (required)
+ * The row block size comes from the tuning table (rows per expert = R / E); the call runs a
+ * small index kernel (the padded row index of each expert, into ws) and the grouped GEMM kernels
+ * of hq_moe_grouped_gemm with every row as its own token. Asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------------- */
+size_t hq_grouped_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t R, int32_t E, int64_t N, int64_t K);
+hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64_t N, int64_t K,
+                          const void* a, const float* a_scale, const void* w_packed,
+                          const int32_t* expert_offsets, void* y, void* ws, size_t ws_bytes,
+                          hq_stream_t stream);
+
 /* Thread-local message describing the last non-HQ_OK status of this thread ("" if none). */
 const char* hq_last_error(void);
 

@@ -36,7 +36,8 @@ EXPORTED = (
     "hq_prepacked_bytes", "hq_prepack_weights", "hq_gemm_workspace_bytes", "hq_gemm",
     "hq_moe_align_capacity", "hq_moe_align_workspace_bytes", "hq_moe_align", "hq_moe_block_m",
     "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_quantize_activations",
-    "hq_moe_silu_mul", "hq_moe_combine", "hq_last_error", "hq_version",
+    "hq_moe_silu_mul", "hq_moe_combine", "hq_grouped_gemm_workspace_bytes", "hq_grouped_gemm",
+    "hq_last_error", "hq_version",
 )
 
 
@@ -91,6 +92,10 @@ _c = {
     "hq_moe_grouped_gemm": _sig("hq_moe_grouped_gemm", ctypes.c_int, _D, _I64, _I32, _I32, _I64, _I64, _P, _P, _P,
                                 _P, _P, _P, _I32, _P, _P, _P, _SZ, _P),
     "hq_quantize_activations": _sig("hq_quantize_activations", ctypes.c_int, _I32, _I64, _I64, _P, _P, _P, _P),
+    "hq_grouped_gemm_workspace_bytes": _sig("hq_grouped_gemm_workspace_bytes", ctypes.c_size_t, _P, _I64, _I32,
+                                            _I64, _I64),
+    "hq_grouped_gemm": _sig("hq_grouped_gemm", ctypes.c_int, _P, _I64, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                            ctypes.c_size_t, _P),
     "hq_moe_silu_mul": _sig("hq_moe_silu_mul", ctypes.c_int, _I64, _I64, _P, _P, _P),
     "hq_moe_combine": _sig("hq_moe_combine", ctypes.c_int, _I64, _I32, _I32, _I64, _P, _P, _P, _P),
     "hq_last_error": _sig("hq_last_error", ctypes.c_char_p),
@@ -193,6 +198,15 @@ def hq_moe_grouped_gemm(desc, T, topk, E, N, K, a, a_scale, w_packed, sorted_ids
                                      _ptr(w_packed), _ptr(sorted_ids), _ptr(block_expert),
                                      _ptr(num_padded), block_m, _ptr(topk_weights), _ptr(y),
                                      _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def hq_grouped_gemm_workspace_bytes(desc, R, E, N, K) -> int:
+    return _c["hq_grouped_gemm_workspace_bytes"](_d(desc), R, E, N, K)
+
+
+def hq_grouped_gemm(desc, R, E, N, K, a, a_scale, w_packed, expert_offsets, y, ws, ws_bytes, stream=None):
+    _check(_c["hq_grouped_gemm"](_d(desc), R, E, N, K, _ptr(a), _ptr(a_scale), _ptr(w_packed),
+                                 _ptr(expert_offsets), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def hq_quantize_activations(act_fmt, M, K, x, xq, s_tok, stream=None):

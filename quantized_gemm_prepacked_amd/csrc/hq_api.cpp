@@ -222,6 +222,69 @@ hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const v
                    "hq_quantize_activations launch");
 }
 
+namespace {
+// Workspace of hq_grouped_gemm: the row index (sorted ids, block -> expert table, num_padded),
+// then the grouped GEMM's own workspace, each 256-byte aligned.
+struct GroupedWs {
+  int32_t bm;
+  size_t cap, sorted_off, bexp_off, npad_off, gemm_off, gemm_bytes, total;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+GroupedWs grouped_ws(const hq::Combo& c, int64_t R, int32_t E, int64_t N, int64_t K) {
+  GroupedWs g{};
+  g.bm = hq::moe_block_m(c, R, 1, E, N, K);
+  g.cap = hq_moe_align_capacity(R, 1, E, g.bm);
+  g.sorted_off = 0;
+  g.bexp_off = align256(g.cap * 4);
+  g.npad_off = g.bexp_off + align256(std::max<size_t>(g.cap / g.bm, 1) * 4);
+  g.gemm_off = g.npad_off + 256;
+  g.gemm_bytes = hq::plan_moe(c, R, 1, E, N, K, g.bm).ws_bytes;
+  g.total = g.gemm_off + align256(g.gemm_bytes);
+  return g;
+}
+}  // namespace
+
+size_t hq_grouped_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t R, int32_t E, int64_t N, int64_t K) {
+  hq::Combo c{};
+  if (resolve(desc, &c) != HQ_OK || check_shape(c, N, K) != HQ_OK || R < 0 || E <= 0 || E > 512) return 0;
+  return grouped_ws(c, R, E, N, K).total;
+}
+
+hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64_t N, int64_t K,
+                          const void* a, const float* a_scale, const void* w_packed,
+                          const int32_t* expert_offsets, void* y, void* ws, size_t ws_bytes,
+                          hq_stream_t stream) {
+  hq::Combo c{};
+  hq_status s = resolve(desc, &c);
+  if (s != HQ_OK) return s;
+  if (c.fam != hq::FAM_WNA16) return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM supports WNA16 only");
+  if ((s = check_shape(c, N, K)) != HQ_OK) return s;
+  if (R < 0 || R > kMaxDim || E <= 0 || E > 512)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld E=%d out of range", (long long)R, E);
+  if (R * N >= (int64_t(1) << 31)) return fail(HQ_ERR_UNSUPPORTED, "R*N must stay below 2^31");
+  if (a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
+  if (!a || !w_packed || !expert_offsets || !y)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, expert_offsets and y must be non-NULL");
+  if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
+  if (R == 0) return ok();
+  const GroupedWs g = grouped_ws(c, R, E, N, K);
+  if (!ws || ws_bytes < g.total) return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, g.total);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 256-byte aligned");
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + g.sorted_off);
+  int32_t* bexp = reinterpret_cast<int32_t*>(base + g.bexp_off);
+  int32_t* npad = reinterpret_cast<int32_t*>(base + g.npad_off);
+  if ((s = check_hip(hq::launch_grouped_index(expert_offsets, R, E, g.bm, int64_t(g.cap), sorted, bexp, npad,
+                                              static_cast<hipStream_t>(stream)),
+                     "hq_grouped_gemm row index launch")) != HQ_OK)
+    return s;
+  return hq_moe_grouped_gemm(desc, R, 1, E, N, K, a, nullptr, w_packed, sorted, bexp, npad, g.bm, nullptr, y,
+                             g.gemm_bytes ? base + g.gemm_off : nullptr, g.gemm_bytes, stream);
+}
+
 hq_status hq_moe_silu_mul(int64_t R, int64_t I, const void* gate_up, void* act, hq_stream_t stream) {
   if (R < 0 || R > kMaxDim || I <= 0 || I > kMaxDim)
     return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld I=%lld out of range", (long long)R, (long long)I);

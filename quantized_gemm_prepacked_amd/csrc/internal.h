@@ -60,6 +60,9 @@ bool moe_block_m_supported(int32_t block_m);
 hipError_t launch_gemm(const GemmCall& call, const Plan& plan);
 
 size_t moe_align_ws_bytes(int64_t T, int32_t topk, int32_t E, int32_t block_m);
+hipError_t launch_grouped_index(const int32_t* offsets, int64_t R, int32_t E, int32_t bm, int64_t cap,
+                                int32_t* sorted, int32_t* block_expert, int32_t* num_padded,
+                                hipStream_t stream);
 hipError_t launch_silu_mul(int64_t R, int64_t I, const void* gate_up, void* act, hipStream_t s);
 hipError_t launch_moe_combine(int64_t T, int32_t topk, int32_t E, int64_t N, const int32_t* topk_ids,
                               const void* y, void* out, hipStream_t s);

@@ -13,6 +13,8 @@
 // the input, independent of scheduling.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "hq.h"
 #include "internal.h"
 
@@ -117,7 +119,65 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
   }
 }
 
+// Row index of the "Grouped" path (rows already grouped by expert): expert e owns rows
+// [offsets[e], offsets[e+1]) clipped to [0, R). The same outputs as the token sort -- each
+// expert's rows padded to a multiple of bm with the sentinel R, the block -> expert table, -1
+// for blocks past the padded rows, num_padded -- so the grouped GEMM kernels run unchanged with
+// every row as its own token. Every workgroup rebuilds the (E <= 1024) padded prefix sum in LDS
+// and fills positions [1024 * blockIdx.x, ...) of the capacity; positions never exceed cap, so
+// offsets that overlap (outside the contract) give unspecified rows but no access out of bounds.
+__global__ __launch_bounds__(kThreads) void grouped_index_kernel(const int32_t* __restrict__ offsets,
+                                                                 int R, int E, int bm, int cap,
+                                                                 int32_t* __restrict__ sorted,
+                                                                 int32_t* __restrict__ block_expert,
+                                                                 int32_t* __restrict__ num_padded) {
+  __shared__ int lo_s[kThreads], cnt_s[kThreads], scan[kThreads];
+  const int tid = threadIdx.x;
+  int padded = 0;
+  if (tid < E) {
+    const int lo = min(max(offsets[tid], 0), R);
+    const int hi = min(max(offsets[tid + 1], 0), R);
+    lo_s[tid] = lo;
+    cnt_s[tid] = max(hi - lo, 0);
+    padded = (cnt_s[tid] + bm - 1) / bm * bm;
+  }
+  scan[tid] = padded;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int t = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += t;
+    __syncthreads();
+  }
+  const int total = min(scan[E - 1], cap);   // inclusive scan: scan[e] = end of expert e's range
+  if (blockIdx.x == 0 && tid == 0) *num_padded = total;
+  for (int pos = blockIdx.x * kThreads + tid; pos < cap; pos += gridDim.x * kThreads) {
+    if (pos < total) {
+      int lo = 0, hi = E - 1;   // first e whose range ends past pos
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] > pos) hi = mid; else lo = mid + 1;
+      }
+      const int i = pos - (scan[lo] - (cnt_s[lo] + bm - 1) / bm * bm);
+      sorted[pos] = i < cnt_s[lo] ? lo_s[lo] + i : R;
+      if (pos % bm == 0) block_expert[pos / bm] = lo;
+    } else {
+      sorted[pos] = R;
+      if (pos % bm == 0) block_expert[pos / bm] = -1;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_grouped_index(const int32_t* offsets, int64_t R, int32_t E, int32_t bm, int64_t cap,
+                                int32_t* sorted, int32_t* block_expert, int32_t* num_padded,
+                                hipStream_t stream) {
+  const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>((cap + kThreads - 1) / kThreads, 1024));
+  hipLaunchKernelGGL(grouped_index_kernel, dim3(unsigned(wgs)), dim3(kThreads), 0, stream, offsets,
+                     int(R), int(E), int(bm), int(cap), sorted, block_expert, num_padded);
+  return hipGetLastError();
+}
 
 size_t moe_align_ws_bytes(int64_t, int32_t, int32_t, int32_t) { return 0; }
 

@@ -117,3 +117,16 @@ def test_prepack_rejections():
     with pytest.raises(hq.HQError) as ei:
         hq.hq_prepack_weights(d, 1, n, k, wq, s, np.zeros_like(s, np.uint8), out[:-1])
     assert ei.value.status == hq.HQ_ERR_WORKSPACE
+
+
+def test_grouped_gemm_host_validation():
+    """Refused on the host before any launch: non-WNA16 formats, E out of range, a_scale given."""
+    d = hq.DESC_W4A16_SYM
+    assert hq.hq_grouped_gemm_workspace_bytes(d, 4096, 256, 4096, 7168) > 4096 * 4
+    assert hq.hq_grouped_gemm_workspace_bytes(d, 16, 0, 256, 256) == 0
+    with pytest.raises(hq.HQError):
+        hq.hq_grouped_gemm(hq.DESC_W8A8, 4, 2, 256, 512, 16, 16, 16, 16, 16, 16, 1 << 20, stream=0)
+    with pytest.raises(hq.HQError):
+        hq.hq_grouped_gemm(d, 4, 600, 256, 512, 16, None, 16, 16, 16, 16, 1 << 20, stream=0)
+    with pytest.raises(hq.HQError):
+        hq.hq_grouped_gemm(d, 4, 2, 256, 512, 16, 16, 16, 16, 16, 16, 1 << 20, stream=0)
