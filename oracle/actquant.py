@@ -13,6 +13,16 @@ but fixes no rule; the plain reading used here is symmetric absmax scaling per r
     e4m3   : q = nearest finite e4m3 ("fn") code to clamp(v, -448, 448), ties to the even code;
              a negative value that rounds to zero gives -0 (0x80)
 
+MXFP4 activations (for W4A4) follow the OCP Microscaling (MX) v1.0 rule instead, per row and per
+block of 32 consecutive k (the MXFP4 format the announcement's W4A4 path consumes, section
+"Results: kernel microbenchmarks"):
+
+    e      = floor(log2(max_k |x|)) - 2, clamped to [-127, 127]   (2 = largest e2m1 exponent)
+    scale  = e8m0 byte e + 127; an all-zero block takes e = -127 (byte 0)
+    v      = x * 2^-e                                   (exact: a power-of-two scaling)
+    code   = nearest e2m1 value to v, ties to the even code, saturating at +-6; the sign bit is
+             set only for a non-zero magnitude (a negative value that rounds to zero gives +0)
+
 Both divisions are binary32 on purpose: the codes are integers decided by floating point, and
 the kernel takes that decision in binary32, so the reference takes it in the same precision
 (numpy float32 division is IEEE correctly rounded).
@@ -21,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import decode_bf16, decode_e4m3
+from .codecs import decode_bf16, decode_e2m1, decode_e4m3
 
 _E4M3_FINITE = np.array([c for c in range(0x80) if not (c & 0x7F) == 0x7F], dtype=np.int64)
 _E4M3_VALUES = decode_e4m3(_E4M3_FINITE)          # non-negative finite magnitudes, ascending
@@ -67,3 +77,39 @@ def quantize_per_token(x_bf16: np.ndarray, act: str):
         v = (x / s[:, None]).astype(np.float32)
         return encode_e4m3(np.clip(v, np.float32(-448.0), np.float32(448.0))), s
     raise ValueError(act)
+
+
+_E2M1_POS = decode_e2m1(np.arange(8))                  # 0, 0.5, 1, 1.5, 2, 3, 4, 6
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 code (4 bits, bit 3 = sign) by brute force over the 8 magnitudes: the lowest
+    code at minimum distance, or the even one of two tied neighbours; saturates at 6; the sign
+    bit only for a non-zero magnitude."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - _E2M1_POS)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    lo = np.argmax(cand, axis=-1)
+    two = cand.sum(axis=-1) > 1
+    code = np.where(two & (lo % 2 == 1), lo + 1, lo)
+    sign = (np.signbit(v) & (code != 0)).astype(np.int64) << 3
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_mxfp4_act(x_bf16: np.ndarray):
+    """x_bf16: uint16 bf16 bits [M, K] (K % 32 == 0). Returns (packed e2m1 codes uint8 [M, K/2],
+    low nibble = even k; e8m0 scale bytes uint8 [M, K/32])."""
+    x = decode_bf16(x_bf16)                                     # exact, float64
+    M, K = x.shape
+    blocks = x.reshape(M, K // 32, 32)
+    amax = np.abs(blocks).max(axis=2)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.floor(np.log2(amax[nz])).astype(np.int64) - 2  # log2 of a bf16 value: exact floor
+    e = np.clip(e, -127, 127)
+    v = blocks * np.ldexp(1.0, -e)[:, :, None]
+    codes = encode_e2m1(v).reshape(M, K)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)

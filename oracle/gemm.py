@@ -92,3 +92,14 @@ def ref_w4a8(xq: np.ndarray, s_tok: np.ndarray, wq: np.ndarray, scales_e8m0: np.
     st = np.asarray(_sel(s_tok, rows), dtype=np.float32).astype(np.float64)
     y = (x @ w.T) * st[:, None]
     return y, round_to_bf16(y)
+
+
+def ref_w4a4(xq: np.ndarray, xs_e8m0: np.ndarray, wq: np.ndarray, scales_e8m0: np.ndarray,
+             rows=None, cols=None):
+    """W4A4-MXFP4: both operands MXFP4 (e2m1 codes with an e8m0 scale per 32-element block
+    along K), y[m, n] = sum_k x[m, k] * w[n, k] with x and w each dequantized per the MX
+    definition; the products and sums are exact in float64. Returns (y float64, y bf16 bits)."""
+    x = dequant_mxfp4(xq, xs_e8m0, rows)
+    w = dequant_mxfp4(wq, scales_e8m0, cols)
+    y = x @ w.T
+    return y, round_to_bf16(y)
