@@ -69,7 +69,9 @@ typedef enum {
 typedef enum {
   HQ_ACT_BF16 = 0,             /* bf16 [M, K] row-major, no activation scale          */
   HQ_ACT_INT8_PER_TOKEN = 1,   /* int8 [M, K] row-major + fp32 scale per row [M]      */
-  HQ_ACT_FP8E4M3_PER_TOKEN = 2 /* OCP e4m3 [M, K] row-major + fp32 scale per row [M]  */
+  HQ_ACT_FP8E4M3_PER_TOKEN = 2, /* OCP e4m3 [M, K] row-major + fp32 scale per row [M] */
+  HQ_ACT_MXFP4 = 3              /* OCP MX e2m1 [M, K/2] (low nibble = even k) + e8m0 byte per
+                                   (row, 32-element block) [M, K/32]                        */
 } hq_act_fmt;
 
 typedef enum {
@@ -107,7 +109,13 @@ typedef struct {
  *   INT8     : xq = clamp(round_half_even(v), -127, 127)
  *   e4m3     : xq = nearest OCP e4m3 code to clamp(v, -448, 448), ties to the even code
  *              (negative values that round to zero give -0, 0x80)
- * act_fmt  HQ_ACT_INT8_PER_TOKEN or HQ_ACT_FP8E4M3_PER_TOKEN (the desc act_fmt of the GEMM)
+ * act_fmt  HQ_ACT_INT8_PER_TOKEN or HQ_ACT_FP8E4M3_PER_TOKEN (the desc act_fmt of the GEMM), or
+ *          HQ_ACT_MXFP4 (W4A4), which follows the OCP Microscaling rule per row and block of 32 k:
+ *            e = floor(log2 max|x|) - 2 clamped to [-127, 127] (-127 for a zero block),
+ *            scale byte e + 127, code = nearest e2m1 to x * 2^-e (ties to even, saturating at 6;
+ *            a value that rounds to zero gives +0). xq then holds packed e2m1 [M, K/2] (low
+ *            nibble = even k) and s_tok receives the e8m0 bytes [M, K/32] through its pointer
+ *            (cast); K % 32 == 0.
  * x        bf16 [M, K] row-major (device, 16-byte aligned); K % 8 == 0
  * xq       int8 / e4m3 bytes [M, K] row-major (device, 16-byte aligned), the GEMM's `a`
  * s_tok    fp32 [M] (device), the GEMM's `a_scale`
@@ -137,7 +145,9 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
 /* ---------------------------------------------------------------------------------------------
  * Dense GEMM (device):  y[m, n] = epilogue( sum_k a[m, k] * w[n, k] ),  0 <= m < M, 0 <= n < N
  *   a        activations, format desc->act_fmt, [M, K] row-major (device)
- *   a_scale  fp32 [M] per-token scales for INT8/FP8 activations (device); NULL for BF16
+ *   a_scale  fp32 [M] per-token scales for INT8/FP8 activations (device); NULL for BF16.
+ *            MXFP4 activations (W4A4): the e8m0 block-scale bytes, uint8 [M, K/32] row-major,
+ *            passed through this pointer (cast) -- the activations' own scale tensor
  *   w_packed the prepacked weights of ONE layer (E = 1) (device)
  *   y        [M, N] row-major, bf16 or int32 per desc->out_fmt (device)
  *   ws       scratch of at least hq_gemm_workspace_bytes(desc, M, N, K) bytes (device); may be
@@ -145,6 +155,8 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
  * Epilogues:  WNA16: bf16( sum_g s[n,g] * sum_{k in g} a*(q - z) )  (fp32 accumulation)
  *             W8A8 : bf16( float(acc) * a_scale[m] * s_ch[n] ),  acc exact int32
  *             W4A8 : bf16( a_scale[m] * sum_k e4m3(a) * e2m1(q) * 2^(e - 127) ) (fp32 accumulation)
+ *             W4A4 : bf16( sum_k e2m1(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation;
+ *                    weights as W4A8, desc act_fmt HQ_ACT_MXFP4)
  * All bf16 results use round-to-nearest-even. M = 0 is a no-op returning HQ_OK.
  * ------------------------------------------------------------------------------------------- */
 size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K);

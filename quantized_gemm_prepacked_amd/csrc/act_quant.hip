@@ -8,6 +8,13 @@
 //   binary32 division), INT8 q = clamp(rne(v), -127, 127), e4m3 q = rne_e4m3(clamp(v, +-448)).
 // One workgroup per row: a pass for the row maximum (wave then LDS reduction), a pass that
 // re-reads the row (from cache) and writes 8 codes per lane per step.
+//
+// MXFP4 activations (W4A4) follow the OCP Microscaling rule per block of 32 k instead: shared
+// exponent e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for a zero block), e8m0 byte
+// e + 127, codes = nearest e2m1 to x * 2^-e with ties to even, saturating at 6, sign only on a
+// non-zero magnitude. One thread per block; every decision is exact (integer maximum of the bf16
+// magnitudes, exponent from the bits, a power-of-two scaling, comparisons with the e2m1
+// midpoints), so no denormal mode or rounding mode can change a code.
 #include <hip/hip_runtime.h>
 
 #include "device_ops.h"
@@ -92,6 +99,51 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   }
 }
 
+// e2m1 magnitude code of a >= 0 (exact binary32), ties to the even code, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_code(float a) {
+  return uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+         uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+}
+
+__global__ __launch_bounds__(kThreads) void act_quant_mxfp4_kernel(const uint16_t* __restrict__ x,
+                                                                   uint8_t* __restrict__ xq,
+                                                                   uint8_t* __restrict__ xs,
+                                                                   int64_t n_blocks) {
+  const int64_t b = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (b >= n_blocks) return;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ldg16(x + b * 32 + 8 * i);
+  uint32_t amax = 0;   // largest |x| as bf16 bits: the bit order of non-negative values
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
+  const int ef = int(amax >> 7);                      // bf16 exponent field (0: zero or subnormal)
+  const int e = ef == 0 ? -127 : max(ef - 127 - 2, -127);
+  xs[b] = uint8_t(e + 127);
+  const float inv = __uint_as_float(uint32_t(127 - e) << 23);   // 2^-e, e in [-127, 125]
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = (v[i][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t mag = h & 0x7FFFu;
+      // a subnormal bf16 magnitude is mag * 2^-133, so v = mag * 2^(-133 - e): exact while that
+      // power of two is a normal binary32 number (e <= -7); past it v < 2^-120 rounds to zero
+      const float a = (mag >> 7) != 0 ? __uint_as_float(mag << 16) * inv
+                      : e <= -7      ? float(mag) * __uint_as_float(uint32_t(-6 - e) << 23)
+                                     : 0.0f;
+      const uint32_t c = e2m1_code(a);
+      word |= (c | (((h >> 15) & uint32_t(c != 0u)) << 3)) << (4 * j);
+    }
+    out[i] = word;
+  }
+  *reinterpret_cast<u32x4*>(xq + b * 16) = u32x4{out[0], out[1], out[2], out[3]};
+}
+
 }  // namespace
 
 hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, void* xq, float* s_tok,
@@ -99,6 +151,12 @@ hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, vo
   const dim3 grid{static_cast<unsigned>(M)};
   const auto* xin = static_cast<const uint16_t*>(x);
   auto* out = static_cast<uint8_t*>(xq);
+  if (act_fmt == HQ_ACT_MXFP4) {
+    const int64_t nb = M * (K / 32);
+    hipLaunchKernelGGL(act_quant_mxfp4_kernel, dim3(unsigned((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, xin, out, reinterpret_cast<uint8_t*>(s_tok), nb);
+    return hipGetLastError();
+  }
   if (act_fmt == HQ_ACT_INT8_PER_TOKEN)
     hipLaunchKernelGGL(act_quant_kernel<HQ_ACT_INT8_PER_TOKEN>, grid, dim3(kThreads), 0, stream, xin, out, s_tok, int(K));
   else

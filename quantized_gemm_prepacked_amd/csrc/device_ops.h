@@ -114,6 +114,14 @@ __device__ __forceinline__ f32x4 mfma_fp8_fp4(u32x4 a_lo, u32x4 a_hi, u32x4 b, i
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, 127, 0, b_scale);
 }
 
+// Both operands fp4 e2m1 (formats 4 and 4), each with its own e8m0 block scales: 4-bit A takes
+// the same K layout as 4-bit B (lane group g holds k = 32g + j in nibble j).
+__device__ __forceinline__ f32x4 mfma_fp4_fp4(u32x4 a, int a_scale, u32x4 b, int b_scale, f32x4 c) {
+  i32x8 av = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+  i32x8 bv = {int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, a_scale, 0, b_scale);
+}
+
 // Position of 16-byte chunk `chunk` of activation row `row` in an LDS tile with `cpr` chunks per
 // row (an XOR swizzle, so each row's chunks stay a permutation of its own slots). For 128-byte
 // rows the key is the row's low three bits. For 256-byte rows the plain key (row & 15) leaves the

@@ -59,8 +59,10 @@ __device__ __forceinline__ void epilogue(const KParams& p, int orow, int srow, i
       const float sch = reinterpret_cast<const float*>(p.w + p.scales_off)[n];
       reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(float(v) * p.a_scale[srow] * sch);
     }
-  } else {
+  } else if constexpr (FAM == FAM_W4A8) {
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * p.a_scale[srow] * tw);
+  } else {   // W4A4: both block scales were applied by the MFMA
+    reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * tw);
   }
 }
 

@@ -37,10 +37,11 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   if (rows <= 16) {
     if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
     if (c.fam == FAM_W4A8) return first_fit({21, 2});
+    if (c.fam == FAM_W4A4) return first_fit({21, 2});
     return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
-    if (c.fam == FAM_W4A8) return first_fit({16, 8});
+    if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4) return first_fit({16, 8});
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
@@ -88,6 +89,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_WNA16>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_W8A8)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W8A8>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_W4A4)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A4>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -115,6 +118,8 @@ constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
 constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
+// W4A4 runs on the skinny and ping-pong kernels only
+constexpr RangeEntry kW4a4Table[] = {{256, 0, 0}, {kInf, 3, 0}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -141,6 +146,9 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_W8A8) {
     t = kW8a8Table;
     n = int(sizeof(kW8a8Table) / sizeof(kW8a8Table[0]));
+  } else if (c.fam == FAM_W4A4) {
+    t = kW4a4Table;
+    n = int(sizeof(kW4a4Table) / sizeof(kW4a4Table[0]));
   } else {
     t = kW4a8Table;
     n = int(sizeof(kW4a8Table) / sizeof(kW4a8Table[0]));
@@ -154,6 +162,14 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
     return t[i];
   }
   // Fallbacks when the preferred tile does not divide N.
+  if (c.fam == FAM_W4A4) {
+    int n_p = 0;
+    const PPCfg* pc = pp_configs(&n_p);
+    for (int cfg : {3, 2})   // 128 x 128 tiles
+      if (M > 256 && N % (16 * pc[cfg].ntw * pc[cfg].wn) == 0 && pp_lds_bytes(c.fam, cfg) <= 160 * 1024)
+        return {kInf, 3, cfg};
+    return {0, 0, 0};
+  }
   const int tc = pick_tiled(c, N, K);
   if (M > 64 && tc >= 0) return {kInf, 1, tc};
   return {0, 0, 0};
@@ -170,6 +186,7 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
     return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
+  if (c.fam == FAM_W4A4 && (o.kind == 1 || o.kind == 2)) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -225,7 +242,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   // The direct-to-LDS kernels address activations with 32-bit offsets.
   if ((pick.kind == 2 || pick.kind == 3) &&
       uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) >= (uint64_t(1) << 32)) {
-    const int tc = pick_tiled(c, N, K);
+    const int tc = c.fam == FAM_W4A4 ? -1 : pick_tiled(c, N, K);
     pick = tc >= 0 ? RangeEntry{kInf, 1, tc} : RangeEntry{0, 0, 0};
   }
   if (pick.kind != 0) {

@@ -35,23 +35,35 @@ namespace {
 
 template <int FAM>
 struct PPTraits;
+// kRowBytes: activation bytes per row per step of 128 k; kAScaleBytes: activation block-scale
+// bytes per row per step (MXFP4 activations: one e8m0 byte per 32 k).
 template <>
 struct PPTraits<FAM_WNA16> {
-  static constexpr int kABytes = 2;
+  static constexpr int kRowBytes = 256;
   static constexpr int kUnitsPerStep = 1;
   static constexpr int kMetaPerTile = 32;   // 16 bf16 group scales
+  static constexpr int kAScaleBytes = 0;
 };
 template <>
 struct PPTraits<FAM_W8A8> {
-  static constexpr int kABytes = 1;
+  static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 2;
   static constexpr int kMetaPerTile = 0;
+  static constexpr int kAScaleBytes = 0;
 };
 template <>
 struct PPTraits<FAM_W4A8> {
-  static constexpr int kABytes = 1;
+  static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 1;
   static constexpr int kMetaPerTile = 64;   // one e8m0 byte per lane
+  static constexpr int kAScaleBytes = 0;
+};
+template <>
+struct PPTraits<FAM_W4A4> {
+  static constexpr int kRowBytes = 64;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 64;
+  static constexpr int kAScaleBytes = 4;
 };
 
 // Workgroup barrier that the instruction scheduler may not move work across: the phases around
@@ -68,8 +80,7 @@ struct PPShape {
   static constexpr int kStages = 3;
   static constexpr int BM = 16 * MW * WM;
   static constexpr int BN = 16 * NTW * WN;
-  static constexpr int AB = PPTraits<FAM>::kABytes;
-  static constexpr int RB = 128 * AB;                 // activation bytes per row per step
+  static constexpr int RB = PPTraits<FAM>::kRowBytes;  // activation bytes per row per step
   static constexpr int CPR = RB / 16;
   static constexpr int A_BYTES = BM * RB;
   static constexpr int NT = BN / 16;
@@ -79,14 +90,17 @@ struct PPShape {
   static constexpr int META_BYTES = NT * MPT;
   static constexpr int META_PER_WAVE = META_BYTES / 8;
   static constexpr int META_LANES = META_PER_WAVE / 16;
-  static constexpr int STAGE = (A_BYTES + B_BYTES + META_BYTES + 1023) / 1024 * 1024;
+  // activation block scales (MXFP4 activations): BM rows x 4 bytes, each wave copies BM / 8 rows
+  static constexpr int ASC_BYTES = BM * PPTraits<FAM>::kAScaleBytes;
+  static constexpr int STAGE = (A_BYTES + B_BYTES + META_BYTES + ASC_BYTES + 1023) / 1024 * 1024;
   static constexpr int LDS = kStages * STAGE;
   static constexpr int A_INSTR = A_BYTES / 1024 / 8;
   static constexpr int B_INSTR = NT * UPS / 8;
-  static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0);
+  static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0) + (ASC_BYTES ? 1 : 0);
   // the copies split evenly over the eight waves (shapes that do not are never launched)
   static constexpr bool kValid = A_BYTES % (1024 * 8) == 0 && (NT * UPS) % 8 == 0 &&
-                                 META_BYTES % (16 * 8) == 0 && META_LANES <= 64;
+                                 META_BYTES % (16 * 8) == 0 && META_LANES <= 64 &&
+                                 (ASC_BYTES == 0 || (BM % 8 == 0 && BM / 8 <= 64));
   static constexpr int LDS_OR_NONE = kValid ? LDS : 1 << 30;
 };
 
@@ -152,7 +166,15 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     } else {
       src_row = min(row0 + r, p.M - 1);
     }
-    a_off[j] = uint32_t(src_row) * uint32_t(p.K * Sh::AB) + uint32_t(c * 16);
+    a_off[j] = uint32_t(src_row) * uint32_t(p.K / 128 * RB) + uint32_t(c * 16);
+  }
+  // MXFP4 activations: lane i < BM / 8 of wave w copies the step's 4 scale bytes of row
+  // w * BM / 8 + i
+  const uint8_t* asc_src = nullptr;
+  if constexpr (Sh::ASC_BYTES > 0) {
+    const int r = wave * (BM / 8) + min(lane, BM / 8 - 1);
+    const int src_row = min(row0 + r, p.M - 1);
+    asc_src = reinterpret_cast<const uint8_t*>(p.a_scale) + size_t(src_row) * (p.K / 32);
   }
   // metadata: this wave copies bytes [wave * META_PER_WAVE, +META_PER_WAVE) of the stage's
   // [tile][MPT] block, 16 per lane
@@ -182,6 +204,10 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       if (lane < Sh::META_LANES)
         lds_dma16(w + p.scales_off + unit * Sh::MPT + meta_byte, sb + Sh::B_BYTES + wave * Sh::META_PER_WAVE);
     }
+    if constexpr (Sh::ASC_BYTES > 0) {
+      if (lane < BM / 8)
+        lds_dma4(asc_src + 4 * ks, sb + Sh::B_BYTES + Sh::META_BYTES + wave * (BM / 8) * 4);
+    }
   };
 
   auto read_a = [&](const uint8_t* st, int mb, int chunk) -> u32x4 {
@@ -200,11 +226,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     for (int t = 0; t < NTW; ++t) acc[mb][t] = Acc{0, 0, 0, 0};
 
   // Operand fragments of one step, filled by the memory phase and used by the compute phase.
-  constexpr int NA = FAM == FAM_WNA16 ? 4 : 2;   // activation fragments per row block
+  constexpr int NA = FAM == FAM_WNA16 ? 4 : (FAM == FAM_W4A4 ? 1 : 2);   // activation fragments per row block
   constexpr int NB = FAM == FAM_W8A8 ? 2 : 1;    // packed weight fragments per channel tile
   u32x4 af[MW][NA];
   u32x4 bq[NTW][NB];
   uint32_t meta[NTW];
+  int asf[MW];   // MXFP4 activations: this lane's row block scale
 
   auto memory_phase = [&](int ks) {
     const uint8_t* st = smem + (ks % S) * Sh::STAGE;
@@ -218,6 +245,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         const int chunk = FAM == FAM_WNA16 ? 4 * (lane >> 4) + d : 4 * d + (lane >> 4);
         af[mb][d] = read_a(st, mb, chunk);
       }
+    if constexpr (Sh::ASC_BYTES > 0) {
+      const uint8_t* sa = sm + Sh::META_BYTES;
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb)
+        asf[mb] = sa[(wm * 16 * MW + 16 * mb + (lane & 15)) * 4 + (lane >> 4)];
+    }
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
 #pragma unroll
@@ -225,7 +258,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       const int tw = wn * NTW + t;
       if constexpr (FAM == FAM_WNA16)
         meta[t] = *reinterpret_cast<const uint16_t*>(sm + tw * 32 + 2 * (lane & 15));
-      else if constexpr (FAM == FAM_W4A8)
+      else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4)
         meta[t] = sm[tw * 64 + lane];
     }
   };
@@ -275,6 +308,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
           for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_i8(af[mb][q], bq[t][q], acc[mb][t]);
+    } else if constexpr (FAM == FAM_W4A4) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb)
+          acc[mb][t] = mfma_fp4_fp4(af[mb][0], asf[mb], bq[t][0], int(meta[t]), acc[mb][t]);
     } else {
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
@@ -373,6 +412,7 @@ int pp_lds_bytes(int fam, int cfg) {
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);
+  if (fam == FAM_W4A4) return pp_lds_table<FAM_W4A4>(cfg, seq);
   return pp_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -410,6 +450,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return launch_pp_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
 }
 

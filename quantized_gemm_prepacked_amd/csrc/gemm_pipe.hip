@@ -297,7 +297,8 @@ int pipe_lds_bytes(int fam, int cfg) {
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return pipe_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return pipe_lds_table<FAM_W8A8>(cfg, seq);
-  return pipe_lds_table<FAM_W4A8>(cfg, seq);
+  if (fam == FAM_W4A8) return pipe_lds_table<FAM_W4A8>(cfg, seq);
+  return 1 << 30;   // no W4A4 instantiation
 }
 
 template <int FAM, bool MOE, int I>
@@ -332,7 +333,8 @@ hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, 
                                    : launch_pipe_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_pipe_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
-  return launch_pipe_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W4A8) return launch_pipe_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hq

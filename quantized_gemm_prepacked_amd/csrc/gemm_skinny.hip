@@ -31,37 +31,44 @@ namespace {
 
 template <int FAM>
 struct SkTraits;
+// kRowBytes: activation bytes per row per unit of kUnitK k; kAScaleBytes: activation block-scale
+// bytes per row per unit (MXFP4 activations: one e8m0 byte per 32 k).
 template <>
 struct SkTraits<FAM_WNA16> {
-  static constexpr int kABytes = 2, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8;
+  static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
 };
 template <>
 struct SkTraits<FAM_W8A8> {
-  static constexpr int kABytes = 1, kUnitK = 64, kScaleBytes = 0, kZeroBytes = 0;
+  static constexpr int kRowBytes = 64, kUnitK = 64, kScaleBytes = 0, kZeroBytes = 0, kAScaleBytes = 0;
 };
 template <>
 struct SkTraits<FAM_W4A8> {
-  static constexpr int kABytes = 1, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0;
+  static constexpr int kRowBytes = 128, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 0;
+};
+template <>
+struct SkTraits<FAM_W4A4> {
+  static constexpr int kRowBytes = 64, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 4;
 };
 
 template <int FAM, int MB, int NTW, int NW, int UNR, bool PP>
 struct SkShape {
   using T = SkTraits<FAM>;
-  static constexpr int ROWB = T::kUnitK * T::kABytes;    // activation bytes per row per unit
+  static constexpr int ROWB = T::kRowBytes;              // activation bytes per row per unit
   static constexpr int CPR = ROWB / 16;
   static constexpr int A_UNIT = 16 * MB * ROWB;
   static constexpr int A_INSTR = A_UNIT / 1024;         // copies of a unit's activation rows
   static constexpr int SC = NTW * T::kScaleBytes;       // per unit, all tiles
   static constexpr int ZB = NTW * T::kZeroBytes;
-  static constexpr int META_INSTR = (SC ? 1 : 0) + (ZB ? 1 : 0);
-  static constexpr int UNIT_LDS = (A_UNIT + SC + ZB + 15) / 16 * 16;
+  static constexpr int ASC = 16 * MB * T::kAScaleBytes;   // activation block scales per unit
+  static constexpr int META_INSTR = (SC ? 1 : 0) + (ZB ? 1 : 0) + (ASC ? 1 : 0);
+  static constexpr int UNIT_LDS = (A_UNIT + SC + ZB + ASC + 15) / 16 * 16;
   static constexpr int NBUF = PP ? 2 : 1;
   static constexpr int WAVE_LDS = NBUF * UNR * UNIT_LDS;
   static constexpr int RED = NW * MB * NTW * 4 * 64 * 4; // epilogue reduction (aliases the slots)
   static constexpr int LDS = (NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED);
   static constexpr int UNIT_INSTR = A_INSTR + NTW + META_INSTR;   // vector-memory ops per unit
   static_assert(A_UNIT % 1024 == 0, "whole-wave activation copies");
-  static_assert(SC / 16 <= 64 && ZB / 4 <= 64, "metadata copies fit one instruction each");
+  static_assert(SC / 16 <= 64 && ZB / 4 <= 64 && ASC / 4 <= 64, "metadata copies fit one instruction each");
   static_assert(UNR * UNIT_INSTR < 64, "vmcnt range");
 };
 
@@ -92,6 +99,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   // [16*MB rows][CPR chunks] block; position (r, slot) holds source chunk swizzle(r, slot). Rows
   // past M (MoE: padding) read a valid row and are never stored, so every lane copies.
   const uint8_t* asrc[Sh::A_INSTR];
+  const size_t a_row_bytes = size_t(p.K) / T::kUnitK * ROWB;
 #pragma unroll
   for (int j = 0; j < Sh::A_INSTR; ++j) {
     const int q = 64 * j + lane;
@@ -104,7 +112,14 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     } else {
       src_row = min(row0 + r, p.M - 1);
     }
-    asrc[j] = p.a + size_t(src_row) * p.K * T::kABytes + 16 * c;
+    asrc[j] = p.a + size_t(src_row) * a_row_bytes + 16 * c;
+  }
+  // MXFP4 activations: lane r < 16*MB copies the 4 e8m0 bytes of row r for each unit
+  const uint8_t* ascale_src = nullptr;
+  if constexpr (Sh::ASC > 0) {
+    const int r = min(lane, 16 * MB - 1);
+    const int src_row = min(row0 + r, p.M - 1);
+    ascale_src = reinterpret_cast<const uint8_t*>(p.a_scale) + size_t(src_row) * (p.K / 32);
   }
 
   Acc acc[MB][NTW];
@@ -142,6 +157,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
       const uint8_t* src = p.asym ? w + p.zeros_off + unit * 8 + 4 * (lane & 1)
                                   : w + p.scales_off + unit * T::kScaleBytes;
       if (lane < Sh::ZB / 4) lds_dma4(src, slot + Sh::A_UNIT + Sh::SC);
+    }
+    if constexpr (Sh::ASC > 0) {
+      if (lane < 16 * MB) lds_dma4(ascale_src + 4 * u, slot + Sh::A_UNIT + Sh::SC + Sh::ZB);
     }
   };
 
@@ -198,6 +216,19 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
         const u32x4 av = read_a(mb, lane >> 4);
 #pragma unroll
         for (int t = 0; t < NTW; ++t) acc[mb][t] = mfma_i8(av, bw[buf][r][t], acc[mb][t]);
+      }
+    } else if constexpr (FAM == FAM_W4A4) {
+      // fp4 A operand: lane group g holds the row's k 32g..32g+31 (chunk g) and that block's
+      // e8m0 scale
+      const uint8_t* sc = slot + Sh::A_UNIT;
+      const uint8_t* asc = sc + Sh::SC + Sh::ZB;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 av = read_a(mb, lane >> 4);
+        const int sa = asc[(16 * mb + (lane & 15)) * 4 + (lane >> 4)];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          acc[mb][t] = mfma_fp4_fp4(av, sa, bw[buf][r][t], int(sc[t * 64 + lane]), acc[mb][t]);
       }
     } else {
       // 8-bit A operand of the scaled MFMA: lane group g holds chunks g and 4 + g
@@ -352,6 +383,7 @@ int skinny_lds_bytes(int fam, int cfg) {
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return skinny_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return skinny_lds_table<FAM_W8A8>(cfg, seq);
+  if (fam == FAM_W4A4) return skinny_lds_table<FAM_W4A4>(cfg, seq);
   return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -391,6 +423,7 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
                                    : launch_skinny_fam<FAM_WNA16, false>(p, cfg, grid, s);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
+  if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);
   return launch_skinny_fam<FAM_W4A8, false>(p, cfg, grid, s);
 }
 

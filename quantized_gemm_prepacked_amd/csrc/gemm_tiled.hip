@@ -282,7 +282,8 @@ hipError_t launch_tiled(const KParams& p, int fam, bool moe, int cfg, dim3 grid,
                                    : launch_tiled_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_tiled_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s);
-  return launch_tiled_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s);
+  if (fam == FAM_W4A8) return launch_tiled_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s);
+  return hipErrorInvalidValue;   // W4A4 runs on the skinny and ping-pong kernels only
 }
 
 }  // namespace hq

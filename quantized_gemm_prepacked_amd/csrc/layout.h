@@ -33,7 +33,8 @@
 
 namespace hq {
 
-enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2 };
+// W4A4 shares W4A8's prepacked weights (MXFP4); only the activation operand differs.
+enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3 };
 
 constexpr int kUnitBytes = 1024;
 constexpr int kTileN = 16;

@@ -115,7 +115,7 @@ __device__ __forceinline__ void store_tile(const KParams& p, const typename AccT
       }
       orow[mb][i] = o;
       tw[mb][i] = wgt;
-      rs[mb][i] = (FAM != FAM_WNA16 && o >= 0) ? p.a_scale[s] : 1.0f;
+      rs[mb][i] = ((FAM == FAM_W8A8 || FAM == FAM_W4A8) && o >= 0) ? p.a_scale[s] : 1.0f;
     }
   float cs[NTW];
 #pragma unroll

@@ -227,6 +227,20 @@ def make_w4a8(config_id: int, M: int, N: int, K: int):
     return {**make_w4a8_activations(config_id, M, K), **qw}
 
 
+def make_w4a4_activations(config_id: int, M: int, K: int):
+    """MXFP4 activations (e2m1 codes + e8m0 per 32 k) quantized from bf16 N(0,1) by the OCP MX
+    rule (the same quantizer as the weights')."""
+    x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))
+    q = quantize_mxfp4(x)
+    return {"xq": q["wq"], "xs": q["scales"]}
+
+
+def make_w4a4(config_id: int, M: int, N: int, K: int):
+    """Dense W4A4-MXFP4: MXFP4 weights (as W4A8) and MXFP4 activations from bf16 N(0,1)."""
+    w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    return {**make_w4a4_activations(config_id, M, K), **quantize_mxfp4(w)}
+
+
 def random_int4_sym_expert(g: np.random.Generator, N: int, K: int, gs: int = 128):
     """Standard-format symmetric INT4 weights with uniformly random codes and bf16 scales near
     absmax/7 of N(0, 0.02) groups. Used where only the data volume matters (throughput runs
