@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | moe | moe_layer.
+--config w8a8 | w4a8 | w4a4 | moe | moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantized GEMM TFLOPS and HBM GB/s vs roofline over M=1..8192; MoE tokens/s"
 HBM_PEAK_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "int8": 5000.0, "fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "int8": 5000.0, "fp8": 5000.0, "fp4": 10100.0}
 
 WORKLOADS = {
     "w4a16": dict(name="dense W4A16 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
@@ -38,6 +38,8 @@ WORKLOADS = {
                  dtype="int8", peak="int8"),
     "w4a8": dict(name="dense W4A8-MXFP4", N=4096, K=7168, Ms=[1, 32, 256, 2048, 8192], cfg=4,
                  dtype="fp8", peak="fp8"),
+    "w4a4": dict(name="dense W4A4-MXFP4", N=4096, K=7168, Ms=[1, 32, 256, 2048, 8192], cfg=4,
+                 dtype="fp4", peak="fp4"),
 }
 
 
@@ -82,6 +84,8 @@ def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
         return w + M * K * 2 + M * N * 2
     if wl == "w8a8":
         return N * K + N * 4 + M * K + M * 4 + M * N * 2
+    if wl == "w4a4":
+        return N * K // 2 + N * (K // 32) + M * K // 2 + M * (K // 32) + M * N * 2
     return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
 
 
@@ -104,6 +108,14 @@ def make_inputs(wl: str, spec: dict):
         for M in spec["Ms"]:
             a = synth.make_w8a8_activations(cfg, M, K)
             acts[M] = (a["xq"], a["s_tok"])
+    elif wl == "w4a4":
+        d = synth.make_w4a4(cfg, 1, N, K)
+        desc = hq.DESC_W4A4_MXFP4
+        std = (d["wq"], d["scales"], None)
+        acts = {}
+        for M in spec["Ms"]:
+            a = synth.make_w4a4_activations(cfg, M, K)
+            acts[M] = (a["xq"], a["xs"])      # the e8m0 block scales travel as a_scale
     else:
         d = synth.make_w4a8(cfg, 1, N, K)
         desc = hq.DESC_W4A8_MXFP4
@@ -140,6 +152,8 @@ def cpu_baseline(wl: str, spec: dict, std, acts):
             oracle.ref_wna16(x, std[0], std[1], std[2], 128, rows=rows)
         elif wl == "w8a8":
             oracle.ref_w8a8(x, s, std[0], std[1], rows=rows)
+        elif wl == "w4a4":
+            oracle.ref_w4a4(x, s, std[0], std[1], rows=rows)
         else:
             oracle.ref_w4a8(x, s, std[0], std[1], rows=rows)
         dt = time.perf_counter() - t0
@@ -171,7 +185,7 @@ def run_dense(args, wl: str):
     for M in Ms:
         x, s = acts[M]
         xt = torch.from_numpy(np.ascontiguousarray(x).view(np.uint8)).to(dev)
-        st = None if s is None else torch.from_numpy(s).to(dev)
+        st = None if s is None else torch.from_numpy(np.ascontiguousarray(s).reshape(-1)).to(dev)
         dev_acts[M] = (xt, st)
         outs[M] = torch.empty((M, N), dtype=torch.int16, device=dev)
         nb = hq.hq_gemm_workspace_bytes(desc, M, N, K)
@@ -253,15 +267,16 @@ def run_dense(args, wl: str):
                       "frac": round(max(frac_c, frac_m), 4), "bytes": by, "flops": fl})
         tot_flops += fl
         tot_s += us * 1e-6
-    if wl in ("w8a8", "w4a8"):
-        # The step before these GEMMs (per-token quantization of bf16 activations), timed the same
+    if wl in ("w8a8", "w4a8", "w4a4"):
+        # The step before these GEMMs (dynamic quantization of bf16 activations), timed the same
         # way for context; it is not part of `value`.
-        act = hq.HQ_ACT_INT8_PER_TOKEN if wl == "w8a8" else hq.HQ_ACT_FP8E4M3_PER_TOKEN
+        act = {"w8a8": hq.HQ_ACT_INT8_PER_TOKEN, "w4a8": hq.HQ_ACT_FP8E4M3_PER_TOKEN,
+               "w4a4": hq.HQ_ACT_MXFP4}[wl]
         for row in sweep:
             M = row["M"]
             xb = torch.randn(M, K, device=dev).to(torch.bfloat16)
             xq = torch.empty(M, K, dtype=torch.uint8, device=dev)
-            sq = torch.empty(M, dtype=torch.float32, device=dev)
+            sq = torch.empty(max(M, M * K // 128), dtype=torch.float32, device=dev)
             r = 32
             gq = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gq):
@@ -296,7 +311,8 @@ def run_dense(args, wl: str):
         "config": {"workload": spec["name"], "N": N, "K": K, "M": Ms,
                    "weights": {"w4a16": "uint4 asym g128 bf16 scale + uint4 zero",
                                "w8a8": "int8 per-channel fp32 scale, int8 per-token act",
-                               "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act"}[wl]},
+                               "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act",
+                               "w4a4": "mxfp4 e2m1 + e8m0 per 32, mxfp4 act (e8m0 per 32)"}[wl]},
         "roofline": roof,
         "sweep": sweep,
     }

@@ -46,6 +46,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return first_fit({29, 22, 3, 7, 8});
   }
   if (c.fam == FAM_WNA16) return first_fit({5, 4, 6});
+  if (c.fam == FAM_W4A4 && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
   return first_fit({4, 5, 6});
 }
 
@@ -118,8 +119,10 @@ constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
 constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
-// W4A4 runs on the skinny and ping-pong kernels only
-constexpr RangeEntry kW4a4Table[] = {{256, 0, 0}, {kInf, 3, 0}};
+// W4A4 runs on the skinny and ping-pong kernels only (measured at N=4096, K=7168: skinny 64-row
+// blocks up to M=512 at 34 us vs 56 us on ping-pong 128x128, which wins from M=2048 on; 128x256
+// at M=8192)
+constexpr RangeEntry kW4a4Table[] = {{768, 0, 0}, {4096, 3, 2}, {kInf, 3, 0}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
