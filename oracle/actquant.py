@@ -23,6 +23,10 @@ block of 32 consecutive k (the MXFP4 format the announcement's W4A4 path consume
     code   = nearest e2m1 value to v, ties to the even code, saturating at +-6; the sign bit is
              set only for a non-zero magnitude (a negative value that rounds to zero gives +0)
 
+MXFP8 activations (e4m3 elements, for W4A8 with MX activations) take the same rule with the
+largest e4m3 exponent, 8: e = floor(log2(max |x|)) - 8 clamped to [-127, 127], v = x * 2^-e,
+code = the e4m3 encoding above of clamp(v, -448, 448) (|v| < 512 always).
+
 Both divisions are binary32 on purpose: the codes are integers decided by floating point, and
 the kernel takes that decision in binary32, so the reference takes it in the same precision
 (numpy float32 division is IEEE correctly rounded).
@@ -113,3 +117,23 @@ def quantize_mxfp4_act(x_bf16: np.ndarray):
     codes = encode_e2m1(v).reshape(M, K)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return packed, (e + 127).astype(np.uint8)
+
+
+def _mx_block_exponent(blocks: np.ndarray, emax: int) -> np.ndarray:
+    amax = np.abs(blocks).max(axis=2)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.floor(np.log2(amax[nz])).astype(np.int64) - emax
+    return np.clip(e, -127, 127)
+
+
+def quantize_mxfp8_act(x_bf16: np.ndarray):
+    """x_bf16: uint16 bf16 bits [M, K] (K % 32 == 0). Returns (e4m3 codes uint8 [M, K], e8m0
+    scale bytes uint8 [M, K/32])."""
+    x = decode_bf16(x_bf16)
+    M, K = x.shape
+    blocks = x.reshape(M, K // 32, 32)
+    e = _mx_block_exponent(blocks, 8)
+    v = blocks * np.ldexp(1.0, -e)[:, :, None]
+    codes = encode_e4m3(np.clip(v, -448.0, 448.0)).reshape(M, K)
+    return codes, (e + 127).astype(np.uint8)

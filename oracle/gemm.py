@@ -103,3 +103,16 @@ def ref_w4a4(xq: np.ndarray, xs_e8m0: np.ndarray, wq: np.ndarray, scales_e8m0: n
     w = dequant_mxfp4(wq, scales_e8m0, cols)
     y = x @ w.T
     return y, round_to_bf16(y)
+
+
+def ref_w4a8_mx(xq: np.ndarray, xs_e8m0: np.ndarray, wq: np.ndarray, scales_e8m0: np.ndarray,
+                rows=None, cols=None):
+    """W4A8 with MXFP8 activations: x[m, k] = e4m3(xq[m, k]) * 2^(xs[m, k // 32] - 127) (an e8m0
+    scale per 32-element block instead of a per-token fp32 scale), w = dequant_mxfp4; the sum is
+    exact in float64. Returns (y float64, y bf16 bits)."""
+    xc = decode_e4m3(_sel(xq, rows))
+    K = xc.shape[1]
+    x = xc * decode_e8m0(_sel(xs_e8m0, rows))[:, np.arange(K) // 32]
+    w = dequant_mxfp4(wq, scales_e8m0, cols)
+    y = x @ w.T
+    return y, round_to_bf16(y)
