@@ -70,8 +70,10 @@ typedef enum {
   HQ_ACT_BF16 = 0,             /* bf16 [M, K] row-major, no activation scale          */
   HQ_ACT_INT8_PER_TOKEN = 1,   /* int8 [M, K] row-major + fp32 scale per row [M]      */
   HQ_ACT_FP8E4M3_PER_TOKEN = 2, /* OCP e4m3 [M, K] row-major + fp32 scale per row [M] */
-  HQ_ACT_MXFP4 = 3              /* OCP MX e2m1 [M, K/2] (low nibble = even k) + e8m0 byte per
+  HQ_ACT_MXFP4 = 3,             /* OCP MX e2m1 [M, K/2] (low nibble = even k) + e8m0 byte per
                                    (row, 32-element block) [M, K/32]                        */
+  HQ_ACT_MXFP8 = 4              /* OCP MX e4m3 [M, K] + e8m0 byte per (row, 32-element block)
+                                   [M, K/32]                                                 */
 } hq_act_fmt;
 
 typedef enum {
@@ -110,6 +112,9 @@ typedef struct {
  *   e4m3     : xq = nearest OCP e4m3 code to clamp(v, -448, 448), ties to the even code
  *              (negative values that round to zero give -0, 0x80)
  * act_fmt  HQ_ACT_INT8_PER_TOKEN or HQ_ACT_FP8E4M3_PER_TOKEN (the desc act_fmt of the GEMM), or
+ *          HQ_ACT_MXFP8: the same rule with e4m3 elements -- e = floor(log2 max|x|) - 8, code =
+ *            e4m3 of clamp(x * 2^-e, -448, 448) as above; xq is e4m3 [M, K], s_tok receives
+ *            the e8m0 bytes [M, K/32] (cast); K % 32 == 0. Or
  *          HQ_ACT_MXFP4 (W4A4), which follows the OCP Microscaling rule per row and block of 32 k:
  *            e = floor(log2 max|x|) - 2 clamped to [-127, 127] (-127 for a zero block),
  *            scale byte e + 127, code = nearest e2m1 to x * 2^-e (ties to even, saturating at 6;
@@ -146,7 +151,7 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
  * Dense GEMM (device):  y[m, n] = epilogue( sum_k a[m, k] * w[n, k] ),  0 <= m < M, 0 <= n < N
  *   a        activations, format desc->act_fmt, [M, K] row-major (device)
  *   a_scale  fp32 [M] per-token scales for INT8/FP8 activations (device); NULL for BF16.
- *            MXFP4 activations (W4A4): the e8m0 block-scale bytes, uint8 [M, K/32] row-major,
+ *            MXFP4 / MXFP8 activations: the e8m0 block-scale bytes, uint8 [M, K/32] row-major,
  *            passed through this pointer (cast) -- the activations' own scale tensor
  *   w_packed the prepacked weights of ONE layer (E = 1) (device)
  *   y        [M, N] row-major, bf16 or int32 per desc->out_fmt (device)
@@ -157,6 +162,8 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
  *             W4A8 : bf16( a_scale[m] * sum_k e4m3(a) * e2m1(q) * 2^(e - 127) ) (fp32 accumulation)
  *             W4A4 : bf16( sum_k e2m1(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation;
  *                    weights as W4A8, desc act_fmt HQ_ACT_MXFP4)
+ *             W4A8 with MXFP8 activations (desc act_fmt HQ_ACT_MXFP8):
+ *                    bf16( sum_k e4m3(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation)
  * All bf16 results use round-to-nearest-even. M = 0 is a no-op returning HQ_OK.
  * ------------------------------------------------------------------------------------------- */
 size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K);

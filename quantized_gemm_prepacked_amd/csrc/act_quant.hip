@@ -144,6 +144,50 @@ __global__ __launch_bounds__(kThreads) void act_quant_mxfp4_kernel(const uint16_
   *reinterpret_cast<u32x4*>(xq + b * 16) = u32x4{out[0], out[1], out[2], out[3]};
 }
 
+// MXFP8 activations: the same block rule with e4m3 elements (largest exponent 8), codes by the
+// per-token path's e4m3 encoder on clamp(x * 2^-e, -448, 448); the sign is kept (-0 = 0x80).
+__global__ __launch_bounds__(kThreads) void act_quant_mxfp8_kernel(const uint16_t* __restrict__ x,
+                                                                   uint8_t* __restrict__ xq,
+                                                                   uint8_t* __restrict__ xs,
+                                                                   int64_t n_blocks) {
+  const int64_t b = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (b >= n_blocks) return;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ldg16(x + b * 32 + 8 * i);
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
+  const int ef = int(amax >> 7);
+  const int e = ef == 0 ? -127 : max(ef - 127 - 8, -127);
+  xs[b] = uint8_t(e + 127);
+  const float inv = __uint_as_float(uint32_t(127 - e) << 23);   // 2^-e, e in [-127, 119]
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * h2 + j;                      // element k of the 8 in v[i]
+        const uint32_t h = (v[i][k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+        const uint32_t mag = h & 0x7FFFu;
+        const float a = (mag >> 7) != 0 ? __uint_as_float(mag << 16) * inv
+                        : e <= -7      ? float(mag) * __uint_as_float(uint32_t(-6 - e) << 23)
+                                       : 0.0f;
+        const float sv = __uint_as_float(__float_as_uint(fminf(a, 448.0f)) | ((h & 0x8000u) << 16));
+        word |= e4m3_rne(sv) << (8 * j);
+      }
+      out[2 * i + h2] = word;
+    }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(xq + b * 32);
+  *reinterpret_cast<u32x4*>(dst) = u32x4{out[0], out[1], out[2], out[3]};
+  *reinterpret_cast<u32x4*>(dst + 4) = u32x4{out[4], out[5], out[6], out[7]};
+}
+
 }  // namespace
 
 hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, void* xq, float* s_tok,
@@ -151,6 +195,12 @@ hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, vo
   const dim3 grid{static_cast<unsigned>(M)};
   const auto* xin = static_cast<const uint16_t*>(x);
   auto* out = static_cast<uint8_t*>(xq);
+  if (act_fmt == HQ_ACT_MXFP8) {
+    const int64_t nb = M * (K / 32);
+    hipLaunchKernelGGL(act_quant_mxfp8_kernel, dim3(unsigned((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, xin, out, reinterpret_cast<uint8_t*>(s_tok), nb);
+    return hipGetLastError();
+  }
   if (act_fmt == HQ_ACT_MXFP4) {
     const int64_t nb = M * (K / 32);
     hipLaunchKernelGGL(act_quant_mxfp4_kernel, dim3(unsigned((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0,

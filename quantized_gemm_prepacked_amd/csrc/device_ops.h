@@ -107,11 +107,11 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
 // The e8m0 scale of K block b (k in [32b, 32b+32)) is taken from lane group b's scale register,
 // for A and for B alike. A is passed unscaled (127 = 2^0); B's scale is the weight block's.
 __device__ __forceinline__ f32x4 mfma_fp8_fp4(u32x4 a_lo, u32x4 a_hi, u32x4 b, int b_scale,
-                                              f32x4 c) {
+                                              f32x4 c, int a_scale = 127) {
   i32x8 av = {int(a_lo[0]), int(a_lo[1]), int(a_lo[2]), int(a_lo[3]),
               int(a_hi[0]), int(a_hi[1]), int(a_hi[2]), int(a_hi[3])};
   i32x8 bv = {int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, 127, 0, b_scale);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, a_scale, 0, b_scale);
 }
 
 // Both operands fp4 e2m1 (formats 4 and 4), each with its own e8m0 block scales: 4-bit A takes

@@ -61,7 +61,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, int orow, int srow, i
     }
   } else if constexpr (FAM == FAM_W4A8) {
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * p.a_scale[srow] * tw);
-  } else {   // W4A4: both block scales were applied by the MFMA
+  } else {   // W4A4, W4A8MX: both block scales were applied by the MFMA
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * tw);
   }
 }

@@ -37,16 +37,16 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   if (rows <= 16) {
     if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
     if (c.fam == FAM_W4A8) return first_fit({21, 2});
-    if (c.fam == FAM_W4A4) return first_fit({21, 2});
+    if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({21, 2});
     return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
-    if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4) return first_fit({16, 8});
+    if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({16, 8});
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
   if (c.fam == FAM_WNA16) return first_fit({5, 4, 6});
-  if (c.fam == FAM_W4A4 && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
+  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
   return first_fit({4, 5, 6});
 }
 
@@ -92,6 +92,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W8A8>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_W4A4)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A4>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_W4A8MX)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8MX>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -119,7 +121,8 @@ constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
 constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
-// W4A4 runs on the skinny and ping-pong kernels only (measured at N=4096, K=7168: skinny 64-row
+// W4A4 (and W4A8 with MXFP8 activations, until measured on its own) run on the skinny and
+// ping-pong kernels only (W4A4 measured at N=4096, K=7168: skinny 64-row
 // blocks up to M=512 at 34 us vs 56 us on ping-pong 128x128, which wins from M=2048 on; 128x256
 // at M=8192)
 constexpr RangeEntry kW4a4Table[] = {{768, 0, 0}, {4096, 3, 2}, {kInf, 3, 0}};
@@ -149,7 +152,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_W8A8) {
     t = kW8a8Table;
     n = int(sizeof(kW8a8Table) / sizeof(kW8a8Table[0]));
-  } else if (c.fam == FAM_W4A4) {
+  } else if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) {
     t = kW4a4Table;
     n = int(sizeof(kW4a4Table) / sizeof(kW4a4Table[0]));
   } else {
@@ -165,7 +168,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
     return t[i];
   }
   // Fallbacks when the preferred tile does not divide N.
-  if (c.fam == FAM_W4A4) {
+  if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
     for (int cfg : {3, 2})   // 128 x 128 tiles
@@ -189,7 +192,7 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
     return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
-  if (c.fam == FAM_W4A4 && (o.kind == 1 || o.kind == 2)) return false;
+  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && (o.kind == 1 || o.kind == 2)) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -245,7 +248,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   // The direct-to-LDS kernels address activations with 32-bit offsets.
   if ((pick.kind == 2 || pick.kind == 3) &&
       uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) >= (uint64_t(1) << 32)) {
-    const int tc = c.fam == FAM_W4A4 ? -1 : pick_tiled(c, N, K);
+    const int tc = (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) ? -1 : pick_tiled(c, N, K);
     pick = tc >= 0 ? RangeEntry{kInf, 1, tc} : RangeEntry{0, 0, 0};
   }
   if (pick.kind != 0) {

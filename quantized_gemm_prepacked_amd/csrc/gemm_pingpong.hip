@@ -59,6 +59,13 @@ struct PPTraits<FAM_W4A8> {
   static constexpr int kAScaleBytes = 0;
 };
 template <>
+struct PPTraits<FAM_W4A8MX> {
+  static constexpr int kRowBytes = 128;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 64;
+  static constexpr int kAScaleBytes = 4;
+};
+template <>
 struct PPTraits<FAM_W4A4> {
   static constexpr int kRowBytes = 64;
   static constexpr int kUnitsPerStep = 1;
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       const int tw = wn * NTW + t;
       if constexpr (FAM == FAM_WNA16)
         meta[t] = *reinterpret_cast<const uint16_t*>(sm + tw * 32 + 2 * (lane & 15));
-      else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4)
+      else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX)
         meta[t] = sm[tw * 64 + lane];
     }
   };
@@ -314,6 +321,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 #pragma unroll
         for (int mb = 0; mb < MW; ++mb)
           acc[mb][t] = mfma_fp4_fp4(af[mb][0], asf[mb], bq[t][0], int(meta[t]), acc[mb][t]);
+    } else if constexpr (FAM == FAM_W4A8MX) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb)
+          acc[mb][t] = mfma_fp8_fp4(af[mb][0], af[mb][1], bq[t][0], int(meta[t]), acc[mb][t], asf[mb]);
     } else {
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
@@ -413,6 +426,7 @@ int pp_lds_bytes(int fam, int cfg) {
   if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return pp_lds_table<FAM_W4A4>(cfg, seq);
+  if (fam == FAM_W4A8MX) return pp_lds_table<FAM_W4A8MX>(cfg, seq);
   return pp_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -451,6 +465,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return launch_pp_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
 }
 

@@ -46,6 +46,10 @@ struct SkTraits<FAM_W4A8> {
   static constexpr int kRowBytes = 128, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 0;
 };
 template <>
+struct SkTraits<FAM_W4A8MX> {
+  static constexpr int kRowBytes = 128, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 4;
+};
+template <>
 struct SkTraits<FAM_W4A4> {
   static constexpr int kRowBytes = 64, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 4;
 };
@@ -231,15 +235,19 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
           acc[mb][t] = mfma_fp4_fp4(av, sa, bw[buf][r][t], int(sc[t * 64 + lane]), acc[mb][t]);
       }
     } else {
-      // 8-bit A operand of the scaled MFMA: lane group g holds chunks g and 4 + g
+      // 8-bit A operand of the scaled MFMA: lane group g holds chunks g and 4 + g; the scale of
+      // k block b comes from lane group b (MXFP8 activations: the row's block scale; per-token
+      // FP8: 2^0, the token scale is applied in the epilogue)
       const uint8_t* sc = slot + Sh::A_UNIT;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const u32x4 alo = read_a(mb, lane >> 4);
         const u32x4 ahi = read_a(mb, 4 + (lane >> 4));
+        int sa = 127;
+        if constexpr (Sh::ASC > 0) sa = sc[Sh::SC + Sh::ZB + (16 * mb + (lane & 15)) * 4 + (lane >> 4)];
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
-          acc[mb][t] = mfma_fp8_fp4(alo, ahi, bw[buf][r][t], int(sc[t * 64 + lane]), acc[mb][t]);
+          acc[mb][t] = mfma_fp8_fp4(alo, ahi, bw[buf][r][t], int(sc[t * 64 + lane]), acc[mb][t], sa);
       }
     }
   };
@@ -384,6 +392,7 @@ int skinny_lds_bytes(int fam, int cfg) {
   if (fam == FAM_WNA16) return skinny_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return skinny_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return skinny_lds_table<FAM_W4A4>(cfg, seq);
+  if (fam == FAM_W4A8MX) return skinny_lds_table<FAM_W4A8MX>(cfg, seq);
   return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -424,6 +433,7 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);
+  if (fam == FAM_W4A8MX) return launch_skinny_fam<FAM_W4A8MX, false>(p, cfg, grid, s);
   return launch_skinny_fam<FAM_W4A8, false>(p, cfg, grid, s);
 }
 

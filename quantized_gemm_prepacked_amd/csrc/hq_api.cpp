@@ -72,11 +72,13 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
       return HQ_OK;
     case HQ_W_FP4_E2M1:
       if (d->group_size != 32 || d->scale_dtype != HQ_SCALE_E8M0 || d->has_zero_point != 0 ||
-          (d->act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN && d->act_fmt != HQ_ACT_MXFP4) || c->out_i32)
+          (d->act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN && d->act_fmt != HQ_ACT_MXFP4 &&
+           d->act_fmt != HQ_ACT_MXFP8) || c->out_i32)
         return fail(HQ_ERR_UNSUPPORTED,
                     "FP4 weights need group_size 32, E8M0 scales, no zero-point, per-token FP8 "
-                    "e4m3 or MXFP4 activations and bf16 output");
-      c->fam = d->act_fmt == HQ_ACT_MXFP4 ? hq::FAM_W4A4 : hq::FAM_W4A8;
+                    "e4m3, MXFP8 or MXFP4 activations and bf16 output");
+      c->fam = d->act_fmt == HQ_ACT_MXFP4 ? hq::FAM_W4A4
+               : d->act_fmt == HQ_ACT_MXFP8 ? hq::FAM_W4A8MX : hq::FAM_W4A8;
       return HQ_OK;
     default:
       return fail(HQ_ERR_INVALID_ARGUMENT, "unknown weight_fmt %d", d->weight_fmt);
@@ -209,14 +211,16 @@ hq_status hq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t
 
 hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const void* x, void* xq,
                                   float* s_tok, hq_stream_t stream) {
-  if (act_fmt != HQ_ACT_INT8_PER_TOKEN && act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN && act_fmt != HQ_ACT_MXFP4)
-    return fail(HQ_ERR_UNSUPPORTED, "act_fmt=%d: INT8 or FP8 e4m3 per-token, or MXFP4", act_fmt);
+  if (act_fmt != HQ_ACT_INT8_PER_TOKEN && act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN && act_fmt != HQ_ACT_MXFP4 &&
+      act_fmt != HQ_ACT_MXFP8)
+    return fail(HQ_ERR_UNSUPPORTED, "act_fmt=%d: INT8 or FP8 e4m3 per-token, MXFP8 or MXFP4", act_fmt);
+  const bool mx = act_fmt == HQ_ACT_MXFP4 || act_fmt == HQ_ACT_MXFP8;
   if (M < 0 || M > kMaxDim || K <= 0 || K > kMaxDim)
     return fail(HQ_ERR_INVALID_ARGUMENT, "M=%lld K=%lld out of range", (long long)M, (long long)K);
   if (K % 8 != 0) return fail(HQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 8", (long long)K);
-  if (act_fmt == HQ_ACT_MXFP4 && K % 32 != 0)
-    return fail(HQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 32 for MXFP4", (long long)K);
-  if (act_fmt == HQ_ACT_MXFP4 && M * (K / 32) >= (int64_t(1) << 40))
+  if (mx && K % 32 != 0)
+    return fail(HQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 32 for MX activations", (long long)K);
+  if (mx && M * (K / 32) >= (int64_t(1) << 40))
     return fail(HQ_ERR_UNSUPPORTED, "M*K/32 must stay below 2^40");
   if (M == 0) return ok();
   if (!x || !xq || !s_tok) return fail(HQ_ERR_INVALID_ARGUMENT, "x, xq and s_tok must be non-NULL");

@@ -227,6 +227,30 @@ def make_w4a8(config_id: int, M: int, N: int, K: int):
     return {**make_w4a8_activations(config_id, M, K), **qw}
 
 
+def quantize_mxfp8_rows(x: np.ndarray):
+    """MXFP8 (OCP MX): e4m3 elements in 32-element blocks along K with an e8m0 shared exponent
+    floor(log2 amax) - 8; elements by torch's e4m3 cast of the clamped scaled values.
+    Returns codes uint8 [M, K], scales uint8 [M, K/32]."""
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    xb = x.reshape(M, K // 32, 32)
+    amax = np.abs(xb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8.0
+    e = np.where(amax > 0, np.clip(e, -127, 127), -127)
+    v = np.clip(xb / np.exp2(e)[:, :, None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(v.reshape(M, K)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes.copy(), (e + 127).astype(np.uint8)
+
+
+def make_w4a8mx(config_id: int, M: int, N: int, K: int):
+    """W4A8 with MXFP8 activations: MXFP4 weights (as W4A8), MXFP8 activations from bf16 N(0,1)."""
+    w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))
+    xq, xs = quantize_mxfp8_rows(x)
+    return {"xq": xq, "xs": xs, **quantize_mxfp4(w)}
+
+
 def make_w4a4_activations(config_id: int, M: int, K: int):
     """MXFP4 activations (e2m1 codes + e8m0 per 32 k) quantized from bf16 N(0,1) by the OCP MX
     rule (the same quantizer as the weights')."""

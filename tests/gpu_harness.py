@@ -7,6 +7,7 @@ import sys
 import numpy as np
 import torch
 
+import oracle
 import quantized_gemm_prepacked_amd as hq
 
 DEV = "cuda:0"
@@ -50,14 +51,24 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def check_float(y_bits: np.ndarray, ref64: np.ndarray, what: str):
+def check_float(y_bits: np.ndarray, ref64: np.ndarray, what: str, rounding_floor: bool = False):
+    """The float bar. rounding_floor: for outputs so heavy-tailed that rounding the exact result
+    once to bf16 already moves it by more than the relative-L2 bar (a few dominant elements, as
+    with block scales spread over 2^+-40), the bar is 1.1x that rounding's own error -- no
+    bf16-output implementation can do better than the exact result rounded once."""
     y = bf16_to_f64(y_bits.view(np.uint16))
     assert np.isfinite(y).all(), f"{what}: non-finite output"
     err = y - ref64
     rel = np.linalg.norm(err) / max(np.linalg.norm(ref64), 1e-300)
     mx = np.abs(err).max() / max(np.abs(ref64).max(), 1e-300)
+    tol = REL_L2_TOL
+    if rounding_floor:
+        rounded = bf16_to_f64(oracle.round_to_bf16(ref64))
+        floor = np.linalg.norm(rounded - ref64) / max(np.linalg.norm(ref64), 1e-300)
+        tol = max(REL_L2_TOL, 1.1 * floor)
+        say(f"  {what}: exact result rounded once to bf16: rel_l2={floor:.3e}")
     say(f"  {what}: rel_l2={rel:.3e} max_abs/max_ref={mx:.3e}")
-    assert rel <= REL_L2_TOL, f"{what}: relative L2 {rel:.3e} > {REL_L2_TOL}"
+    assert rel <= tol, f"{what}: relative L2 {rel:.3e} > {tol:.3e}"
     assert mx <= MAX_ABS_FRAC, f"{what}: max abs err {mx:.3e} x max|ref| > {MAX_ABS_FRAC}"
     return rel, mx
 

@@ -59,7 +59,7 @@ def test_w4a4_block_scale_extremes():
     d["scales"] = g.integers(87, 168, d["scales"].shape).astype(np.uint8)
     y = _gemm(d, M, N, K)
     ref, _ = oracle.ref_w4a4(d["xq"], d["xs"], d["wq"], d["scales"])
-    check_float(y, ref, "w4a4 scale extremes")
+    check_float(y, ref, "w4a4 scale extremes", rounding_floor=True)
 
 
 def _quantize_gpu(x_bits):
