@@ -244,6 +244,28 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
                           const int32_t* expert_offsets, void* y, void* ws, size_t ws_bytes,
                           hq_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Tuning (host). The built-in table picks a kernel per range of M (the announcement's section
+ * "Tuning and JIT compilation per workload"); a tuning table measured on the device by
+ * `python -m quantized_gemm_prepacked_amd.autotune` (the roadmap's autotune, run offline) takes
+ * precedence for the shapes it lists. Text, one entry per line ('#' comments):
+ *     <family> <asym 0|1> <N> <K> <max_m> <kind> <cfg> <split>
+ * family wna16 | w8a8 | w4a8 | w4a4 | w4a8mx; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
+ * 3 ping-pong; cfg indexes that kind's configurations (hq_kernel_config_count); split = K splits
+ * of the skinny kernel, -1 = the heuristic's. A dense call uses the first entry of its family,
+ * asym, N and K whose max_m >= M, if that configuration fits the shape; otherwise the built-in
+ * choice. The table is process-wide:
+ *   hq_load_tuning_table(path)  replaces it (NULL clears it); a malformed line fails with
+ *                               HQ_ERR_INVALID_ARGUMENT and leaves the table unchanged.
+ *   Without a call, the file named by the environment variable HQ_TUNING_FILE (if any) is read
+ *   at the first dense plan. Loading while other threads launch GEMMs is safe (locked).
+ * hq_gemm_plan reports the (kind, cfg, split) a dense call of that shape would run.
+ * ------------------------------------------------------------------------------------------- */
+hq_status hq_load_tuning_table(const char* path);
+hq_status hq_gemm_plan(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, int32_t* kind,
+                       int32_t* cfg, int32_t* split);
+int32_t hq_kernel_config_count(int32_t kind);
+
 /* Thread-local message describing the last non-HQ_OK status of this thread ("" if none). */
 const char* hq_last_error(void);
 

@@ -37,6 +37,7 @@ EXPORTED = (
     "hq_moe_align_capacity", "hq_moe_align_workspace_bytes", "hq_moe_align", "hq_moe_block_m",
     "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_quantize_activations",
     "hq_moe_silu_mul", "hq_moe_combine", "hq_grouped_gemm_workspace_bytes", "hq_grouped_gemm",
+    "hq_load_tuning_table", "hq_gemm_plan", "hq_kernel_config_count",
     "hq_last_error", "hq_version",
 )
 
@@ -98,6 +99,9 @@ _c = {
                                             _I64, _I64),
     "hq_grouped_gemm": _sig("hq_grouped_gemm", ctypes.c_int, _P, _I64, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P,
                             ctypes.c_size_t, _P),
+    "hq_load_tuning_table": _sig("hq_load_tuning_table", ctypes.c_int, ctypes.c_char_p),
+    "hq_gemm_plan": _sig("hq_gemm_plan", ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P),
+    "hq_kernel_config_count": _sig("hq_kernel_config_count", _I32, _I32),
     "hq_moe_silu_mul": _sig("hq_moe_silu_mul", ctypes.c_int, _I64, _I64, _P, _P, _P),
     "hq_moe_combine": _sig("hq_moe_combine", ctypes.c_int, _I64, _I32, _I32, _I64, _P, _P, _P, _P),
     "hq_last_error": _sig("hq_last_error", ctypes.c_char_p),
@@ -209,6 +213,22 @@ def hq_grouped_gemm_workspace_bytes(desc, R, E, N, K) -> int:
 def hq_grouped_gemm(desc, R, E, N, K, a, a_scale, w_packed, expert_offsets, y, ws, ws_bytes, stream=None):
     _check(_c["hq_grouped_gemm"](_d(desc), R, E, N, K, _ptr(a), _ptr(a_scale), _ptr(w_packed),
                                  _ptr(expert_offsets), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def hq_load_tuning_table(path):
+    """Replace the process-wide tuning table with the file at `path` (None clears it)."""
+    _check(_c["hq_load_tuning_table"](None if path is None else os.fsencode(path)))
+
+
+def hq_gemm_plan(desc, M, N, K):
+    """(kind, cfg, split) that a dense call of this shape would run."""
+    k, c, s = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_c["hq_gemm_plan"](_d(desc), M, N, K, ctypes.byref(k), ctypes.byref(c), ctypes.byref(s)))
+    return k.value, c.value, s.value
+
+
+def hq_kernel_config_count(kind) -> int:
+    return _c["hq_kernel_config_count"](kind)
 
 
 def hq_quantize_activations(act_fmt, M, K, x, xq, s_tok, stream=None):

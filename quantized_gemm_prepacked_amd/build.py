@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libhq.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["hq_api.cpp", "prepack.cpp", "gemm_dispatch.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gemm_pipe.hip", "gemm_pingpong.hip", "moe_align.hip", "moe_layer.hip", "act_quant.hip"]
+SOURCES = ["hq_api.cpp", "prepack.cpp", "gemm_dispatch.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gemm_pipe.hip", "gemm_pingpong.hip", "moe_align.hip", "moe_layer.hip", "act_quant.hip", "tuning_table.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -213,9 +213,23 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
 
 }  // namespace
 
+int kernel_config_count(int kind) {
+  int n = 0;
+  if (kind == 0) skinny_configs(&n);
+  else if (kind == 1) tiled_configs(&n);
+  else if (kind == 2) pipe_configs(&n);
+  else if (kind == 3) pp_configs(&n);
+  return n;
+}
+
 Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   Plan pl{};
-  const TuneOverride tov = tune_override();
+  TuneOverride tov = tune_override();
+  if (tov.kind < 0) {
+    // the run-time tuning table, when it has an entry for this shape that fits
+    TuneOverride t;
+    if (tuning_lookup(c, M, N, K, &t.kind, &t.cfg, &t.split) && override_fits(c, t, M, N, K)) tov = t;
+  }
   RangeEntry pick = pick_range(c, M, N, K);
   // Sweep overrides (HQ_TUNE): an override that does not fit the shape (tile, LDS, K) is
   // refused (kind -1, the call fails) rather than silently replaced.

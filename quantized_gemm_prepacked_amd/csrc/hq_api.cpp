@@ -132,6 +132,29 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
   return ok();
 }
 
+hq_status hq_load_tuning_table(const char* path) {
+  std::string err;
+  if (hq::load_tuning_table(path, &err) != 0) return fail(HQ_ERR_INVALID_ARGUMENT, "%s", err.c_str());
+  return ok();
+}
+
+hq_status hq_gemm_plan(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, int32_t* kind,
+                       int32_t* cfg, int32_t* split) {
+  hq::Combo c{};
+  hq_status s = resolve(desc, &c);
+  if (s != HQ_OK) return s;
+  if ((s = check_shape(c, N, K)) != HQ_OK) return s;
+  if (M <= 0 || M > kMaxDim) return fail(HQ_ERR_INVALID_ARGUMENT, "M=%lld out of range", (long long)M);
+  if (!kind || !cfg || !split) return fail(HQ_ERR_INVALID_ARGUMENT, "kind, cfg and split must be non-NULL");
+  const hq::Plan p = hq::plan_dense(c, M, N, K);
+  *kind = p.kind;
+  *cfg = p.cfg;
+  *split = p.split;
+  return p.kind < 0 ? fail(HQ_ERR_INVALID_ARGUMENT, "the HQ_TUNE override does not fit this shape") : ok();
+}
+
+int32_t hq_kernel_config_count(int32_t kind) { return kind < 0 || kind > 3 ? 0 : hq::kernel_config_count(kind); }
+
 size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K) {
   hq::Combo c{};
   if (resolve(desc, &c) != HQ_OK || M <= 0 || M > kMaxDim || check_shape(c, N, K) != HQ_OK) return 0;

@@ -1,6 +1,7 @@
 // internal.h -- declarations shared by the C ABI (hq_api.cpp), the host prepack and the HIP
 // launchers. Not part of the public interface.
 #pragma once
+#include <string>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -53,6 +54,10 @@ struct GemmCall {
 };
 
 Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K);
+// Run-time tuning table (tuning_table.cpp): load (path NULL clears), lookup for a dense call.
+int load_tuning_table(const char* path, std::string* err);
+bool tuning_lookup(const Combo& c, int64_t M, int64_t N, int64_t K, int* kind, int* cfg, int* split);
+int kernel_config_count(int kind);
 Plan plan_moe(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K,
               int32_t block_m);
 int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K);
