@@ -90,7 +90,17 @@ typedef struct {
   int32_t has_zero_point; /* 1 for HQ_W_UINT4_ASYM, else 0                                   */
   int32_t act_fmt;        /* hq_act_fmt                                                      */
   int32_t out_fmt;        /* hq_out_fmt                                                      */
+  int32_t compute_flags;  /* HQ_COMPUTE_* bits, 0 = none                                     */
 } hq_quant_desc;
+
+/* Batch invariance (a compute option of the announcement's section "Tuning and JIT compilation
+ * per workload"): every output row is a function of its own activation row (and the weights)
+ * alone, bit for bit, whatever M (dense) or T (MoE) and whatever the other rows. The library
+ * then runs one fixed kernel configuration per (format, N) for all M -- the skinny kernel, two
+ * 16-row blocks per workgroup, no K split across workgroups -- and ignores tuning tables and
+ * overrides; MoE calls need block_m = 32 (what hq_moe_block_m returns with the flag). The cost
+ * is the tuned kernels' speed at large M (measured about 2x slower for W4A16 at M = 8192). */
+#define HQ_COMPUTE_BATCH_INVARIANT 1
 
 /*
  * Supported combinations (others return HQ_ERR_UNSUPPORTED):

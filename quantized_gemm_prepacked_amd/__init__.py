@@ -51,12 +51,23 @@ class hq_quant_desc(ctypes.Structure):
         ("has_zero_point", ctypes.c_int32),
         ("act_fmt", ctypes.c_int32),
         ("out_fmt", ctypes.c_int32),
+        ("compute_flags", ctypes.c_int32),
     ]
 
 
-def make_desc(weight_fmt, group_size, scale_dtype, has_zero_point, act_fmt, out_fmt=HQ_OUT_BF16):
+HQ_COMPUTE_BATCH_INVARIANT = 1
+
+
+def make_desc(weight_fmt, group_size, scale_dtype, has_zero_point, act_fmt, out_fmt=HQ_OUT_BF16,
+              compute_flags=0):
     return hq_quant_desc(ctypes.sizeof(hq_quant_desc), weight_fmt, group_size, scale_dtype,
-                         has_zero_point, act_fmt, out_fmt)
+                         has_zero_point, act_fmt, out_fmt, compute_flags)
+
+
+def with_flags(desc, compute_flags):
+    """A copy of `desc` with its compute flags set (e.g. HQ_COMPUTE_BATCH_INVARIANT)."""
+    return make_desc(desc.weight_fmt, desc.group_size, desc.scale_dtype, desc.has_zero_point,
+                     desc.act_fmt, desc.out_fmt, compute_flags)
 
 
 # The four supported combinations (plus the W8A8 raw-accumulator test mode).

@@ -222,8 +222,26 @@ int kernel_config_count(int kind) {
   return n;
 }
 
+// The batch-invariant configuration: one skinny configuration per (family, N) for every M, no
+// K split across workgroups (a row's sum order is then its own units in order per wave and the
+// waves in order, whatever the other rows), two 16-row blocks per workgroup.
+int invariant_skinny_cfg(const Combo& c, int64_t N) {
+  int n_cfg = 0;
+  const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
+  for (int i : {29, 15, 8})
+    if ((N / 16) % cfgs[i].ntw == 0 && skinny_lds_bytes(c.fam, i) <= 160 * 1024) return i;
+  return 8;
+}
+
 Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   Plan pl{};
+  if (c.invariant) {
+    pl.kind = 0;
+    pl.cfg = invariant_skinny_cfg(c, N);
+    pl.split = 1;
+    pl.ws_bytes = 0;
+    return pl;
+  }
   TuneOverride tov = tune_override();
   if (tov.kind < 0) {
     // the run-time tuning table, when it has an entry for this shape that fits
@@ -298,6 +316,11 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   Plan pl{};
   pl.split = 1;
   pl.ws_bytes = 0;
+  if (c.invariant) {   // the dense path's fixed configuration; its 32-row blocks are block_m
+    pl.kind = 0;
+    pl.cfg = invariant_skinny_cfg(c, N);
+    return pl;
+  }
   // Sweep override (HQ_TUNE="kind=3,cfg=<i>"): a ping-pong configuration whose tile rows equal
   // block_m; one that does not fit is refused (kind -1).
   const TuneOverride tov = tune_override();
@@ -363,7 +386,8 @@ bool moe_block_m_supported(int32_t block_m) { return block_m == 16 || block_m ==
 // routing): 16-row blocks below 2 routed rows per expert, 32-row blocks (ping-pong 32 x 256)
 // from 2, 64-row blocks (ping-pong 64 x 512) from 32 -- the two tie at 16 rows per expert and the
 // wider tile wins by ~11% at 64, where the padding of the small experts costs less than it gains.
-int32_t moe_block_m(const Combo&, int64_t T, int32_t topk, int32_t E, int64_t, int64_t) {
+int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t, int64_t) {
+  if (c.invariant) return 32;
   const double rows_per_expert = double(T) * topk / std::max(1, E);
   if (rows_per_expert < 2) return 16;
   if (rows_per_expert < 32) return 32;

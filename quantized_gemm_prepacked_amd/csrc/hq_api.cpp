@@ -48,6 +48,9 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
     return fail(HQ_ERR_INVALID_ARGUMENT, "unknown out_fmt %d", d->out_fmt);
   c->out_i32 = d->out_fmt == HQ_OUT_INT32_ACC;
   c->asym = false;
+  if (d->compute_flags & ~int32_t(HQ_COMPUTE_BATCH_INVARIANT))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "unknown compute_flags bits 0x%x", unsigned(d->compute_flags));
+  c->invariant = (d->compute_flags & HQ_COMPUTE_BATCH_INVARIANT) != 0;
   switch (d->weight_fmt) {
     case HQ_W_INT4_SYM:
     case HQ_W_UINT4_ASYM: {
@@ -106,7 +109,7 @@ extern "C" {
 
 const char* hq_last_error(void) { return g_last_error.c_str(); }
 
-int32_t hq_version(void) { return 100; }
+int32_t hq_version(void) { return 101; }
 
 size_t hq_prepacked_bytes(const hq_quant_desc* desc, int64_t E, int64_t N, int64_t K) {
   hq::Combo c{};
@@ -374,6 +377,8 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
     return fail(HQ_ERR_UNSUPPORTED, "T*topk*N must stay below 2^31");
   if (!hq::moe_block_m_supported(block_m))
     return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: supported values are 16, 32, 64", block_m);
+  if (c.invariant && block_m != 32)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "block_m=%d: batch-invariant MoE calls use block_m 32", block_m);
   if (a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (!a || !w_packed || !sorted_ids || !block_expert || !num_padded || !y)
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, sorted_ids, block_expert, num_padded and y must be non-NULL");

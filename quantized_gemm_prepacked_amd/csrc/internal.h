@@ -17,6 +17,7 @@ struct Combo {
   Family fam;
   bool asym;     // WNA16 with zero-points
   bool out_i32;  // W8A8 raw accumulator output
+  bool invariant;  // HQ_COMPUTE_BATCH_INVARIANT: one fixed kernel configuration for every M
 };
 
 size_t prepacked_bytes(const Combo& c, int64_t E, int64_t N, int64_t K);

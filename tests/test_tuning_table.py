@@ -81,3 +81,15 @@ def test_autotune_table_lines_cover_m_ranges(tmp_path):
     assert hq.hq_gemm_plan(d, 4, 14336, 4096)[:2] == (0, 28)
     assert hq.hq_gemm_plan(d, 5, 14336, 4096)[:2] == (0, 13)
     assert hq.hq_gemm_plan(d, 46, 14336, 4096)[:2] == (2, 2)
+
+
+def test_batch_invariant_plan_is_fixed_and_ignores_tables(tmp_path):
+    inv = hq.with_flags(hq.DESC_W4A16_ASYM, hq.HQ_COMPUTE_BATCH_INVARIANT)
+    plans = {hq.hq_gemm_plan(inv, M, 14336, 4096) for M in (1, 16, 128, 1024, 8192)}
+    assert len(plans) == 1 and next(iter(plans))[0] == 0 and next(iter(plans))[2] == 1
+    hq.hq_load_tuning_table(_write(tmp_path, "wna16 1 14336 4096 16 0 13 -1\n"))
+    assert hq.hq_gemm_plan(inv, 1, 14336, 4096) in plans
+    assert hq.hq_moe_block_m(hq.with_flags(hq.DESC_W4A16_SYM, hq.HQ_COMPUTE_BATCH_INVARIANT), 4096, 8, 256, 4096, 7168) == 32
+    bad = hq.with_flags(hq.DESC_W4A16_ASYM, 6)
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(bad, 1, 14336, 4096)
