@@ -29,7 +29,7 @@ from .codecs import (  # noqa: F401
     decode_e4m3, decode_bf16, round_to_bf16, decode_sign_magnitude,
 )
 from .gemm import (  # noqa: F401
-    dequant_wna16, dequant_mxfp4, ref_wna16, ref_w8a8, ref_w4a8, ref_w4a4, ref_w4a8_mx,
+    dequant_wna16, dequant_mxfp4, ref_wna16, ref_w8a8, ref_w4a8, ref_w4a4, ref_w4a8_mx, ref_w4a16_mx,
 )
 from .moe import (  # noqa: F401
     ref_moe_align, ref_moe_gemm, ref_grouped_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer,

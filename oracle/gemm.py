@@ -116,3 +116,12 @@ def ref_w4a8_mx(xq: np.ndarray, xs_e8m0: np.ndarray, wq: np.ndarray, scales_e8m0
     w = dequant_mxfp4(wq, scales_e8m0, cols)
     y = x @ w.T
     return y, round_to_bf16(y)
+
+
+def ref_w4a16_mx(x_bf16: np.ndarray, wq: np.ndarray, scales_e8m0: np.ndarray, rows=None, cols=None):
+    """MXFP4 weights with bf16 activations ("W4A16-MXFP4"): y = x . dequant_mxfp4(w)^T, exact
+    float64 products and sums, rounded once to bf16. Returns (y float64, y bf16 bits)."""
+    x = decode_bf16(_sel(x_bf16, rows))
+    w = dequant_mxfp4(wq, scales_e8m0, cols)
+    y = x @ w.T
+    return y, round_to_bf16(y)

@@ -14,7 +14,8 @@ block size block_m:
   block_expert[b] = the expert whose range holds row b*block_m
 Entries whose expert id is outside [0, E) are routed nowhere.
 
-Grouped GEMM: Y[t*topk + j, :] = X[t, :] . dequant(W_e)^T with e = topk_ids[t, j], optionally
+Grouped GEMM: Y[t*topk + j, :] = X[t, :] . dequant(W_e)^T with e = topk_ids[t, j] (W_e INT4
+group-quantized with bf16 scales, or MXFP4 with e8m0 block scales), optionally
 multiplied by topk_weights[t, j]. It does not depend on the order of sorted_ids.
 """
 from __future__ import annotations
@@ -22,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import decode_bf16, round_to_bf16
-from .gemm import dequant_wna16
+from .gemm import dequant_mxfp4, dequant_wna16
 
 
 def ref_moe_align(topk_ids: np.ndarray, E: int, block_m: int):
@@ -55,6 +56,14 @@ def _values(a: np.ndarray) -> np.ndarray:
     return decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
+def _dequant_expert(wd, g: int, cols):
+    """An expert's standard-format weights -> float64 [N, K]: INT4 groups with bf16 scales
+    (uint16 bits) or MXFP4 blocks with e8m0 scales (uint8)."""
+    if np.asarray(wd["scales"]).dtype == np.uint8:
+        return dequant_mxfp4(wd["wq"], wd["scales"], cols)
+    return dequant_wna16(wd["wq"], wd["scales"], wd.get("zeros"), g, cols)
+
+
 def ref_moe_gemm(x_bf16: np.ndarray, topk_ids: np.ndarray, expert_weights, N: int, E: int,
                  g: int, topk_weights: np.ndarray | None = None, rows=None, cols=None):
     """Grouped WNA16 GEMM over routed rows. ``expert_weights(e)`` returns the standard-format
@@ -72,8 +81,7 @@ def ref_moe_gemm(x_bf16: np.ndarray, topk_ids: np.ndarray, expert_weights, N: in
         if e < 0 or e >= E:
             continue
         sel = np.flatnonzero(experts == e)
-        wd = expert_weights(int(e))
-        w = dequant_wna16(wd["wq"], wd["scales"], wd.get("zeros"), g, cols)
+        w = _dequant_expert(expert_weights(int(e)), g, cols)
         y[sel] = x[flat[sel] // topk] @ w.T
     if topk_weights is not None:
         tw = np.asarray(topk_weights, dtype=np.float32).astype(np.float64).reshape(-1)[flat]
@@ -100,8 +108,7 @@ def ref_grouped_gemm(x_bf16: np.ndarray, expert_offsets: np.ndarray, expert_weig
         lo, hi = min(max(int(offs[e]), 0), R), min(max(int(offs[e + 1]), 0), R)
         if hi <= lo:
             continue
-        wd = expert_weights(e)
-        w = dequant_wna16(wd["wq"], wd["scales"], wd.get("zeros"), g, cols)
+        w = _dequant_expert(expert_weights(e), g, cols)
         y[lo:hi] = x[lo:hi] @ w.T
     valid = ~np.isnan(y[:, 0]) if n_cols else np.ones(R, dtype=bool)
     bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))

@@ -251,6 +251,18 @@ def make_w4a8mx(config_id: int, M: int, N: int, K: int):
     return {"xq": xq, "xs": xs, **quantize_mxfp4(w)}
 
 
+def make_w4a16mx(config_id: int, M: int, N: int, K: int):
+    """Dense W4A16-MXFP4: bf16 N(0,1) activations, MXFP4 weights from N(0, 0.02)."""
+    w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    return {"x": normal_bf16(rng(config_id, M), (M, K)), **quantize_mxfp4(w)}
+
+
+def make_moe_weights_expert_mx(config_id: int, e: int, N: int, K: int):
+    """One expert's MXFP4 weights, drawn from its own stream [config, 1, e]."""
+    w = rng(config_id, 1, e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    return quantize_mxfp4(w)
+
+
 def make_w4a4_activations(config_id: int, M: int, K: int):
     """MXFP4 activations (e2m1 codes + e8m0 per 32 k) quantized from bf16 N(0,1) by the OCP MX
     rule (the same quantizer as the weights')."""
