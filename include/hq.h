@@ -108,7 +108,11 @@ typedef struct {
  *   UINT4_ASYM + BF16 scale, group 128, zero-point    + ACT_BF16              -> OUT_BF16
  *   INT8_SYM   + FP32 scale, group 0                  + ACT_INT8_PER_TOKEN    -> OUT_BF16 | OUT_INT32_ACC
  *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_FP8E4M3_PER_TOKEN -> OUT_BF16
- * MoE grouped GEMM: the two WNA16 combinations.
+ *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_MXFP8             -> OUT_BF16
+ *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_MXFP4  (W4A4)     -> OUT_BF16
+ *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_BF16   (W4A16)    -> OUT_BF16
+ * MoE grouped GEMM and grouped GEMM: the combinations with ACT_BF16 (INT4 sym / asym, FP4).
+ * Every combination also takes compute_flags = HQ_COMPUTE_BATCH_INVARIANT.
  */
 
 /* ---------------------------------------------------------------------------------------------
@@ -172,6 +176,9 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
  *             W4A8 : bf16( a_scale[m] * sum_k e4m3(a) * e2m1(q) * 2^(e - 127) ) (fp32 accumulation)
  *             W4A4 : bf16( sum_k e2m1(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation;
  *                    weights as W4A8, desc act_fmt HQ_ACT_MXFP4)
+ *             MXFP4 weights with bf16 activations (desc act_fmt HQ_ACT_BF16), "W4A16-MXFP4":
+ *                    bf16( sum_k a * e2m1(q) 2^(e - 127) ) (each weight dequantized exactly to
+ *                    bf16, fp32 accumulation); also for hq_moe_grouped_gemm / hq_grouped_gemm
  *             W4A8 with MXFP8 activations (desc act_fmt HQ_ACT_MXFP8):
  *                    bf16( sum_k e4m3(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation)
  * All bf16 results use round-to-nearest-even. M = 0 is a no-op returning HQ_OK.
@@ -211,7 +218,7 @@ int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32
                        int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------------------------
- * MoE grouped GEMM (device), WNA16 only:
+ * MoE grouped GEMM (device), bf16 activations: INT4 group weights (WNA16) or MXFP4 weights:
  *   y[f, :] = (topk_weights ? topk_weights[f] : 1) * a[f / topk, :] . dequant(W_{e(f)})^T
  * for every flat index f = t*topk + j that hq_moe_align routed to a valid expert e(f). Rows of
  * y for unrouted f are not written.
@@ -260,7 +267,7 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
  * `python -m quantized_gemm_prepacked_amd.autotune` (the roadmap's autotune, run offline) takes
  * precedence for the shapes it lists. Text, one entry per line ('#' comments):
  *     <family> <asym 0|1> <N> <K> <max_m> <kind> <cfg> <split>
- * family wna16 | w8a8 | w4a8 | w4a4 | w4a8mx; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
+ * family wna16 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
  * 3 ping-pong; cfg indexes that kind's configurations (hq_kernel_config_count); split = K splits
  * of the skinny kernel, -1 = the heuristic's. A dense call uses the first entry of its family,
  * asym, N and K whose max_m >= M, if that configuration fits the shape; otherwise the built-in

@@ -78,6 +78,7 @@ DESC_W8A8_I32 = make_desc(HQ_W_INT8_SYM, 0, HQ_SCALE_FP32, 0, HQ_ACT_INT8_PER_TO
 DESC_W4A8_MXFP4 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_FP8E4M3_PER_TOKEN)
 DESC_W4A4_MXFP4 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_MXFP4)
 DESC_W4A8_MXFP8 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_MXFP8)
+DESC_W4A16_MXFP4 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_BF16)
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

@@ -27,7 +27,8 @@ import time
 import numpy as np
 import torch
 
-from . import (DESC_W4A16_ASYM, DESC_W4A16_SYM, DESC_W4A4_MXFP4, DESC_W4A8_MXFP4, DESC_W4A8_MXFP8, DESC_W8A8,
+from . import (DESC_W4A16_ASYM, DESC_W4A16_MXFP4, DESC_W4A16_SYM, DESC_W4A4_MXFP4, DESC_W4A8_MXFP4,
+               DESC_W4A8_MXFP8, DESC_W8A8,
                HQError, hq_gemm, hq_gemm_plan, hq_gemm_workspace_bytes, hq_kernel_config_count,
                hq_load_tuning_table, hq_prepack_weights, hq_prepacked_bytes)
 
@@ -39,6 +40,7 @@ FORMATS = {
     "w4a8": (DESC_W4A8_MXFP4, "w4a8", 0),
     "w4a4": (DESC_W4A4_MXFP4, "w4a4", 0),
     "w4a8mx": (DESC_W4A8_MXFP8, "w4a8mx", 0),
+    "w4a16mx": (DESC_W4A16_MXFP4, "mxw4a16", 0),
 }
 INF_M = 1 << 40
 
@@ -60,7 +62,7 @@ def _weights(fmt: str, N: int, K: int, g: np.random.Generator):
 
 def _activations(fmt: str, M: int, K: int, g: np.random.Generator):
     """(a bytes, a_scale) in the format's activation layout."""
-    if fmt in ("w4a16", "w4a16a"):
+    if fmt in ("w4a16", "w4a16a", "w4a16mx"):
         x = g.standard_normal((M, K)).astype(np.float32)
         return (x.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8), None
     if fmt == "w8a8":

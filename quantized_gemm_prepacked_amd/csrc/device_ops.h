@@ -122,6 +122,24 @@ __device__ __forceinline__ f32x4 mfma_fp4_fp4(u32x4 a, int a_scale, u32x4 b, int
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, a_scale, 0, b_scale);
 }
 
+// ---- MXFP4 weights for the bf16 MFMA -----------------------------------------------------------
+// e8m0 byte -> its power of two as binary32 (0 -> 2^-127, a subnormal; 255 -> NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u) : e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float(e << 23);
+}
+
+// One dword of 8 e2m1 codes (k in nibble order, low nibble first) -> the 8 values times the block
+// scale s, as the bf16 MFMA operand in k order: gfx950's scaled fp4 -> bf16 conversion, two
+// codes per instruction. e2m1 values times a power of two are exact in bf16 (two significant
+// bits) wherever the power of two is in bf16's range.
+__device__ __forceinline__ bf16x8 dequant_fp4x8_scaled(uint32_t v, float s) {
+  const bf16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
+  const bf16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
+  const bf16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
+  const bf16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
+  return bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
 // Position of 16-byte chunk `chunk` of activation row `row` in an LDS tile with `cpr` chunks per
 // row (an XOR swizzle, so each row's chunks stay a permutation of its own slots). For 128-byte
 // rows the key is the row's low three bits. For 256-byte rows the plain key (row & 15) leaves the

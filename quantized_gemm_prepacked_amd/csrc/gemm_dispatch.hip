@@ -35,17 +35,19 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
   };
   if (rows <= 16) {
+    if (c.fam == FAM_MXW4A16) return first_fit({28, 13, 0, 1, 2});
     if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
     if (c.fam == FAM_W4A8) return first_fit({21, 2});
     if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({21, 2});
     return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
+    if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
     if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({16, 8});
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
-  if (c.fam == FAM_WNA16) return first_fit({5, 4, 6});
+  if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
   if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
   return first_fit({4, 5, 6});
 }
@@ -94,6 +96,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A4>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_W4A8MX)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8MX>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_MXW4A16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_MXW4A16>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -126,6 +130,8 @@ constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {k
 // blocks up to M=512 at 34 us vs 56 us on ping-pong 128x128, which wins from M=2048 on; 128x256
 // at M=8192)
 constexpr RangeEntry kW4a4Table[] = {{768, 0, 0}, {4096, 3, 2}, {kInf, 3, 0}};
+// MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
+constexpr RangeEntry kMxW4a16Table[] = {{64, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -152,6 +158,9 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_W8A8) {
     t = kW8a8Table;
     n = int(sizeof(kW8a8Table) / sizeof(kW8a8Table[0]));
+  } else if (c.fam == FAM_MXW4A16) {
+    t = kMxW4a16Table;
+    n = int(sizeof(kMxW4a16Table) / sizeof(kMxW4a16Table[0]));
   } else if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) {
     t = kW4a4Table;
     n = int(sizeof(kW4a4Table) / sizeof(kW4a4Table[0]));
@@ -168,7 +177,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
     return t[i];
   }
   // Fallbacks when the preferred tile does not divide N.
-  if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) {
+  if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
     for (int cfg : {3, 2})   // 128 x 128 tiles
@@ -192,7 +201,7 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
     return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
-  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && (o.kind == 1 || o.kind == 2)) return false;
+  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16) && (o.kind == 1 || o.kind == 2)) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -280,7 +289,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   // The direct-to-LDS kernels address activations with 32-bit offsets.
   if ((pick.kind == 2 || pick.kind == 3) &&
       uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) >= (uint64_t(1) << 32)) {
-    const int tc = (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) ? -1 : pick_tiled(c, N, K);
+    const int tc = (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16) ? -1 : pick_tiled(c, N, K);
     pick = tc >= 0 ? RangeEntry{kInf, 1, tc} : RangeEntry{0, 0, 0};
   }
   if (pick.kind != 0) {
@@ -332,7 +341,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
                       pp_lds_bytes(c.fam, tov.cfg) <= 160 * 1024 && uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);
     pl.kind = fits ? 3 : -1;
     pl.cfg = tov.cfg;
-    pl.ws_bytes = group_sums_split_bytes(T, K);
+    pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(T, K) : 0;
     return pl;
   }
   // Blocks of 32 and 64 rows: the ping-pong kernel with one expert block per tile row, its
@@ -340,7 +349,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
   // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
   const bool a32 = uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);   // 32-bit row offsets
-  if (c.fam == FAM_WNA16 && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+  if ((c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
     static const int pp32[1] = {7}, pp64[2] = {5, 4};
     const int* cands = block_m == 32 ? pp32 : pp64;
     const int n_c = block_m == 32 ? 1 : 2;
@@ -351,12 +360,12 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
       if (N % (16 * t.ntw * t.wn) == 0 && pp_lds_bytes(c.fam, cands[j]) <= 160 * 1024) {
         pl.kind = 3;
         pl.cfg = cands[j];
-        pl.ws_bytes = group_sums_split_bytes(T, K);  // per-token activation group sums
+        pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(T, K) : 0;  // WNA16 offset term
         return pl;
       }
     }
   }
-  if (block_m == 64 && N % 128 == 0 && K % 128 == 0) {
+  if (c.fam == FAM_WNA16 && block_m == 64 && N % 128 == 0 && K % 128 == 0) {
     pl.kind = 1;       // LDS-tiled, 64 x 128 tiles: one expert block per tile row
     pl.cfg = 3;
     pl.ws_bytes = group_sums_split_bytes(T, K);  // per-token activation group sums
@@ -442,8 +451,10 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.topk_weights = call.topk_weights;
     p.topk = call.topk;
     p.E = call.E;
-    hipError_t e = launch_group_sums_split(p.a, int(call.T), p.K, call.ws, call.stream);
-    if (e != hipSuccess) return e;
+    if (c.fam == FAM_WNA16) {
+      hipError_t e = launch_group_sums_split(p.a, int(call.T), p.K, call.ws, call.stream);
+      if (e != hipSuccess) return e;
+    }
     const int tiles_n = int(call.N / bn);
     const int tiles_m = int(call.max_blocks);
     return launch_pingpong(p, c.fam, true, plan.cfg, dim3(unsigned(tiles_m * tiles_n)), tiles_m, tiles_n,

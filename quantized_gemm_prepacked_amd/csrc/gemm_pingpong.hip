@@ -59,6 +59,13 @@ struct PPTraits<FAM_W4A8> {
   static constexpr int kAScaleBytes = 0;
 };
 template <>
+struct PPTraits<FAM_MXW4A16> {
+  static constexpr int kRowBytes = 256;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 64;   // one e8m0 byte per lane
+  static constexpr int kAScaleBytes = 0;
+};
+template <>
 struct PPTraits<FAM_W4A8MX> {
   static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 1;
@@ -233,7 +240,8 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     for (int t = 0; t < NTW; ++t) acc[mb][t] = Acc{0, 0, 0, 0};
 
   // Operand fragments of one step, filled by the memory phase and used by the compute phase.
-  constexpr int NA = FAM == FAM_WNA16 ? 4 : (FAM == FAM_W4A4 ? 1 : 2);   // activation fragments per row block
+  constexpr bool BF16A = FAM == FAM_WNA16 || FAM == FAM_MXW4A16;   // bf16 activations
+  constexpr int NA = BF16A ? 4 : (FAM == FAM_W4A4 ? 1 : 2);   // activation fragments per row block
   constexpr int NB = FAM == FAM_W8A8 ? 2 : 1;    // packed weight fragments per channel tile
   u32x4 af[MW][NA];
   u32x4 bq[NTW][NB];
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       for (int d = 0; d < NA; ++d) {
         // WNA16: lane group g holds k 32g..32g+31 of the step (chunks 4g..4g+3); 8-bit
         // activations: MFMA d takes chunk 4d + g (W8A8: k 64d + 16g..; W4A8: the two halves)
-        const int chunk = FAM == FAM_WNA16 ? 4 * (lane >> 4) + d : 4 * d + (lane >> 4);
+        const int chunk = BF16A ? 4 * (lane >> 4) + d : 4 * d + (lane >> 4);
         af[mb][d] = read_a(st, mb, chunk);
       }
     if constexpr (Sh::ASC_BYTES > 0) {
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       const int tw = wn * NTW + t;
       if constexpr (FAM == FAM_WNA16)
         meta[t] = *reinterpret_cast<const uint16_t*>(sm + tw * 32 + 2 * (lane & 15));
-      else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX)
+      else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX || FAM == FAM_MXW4A16)
         meta[t] = sm[tw * 64 + lane];
     }
   };
@@ -307,6 +315,19 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       for (int i = 0; i < 4 * MW * NTW; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    } else if constexpr (FAM == FAM_MXW4A16) {
+      // the lane's 32 weights of a tile share k block (lane >> 4): its scale is folded into the
+      // conversion, and the MFMAs accumulate straight into the tile
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float s = e8m0_to_f32(meta[t]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_fp4x8_scaled(bq[t][0][d], s);
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+        }
       }
     } else if constexpr (FAM == FAM_W8A8) {
 #pragma unroll
@@ -427,6 +448,7 @@ int pp_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return pp_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return pp_lds_table<FAM_W4A8MX>(cfg, seq);
+  if (fam == FAM_MXW4A16) return pp_lds_table<FAM_MXW4A16>(cfg, seq);
   return pp_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -434,7 +456,7 @@ template <int FAM, bool MOE, int I>
 static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PPCfg C = kPP[I];
   using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn>;
-  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || FAM == FAM_WNA16)) {
+  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || FAM == FAM_WNA16 || FAM == FAM_MXW4A16)) {
     auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
@@ -459,13 +481,15 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   if (cfg < 0 || cfg >= n) return hipErrorInvalidValue;
   auto seq = std::make_integer_sequence<int, n>{};
   if (moe) {
-    if (fam != FAM_WNA16) return hipErrorInvalidValue;
-    return launch_pp_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    return hipErrorInvalidValue;
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return launch_pp_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
 }
 

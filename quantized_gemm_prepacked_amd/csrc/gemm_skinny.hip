@@ -46,6 +46,10 @@ struct SkTraits<FAM_W4A8> {
   static constexpr int kRowBytes = 128, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 0;
 };
 template <>
+struct SkTraits<FAM_MXW4A16> {
+  static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 0;
+};
+template <>
 struct SkTraits<FAM_W4A8MX> {
   static constexpr int kRowBytes = 128, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 4;
 };
@@ -213,6 +217,25 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb][t] += part[mb] * s + rsum[mb] * c;
+      }
+    } else if constexpr (FAM == FAM_MXW4A16) {
+      // bf16 activations in the WNA16 chunk order; the lane's 32 weights all belong to k block
+      // (lane >> 4) of the unit, so one scale per lane and tile is folded into the conversion
+      u32x4 af[MB][4];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) af[mb][d] = read_a(mb, 4 * (lane >> 4) + d);
+      const uint8_t* sc = slot + Sh::A_UNIT;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float s = e8m0_to_f32(sc[t * 64 + lane]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_fp4x8_scaled(bw[buf][r][t][d], s);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+        }
       }
     } else if constexpr (FAM == FAM_W8A8) {
 #pragma unroll
@@ -393,6 +416,7 @@ int skinny_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W8A8) return skinny_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return skinny_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return skinny_lds_table<FAM_W4A8MX>(cfg, seq);
+  if (fam == FAM_MXW4A16) return skinny_lds_table<FAM_MXW4A16>(cfg, seq);
   return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -430,6 +454,8 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
                          hipStream_t s) {
   if (fam == FAM_WNA16) return moe ? launch_skinny_fam<FAM_WNA16, true>(p, cfg, grid, s)
                                    : launch_skinny_fam<FAM_WNA16, false>(p, cfg, grid, s);
+  if (fam == FAM_MXW4A16) return moe ? launch_skinny_fam<FAM_MXW4A16, true>(p, cfg, grid, s)
+                                     : launch_skinny_fam<FAM_MXW4A16, false>(p, cfg, grid, s);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);

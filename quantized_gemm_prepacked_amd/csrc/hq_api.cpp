@@ -76,12 +76,14 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
     case HQ_W_FP4_E2M1:
       if (d->group_size != 32 || d->scale_dtype != HQ_SCALE_E8M0 || d->has_zero_point != 0 ||
           (d->act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN && d->act_fmt != HQ_ACT_MXFP4 &&
-           d->act_fmt != HQ_ACT_MXFP8) || c->out_i32)
+           d->act_fmt != HQ_ACT_MXFP8 && d->act_fmt != HQ_ACT_BF16) || c->out_i32)
         return fail(HQ_ERR_UNSUPPORTED,
-                    "FP4 weights need group_size 32, E8M0 scales, no zero-point, per-token FP8 "
+                    "FP4 weights need group_size 32, E8M0 scales, no zero-point, BF16, per-token FP8 "
                     "e4m3, MXFP8 or MXFP4 activations and bf16 output");
-      c->fam = d->act_fmt == HQ_ACT_MXFP4 ? hq::FAM_W4A4
-               : d->act_fmt == HQ_ACT_MXFP8 ? hq::FAM_W4A8MX : hq::FAM_W4A8;
+      c->fam = d->act_fmt == HQ_ACT_MXFP4   ? hq::FAM_W4A4
+               : d->act_fmt == HQ_ACT_MXFP8 ? hq::FAM_W4A8MX
+               : d->act_fmt == HQ_ACT_BF16  ? hq::FAM_MXW4A16
+                                            : hq::FAM_W4A8;
       return HQ_OK;
     default:
       return fail(HQ_ERR_INVALID_ARGUMENT, "unknown weight_fmt %d", d->weight_fmt);
@@ -177,7 +179,7 @@ hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, co
   if (!a || !w_packed || !y) return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be non-NULL");
   if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
-  const bool needs_scale = c.fam != hq::FAM_WNA16;
+  const bool needs_scale = c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16;
   if (needs_scale && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale is required for INT8/FP8 activations");
   if (!needs_scale && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (a_scale && (reinterpret_cast<uintptr_t>(a_scale) & 3u))
@@ -293,7 +295,8 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (c.fam != hq::FAM_WNA16) return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM supports WNA16 only");
+  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16)
+    return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM supports bf16 activations (INT4 or MXFP4 weights) only");
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (R < 0 || R > kMaxDim || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld E=%d out of range", (long long)R, E);
@@ -369,7 +372,8 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (c.fam != hq::FAM_WNA16) return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM supports WNA16 only");
+  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16)
+    return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM supports bf16 activations (INT4 or MXFP4 weights) only");
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (T < 0 || topk <= 0 || topk > 64 || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld topk=%d E=%d out of range", (long long)T, topk, E);

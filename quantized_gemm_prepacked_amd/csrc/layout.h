@@ -33,9 +33,9 @@
 
 namespace hq {
 
-// W4A4 and W4A8 with MXFP8 activations (W4A8MX) share W4A8's prepacked weights (MXFP4); only
-// the activation operand differs.
-enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4 };
+// W4A4, W4A8 with MXFP8 activations (W4A8MX) and MXFP4 weights with bf16 activations (MXW4A16)
+// share W4A8's prepacked weights (MXFP4); only the activation operand differs.
+enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5 };
 
 constexpr int kUnitBytes = 1024;
 constexpr int kTileN = 16;

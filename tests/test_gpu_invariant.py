@@ -31,11 +31,14 @@ def _inputs(fmt, M, N, K):
     if fmt == "w4a4":
         d = synth.make_w4a4(900, M, N, K)
         return hq.DESC_W4A4_MXFP4, (d["wq"], d["scales"], None), d["xq"], d["xs"]
+    if fmt == "w4a16mx":
+        d = synth.make_w4a16mx(900, M, N, K)
+        return hq.DESC_W4A16_MXFP4, (d["wq"], d["scales"], None), d["x"], None
     d = synth.make_w4a8mx(900, M, N, K)
     return hq.DESC_W4A8_MXFP8, (d["wq"], d["scales"], None), d["xq"], d["xs"]
 
 
-@pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx"])
+@pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx", "w4a16mx"])
 def test_rows_do_not_depend_on_the_batch(fmt):
     M, N, K = 300, 512, 1024
     desc, std, x, s = _inputs(fmt, M, N, K)
@@ -67,6 +70,8 @@ def test_rows_do_not_depend_on_the_batch(fmt):
         ref, _ = oracle.ref_w4a8(x, s, std[0], std[1])
     elif fmt == "w4a4":
         ref, _ = oracle.ref_w4a4(x, s, std[0], std[1])
+    elif fmt == "w4a16mx":
+        ref, _ = oracle.ref_w4a16_mx(x, std[0], std[1])
     else:
         ref, _ = oracle.ref_w4a8_mx(x, s, std[0], std[1])
     check_float(ref_rows, ref, f"invariant {fmt}")
