@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | w4a4 | moe | moe_layer.
+--config w8a8 | w4a8 | w4a4 | w4a16mx | moe | moe_mx | moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -40,6 +40,8 @@ WORKLOADS = {
                  dtype="fp8", peak="fp8"),
     "w4a4": dict(name="dense W4A4-MXFP4", N=4096, K=7168, Ms=[1, 32, 256, 2048, 8192], cfg=4,
                  dtype="fp4", peak="fp4"),
+    "w4a16mx": dict(name="dense W4A16-MXFP4 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
+                    dtype="bf16", peak="bf16"),
 }
 
 
@@ -86,6 +88,8 @@ def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
         return N * K + N * 4 + M * K + M * 4 + M * N * 2
     if wl == "w4a4":
         return N * K // 2 + N * (K // 32) + M * K // 2 + M * (K // 32) + M * N * 2
+    if wl == "w4a16mx":
+        return N * K // 2 + N * (K // 32) + M * K * 2 + M * N * 2
     return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
 
 
@@ -108,6 +112,11 @@ def make_inputs(wl: str, spec: dict):
         for M in spec["Ms"]:
             a = synth.make_w8a8_activations(cfg, M, K)
             acts[M] = (a["xq"], a["s_tok"])
+    elif wl == "w4a16mx":
+        d = synth.make_w4a16mx(cfg, 1, N, K)
+        desc = hq.DESC_W4A16_MXFP4
+        std = (d["wq"], d["scales"], None)
+        acts = {M: (synth.normal_bf16(synth.rng(cfg, M), (M, K)), None) for M in spec["Ms"]}
     elif wl == "w4a4":
         d = synth.make_w4a4(cfg, 1, N, K)
         desc = hq.DESC_W4A4_MXFP4
@@ -154,6 +163,8 @@ def cpu_baseline(wl: str, spec: dict, std, acts):
             oracle.ref_w8a8(x, s, std[0], std[1], rows=rows)
         elif wl == "w4a4":
             oracle.ref_w4a4(x, s, std[0], std[1], rows=rows)
+        elif wl == "w4a16mx":
+            oracle.ref_w4a16_mx(x, std[0], std[1], rows=rows)
         else:
             oracle.ref_w4a8(x, s, std[0], std[1], rows=rows)
         dt = time.perf_counter() - t0
@@ -312,7 +323,8 @@ def run_dense(args, wl: str):
                    "weights": {"w4a16": "uint4 asym g128 bf16 scale + uint4 zero",
                                "w8a8": "int8 per-channel fp32 scale, int8 per-token act",
                                "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act",
-                               "w4a4": "mxfp4 e2m1 + e8m0 per 32, mxfp4 act (e8m0 per 32)"}[wl]},
+                               "w4a4": "mxfp4 e2m1 + e8m0 per 32, mxfp4 act (e8m0 per 32)",
+                               "w4a16mx": "mxfp4 e2m1 + e8m0 per 32, bf16 act"}[wl]},
         "roofline": roof,
         "sweep": sweep,
     }
@@ -328,8 +340,17 @@ MOE = dict(name="MoE grouped GEMM W4A16 (DeepSeek-V3-shaped gate_up)", E=256, to
            K=7168, Ts=[1, 32, 512, 4096], cfg=5)
 
 
-def run_moe(args):
-    """Token sort + grouped GEMM per T. tokens/s = T / (t_align + t_gemm)."""
+def _random_mxfp4_expert(g, N: int, K: int):
+    """Standard-format MXFP4 weights with uniformly random codes and e8m0 scales near those of
+    N(0, 0.02) blocks (only the data volume matters for throughput)."""
+    import numpy as np
+    return {"wq": g.integers(0, 256, (N, K // 2), dtype=np.uint8),
+            "scales": g.integers(119, 123, (N, K // 32)).astype(np.uint8)}
+
+
+def run_moe(args, mx: bool = False):
+    """Token sort + grouped GEMM per T. tokens/s = T / (t_align + t_gemm). mx: MXFP4 experts
+    (W4A16-MXFP4) instead of INT4 group-128."""
     import numpy as np
     import torch
 
@@ -338,15 +359,17 @@ def run_moe(args):
 
     E, topk, N, K, Ts, cfg = (MOE[k] for k in ("E", "topk", "N", "K", "Ts", "cfg"))
     dev = torch.device("cuda:0")
-    desc = hq.DESC_W4A16_SYM
+    desc = hq.DESC_W4A16_MXFP4 if mx else hq.DESC_W4A16_SYM
+    name = MOE["name"].replace("W4A16", "W4A16-MXFP4") if mx else MOE["name"]
+    expert_gen = _random_mxfp4_expert if mx else synth.random_int4_sym_expert
     stride = hq.hq_prepacked_bytes(desc, 1, N, K)
-    log(f"[bench] {MOE['name']}: {E} experts x {stride / 1e6:.1f} MB prepacked (random INT4 codes)")
+    log(f"[bench] {name}: {E} experts x {stride / 1e6:.1f} MB prepacked (random codes)")
     w0 = torch.empty(stride * E, dtype=torch.uint8, device=dev)
     g = synth.rng(cfg, 0)
     std = {}
     host = np.zeros(stride, np.uint8)
     for e in range(E):
-        d = synth.random_int4_sym_expert(g, N, K)
+        d = expert_gen(g, N, K)
         if e < 16:
             std[e] = d
         hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, host)
@@ -447,13 +470,13 @@ def run_moe(args):
     else:
         roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
-    roof.update(traffic=measured_traffic("moe", f"T={dom['T']}"), kernel=f"grouped GEMM T={dom['T']}")
+    roof.update(traffic=measured_traffic("moe_mx" if mx else "moe", f"T={dom['T']}"), kernel=f"grouped GEMM T={dom['T']}")
     line = {
         "metric": METRIC, "value": round(tot_tok / tot_t, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": MOE["name"], "E": E, "topk": topk, "N": N, "K": K, "T": Ts,
+        "config": {"workload": name, "E": E, "topk": topk, "N": N, "K": K, "T": Ts,
                    "routing": "N(0,1) logits + Zipf(1.1) log-prior, softmax top-8"},
         "roofline": roof, "sweep": sweep, "cpu_baseline": None,
     }
@@ -465,7 +488,7 @@ def run_moe(args):
         rg = synth.rng(cfg, 0)
         ws = {}
         for e in range(max(need) + 1):      # regenerate the same random experts in order
-            d = synth.random_int4_sym_expert(rg, N, K)
+            d = expert_gen(rg, N, K)
             if e in need:
                 ws[e] = d
         t0 = time.perf_counter()
@@ -668,7 +691,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_layer"])
+    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -677,6 +700,8 @@ def main():
         sys.exit(2)
     if args.config == "moe":
         line = run_moe(args)
+    elif args.config == "moe_mx":
+        line = run_moe(args, mx=True)
     elif args.config == "moe_layer":
         line = run_moe_layer(args)
     else:
