@@ -23,6 +23,11 @@ block of 32 consecutive k (the MXFP4 format the announcement's W4A4 path consume
     code   = nearest e2m1 value to v, ties to the even code, saturating at +-6; the sign bit is
              set only for a non-zero magnitude (a negative value that rounds to zero gives +0)
 
+FP8 activations with block scales (for the block-scaled FP8 W8A8) apply the per-token e4m3 rule
+above to every block of 128 consecutive k of a row instead of the whole row: s[m, g] =
+fp32(max |x| over the block / 448) (1 for an all-zero block), codes = e4m3 of
+clamp(fp32(x / s[m, g]), -448, 448).
+
 MXFP8 activations (e4m3 elements, for W4A8 with MX activations) take the same rule with the
 largest e4m3 exponent, 8: e = floor(log2(max |x|)) - 8 clamped to [-127, 127], v = x * 2^-e,
 code = the e4m3 encoding above of clamp(v, -448, 448) (|v| < 512 always).
@@ -137,3 +142,18 @@ def quantize_mxfp8_act(x_bf16: np.ndarray):
     v = blocks * np.ldexp(1.0, -e)[:, :, None]
     codes = encode_e4m3(np.clip(v, -448.0, 448.0)).reshape(M, K)
     return codes, (e + 127).astype(np.uint8)
+
+
+def quantize_fp8_block_act(x_bf16: np.ndarray, block: int = 128):
+    """x_bf16: uint16 bf16 bits [M, K] (K % block == 0). Returns (e4m3 codes uint8 [M, K], fp32
+    scales [M, K/block]): the per-token e4m3 rule applied to each block of `block` k."""
+    M, K = x_bf16.shape
+    G = K // block
+    xb = np.ascontiguousarray(np.asarray(x_bf16).reshape(M, G, block).transpose(1, 0, 2))  # [G, M, block]
+    codes = np.empty((M, K), dtype=np.uint8)
+    scales = np.empty((M, G), dtype=np.float32)
+    for g in range(G):
+        q, s = quantize_per_token(xb[g], "e4m3")
+        codes[:, g * block:(g + 1) * block] = q
+        scales[:, g] = s
+    return codes, scales

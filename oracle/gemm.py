@@ -125,3 +125,22 @@ def ref_w4a16_mx(x_bf16: np.ndarray, wq: np.ndarray, scales_e8m0: np.ndarray, ro
     w = dequant_mxfp4(wq, scales_e8m0, cols)
     y = x @ w.T
     return y, round_to_bf16(y)
+
+
+def ref_w8a8_fp8_block(xq: np.ndarray, xs: np.ndarray, wq: np.ndarray, ws: np.ndarray, rows=None, cols=None):
+    """FP8 W8A8 with block scales (the page's "FP8 W8A8 with blockwise scaling"): e4m3 activations
+    with an fp32 scale per (token, 128-k block), e4m3 weights with an fp32 scale per (128-n block,
+    128-k block):
+        y[m, n] = sum_g xs[m, g] * ws[n // 128, g] * sum_{k in g} e4m3(xq[m, k]) * e4m3(wq[n, k])
+    exact in float64, rounded once to bf16. Returns (y float64, y bf16 bits)."""
+    x = decode_e4m3(_sel(xq, rows))
+    w = decode_e4m3(_sel(wq, cols))
+    sa = np.asarray(_sel(xs, rows), dtype=np.float32).astype(np.float64)
+    n_idx = np.arange(wq.shape[0]) if cols is None else np.asarray(cols)
+    sw = np.asarray(ws, dtype=np.float32).astype(np.float64)[n_idx // 128]      # [N', G]
+    G = x.shape[1] // 128
+    y = np.zeros((x.shape[0], w.shape[0]))
+    for g in range(G):
+        part = x[:, 128 * g:128 * (g + 1)] @ w[:, 128 * g:128 * (g + 1)].T
+        y += part * sa[:, g:g + 1] * sw[None, :, g]
+    return y, round_to_bf16(y)

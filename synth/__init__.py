@@ -263,6 +263,30 @@ def make_moe_weights_expert_mx(config_id: int, e: int, N: int, K: int):
     return quantize_mxfp4(w)
 
 
+def quantize_fp8_blocks(x: np.ndarray, bm: int, bk: int):
+    """e4m3 codes with an fp32 scale per (bm x bk) block: s = amax / 448 (1 for a zero block),
+    codes by torch's e4m3 cast of clamp(x / s). Returns codes uint8 [R, C], scales fp32 [R/bm, C/bk]."""
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    xb = x.reshape(R // bm, bm, C // bk, bk)
+    amax = np.abs(xb).max(axis=(1, 3))
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    s = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    v = np.clip(xb / s[:, None, :, None], -448.0, 448.0).astype(np.float32).reshape(R, C)
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes.copy(), s
+
+
+def make_w8a8_fp8_block(config_id: int, M: int, N: int, K: int):
+    """Block-scaled FP8 W8A8: weights N(0, 0.02) with a scale per 128 x 128 block, activations
+    bf16 N(0,1) with a scale per (token, 128 k)."""
+    w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    wq, ws = quantize_fp8_blocks(w, 128, 128)
+    x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))
+    xq, xs = quantize_fp8_blocks(x, 1, 128)
+    return {"xq": xq, "xs": xs, "wq": wq, "ws": ws}
+
+
 def make_w4a4_activations(config_id: int, M: int, K: int):
     """MXFP4 activations (e2m1 codes + e8m0 per 32 k) quantized from bf16 N(0,1) by the OCP MX
     rule (the same quantizer as the weights')."""
