@@ -57,7 +57,8 @@ typedef enum {
   HQ_W_INT4_SYM = 0,   /* two's-complement INT4 in [-8, 7], packed 2 per byte, low nibble = even k */
   HQ_W_UINT4_ASYM = 1, /* unsigned INT4 in [0, 15] with a uint4 zero-point per (n, group)          */
   HQ_W_INT8_SYM = 2,   /* two's-complement INT8 (codes in [-127, 127])                              */
-  HQ_W_FP4_E2M1 = 3    /* OCP MX e2m1, packed 2 per byte, low nibble = even k                      */
+  HQ_W_FP4_E2M1 = 3,   /* OCP MX e2m1, packed 2 per byte, low nibble = even k                      */
+  HQ_W_FP8_E4M3 = 4    /* OCP e4m3 [N, K], one fp32 scale per 128 x 128 block (group_size 128)     */
 } hq_weight_fmt;
 
 typedef enum {
@@ -72,8 +73,9 @@ typedef enum {
   HQ_ACT_FP8E4M3_PER_TOKEN = 2, /* OCP e4m3 [M, K] row-major + fp32 scale per row [M] */
   HQ_ACT_MXFP4 = 3,             /* OCP MX e2m1 [M, K/2] (low nibble = even k) + e8m0 byte per
                                    (row, 32-element block) [M, K/32]                        */
-  HQ_ACT_MXFP8 = 4              /* OCP MX e4m3 [M, K] + e8m0 byte per (row, 32-element block)
+  HQ_ACT_MXFP8 = 4,             /* OCP MX e4m3 [M, K] + e8m0 byte per (row, 32-element block)
                                    [M, K/32]                                                 */
+  HQ_ACT_FP8E4M3_BLOCK128 = 5   /* OCP e4m3 [M, K] + fp32 scale per (row, 128-k block) [M, K/128] */
 } hq_act_fmt;
 
 typedef enum {
@@ -111,6 +113,8 @@ typedef struct {
  *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_MXFP8             -> OUT_BF16
  *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_MXFP4  (W4A4)     -> OUT_BF16
  *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_BF16   (W4A16)    -> OUT_BF16
+ *   FP8_E4M3   + FP32 scale, 128 x 128 blocks         + ACT_FP8E4M3_BLOCK128  -> OUT_BF16
+ *              (N % 128 == 0, K % 128 == 0)
  * MoE grouped GEMM and grouped GEMM: the combinations with ACT_BF16 (INT4 sym / asym, FP4).
  * Every combination also takes compute_flags = HQ_COMPUTE_BATCH_INVARIANT.
  */
@@ -126,6 +130,8 @@ typedef struct {
  *   e4m3     : xq = nearest OCP e4m3 code to clamp(v, -448, 448), ties to the even code
  *              (negative values that round to zero give -0, 0x80)
  * act_fmt  HQ_ACT_INT8_PER_TOKEN or HQ_ACT_FP8E4M3_PER_TOKEN (the desc act_fmt of the GEMM), or
+ *          HQ_ACT_FP8E4M3_BLOCK128: the e4m3 rule above on every 128-k block of a row (s_tok then
+ *            receives fp32 [M, K/128], xq e4m3 [M, K]; K % 128 == 0). Or
  *          HQ_ACT_MXFP8: the same rule with e4m3 elements -- e = floor(log2 max|x|) - 8, code =
  *            e4m3 of clamp(x * 2^-e, -448, 448) as above; xq is e4m3 [M, K], s_tok receives
  *            the e8m0 bytes [M, K/32] (cast); K % 32 == 0. Or
@@ -146,8 +152,9 @@ hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const v
 /* ---------------------------------------------------------------------------------------------
  * Weight prepack (host).  Standard-format inputs, all host memory, row-major:
  *   wq      INT4/FP4: uint8 [E, N, K/2] (two codes per byte, low nibble = even k)
- *           INT8    : int8  [E, N, K]
- *   scales  BF16: uint16 bf16 bits [E, N, K/group];  FP32: float [E, N];  E8M0: uint8 [E, N, K/32]
+ *           INT8    : int8  [E, N, K];  FP8: e4m3 bytes [E, N, K]
+ *   scales  BF16: uint16 bf16 bits [E, N, K/group];  FP32: float [E, N] (INT8) or
+ *           float [E, N/128, K/128] (FP8 block scales);  E8M0: uint8 [E, N, K/32]
  *   zeros   UINT4_ASYM only: uint8 [E, N, K/group], values 0..15; NULL otherwise
  * E = 1 for a dense layer, E = number of experts for MoE (experts stacked).
  * Output: `out` (host, `hq_prepacked_bytes` bytes) receives the weights rearranged into the
@@ -179,6 +186,9 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
  *             MXFP4 weights with bf16 activations (desc act_fmt HQ_ACT_BF16), "W4A16-MXFP4":
  *                    bf16( sum_k a * e2m1(q) 2^(e - 127) ) (each weight dequantized exactly to
  *                    bf16, fp32 accumulation); also for hq_moe_grouped_gemm / hq_grouped_gemm
+ *             FP8 W8A8 with block scales (HQ_W_FP8_E4M3 + HQ_ACT_FP8E4M3_BLOCK128; a_scale =
+ *                    fp32 [M, K/128]): bf16( sum_g a_scale[m, g] * s_w[n/128, g] *
+ *                    sum_{k in g} e4m3(a) * e4m3(q) ) (fp32 accumulation)
  *             W4A8 with MXFP8 activations (desc act_fmt HQ_ACT_MXFP8):
  *                    bf16( sum_k e4m3(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation)
  * All bf16 results use round-to-nearest-even. M = 0 is a no-op returning HQ_OK.
@@ -267,7 +277,7 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
  * `python -m quantized_gemm_prepacked_amd.autotune` (the roadmap's autotune, run offline) takes
  * precedence for the shapes it lists. Text, one entry per line ('#' comments):
  *     <family> <asym 0|1> <N> <K> <max_m> <kind> <cfg> <split>
- * family wna16 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
+ * family wna16 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16 | fp8b; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
  * 3 ping-pong; cfg indexes that kind's configurations (hq_kernel_config_count); split = K splits
  * of the skinny kernel, -1 = the heuristic's. A dense call uses the first entry of its family,
  * asym, N and K whose max_m >= M, if that configuration fits the shape; otherwise the built-in

@@ -188,6 +188,40 @@ __global__ __launch_bounds__(kThreads) void act_quant_mxfp8_kernel(const uint16_
   *reinterpret_cast<u32x4*>(dst + 4) = u32x4{out[4], out[5], out[6], out[7]};
 }
 
+// FP8 activations with a scale per (row, 128-k block), for the block-scaled FP8 W8A8: the
+// per-token rule on each block -- s = fp32(amax / 448) (1 for a zero block), codes = e4m3 of
+// clamp(fp32(x / s), +-448). Sixteen lanes per block, eight elements per lane; the block maximum
+// by shuffles within the sixteen lanes.
+__global__ __launch_bounds__(kThreads) void act_quant_fp8block_kernel(const uint16_t* __restrict__ x,
+                                                                      uint8_t* __restrict__ xq,
+                                                                      float* __restrict__ xs,
+                                                                      int64_t n_groups) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;   // 8-element group index
+  const bool live = i < n_groups;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (live) v = ldg16(x + i * 8);
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  float s = amax / 448.0f;
+  if (s == 0.0f) s = 1.0f;
+  if (!live) return;
+  if ((i & 15) == 0) xs[i >> 4] = s;
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t bits = (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
+    const float q = __uint_as_float(bits) / s;
+    out[j >> 2] |= e4m3_rne(fminf(fmaxf(q, -448.0f), 448.0f)) << (8 * (j & 3));
+  }
+  *reinterpret_cast<uint2*>(xq + i * 8) = make_uint2(out[0], out[1]);
+}
+
 }  // namespace
 
 hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, void* xq, float* s_tok,
@@ -195,6 +229,12 @@ hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, vo
   const dim3 grid{static_cast<unsigned>(M)};
   const auto* xin = static_cast<const uint16_t*>(x);
   auto* out = static_cast<uint8_t*>(xq);
+  if (act_fmt == HQ_ACT_FP8E4M3_BLOCK128) {
+    const int64_t ng = M * (K / 8);   // a multiple of 16: K % 128 == 0
+    hipLaunchKernelGGL(act_quant_fp8block_kernel, dim3(unsigned((ng + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, xin, out, s_tok, ng);
+    return hipGetLastError();
+  }
   if (act_fmt == HQ_ACT_MXFP8) {
     const int64_t nb = M * (K / 32);
     hipLaunchKernelGGL(act_quant_mxfp8_kernel, dim3(unsigned((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0,

@@ -114,6 +114,16 @@ __device__ __forceinline__ f32x4 mfma_fp8_fp4(u32x4 a_lo, u32x4 a_hi, u32x4 b, i
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, a_scale, 0, b_scale);
 }
 
+// Both operands fp8 e4m3 (formats 0 and 0), unit block scales: one 128-k step of A and B in the
+// 8-bit layout above (each as two 16-byte halves).
+__device__ __forceinline__ f32x4 mfma_fp8_fp8(u32x4 a_lo, u32x4 a_hi, u32x4 b_lo, u32x4 b_hi, f32x4 c) {
+  i32x8 av = {int(a_lo[0]), int(a_lo[1]), int(a_lo[2]), int(a_lo[3]),
+              int(a_hi[0]), int(a_hi[1]), int(a_hi[2]), int(a_hi[3])};
+  i32x8 bv = {int(b_lo[0]), int(b_lo[1]), int(b_lo[2]), int(b_lo[3]),
+              int(b_hi[0]), int(b_hi[1]), int(b_hi[2]), int(b_hi[3])};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+}
+
 // Both operands fp4 e2m1 (formats 4 and 4), each with its own e8m0 block scales: 4-bit A takes
 // the same K layout as 4-bit B (lane group g holds k = 32g + j in nibble j).
 __device__ __forceinline__ f32x4 mfma_fp4_fp4(u32x4 a, int a_scale, u32x4 b, int b_scale, f32x4 c) {

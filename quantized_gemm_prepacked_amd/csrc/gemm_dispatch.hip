@@ -21,7 +21,8 @@ namespace {
 
 constexpr int kCUs = 256;
 
-int k_unit(const Combo& c) { return family_k_unit(c.fam); }
+// K per skinny unit (block-scaled FP8 steps over two 64-k layout units at a time)
+int k_unit(const Combo& c) { return c.fam == FAM_FP8B ? 128 : family_k_unit(c.fam); }
 
 // Pick the skinny configuration for a row block of `rows` rows and N channels (measured on
 // MI355X at the benchmark shapes; the first candidate whose channel-tile count divides N/16).
@@ -36,6 +37,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   };
   if (rows <= 16) {
     if (c.fam == FAM_MXW4A16) return first_fit({28, 13, 0, 1, 2});
+    if (c.fam == FAM_FP8B) return first_fit({21, 2});
     if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
     if (c.fam == FAM_W4A8) return first_fit({21, 2});
     if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({21, 2});
@@ -43,6 +45,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   }
   if (rows <= 32) {
     if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
+    if (c.fam == FAM_FP8B) return first_fit({16, 8});
     if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({16, 8});
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
@@ -98,6 +101,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8MX>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_MXW4A16)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_MXW4A16>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_FP8B)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_FP8B>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -132,6 +137,8 @@ constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {k
 constexpr RangeEntry kW4a4Table[] = {{768, 0, 0}, {4096, 3, 2}, {kInf, 3, 0}};
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
 constexpr RangeEntry kMxW4a16Table[] = {{64, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
+// Block-scaled FP8 W8A8: skinny and ping-pong only (first guess, W4A8's crossover)
+constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {2048, 3, 2}, {kInf, 3, 0}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -158,6 +165,9 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_W8A8) {
     t = kW8a8Table;
     n = int(sizeof(kW8a8Table) / sizeof(kW8a8Table[0]));
+  } else if (c.fam == FAM_FP8B) {
+    t = kFp8bTable;
+    n = int(sizeof(kFp8bTable) / sizeof(kFp8bTable[0]));
   } else if (c.fam == FAM_MXW4A16) {
     t = kMxW4a16Table;
     n = int(sizeof(kMxW4a16Table) / sizeof(kMxW4a16Table[0]));
@@ -177,7 +187,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
     return t[i];
   }
   // Fallbacks when the preferred tile does not divide N.
-  if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16) {
+  if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
     for (int cfg : {3, 2})   // 128 x 128 tiles
@@ -201,7 +211,9 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
     return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
-  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16) && (o.kind == 1 || o.kind == 2)) return false;
+  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B) &&
+      (o.kind == 1 || o.kind == 2))
+    return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -289,7 +301,8 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   // The direct-to-LDS kernels address activations with 32-bit offsets.
   if ((pick.kind == 2 || pick.kind == 3) &&
       uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) >= (uint64_t(1) << 32)) {
-    const int tc = (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16) ? -1 : pick_tiled(c, N, K);
+    const int tc = (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B)
+                       ? -1 : pick_tiled(c, N, K);
     pick = tc >= 0 ? RangeEntry{kInf, 1, tc} : RangeEntry{0, 0, 0};
   }
   if (pick.kind != 0) {
@@ -528,7 +541,8 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   }
   p.M = int(call.M);
   p.split = plan.split;
-  p.units_per_split = (p.k_units + plan.split - 1) / plan.split;
+  const int sk_units = int(call.K / k_unit(c));   // skinny units (128-k steps for block-scaled FP8)
+  p.units_per_split = (sk_units + plan.split - 1) / plan.split;
   dim3 grid(unsigned(call.N / 16 / sc.ntw), unsigned((call.M + rows_per_block - 1) / rows_per_block),
             unsigned(plan.split));
   hipError_t e = launch_skinny(p, c.fam, false, plan.cfg, grid, call.stream);

@@ -52,6 +52,13 @@ struct PPTraits<FAM_W8A8> {
   static constexpr int kAScaleBytes = 0;
 };
 template <>
+struct PPTraits<FAM_FP8B> {
+  static constexpr int kRowBytes = 128;
+  static constexpr int kUnitsPerStep = 2;
+  static constexpr int kMetaPerTile = 16;   // the block's fp32 weight scale, four copies
+  static constexpr int kAScaleBytes = 4;    // fp32 activation scale of the row's 128-k block
+};
+template <>
 struct PPTraits<FAM_W4A8> {
   static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 1;
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     if constexpr (Sh::META_BYTES > 0) {
       // lanes past META_LANES skip the copy (a direct-to-LDS load writes lane i at base + 16 i);
       // the instruction still counts once in this wave's vmcnt
-      const size_t unit = size_t(nt_wg + meta_tile) * p.k_units + ks;
+      const size_t unit = size_t(nt_wg + meta_tile) * (p.k_units / UPS) + ks;
       if (lane < Sh::META_LANES)
         lds_dma16(w + p.scales_off + unit * Sh::MPT + meta_byte, sb + Sh::B_BYTES + wave * Sh::META_PER_WAVE);
     }
@@ -242,11 +249,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   // Operand fragments of one step, filled by the memory phase and used by the compute phase.
   constexpr bool BF16A = FAM == FAM_WNA16 || FAM == FAM_MXW4A16;   // bf16 activations
   constexpr int NA = BF16A ? 4 : (FAM == FAM_W4A4 ? 1 : 2);   // activation fragments per row block
-  constexpr int NB = FAM == FAM_W8A8 ? 2 : 1;    // packed weight fragments per channel tile
+  constexpr int NB = (FAM == FAM_W8A8 || FAM == FAM_FP8B) ? 2 : 1;    // packed weight fragments per channel tile
   u32x4 af[MW][NA];
   u32x4 bq[NTW][NB];
   uint32_t meta[NTW];
   int asf[MW];   // MXFP4 activations: this lane's row block scale
+  float asr[MW][4];   // block-scaled FP8: the activation scale of each output row of the lane
 
   auto memory_phase = [&](int ks) {
     const uint8_t* st = smem + (ks % S) * Sh::STAGE;
@@ -260,7 +268,13 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         const int chunk = BF16A ? 4 * (lane >> 4) + d : 4 * d + (lane >> 4);
         af[mb][d] = read_a(st, mb, chunk);
       }
-    if constexpr (Sh::ASC_BYTES > 0) {
+    if constexpr (FAM == FAM_FP8B) {
+      const float* sa = reinterpret_cast<const float*>(sm + Sh::META_BYTES);
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asr[mb][i] = sa[wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i];
+    } else if constexpr (Sh::ASC_BYTES > 0) {
       const uint8_t* sa = sm + Sh::META_BYTES;
 #pragma unroll
       for (int mb = 0; mb < MW; ++mb)
@@ -275,6 +289,8 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         meta[t] = *reinterpret_cast<const uint16_t*>(sm + tw * 32 + 2 * (lane & 15));
       else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX || FAM == FAM_MXW4A16)
         meta[t] = sm[tw * 64 + lane];
+      else if constexpr (FAM == FAM_FP8B)
+        meta[t] = *reinterpret_cast<const uint32_t*>(sm + tw * 16);
     }
   };
 
@@ -327,6 +343,17 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
           const bf16x8 bv = dequant_fp4x8_scaled(bq[t][0][d], s);
 #pragma unroll
           for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+        }
+      }
+    } else if constexpr (FAM == FAM_FP8B) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float sw = __uint_as_float(meta[t]);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) {
+          const f32x4 part = mfma_fp8_fp8(af[mb][0], af[mb][1], bq[t][0], bq[t][1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[i] * (asr[mb][i] * sw);
         }
       }
     } else if constexpr (FAM == FAM_W8A8) {
@@ -449,6 +476,7 @@ int pp_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W4A4) return pp_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return pp_lds_table<FAM_W4A8MX>(cfg, seq);
   if (fam == FAM_MXW4A16) return pp_lds_table<FAM_MXW4A16>(cfg, seq);
+  if (fam == FAM_FP8B) return pp_lds_table<FAM_FP8B>(cfg, seq);
   return pp_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -490,6 +518,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_FP8B) return launch_pp_fam<FAM_FP8B, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return launch_pp_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
 }
 

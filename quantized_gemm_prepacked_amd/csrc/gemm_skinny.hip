@@ -32,7 +32,12 @@ namespace {
 template <int FAM>
 struct SkTraits;
 // kRowBytes: activation bytes per row per unit of kUnitK k; kAScaleBytes: activation block-scale
-// bytes per row per unit (MXFP4 activations: one e8m0 byte per 32 k).
+// bytes per row per unit (MXFP4 activations: one e8m0 byte per 32 k; block-scaled FP8: one fp32);
+// kWLoads: 1 KB weight units per kernel unit (block-scaled FP8: two 64-k units per 128-k step).
+template <int FAM>
+struct SkWLoads {
+  static constexpr int value = FAM == FAM_FP8B ? 2 : 1;
+};
 template <>
 struct SkTraits<FAM_WNA16> {
   static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
@@ -40,6 +45,10 @@ struct SkTraits<FAM_WNA16> {
 template <>
 struct SkTraits<FAM_W8A8> {
   static constexpr int kRowBytes = 64, kUnitK = 64, kScaleBytes = 0, kZeroBytes = 0, kAScaleBytes = 0;
+};
+template <>
+struct SkTraits<FAM_FP8B> {
+  static constexpr int kRowBytes = 128, kUnitK = 128, kScaleBytes = 16, kZeroBytes = 0, kAScaleBytes = 4;
 };
 template <>
 struct SkTraits<FAM_W4A8> {
@@ -74,7 +83,8 @@ struct SkShape {
   static constexpr int WAVE_LDS = NBUF * UNR * UNIT_LDS;
   static constexpr int RED = NW * MB * NTW * 4 * 64 * 4; // epilogue reduction (aliases the slots)
   static constexpr int LDS = (NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED);
-  static constexpr int UNIT_INSTR = A_INSTR + NTW + META_INSTR;   // vector-memory ops per unit
+  static constexpr int WL = SkWLoads<FAM>::value;
+  static constexpr int UNIT_INSTR = A_INSTR + NTW * WL + META_INSTR;   // vector-memory ops per unit
   static_assert(A_UNIT % 1024 == 0, "whole-wave activation copies");
   static_assert(SC / 16 <= 64 && ZB / 4 <= 64 && ASC / 4 <= 64, "metadata copies fit one instruction each");
   static_assert(UNR * UNIT_INSTR < 64, "vmcnt range");
@@ -138,6 +148,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 
   uint8_t* wlds = smem + wave * Sh::WAVE_LDS;
   u32x4 bw[Sh::NBUF][UNR][NTW];   // packed weights of the batches in flight
+  u32x4 bw2[Sh::NBUF][UNR][Sh::WL == 2 ? NTW : 1];   // block-scaled FP8: the step's second unit
+  const int k_units = p.k_units / Sh::WL;             // kernel units (steps of kUnitK k)
 
   // Issue every copy and load of unit u into slot (buf, r).
   auto issue_unit = [&](int buf, int r, int u) __attribute__((always_inline)) {
@@ -146,14 +158,15 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     for (int j = 0; j < Sh::A_INSTR; ++j) lds_dma16(asrc[j] + size_t(u) * ROWB, slot + 1024 * j);
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const size_t unit = size_t(nt0 + t) * p.k_units + u;
+      const size_t unit = (size_t(nt0 + t) * k_units + u) * Sh::WL;
       bw[buf][r][t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
+      if constexpr (Sh::WL == 2) bw2[buf][r][t] = ldg16_stream(w + (unit + 1) * kUnitBytes + 16 * lane);
     }
     if constexpr (Sh::SC > 0) {
       // the NTW tiles' scale blocks of this unit, T::kScaleBytes each, 16 bytes per lane
       constexpr int per_tile = T::kScaleBytes / 16;
       const int t = min(lane / per_tile, NTW - 1);
-      const size_t unit = size_t(nt0 + t) * p.k_units + u;
+      const size_t unit = size_t(nt0 + t) * k_units + u;
       if (lane < Sh::SC / 16)
         lds_dma16(w + p.scales_off + unit * T::kScaleBytes + 16 * (lane % per_tile), slot + Sh::A_UNIT);
     }
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
       // zero points (8 bytes per tile), 4 bytes per lane; symmetric weights have none and copy
       // scale bytes instead, which are never read
       const int t = min(lane >> 1, NTW - 1);
-      const size_t unit = size_t(nt0 + t) * p.k_units + u;
+      const size_t unit = size_t(nt0 + t) * k_units + u;
       const uint8_t* src = p.asym ? w + p.zeros_off + unit * 8 + 4 * (lane & 1)
                                   : w + p.scales_off + unit * T::kScaleBytes;
       if (lane < Sh::ZB / 4) lds_dma4(src, slot + Sh::A_UNIT + Sh::SC);
@@ -237,6 +250,27 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
           for (int mb = 0; mb < MB; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
         }
       }
+    } else if constexpr (FAM == FAM_FP8B) {
+      // one 128-k step = one scale block: the fp8 MFMA's partial, times (row scale x block
+      // scale), into the tile; the row scale is per output row (D rows 4 (lane >> 4) + i)
+      const uint8_t* sc = slot + Sh::A_UNIT;
+      const float* asc = reinterpret_cast<const float*>(sc + Sh::SC + Sh::ZB);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 alo = read_a(mb, lane >> 4);
+        const u32x4 ahi = read_a(mb, 4 + (lane >> 4));
+        float sa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = asc[16 * mb + 4 * (lane >> 4) + i];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const float sw = *reinterpret_cast<const float*>(sc + t * 16);
+          const f32x4 part = mfma_fp8_fp8(alo, ahi, bw[buf][r][t], bw2[buf][r][Sh::WL == 2 ? t : 0],
+                                          f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[i] * (sa[i] * sw);
+        }
+      }
     } else if constexpr (FAM == FAM_W8A8) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -278,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   // This wave's units are u0, u0 + NW, ... < uend, in batches of UNR; a remainder below UNR is
   // taken one unit at a time.
   const int ubeg = blockIdx.z * p.units_per_split;
-  const int uend = min(p.k_units, ubeg + p.units_per_split);
+  const int uend = min(k_units, ubeg + p.units_per_split);
   const int u0 = ubeg + wave;
   const int nunits = u0 < uend ? (uend - u0 + NW - 1) / NW : 0;
   const int nbatch = nunits / UNR;
@@ -417,6 +451,7 @@ int skinny_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W4A4) return skinny_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return skinny_lds_table<FAM_W4A8MX>(cfg, seq);
   if (fam == FAM_MXW4A16) return skinny_lds_table<FAM_MXW4A16>(cfg, seq);
+  if (fam == FAM_FP8B) return skinny_lds_table<FAM_FP8B>(cfg, seq);
   return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -460,6 +495,7 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);
   if (fam == FAM_W4A8MX) return launch_skinny_fam<FAM_W4A8MX, false>(p, cfg, grid, s);
+  if (fam == FAM_FP8B) return launch_skinny_fam<FAM_FP8B, false>(p, cfg, grid, s);
   return launch_skinny_fam<FAM_W4A8, false>(p, cfg, grid, s);
 }
 

@@ -85,6 +85,14 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
                : d->act_fmt == HQ_ACT_BF16  ? hq::FAM_MXW4A16
                                             : hq::FAM_W4A8;
       return HQ_OK;
+    case HQ_W_FP8_E4M3:
+      if (d->group_size != 128 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 ||
+          d->act_fmt != HQ_ACT_FP8E4M3_BLOCK128 || c->out_i32)
+        return fail(HQ_ERR_UNSUPPORTED,
+                    "FP8 weights need group_size 128 (128 x 128 blocks), FP32 scales, no zero-point, "
+                    "FP8 activations with 128-k block scales and bf16 output");
+      c->fam = hq::FAM_FP8B;
+      return HQ_OK;
     default:
       return fail(HQ_ERR_INVALID_ARGUMENT, "unknown weight_fmt %d", d->weight_fmt);
   }
@@ -93,7 +101,9 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
 hq_status check_shape(const hq::Combo& c, int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
     return fail(HQ_ERR_INVALID_ARGUMENT, "N=%lld K=%lld out of range", (long long)N, (long long)K);
-  const int ku = hq::family_k_unit(c.fam);
+  const int ku = c.fam == hq::FAM_FP8B ? 128 : hq::family_k_unit(c.fam);
+  if (c.fam == hq::FAM_FP8B && N % 128 != 0)
+    return fail(HQ_ERR_UNSUPPORTED, "FP8 block-scaled weights need N %% 128 == 0 (N=%lld)", (long long)N);
   if (N % 16 != 0 || K % ku != 0)
     return fail(HQ_ERR_UNSUPPORTED, "N must be a multiple of 16 and K of %d (N=%lld K=%lld)", ku,
                 (long long)N, (long long)K);
@@ -240,8 +250,11 @@ hq_status hq_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t
 hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const void* x, void* xq,
                                   float* s_tok, hq_stream_t stream) {
   if (act_fmt != HQ_ACT_INT8_PER_TOKEN && act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN && act_fmt != HQ_ACT_MXFP4 &&
-      act_fmt != HQ_ACT_MXFP8)
-    return fail(HQ_ERR_UNSUPPORTED, "act_fmt=%d: INT8 or FP8 e4m3 per-token, MXFP8 or MXFP4", act_fmt);
+      act_fmt != HQ_ACT_MXFP8 && act_fmt != HQ_ACT_FP8E4M3_BLOCK128)
+    return fail(HQ_ERR_UNSUPPORTED, "act_fmt=%d: INT8 or FP8 e4m3 per-token, FP8 per 128-k block, MXFP8 or MXFP4",
+                act_fmt);
+  if (act_fmt == HQ_ACT_FP8E4M3_BLOCK128 && K % 128 != 0)
+    return fail(HQ_ERR_UNSUPPORTED, "K=%lld must be a multiple of 128 for FP8 block scales", (long long)K);
   const bool mx = act_fmt == HQ_ACT_MXFP4 || act_fmt == HQ_ACT_MXFP8;
   if (M < 0 || M > kMaxDim || K <= 0 || K > kMaxDim)
     return fail(HQ_ERR_INVALID_ARGUMENT, "M=%lld K=%lld out of range", (long long)M, (long long)K);

@@ -35,12 +35,14 @@ namespace hq {
 
 // W4A4, W4A8 with MXFP8 activations (W4A8MX) and MXFP4 weights with bf16 activations (MXW4A16)
 // share W4A8's prepacked weights (MXFP4); only the activation operand differs.
-enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5 };
+// FP8B: block-scaled FP8 W8A8 (e4m3 weights with an fp32 scale per 128 x 128 block, e4m3
+// activations with an fp32 scale per (row, 128 k)); its codes use W8A8's 64-k units.
+enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5, FAM_FP8B = 6 };
 
 constexpr int kUnitBytes = 1024;
 constexpr int kTileN = 16;
 
-inline int family_k_unit(Family f) { return f == FAM_W8A8 ? 64 : 128; }
+inline int family_k_unit(Family f) { return (f == FAM_W8A8 || f == FAM_FP8B) ? 64 : 128; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -70,6 +72,10 @@ inline PackedLayout make_layout(Family fam, bool asym, int64_t N, int64_t K) {
     L.scales_bytes = size_t(L.n_tiles) * L.k_units * 16 * 2;
   } else if (fam == FAM_W8A8) {
     L.scales_bytes = size_t(N) * 4;
+  } else if (fam == FAM_FP8B) {
+    // per 16-channel tile and 128-k step: the 128 x 128 block's fp32 scale, four copies (one
+    // 16-byte copy granule)
+    L.scales_bytes = size_t(L.n_tiles) * size_t(K / 128) * 16;
   } else {
     L.scales_bytes = size_t(L.n_tiles) * L.k_units * 64;
   }

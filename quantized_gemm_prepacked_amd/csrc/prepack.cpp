@@ -88,7 +88,19 @@ void pack_w8a8(const PackedLayout& L, const int8_t* wq, const float* scales, uin
       }
     }
   });
-  std::memcpy(out + L.scales_off, scales, size_t(L.N) * 4);
+  if (scales) std::memcpy(out + L.scales_off, scales, size_t(L.N) * 4);
+}
+
+void pack_fp8b(const PackedLayout& L, const uint8_t* wq, const float* scales, uint8_t* out) {
+  const int64_t K = L.K, G = K / 128;
+  pack_w8a8(L, reinterpret_cast<const int8_t*>(wq), nullptr, out);   // the codes: W8A8's units
+  parallel_for(L.n_tiles, [&](int64_t nt) {
+    for (int64_t g = 0; g < G; ++g) {
+      const float s = scales[size_t(nt * 16 / 128) * G + g];
+      float* dst = reinterpret_cast<float*>(out + L.scales_off + (size_t(nt) * G + g) * 16);
+      for (int i = 0; i < 4; ++i) dst[i] = s;
+    }
+  });
 }
 
 void pack_w4a8(const PackedLayout& L, const uint8_t* wq, const uint8_t* scales, uint8_t* out) {
@@ -128,6 +140,9 @@ void prepack(const Combo& c, int64_t E, int64_t N, int64_t K, const void* wq,
     } else if (c.fam == FAM_W8A8) {
       pack_w8a8(L, static_cast<const int8_t*>(wq) + e * size_t(N) * K,
                 static_cast<const float*>(scales) + e * size_t(N), o);
+    } else if (c.fam == FAM_FP8B) {
+      pack_fp8b(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * K,
+                static_cast<const float*>(scales) + e * size_t(N / 128) * (K / 128), o);
     } else {
       pack_w4a8(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * (K / 2),
                 static_cast<const uint8_t*>(scales) + e * size_t(N) * (K / 32), o);

@@ -6,7 +6,7 @@
 // target device. Here the benchmarking is offline (quantized_gemm_prepacked_amd/autotune.py) and
 // its result is a text table, one entry per line:
 //     <family> <asym 0|1> <N> <K> <max_m> <kind> <cfg> <split>
-// family = wna16 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
+// family = wna16 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16 | fp8b; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
 // 3 ping-pong; split = K splits of the skinny kernel (-1 = the heuristic's). For a dense call the
 // first entry of its (family, asym, N, K) whose max_m covers M is used when that configuration
 // fits the shape; otherwise the built-in table decides. '#' starts a comment.
@@ -42,6 +42,7 @@ bool parse_family(const std::string& s, Family* f) {
   else if (s == "w4a4") *f = FAM_W4A4;
   else if (s == "w4a8mx") *f = FAM_W4A8MX;
   else if (s == "mxw4a16") *f = FAM_MXW4A16;
+  else if (s == "fp8b") *f = FAM_FP8B;
   else return false;
   return true;
 }

@@ -31,6 +31,9 @@ def _inputs(fmt, M, N, K):
     if fmt == "w4a4":
         d = synth.make_w4a4(900, M, N, K)
         return hq.DESC_W4A4_MXFP4, (d["wq"], d["scales"], None), d["xq"], d["xs"]
+    if fmt == "fp8block":
+        d = synth.make_w8a8_fp8_block(900, M, N, K)
+        return hq.DESC_W8A8_FP8_BLOCK, (d["wq"], d["ws"], None), d["xq"], d["xs"]
     if fmt == "w4a16mx":
         d = synth.make_w4a16mx(900, M, N, K)
         return hq.DESC_W4A16_MXFP4, (d["wq"], d["scales"], None), d["x"], None
@@ -38,7 +41,7 @@ def _inputs(fmt, M, N, K):
     return hq.DESC_W4A8_MXFP8, (d["wq"], d["scales"], None), d["xq"], d["xs"]
 
 
-@pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx", "w4a16mx"])
+@pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx", "w4a16mx", "fp8block"])
 def test_rows_do_not_depend_on_the_batch(fmt):
     M, N, K = 300, 512, 1024
     desc, std, x, s = _inputs(fmt, M, N, K)
@@ -50,7 +53,7 @@ def test_rows_do_not_depend_on_the_batch(fmt):
     assert len(plans) == 1, plans
     for sub in SUBSETS:
         xs = x[sub]
-        ss = None if s is None else np.ascontiguousarray(s[sub]).reshape(-1)
+        ss = None if s is None else np.ascontiguousarray(s[sub])
         m = xs.shape[0]
         y = gemm(inv, m, N, K, to_dev(np.ascontiguousarray(xs)), None if ss is None else to_dev(ss), w)
         if full is None:
@@ -72,6 +75,8 @@ def test_rows_do_not_depend_on_the_batch(fmt):
         ref, _ = oracle.ref_w4a4(x, s, std[0], std[1])
     elif fmt == "w4a16mx":
         ref, _ = oracle.ref_w4a16_mx(x, std[0], std[1])
+    elif fmt == "fp8block":
+        ref, _ = oracle.ref_w8a8_fp8_block(x, s, std[0], std[1])
     else:
         ref, _ = oracle.ref_w4a8_mx(x, s, std[0], std[1])
     check_float(ref_rows, ref, f"invariant {fmt}")

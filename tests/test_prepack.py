@@ -122,3 +122,34 @@ def test_prepacked_sizes_match_nominal_bytes():
     b = hq.hq_prepacked_bytes(hq.DESC_W4A16_ASYM, 1, N, K)
     nominal = N * K // 2 + N * (K // 128) * 2 + N * (K // 128) // 2
     assert nominal <= b < nominal + 3 * 256
+
+
+def test_fp8_block_roundtrip():
+    """Block-scaled FP8: codes in W8A8's 64-k units, then per (16-channel tile, 128-k step) the
+    128 x 128 block's fp32 scale four times."""
+    N, K = 256, 384
+    d = synth.make_w8a8_fp8_block(914, 2, N, K)
+    desc = hq.DESC_W8A8_FP8_BLOCK
+    out = np.zeros(hq.hq_prepacked_bytes(desc, 1, N, K), np.uint8)
+    hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["ws"], None, out)
+    nt_n, G = N // 16, K // 128
+    codes = nt_n * (K // 64) * 1024
+    u = out[:codes].reshape(nt_n, K // 64, 4, 16, 16)
+    assert np.array_equal(u.transpose(0, 3, 1, 2, 4).reshape(N, K), d["wq"])
+    s_off = _a256(codes)
+    s = out[s_off:s_off + nt_n * G * 16].view(np.float32).reshape(nt_n, G, 4)
+    assert (s == s[:, :, :1]).all()
+    assert np.array_equal(s[:, :, 0], d["ws"][np.arange(nt_n) * 16 // 128])
+    assert out.size == _a256(s_off + nt_n * G * 16)
+
+
+def test_mxfp4_weight_layout_is_shared_by_its_activation_formats():
+    """W4A8, W4A4, MXFP8-activation W4A8 and bf16-activation W4A16 take the same MXFP4 weights."""
+    N, K = 32, 256
+    d = synth.make_w4a8(915, 1, N, K)
+    outs = []
+    for desc in (hq.DESC_W4A8_MXFP4, hq.DESC_W4A4_MXFP4, hq.DESC_W4A8_MXFP8, hq.DESC_W4A16_MXFP4):
+        out = np.zeros(hq.hq_prepacked_bytes(desc, 1, N, K), np.uint8)
+        hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, out)
+        outs.append(out)
+    assert all(np.array_equal(o, outs[0]) for o in outs)
