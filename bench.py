@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | w4a4 | w4a16mx | moe | moe_mx | moe_layer.
+--config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | moe | moe_mx | moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -42,6 +42,8 @@ WORKLOADS = {
                  dtype="fp4", peak="fp4"),
     "w4a16mx": dict(name="dense W4A16-MXFP4 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
                     dtype="bf16", peak="bf16"),
+    "fp8block": dict(name="dense FP8 W8A8 with 128x128 / 1x128 block scales", N=8192, K=8192,
+                     Ms=[1, 64, 512, 4096], cfg=3, dtype="fp8", peak="fp8"),
 }
 
 
@@ -90,6 +92,8 @@ def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
         return N * K // 2 + N * (K // 32) + M * K // 2 + M * (K // 32) + M * N * 2
     if wl == "w4a16mx":
         return N * K // 2 + N * (K // 32) + M * K * 2 + M * N * 2
+    if wl == "fp8block":
+        return N * K + (N // 128) * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
     return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
 
 
@@ -112,6 +116,14 @@ def make_inputs(wl: str, spec: dict):
         for M in spec["Ms"]:
             a = synth.make_w8a8_activations(cfg, M, K)
             acts[M] = (a["xq"], a["s_tok"])
+    elif wl == "fp8block":
+        d = synth.make_w8a8_fp8_block(cfg, 1, N, K)
+        desc = hq.DESC_W8A8_FP8_BLOCK
+        std = (d["wq"], d["ws"], None)
+        acts = {}
+        for M in spec["Ms"]:
+            a = synth.make_w8a8_fp8_block(cfg, M, 128, K)          # activations only (N unused)
+            acts[M] = (a["xq"], a["xs"])
     elif wl == "w4a16mx":
         d = synth.make_w4a16mx(cfg, 1, N, K)
         desc = hq.DESC_W4A16_MXFP4
@@ -165,6 +177,8 @@ def cpu_baseline(wl: str, spec: dict, std, acts):
             oracle.ref_w4a4(x, s, std[0], std[1], rows=rows)
         elif wl == "w4a16mx":
             oracle.ref_w4a16_mx(x, std[0], std[1], rows=rows)
+        elif wl == "fp8block":
+            oracle.ref_w8a8_fp8_block(x, s, std[0], std[1], rows=rows)
         else:
             oracle.ref_w4a8(x, s, std[0], std[1], rows=rows)
         dt = time.perf_counter() - t0
@@ -278,11 +292,11 @@ def run_dense(args, wl: str):
                       "frac": round(max(frac_c, frac_m), 4), "bytes": by, "flops": fl})
         tot_flops += fl
         tot_s += us * 1e-6
-    if wl in ("w8a8", "w4a8", "w4a4"):
+    if wl in ("w8a8", "w4a8", "w4a4", "fp8block"):
         # The step before these GEMMs (dynamic quantization of bf16 activations), timed the same
         # way for context; it is not part of `value`.
         act = {"w8a8": hq.HQ_ACT_INT8_PER_TOKEN, "w4a8": hq.HQ_ACT_FP8E4M3_PER_TOKEN,
-               "w4a4": hq.HQ_ACT_MXFP4}[wl]
+               "w4a4": hq.HQ_ACT_MXFP4, "fp8block": hq.HQ_ACT_FP8E4M3_BLOCK128}[wl]
         for row in sweep:
             M = row["M"]
             xb = torch.randn(M, K, device=dev).to(torch.bfloat16)
@@ -324,7 +338,8 @@ def run_dense(args, wl: str):
                                "w8a8": "int8 per-channel fp32 scale, int8 per-token act",
                                "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act",
                                "w4a4": "mxfp4 e2m1 + e8m0 per 32, mxfp4 act (e8m0 per 32)",
-                               "w4a16mx": "mxfp4 e2m1 + e8m0 per 32, bf16 act"}[wl]},
+                               "w4a16mx": "mxfp4 e2m1 + e8m0 per 32, bf16 act",
+                               "fp8block": "e4m3 + fp32 per 128x128 block, e4m3 act + fp32 per 1x128"}[wl]},
         "roofline": roof,
         "sweep": sweep,
     }

@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 from . import (DESC_W4A16_ASYM, DESC_W4A16_MXFP4, DESC_W4A16_SYM, DESC_W4A4_MXFP4, DESC_W4A8_MXFP4,
-               DESC_W4A8_MXFP8, DESC_W8A8,
+               DESC_W4A8_MXFP8, DESC_W8A8, DESC_W8A8_FP8_BLOCK,
                HQError, hq_gemm, hq_gemm_plan, hq_gemm_workspace_bytes, hq_kernel_config_count,
                hq_load_tuning_table, hq_prepack_weights, hq_prepacked_bytes)
 
@@ -41,6 +41,7 @@ FORMATS = {
     "w4a4": (DESC_W4A4_MXFP4, "w4a4", 0),
     "w4a8mx": (DESC_W4A8_MXFP8, "w4a8mx", 0),
     "w4a16mx": (DESC_W4A16_MXFP4, "mxw4a16", 0),
+    "fp8block": (DESC_W8A8_FP8_BLOCK, "fp8b", 0),
 }
 INF_M = 1 << 40
 
@@ -56,6 +57,9 @@ def _weights(fmt: str, N: int, K: int, g: np.random.Generator):
     if fmt == "w8a8":
         return (g.integers(-127, 128, (N, K)).astype(np.int8),
                 (0.001 * (1 + g.random(N))).astype(np.float32), None)
+    if fmt == "fp8block":
+        return (g.integers(0, 0x78, (N, K)).astype(np.uint8),
+                (0.001 * (1 + g.random((N // 128, K // 128)))).astype(np.float32), None)
     return (g.integers(0, 256, (N, K // 2), dtype=np.uint8),
             g.integers(118, 124, (N, K // 32)).astype(np.uint8), None)
 
@@ -69,6 +73,8 @@ def _activations(fmt: str, M: int, K: int, g: np.random.Generator):
         return g.integers(-127, 128, (M, K)).astype(np.int8).view(np.uint8), (0.01 * (1 + g.random(M))).astype(np.float32)
     if fmt == "w4a8":
         return g.integers(0, 0x78, (M, K)).astype(np.uint8), (0.01 * (1 + g.random(M))).astype(np.float32)
+    if fmt == "fp8block":
+        return g.integers(0, 0x78, (M, K)).astype(np.uint8), (0.01 * (1 + g.random((M, K // 128)))).astype(np.float32)
     if fmt == "w4a4":
         return (g.integers(0, 256, (M, K // 2), dtype=np.uint8),
                 g.integers(124, 130, (M, K // 32)).astype(np.uint8).reshape(-1))

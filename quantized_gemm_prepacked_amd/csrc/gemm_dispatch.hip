@@ -45,13 +45,14 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   }
   if (rows <= 32) {
     if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
-    if (c.fam == FAM_FP8B) return first_fit({16, 8});
+    if (c.fam == FAM_FP8B) return first_fit({29, 15, 8});
     if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({16, 8});
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
   if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
   if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
+  if (c.fam == FAM_FP8B && rows <= 64) return first_fit({29, 15, 8});   // M=64: 31.9 us vs 40.6
   return first_fit({4, 5, 6});
 }
 
@@ -137,8 +138,9 @@ constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {k
 constexpr RangeEntry kW4a4Table[] = {{768, 0, 0}, {4096, 3, 2}, {kInf, 3, 0}};
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
 constexpr RangeEntry kMxW4a16Table[] = {{64, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
-// Block-scaled FP8 W8A8: skinny and ping-pong only (first guess, W4A8's crossover)
-constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {2048, 3, 2}, {kInf, 3, 0}};
+// Block-scaled FP8 W8A8: skinny and ping-pong only (measured at N=K=8192: skinny to M=64, 64 x 256
+// ping-pong tiles at M=512 (98 vs 105 us), 256 x 128 at M=4096 (542 vs 559 us for 128 x 256))
+constexpr RangeEntry kFp8bTable[] = {{64, 0, 0}, {1024, 3, 4}, {kInf, 3, 1}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
