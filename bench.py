@@ -51,31 +51,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha() -> str:
-    """sha256 over the HIP/C++ sources of the library (file names and contents, sorted)."""
+def kernel_sources_sha(files=None) -> str:
+    """sha256 over HIP/C++ sources of the library (file names and contents, sorted): the files
+    named (those the measured kernel is built from), or every source."""
     import hashlib
     d = os.path.join(ROOT, "quantized_gemm_prepacked_amd", "csrc")
+    names = sorted(files) if files else sorted(f for f in os.listdir(d) if f.endswith((".hip", ".h", ".cpp")))
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+    for f in names:
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, point: str):
+def measured_traffic(workload: str, point: str, plan=None):
     """HBM bytes per launch of the dominant kernel from the FETCH_SIZE / WRITE_SIZE counter passes
     recorded in profiles/traffic_<workload>.json (each counter scaled by what it reads for a copy of
-    known size). None when there is no record for this point or the kernel sources have changed
-    since the counters were taken."""
+    known size). None when there is no record for this point, when the sources the kernel is built
+    from (the record's kernel_files) have changed since the counters were taken, or when the
+    library would now run another configuration there (plan, for dense calls)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
         with open(path) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("point") != point or rec.get("kernel_sources_sha256") != kernel_sources_sha():
+    if rec.get("point") != point or rec.get("kernel_sources_sha256") != kernel_sources_sha(rec.get("kernel_files")):
+        return None
+    if plan is not None and rec.get("plan") is not None and list(plan) != list(rec["plan"]):
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -326,7 +330,7 @@ def run_dense(args, wl: str):
     else:
         roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = measured_traffic(wl, f"M={dom['M']}")
+    roof["traffic"] = measured_traffic(wl, f"M={dom['M']}", plan=hq.hq_gemm_plan(desc, dom["M"], N, K))
     roof["kernel"] = f"M={dom['M']}"
     line = {
         "metric": METRIC, "value": round(tot_flops / tot_s / 1e12, 4), "unit": "TFLOP/s",

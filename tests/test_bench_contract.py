@@ -29,8 +29,19 @@ def test_traffic_records_are_well_formed():
 
 def test_traffic_is_dropped_when_sources_change(monkeypatch):
     rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_w4a16.json")))
-    monkeypatch.setattr(bench, "kernel_sources_sha", lambda: rec["kernel_sources_sha256"])
+    monkeypatch.setattr(bench, "kernel_sources_sha", lambda files=None: rec["kernel_sources_sha256"])
     assert bench.measured_traffic("w4a16", rec["point"]) == rec["hbm_bytes_per_launch"]
     assert bench.measured_traffic("w4a16", "M=0") is None
-    monkeypatch.setattr(bench, "kernel_sources_sha", lambda: "0" * 64)
+    if rec.get("plan") is not None:      # another configuration at that point: dropped too
+        other = [rec["plan"][0], rec["plan"][1] + 1, rec["plan"][2]]
+        assert bench.measured_traffic("w4a16", rec["point"], plan=other) is None
+        assert bench.measured_traffic("w4a16", rec["point"], plan=rec["plan"]) == rec["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_sources_sha", lambda files=None: "0" * 64)
     assert bench.measured_traffic("w4a16", rec["point"]) is None
+
+
+def test_kernel_sources_sha_covers_the_named_files_only(tmp_path):
+    full = bench.kernel_sources_sha()
+    part = bench.kernel_sources_sha(["gemm_pingpong.hip", "device_ops.h"])
+    assert len(full) == len(part) == 64 and full != part
+    assert part == bench.kernel_sources_sha(["device_ops.h", "gemm_pingpong.hip"])   # order-free
