@@ -17,14 +17,14 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_records_are_well_formed():
-    for wl in ("w4a16", "w8a8", "w4a8", "moe"):
+    for wl in ("w4a16", "w8a8", "w4a8", "w4a4", "w4a16mx", "fp8block", "moe", "moe_mx", "moe_layer"):
         path = os.path.join(ROOT, "profiles", f"traffic_{wl}.json")
         rec = json.load(open(path))
         cal = rec["copy_calibration"]
         fetch = rec["fetch_size_kib_per_dispatch"] * 1024 * cal["fetch_factor"]
         write = rec["write_size_kib_per_dispatch"] * 1024 * cal["write_factor"]
         assert abs(fetch + write - rec["hbm_bytes_per_launch"]) <= 1e-4 * rec["hbm_bytes_per_launch"]
-        assert len(rec["kernel_sources_sha256"]) == 64
+        assert len(rec["kernel_sources_sha256"]) == 64 and rec["kernel_files"]
 
 
 def test_traffic_is_dropped_when_sources_change(monkeypatch):
