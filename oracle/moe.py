@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import decode_bf16, round_to_bf16
+from .codecs import decode_bf16, decode_e4m3, decode_int8, round_to_bf16
 from .gemm import dequant_mxfp4, dequant_wna16
 
 
@@ -111,6 +111,43 @@ def ref_grouped_gemm(x_bf16: np.ndarray, expert_offsets: np.ndarray, expert_weig
         w = _dequant_expert(expert_weights(e), g, cols)
         y[lo:hi] = x[lo:hi] @ w.T
     valid = ~np.isnan(y[:, 0]) if n_cols else np.ones(R, dtype=bool)
+    bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
+    return y, bits, valid
+
+
+def ref_moe_gemm_q(xq: np.ndarray, s_tok: np.ndarray, topk_ids: np.ndarray, expert_weights, N: int, E: int,
+                   act: str, topk_weights: np.ndarray | None = None, rows=None, cols=None):
+    """Grouped GEMM with 8-bit per-token activations: act "e4m3" (W4A8: MXFP4 experts) or "int8"
+    (W8A8: int8 experts with an fp32 scale per channel, expert dict {"wq", "s_ch"}).
+    Y[t*topk + j, :] = s_tok[t] * (X_q[t, :] . W_e^T) (* s_ch for INT8) (* topk_weights[t, j]),
+    exact in float64 (the INT8 sum is an exact integer). Returns (y float64 [R, N'], y bf16 bits,
+    valid) like ref_moe_gemm."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, topk = ids.shape
+    flat = np.arange(T * topk) if rows is None else np.asarray(rows, dtype=np.int64)
+    x = decode_e4m3(xq) if act == "e4m3" else decode_int8(xq)
+    st = np.asarray(s_tok, dtype=np.float32).astype(np.float64)
+    n_cols = N if cols is None else len(cols)
+    cidx = np.arange(N) if cols is None else np.asarray(cols)
+    y = np.full((flat.size, n_cols), np.nan, dtype=np.float64)
+    experts = ids.reshape(-1)[flat]
+    for e in np.unique(experts):
+        if e < 0 or e >= E:
+            continue
+        sel = np.flatnonzero(experts == e)
+        wd = expert_weights(int(e))
+        tok = flat[sel] // topk
+        if act == "e4m3":
+            w = dequant_mxfp4(wd["wq"], wd["scales"], cols)
+            y[sel] = (x[tok] @ w.T) * st[tok][:, None]
+        else:
+            w = decode_int8(np.asarray(wd["wq"])[cidx]).astype(np.float64)
+            sc = np.asarray(wd["s_ch"], dtype=np.float32).astype(np.float64)[cidx]
+            y[sel] = (x[tok] @ w.T) * st[tok][:, None] * sc[None, :]
+    if topk_weights is not None:
+        tw = np.asarray(topk_weights, dtype=np.float32).astype(np.float64).reshape(-1)[flat]
+        y = y * tw[:, None]
+    valid = ~np.isnan(y[:, 0]) if n_cols else np.ones(flat.size, dtype=bool)
     bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
     return y, bits, valid
 

@@ -287,6 +287,13 @@ def make_w8a8_fp8_block(config_id: int, M: int, N: int, K: int):
     return {"xq": xq, "xs": xs, "wq": wq, "ws": ws}
 
 
+def make_moe_weights_expert_w8a8(config_id: int, e: int, N: int, K: int):
+    """One expert's INT8 weights with an fp32 scale per channel, from its own stream [config, 2, e]."""
+    w = rng(config_id, 2, e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    q, s = quantize_int8_rows(w)
+    return {"wq": q, "s_ch": s}
+
+
 def make_w4a4_activations(config_id: int, M: int, K: int):
     """MXFP4 activations (e2m1 codes + e8m0 per 32 k) quantized from bf16 N(0,1) by the OCP MX
     rule (the same quantizer as the weights')."""

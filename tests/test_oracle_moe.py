@@ -113,3 +113,32 @@ def test_grouped_gemm_brute_force_and_gaps():
     yd, _ = oracle.ref_wna16(x, ws[0]["wq"], ws[0]["scales"], None, 128)
     y1, _, _ = oracle.ref_grouped_gemm(x, np.array([0, R]), lambda e: ws[0], N, 1, 128)
     assert np.array_equal(y1, yd)
+
+
+def test_quantized_moe_gemm_equals_per_token_dense():
+    """8-bit activations: W4A8 (MXFP4 experts, e4m3 tokens) and W8A8 (INT8 experts, int8 tokens)
+    grouped GEMMs equal the per-token dense oracles, times the router weight."""
+    T, topk, E, N, K = 4, 2, 3, 16, 256
+    ids = np.array([[0, 2], [1, 0], [2, 2], [1, -1]], np.int32)
+    tw = np.random.default_rng(5).random((T, topk)).astype(np.float32)
+    a8 = synth.make_w4a8_activations(961, T, K)
+    ws = {e: synth.make_moe_weights_expert_mx(961, e, N, K) for e in range(E)}
+    y, _, valid = oracle.ref_moe_gemm_q(a8["xq"], a8["s_tok"], ids, lambda e: ws[e], N, E, "e4m3", topk_weights=tw)
+    assert valid.tolist() == [True] * 7 + [False]
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            if e < 0:
+                continue
+            yd, _ = oracle.ref_w4a8(a8["xq"][t:t + 1], a8["s_tok"][t:t + 1], ws[e]["wq"], ws[e]["scales"])
+            assert np.array_equal(y[t * topk + j], yd[0] * float(tw[t, j]))
+    a1 = synth.make_w8a8_activations(962, T, K)
+    wi = {e: synth.make_moe_weights_expert_w8a8(962, e, N, K) for e in range(E)}
+    y, _, _ = oracle.ref_moe_gemm_q(a1["xq"], a1["s_tok"], ids, lambda e: wi[e], N, E, "int8")
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            if e < 0:
+                continue
+            _, yd, _ = oracle.ref_w8a8(a1["xq"][t:t + 1], a1["s_tok"][t:t + 1], wi[e]["wq"], wi[e]["s_ch"])
+            assert np.array_equal(y[t * topk + j], yd[0])
