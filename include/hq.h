@@ -115,7 +115,8 @@ typedef struct {
  *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_BF16   (W4A16)    -> OUT_BF16
  *   FP8_E4M3   + FP32 scale, 128 x 128 blocks         + ACT_FP8E4M3_BLOCK128  -> OUT_BF16
  *              (N % 128 == 0, K % 128 == 0)
- * MoE grouped GEMM and grouped GEMM: the combinations with ACT_BF16 (INT4 sym / asym, FP4).
+ * MoE grouped GEMM and grouped GEMM: the combinations with ACT_BF16 (INT4 sym / asym, FP4), and
+ * those with per-token activations (INT8 W8A8 with OUT_BF16, FP4 + ACT_FP8E4M3_PER_TOKEN W4A8).
  * Every combination also takes compute_flags = HQ_COMPUTE_BATCH_INVARIANT.
  */
 
@@ -228,11 +229,14 @@ int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32
                        int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------------------------
- * MoE grouped GEMM (device), bf16 activations: INT4 group weights (WNA16) or MXFP4 weights:
+ * MoE grouped GEMM (device): bf16 activations with INT4 group weights (WNA16) or MXFP4 weights,
+ * or per-token 8-bit activations with INT8 (W8A8) or MXFP4 (W4A8) weights:
  *   y[f, :] = (topk_weights ? topk_weights[f] : 1) * a[f / topk, :] . dequant(W_{e(f)})^T
- * for every flat index f = t*topk + j that hq_moe_align routed to a valid expert e(f). Rows of
- * y for unrouted f are not written.
- *   a             bf16 [T, K] row-major (device);  a_scale must be NULL
+ * for every flat index f = t*topk + j that hq_moe_align routed to a valid expert e(f), with the
+ * dense path's epilogue per format (W8A8: bf16(float(acc) * a_scale[t] * s_ch_e[n] * weight),
+ * W4A8: bf16(acc * a_scale[t] * weight)). Rows of y for unrouted f are not written.
+ *   a             [T, K] row-major (device): bf16, or int8 / e4m3 codes
+ *   a_scale       fp32 [T] per-token scales for INT8 / FP8 activations (required), NULL for bf16
  *   w_packed      prepacked weights of all E experts (hq_prepack_weights with E experts)
  *   sorted_ids, block_expert, num_padded: outputs of hq_moe_align with the same T, topk, E,
  *                 block_m (device)
@@ -250,10 +254,12 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
                               void* ws, size_t ws_bytes, hq_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Grouped GEMM (device), WNA16 only: the "Grouped" MoE path of the announcement's section
+ * Grouped GEMM (device), the formats of hq_moe_grouped_gemm: the "Grouped" MoE path of the announcement's section
  * "Results: kernel microbenchmarks", for activations that arrive already grouped by expert.
  *   y[r, :] = a[r, :] . dequant(W_e)^T   for r in [expert_offsets[e], expert_offsets[e+1])
- *   a               bf16 [R, K] row-major (device); a_scale must be NULL
+ *             (times a_scale[r], and W8A8's channel scale, for 8-bit activations)
+ *   a               [R, K] row-major (device), bf16 or int8 / e4m3 codes
+ *   a_scale         fp32 [R] per-row scales for INT8 / FP8 activations (required), NULL for bf16
  *   w_packed        prepacked weights of all E experts (hq_prepack_weights with E experts)
  *   expert_offsets  int32 [E + 1] (device): non-decreasing, 0 <= offsets[0], offsets[E] <= R.
  *                   Each range is clipped to [0, R); rows in no range are not written. Offsets

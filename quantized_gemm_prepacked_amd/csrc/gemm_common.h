@@ -46,8 +46,9 @@ struct AccType<FAM_W8A8> {
 };
 
 // Final value of output (orow, n): `v` is the full K sum; srow indexes the per-token scale.
+// w: the weights of the expert (MoE) or the layer, for W8A8's per-channel scales.
 template <int FAM>
-__device__ __forceinline__ void epilogue(const KParams& p, int orow, int srow, int n,
+__device__ __forceinline__ void epilogue(const KParams& p, const uint8_t* w, int orow, int srow, int n,
                                          typename AccType<FAM>::elem v, float tw) {
   const size_t o = size_t(orow) * p.N + n;
   if constexpr (FAM == FAM_WNA16) {
@@ -56,8 +57,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, int orow, int srow, i
     if (p.out_i32) {
       reinterpret_cast<int*>(p.y)[o] = v;
     } else {
-      const float sch = reinterpret_cast<const float*>(p.w + p.scales_off)[n];
-      reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(float(v) * p.a_scale[srow] * sch);
+      const float sch = reinterpret_cast<const float*>(w + p.scales_off)[n];
+      reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(float(v) * p.a_scale[srow] * sch * tw);
     }
   } else if constexpr (FAM == FAM_W4A8) {
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * p.a_scale[srow] * tw);
@@ -68,13 +69,13 @@ __device__ __forceinline__ void epilogue(const KParams& p, int orow, int srow, i
 
 // Row `row` of the workgroup's row space (dense: m; MoE: position in sorted_ids).
 template <int FAM, bool MOE>
-__device__ __forceinline__ void store_result(const KParams& p, int row, int n,
+__device__ __forceinline__ void store_result(const KParams& p, const uint8_t* w, int row, int n,
                                              typename AccType<FAM>::elem v, int z) {
   if constexpr (MOE) {
     const int id = p.sorted_ids[row];
     if (id >= p.M) return;
     const float tw = p.topk_weights ? p.topk_weights[id] : 1.0f;
-    epilogue<FAM>(p, id, id / p.topk, n, v, tw);
+    epilogue<FAM>(p, w, id, id / p.topk, n, v, tw);
   } else {
     if (row >= p.M) return;
     if (p.split > 1) {
@@ -82,7 +83,7 @@ __device__ __forceinline__ void store_result(const KParams& p, int row, int n,
       reinterpret_cast<E*>(p.ws)[(size_t(z) * p.M + row) * p.N + n] = v;
       return;
     }
-    epilogue<FAM>(p, row, row, n, v, 1.0f);
+    epilogue<FAM>(p, w, row, row, n, v, 1.0f);
   }
 }
 

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(KParams p) {
   for (int z = 1; z < p.split; ++z) s += ws[size_t(z) * total + idx];
   const int m = int(idx / p.N);
   const int n = int(idx % p.N);
-  epilogue<FAM>(p, m, m, n, s, 1.0f);
+  epilogue<FAM>(p, p.w, m, m, n, s, 1.0f);
 }
 
 }  // namespace
@@ -373,7 +373,9 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
   // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
   const bool a32 = uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);   // 32-bit row offsets
-  if ((c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+  const bool pp_fam = c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16 || c.fam == FAM_W8A8 || c.fam == FAM_W4A8;
+  if (pp_fam && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+    // (the 8-bit-activation formats' 32-row tiles do not split into whole-wave copies: skinny)
     static const int pp32[1] = {7}, pp64[2] = {5, 4};
     const int* cands = block_m == 32 ? pp32 : pp64;
     const int n_c = block_m == 32 ? 1 : 2;
@@ -381,7 +383,8 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
     const PPCfg* pc = pp_configs(&n_p);
     for (int j = 0; j < n_c; ++j) {
       const PPCfg& t = pc[cands[j]];
-      if (N % (16 * t.ntw * t.wn) == 0 && pp_lds_bytes(c.fam, cands[j]) <= 160 * 1024) {
+      if (N % (16 * t.ntw * t.wn) == 0 && pp_lds_bytes(c.fam, cands[j]) <= 160 * 1024 &&
+          16 * t.mw * t.wm == block_m) {
         pl.kind = 3;
         pl.cfg = cands[j];
         pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(T, K) : 0;  // WNA16 offset term

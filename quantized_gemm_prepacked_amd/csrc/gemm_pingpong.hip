@@ -408,7 +408,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 
   const int row_base = row0 + wm * 16 * MW;
   if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
-  store_tile<FAM, MOE, MW, NTW>(p, acc, row_base, nt0, lane);
+  store_tile<FAM, MOE, MW, NTW>(p, w, acc, row_base, nt0, lane);
 }
 
 // Group sums of bf16 activation rows over 128-k groups, split into bf16 high and low halves:
@@ -484,7 +484,9 @@ template <int FAM, bool MOE, int I>
 static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PPCfg C = kPP[I];
   using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn>;
-  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || FAM == FAM_WNA16 || FAM == FAM_MXW4A16)) {
+  // MoE instantiations: the formats whose activation scales are per token (or absent)
+  constexpr bool kMoeFam = FAM == FAM_WNA16 || FAM == FAM_MXW4A16 || FAM == FAM_W8A8 || FAM == FAM_W4A8;
+  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || kMoeFam)) {
     auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
@@ -511,6 +513,8 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   if (moe) {
     if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_W4A8) return launch_pp_fam<FAM_W4A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     return hipErrorInvalidValue;
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
 
   const int row_base = row0 + wm * 16 * MW;
   if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
-  store_tile<FAM, MOE, MW, NTW>(p, acc, row_base, nt0, lane);
+  store_tile<FAM, MOE, MW, NTW>(p, w, acc, row_base, nt0, lane);
 }
 
 }  // namespace

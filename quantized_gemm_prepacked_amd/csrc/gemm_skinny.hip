@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     for (int ww = 1; ww < NW; ++ww) sum += red[ww][q][le];
     const int ib = 16 * mb + 4 * (le >> 4) + j;
     const int n = (nt0 + t) * 16 + (le & 15);
-    store_result<FAM, MOE>(p, row0 + ib, n, sum, blockIdx.z);
+    store_result<FAM, MOE>(p, w, row0 + ib, n, sum, blockIdx.z);
   }
 }
 
@@ -491,6 +491,8 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
                                    : launch_skinny_fam<FAM_WNA16, false>(p, cfg, grid, s);
   if (fam == FAM_MXW4A16) return moe ? launch_skinny_fam<FAM_MXW4A16, true>(p, cfg, grid, s)
                                      : launch_skinny_fam<FAM_MXW4A16, false>(p, cfg, grid, s);
+  if (moe && fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, true>(p, cfg, grid, s);
+  if (moe && fam == FAM_W4A8) return launch_skinny_fam<FAM_W4A8, true>(p, cfg, grid, s);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);

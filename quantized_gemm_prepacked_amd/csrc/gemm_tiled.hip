@@ -234,7 +234,7 @@ void tiled_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
 
   const int row_base = row0 + wm * 16 * MW;
   if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
-  store_tile<FAM, MOE, MW, NTW>(p, acc, row_base, nt0, lane);
+  store_tile<FAM, MOE, MW, NTW>(p, w, acc, row_base, nt0, lane);
 }
 
 }  // namespace

@@ -308,13 +308,16 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16)
-    return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM supports bf16 activations (INT4 or MXFP4 weights) only");
+  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16 && c.fam != hq::FAM_W8A8 && c.fam != hq::FAM_W4A8)
+    return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM: bf16 activations (INT4 or MXFP4 weights) or per-token "
+                                    "INT8 / FP8 activations (INT8 or MXFP4 weights)");
+  const bool per_token = c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8;
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (R < 0 || R > kMaxDim || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld E=%d out of range", (long long)R, E);
   if (R * N >= (int64_t(1) << 31)) return fail(HQ_ERR_UNSUPPORTED, "R*N must stay below 2^31");
-  if (a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
+  if (per_token && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale [R] is required for INT8/FP8 activations");
+  if (!per_token && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (!a || !w_packed || !expert_offsets || !y)
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, expert_offsets and y must be non-NULL");
   if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
@@ -331,7 +334,7 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
                                               static_cast<hipStream_t>(stream)),
                      "hq_grouped_gemm row index launch")) != HQ_OK)
     return s;
-  return hq_moe_grouped_gemm(desc, R, 1, E, N, K, a, nullptr, w_packed, sorted, bexp, npad, g.bm, nullptr, y,
+  return hq_moe_grouped_gemm(desc, R, 1, E, N, K, a, a_scale, w_packed, sorted, bexp, npad, g.bm, nullptr, y,
                              g.gemm_bytes ? base + g.gemm_off : nullptr, g.gemm_bytes, stream);
 }
 
@@ -385,8 +388,11 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16)
-    return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM supports bf16 activations (INT4 or MXFP4 weights) only");
+  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16 && c.fam != hq::FAM_W8A8 && c.fam != hq::FAM_W4A8)
+    return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM: bf16 activations (INT4 or MXFP4 weights) or per-token "
+                                    "INT8 / FP8 activations (INT8 or MXFP4 weights)");
+  if (c.out_i32) return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM writes bf16 only");
+  const bool per_token = c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8;
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (T < 0 || topk <= 0 || topk > 64 || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld topk=%d E=%d out of range", (long long)T, topk, E);
@@ -396,7 +402,8 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
     return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: supported values are 16, 32, 64", block_m);
   if (c.invariant && block_m != 32)
     return fail(HQ_ERR_INVALID_ARGUMENT, "block_m=%d: batch-invariant MoE calls use block_m 32", block_m);
-  if (a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
+  if (per_token && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale [T] is required for INT8/FP8 activations");
+  if (!per_token && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (!a || !w_packed || !sorted_ids || !block_expert || !num_padded || !y)
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, sorted_ids, block_expert, num_padded and y must be non-NULL");
   if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
@@ -413,6 +420,7 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
   call.N = N;
   call.K = K;
   call.a = a;
+  call.a_scale = a_scale;
   call.w = static_cast<const uint8_t*>(w_packed);
   call.y = y;
   call.ws = ws;

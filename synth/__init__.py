@@ -317,6 +317,22 @@ def random_int4_sym_expert(g: np.random.Generator, N: int, K: int, gs: int = 128
     return {"wq": wq, "scales": bf16_bits(s)}
 
 
+def random_int8_expert(g: np.random.Generator, N: int, K: int):
+    """INT8 weights with uniformly random codes in [-127, 127] and fp32 channel scales near
+    absmax/127 of N(0, 0.02) rows (for throughput runs over hundreds of experts)."""
+    wq = g.integers(-127, 128, (N, K), dtype=np.int8)
+    s = (7e-4 * (1.0 + 0.1 * g.standard_normal(N))).astype(np.float32)
+    return {"wq": wq, "s_ch": s}
+
+
+def random_mxfp4_expert(g: np.random.Generator, N: int, K: int):
+    """MXFP4 weights with uniformly random e2m1 codes and e8m0 exponents 2^-9 .. 2^-6 (the range
+    N(0, 0.02) blocks quantize to), for throughput runs over hundreds of experts."""
+    wq = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = g.integers(118, 122, (N, K // 32), dtype=np.uint8)
+    return {"wq": wq, "scales": scales}
+
+
 def make_moe_weights_expert(config_id: int, e: int, N: int, K: int, g: int = 128):
     """One expert's symmetric INT4 group-g weights, drawn from its own stream [config, 0, e]."""
     w = rng(config_id, 0, e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)

@@ -89,10 +89,18 @@ def test_moe_rejections():
         hq.hq_moe_align(16, 4, 8, 1000, 16, 16, 16, 16, 16, stream=0)       # E > 512
     with pytest.raises(hq.HQError):
         hq.hq_moe_align(16, 4, 8, 256, 16, 0, 16, 16, 16, stream=0)         # null output
-    with pytest.raises(hq.HQError) as ei:
-        hq.hq_moe_grouped_gemm(hq.DESC_W8A8, 4, 8, 256, 256, 512, 16, 64, 16, 16, 16, 16, 16,
+    with pytest.raises(hq.HQError) as ei:      # activations with block scales: no MoE path
+        hq.hq_moe_grouped_gemm(hq.DESC_W4A4_MXFP4, 4, 8, 256, 256, 512, 16, 64, 16, 16, 16, 16, 16,
                                None, 16, stream=0)
     assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
+    with pytest.raises(hq.HQError) as ei:      # int32 accumulators are a dense-only output
+        hq.hq_moe_grouped_gemm(hq.DESC_W8A8_I32, 4, 8, 256, 256, 512, 16, 64, 16, 16, 16, 16, 16,
+                               None, 16, stream=0)
+    assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
+    for dq in (hq.DESC_W8A8, hq.DESC_W4A8_MXFP4):   # per-token activations need their scales
+        with pytest.raises(hq.HQError) as ei:
+            hq.hq_moe_grouped_gemm(dq, 4, 8, 256, 256, 512, 16, None, 16, 16, 16, 16, 16, None, 16, stream=0)
+        assert ei.value.status == hq.HQ_ERR_INVALID_ARGUMENT
     with pytest.raises(hq.HQError) as ei:
         hq.hq_moe_grouped_gemm(d, 4, 8, 256, 256, 512, 16, None, 16, 16, 16, 16, 48, None, 16, stream=0)
     assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
@@ -120,12 +128,15 @@ def test_prepack_rejections():
 
 
 def test_grouped_gemm_host_validation():
-    """Refused on the host before any launch: non-WNA16 formats, E out of range, a_scale given."""
+    """Refused on the host before any launch: block-scaled activations, E out of range, a_scale
+    given for bf16 activations or missing for per-token ones."""
     d = hq.DESC_W4A16_SYM
     assert hq.hq_grouped_gemm_workspace_bytes(d, 4096, 256, 4096, 7168) > 4096 * 4
     assert hq.hq_grouped_gemm_workspace_bytes(d, 16, 0, 256, 256) == 0
     with pytest.raises(hq.HQError):
-        hq.hq_grouped_gemm(hq.DESC_W8A8, 4, 2, 256, 512, 16, 16, 16, 16, 16, 16, 1 << 20, stream=0)
+        hq.hq_grouped_gemm(hq.DESC_W4A4_MXFP4, 4, 2, 256, 512, 16, 16, 16, 16, 16, 16, 1 << 20, stream=0)
+    with pytest.raises(hq.HQError):
+        hq.hq_grouped_gemm(hq.DESC_W8A8, 4, 2, 256, 512, 16, None, 16, 16, 16, 16, 1 << 20, stream=0)
     with pytest.raises(hq.HQError):
         hq.hq_grouped_gemm(d, 4, 600, 256, 512, 16, None, 16, 16, 16, 16, 1 << 20, stream=0)
     with pytest.raises(hq.HQError):
