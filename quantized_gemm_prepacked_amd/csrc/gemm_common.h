@@ -114,10 +114,11 @@ int pipe_lds_bytes(int fam, int cfg);
 hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, int tiles_m,
                        int tiles_n, hipStream_t s);
 
-// A ping-pong-kernel instantiation: eight waves (WM x WN) of (16*MW) x (16*NTW), three K steps
-// in flight; the workgroup tile is (16*MW*WM) x (16*NTW*WN).
+// A ping-pong-kernel instantiation: eight waves (WM x WN) of (16*MW) x (16*NTW), `stages` LDS
+// slots (K steps resident or in flight); the workgroup tile is (16*MW*WM) x (16*NTW*WN).
 struct PPCfg {
   int mw, ntw, wm, wn;
+  int stages = 3;
 };
 const PPCfg* pp_configs(int* count);
 int pp_lds_bytes(int fam, int cfg);

@@ -129,18 +129,26 @@ struct RangeEntry {
 };
 constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
-constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 3}, {1024, 3, 1}, {kInf, 2, 8}};
+// (M in (256, 512]: ping-pong 128 x 128 with four LDS slots, 57.7 vs 61.3 us with three)
+constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
-// W4A4 (and W4A8 with MXFP8 activations, until measured on its own) run on the skinny and
-// ping-pong kernels only (W4A4 measured at N=4096, K=7168: skinny 64-row
-// blocks up to M=512 at 34 us vs 56 us on ping-pong 128x128, which wins from M=2048 on; 128x256
-// at M=8192)
-constexpr RangeEntry kW4a4Table[] = {{768, 0, 0}, {4096, 3, 2}, {kInf, 3, 0}};
+// W4A4 and W4A8 with MXFP8 activations run on the skinny and ping-pong kernels only. W4A4,
+// measured at N=4096, K=7168: skinny 64-row blocks to M=512 (34 vs 49 us), then ping-pong
+// 128 x 128 with four LDS slots (M=768 / 1024 / 2048 / 4096: 50.7 / 51.2 / 67.3 / 121.9 us,
+// against 66.9 skinny and 60.2 / 74.1 / 135.5 with three slots), 128 x 256 with three at M=8192
+// (187 us; four or five slots: 235 / 243).
+constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {4096, 3, 10}, {kInf, 3, 0}};
+// W4A8-MXFP8 at the same shape: skinny to M=512 (45.5 vs 50.9 us), ping-pong 64 x 256 with four
+// slots at M=768 / 1024 (52.6 / 52.9 us; 75.3 / 70.1 with the W4A4 choices), 128 x 256 with four
+// slots from M=2048 (M=2048 / 4096 / 8192: 74.9 / 136.9 / 256.0 us, against 84.8 / 154.4 / 364.8).
+constexpr RangeEntry kW4a8mxTable[] = {{576, 0, 0}, {1536, 3, 13}, {kInf, 3, 8}};
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
 constexpr RangeEntry kMxW4a16Table[] = {{64, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
-// Block-scaled FP8 W8A8: skinny and ping-pong only (measured at N=K=8192: skinny to M=64, 64 x 256
-// ping-pong tiles at M=512 (98 vs 105 us), 256 x 128 at M=4096 (542 vs 559 us for 128 x 256))
-constexpr RangeEntry kFp8bTable[] = {{64, 0, 0}, {1024, 3, 4}, {kInf, 3, 1}};
+// Block-scaled FP8 W8A8: skinny and ping-pong only (measured at N=K=8192: skinny to M=64, then
+// ping-pong 128 x 128 with four LDS slots: M=128 / 512 / 1024 / 2048 / 4096 at 66.3 / 75.4 / 138.0
+// / 272.9 / 517.0 us, against 91.7 / 101.6 / 194.0 / 304.2 / 610.4 for the three-slot 64 x 256 and
+// 256 x 128 tiles)
+constexpr RangeEntry kFp8bTable[] = {{64, 0, 0}, {kInf, 3, 10}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -173,9 +181,12 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_MXW4A16) {
     t = kMxW4a16Table;
     n = int(sizeof(kMxW4a16Table) / sizeof(kMxW4a16Table[0]));
-  } else if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) {
+  } else if (c.fam == FAM_W4A4) {
     t = kW4a4Table;
     n = int(sizeof(kW4a4Table) / sizeof(kW4a4Table[0]));
+  } else if (c.fam == FAM_W4A8MX) {
+    t = kW4a8mxTable;
+    n = int(sizeof(kW4a8mxTable) / sizeof(kW4a8mxTable[0]));
   } else {
     t = kW4a8Table;
     n = int(sizeof(kW4a8Table) / sizeof(kW4a8Table[0]));
@@ -192,7 +203,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
-    for (int cfg : {3, 2})   // 128 x 128 tiles
+    for (int cfg : {10, 3, 2})   // 128 x 128 tiles (four LDS slots where they fit)
       if (M > 256 && N % (16 * pc[cfg].ntw * pc[cfg].wn) == 0 && pp_lds_bytes(c.fam, cfg) <= 160 * 1024)
         return {kInf, 3, cfg};
     return {0, 0, 0};

@@ -5,14 +5,15 @@
 // "Tuning and JIT compilation per workload"), scheduled so the matrix cores never wait for the
 // memory work of their own SIMD:
 //   - the workgroup's eight waves form two groups of four, one wave of each group per SIMD;
-//   - every K step (128 k) a wave runs a memory phase (issue the direct-to-LDS copies of a step
-//     two ahead, read its operand fragments of this step from LDS into registers) and then a
+//   - every K step (128 k) a wave runs a memory phase (issue the direct-to-LDS copies of the step
+//     S - 1 ahead, read its operand fragments of this step from LDS into registers) and then a
 //     compute phase (dequantization, MFMAs and the group scaling, registers only);
 //   - group 1 runs one phase behind group 0, and a workgroup barrier separates the phases, so
 //     on each SIMD one wave computes while the other loads;
-//   - three LDS slots hold steps s (being read), s + 1 (landed or landing) and s + 2 (in
-//     flight); a wave waits only for its own copies of step s + 1 before the barrier that ends
-//     its memory phase of step s, so a copy has about three phases to land.
+//   - S LDS slots (S = 3..5, per configuration) hold steps s (being read), s + 1 (landed or
+//     landing) and s + 2 .. s + S - 1 (in flight); a wave waits only for its own copies of step
+//     s + 1 before the barrier that ends its memory phase of step s, so a copy has about
+//     2 S - 3 phases to land (more slots hide a longer HBM / L2 latency where the LDS allows).
 // WNA16 keeps the offset-128 operand of the other kernels; the offset term is removed at the end
 // (tile_epilogue.h).
 //
@@ -95,10 +96,11 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FAM, int MW, int NTW, int WM, int WN>
+template <int FAM, int MW, int NTW, int WM, int WN, int STAGES>
 struct PPShape {
   static_assert(WM * WN == 8, "eight waves");
-  static constexpr int kStages = 3;
+  static_assert(STAGES >= 3 && STAGES <= 5, "three to five LDS slots");
+  static constexpr int kStages = STAGES;
   static constexpr int BM = 16 * MW * WM;
   static constexpr int BN = 16 * NTW * WN;
   static constexpr int RB = PPTraits<FAM>::kRowBytes;  // activation bytes per row per step
@@ -119,15 +121,18 @@ struct PPShape {
   static constexpr int B_INSTR = NT * UPS / 8;
   static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0) + (ASC_BYTES ? 1 : 0);
   // the copies split evenly over the eight waves (shapes that do not are never launched)
+  // the copies split evenly over the eight waves (shapes that do not are never launched), and
+  // the copies of S - 2 steps in flight fit the 6-bit vmcnt
   static constexpr bool kValid = A_BYTES % (1024 * 8) == 0 && (NT * UPS) % 8 == 0 &&
                                  META_BYTES % (16 * 8) == 0 && META_LANES <= 64 &&
-                                 (ASC_BYTES == 0 || (BM % 8 == 0 && BM / 8 <= 64));
+                                 (ASC_BYTES == 0 || (BM % 8 == 0 && BM / 8 <= 64)) &&
+                                 (kStages - 2) * INSTR < 64;
   static constexpr int LDS_OR_NONE = kValid ? LDS : 1 << 30;
 };
 
-template <int FAM, bool MOE, int MW, int NTW, int WM, int WN>
+template <int FAM, bool MOE, int MW, int NTW, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
-  using Sh = PPShape<FAM, MW, NTW, WM, WN>;
+  using Sh = PPShape<FAM, MW, NTW, WM, WN, STAGES>;
   static_assert(Sh::kValid, "copies must split over the eight waves");
   using Acc = typename AccType<FAM>::type;
   constexpr int BM = Sh::BM, RB = Sh::RB, CPR = Sh::CPR, NT = Sh::NT, UPS = Sh::UPS;
@@ -385,20 +390,29 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   };
 
   const int nks = p.K / 128;
-  issue_stage(0);
-  if (nks > 1) issue_stage(1);
-  if (nks > 1) wait_vmcnt<Sh::INSTR>();
-  else wait_vmcnt<0>();
+  // Wait until this wave's copies of every step up to `step` have landed, given that the copies
+  // of the steps after it, up to min(step + S - 2, nks - 1), may still be in flight.
+  auto wait_step = [&](int step) __attribute__((always_inline)) {
+    const int after = min(S - 2, nks - 1 - step);
+    if (after >= 3) wait_vmcnt<(S >= 5 ? 3 : 0) * Sh::INSTR>();
+    else if (after == 2) wait_vmcnt<(S >= 4 ? 2 : 0) * Sh::INSTR>();
+    else if (after == 1) wait_vmcnt<Sh::INSTR>();
+    else wait_vmcnt<0>();
+  };
+
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < nks) issue_stage(j);
+  wait_step(0);
   phase_barrier();
   if (group == 1) phase_barrier();   // group 1 runs one phase behind
 
   for (int ks = 0; ks < nks; ++ks) {
-    // memory phase of step ks: the slot of step ks + 2 held step ks - 1, which both groups
+    // memory phase of step ks: the slot of step ks + S - 1 held step ks - 1, which both groups
     // finished reading before the barrier that opened this phase
-    if (ks + 2 < nks) issue_stage(ks + 2);
+    if (ks + S - 1 < nks) issue_stage(ks + S - 1);
     memory_phase(ks);
-    if (ks + 2 < nks) wait_vmcnt<Sh::INSTR>();   // own copies of step ks + 1 have landed
-    else wait_vmcnt<0>();
+    wait_step(ks + 1);   // own copies of step ks + 1 have landed
     wait_lgkm0();
     phase_barrier();
     compute_phase();
@@ -449,6 +463,13 @@ static constexpr PPCfg kPP[] = {
     {2, 8, 2, 4},  // 5: 64 x 512, waves of 32 x 128
     {1, 8, 2, 4},  // 6: 32 x 512, waves of 16 x 128 (MoE blocks of 32 rows)
     {1, 4, 2, 4},  // 7: 32 x 256, waves of 16 x 64
+    // deeper pipelines (more steps in flight) where the LDS allows
+    {4, 4, 2, 4, 4},  // 8: as 0, four slots (8- and 4-bit activations)
+    {4, 4, 2, 4, 5},  // 9: as 0, five slots (4-bit activations)
+    {2, 4, 4, 2, 4},  // 10: as 2, four slots
+    {4, 2, 2, 4, 4},  // 11: as 3, four slots
+    {4, 4, 4, 2, 4},  // 12: as 1, four slots
+    {2, 4, 2, 4, 4},  // 13: as 4, four slots
 };
 
 const PPCfg* pp_configs(int* count) {
@@ -458,7 +479,7 @@ const PPCfg* pp_configs(int* count) {
 
 template <int FAM, int I>
 constexpr int pp_lds_of() {
-  return PPShape<FAM, kPP[I].mw, kPP[I].ntw, kPP[I].wm, kPP[I].wn>::LDS_OR_NONE;
+  return PPShape<FAM, kPP[I].mw, kPP[I].ntw, kPP[I].wm, kPP[I].wn, kPP[I].stages>::LDS_OR_NONE;
 }
 
 template <int FAM, int... I>
@@ -483,11 +504,11 @@ int pp_lds_bytes(int fam, int cfg) {
 template <int FAM, bool MOE, int I>
 static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PPCfg C = kPP[I];
-  using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn>;
+  using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn, C.stages>;
   // MoE instantiations: the formats whose activation scales are per token (or absent)
   constexpr bool kMoeFam = FAM == FAM_WNA16 || FAM == FAM_MXW4A16 || FAM == FAM_W8A8 || FAM == FAM_W4A8;
   if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || kMoeFam)) {
-    auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn>;
+    auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn, C.stages>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     hipLaunchKernelGGL(kern, grid, dim3(512), Sh::LDS, s, p, tiles_m, tiles_n);

@@ -25,6 +25,8 @@ def _gemm(d, M, N, K):
     (300, 256, 640),     # ping-pong, ragged M, 5 K steps
     (1000, 384, 512),    # N not a multiple of 256
     (700, 512, 1024),
+    (200, 256, 128),     # ping-pong with four LDS slots, one K step
+    (150, 128, 256),     # two K steps
 ])
 def test_fp8block_small(M, N, K):
     say(f"[fp8block] M={M} N={N} K={K}")

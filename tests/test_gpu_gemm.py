@@ -91,7 +91,9 @@ def test_wna16_full_size_sampled(cfg2_weights, M):
 W8A8_SMALL = [(1, 256, 8192), (64, 512, 1024), (7, 272, 320), (16, 256, 64), (200, 512, 2048),
               (20, 512, 1024),     # two 16-row blocks per skinny workgroup
               (700, 384, 1024),    # 256 x 128 ping-pong tiles
-              (400, 256, 640),     # 128 x 128 ping-pong tiles
+              (400, 256, 640),     # 128 x 128 ping-pong tiles, four LDS slots
+              (300, 256, 128),     # four slots, one K step
+              (480, 384, 256),     # four slots, two K steps
               (1100, 512, 1024),   # 256 x 256 pipelined tiles, ragged M
               (2100, 640, 512),    # 256 x 256 tiles do not divide N: LDS-tiled fallback
               (2050, 512, 640)]    # 256 x 256 pipelined tiles, ragged M

@@ -24,8 +24,11 @@ def _gemm(d, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024),
-    (300, 256, 512),     # ping-pong 128 x 256 tiles, ragged M
-    (600, 384, 640),     # ping-pong 128 x 128 fallback, 5 K steps
+    (300, 256, 512),     # skinny, 64-row blocks, ragged M
+    (700, 384, 640),     # ping-pong 128 x 128, four LDS slots, 5 K steps
+    (1000, 256, 128),    # four slots, one K step
+    (900, 128, 256),     # four slots, two K steps
+    (4200, 256, 512),    # ping-pong 128 x 256, three slots, ragged M
     (257, 128, 256),
 ])
 def test_w4a4_small(M, N, K):

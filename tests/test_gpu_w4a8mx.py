@@ -21,7 +21,12 @@ def _gemm(d, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (64, 256, 512), (300, 256, 512), (1100, 384, 640),
+    (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (64, 256, 512), (300, 256, 512),
+    (1100, 384, 640),    # ping-pong 128 x 128 fallback (four LDS slots), 5 K steps
+    (700, 512, 640),     # ping-pong 64 x 256, four slots
+    (1600, 256, 1024),   # ping-pong 128 x 256, four slots, ragged M
+    (800, 256, 128),     # four slots, one K step
+    (2000, 256, 256),    # four slots, two K steps
 ])
 def test_w4a8mx_small(M, N, K):
     say(f"[w4a8mx] M={M} N={N} K={K}")
