@@ -30,6 +30,7 @@ from .codecs import (  # noqa: F401
 )
 from .gemm import (  # noqa: F401
     dequant_wna16, dequant_mxfp4, ref_wna16, ref_w8a8, ref_w4a8, ref_w4a4, ref_w4a8_mx, ref_w4a16_mx, ref_w8a8_fp8_block,
+    ref_w8a16,
 )
 from .moe import (  # noqa: F401
     ref_moe_align, ref_moe_gemm, ref_moe_gemm_q, ref_grouped_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer,

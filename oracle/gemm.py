@@ -144,3 +144,21 @@ def ref_w8a8_fp8_block(xq: np.ndarray, xs: np.ndarray, wq: np.ndarray, ws: np.nd
         part = x[:, 128 * g:128 * (g + 1)] @ w[:, 128 * g:128 * (g + 1)].T
         y += part * sa[:, g:g + 1] * sw[None, :, g]
     return y, round_to_bf16(y)
+
+
+def ref_w8a16(x_bf16: np.ndarray, wq: np.ndarray, s_ch: np.ndarray, fp8: bool = False,
+              rows=None, cols=None):
+    """8-bit weights with bf16 activations (the page's WnA16 at an 8-bit weight width, section
+    "Results: kernel microbenchmarks", WnA16 paragraph on integer and floating-point weights up
+    to FP8): symmetric INT8 codes (two's complement, [-127, 127]) or FP8 e4m3 codes, each with an
+    fp32 scale per output channel (scale granularity "per channel", section "A unified
+    quantization representation"):
+        w[n, k] = decode(wq[n, k]) * s_ch[n],        y = x . w^T
+    dequantized and multiplied in float64, rounded once to bf16. Returns (y float64, y bf16 bits)."""
+    x = decode_bf16(_sel(x_bf16, rows))
+    c = _sel(wq, cols)
+    q = decode_e4m3(c) if fp8 else decode_int8(c).astype(np.float64)
+    s = np.asarray(_sel(s_ch, cols), dtype=np.float32).astype(np.float64)
+    w = q * s[:, None]
+    y = x @ w.T
+    return y, round_to_bf16(y)

@@ -257,6 +257,14 @@ def make_w4a16mx(config_id: int, M: int, N: int, K: int):
     return {"x": normal_bf16(rng(config_id, M), (M, K)), **quantize_mxfp4(w)}
 
 
+def make_w8a16(config_id: int, M: int, N: int, K: int, fp8: bool = False):
+    """Dense 8-bit weights with bf16 activations: bf16 N(0,1) activations; weights N(0, 0.02)
+    quantized per output channel to symmetric INT8 (s = absmax/127) or FP8 e4m3 (s = absmax/448)."""
+    w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    wq, s_ch = quantize_fp8_rows(w) if fp8 else quantize_int8_rows(w)
+    return {"x": normal_bf16(rng(config_id, M), (M, K)), "wq": wq, "s_ch": s_ch}
+
+
 def make_moe_weights_expert_mx(config_id: int, e: int, N: int, K: int):
     """One expert's MXFP4 weights, drawn from its own stream [config, 1, e]."""
     w = rng(config_id, 1, e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
