@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | moe | moe_mx | moe_layer.
+--config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | moe | moe_mx | moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -44,6 +44,10 @@ WORKLOADS = {
                     dtype="bf16", peak="bf16"),
     "fp8block": dict(name="dense FP8 W8A8 with 128x128 / 1x128 block scales", N=8192, K=8192,
                      Ms=[1, 64, 512, 4096], cfg=3, dtype="fp8", peak="fp8"),
+    "w8a16": dict(name="dense W8A16 INT8 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
+                  dtype="bf16", peak="bf16"),
+    "f8a16": dict(name="dense W8A16 FP8 e4m3 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
+                  dtype="bf16", peak="bf16"),
 }
 
 
@@ -98,6 +102,8 @@ def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
         return N * K // 2 + N * (K // 32) + M * K * 2 + M * N * 2
     if wl == "fp8block":
         return N * K + (N // 128) * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
+    if wl in ("w8a16", "f8a16"):
+        return N * K + N * 4 + M * K * 2 + M * N * 2
     return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
 
 
@@ -128,6 +134,11 @@ def make_inputs(wl: str, spec: dict):
         for M in spec["Ms"]:
             a = synth.make_w8a8_fp8_block(cfg, M, 128, K)          # activations only (N unused)
             acts[M] = (a["xq"], a["xs"])
+    elif wl in ("w8a16", "f8a16"):
+        d = synth.make_w8a16(cfg, 1, N, K, fp8=wl == "f8a16")
+        desc = hq.DESC_W8A16_FP8 if wl == "f8a16" else hq.DESC_W8A16_INT8
+        std = (d["wq"], d["s_ch"], None)
+        acts = {M: (synth.normal_bf16(synth.rng(cfg, M), (M, K)), None) for M in spec["Ms"]}
     elif wl == "w4a16mx":
         d = synth.make_w4a16mx(cfg, 1, N, K)
         desc = hq.DESC_W4A16_MXFP4
@@ -181,6 +192,8 @@ def cpu_baseline(wl: str, spec: dict, std, acts):
             oracle.ref_w4a4(x, s, std[0], std[1], rows=rows)
         elif wl == "w4a16mx":
             oracle.ref_w4a16_mx(x, std[0], std[1], rows=rows)
+        elif wl in ("w8a16", "f8a16"):
+            oracle.ref_w8a16(x, std[0], std[1], fp8=wl == "f8a16", rows=rows)
         elif wl == "fp8block":
             oracle.ref_w8a8_fp8_block(x, s, std[0], std[1], rows=rows)
         else:

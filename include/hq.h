@@ -56,9 +56,10 @@ typedef enum {
 typedef enum {
   HQ_W_INT4_SYM = 0,   /* two's-complement INT4 in [-8, 7], packed 2 per byte, low nibble = even k */
   HQ_W_UINT4_ASYM = 1, /* unsigned INT4 in [0, 15] with a uint4 zero-point per (n, group)          */
-  HQ_W_INT8_SYM = 2,   /* two's-complement INT8 (codes in [-127, 127])                              */
+  HQ_W_INT8_SYM = 2,   /* two's-complement INT8 (codes in [-127, 127]), fp32 scale per channel      */
   HQ_W_FP4_E2M1 = 3,   /* OCP MX e2m1, packed 2 per byte, low nibble = even k                      */
-  HQ_W_FP8_E4M3 = 4    /* OCP e4m3 [N, K], one fp32 scale per 128 x 128 block (group_size 128)     */
+  HQ_W_FP8_E4M3 = 4    /* OCP e4m3 [N, K]: one fp32 scale per 128 x 128 block (group_size 128) or,
+                          with bf16 activations, per output channel (group_size 0)              */
 } hq_weight_fmt;
 
 typedef enum {
@@ -115,6 +116,9 @@ typedef struct {
  *   FP4_E2M1   + E8M0 scale, group 32                 + ACT_BF16   (W4A16)    -> OUT_BF16
  *   FP8_E4M3   + FP32 scale, 128 x 128 blocks         + ACT_FP8E4M3_BLOCK128  -> OUT_BF16
  *              (N % 128 == 0, K % 128 == 0)
+ *   INT8_SYM   + FP32 scale, group 0                  + ACT_BF16   (W8A16)    -> OUT_BF16
+ *   FP8_E4M3   + FP32 scale, group 0                  + ACT_BF16   (W8A16)    -> OUT_BF16
+ *              (the 8-bit WnA16 widths; K % 128 == 0)
  * MoE grouped GEMM and grouped GEMM: the combinations with ACT_BF16 (INT4 sym / asym, FP4), and
  * those with per-token activations (INT8 W8A8 with OUT_BF16, FP4 + ACT_FP8E4M3_PER_TOKEN W4A8).
  * Every combination also takes compute_flags = HQ_COMPUTE_BATCH_INVARIANT.
@@ -154,8 +158,9 @@ hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const v
  * Weight prepack (host).  Standard-format inputs, all host memory, row-major:
  *   wq      INT4/FP4: uint8 [E, N, K/2] (two codes per byte, low nibble = even k)
  *           INT8    : int8  [E, N, K];  FP8: e4m3 bytes [E, N, K]
- *   scales  BF16: uint16 bf16 bits [E, N, K/group];  FP32: float [E, N] (INT8) or
- *           float [E, N/128, K/128] (FP8 block scales);  E8M0: uint8 [E, N, K/32]
+ *   scales  BF16: uint16 bf16 bits [E, N, K/group];  FP32: float [E, N] (per channel: INT8,
+ *           and FP8 with group_size 0) or float [E, N/128, K/128] (FP8 block scales);
+ *           E8M0: uint8 [E, N, K/32]
  *   zeros   UINT4_ASYM only: uint8 [E, N, K/group], values 0..15; NULL otherwise
  * E = 1 for a dense layer, E = number of experts for MoE (experts stacked).
  * Output: `out` (host, `hq_prepacked_bytes` bytes) receives the weights rearranged into the
@@ -190,6 +195,10 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
  *             FP8 W8A8 with block scales (HQ_W_FP8_E4M3 + HQ_ACT_FP8E4M3_BLOCK128; a_scale =
  *                    fp32 [M, K/128]): bf16( sum_g a_scale[m, g] * s_w[n/128, g] *
  *                    sum_{k in g} e4m3(a) * e4m3(q) ) (fp32 accumulation)
+ *             INT8 or FP8 e4m3 weights with bf16 activations ("W8A16"; the page's WnA16 at an
+ *                    8-bit weight width, section "Results: kernel microbenchmarks"):
+ *                    bf16( s_ch[n] * sum_k a * q ), q the INT8 integer or the e4m3 value (each
+ *                    exact in bf16), fp32 accumulation
  *             W4A8 with MXFP8 activations (desc act_fmt HQ_ACT_MXFP8):
  *                    bf16( sum_k e4m3(a) 2^(ea - 127) * e2m1(q) 2^(e - 127) ) (fp32 accumulation)
  * All bf16 results use round-to-nearest-even. M = 0 is a no-op returning HQ_OK.

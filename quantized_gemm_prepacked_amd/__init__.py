@@ -80,6 +80,8 @@ DESC_W4A4_MXFP4 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_MXFP4)
 DESC_W4A8_MXFP8 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_MXFP8)
 DESC_W4A16_MXFP4 = make_desc(HQ_W_FP4_E2M1, 32, HQ_SCALE_E8M0, 0, HQ_ACT_BF16)
 DESC_W8A8_FP8_BLOCK = make_desc(HQ_W_FP8_E4M3, 128, HQ_SCALE_FP32, 0, HQ_ACT_FP8E4M3_BLOCK128)
+DESC_W8A16_INT8 = make_desc(HQ_W_INT8_SYM, 0, HQ_SCALE_FP32, 0, HQ_ACT_BF16)
+DESC_W8A16_FP8 = make_desc(HQ_W_FP8_E4M3, 0, HQ_SCALE_FP32, 0, HQ_ACT_BF16)
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

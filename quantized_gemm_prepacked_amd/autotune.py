@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 from . import (DESC_W4A16_ASYM, DESC_W4A16_MXFP4, DESC_W4A16_SYM, DESC_W4A4_MXFP4, DESC_W4A8_MXFP4,
-               DESC_W4A8_MXFP8, DESC_W8A8, DESC_W8A8_FP8_BLOCK,
+               DESC_W4A8_MXFP8, DESC_W8A8, DESC_W8A8_FP8_BLOCK, DESC_W8A16_FP8, DESC_W8A16_INT8,
                HQError, hq_gemm, hq_gemm_plan, hq_gemm_workspace_bytes, hq_kernel_config_count,
                hq_load_tuning_table, hq_prepack_weights, hq_prepacked_bytes)
 
@@ -42,6 +42,8 @@ FORMATS = {
     "w4a8mx": (DESC_W4A8_MXFP8, "w4a8mx", 0),
     "w4a16mx": (DESC_W4A16_MXFP4, "mxw4a16", 0),
     "fp8block": (DESC_W8A8_FP8_BLOCK, "fp8b", 0),
+    "w8a16": (DESC_W8A16_INT8, "w8a16", 0),
+    "f8a16": (DESC_W8A16_FP8, "f8a16", 0),
 }
 INF_M = 1 << 40
 
@@ -54,8 +56,11 @@ def _weights(fmt: str, N: int, K: int, g: np.random.Generator):
         scales = (s.view(np.uint32) >> 16).astype(np.uint16)
         zeros = g.integers(0, 16, (N, K // 128), dtype=np.uint8) if fmt == "w4a16a" else None
         return wq, scales, zeros
-    if fmt == "w8a8":
+    if fmt in ("w8a8", "w8a16"):
         return (g.integers(-127, 128, (N, K)).astype(np.int8),
+                (0.001 * (1 + g.random(N))).astype(np.float32), None)
+    if fmt == "f8a16":
+        return (g.integers(0, 0x78, (N, K)).astype(np.uint8) | (g.integers(0, 2, (N, K)).astype(np.uint8) << 7),
                 (0.001 * (1 + g.random(N))).astype(np.float32), None)
     if fmt == "fp8block":
         return (g.integers(0, 0x78, (N, K)).astype(np.uint8),
@@ -66,7 +71,7 @@ def _weights(fmt: str, N: int, K: int, g: np.random.Generator):
 
 def _activations(fmt: str, M: int, K: int, g: np.random.Generator):
     """(a bytes, a_scale) in the format's activation layout."""
-    if fmt in ("w4a16", "w4a16a", "w4a16mx"):
+    if fmt in ("w4a16", "w4a16a", "w4a16mx", "w8a16", "f8a16"):
         x = g.standard_normal((M, K)).astype(np.float32)
         return (x.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8), None
     if fmt == "w8a8":

@@ -150,6 +150,39 @@ __device__ __forceinline__ bf16x8 dequant_fp4x8_scaled(uint32_t v, float s) {
   return bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
+// ---- 8-bit weights for the bf16 MFMA -----------------------------------------------------------
+// Two dwords of 8 consecutive-k weight codes (byte b = k b, two's-complement INT8 or OCP e4m3) ->
+// the 8 values as the bf16 MFMA operand in k order. Both are exact: |q| <= 128 needs 8
+// significant bits, and every finite e4m3 value (4 significant bits, exponents 2^-9 .. 2^8) is a
+// bf16 value. INT8: one sign-extending byte -> fp32 conversion per code (an SDWA byte select)
+// and one fp32 pair -> bf16 pair pack per two codes; FP8: gfx950's fp8 pair -> bf16 pair
+// conversion at unit scale, one per two codes.
+__device__ __forceinline__ bf16x2 int8_pair_to_bf16(uint32_t v, int shift) {
+  const f32x2 p = {float(int8_t(v >> shift)), float(int8_t(v >> (shift + 8)))};
+  return __builtin_convertvector(p, bf16x2);
+}
+__device__ __forceinline__ bf16x8 dequant_int8x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 r0 = int8_pair_to_bf16(lo, 0), r1 = int8_pair_to_bf16(lo, 16);
+  const bf16x2 r2 = int8_pair_to_bf16(hi, 0), r3 = int8_pair_to_bf16(hi, 16);
+  return bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+__device__ __forceinline__ bf16x8 dequant_fp8x8(uint32_t lo, uint32_t hi) {
+  const bf16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+// MFMA d (0..3) of a 128-k step of W8A16 / F8A16 weights: unit d >> 1 of the step (q0 / q1),
+// dwords 2 (d & 1) and 2 (d & 1) + 1 (layout.h).
+template <bool FP8>
+__device__ __forceinline__ bf16x8 dequant_w8_step(const u32x4& q0, const u32x4& q1, int d) {
+  const u32x4& q = d < 2 ? q0 : q1;
+  const int i = 2 * (d & 1);
+  if constexpr (FP8) return dequant_fp8x8(q[i], q[i + 1]);
+  else return dequant_int8x8(q[i], q[i + 1]);
+}
+
 // Position of 16-byte chunk `chunk` of activation row `row` in an LDS tile with `cpr` chunks per
 // row (an XOR swizzle, so each row's chunks stay a permutation of its own slots). For 128-byte
 // rows the key is the row's low three bits. For 256-byte rows the plain key (row & 15) leaves the

@@ -46,7 +46,8 @@ struct AccType<FAM_W8A8> {
 };
 
 // Final value of output (orow, n): `v` is the full K sum; srow indexes the per-token scale.
-// w: the weights of the expert (MoE) or the layer, for W8A8's per-channel scales.
+// w: the weights of the expert (MoE) or the layer, for the per-channel scales (W8A8, W8A16,
+// F8A16).
 template <int FAM>
 __device__ __forceinline__ void epilogue(const KParams& p, const uint8_t* w, int orow, int srow, int n,
                                          typename AccType<FAM>::elem v, float tw) {
@@ -62,6 +63,9 @@ __device__ __forceinline__ void epilogue(const KParams& p, const uint8_t* w, int
     }
   } else if constexpr (FAM == FAM_W4A8) {
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * p.a_scale[srow] * tw);
+  } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
+    const float sch = reinterpret_cast<const float*>(w + p.scales_off)[n];
+    reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * sch * tw);
   } else {   // W4A4, W4A8MX: both block scales were applied by the MFMA
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * tw);
   }

@@ -21,8 +21,23 @@ namespace {
 
 constexpr int kCUs = 256;
 
-// K per skinny unit (block-scaled FP8 steps over two 64-k layout units at a time)
-int k_unit(const Combo& c) { return c.fam == FAM_FP8B ? 128 : family_k_unit(c.fam); }
+// K per skinny unit (8-bit weights other than W8A8's step over two 64-k layout units at a time)
+int k_unit(const Combo& c) {
+  return (c.fam == FAM_FP8B || c.fam == FAM_W8A16 || c.fam == FAM_F8A16) ? 128 : family_k_unit(c.fam);
+}
+
+// Families that run on the skinny and ping-pong kernels only (no LDS-tiled or pipelined
+// instantiation).
+bool pp_only(const Combo& c) {
+  return c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B ||
+         c.fam == FAM_W8A16 || c.fam == FAM_F8A16;
+}
+
+// Activation bytes per 2 k (bf16: 4; 8-bit: 2; 4-bit: 1): the direct-to-LDS kernels address
+// activation rows with 32-bit offsets, so M * K * this / 2 must stay below 2^32.
+uint64_t act_bytes_2k(const Combo& c) {
+  return family_bf16_act(c.fam) ? 4u : c.fam == FAM_W4A4 ? 1u : 2u;
+}
 
 // Pick the skinny configuration for a row block of `rows` rows and N channels (measured on
 // MI355X at the benchmark shapes; the first candidate whose channel-tile count divides N/16).
@@ -36,6 +51,9 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
   };
   if (rows <= 16) {
+    // 8-bit weights with bf16 activations, N=14336 K=4096: 16 waves of 64 channels, two units in
+    // flight (M=1 INT8 / FP8: 13.2 / 12.3 us; the 8-wave form 13.5 / 12.6)
+    if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) return first_fit({27, 0, 1, 2});
     if (c.fam == FAM_MXW4A16) return first_fit({28, 13, 0, 1, 2});
     if (c.fam == FAM_FP8B) return first_fit({21, 2});
     if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
@@ -44,6 +62,8 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
+    if (c.fam == FAM_W8A16) return first_fit({29, 22, 3, 7, 8});   // M=32: 16.0 us (next 18.9)
+    if (c.fam == FAM_F8A16) return first_fit({22, 29, 3, 7, 8});   // M=32: 15.8 us (next 16.3)
     if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
     if (c.fam == FAM_FP8B) return first_fit({29, 15, 8});
     if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({16, 8});
@@ -104,6 +124,10 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_MXW4A16>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_FP8B)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_FP8B>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_W8A16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W8A16>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_F8A16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_F8A16>, grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W4A8>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -149,6 +173,12 @@ constexpr RangeEntry kMxW4a16Table[] = {{64, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
 // / 272.9 / 517.0 us, against 91.7 / 101.6 / 194.0 / 304.2 / 610.4 for the three-slot 64 x 256 and
 // 256 x 128 tiles)
 constexpr RangeEntry kFp8bTable[] = {{64, 0, 0}, {kInf, 3, 10}};
+// INT8 / FP8 weights with bf16 activations (the 128 x 256 tiles' three-slot ring of 64 KiB steps
+// exceeds the LDS). Measured at N=14336, K=4096 (INT8 / FP8): skinny 64-row blocks to M=128
+// (34.5 / 32.5 us; ping-pong 41.7 / 32.1), then ping-pong 128 x 128 with waves of 64 x 32:
+// M=256 / 1024 / 8192 at 45.7 / 171.7 / 1161 us and 40.4 / 155.0 / 1067 us, against 55.2 / 210.9
+// / 1364 and 41.9 / 158.9 / 1133 for waves of 32 x 64.
+constexpr RangeEntry kW8a16Table[] = {{128, 0, 0}, {kInf, 3, 3}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -181,6 +211,9 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_MXW4A16) {
     t = kMxW4a16Table;
     n = int(sizeof(kMxW4a16Table) / sizeof(kMxW4a16Table[0]));
+  } else if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) {
+    t = kW8a16Table;
+    n = int(sizeof(kW8a16Table) / sizeof(kW8a16Table[0]));
   } else if (c.fam == FAM_W4A4) {
     t = kW4a4Table;
     n = int(sizeof(kW4a4Table) / sizeof(kW4a4Table[0]));
@@ -200,7 +233,7 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
     return t[i];
   }
   // Fallbacks when the preferred tile does not divide N.
-  if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B) {
+  if (pp_only(c)) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
     for (int cfg : {10, 3, 2})   // 128 x 128 tiles (four LDS slots where they fit)
@@ -224,14 +257,12 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
     return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
-  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B) &&
-      (o.kind == 1 || o.kind == 2))
-    return false;
+  if (pp_only(c) && (o.kind == 1 || o.kind == 2)) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
   }
-  const bool a32 = uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) < (uint64_t(1) << 32);
+  const bool a32 = uint64_t(M) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);
   if (o.kind == 2) {
     const PipeCfg* cfgs = pipe_configs(&n);
     return a32 && K % 128 == 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0 &&
@@ -313,9 +344,8 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   }
   // The direct-to-LDS kernels address activations with 32-bit offsets.
   if ((pick.kind == 2 || pick.kind == 3) &&
-      uint64_t(M) * uint64_t(K) * (c.fam == FAM_WNA16 ? 2u : 1u) >= (uint64_t(1) << 32)) {
-    const int tc = (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B)
-                       ? -1 : pick_tiled(c, N, K);
+      uint64_t(M) * uint64_t(K) * act_bytes_2k(c) / 2 >= (uint64_t(1) << 32)) {
+    const int tc = pp_only(c) ? -1 : pick_tiled(c, N, K);
     pick = tc >= 0 ? RangeEntry{kInf, 1, tc} : RangeEntry{0, 0, 0};
   }
   if (pick.kind != 0) {

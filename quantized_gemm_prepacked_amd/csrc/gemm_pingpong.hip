@@ -74,6 +74,20 @@ struct PPTraits<FAM_MXW4A16> {
   static constexpr int kAScaleBytes = 0;
 };
 template <>
+struct PPTraits<FAM_W8A16> {
+  static constexpr int kRowBytes = 256;
+  static constexpr int kUnitsPerStep = 2;
+  static constexpr int kMetaPerTile = 0;
+  static constexpr int kAScaleBytes = 0;
+};
+template <>
+struct PPTraits<FAM_F8A16> {
+  static constexpr int kRowBytes = 256;
+  static constexpr int kUnitsPerStep = 2;
+  static constexpr int kMetaPerTile = 0;
+  static constexpr int kAScaleBytes = 0;
+};
+template <>
 struct PPTraits<FAM_W4A8MX> {
   static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 1;
@@ -252,9 +266,9 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     for (int t = 0; t < NTW; ++t) acc[mb][t] = Acc{0, 0, 0, 0};
 
   // Operand fragments of one step, filled by the memory phase and used by the compute phase.
-  constexpr bool BF16A = FAM == FAM_WNA16 || FAM == FAM_MXW4A16;   // bf16 activations
+  constexpr bool BF16A = family_bf16_act(FAM);   // bf16 activations
   constexpr int NA = BF16A ? 4 : (FAM == FAM_W4A4 ? 1 : 2);   // activation fragments per row block
-  constexpr int NB = (FAM == FAM_W8A8 || FAM == FAM_FP8B) ? 2 : 1;    // packed weight fragments per channel tile
+  constexpr int NB = family_8bit_weights(FAM) ? 2 : 1;    // packed weight fragments per channel tile
   u32x4 af[MW][NA];
   u32x4 bq[NTW][NB];
   uint32_t meta[NTW];
@@ -350,6 +364,17 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
           for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
         }
       }
+    } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
+      // 8-bit codes of the step's two units -> bf16, MFMA d taking unit d >> 1; the per-channel
+      // scale is applied in the epilogue
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_w8_step<FAM == FAM_F8A16>(bq[t][0], bq[t][NB - 1], d);
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+        }
     } else if constexpr (FAM == FAM_FP8B) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
@@ -498,6 +523,8 @@ int pp_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W4A8MX) return pp_lds_table<FAM_W4A8MX>(cfg, seq);
   if (fam == FAM_MXW4A16) return pp_lds_table<FAM_MXW4A16>(cfg, seq);
   if (fam == FAM_FP8B) return pp_lds_table<FAM_FP8B>(cfg, seq);
+  if (fam == FAM_W8A16) return pp_lds_table<FAM_W8A16>(cfg, seq);
+  if (fam == FAM_F8A16) return pp_lds_table<FAM_F8A16>(cfg, seq);
   return pp_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -544,6 +571,8 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_FP8B) return launch_pp_fam<FAM_FP8B, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W8A16) return launch_pp_fam<FAM_W8A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_F8A16) return launch_pp_fam<FAM_F8A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return launch_pp_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
 }
 

@@ -33,10 +33,11 @@ template <int FAM>
 struct SkTraits;
 // kRowBytes: activation bytes per row per unit of kUnitK k; kAScaleBytes: activation block-scale
 // bytes per row per unit (MXFP4 activations: one e8m0 byte per 32 k; block-scaled FP8: one fp32);
-// kWLoads: 1 KB weight units per kernel unit (block-scaled FP8: two 64-k units per 128-k step).
+// kWLoads: 1 KB weight units per kernel unit (8-bit weights other than W8A8's: two 64-k units per
+// 128-k step).
 template <int FAM>
 struct SkWLoads {
-  static constexpr int value = FAM == FAM_FP8B ? 2 : 1;
+  static constexpr int value = (FAM == FAM_FP8B || FAM == FAM_W8A16 || FAM == FAM_F8A16) ? 2 : 1;
 };
 template <>
 struct SkTraits<FAM_WNA16> {
@@ -57,6 +58,14 @@ struct SkTraits<FAM_W4A8> {
 template <>
 struct SkTraits<FAM_MXW4A16> {
   static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 0;
+};
+template <>
+struct SkTraits<FAM_W8A16> {
+  static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 0, kZeroBytes = 0, kAScaleBytes = 0;
+};
+template <>
+struct SkTraits<FAM_F8A16> {
+  static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 0, kZeroBytes = 0, kAScaleBytes = 0;
 };
 template <>
 struct SkTraits<FAM_W4A8MX> {
@@ -250,6 +259,23 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
           for (int mb = 0; mb < MB; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
         }
       }
+    } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
+      // bf16 activations in the WNA16 chunk order; the step's two weight units hold the lane
+      // group's 32 k, MFMA d taking 8 of them from unit d >> 1. The per-channel scale is applied
+      // in the epilogue.
+      u32x4 af[MB][4];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) af[mb][d] = read_a(mb, 4 * (lane >> 4) + d);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_w8_step<FAM == FAM_F8A16>(bw[buf][r][t], bw2[buf][r][Sh::WL == 2 ? t : 0], d);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+        }
     } else if constexpr (FAM == FAM_FP8B) {
       // one 128-k step = one scale block: the fp8 MFMA's partial, times (row scale x block
       // scale), into the tile; the row scale is per output row (D rows 4 (lane >> 4) + i)
@@ -452,6 +478,8 @@ int skinny_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W4A8MX) return skinny_lds_table<FAM_W4A8MX>(cfg, seq);
   if (fam == FAM_MXW4A16) return skinny_lds_table<FAM_MXW4A16>(cfg, seq);
   if (fam == FAM_FP8B) return skinny_lds_table<FAM_FP8B>(cfg, seq);
+  if (fam == FAM_W8A16) return skinny_lds_table<FAM_W8A16>(cfg, seq);
+  if (fam == FAM_F8A16) return skinny_lds_table<FAM_F8A16>(cfg, seq);
   return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
@@ -498,6 +526,8 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);
   if (fam == FAM_W4A8MX) return launch_skinny_fam<FAM_W4A8MX, false>(p, cfg, grid, s);
   if (fam == FAM_FP8B) return launch_skinny_fam<FAM_FP8B, false>(p, cfg, grid, s);
+  if (fam == FAM_W8A16) return launch_skinny_fam<FAM_W8A16, false>(p, cfg, grid, s);
+  if (fam == FAM_F8A16) return launch_skinny_fam<FAM_F8A16, false>(p, cfg, grid, s);
   return launch_skinny_fam<FAM_W4A8, false>(p, cfg, grid, s);
 }
 

@@ -66,11 +66,19 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
       return HQ_OK;
     }
     case HQ_W_INT8_SYM:
+      if (d->act_fmt == HQ_ACT_BF16) {
+        if (d->group_size != 0 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 || c->out_i32)
+          return fail(HQ_ERR_UNSUPPORTED,
+                      "INT8 weights with BF16 activations need group_size 0 (per channel), FP32 "
+                      "scales, no zero-point and bf16 output");
+        c->fam = hq::FAM_W8A16;
+        return HQ_OK;
+      }
       if (d->group_size != 0 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 ||
           d->act_fmt != HQ_ACT_INT8_PER_TOKEN)
         return fail(HQ_ERR_UNSUPPORTED,
                     "INT8 weights need group_size 0 (per channel), FP32 scales, no zero-point "
-                    "and per-token INT8 activations");
+                    "and per-token INT8 activations (or BF16 activations, see above)");
       c->fam = hq::FAM_W8A8;
       return HQ_OK;
     case HQ_W_FP4_E2M1:
@@ -86,6 +94,14 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
                                             : hq::FAM_W4A8;
       return HQ_OK;
     case HQ_W_FP8_E4M3:
+      if (d->act_fmt == HQ_ACT_BF16) {
+        if (d->group_size != 0 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 || c->out_i32)
+          return fail(HQ_ERR_UNSUPPORTED,
+                      "FP8 weights with BF16 activations need group_size 0 (per channel), FP32 "
+                      "scales, no zero-point and bf16 output");
+        c->fam = hq::FAM_F8A16;
+        return HQ_OK;
+      }
       if (d->group_size != 128 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 ||
           d->act_fmt != HQ_ACT_FP8E4M3_BLOCK128 || c->out_i32)
         return fail(HQ_ERR_UNSUPPORTED,
@@ -101,7 +117,8 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
 hq_status check_shape(const hq::Combo& c, int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
     return fail(HQ_ERR_INVALID_ARGUMENT, "N=%lld K=%lld out of range", (long long)N, (long long)K);
-  const int ku = c.fam == hq::FAM_FP8B ? 128 : hq::family_k_unit(c.fam);
+  const int ku = (c.fam == hq::FAM_FP8B || c.fam == hq::FAM_W8A16 || c.fam == hq::FAM_F8A16)
+                     ? 128 : hq::family_k_unit(c.fam);
   if (c.fam == hq::FAM_FP8B && N % 128 != 0)
     return fail(HQ_ERR_UNSUPPORTED, "FP8 block-scaled weights need N %% 128 == 0 (N=%lld)", (long long)N);
   if (N % 16 != 0 || K % ku != 0)
@@ -189,7 +206,7 @@ hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, co
   if (!a || !w_packed || !y) return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be non-NULL");
   if (!aligned16(a) || !aligned16(w_packed) || !aligned16(y))
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
-  const bool needs_scale = c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16;
+  const bool needs_scale = !hq::family_bf16_act(c.fam);
   if (needs_scale && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale is required for INT8/FP8 activations");
   if (!needs_scale && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (a_scale && (reinterpret_cast<uintptr_t>(a_scale) & 3u))

@@ -20,12 +20,18 @@
 //     scale from lane group b). The fp8 activations are fed in the instruction's own 8-bit A
 //     layout (two 16-byte halves per lane, see device_ops.h).
 //
+//   W8A16 / F8A16 (8-bit INT8 or FP8 e4m3 weights with bf16 activations, K step 128 = two 64-k
+//   units, v_mfma_f32_16x16x32_bf16 x 4 per step): in step kt, unit j (0, 1) lane l holds
+//     k = 128*kt + 32*(l>>4) + 16*j + b in byte b (0..15),
+//   so a lane's two units cover its lane group's 32 consecutive k of the step, the WNA16 K
+//   order: MFMA d (0..3) of the step takes unit d>>1, bytes 8*(d&1) .. +7.
+//
 // Regions per expert (each starts at a 256-byte aligned offset; experts are stacked with a
 // 256-byte aligned stride):
 //   codes : [N/16][K/KU] units of 1024 bytes (K units of one channel tile are contiguous)
 //   WNA16 scales: [N/16][K/128][16] bf16;  zeros (asym): [N/16][K/128][8] bytes, byte i holds
 //                 the zero of channel 2i (low nibble) and 2i+1 (high nibble)
-//   W8A8  scales: [N] fp32 per channel
+//   W8A8, W8A16, F8A16 scales: [N] fp32 per channel
 //   W4A8  scales: [N/16][K/128][64] e8m0 bytes, byte l = scale of lane l's block
 #pragma once
 #include <stdint.h>
@@ -37,12 +43,24 @@ namespace hq {
 // share W4A8's prepacked weights (MXFP4); only the activation operand differs.
 // FP8B: block-scaled FP8 W8A8 (e4m3 weights with an fp32 scale per 128 x 128 block, e4m3
 // activations with an fp32 scale per (row, 128 k)); its codes use W8A8's 64-k units.
-enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5, FAM_FP8B = 6 };
+// W8A16 / F8A16: INT8 / FP8 e4m3 weights with a per-channel fp32 scale and bf16 activations.
+enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5, FAM_FP8B = 6,
+              FAM_W8A16 = 7, FAM_F8A16 = 8 };
+
+// 8-bit weight codes in 64-k units
+inline constexpr bool family_8bit_weights(int f) {
+  return f == FAM_W8A8 || f == FAM_FP8B || f == FAM_W8A16 || f == FAM_F8A16;
+}
+
+// bf16 activations (2 bytes per k)
+inline constexpr bool family_bf16_act(int f) {
+  return f == FAM_WNA16 || f == FAM_MXW4A16 || f == FAM_W8A16 || f == FAM_F8A16;
+}
 
 constexpr int kUnitBytes = 1024;
 constexpr int kTileN = 16;
 
-inline int family_k_unit(Family f) { return (f == FAM_W8A8 || f == FAM_FP8B) ? 64 : 128; }
+inline int family_k_unit(Family f) { return family_8bit_weights(f) ? 64 : 128; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -70,7 +88,7 @@ inline PackedLayout make_layout(Family fam, bool asym, int64_t N, int64_t K) {
   L.scales_off = align256(L.codes_bytes);
   if (fam == FAM_WNA16) {
     L.scales_bytes = size_t(L.n_tiles) * L.k_units * 16 * 2;
-  } else if (fam == FAM_W8A8) {
+  } else if (fam == FAM_W8A8 || fam == FAM_W8A16 || fam == FAM_F8A16) {
     L.scales_bytes = size_t(N) * 4;
   } else if (fam == FAM_FP8B) {
     // per 16-channel tile and 128-k step: the 128 x 128 block's fp32 scale, four copies (one

@@ -103,6 +103,24 @@ void pack_fp8b(const PackedLayout& L, const uint8_t* wq, const float* scales, ui
   });
 }
 
+// 8-bit codes for the bf16 MFMA (layout.h, W8A16 / F8A16): unit j of step kt, lane l, byte b
+// holds k = 128 kt + 32 (l >> 4) + 16 j + b of channel 16 nt + (l & 15).
+void pack_w8a16(const PackedLayout& L, const uint8_t* wq, const float* scales, uint8_t* out) {
+  const int64_t K = L.K;
+  parallel_for(L.n_tiles, [&](int64_t nt) {
+    for (int64_t u = 0; u < L.k_units; ++u) {
+      const int64_t kt = u >> 1, j = u & 1;
+      uint8_t* unit = out + L.codes_off + (size_t(nt) * L.k_units + u) * kUnitBytes;
+      for (int l = 0; l < 64; ++l) {
+        const int64_t n = nt * 16 + (l & 15);
+        const int64_t k0 = kt * 128 + 32 * (l >> 4) + 16 * j;
+        std::memcpy(unit + 16 * l, wq + size_t(n) * K + k0, 16);
+      }
+    }
+  });
+  std::memcpy(out + L.scales_off, scales, size_t(L.N) * 4);
+}
+
 void pack_w4a8(const PackedLayout& L, const uint8_t* wq, const uint8_t* scales, uint8_t* out) {
   const int64_t K = L.K, B = K / 32;
   parallel_for(L.n_tiles, [&](int64_t nt) {
@@ -140,6 +158,9 @@ void prepack(const Combo& c, int64_t E, int64_t N, int64_t K, const void* wq,
     } else if (c.fam == FAM_W8A8) {
       pack_w8a8(L, static_cast<const int8_t*>(wq) + e * size_t(N) * K,
                 static_cast<const float*>(scales) + e * size_t(N), o);
+    } else if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) {
+      pack_w8a16(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * K,
+                 static_cast<const float*>(scales) + e * size_t(N), o);
     } else if (c.fam == FAM_FP8B) {
       pack_fp8b(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * K,
                 static_cast<const float*>(scales) + e * size_t(N / 128) * (K / 128), o);

@@ -91,7 +91,7 @@ __device__ __forceinline__ void wna16_offset_contraction(const KParams& p, const
 // ---- stores ------------------------------------------------------------------------------------
 // row_base: the wave's first row in the workgroup's row space (dense: m; MoE: position in
 // sorted_ids). No K split here (p.split == 1).
-// w: the weights of the expert (MoE) or the layer, for W8A8's per-channel scales.
+// w: the weights of the expert (MoE) or the layer, for the per-channel scales.
 template <int FAM, bool MOE, int MW, int NTW>
 __device__ __forceinline__ void store_tile(const KParams& p, const uint8_t* w,
                                            const typename AccType<FAM>::type (&acc)[MW][NTW],
@@ -123,7 +123,8 @@ __device__ __forceinline__ void store_tile(const KParams& p, const uint8_t* w,
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int n = (nt0 + t) * 16 + (lane & 15);
-    cs[t] = (FAM == FAM_W8A8 && !p.out_i32) ? reinterpret_cast<const float*>(w + p.scales_off)[n] : 1.0f;
+    constexpr bool kChannelScale = FAM == FAM_W8A8 || FAM == FAM_W8A16 || FAM == FAM_F8A16;
+    cs[t] = (kChannelScale && !p.out_i32) ? reinterpret_cast<const float*>(w + p.scales_off)[n] : 1.0f;
   }
 #pragma unroll
   for (int mb = 0; mb < MW; ++mb)
@@ -140,6 +141,8 @@ __device__ __forceinline__ void store_tile(const KParams& p, const uint8_t* w,
         } else if constexpr (FAM == FAM_W8A8) {
           if (p.out_i32) reinterpret_cast<int*>(p.y)[idx] = v;
           else reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(float(v) * rs[mb][i] * cs[t] * tw[mb][i]);
+        } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
+          reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * cs[t] * tw[mb][i]);
         } else {
           reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * rs[mb][i] * tw[mb][i]);
         }

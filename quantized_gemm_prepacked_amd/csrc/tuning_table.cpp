@@ -43,6 +43,8 @@ bool parse_family(const std::string& s, Family* f) {
   else if (s == "w4a8mx") *f = FAM_W4A8MX;
   else if (s == "mxw4a16") *f = FAM_MXW4A16;
   else if (s == "fp8b") *f = FAM_FP8B;
+  else if (s == "w8a16") *f = FAM_W8A16;
+  else if (s == "f8a16") *f = FAM_F8A16;
   else return false;
   return true;
 }

@@ -141,3 +141,22 @@ def test_grouped_gemm_host_validation():
         hq.hq_grouped_gemm(d, 4, 600, 256, 512, 16, None, 16, 16, 16, 16, 1 << 20, stream=0)
     with pytest.raises(hq.HQError):
         hq.hq_grouped_gemm(d, 4, 2, 256, 512, 16, 16, 16, 16, 16, 16, 1 << 20, stream=0)
+
+
+def test_w8a16_descriptors():
+    """INT8 and FP8 weights with bf16 activations: per-channel fp32 scales only, K % 128, bf16
+    output, no activation scale."""
+    for desc in (hq.DESC_W8A16_INT8, hq.DESC_W8A16_FP8):
+        assert hq.hq_prepacked_bytes(desc, 1, 256, 512) > 0
+        assert hq.hq_prepacked_bytes(desc, 1, 256, 448) == 0          # K % 128
+        with pytest.raises(hq.HQError) as ei:
+            hq.hq_gemm(desc, 4, 256, 512, 16, 64, 16, 16, stream=0)   # a_scale with bf16 activations
+        assert ei.value.status == hq.HQ_ERR_INVALID_ARGUMENT
+    for wf in (hq.HQ_W_INT8_SYM, hq.HQ_W_FP8_E4M3):
+        for bad in (hq.make_desc(wf, 128, hq.HQ_SCALE_FP32, 0, hq.HQ_ACT_BF16),
+                    hq.make_desc(wf, 0, hq.HQ_SCALE_BF16, 0, hq.HQ_ACT_BF16),
+                    hq.make_desc(wf, 0, hq.HQ_SCALE_FP32, 0, hq.HQ_ACT_BF16, hq.HQ_OUT_INT32_ACC)):
+            assert hq.hq_prepacked_bytes(bad, 1, 256, 512) == 0
+            with pytest.raises(hq.HQError) as ei:
+                hq.hq_gemm(bad, 4, 256, 512, 16, None, 16, 16, stream=0)
+            assert ei.value.status == hq.HQ_ERR_UNSUPPORTED

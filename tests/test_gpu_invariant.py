@@ -37,11 +37,16 @@ def _inputs(fmt, M, N, K):
     if fmt == "w4a16mx":
         d = synth.make_w4a16mx(900, M, N, K)
         return hq.DESC_W4A16_MXFP4, (d["wq"], d["scales"], None), d["x"], None
+    if fmt in ("w8a16", "f8a16"):
+        d = synth.make_w8a16(900, M, N, K, fp8=fmt == "f8a16")
+        desc = hq.DESC_W8A16_FP8 if fmt == "f8a16" else hq.DESC_W8A16_INT8
+        return desc, (d["wq"], d["s_ch"], None), d["x"], None
     d = synth.make_w4a8mx(900, M, N, K)
     return hq.DESC_W4A8_MXFP8, (d["wq"], d["scales"], None), d["xq"], d["xs"]
 
 
-@pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx", "w4a16mx", "fp8block"])
+@pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx", "w4a16mx", "fp8block",
+                                 "w8a16", "f8a16"])
 def test_rows_do_not_depend_on_the_batch(fmt):
     M, N, K = 300, 512, 1024
     desc, std, x, s = _inputs(fmt, M, N, K)
@@ -77,6 +82,8 @@ def test_rows_do_not_depend_on_the_batch(fmt):
         ref, _ = oracle.ref_w4a16_mx(x, std[0], std[1])
     elif fmt == "fp8block":
         ref, _ = oracle.ref_w8a8_fp8_block(x, s, std[0], std[1])
+    elif fmt in ("w8a16", "f8a16"):
+        ref, _ = oracle.ref_w8a16(x, std[0], std[1], fp8=fmt == "f8a16")
     else:
         ref, _ = oracle.ref_w4a8_mx(x, s, std[0], std[1])
     check_float(ref_rows, ref, f"invariant {fmt}")

@@ -1,0 +1,108 @@
+"""GPU parity of 8-bit weights with bf16 activations ("W8A16": INT8 or FP8 e4m3 codes with a
+per-channel fp32 scale, each code converted exactly to bf16 in registers, bf16 MFMA, scale in the
+epilogue) against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_gemm_prepacked_amd as hq
+import synth
+
+from gpu_harness import check_float, gemm, prepack, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [False, True]   # fp8
+
+
+def _desc(fp8):
+    return hq.DESC_W8A16_FP8 if fp8 else hq.DESC_W8A16_INT8
+
+
+def _run(d, M, N, K, fp8):
+    w = prepack(_desc(fp8), 1, N, K, d["wq"], d["s_ch"])
+    return gemm(_desc(fp8), M, N, K, to_dev(d["x"]), None, w)
+
+
+@pytest.mark.parametrize("fp8", FMTS)
+@pytest.mark.parametrize("M,N,K", [
+    (1, 512, 4096), (3, 272, 384), (16, 64, 128), (32, 256, 1024), (64, 512, 512),
+    (1, 64, 8192),      # 4 workgroups: K split across workgroups, then the reduction launch
+    (200, 256, 640),    # ping-pong 128 x 128, 5 K steps
+    (300, 512, 1024),   # ragged M
+    (1000, 400, 512),   # N not a multiple of the 128-wide tile: skinny fallback
+])
+def test_w8a16_small(M, N, K, fp8):
+    say(f"[w8a16 fp8={fp8}] M={M} N={N} K={K}")
+    d = synth.make_w8a16(1300, M, N, K, fp8=fp8)
+    y = _run(d, M, N, K, fp8)
+    ref, _ = oracle.ref_w8a16(d["x"], d["wq"], d["s_ch"], fp8=fp8)
+    check_float(y, ref, f"w8a16 fp8={fp8}")
+
+
+@pytest.mark.parametrize("fp8", FMTS)
+@pytest.mark.parametrize("M", [1, 16, 128, 8192])
+def test_w8a16_full_size_sampled(M, fp8):
+    N, K = 14336, 4096
+    say(f"[w8a16 full fp8={fp8}] M={M}")
+    d = synth.make_w8a16(2, M, N, K, fp8=fp8)
+    y = _run(d, M, N, K, fp8)
+    g = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, 48)]))
+    cols = np.unique(np.concatenate([[0, N - 1], g.integers(0, N, 96)]))
+    ref, _ = oracle.ref_w8a16(d["x"], d["wq"], d["s_ch"], fp8=fp8, rows=rows, cols=cols)
+    check_float(y[np.ix_(rows, cols)], ref, f"w8a16 fp8={fp8} M={M}")
+
+
+@pytest.mark.parametrize("fp8", FMTS)
+def test_w8a16_every_kernel_configuration(fp8, monkeypatch):
+    """Every skinny and ping-pong configuration that fits the shape (the tuner may pick any)."""
+    M, N, K = 96, 512, 768
+    d = synth.make_w8a16(1301, M, N, K, fp8=fp8)
+    desc = _desc(fp8)
+    w = prepack(desc, 1, N, K, d["wq"], d["s_ch"])
+    ref, _ = oracle.ref_w8a16(d["x"], d["wq"], d["s_ch"], fp8=fp8)
+    ran = 0
+    for kind in (0, 3):
+        for cfg in range(hq.hq_kernel_config_count(kind)):
+            monkeypatch.setenv("HQ_TUNE", f"kind={kind},cfg={cfg},split=1")
+            try:
+                plan = hq.hq_gemm_plan(desc, M, N, K)
+            except hq.HQError:
+                continue            # the configuration does not fit this shape
+            say(f"[w8a16 fp8={fp8}] kind={kind} cfg={cfg} plan={plan}")
+            y = gemm(desc, M, N, K, to_dev(d["x"]), None, w)
+            check_float(y, ref, f"w8a16 fp8={fp8} kind={kind} cfg={cfg}")
+            ran += 1
+    assert ran >= 20
+
+
+def test_w8a16_code_and_scale_extremes():
+    """INT8 codes -128 .. 127 (-128 accepted as is), FP8 codes up to +-448 incl. subnormals, and
+    per-channel scales over 2^-30 .. 2^30."""
+    M, N, K = 48, 256, 512
+    g = np.random.default_rng(9)
+    x = synth.normal_bf16(g, (M, K))
+    s = (2.0 ** g.integers(-30, 31, N)).astype(np.float32)
+    q8 = g.integers(-128, 128, (N, K)).astype(np.int8)
+    y = _run({"x": x, "wq": q8, "s_ch": s}, M, N, K, False)
+    ref, _ = oracle.ref_w8a16(x, q8, s)
+    check_float(y, ref, "w8a16 int8 extremes", rounding_floor=True)
+    f8 = g.integers(0, 0x7F, (N, K)).astype(np.uint8) | (g.integers(0, 2, (N, K)).astype(np.uint8) << 7)
+    y = _run({"x": x, "wq": f8, "s_ch": s}, M, N, K, True)
+    ref, _ = oracle.ref_w8a16(x, f8, s, fp8=True)
+    check_float(y, ref, "w8a16 fp8 extremes", rounding_floor=True)
+
+
+def test_w8a16_int8_integer_activations_are_exact():
+    """Integer activations and weights with a power-of-two scale: every product and partial sum is
+    an integer below 2^24, so fp32 accumulation is exact and the output is the oracle rounded once."""
+    M, N, K = 20, 128, 1024
+    g = np.random.default_rng(11)
+    xi = g.integers(-8, 9, (M, K)).astype(np.float32)
+    x = synth.bf16_bits(xi)
+    q = g.integers(-127, 128, (N, K)).astype(np.int8)
+    s = np.full(N, 0.5, np.float32)
+    y = _run({"x": x, "wq": q, "s_ch": s}, M, N, K, False)
+    _, ref_bits = oracle.ref_w8a16(x, q, s)
+    assert np.array_equal(y.view(np.uint16), ref_bits)

@@ -153,3 +153,26 @@ def test_mxfp4_weight_layout_is_shared_by_its_activation_formats():
         hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, out)
         outs.append(out)
     assert all(np.array_equal(o, outs[0]) for o in outs)
+
+
+def unpack_w8a16(buf, N, K):
+    """8-bit codes for the bf16 MFMA: in 128-k step kt, 64-k unit j (0, 1), lane l, byte b holds
+    k = 128 kt + 32 (l >> 4) + 16 j + b of channel 16 nt + (l & 15); fp32 scales [N] follow."""
+    nt_n, u_n = N // 16, K // 64
+    units = buf[:nt_n * u_n * 1024].reshape(nt_n, K // 128, 2, 4, 16, 16)   # nt, kt, j, g, c, b
+    # -> [nt, c, kt, g, j, b] = channel 16 nt + c, k = 128 kt + 32 g + 16 j + b
+    wq = units.transpose(0, 4, 1, 3, 2, 5).reshape(N, K)
+    s_off = _a256(nt_n * u_n * 1024)
+    return wq, buf[s_off:s_off + 4 * N].view(np.float32)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_w8a16_roundtrip(fp8):
+    N, K = 48, 384
+    d = synth.make_w8a16(913, 2, N, K, fp8=fp8)
+    desc = hq.DESC_W8A16_FP8 if fp8 else hq.DESC_W8A16_INT8
+    out = np.zeros(hq.hq_prepacked_bytes(desc, 1, N, K), np.uint8)
+    hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["s_ch"], None, out)
+    wq, s = unpack_w8a16(out, N, K)
+    assert np.array_equal(wq, d["wq"].view(np.uint8)) and np.array_equal(s, d["s_ch"])
+    assert out.size == _a256(_a256((N // 16) * (K // 64) * 1024) + 4 * N)
