@@ -152,6 +152,45 @@ def ref_moe_gemm_q(xq: np.ndarray, s_tok: np.ndarray, topk_ids: np.ndarray, expe
     return y, bits, valid
 
 
+def ref_moe_gemm_fp8_block(xq: np.ndarray, xs: np.ndarray, topk_ids: np.ndarray, expert_weights, N: int,
+                           E: int, topk_weights: np.ndarray | None = None, rows=None, cols=None):
+    """Grouped GEMM with block-scaled FP8 experts and tokens (the page's FP8 W8A8 with blockwise
+    scaling in its MoE form, section "W8A8 / W4A8 / W4A4", Indexed and Grouped layouts): expert
+    dict {"wq": e4m3 [N, K], "ws": fp32 [N/128, K/128]}, tokens e4m3 [T, K] with fp32 scales
+    xs [T, K/128]. For routed row (t, j) with expert e and 128-k blocks g:
+        Y[t*topk + j, n] = sum_g xs[t, g] * ws_e[n // 128, g] * sum_{k in g} xq[t, k] * wq_e[n, k]
+    (* topk_weights[t, j]), in float64. Returns (y float64 [R, N'], y bf16 bits, valid) like
+    ref_moe_gemm."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, topk = ids.shape
+    flat = np.arange(T * topk) if rows is None else np.asarray(rows, dtype=np.int64)
+    x = decode_e4m3(xq)
+    sa = np.asarray(xs, dtype=np.float32).astype(np.float64)
+    G = x.shape[1] // 128
+    cidx = np.arange(N) if cols is None else np.asarray(cols)
+    y = np.full((flat.size, cidx.size), np.nan, dtype=np.float64)
+    experts = ids.reshape(-1)[flat]
+    for e in np.unique(experts):
+        if e < 0 or e >= E:
+            continue
+        sel = np.flatnonzero(experts == e)
+        wd = expert_weights(int(e))
+        tok = flat[sel] // topk
+        w = decode_e4m3(np.asarray(wd["wq"])[cidx])
+        sw = np.asarray(wd["ws"], dtype=np.float32).astype(np.float64)[cidx // 128]   # [N', G]
+        acc = np.zeros((sel.size, cidx.size))
+        for g in range(G):
+            blk = slice(128 * g, 128 * (g + 1))
+            acc += (x[tok, blk] @ w[:, blk].T) * sa[tok, g][:, None] * sw[None, :, g]
+        y[sel] = acc
+    if topk_weights is not None:
+        tw = np.asarray(topk_weights, dtype=np.float32).astype(np.float64).reshape(-1)[flat]
+        y = y * tw[:, None]
+    valid = ~np.isnan(y[:, 0]) if cidx.size else np.ones(flat.size, dtype=bool)
+    bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
+    return y, bits, valid
+
+
 def ref_silu_mul(gate_up_bf16: np.ndarray):
     """Gated activation of the MoE expert MLP: for each routed row, the first half of the
     gate_up output is the gate g, the second half the up projection u, and

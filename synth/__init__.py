@@ -302,6 +302,23 @@ def make_moe_weights_expert_w8a8(config_id: int, e: int, N: int, K: int):
     return {"wq": q, "s_ch": s}
 
 
+def make_moe_weights_expert_fp8b(config_id: int, e: int, N: int, K: int):
+    """One expert's FP8 e4m3 weights with an fp32 scale per 128 x 128 block, from its own stream
+    [config, 3, e]."""
+    w = rng(config_id, 3, e).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    q, s = quantize_fp8_blocks(w, 128, 128)
+    return {"wq": q, "ws": s}
+
+
+def random_fp8b_expert(g: np.random.Generator, N: int, K: int):
+    """Random finite e4m3 codes with block scales near 1/448 (MoE benchmark and large parity tests:
+    drawing and quantizing normals for many experts is slow, the kernel's work does not depend on
+    the values)."""
+    q = g.integers(0, 0x7F, (N, K)).astype(np.uint8) | (g.integers(0, 2, (N, K)).astype(np.uint8) << 7)
+    s = (np.float32(1.0 / 448.0) * (1 + 0.25 * g.random((N // 128, K // 128)))).astype(np.float32)
+    return {"wq": q, "ws": s}
+
+
 def make_w4a4_activations(config_id: int, M: int, K: int):
     """MXFP4 activations (e2m1 codes + e8m0 per 32 k) quantized from bf16 N(0,1) by the OCP MX
     rule (the same quantizer as the weights')."""
