@@ -58,7 +58,13 @@ def _values(a: np.ndarray) -> np.ndarray:
 
 def _dequant_expert(wd, g: int, cols):
     """An expert's standard-format weights -> float64 [N, K]: INT4 groups with bf16 scales
-    (uint16 bits) or MXFP4 blocks with e8m0 scales (uint8)."""
+    (uint16 bits), MXFP4 blocks with e8m0 scales (uint8), or 8-bit codes with an fp32 scale per
+    channel ({"wq", "s_ch", "fp8"}: INT8, or e4m3 when fp8 is true)."""
+    if "s_ch" in wd:
+        c = np.asarray(wd["wq"]) if cols is None else np.asarray(wd["wq"])[np.asarray(cols)]
+        q = decode_e4m3(c) if wd.get("fp8") else decode_int8(c).astype(np.float64)
+        s = np.asarray(wd["s_ch"], dtype=np.float32).astype(np.float64)
+        return q * (s if cols is None else s[np.asarray(cols)])[:, None]
     if np.asarray(wd["scales"]).dtype == np.uint8:
         return dequant_mxfp4(wd["wq"], wd["scales"], cols)
     return dequant_wna16(wd["wq"], wd["scales"], wd.get("zeros"), g, cols)

@@ -114,3 +114,23 @@ def test_w8a16_row_and_column_subsets():
     rows, cols = [0, 4, 8], [1, 17, 47]
     ys, bs = oracle.ref_w8a16(d["x"], d["wq"], d["s_ch"], fp8=True, rows=rows, cols=cols)
     assert np.array_equal(ys, y[np.ix_(rows, cols)]) and np.array_equal(bs, bits[np.ix_(rows, cols)])
+
+
+def test_moe_gemm_with_8bit_experts_equals_per_token_dense():
+    T, topk, E, N, K = 4, 2, 3, 32, 256
+    x = synth.normal_bf16(synth.rng(55), (T, K))
+    ids = np.array([[0, 2], [1, 0], [2, 2], [1, 1]])
+    for fp8 in (False, True):
+        ws = {}
+        for e in range(E):
+            d = synth.make_w8a16(980 + e, 1, N, K, fp8=fp8)
+            ws[e] = {"wq": d["wq"], "s_ch": d["s_ch"], "fp8": fp8}
+        y, _, valid = oracle.ref_moe_gemm(x, ids, lambda e: ws[e], N, E, 128)
+        assert valid.all()
+        for t in range(T):
+            for j in range(topk):
+                e = ids[t, j]
+                yd, _ = oracle.ref_w8a16(x[t:t + 1], ws[e]["wq"], ws[e]["s_ch"], fp8=fp8)
+                np.testing.assert_allclose(y[t * topk + j], yd[0], rtol=1e-13)
+        yc, _, _ = oracle.ref_moe_gemm(x, ids, lambda e: ws[e], N, E, 128, cols=[3, 31])
+        assert np.array_equal(yc, y[:, [3, 31]])
