@@ -213,7 +213,13 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   const uint8_t* asc_src = nullptr;
   if constexpr (Sh::ASC_BYTES > 0) {
     const int r = wave * (BM / 8) + min(lane, BM / 8 - 1);
-    const int src_row = min(row0 + r, p.M - 1);
+    int src_row;   // MoE: the row's token
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[row0 + r];
+      src_row = id < p.M ? id / p.topk : 0;
+    } else {
+      src_row = min(row0 + r, p.M - 1);
+    }
     asc_src = reinterpret_cast<const uint8_t*>(p.a_scale) + size_t(src_row) * (p.K / 32);
   }
   // metadata: this wave copies bytes [wave * META_PER_WAVE, +META_PER_WAVE) of the stage's
@@ -532,8 +538,10 @@ template <int FAM, bool MOE, int I>
 static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PPCfg C = kPP[I];
   using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn, C.stages>;
-  // MoE instantiations: the formats whose activation scales are per token (or absent)
-  constexpr bool kMoeFam = FAM == FAM_WNA16 || FAM == FAM_MXW4A16 || FAM == FAM_W8A8 || FAM == FAM_W4A8;
+  // MoE instantiations: the formats whose activation scales are per token, per token and 128-k
+  // block, or absent
+  constexpr bool kMoeFam = FAM == FAM_WNA16 || FAM == FAM_MXW4A16 || FAM == FAM_W8A8 || FAM == FAM_W4A8 ||
+                           FAM == FAM_FP8B || FAM == FAM_W8A16 || FAM == FAM_F8A16;
   if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || kMoeFam)) {
     auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn, C.stages>;
     if (Sh::LDS > 65536)
@@ -563,6 +571,9 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
     if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W4A8) return launch_pp_fam<FAM_W4A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_FP8B) return launch_pp_fam<FAM_FP8B, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_W8A16) return launch_pp_fam<FAM_W8A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_F8A16) return launch_pp_fam<FAM_F8A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     return hipErrorInvalidValue;
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);

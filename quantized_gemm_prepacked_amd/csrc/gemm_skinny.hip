@@ -141,11 +141,18 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     }
     asrc[j] = p.a + size_t(src_row) * a_row_bytes + 16 * c;
   }
-  // MXFP4 activations: lane r < 16*MB copies the 4 e8m0 bytes of row r for each unit
+  // Activation block scales (MXFP4 / MXFP8: 4 e8m0 bytes per unit; block-scaled FP8: one fp32):
+  // lane r < 16*MB copies those of row r for each unit (MoE: of the row's token)
   const uint8_t* ascale_src = nullptr;
   if constexpr (Sh::ASC > 0) {
     const int r = min(lane, 16 * MB - 1);
-    const int src_row = min(row0 + r, p.M - 1);
+    int src_row;
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[row0 + r];
+      src_row = id < p.M ? id / p.topk : 0;
+    } else {
+      src_row = min(row0 + r, p.M - 1);
+    }
     ascale_src = reinterpret_cast<const uint8_t*>(p.a_scale) + size_t(src_row) * (p.K / 32);
   }
 
@@ -521,6 +528,9 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
                                      : launch_skinny_fam<FAM_MXW4A16, false>(p, cfg, grid, s);
   if (moe && fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, true>(p, cfg, grid, s);
   if (moe && fam == FAM_W4A8) return launch_skinny_fam<FAM_W4A8, true>(p, cfg, grid, s);
+  if (moe && fam == FAM_FP8B) return launch_skinny_fam<FAM_FP8B, true>(p, cfg, grid, s);
+  if (moe && fam == FAM_W8A16) return launch_skinny_fam<FAM_W8A16, true>(p, cfg, grid, s);
+  if (moe && fam == FAM_F8A16) return launch_skinny_fam<FAM_F8A16, true>(p, cfg, grid, s);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);

@@ -298,6 +298,12 @@ struct GroupedWs {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+// Formats with MoE / grouped kernels: activations in bf16, per token, or per token and 128-k block.
+bool moe_family(const hq::Combo& c) {
+  return c.fam == hq::FAM_WNA16 || c.fam == hq::FAM_MXW4A16 || c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8 ||
+         c.fam == hq::FAM_FP8B || c.fam == hq::FAM_W8A16 || c.fam == hq::FAM_F8A16;
+}
+
 GroupedWs grouped_ws(const hq::Combo& c, int64_t R, int32_t E, int64_t N, int64_t K) {
   GroupedWs g{};
   g.bm = hq::moe_block_m(c, R, 1, E, N, K);
@@ -325,15 +331,16 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16 && c.fam != hq::FAM_W8A8 && c.fam != hq::FAM_W4A8)
-    return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM: bf16 activations (INT4 or MXFP4 weights) or per-token "
-                                    "INT8 / FP8 activations (INT8 or MXFP4 weights)");
-  const bool per_token = c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8;
+  if (!moe_family(c))
+    return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM: bf16 activations (INT4, MXFP4, INT8 or FP8 weights), "
+                                    "per-token INT8 / FP8 activations (INT8 or MXFP4 weights) or block-scaled FP8");
+  const bool per_token = !hq::family_bf16_act(c.fam);   // per token, or per token and 128-k block
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (R < 0 || R > kMaxDim || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld E=%d out of range", (long long)R, E);
   if (R * N >= (int64_t(1) << 31)) return fail(HQ_ERR_UNSUPPORTED, "R*N must stay below 2^31");
-  if (per_token && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale [R] is required for INT8/FP8 activations");
+  if (per_token && !a_scale)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale ([R], or [R, K/128] for block-scaled FP8) is required for INT8/FP8 activations");
   if (!per_token && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (!a || !w_packed || !expert_offsets || !y)
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, expert_offsets and y must be non-NULL");
@@ -405,11 +412,11 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (c.fam != hq::FAM_WNA16 && c.fam != hq::FAM_MXW4A16 && c.fam != hq::FAM_W8A8 && c.fam != hq::FAM_W4A8)
-    return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM: bf16 activations (INT4 or MXFP4 weights) or per-token "
-                                    "INT8 / FP8 activations (INT8 or MXFP4 weights)");
+  if (!moe_family(c))
+    return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM: bf16 activations (INT4, MXFP4, INT8 or FP8 weights), "
+                                    "per-token INT8 / FP8 activations (INT8 or MXFP4 weights) or block-scaled FP8");
   if (c.out_i32) return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM writes bf16 only");
-  const bool per_token = c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8;
+  const bool per_token = !hq::family_bf16_act(c.fam);   // per token, or per token and 128-k block
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (T < 0 || topk <= 0 || topk > 64 || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld topk=%d E=%d out of range", (long long)T, topk, E);
@@ -419,7 +426,8 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
     return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: supported values are 16, 32, 64", block_m);
   if (c.invariant && block_m != 32)
     return fail(HQ_ERR_INVALID_ARGUMENT, "block_m=%d: batch-invariant MoE calls use block_m 32", block_m);
-  if (per_token && !a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale [T] is required for INT8/FP8 activations");
+  if (per_token && !a_scale)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale ([T], or [T, K/128] for block-scaled FP8) is required for INT8/FP8 activations");
   if (!per_token && a_scale) return fail(HQ_ERR_INVALID_ARGUMENT, "a_scale must be NULL for BF16 activations");
   if (!a || !w_packed || !sorted_ids || !block_expert || !num_padded || !y)
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed, sorted_ids, block_expert, num_padded and y must be non-NULL");

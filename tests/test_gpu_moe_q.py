@@ -1,6 +1,7 @@
-"""GPU parity of the MoE grouped GEMM and the grouped GEMM with per-token 8-bit activations:
-W4A8 (MXFP4 experts, FP8 e4m3 tokens; oracle float bar) and W8A8 (INT8 experts, INT8 tokens;
-within 1 bf16 ulp of the exactly rounded result)."""
+"""GPU parity of the MoE grouped GEMM and the grouped GEMM with 8-bit activations: W4A8 (MXFP4
+experts, FP8 e4m3 tokens; oracle float bar), W8A8 (INT8 experts, INT8 tokens; within 1 bf16 ulp
+of the exactly rounded result) and block-scaled FP8 (e4m3 experts with 128 x 128 block scales,
+e4m3 tokens with a scale per 128 k; oracle float bar)."""
 import numpy as np
 import pytest
 import torch
@@ -20,14 +21,25 @@ FORMATS = {
              lambda seed, e, N, K: synth.make_moe_weights_expert_mx(seed, e, N, K), synth.random_mxfp4_expert),
     "w8a8": (hq.DESC_W8A8, "int8", synth.quantize_int8_rows,
              lambda seed, e, N, K: synth.make_moe_weights_expert_w8a8(seed, e, N, K), synth.random_int8_expert),
+    "fp8b": (hq.DESC_W8A8_FP8_BLOCK, "fp8b", lambda x: synth.quantize_fp8_blocks(x, 1, 128),
+             lambda seed, e, N, K: synth.make_moe_weights_expert_fp8b(seed, e, N, K), synth.random_fp8b_expert),
 }
+ALL = ["w4a8", "w8a8", "fp8b"]
+
+
+def _ref(act, xq, s, ids, experts, N, E, topk_weights=None, cols=None):
+    if act == "fp8b":
+        return oracle.ref_moe_gemm_fp8_block(xq, s, ids, lambda e: experts[e], N, E,
+                                             topk_weights=topk_weights, cols=cols)
+    return oracle.ref_moe_gemm_q(xq, s, ids, lambda e: experts[e], N, E, act, topk_weights=topk_weights,
+                                 cols=cols)
 
 
 def _stack(desc, E, N, K, experts):
     stride = hq.hq_prepacked_bytes(desc, 1, N, K)
     w = torch.zeros(stride * E, dtype=torch.uint8, device=DEV)
     for e, wd in experts.items():
-        sc = wd["scales"] if "scales" in wd else wd["s_ch"]
+        sc = wd["scales"] if "scales" in wd else wd["ws"] if "ws" in wd else wd["s_ch"]
         w[e * stride:(e + 1) * stride] = prepack(desc, 1, N, K, wd["wq"], sc)
     return w
 
@@ -68,8 +80,7 @@ def _moe(fmt, T, topk, E, N, K, bm, with_weights, seed, random_codes=False, cols
                            npad, bm, None if tw is None else to_dev(tw.reshape(-1)), y, ws, wsb)
     torch.cuda.synchronize()
     y = y.cpu().numpy().view(np.uint16)
-    ref, bits, valid = oracle.ref_moe_gemm_q(xq, s_tok, ids, lambda e: experts[e], N, E, act,
-                                             topk_weights=tw, cols=cols)
+    ref, bits, valid = _ref(act, xq, s_tok, ids, experts, N, E, topk_weights=tw, cols=cols)
     assert valid.all()
     got = y if cols is None else y[:, cols]
     _check(fmt, got, ref, bits, f"moe {fmt} T={T} bm={bm}")
@@ -85,13 +96,15 @@ MOE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("fmt", ["w4a8", "w8a8"])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("T,topk,E,N,K,bm,tw", MOE_CASES)
 def test_moe_q_small(fmt, T, topk, E, N, K, bm, tw):
+    if fmt == "fp8b" and N % 128:
+        pytest.skip("block-scaled FP8 weights need N % 128 == 0 (128 x 128 scale blocks)")
     _moe(fmt, T, topk, E, N, K, bm, tw, 600 + T)
 
 
-@pytest.mark.parametrize("fmt", ["w4a8", "w8a8"])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("T", [8, 128, 1024])
 def test_moe_q_full_size_sampled(fmt, T):
     """DeepSeek-V3 gate_up shape (256 experts, top-8, K = 7168, N = 4096) at the block size the
@@ -123,12 +136,12 @@ def _grouped(fmt, R, E, N, K, counts, seed, lead=0):
     ids = np.full((R, 1), -1, np.int64)
     for e in range(E):
         ids[max(offs[e], 0):min(offs[e + 1], R), 0] = e
-    ref, bits, valid = oracle.ref_moe_gemm_q(xq, s_row, ids, lambda e: experts[e], N, E, act)
+    ref, bits, valid = _ref(act, xq, s_row, ids, experts, N, E)
     _check(fmt, y[valid], ref[valid], bits[valid], f"grouped {fmt} R={R}")
     assert (y[~valid] == NAN_BF16).all(), "rows outside every range must not be written"
 
 
-@pytest.mark.parametrize("fmt", ["w4a8", "w8a8"])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("R,E,N,K,counts,lead", [
     (100, 4, 256, 512, [30, 0, 50, 20], 0),
     (1000, 8, 512, 1024, [400, 10, 0, 250, 1, 200, 39, 100], 0),
