@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | moe | moe_mx | moe_layer.
+--config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | moe | moe_mx | moe_fp8b | moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -356,7 +356,9 @@ def run_dense(args, wl: str):
                                "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act",
                                "w4a4": "mxfp4 e2m1 + e8m0 per 32, mxfp4 act (e8m0 per 32)",
                                "w4a16mx": "mxfp4 e2m1 + e8m0 per 32, bf16 act",
-                               "fp8block": "e4m3 + fp32 per 128x128 block, e4m3 act + fp32 per 1x128"}[wl]},
+                               "fp8block": "e4m3 + fp32 per 128x128 block, e4m3 act + fp32 per 1x128",
+                               "w8a16": "int8 per-channel fp32 scale, bf16 act",
+                               "f8a16": "fp8 e4m3 per-channel fp32 scale, bf16 act"}[wl]},
         "roofline": roof,
         "sweep": sweep,
     }
@@ -380,9 +382,10 @@ def _random_mxfp4_expert(g, N: int, K: int):
             "scales": g.integers(119, 123, (N, K // 32)).astype(np.uint8)}
 
 
-def run_moe(args, mx: bool = False):
-    """Token sort + grouped GEMM per T. tokens/s = T / (t_align + t_gemm). mx: MXFP4 experts
-    (W4A16-MXFP4) instead of INT4 group-128."""
+def run_moe(args, mx=False):
+    """Token sort + grouped GEMM per T. tokens/s = T / (t_align + t_gemm). mx: True for MXFP4
+    experts (W4A16-MXFP4) instead of INT4 group-128, "fp8b" for block-scaled FP8 experts and
+    tokens (the token quantization happens before the timed region)."""
     import numpy as np
     import torch
 
@@ -391,9 +394,15 @@ def run_moe(args, mx: bool = False):
 
     E, topk, N, K, Ts, cfg = (MOE[k] for k in ("E", "topk", "N", "K", "Ts", "cfg"))
     dev = torch.device("cuda:0")
-    desc = hq.DESC_W4A16_MXFP4 if mx else hq.DESC_W4A16_SYM
-    name = MOE["name"].replace("W4A16", "W4A16-MXFP4") if mx else MOE["name"]
-    expert_gen = _random_mxfp4_expert if mx else synth.random_int4_sym_expert
+    fp8b = mx == "fp8b"
+    if fp8b:
+        desc, name, expert_gen = hq.DESC_W8A8_FP8_BLOCK, MOE["name"].replace(
+            "W4A16", "FP8 W8A8 block-scaled (128x128 weights, 1x128 tokens)"), synth.random_fp8b_expert
+    else:
+        desc = hq.DESC_W4A16_MXFP4 if mx else hq.DESC_W4A16_SYM
+        name = MOE["name"].replace("W4A16", "W4A16-MXFP4") if mx else MOE["name"]
+        expert_gen = _random_mxfp4_expert if mx else synth.random_int4_sym_expert
+    peak = "fp8" if fp8b else "bf16"
     stride = hq.hq_prepacked_bytes(desc, 1, N, K)
     log(f"[bench] {name}: {E} experts x {stride / 1e6:.1f} MB prepacked (random codes)")
     w0 = torch.empty(stride * E, dtype=torch.uint8, device=dev)
@@ -404,7 +413,7 @@ def run_moe(args, mx: bool = False):
         d = expert_gen(g, N, K)
         if e < 16:
             std[e] = d
-        hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, host)
+        hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["ws"] if fp8b else d["scales"], None, host)
         w0[e * stride:(e + 1) * stride].copy_(torch.from_numpy(host))
     n_copies = 4                      # > 256 MB Infinity Cache between reuses even at T = 1
     weights = [w0] + [w0.clone() for _ in range(n_copies - 1)]
@@ -414,8 +423,14 @@ def run_moe(args, mx: bool = False):
         bm = hq.hq_moe_block_m(desc, T, topk, E, N, K)
         cap = hq.hq_moe_align_capacity(T, topk, E, bm)
         hist = np.bincount(inp["topk_ids"].reshape(-1), minlength=E)
+        if fp8b:   # tokens quantized to e4m3 with an fp32 scale per 128 k (outside the timed region)
+            xq, xs = synth.quantize_fp8_blocks(synth.bf16_bits_to_f32(inp["x"]), 1, 128)
+            inp = dict(inp, xq=xq, xs=xs)
+            xdev, sdev = torch.from_numpy(xq).to(dev), torch.from_numpy(xs.reshape(-1)).to(dev)
+        else:
+            xdev, sdev = torch.from_numpy(inp["x"].view(np.int16)).to(dev), None
         state[T] = dict(
-            x=torch.from_numpy(inp["x"].view(np.int16)).to(dev),
+            x=xdev, xs=sdev,
             ids=torch.from_numpy(inp["topk_ids"]).to(dev), bm=bm,
             sorted=torch.empty(cap, dtype=torch.int32, device=dev),
             bexp=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
@@ -438,7 +453,7 @@ def run_moe(args, mx: bool = False):
         s = state[T]
         w = weights[ctr[0] % n_copies]
         ctr[0] += 1
-        hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, s["x"], None, w, s["sorted"], s["bexp"],
+        hq.hq_moe_grouped_gemm(desc, T, topk, E, N, K, s["x"], s["xs"], w, s["sorted"], s["bexp"],
                                s["npad"], s["bm"], None, s["y"], s["ws"], s["wsb"], None)
 
     # One HIP graph of R back-to-back launches per (T, stage); the sort's outputs persist, so R
@@ -484,10 +499,10 @@ def run_moe(args, mx: bool = False):
         tg = float(np.mean([e[1].elapsed_time(e[2]) for e in rec[T]])) * 1e3 / reps[T]
         s = state[T]
         fl = 2.0 * T * topk * N * K
-        by = s["active"] * stride + T * K * 2 + T * topk * N * 2
+        by = s["active"] * stride + (T * K + T * (K // 128) * 4 if fp8b else T * K * 2) + T * topk * N * 2
         tf = fl / (tg * 1e-6) / 1e12
         gbs = by / (tg * 1e-6) / 1e9
-        fc, fm = tf / PEAK_TFLOPS["bf16"], gbs / HBM_PEAK_GBS
+        fc, fm = tf / PEAK_TFLOPS[peak], gbs / HBM_PEAK_GBS
         sweep.append({"T": T, "launches_per_graph": reps[T], "block_m": s["bm"], "active_experts": s["active"], "top_expert_rows": s["top"],
                       "align_us": round(ta, 3), "gemm_us": round(tg, 3),
                       "tokens_per_s": round(T / ((ta + tg) * 1e-6), 1), "tflops": round(tf, 3),
@@ -497,16 +512,17 @@ def run_moe(args, mx: bool = False):
         tot_tok += T * reps[T]
     dom = max(sweep, key=lambda r: r["gemm_us"])
     if dom["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(dom["tflops"] / PEAK_TFLOPS["bf16"], 4)}
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS[peak], "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / PEAK_TFLOPS[peak], 4)}
     else:
         roof = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbps"] / HBM_PEAK_GBS, 4)}
-    roof.update(traffic=measured_traffic("moe_mx" if mx else "moe", f"T={dom['T']}"), kernel=f"grouped GEMM T={dom['T']}")
+    wl_name = "moe_fp8b" if fp8b else "moe_mx" if mx else "moe"
+    roof.update(traffic=measured_traffic(wl_name, f"T={dom['T']}"), kernel=f"grouped GEMM T={dom['T']}")
     line = {
         "metric": METRIC, "value": round(tot_tok / tot_t, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": peak,
         "data": "synthetic",
         "config": {"workload": name, "E": E, "topk": topk, "N": N, "K": K, "T": Ts,
                    "routing": "N(0,1) logits + Zipf(1.1) log-prior, softmax top-8"},
@@ -524,7 +540,10 @@ def run_moe(args, mx: bool = False):
             if e in need:
                 ws[e] = d
         t0 = time.perf_counter()
-        oracle.ref_moe_gemm(inp["x"], ids, lambda e: ws[e], N, E, 128)
+        if fp8b:
+            oracle.ref_moe_gemm_fp8_block(inp["xq"], inp["xs"], ids, lambda e: ws[e], N, E)
+        else:
+            oracle.ref_moe_gemm(inp["x"], ids, lambda e: ws[e], N, E, 128)
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(),
                                 "kind": "oracle", "sample": f"T=1 ({len(need)} experts), {dt:.1f} s"}
@@ -723,7 +742,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_layer"])
+    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_fp8b", "moe_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -734,6 +753,8 @@ def main():
         line = run_moe(args)
     elif args.config == "moe_mx":
         line = run_moe(args, mx=True)
+    elif args.config == "moe_fp8b":
+        line = run_moe(args, mx="fp8b")
     elif args.config == "moe_layer":
         line = run_moe_layer(args)
     else:

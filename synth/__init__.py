@@ -314,7 +314,8 @@ def random_fp8b_expert(g: np.random.Generator, N: int, K: int):
     """Random finite e4m3 codes with block scales near 1/448 (MoE benchmark and large parity tests:
     drawing and quantizing normals for many experts is slow, the kernel's work does not depend on
     the values)."""
-    q = g.integers(0, 0x7F, (N, K)).astype(np.uint8) | (g.integers(0, 2, (N, K)).astype(np.uint8) << 7)
+    q = g.integers(0, 256, (N, K), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] -= 1                       # the two NaN codes -> +-448
     s = (np.float32(1.0 / 448.0) * (1 + 0.25 * g.random((N // 128, K // 128)))).astype(np.float32)
     return {"wq": q, "ws": s}
 
