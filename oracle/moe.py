@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import decode_bf16, decode_e4m3, decode_int8, round_to_bf16
+from .codecs import decode_bf16, decode_e4m3, decode_e8m0, decode_int8, round_to_bf16
 from .gemm import dequant_mxfp4, dequant_wna16
 
 
@@ -193,6 +193,41 @@ def ref_moe_gemm_fp8_block(xq: np.ndarray, xs: np.ndarray, topk_ids: np.ndarray,
         tw = np.asarray(topk_weights, dtype=np.float32).astype(np.float64).reshape(-1)[flat]
         y = y * tw[:, None]
     valid = ~np.isnan(y[:, 0]) if cidx.size else np.ones(flat.size, dtype=bool)
+    bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
+    return y, bits, valid
+
+
+def ref_moe_gemm_mx(xq: np.ndarray, xs: np.ndarray, topk_ids: np.ndarray, expert_weights, N: int, E: int,
+                    act: str, topk_weights: np.ndarray | None = None, rows=None, cols=None):
+    """Grouped GEMM with MX-scaled tokens and MXFP4 experts (the page's W4A4 and W4A8 with
+    microscaling formats, section "W8A8 / W4A8 / W4A4", whose Indexed and Grouped paths it
+    names): tokens are MXFP4 (act "mxfp4": packed e2m1 [T, K/2]) or MXFP8 (act "mxfp8": e4m3
+    [T, K]) with an e8m0 scale byte per 32 k in xs [T, K/32]; experts {"wq", "scales"} as MXFP4.
+        Y[t*topk + j, :] = x_t . dequant_mxfp4(W_e)^T (* topk_weights[t, j]),
+    x_t[k] = decode(xq[t, k]) * 2^(xs[t, k // 32] - 127), exact in float64. Returns
+    (y float64 [R, N'], y bf16 bits, valid) like ref_moe_gemm."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, topk = ids.shape
+    flat = np.arange(T * topk) if rows is None else np.asarray(rows, dtype=np.int64)
+    if act == "mxfp4":
+        x = dequant_mxfp4(xq, xs)
+    else:
+        xc = decode_e4m3(xq)
+        x = xc * decode_e8m0(xs)[:, np.arange(xc.shape[1]) // 32]
+    n_cols = N if cols is None else len(cols)
+    y = np.full((flat.size, n_cols), np.nan, dtype=np.float64)
+    experts = ids.reshape(-1)[flat]
+    for e in np.unique(experts):
+        if e < 0 or e >= E:
+            continue
+        sel = np.flatnonzero(experts == e)
+        wd = expert_weights(int(e))
+        w = dequant_mxfp4(wd["wq"], wd["scales"], cols)
+        y[sel] = x[flat[sel] // topk] @ w.T
+    if topk_weights is not None:
+        tw = np.asarray(topk_weights, dtype=np.float32).astype(np.float64).reshape(-1)[flat]
+        y = y * tw[:, None]
+    valid = ~np.isnan(y[:, 0]) if n_cols else np.ones(flat.size, dtype=bool)
     bits = round_to_bf16(np.where(np.isnan(y), 0.0, y))
     return y, bits, valid
 

@@ -1,7 +1,8 @@
-"""Pins of the oracle's MoE grouped GEMM with block-scaled FP8 experts and tokens, CPU only: every
-routed row equals the dense block-scaled FP8 oracle on that token and expert, rows routed outside
-[0, E) stay invalid, the router weight multiplies, and a scalar loop over the definition on a tiny
-case with distinct block scales."""
+"""Pins of the oracle's MoE grouped GEMMs with block-scaled FP8 experts and tokens, and with MX-scaled
+tokens (MXFP4, MXFP8) and MXFP4 experts, CPU only: every routed row equals the dense oracle of the
+format on that token and expert, rows routed outside [0, E) stay invalid, the router weight
+multiplies, and a scalar loop over the block-scaled definition on a tiny case with distinct
+block scales."""
 import numpy as np
 
 import oracle
@@ -57,3 +58,27 @@ def test_moe_fp8_block_scalar_loop():
                 for k in range(K):
                     acc += float(xs[t, k // 128]) * float(ws[e]["ws"][n // 128, k // 128]) * xv[t, k] * wv[n, k]
                 assert abs(y[t * topk + j, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def test_moe_mx_tokens_equal_per_token_dense():
+    T, topk, E, N, K = 4, 2, 3, 32, 256
+    ids = np.array([[0, 2], [1, 0], [2, 2], [1, 5]])          # 5 is outside [0, E)
+    ws = {e: synth.make_moe_weights_expert_mx(975, e, N, K) for e in range(E)}
+    tw = synth.rng(64).random((T, topk)).astype(np.float32)
+    a4 = synth.make_w4a4_activations(976, T, K)
+    x8 = synth.bf16_bits_to_f32(synth.normal_bf16(synth.rng(977), (T, K)))
+    xq8, xs8 = synth.quantize_mxfp8_rows(x8)
+    for act, xq, xs, dense in (("mxfp4", a4["xq"], a4["xs"], oracle.ref_w4a4),
+                               ("mxfp8", xq8, xs8, oracle.ref_w4a8_mx)):
+        y, bits, valid = oracle.ref_moe_gemm_mx(xq, xs, ids, lambda e: ws[e], N, E, act, topk_weights=tw)
+        assert valid.tolist() == [True] * 7 + [False]
+        for t in range(T):
+            for j in range(topk):
+                e = ids[t, j]
+                if e >= E:
+                    continue
+                yd, _ = dense(xq[t:t + 1], xs[t:t + 1], ws[e]["wq"], ws[e]["scales"])
+                np.testing.assert_allclose(y[t * topk + j], yd[0] * np.float64(tw[t, j]), rtol=1e-13)
+        ys, _, _ = oracle.ref_moe_gemm_mx(xq, xs, ids, lambda e: ws[e], N, E, act, topk_weights=tw,
+                                          rows=[0, 5], cols=[1, 30])
+        assert np.array_equal(ys, y[np.ix_([0, 5], [1, 30])])
