@@ -119,9 +119,10 @@ typedef struct {
  *   INT8_SYM   + FP32 scale, group 0                  + ACT_BF16   (W8A16)    -> OUT_BF16
  *   FP8_E4M3   + FP32 scale, group 0                  + ACT_BF16   (W8A16)    -> OUT_BF16
  *              (the 8-bit WnA16 widths; K % 128 == 0)
- * MoE grouped GEMM and grouped GEMM: the combinations with ACT_BF16 (INT4 sym / asym, FP4, INT8,
- * FP8), those with per-token activations (INT8 W8A8 with OUT_BF16, FP4 + ACT_FP8E4M3_PER_TOKEN
- * W4A8), and block-scaled FP8 (a_scale = fp32 [T, K/128], one row per token).
+ * MoE grouped GEMM and grouped GEMM: every combination above with OUT_BF16 -- ACT_BF16 (INT4 sym /
+ * asym, FP4, INT8, FP8 weights), per-token activations (INT8 W8A8, FP4 + ACT_FP8E4M3_PER_TOKEN
+ * W4A8), block-scaled FP8 (a_scale = fp32 [T, K/128]) and MX activations (ACT_MXFP4, ACT_MXFP8:
+ * a_scale = the e8m0 bytes [T, K/32]); activation scales are one row per token.
  * Every combination also takes compute_flags = HQ_COMPUTE_BATCH_INVARIANT.
  */
 
@@ -241,8 +242,9 @@ int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32
 /* ---------------------------------------------------------------------------------------------
  * MoE grouped GEMM (device): bf16 activations with INT4 group weights (WNA16), MXFP4 weights or
  * per-channel INT8 / FP8 weights (W8A16), per-token 8-bit activations with INT8 (W8A8) or MXFP4
- * (W4A8) weights, or block-scaled FP8 activations and weights (the page's FP8 W8A8 with blockwise
- * scaling, whose MoE form it compares in section "W8A8 / W4A8 / W4A4"):
+ * (W4A8) weights, block-scaled FP8 activations and weights (the page's FP8 W8A8 with blockwise
+ * scaling, whose MoE form it compares in section "W8A8 / W4A8 / W4A4"), or MXFP4 / MXFP8
+ * activations with MXFP4 weights (W4A4, W4A8-MXFP8; same section):
  *   y[f, :] = (topk_weights ? topk_weights[f] : 1) * a[f / topk, :] . dequant(W_{e(f)})^T
  * for every flat index f = t*topk + j that hq_moe_align routed to a valid expert e(f), with the
  * dense path's epilogue per format (W8A8: bf16(float(acc) * a_scale[t] * s_ch_e[n] * weight),
@@ -250,7 +252,8 @@ int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32
  * expert per 128-k step, then * weight). Rows of y for unrouted f are not written.
  *   a             [T, K] row-major (device): bf16, or int8 / e4m3 codes
  *   a_scale       fp32 [T] per-token scales for INT8 / FP8 activations, fp32 [T, K/128] for
- *                 block-scaled FP8 (required); NULL for bf16
+ *                 block-scaled FP8, e8m0 bytes [T, K/32] for MXFP4 / MXFP8 activations
+ *                 (required); NULL for bf16
  *   w_packed      prepacked weights of all E experts (hq_prepack_weights with E experts)
  *   sorted_ids, block_expert, num_padded: outputs of hq_moe_align with the same T, topk, E,
  *                 block_m (device)

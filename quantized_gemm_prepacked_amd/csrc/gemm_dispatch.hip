@@ -414,9 +414,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
   // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
   const bool a32 = uint64_t(T) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);   // 32-bit row offsets
-  const bool pp_fam = c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16 || c.fam == FAM_W8A8 || c.fam == FAM_W4A8 ||
-                      c.fam == FAM_FP8B || c.fam == FAM_W8A16 || c.fam == FAM_F8A16;
-  if (pp_fam && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+  if (K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
     // (the 8-bit-activation formats' 32-row tiles do not split into whole-wave copies: skinny)
     static const int pp32[1] = {7}, pp64[2] = {5, 4};
     const int* cands = block_m == 32 ? pp32 : pp64;

@@ -538,11 +538,9 @@ template <int FAM, bool MOE, int I>
 static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PPCfg C = kPP[I];
   using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn, C.stages>;
-  // MoE instantiations: the formats whose activation scales are per token, per token and 128-k
-  // block, or absent
-  constexpr bool kMoeFam = FAM == FAM_WNA16 || FAM == FAM_MXW4A16 || FAM == FAM_W8A8 || FAM == FAM_W4A8 ||
-                           FAM == FAM_FP8B || FAM == FAM_W8A16 || FAM == FAM_F8A16;
-  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && (!MOE || kMoeFam)) {
+  // (MoE instantiations exist for every format: activation scales, where there are any, are
+  // gathered per routed row from its token's row)
+  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024) {
     auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn, C.stages>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
@@ -574,6 +572,8 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
     if (fam == FAM_FP8B) return launch_pp_fam<FAM_FP8B, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W8A16) return launch_pp_fam<FAM_W8A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_F8A16) return launch_pp_fam<FAM_F8A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     return hipErrorInvalidValue;
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);

@@ -531,6 +531,8 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
   if (moe && fam == FAM_FP8B) return launch_skinny_fam<FAM_FP8B, true>(p, cfg, grid, s);
   if (moe && fam == FAM_W8A16) return launch_skinny_fam<FAM_W8A16, true>(p, cfg, grid, s);
   if (moe && fam == FAM_F8A16) return launch_skinny_fam<FAM_F8A16, true>(p, cfg, grid, s);
+  if (moe && fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, true>(p, cfg, grid, s);
+  if (moe && fam == FAM_W4A8MX) return launch_skinny_fam<FAM_W4A8MX, true>(p, cfg, grid, s);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, false>(p, cfg, grid, s);
   if (fam == FAM_W4A4) return launch_skinny_fam<FAM_W4A4, false>(p, cfg, grid, s);

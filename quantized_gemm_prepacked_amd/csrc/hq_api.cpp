@@ -298,10 +298,12 @@ struct GroupedWs {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Formats with MoE / grouped kernels: activations in bf16, per token, or per token and 128-k block.
+// Formats with MoE / grouped kernels: all of them (activations in bf16, per token, per token and
+// 128-k block, or MX-scaled per 32 k).
 bool moe_family(const hq::Combo& c) {
   return c.fam == hq::FAM_WNA16 || c.fam == hq::FAM_MXW4A16 || c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8 ||
-         c.fam == hq::FAM_FP8B || c.fam == hq::FAM_W8A16 || c.fam == hq::FAM_F8A16;
+         c.fam == hq::FAM_FP8B || c.fam == hq::FAM_W8A16 || c.fam == hq::FAM_F8A16 || c.fam == hq::FAM_W4A4 ||
+         c.fam == hq::FAM_W4A8MX;
 }
 
 GroupedWs grouped_ws(const hq::Combo& c, int64_t R, int32_t E, int64_t N, int64_t K) {

@@ -89,10 +89,10 @@ def test_moe_rejections():
         hq.hq_moe_align(16, 4, 8, 1000, 16, 16, 16, 16, 16, stream=0)       # E > 512
     with pytest.raises(hq.HQError):
         hq.hq_moe_align(16, 4, 8, 256, 16, 0, 16, 16, 16, stream=0)         # null output
-    with pytest.raises(hq.HQError) as ei:      # activations with block scales: no MoE path
-        hq.hq_moe_grouped_gemm(hq.DESC_W4A4_MXFP4, 4, 8, 256, 256, 512, 16, 64, 16, 16, 16, 16, 16,
+    with pytest.raises(hq.HQError) as ei:      # MX activations need their e8m0 scale rows
+        hq.hq_moe_grouped_gemm(hq.DESC_W4A4_MXFP4, 4, 8, 256, 256, 512, 16, None, 16, 16, 16, 16, 16,
                                None, 16, stream=0)
-    assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
+    assert ei.value.status == hq.HQ_ERR_INVALID_ARGUMENT
     with pytest.raises(hq.HQError) as ei:      # int32 accumulators are a dense-only output
         hq.hq_moe_grouped_gemm(hq.DESC_W8A8_I32, 4, 8, 256, 256, 512, 16, 64, 16, 16, 16, 16, 16,
                                None, 16, stream=0)

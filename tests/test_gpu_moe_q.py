@@ -1,7 +1,8 @@
-"""GPU parity of the MoE grouped GEMM and the grouped GEMM with 8-bit activations: W4A8 (MXFP4
+"""GPU parity of the MoE grouped GEMM and the grouped GEMM with quantized activations: W4A8 (MXFP4
 experts, FP8 e4m3 tokens; oracle float bar), W8A8 (INT8 experts, INT8 tokens; within 1 bf16 ulp
-of the exactly rounded result) and block-scaled FP8 (e4m3 experts with 128 x 128 block scales,
-e4m3 tokens with a scale per 128 k; oracle float bar)."""
+of the exactly rounded result), block-scaled FP8 (e4m3 experts with 128 x 128 block scales,
+e4m3 tokens with a scale per 128 k), W4A4 and W4A8-MXFP8 (MXFP4 experts, MXFP4 / MXFP8 tokens
+with e8m0 scales per 32 k); float formats at the oracle float bar."""
 import numpy as np
 import pytest
 import torch
@@ -23,11 +24,18 @@ FORMATS = {
              lambda seed, e, N, K: synth.make_moe_weights_expert_w8a8(seed, e, N, K), synth.random_int8_expert),
     "fp8b": (hq.DESC_W8A8_FP8_BLOCK, "fp8b", lambda x: synth.quantize_fp8_blocks(x, 1, 128),
              lambda seed, e, N, K: synth.make_moe_weights_expert_fp8b(seed, e, N, K), synth.random_fp8b_expert),
+    "w4a4": (hq.DESC_W4A4_MXFP4, "mxfp4", lambda x: tuple(synth.quantize_mxfp4(x).values()),
+             lambda seed, e, N, K: synth.make_moe_weights_expert_mx(seed, e, N, K), synth.random_mxfp4_expert),
+    "w4a8mx": (hq.DESC_W4A8_MXFP8, "mxfp8", synth.quantize_mxfp8_rows,
+               lambda seed, e, N, K: synth.make_moe_weights_expert_mx(seed, e, N, K), synth.random_mxfp4_expert),
 }
-ALL = ["w4a8", "w8a8", "fp8b"]
+ALL = ["w4a8", "w8a8", "fp8b", "w4a4", "w4a8mx"]
 
 
 def _ref(act, xq, s, ids, experts, N, E, topk_weights=None, cols=None):
+    if act in ("mxfp4", "mxfp8"):
+        return oracle.ref_moe_gemm_mx(xq, s, ids, lambda e: experts[e], N, E, act,
+                                      topk_weights=topk_weights, cols=cols)
     if act == "fp8b":
         return oracle.ref_moe_gemm_fp8_block(xq, s, ids, lambda e: experts[e], N, E,
                                              topk_weights=topk_weights, cols=cols)
