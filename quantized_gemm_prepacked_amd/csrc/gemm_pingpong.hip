@@ -382,16 +382,27 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
           for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
         }
     } else if constexpr (FAM == FAM_FP8B) {
+      // A wave's NTW tiles (NTW divides 8, first tile a multiple of NTW) lie in one 128-channel
+      // scale block, so one factor per output row serves all of them. All MFMAs of the step
+      // first, then the scaled accumulation of their partial sums.
+      const float sw = __uint_as_float(meta[0]);
+      float c[MW][4];
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const float sw = __uint_as_float(meta[t]);
+      for (int mb = 0; mb < MW; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb) {
-          const f32x4 part = mfma_fp8_fp8(af[mb][0], af[mb][1], bq[t][0], bq[t][1], f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int i = 0; i < 4; ++i) c[mb][i] = asr[mb][i] * sw;
+      f32x4 part[MW][NTW];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[i] * (asr[mb][i] * sw);
-        }
-      }
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb)
+          part[mb][t] = mfma_fp8_fp8(af[mb][0], af[mb][1], bq[t][0], bq[t][1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[mb][t][i] * c[mb][i];
     } else if constexpr (FAM == FAM_W8A8) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
