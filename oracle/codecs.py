@@ -32,6 +32,16 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def unpack_crumbs(packed: np.ndarray) -> np.ndarray:
+    """[..., K/4] bytes -> [..., K] 2-bit codes (uint8): code k sits in bits 2 (k % 4) and
+    2 (k % 4) + 1 of byte k // 4 (lowest k in the lowest bits)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 4,), dtype=np.uint8)
+    for j in range(4):
+        out[..., j::4] = (p >> (2 * j)) & 0x3
+    return out
+
+
 def decode_int4_sym(codes: np.ndarray) -> np.ndarray:
     c = np.asarray(codes).astype(np.int64) & 0xF
     return np.where(c >= 8, c - 16, c)

@@ -17,7 +17,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import (
-    unpack_nibbles, decode_int4_sym, decode_uint4, decode_e2m1, decode_e8m0, decode_e4m3,
+    unpack_nibbles, unpack_crumbs, decode_int4_sym, decode_uint4, decode_e2m1, decode_e8m0, decode_e4m3,
     decode_bf16, round_to_bf16, decode_int8,
 )
 
@@ -42,6 +42,18 @@ def dequant_wna16(wq: np.ndarray, scales_bf16: np.ndarray, zeros: np.ndarray | N
         return q.astype(np.float64) * s[:, grp]
     q = decode_uint4(codes)
     z = decode_uint4(_sel(zeros, cols))
+    return (q - z[:, grp]).astype(np.float64) * s[:, grp]
+
+
+def dequant_wna2(wq: np.ndarray, scales_bf16: np.ndarray, zeros: np.ndarray, g: int, cols=None) -> np.ndarray:
+    """Group-wise asymmetric UINT2 weights -> float64 [N, K] (the page's WnA16 at a 2-bit weight
+    width, section "Results: kernel microbenchmarks"):
+        w[n, k] = (q[n, k] - z[n, k // g]) * s[n, k // g],    q, z in [0, 3]
+    wq packs four codes per byte (lowest k in the lowest bits), scales are bf16 bits."""
+    q = unpack_crumbs(_sel(wq, cols)).astype(np.int64)
+    s = decode_bf16(_sel(scales_bf16, cols))
+    z = np.asarray(_sel(zeros, cols)).astype(np.int64) & 0x3
+    grp = np.arange(q.shape[1]) // g
     return (q - z[:, grp]).astype(np.float64) * s[:, grp]
 
 
@@ -160,5 +172,15 @@ def ref_w8a16(x_bf16: np.ndarray, wq: np.ndarray, s_ch: np.ndarray, fp8: bool = 
     q = decode_e4m3(c) if fp8 else decode_int8(c).astype(np.float64)
     s = np.asarray(_sel(s_ch, cols), dtype=np.float32).astype(np.float64)
     w = q * s[:, None]
+    y = x @ w.T
+    return y, round_to_bf16(y)
+
+
+def ref_wna2(x_bf16: np.ndarray, wq: np.ndarray, scales_bf16: np.ndarray, zeros: np.ndarray, g: int,
+             rows=None, cols=None):
+    """2-bit WnA16: bf16 activations times group-wise UINT2 weights with zero-points,
+    y = x . dequant_wna2(w)^T in float64, rounded once to bf16. Returns (y float64, y bf16 bits)."""
+    x = decode_bf16(_sel(x_bf16, rows))
+    w = dequant_wna2(wq, scales_bf16, zeros, g, cols)
     y = x @ w.T
     return y, round_to_bf16(y)
