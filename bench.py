@@ -4,7 +4,8 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | moe | moe_mx | moe_fp8b | moe_layer.
+--config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | w2a16 | moe | moe_mx | moe_fp8b |
+moe_layer.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -45,6 +46,8 @@ WORKLOADS = {
     "fp8block": dict(name="dense FP8 W8A8 with 128x128 / 1x128 block scales", N=8192, K=8192,
                      Ms=[1, 64, 512, 4096], cfg=3, dtype="fp8", peak="fp8"),
     "w8a16": dict(name="dense W8A16 INT8 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
+                  dtype="bf16", peak="bf16"),
+    "w2a16": dict(name="dense W2A16 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
                   dtype="bf16", peak="bf16"),
     "f8a16": dict(name="dense W8A16 FP8 e4m3 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
                   dtype="bf16", peak="bf16"),
@@ -104,6 +107,8 @@ def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
         return N * K + (N // 128) * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
     if wl in ("w8a16", "f8a16"):
         return N * K + N * 4 + M * K * 2 + M * N * 2
+    if wl == "w2a16":
+        return N * K // 4 + N * (K // 128) * 2 + N * (K // 128) // 2 + M * K * 2 + M * N * 2
     return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
 
 
@@ -134,6 +139,11 @@ def make_inputs(wl: str, spec: dict):
         for M in spec["Ms"]:
             a = synth.make_w8a8_fp8_block(cfg, M, 128, K)          # activations only (N unused)
             acts[M] = (a["xq"], a["xs"])
+    elif wl == "w2a16":
+        d = synth.make_wna2(cfg, 1, N, K)
+        desc = hq.DESC_W2A16_ASYM
+        std = (d["wq"], d["scales"], d["zeros"])
+        acts = {M: (synth.normal_bf16(synth.rng(cfg, M), (M, K)), None) for M in spec["Ms"]}
     elif wl in ("w8a16", "f8a16"):
         d = synth.make_w8a16(cfg, 1, N, K, fp8=wl == "f8a16")
         desc = hq.DESC_W8A16_FP8 if wl == "f8a16" else hq.DESC_W8A16_INT8
@@ -194,6 +204,8 @@ def cpu_baseline(wl: str, spec: dict, std, acts):
             oracle.ref_w4a16_mx(x, std[0], std[1], rows=rows)
         elif wl in ("w8a16", "f8a16"):
             oracle.ref_w8a16(x, std[0], std[1], fp8=wl == "f8a16", rows=rows)
+        elif wl == "w2a16":
+            oracle.ref_wna2(x, std[0], std[1], std[2], 128, rows=rows)
         elif wl == "fp8block":
             oracle.ref_w8a8_fp8_block(x, s, std[0], std[1], rows=rows)
         else:
@@ -358,7 +370,8 @@ def run_dense(args, wl: str):
                                "w4a16mx": "mxfp4 e2m1 + e8m0 per 32, bf16 act",
                                "fp8block": "e4m3 + fp32 per 128x128 block, e4m3 act + fp32 per 1x128",
                                "w8a16": "int8 per-channel fp32 scale, bf16 act",
-                               "f8a16": "fp8 e4m3 per-channel fp32 scale, bf16 act"}[wl]},
+                               "f8a16": "fp8 e4m3 per-channel fp32 scale, bf16 act",
+                               "w2a16": "uint2 asym g128 bf16 scale + uint2 zero"}[wl]},
         "roofline": roof,
         "sweep": sweep,
     }

@@ -31,6 +31,13 @@ __device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// 8 bytes (2-bit weights: a lane's half unit), streamed; returned in the low two dwords.
+__device__ __forceinline__ u32x4 ldg8_stream(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return u32x4{v[0], v[1], 0u, 0u};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
@@ -76,6 +83,22 @@ __device__ __forceinline__ bf16x8 dequant_int4x8_offset128(uint32_t v) {
   const uint32_t p1 = ((v >> 4) & m) | c;
   const uint32_t p2 = ((v >> 8) & m) | c;
   const uint32_t p3 = ((v >> 12) & m) | c;
+  const u32x4 r = {p0, p1, p2, p3};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 2-bit form (WNA2): one dword holds 16 codes u in [0, 3] of consecutive k, code 2s + e in bits
+// 16 e + 2 s (layout.h); returns (128 + u) for the 8 codes of k 8 h .. 8 h + 7 (h = 0, 1) as the
+// MFMA operand in k order, one bit-select per pair of weights as for 4-bit codes.
+__device__ __forceinline__ bf16x8 dequant_uint2x8_offset128(uint32_t v, int h) {
+  uint32_t m = 0x00030003u, c = 0x43004300u;
+  asm("" : "+s"(m));
+  asm("" : "+v"(c));
+  const uint32_t w = v >> (8 * h);
+  const uint32_t p0 = (w & m) | c;
+  const uint32_t p1 = ((w >> 2) & m) | c;
+  const uint32_t p2 = ((w >> 4) & m) | c;
+  const uint32_t p3 = ((w >> 6) & m) | c;
   const u32x4 r = {p0, p1, p2, p3};
   return __builtin_bit_cast(bf16x8, r);
 }

@@ -52,7 +52,7 @@ template <int FAM>
 __device__ __forceinline__ void epilogue(const KParams& p, const uint8_t* w, int orow, int srow, int n,
                                          typename AccType<FAM>::elem v, float tw) {
   const size_t o = size_t(orow) * p.N + n;
-  if constexpr (FAM == FAM_WNA16) {
+  if constexpr (family_int_groups(FAM)) {
     reinterpret_cast<uint16_t*>(p.y)[o] = f32_to_bf16_rne(v * tw);
   } else if constexpr (FAM == FAM_W8A8) {
     if (p.out_i32) {

@@ -33,6 +33,10 @@ bool pp_only(const Combo& c) {
          c.fam == FAM_W8A16 || c.fam == FAM_F8A16;
 }
 
+// Families with skinny instantiations only (2-bit WnA16: its half-size units do not fit the LDS
+// kernels' whole-unit copies).
+bool skinny_only(const Combo& c) { return c.fam == FAM_WNA2; }
+
 // Activation bytes per 2 k (bf16: 4; 8-bit: 2; 4-bit: 1): the direct-to-LDS kernels address
 // activation rows with 32-bit offsets, so M * K * this / 2 must stay below 2^32.
 uint64_t act_bytes_2k(const Combo& c) {
@@ -51,6 +55,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
   };
   if (rows <= 16) {
+    if (c.fam == FAM_WNA2) return first_fit({28, 13, 0, 1, 2});
     // 8-bit weights with bf16 activations, N=14336 K=4096: 16 waves of 64 channels, two units in
     // flight (M=1 INT8 / FP8: 13.2 / 12.3 us; the 8-wave form 13.5 / 12.6)
     if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) return first_fit({27, 0, 1, 2});
@@ -62,6 +67,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
+    if (c.fam == FAM_WNA2) return first_fit({29, 22, 3, 7, 8});
     if (c.fam == FAM_W8A16) return first_fit({29, 22, 3, 7, 8});   // M=32: 16.0 us (next 18.9)
     if (c.fam == FAM_F8A16) return first_fit({22, 29, 3, 7, 8});   // M=32: 15.8 us (next 16.3)
     if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
@@ -70,6 +76,9 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
+  // 2-bit weights (the small-M kernel at every M): two 32-row blocks, double-buffered (N=14336,
+  // K=4096, M=64 / 128 / 1024: 20.4 / 37.2 / 240 us against 22.4 / 39.2 / 266 with 64-row blocks)
+  if (c.fam == FAM_WNA2) return first_fit({22, 5, 4, 6});
   if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
   if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
   if (c.fam == FAM_FP8B && rows <= 64) return first_fit({29, 15, 8});   // M=64: 31.9 us vs 40.6
@@ -126,6 +135,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_FP8B>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_W8A16)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W8A16>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_WNA2)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_WNA2>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_F8A16)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_F8A16>, grid, dim3(256), 0, s, p);
   else
@@ -196,7 +207,7 @@ int tile_n_of(int kind, int cfg) {
 
 // (kind, cfg) from the table, or kind 0 for the skinny kernel.
 RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
-  if (K % 128 != 0) return {0, 0, 0};
+  if (K % 128 != 0 || skinny_only(c)) return {0, 0, 0};
   const RangeEntry* t;
   int n;
   if (c.fam == FAM_WNA16) {
@@ -258,6 +269,7 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
   if (pp_only(c) && (o.kind == 1 || o.kind == 2)) return false;
+  if (skinny_only(c) && o.kind != 0) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -401,7 +413,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   if (tov.kind == 3) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
-    const bool fits = tov.cfg >= 0 && tov.cfg < n_p && 16 * pc[tov.cfg].mw * pc[tov.cfg].wm == block_m &&
+    const bool fits = !skinny_only(c) && tov.cfg >= 0 && tov.cfg < n_p && 16 * pc[tov.cfg].mw * pc[tov.cfg].wm == block_m &&
                       K % 128 == 0 && N % (16 * pc[tov.cfg].ntw * pc[tov.cfg].wn) == 0 &&
                       pp_lds_bytes(c.fam, tov.cfg) <= 160 * 1024 && uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);
     pl.kind = fits ? 3 : -1;
@@ -414,7 +426,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
   // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
   const bool a32 = uint64_t(T) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);   // 32-bit row offsets
-  if (K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+  if (!skinny_only(c) && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
     // (the 8-bit-activation formats' 32-row tiles do not split into whole-wave copies: skinny)
     static const int pp32[1] = {7}, pp64[2] = {5, 4};
     const int* cands = block_m == 32 ? pp32 : pp64;

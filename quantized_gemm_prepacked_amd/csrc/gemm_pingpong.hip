@@ -532,7 +532,7 @@ int pp_lds_table(int cfg, std::integer_sequence<int, I...>) {
 
 int pp_lds_bytes(int fam, int cfg) {
   constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
-  if (cfg < 0 || cfg >= n) return 1 << 30;
+  if (cfg < 0 || cfg >= n || fam == FAM_WNA2) return 1 << 30;   // (2-bit weights: skinny kernel only)
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);

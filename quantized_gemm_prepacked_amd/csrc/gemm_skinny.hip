@@ -44,6 +44,10 @@ struct SkTraits<FAM_WNA16> {
   static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
 };
 template <>
+struct SkTraits<FAM_WNA2> {
+  static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
+};
+template <>
 struct SkTraits<FAM_W8A8> {
   static constexpr int kRowBytes = 64, kUnitK = 64, kScaleBytes = 0, kZeroBytes = 0, kAScaleBytes = 0;
 };
@@ -175,7 +179,10 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       const size_t unit = (size_t(nt0 + t) * k_units + u) * Sh::WL;
-      bw[buf][r][t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
+      if constexpr (FAM == FAM_WNA2)
+        bw[buf][r][t] = ldg8_stream(w + unit * 512 + 8 * lane);
+      else
+        bw[buf][r][t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
       if constexpr (Sh::WL == 2) bw2[buf][r][t] = ldg16_stream(w + (unit + 1) * kUnitBytes + 16 * lane);
     }
     if constexpr (Sh::SC > 0) {
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
       const int row = 16 * mb + (lane & 15);
       return *reinterpret_cast<const u32x4*>(slot + row * ROWB + 16 * lds_chunk_swizzle(row, chunk, CPR));
     };
-    if constexpr (FAM == FAM_WNA16) {
+    if constexpr (family_int_groups(FAM)) {
       // The group's partial sum_k x*(u - z) is formed as sum_k x*(128 + u) (the offset-128
       // operand costs one bit-select per weight pair) minus (128 + z) * sum_k x; the row sums
       // come from one MFMA against an all-ones operand, shared by the NTW tiles.
@@ -238,7 +245,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
         f32x4 part[MB];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const bf16x8 bv = dequant_int4x8_offset128(bw[buf][r][t][d]);
+          bf16x8 bv;
+          if constexpr (FAM == FAM_WNA2) bv = dequant_uint2x8_offset128(bw[buf][r][t][d >> 1], d & 1);
+          else bv = dequant_int4x8_offset128(bw[buf][r][t][d]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             part[mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv,
@@ -480,6 +489,7 @@ int skinny_lds_bytes(int fam, int cfg) {
   if (cfg < 0 || cfg >= n) return 1 << 30;
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return skinny_lds_table<FAM_WNA16>(cfg, seq);
+  if (fam == FAM_WNA2) return skinny_lds_table<FAM_WNA2>(cfg, seq);
   if (fam == FAM_W8A8) return skinny_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return skinny_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return skinny_lds_table<FAM_W4A8MX>(cfg, seq);
@@ -524,6 +534,8 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
                          hipStream_t s) {
   if (fam == FAM_WNA16) return moe ? launch_skinny_fam<FAM_WNA16, true>(p, cfg, grid, s)
                                    : launch_skinny_fam<FAM_WNA16, false>(p, cfg, grid, s);
+  if (fam == FAM_WNA2) return moe ? launch_skinny_fam<FAM_WNA2, true>(p, cfg, grid, s)
+                                  : launch_skinny_fam<FAM_WNA2, false>(p, cfg, grid, s);
   if (fam == FAM_MXW4A16) return moe ? launch_skinny_fam<FAM_MXW4A16, true>(p, cfg, grid, s)
                                      : launch_skinny_fam<FAM_MXW4A16, false>(p, cfg, grid, s);
   if (moe && fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, true>(p, cfg, grid, s);

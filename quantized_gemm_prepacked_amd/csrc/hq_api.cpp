@@ -65,6 +65,15 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
       c->asym = asym;
       return HQ_OK;
     }
+    case HQ_W_UINT2_ASYM:
+      if (d->group_size != 128 || d->scale_dtype != HQ_SCALE_BF16 || d->has_zero_point != 1 ||
+          d->act_fmt != HQ_ACT_BF16 || c->out_i32)
+        return fail(HQ_ERR_UNSUPPORTED,
+                    "UINT2 weights need group_size 128, BF16 scales, has_zero_point 1, BF16 "
+                    "activations and bf16 output");
+      c->fam = hq::FAM_WNA2;
+      c->asym = true;
+      return HQ_OK;
     case HQ_W_INT8_SYM:
       if (d->act_fmt == HQ_ACT_BF16) {
         if (d->group_size != 0 || d->scale_dtype != HQ_SCALE_FP32 || d->has_zero_point != 0 || c->out_i32)
@@ -155,7 +164,7 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
   if (E <= 0 || E > 65536) return fail(HQ_ERR_INVALID_ARGUMENT, "E=%lld out of range", (long long)E);
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (!wq || !scales || !out) return fail(HQ_ERR_INVALID_ARGUMENT, "wq, scales and out must be non-NULL");
-  if (c.asym && !zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for UINT4_ASYM");
+  if (c.asym && !zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for UINT4_ASYM / UINT2_ASYM");
   if (!c.asym && zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be NULL without zero-points");
   const size_t need = hq::prepacked_bytes(c, E, N, K);
   if (out_bytes < need)
@@ -303,7 +312,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 bool moe_family(const hq::Combo& c) {
   return c.fam == hq::FAM_WNA16 || c.fam == hq::FAM_MXW4A16 || c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8 ||
          c.fam == hq::FAM_FP8B || c.fam == hq::FAM_W8A16 || c.fam == hq::FAM_F8A16 || c.fam == hq::FAM_W4A4 ||
-         c.fam == hq::FAM_W4A8MX;
+         c.fam == hq::FAM_W4A8MX || c.fam == hq::FAM_WNA2;
 }
 
 GroupedWs grouped_ws(const hq::Combo& c, int64_t R, int32_t E, int64_t N, int64_t K) {

@@ -25,6 +25,11 @@
 //     k = 128*kt + 32*(l>>4) + 16*j + b in byte b (0..15),
 //   so a lane's two units cover its lane group's 32 consecutive k of the step, the WNA16 K
 //   order: MFMA d (0..3) of the step takes unit d>>1, bytes 8*(d&1) .. +7.
+//   WNA2 (UINT2 with zero-points, group 128, bf16 activations; v_mfma_f32_16x16x32_bf16 x 4 per
+//   group): a unit is 16 channels x 128 k in 512 bytes (half a 1 KiB unit); lane l holds 8 bytes,
+//   k = 128*kt + 32*(l>>4) + 16*h + c in dword h (0, 1), code c = 2s + e (s = 0..7, e = 0, 1) in
+//   bits 16*e + 2*s .. +1, so (dword >> 2s) & 0x00030003 yields the pair (k 2s, 2s+1) as two
+//   16-bit lanes. Scales and zeros as WNA16's (zeros 0..3 in the 4-bit slots).
 //
 // Regions per expert (each starts at a 256-byte aligned offset; experts are stacked with a
 // 256-byte aligned stride):
@@ -44,8 +49,13 @@ namespace hq {
 // FP8B: block-scaled FP8 W8A8 (e4m3 weights with an fp32 scale per 128 x 128 block, e4m3
 // activations with an fp32 scale per (row, 128 k)); its codes use W8A8's 64-k units.
 // W8A16 / F8A16: INT8 / FP8 e4m3 weights with a per-channel fp32 scale and bf16 activations.
+// WNA2: 2-bit WnA16 (UINT2 codes with zero-points, the WNA16 scale and zero layout).
 enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5, FAM_FP8B = 6,
-              FAM_W8A16 = 7, FAM_F8A16 = 8 };
+              FAM_W8A16 = 7, FAM_F8A16 = 8, FAM_WNA2 = 9 };
+
+// Integer group-wise weights with bf16 activations: group scales and zero-points, the offset-128
+// operand (WNA16, WNA2).
+inline constexpr bool family_int_groups(int f) { return f == FAM_WNA16 || f == FAM_WNA2; }
 
 // 8-bit weight codes in 64-k units
 inline constexpr bool family_8bit_weights(int f) {
@@ -54,10 +64,12 @@ inline constexpr bool family_8bit_weights(int f) {
 
 // bf16 activations (2 bytes per k)
 inline constexpr bool family_bf16_act(int f) {
-  return f == FAM_WNA16 || f == FAM_MXW4A16 || f == FAM_W8A16 || f == FAM_F8A16;
+  return f == FAM_WNA16 || f == FAM_MXW4A16 || f == FAM_W8A16 || f == FAM_F8A16 || f == FAM_WNA2;
 }
 
 constexpr int kUnitBytes = 1024;
+// Bytes of one 16-channel unit of codes (WNA2: 128 k of 2-bit codes).
+inline constexpr int family_unit_bytes(int f) { return f == FAM_WNA2 ? 512 : kUnitBytes; }
 constexpr int kTileN = 16;
 
 inline int family_k_unit(Family f) { return family_8bit_weights(f) ? 64 : 128; }
@@ -84,9 +96,9 @@ inline PackedLayout make_layout(Family fam, bool asym, int64_t N, int64_t K) {
   L.n_tiles = N / kTileN;
   L.k_units = K / family_k_unit(fam);
   L.codes_off = 0;
-  L.codes_bytes = size_t(L.n_tiles) * size_t(L.k_units) * kUnitBytes;
+  L.codes_bytes = size_t(L.n_tiles) * size_t(L.k_units) * family_unit_bytes(fam);
   L.scales_off = align256(L.codes_bytes);
-  if (fam == FAM_WNA16) {
+  if (family_int_groups(fam)) {
     L.scales_bytes = size_t(L.n_tiles) * L.k_units * 16 * 2;
   } else if (fam == FAM_W8A8 || fam == FAM_W8A16 || fam == FAM_F8A16) {
     L.scales_bytes = size_t(N) * 4;
@@ -98,7 +110,7 @@ inline PackedLayout make_layout(Family fam, bool asym, int64_t N, int64_t K) {
     L.scales_bytes = size_t(L.n_tiles) * L.k_units * 64;
   }
   L.zeros_off = align256(L.scales_off + L.scales_bytes);
-  L.zeros_bytes = (fam == FAM_WNA16 && asym) ? size_t(L.n_tiles) * L.k_units * 8 : 0;
+  L.zeros_bytes = (family_int_groups(fam) && asym) ? size_t(L.n_tiles) * L.k_units * 8 : 0;
   L.expert_stride = align256(L.zeros_off + L.zeros_bytes);
   return L;
 }

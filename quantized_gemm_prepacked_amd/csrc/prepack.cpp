@@ -76,6 +76,40 @@ void pack_wna16(const PackedLayout& L, bool sym, const uint8_t* wq, const uint16
   });
 }
 
+// 2-bit codes (layout.h, WNA2): input wq [N, K/4] (code k in bits 2 (k % 4) of byte k / 4);
+// scales and zeros as WNA16's.
+void pack_wna2(const PackedLayout& L, const uint8_t* wq, const uint16_t* scales, const uint8_t* zeros,
+               uint8_t* out) {
+  const int64_t K = L.K, G = K / 128;
+  parallel_for(L.n_tiles, [&](int64_t nt) {
+    for (int64_t kt = 0; kt < L.k_units; ++kt) {
+      uint8_t* unit = out + L.codes_off + (size_t(nt) * L.k_units + kt) * 512;
+      for (int l = 0; l < 64; ++l) {
+        const int64_t n = nt * 16 + (l & 15);
+        const uint8_t* row = wq + size_t(n) * (K / 4);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(unit + 8 * l);
+        for (int h = 0; h < 2; ++h) {
+          uint32_t v = 0;
+          for (int c = 0; c < 16; ++c) {
+            const int64_t k = kt * 128 + 32 * (l >> 4) + 16 * h + c;
+            const uint32_t code = (row[k >> 2] >> (2 * (k & 3))) & 3u;
+            v |= code << (16 * (c & 1) + 2 * (c >> 1));
+          }
+          dst[h] = v;
+        }
+      }
+      uint16_t* sdst = reinterpret_cast<uint16_t*>(out + L.scales_off) + (size_t(nt) * L.k_units + kt) * 16;
+      for (int i = 0; i < 16; ++i) sdst[i] = scales[size_t(nt * 16 + i) * G + kt];
+      uint8_t* zdst = out + L.zeros_off + (size_t(nt) * L.k_units + kt) * 8;
+      for (int i = 0; i < 8; ++i) {
+        const uint8_t lo = zeros[size_t(nt * 16 + 2 * i) * G + kt] & 0x3;
+        const uint8_t hi = zeros[size_t(nt * 16 + 2 * i + 1) * G + kt] & 0x3;
+        zdst[i] = uint8_t(lo | (hi << 4));
+      }
+    }
+  });
+}
+
 void pack_w8a8(const PackedLayout& L, const int8_t* wq, const float* scales, uint8_t* out) {
   const int64_t K = L.K;
   parallel_for(L.n_tiles, [&](int64_t nt) {
@@ -155,6 +189,10 @@ void prepack(const Combo& c, int64_t E, int64_t N, int64_t K, const void* wq,
       pack_wna16(L, !c.asym, static_cast<const uint8_t*>(wq) + e * wq_stride,
                  static_cast<const uint16_t*>(scales) + e * s_stride,
                  c.asym ? static_cast<const uint8_t*>(zeros) + e * s_stride : nullptr, o);
+    } else if (c.fam == FAM_WNA2) {
+      const size_t s_stride = size_t(N) * (K / 128);
+      pack_wna2(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * (K / 4),
+                static_cast<const uint16_t*>(scales) + e * s_stride, static_cast<const uint8_t*>(zeros) + e * s_stride, o);
     } else if (c.fam == FAM_W8A8) {
       pack_w8a8(L, static_cast<const int8_t*>(wq) + e * size_t(N) * K,
                 static_cast<const float*>(scales) + e * size_t(N), o);

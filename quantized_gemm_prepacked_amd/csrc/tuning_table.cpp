@@ -45,6 +45,7 @@ bool parse_family(const std::string& s, Family* f) {
   else if (s == "fp8b") *f = FAM_FP8B;
   else if (s == "w8a16") *f = FAM_W8A16;
   else if (s == "f8a16") *f = FAM_F8A16;
+  else if (s == "wna2") *f = FAM_WNA2;
   else return false;
   return true;
 }

@@ -160,3 +160,16 @@ def test_w8a16_descriptors():
             with pytest.raises(hq.HQError) as ei:
                 hq.hq_gemm(bad, 4, 256, 512, 16, None, 16, 16, stream=0)
             assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
+
+
+def test_w2a16_descriptor():
+    d = hq.DESC_W2A16_ASYM
+    assert hq.hq_prepacked_bytes(d, 1, 256, 512) > 0
+    assert hq.hq_gemm_plan(d, 8192, 256, 512)[0] == 0          # the small-M kernel at every M
+    for bad in (hq.make_desc(hq.HQ_W_UINT2_ASYM, 64, hq.HQ_SCALE_BF16, 1, hq.HQ_ACT_BF16),
+                hq.make_desc(hq.HQ_W_UINT2_ASYM, 128, hq.HQ_SCALE_BF16, 0, hq.HQ_ACT_BF16),
+                hq.make_desc(hq.HQ_W_UINT2_ASYM, 128, hq.HQ_SCALE_BF16, 1, hq.HQ_ACT_INT8_PER_TOKEN)):
+        assert hq.hq_prepacked_bytes(bad, 1, 256, 512) == 0
+    with pytest.raises(hq.HQError):
+        hq.hq_prepack_weights(d, 1, 256, 512, np.zeros((256, 128), np.uint8), np.zeros((256, 4), np.uint16),
+                              None, np.zeros(hq.hq_prepacked_bytes(d, 1, 256, 512), np.uint8))   # zeros missing

@@ -66,3 +66,17 @@ def test_uint2_quantizer_reconstructs_within_half_a_step():
     inside = (w >= lo) & (w <= hi)
     assert inside.mean() > 0.9
     assert np.all(np.abs(deq - w)[inside] <= 0.5 * s[inside] * (1 + 1e-6))
+
+
+def test_moe_gemm_with_2bit_experts_equals_per_token_dense():
+    T, topk, E, N, K = 4, 2, 3, 32, 256
+    x = synth.normal_bf16(synth.rng(73), (T, K))
+    ids = np.array([[0, 2], [1, 0], [2, 2], [1, 1]])
+    ws = {e: dict(synth.make_wna2(990 + e, 1, N, K), bits=2) for e in range(E)}
+    y, _, valid = oracle.ref_moe_gemm(x, ids, lambda e: ws[e], N, E, 128)
+    assert valid.all()
+    for t in range(T):
+        for j in range(topk):
+            w = ws[ids[t, j]]
+            yd, _ = oracle.ref_wna2(x[t:t + 1], w["wq"], w["scales"], w["zeros"], 128)
+            assert np.array_equal(y[t * topk + j], yd[0])

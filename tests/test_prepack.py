@@ -176,3 +176,34 @@ def test_w8a16_roundtrip(fp8):
     wq, s = unpack_w8a16(out, N, K)
     assert np.array_equal(wq, d["wq"].view(np.uint8)) and np.array_equal(s, d["s_ch"])
     assert out.size == _a256(_a256((N // 16) * (K // 64) * 1024) + 4 * N)
+
+
+def unpack_wna2(buf, N, K):
+    """2-bit units of 16 channels x 128 k in 512 bytes: lane l holds two dwords, dword h holds
+    k = 128 kt + 32 (l >> 4) + 16 h + c, code c = 2 s + e in bits 16 e + 2 s; then WNA16's scale
+    and zero regions."""
+    nt_n, kt_n = N // 16, K // 128
+    d = buf[:nt_n * kt_n * 512].view(np.uint32).reshape(nt_n, kt_n, 4, 16, 2)   # nt, kt, g, ch, h
+    codes = np.zeros((N, K), np.uint8)
+    for c in range(16):
+        s, e = c >> 1, c & 1
+        v = ((d >> np.uint32(16 * e + 2 * s)) & np.uint32(3)).astype(np.uint8)     # nt, kt, g, ch, h
+        # k = 128 kt + 32 g + 16 h + c of channel 16 nt + ch
+        codes.reshape(nt_n, 16, kt_n, 4, 2, 16)[..., c] = v.transpose(0, 3, 1, 2, 4)
+    wq = (codes[:, 0::4] | (codes[:, 1::4] << 2) | (codes[:, 2::4] << 4) | (codes[:, 3::4] << 6)).astype(np.uint8)
+    s_off = _a256(nt_n * kt_n * 512)
+    sc = buf[s_off:s_off + nt_n * kt_n * 32].view(np.uint16).reshape(nt_n, kt_n, 16)
+    scales = sc.transpose(0, 2, 1).reshape(N, kt_n)
+    z_off = _a256(s_off + nt_n * kt_n * 32)
+    zb = buf[z_off:z_off + nt_n * kt_n * 8].reshape(nt_n, kt_n, 8)
+    z = np.stack([zb & 0xF, zb >> 4], axis=-1).reshape(nt_n, kt_n, 16).transpose(0, 2, 1).reshape(N, kt_n)
+    return wq, scales, z
+
+
+def test_wna2_roundtrip():
+    N, K = 48, 384
+    d = synth.make_wna2(914, 2, N, K)
+    out = np.zeros(hq.hq_prepacked_bytes(hq.DESC_W2A16_ASYM, 1, N, K), np.uint8)
+    hq.hq_prepack_weights(hq.DESC_W2A16_ASYM, 1, N, K, d["wq"], d["scales"], d["zeros"], out)
+    wq, s, z = unpack_wna2(out, N, K)
+    assert np.array_equal(wq, d["wq"]) and np.array_equal(s, d["scales"]) and np.array_equal(z, d["zeros"])
