@@ -103,6 +103,14 @@ __device__ __forceinline__ bf16x8 dequant_uint2x8_offset128(uint32_t v, int h) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// The offset-128 operand of MFMA d (0..3) of a 128-k group from a lane's packed codes: 4-bit
+// codes hold it in dword d, 2-bit codes in half d & 1 of dword d >> 1.
+template <int FAM>
+__device__ __forceinline__ bf16x8 dequant_offset128(const u32x4& q, int d) {
+  if constexpr (FAM == FAM_WNA2) return dequant_uint2x8_offset128(q[d >> 1], d & 1);
+  else return dequant_int4x8_offset128(q[d]);
+}
+
 // -(128 + z) in all 8 bf16 slots (z in [0, 15]): the constant operand that removes the offset of
 // dequant_int4x8_offset128 inside an MFMA chain.
 __device__ __forceinline__ bf16x8 neg_offset_bf16x8(uint32_t z) {

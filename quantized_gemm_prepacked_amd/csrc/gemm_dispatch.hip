@@ -30,12 +30,8 @@ int k_unit(const Combo& c) {
 // instantiation).
 bool pp_only(const Combo& c) {
   return c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B ||
-         c.fam == FAM_W8A16 || c.fam == FAM_F8A16;
+         c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_WNA2;
 }
-
-// Families with skinny instantiations only (2-bit WnA16: its half-size units do not fit the LDS
-// kernels' whole-unit copies).
-bool skinny_only(const Combo& c) { return c.fam == FAM_WNA2; }
 
 // Activation bytes per 2 k (bf16: 4; 8-bit: 2; 4-bit: 1): the direct-to-LDS kernels address
 // activation rows with 32-bit offsets, so M * K * this / 2 must stay below 2^32.
@@ -76,8 +72,8 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
-  // 2-bit weights (the small-M kernel at every M): two 32-row blocks, double-buffered (N=14336,
-  // K=4096, M=64 / 128 / 1024: 20.4 / 37.2 / 240 us against 22.4 / 39.2 / 266 with 64-row blocks)
+  // 2-bit weights: two 32-row blocks, double-buffered (N=14336, K=4096, M=64 / 128: 20.4 / 37.2
+  // us against 22.4 / 39.2 with 64-row blocks)
   if (c.fam == FAM_WNA2) return first_fit({22, 5, 4, 6});
   if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
   if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
@@ -190,6 +186,11 @@ constexpr RangeEntry kFp8bTable[] = {{64, 0, 0}, {kInf, 3, 10}};
 // M=256 / 1024 / 8192 at 45.7 / 171.7 / 1161 us and 40.4 / 155.0 / 1067 us, against 55.2 / 210.9
 // / 1364 and 41.9 / 158.9 / 1133 for waves of 32 x 64.
 constexpr RangeEntry kW8a16Table[] = {{128, 0, 0}, {kInf, 3, 3}};
+// 2-bit WnA16 on the ping-pong kernel's 256-wide tiles (the only ones whose half-unit weight copies
+// split over the eight waves), measured at N=14336, K=4096: skinny to M=128 (36.8 us; ping-pong
+// 52.1), 64 x 256 with four slots to 512 (M=256: 49.5 us against 53.1 with three), 128 x 256
+// beyond (M=1024 / 8192: 133 / 916 us; the skinny kernel 242 / 1834)
+constexpr RangeEntry kWna2Table[] = {{128, 0, 0}, {512, 3, 13}, {kInf, 3, 0}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -207,7 +208,7 @@ int tile_n_of(int kind, int cfg) {
 
 // (kind, cfg) from the table, or kind 0 for the skinny kernel.
 RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
-  if (K % 128 != 0 || skinny_only(c)) return {0, 0, 0};
+  if (K % 128 != 0) return {0, 0, 0};
   const RangeEntry* t;
   int n;
   if (c.fam == FAM_WNA16) {
@@ -222,6 +223,9 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_MXW4A16) {
     t = kMxW4a16Table;
     n = int(sizeof(kMxW4a16Table) / sizeof(kMxW4a16Table[0]));
+  } else if (c.fam == FAM_WNA2) {
+    t = kWna2Table;
+    n = int(sizeof(kWna2Table) / sizeof(kWna2Table[0]));
   } else if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) {
     t = kW8a16Table;
     n = int(sizeof(kW8a16Table) / sizeof(kW8a16Table[0]));
@@ -269,7 +273,6 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
   }
   if (pp_only(c) && (o.kind == 1 || o.kind == 2)) return false;
-  if (skinny_only(c) && o.kind != 0) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -365,7 +368,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
     pl.cfg = pick.cfg;
     pl.split = 1;
     // WNA16: the activation group sums of the offset term
-    pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(M, K) : 0;
+    pl.ws_bytes = family_int_groups(c.fam) ? group_sums_split_bytes(M, K) : 0;
     return pl;
   }
   pl.kind = 0;
@@ -413,12 +416,12 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   if (tov.kind == 3) {
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
-    const bool fits = !skinny_only(c) && tov.cfg >= 0 && tov.cfg < n_p && 16 * pc[tov.cfg].mw * pc[tov.cfg].wm == block_m &&
+    const bool fits = tov.cfg >= 0 && tov.cfg < n_p && 16 * pc[tov.cfg].mw * pc[tov.cfg].wm == block_m &&
                       K % 128 == 0 && N % (16 * pc[tov.cfg].ntw * pc[tov.cfg].wn) == 0 &&
                       pp_lds_bytes(c.fam, tov.cfg) <= 160 * 1024 && uint64_t(T) * uint64_t(K) * 2u < (uint64_t(1) << 32);
     pl.kind = fits ? 3 : -1;
     pl.cfg = tov.cfg;
-    pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(T, K) : 0;
+    pl.ws_bytes = family_int_groups(c.fam) ? group_sums_split_bytes(T, K) : 0;
     return pl;
   }
   // Blocks of 32 and 64 rows: the ping-pong kernel with one expert block per tile row, its
@@ -426,7 +429,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
   // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
   const bool a32 = uint64_t(T) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);   // 32-bit row offsets
-  if (!skinny_only(c) && K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+  if (K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
     // (the 8-bit-activation formats' 32-row tiles do not split into whole-wave copies: skinny)
     static const int pp32[1] = {7}, pp64[2] = {5, 4};
     const int* cands = block_m == 32 ? pp32 : pp64;
@@ -439,7 +442,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
           16 * t.mw * t.wm == block_m) {
         pl.kind = 3;
         pl.cfg = cands[j];
-        pl.ws_bytes = c.fam == FAM_WNA16 ? group_sums_split_bytes(T, K) : 0;  // WNA16 offset term
+        pl.ws_bytes = family_int_groups(c.fam) ? group_sums_split_bytes(T, K) : 0;  // WNA16 offset term
         return pl;
       }
     }
@@ -509,7 +512,7 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.split = 1;
     p.units_per_split = p.k_units;
     p.M = int(call.M);
-    if (c.fam == FAM_WNA16) {
+    if (family_int_groups(c.fam)) {
       hipError_t e = launch_group_sums_split(p.a, p.M, p.K, call.ws, call.stream);
       if (e != hipSuccess) return e;
     }
@@ -532,7 +535,7 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.topk_weights = call.topk_weights;
     p.topk = call.topk;
     p.E = call.E;
-    if (c.fam == FAM_WNA16) {
+    if (family_int_groups(c.fam)) {
       hipError_t e = launch_group_sums_split(p.a, int(call.T), p.K, call.ws, call.stream);
       if (e != hipSuccess) return e;
     }
@@ -560,7 +563,7 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     p.split = 1;
     p.units_per_split = p.k_units;
     const int tiles_n = int(call.N / bn);
-    if (c.fam == FAM_WNA16) {
+    if (family_int_groups(c.fam)) {
       hipError_t e = launch_group_sums_split(p.a, int(moe ? call.T : call.M), p.K, call.ws, call.stream);
       if (e != hipSuccess) return e;
     }

@@ -46,6 +46,13 @@ struct PPTraits<FAM_WNA16> {
   static constexpr int kAScaleBytes = 0;
 };
 template <>
+struct PPTraits<FAM_WNA2> {   // 2-bit codes: 512 bytes per tile and step (half a unit)
+  static constexpr int kRowBytes = 256;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 32;   // 16 bf16 group scales
+  static constexpr int kAScaleBytes = 0;
+};
+template <>
 struct PPTraits<FAM_W8A8> {
   static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 2;
@@ -122,7 +129,8 @@ struct PPShape {
   static constexpr int A_BYTES = BM * RB;
   static constexpr int NT = BN / 16;
   static constexpr int UPS = PPTraits<FAM>::kUnitsPerStep;
-  static constexpr int B_BYTES = NT * UPS * kUnitBytes;
+  static constexpr int TILE_STEP_BYTES = UPS * family_unit_bytes(FAM);   // weight bytes per tile and step
+  static constexpr int B_BYTES = NT * TILE_STEP_BYTES;
   static constexpr int MPT = PPTraits<FAM>::kMetaPerTile;
   static constexpr int META_BYTES = NT * MPT;
   static constexpr int META_PER_WAVE = META_BYTES / 8;
@@ -132,12 +140,12 @@ struct PPShape {
   static constexpr int STAGE = (A_BYTES + B_BYTES + META_BYTES + ASC_BYTES + 1023) / 1024 * 1024;
   static constexpr int LDS = kStages * STAGE;
   static constexpr int A_INSTR = A_BYTES / 1024 / 8;
-  static constexpr int B_INSTR = NT * UPS / 8;
+  static constexpr int B_INSTR = B_BYTES / 1024 / 8;
   static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0) + (ASC_BYTES ? 1 : 0);
   // the copies split evenly over the eight waves (shapes that do not are never launched)
   // the copies split evenly over the eight waves (shapes that do not are never launched), and
   // the copies of S - 2 steps in flight fit the 6-bit vmcnt
-  static constexpr bool kValid = A_BYTES % (1024 * 8) == 0 && (NT * UPS) % 8 == 0 &&
+  static constexpr bool kValid = A_BYTES % (1024 * 8) == 0 && B_BYTES % (1024 * 8) == 0 &&
                                  META_BYTES % (16 * 8) == 0 && META_LANES <= 64 &&
                                  (ASC_BYTES == 0 || (BM % 8 == 0 && BM / 8 <= 64)) &&
                                  (kStages - 2) * INSTR < 64;
@@ -240,8 +248,14 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 #pragma unroll
     for (int j = 0; j < Sh::B_INSTR; ++j) {
       const int u = wave * Sh::B_INSTR + j;
-      const size_t unit = size_t(nt_wg + u / UPS) * p.k_units + size_t(ks) * UPS + (u % UPS);
-      lds_dma16(w + unit * kUnitBytes + 16 * lane, sb + u * 1024);
+      if constexpr (FAM == FAM_WNA2) {
+        // one copy moves the step's 512 bytes of tiles 2u (lanes 0-31) and 2u + 1 (lanes 32-63)
+        const size_t unit = size_t(nt_wg + 2 * u + (lane >> 5)) * p.k_units + size_t(ks);
+        lds_dma16(w + unit * 512 + 16 * (lane & 31), sb + u * 1024);
+      } else {
+        const size_t unit = size_t(nt_wg + u / UPS) * p.k_units + size_t(ks) * UPS + (u % UPS);
+        lds_dma16(w + unit * kUnitBytes + 16 * lane, sb + u * 1024);
+      }
     }
     if constexpr (Sh::META_BYTES > 0) {
       // lanes past META_LANES skip the copy (a direct-to-LDS load writes lane i at base + 16 i);
@@ -261,8 +275,14 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     return *reinterpret_cast<const u32x4*>(st + r * RB + lds_chunk_swizzle(r, chunk, CPR) * 16);
   };
   auto read_b = [&](const uint8_t* st, int t, int q) -> u32x4 {
-    const int u = (wn * NTW + t) * UPS + q;
-    return *reinterpret_cast<const u32x4*>(st + Sh::A_BYTES + u * 1024 + 16 * lane);
+    if constexpr (FAM == FAM_WNA2) {   // 8 bytes per lane of the tile's 512
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = *reinterpret_cast<const u32x2*>(st + Sh::A_BYTES + (wn * NTW + t) * 512 + 8 * lane);
+      return u32x4{v[0], v[1], 0u, 0u};
+    } else {
+      const int u = (wn * NTW + t) * UPS + q;
+      return *reinterpret_cast<const u32x4*>(st + Sh::A_BYTES + u * 1024 + 16 * lane);
+    }
   };
 
   Acc acc[MW][NTW];
@@ -310,7 +330,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 #pragma unroll
       for (int q = 0; q < NB; ++q) bq[t][q] = read_b(st, t, q);
       const int tw = wn * NTW + t;
-      if constexpr (FAM == FAM_WNA16)
+      if constexpr (family_int_groups(FAM))
         meta[t] = *reinterpret_cast<const uint16_t*>(sm + tw * 32 + 2 * (lane & 15));
       else if constexpr (FAM == FAM_W4A8 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX || FAM == FAM_MXW4A16)
         meta[t] = sm[tw * 64 + lane];
@@ -320,13 +340,13 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   };
 
   auto compute_phase = [&]() {
-    if constexpr (FAM == FAM_WNA16) {
+    if constexpr (family_int_groups(FAM)) {
       // Software-pipelined over the channel tiles: while the MFMAs of tile t run, the VALU
       // dequantizes tile t + 1 and applies the group scale to tile t - 1's partial sums.
       bf16x8 bw[2][4];
       f32x4 part[2][MW];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) bw[0][d] = dequant_int4x8_offset128(bq[0][0][d]);
+      for (int d = 0; d < 4; ++d) bw[0][d] = dequant_offset128<FAM>(bq[0][0], d);
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
         const int cur = t & 1;
@@ -338,7 +358,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
                                       d == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : part[cur][mb]);
         if (t + 1 < NTW) {
 #pragma unroll
-          for (int d = 0; d < 4; ++d) bw[cur ^ 1][d] = dequant_int4x8_offset128(bq[t + 1][0][d]);
+          for (int d = 0; d < 4; ++d) bw[cur ^ 1][d] = dequant_offset128<FAM>(bq[t + 1][0], d);
         }
         if (t > 0) {
           const float s = __uint_as_float(meta[t - 1] << 16);
@@ -463,7 +483,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   }
 
   const int row_base = row0 + wm * 16 * MW;
-  if constexpr (FAM == FAM_WNA16) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
+  if constexpr (family_int_groups(FAM)) wna16_offset_contraction<MW, NTW, MOE>(p, w, acc, row_base, nt0, lane);
   store_tile<FAM, MOE, MW, NTW>(p, w, acc, row_base, nt0, lane);
 }
 
@@ -532,9 +552,10 @@ int pp_lds_table(int cfg, std::integer_sequence<int, I...>) {
 
 int pp_lds_bytes(int fam, int cfg) {
   constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
-  if (cfg < 0 || cfg >= n || fam == FAM_WNA2) return 1 << 30;   // (2-bit weights: skinny kernel only)
+  if (cfg < 0 || cfg >= n) return 1 << 30;
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
+  if (fam == FAM_WNA2) return pp_lds_table<FAM_WNA2>(cfg, seq);
   if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return pp_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return pp_lds_table<FAM_W4A8MX>(cfg, seq);
@@ -577,6 +598,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   auto seq = std::make_integer_sequence<int, n>{};
   if (moe) {
     if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_WNA2) return launch_pp_fam<FAM_WNA2, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W4A8) return launch_pp_fam<FAM_W4A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
@@ -588,6 +610,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
     return hipErrorInvalidValue;
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_WNA2) return launch_pp_fam<FAM_WNA2, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);

@@ -136,7 +136,7 @@ __device__ __forceinline__ void store_tile(const KParams& p, const uint8_t* w,
         if (o < 0) continue;
         const size_t idx = size_t(o) * p.N + (nt0 + t) * 16 + (lane & 15);
         const auto v = acc[mb][t][i];
-        if constexpr (FAM == FAM_WNA16) {
+        if constexpr (family_int_groups(FAM)) {
           reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * tw[mb][i]);
         } else if constexpr (FAM == FAM_W8A8) {
           if (p.out_i32) reinterpret_cast<int*>(p.y)[idx] = v;

@@ -165,7 +165,9 @@ def test_w8a16_descriptors():
 def test_w2a16_descriptor():
     d = hq.DESC_W2A16_ASYM
     assert hq.hq_prepacked_bytes(d, 1, 256, 512) > 0
-    assert hq.hq_gemm_plan(d, 8192, 256, 512)[0] == 0          # the small-M kernel at every M
+    assert hq.hq_gemm_plan(d, 8, 256, 512)[0] == 0               # small M: the skinny kernel
+    assert hq.hq_gemm_plan(d, 8192, 256, 512)[0:2] == (3, 0)     # large M: ping-pong 128 x 256
+    assert hq.hq_gemm_plan(d, 8192, 384, 512)[0] == 0            # no 256-wide tile divides N
     for bad in (hq.make_desc(hq.HQ_W_UINT2_ASYM, 64, hq.HQ_SCALE_BF16, 1, hq.HQ_ACT_BF16),
                 hq.make_desc(hq.HQ_W_UINT2_ASYM, 128, hq.HQ_SCALE_BF16, 0, hq.HQ_ACT_BF16),
                 hq.make_desc(hq.HQ_W_UINT2_ASYM, 128, hq.HQ_SCALE_BF16, 1, hq.HQ_ACT_INT8_PER_TOKEN)):

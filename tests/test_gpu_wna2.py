@@ -25,8 +25,9 @@ def _run(d, M, N, K):
 @pytest.mark.parametrize("M,N,K", [
     (1, 512, 4096), (3, 272, 384), (16, 64, 128), (32, 256, 1024), (64, 512, 512),
     (1, 64, 8192),      # 4 workgroups: K split across workgroups, then the reduction launch
-    (200, 256, 640),    # several 64-row blocks, ragged M
-    (1000, 400, 512),
+    (200, 256, 640),    # ping-pong 64 x 256 (half-unit weight copies), ragged M
+    (300, 512, 1024),   # ping-pong 128 x 256
+    (1000, 400, 512),   # no 256-wide tile divides N: skinny
 ])
 def test_wna2_small(M, N, K):
     say(f"[wna2] M={M} N={N} K={K}")
@@ -36,7 +37,7 @@ def test_wna2_small(M, N, K):
     check_float(y, ref, "wna2")
 
 
-@pytest.mark.parametrize("M", [1, 16, 128])
+@pytest.mark.parametrize("M", [1, 16, 128, 8192])
 def test_wna2_full_size_sampled(M):
     N, K = 14336, 4096
     say(f"[wna2 full] M={M}")
@@ -50,23 +51,26 @@ def test_wna2_full_size_sampled(M):
 
 
 def test_wna2_every_kernel_configuration(monkeypatch):
-    M, N, K = 40, 512, 768
+    """Every skinny and ping-pong configuration that fits (the ping-pong kernel's 128-wide tiles
+    do not: their half-unit copies do not split over eight waves)."""
+    M, N, K = 96, 512, 768
     d = synth.make_wna2(1601, M, N, K)
     w = prepack(D, 1, N, K, d["wq"], d["scales"], d["zeros"])
     ref, _ = oracle.ref_wna2(d["x"], d["wq"], d["scales"], d["zeros"], 128)
-    ran = 0
-    for cfg in range(hq.hq_kernel_config_count(0)):
-        monkeypatch.setenv("HQ_TUNE", f"kind=0,cfg={cfg},split=1")
-        try:
-            hq.hq_gemm_plan(D, M, N, K)
-        except hq.HQError:
-            continue
-        say(f"[wna2] skinny cfg={cfg}")
-        y = gemm(D, M, N, K, to_dev(d["x"]), None, w)
-        check_float(y, ref, f"wna2 cfg={cfg}")
-        ran += 1
-    assert ran >= 20
-    monkeypatch.setenv("HQ_TUNE", "kind=3,cfg=0,split=1")     # no LDS-kernel instantiation: refused
+    ran = {0: 0, 3: 0}
+    for kind in (0, 3):
+        for cfg in range(hq.hq_kernel_config_count(kind)):
+            monkeypatch.setenv("HQ_TUNE", f"kind={kind},cfg={cfg},split=1")
+            try:
+                hq.hq_gemm_plan(D, M, N, K)
+            except hq.HQError:
+                continue
+            say(f"[wna2] kind={kind} cfg={cfg}")
+            y = gemm(D, M, N, K, to_dev(d["x"]), None, w)
+            check_float(y, ref, f"wna2 kind={kind} cfg={cfg}")
+            ran[kind] += 1
+    assert ran[0] >= 20 and ran[3] >= 4
+    monkeypatch.setenv("HQ_TUNE", "kind=3,cfg=2,split=1")     # 128 x 128: refused
     with pytest.raises(hq.HQError):
         hq.hq_gemm_plan(D, M, N, K)
 
