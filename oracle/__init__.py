@@ -33,7 +33,7 @@ from .gemm import (  # noqa: F401
     ref_w8a16, dequant_wna2, ref_wna2,
 )
 from .moe import (  # noqa: F401
-    ref_moe_align, ref_moe_gemm, ref_moe_gemm_q, ref_moe_gemm_fp8_block, ref_moe_gemm_mx, ref_grouped_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer,
+    ref_moe_align, ref_moe_gemm, ref_moe_gemm_q, ref_moe_gemm_fp8_block, ref_moe_gemm_mx, ref_grouped_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer, ref_moe_layer_w4a8,
 )
 from .actquant import (  # noqa: F401
     encode_e4m3, quantize_per_token, encode_e2m1, quantize_mxfp4_act, quantize_mxfp8_act,

@@ -283,3 +283,28 @@ def ref_moe_layer(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_weights: np.nda
                           topk_weights=np.asarray(topk_weights).reshape(-1, 1)))
     out = pick(ref_moe_combine(d, ids, E))
     return {"gate_up": gu, "act": act, "down": d, "out": out}
+
+
+def ref_moe_layer_w4a8(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
+                       gate_up_weights, down_weights, I: int, H: int, E: int):
+    """The MoE layer with MXFP4 experts and tokenwise FP8 activations -- the page's end-to-end
+    W4A8 setting (section "End-to-end inference performance": the model's MXFP4 weights kept,
+    activations quantized per token to FP8). Per routed row (t, k) with expert e:
+        xq, xs = per-token e4m3 quantization of x            (each token row)
+        gu  = bf16(xs[t] * xq[t] . Wgu_e^T)
+        a   = bf16(silu(gu[:I]) * gu[I:])
+        aq, as = per-token e4m3 quantization of a           (each routed row)
+        d   = bf16(w[t, k] * as[r] * aq[r] . Wd_e^T)
+        out[t] = bf16(sum_k d)
+    Stages as in ref_moe_layer, with the quantizer of actquant.quantize_per_token before each
+    GEMM. Returns the bf16 bits of every stage and the activation codes and scales."""
+    from .actquant import quantize_per_token
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    xq, xs = quantize_per_token(x_bf16, "e4m3")
+    gu = ref_moe_gemm_q(xq, xs, ids, gate_up_weights, 2 * I, E, "e4m3")[1]
+    act = ref_silu_mul(gu)[1]
+    aq, as_ = quantize_per_token(act, "e4m3")
+    d = ref_moe_gemm_q(aq, as_, ids.reshape(-1, 1), down_weights, H, E, "e4m3",
+                       topk_weights=np.asarray(topk_weights).reshape(-1, 1))[1]
+    out = ref_moe_combine(d, ids, E)[1]
+    return {"xq": xq, "xs": xs, "gate_up": gu, "act": act, "aq": aq, "as": as_, "down": d, "out": out}

@@ -83,3 +83,41 @@ def test_layer_matches_scalar_loops():
     assert np.allclose(exact["out"], brute, rtol=1e-12, atol=1e-12 * np.abs(brute).max())
     # the bf16 boundaries move the result by rounding noise only: a few bf16 ulps at most
     assert np.abs(decode_bf16(ref["out"]) - exact["out"]).max() <= 2.0 ** -5 * np.abs(exact["out"]).max()
+
+
+def test_w4a8_layer_with_one_expert_is_the_dense_chain():
+    """E = 1, top-1: every stage of the W4A8 layer is the dense chain quantize -> W4A8 GEMM ->
+    SiLU*mul -> quantize -> W4A8 GEMM (router weight 1) computed with the dense oracles."""
+    T, H, I = 6, 256, 128
+    x = synth.normal_bf16(synth.rng(81), (T, H))
+    gu_w = synth.make_moe_weights_expert_mx(82, 0, 2 * I, H)
+    dn_w = synth.make_moe_weights_expert_mx(83, 0, H, I)
+    ids = np.zeros((T, 1), np.int64)
+    tw = np.ones((T, 1), np.float32)
+    r = oracle.ref_moe_layer_w4a8(x, ids, tw, lambda e: gu_w, lambda e: dn_w, I, H, 1)
+    xq, xs = oracle.quantize_per_token(x, "e4m3")
+    _, gu = oracle.ref_w4a8(xq, xs, gu_w["wq"], gu_w["scales"])
+    _, act = oracle.ref_silu_mul(gu)
+    aq, as_ = oracle.quantize_per_token(act, "e4m3")
+    _, dn = oracle.ref_w4a8(aq, as_, dn_w["wq"], dn_w["scales"])
+    assert np.array_equal(r["gate_up"], gu) and np.array_equal(r["act"], act)
+    assert np.array_equal(r["down"], dn) and np.array_equal(r["out"], dn)
+    assert np.array_equal(r["xq"], xq) and np.array_equal(r["aq"], aq)
+
+
+def test_w4a8_layer_routes_each_row_to_its_expert():
+    T, topk, E, H, I = 5, 2, 3, 128, 64
+    x = synth.normal_bf16(synth.rng(84), (T, H))
+    ids = np.array([[0, 2], [1, 0], [2, 2], [1, 1], [0, 1]])
+    tw = synth.rng(85).random((T, topk)).astype(np.float32)
+    gw = {e: synth.make_moe_weights_expert_mx(86, e, 2 * I, H) for e in range(E)}
+    dw = {e: synth.make_moe_weights_expert_mx(87, e, H, I) for e in range(E)}
+    r = oracle.ref_moe_layer_w4a8(x, ids, tw, lambda e: gw[e], lambda e: dw[e], I, H, E)
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            _, gu = oracle.ref_w4a8(r["xq"][t:t + 1], r["xs"][t:t + 1], gw[e]["wq"], gw[e]["scales"])
+            assert np.array_equal(r["gate_up"][t * topk + j], gu[0])
+            y, _ = oracle.ref_w4a8(r["aq"][t * topk + j:t * topk + j + 1], r["as"][t * topk + j:t * topk + j + 1],
+                                   dw[e]["wq"], dw[e]["scales"])
+            assert np.array_equal(r["down"][t * topk + j], oracle.round_to_bf16(y[0] * np.float64(tw[t, j])))
