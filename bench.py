@@ -5,7 +5,7 @@ Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
 --config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | w2a16 | moe | moe_mx | moe_fp8b |
-moe_layer.
+moe_layer | moe_layer_w4a8.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
 microbenchmarks": M over powers of two, kernels warmed up and timed independently with cold
@@ -567,11 +567,13 @@ MOE_LAYER = dict(name="MoE layer W4A16 (DeepSeek-V3-shaped: gate_up, SiLU*mul, D
                  E=256, topk=8, H=7168, I=2048, Ts=[1, 32, 512, 4096], cfg=5)
 
 
-def run_moe_layer(args):
+def run_moe_layer(args, w4a8=False):
     """One MoE layer per T: token sort -> gate_up grouped GEMM [T*8, 4096] -> SiLU*mul ->
     Down grouped GEMM [T*8, 7168] with router weights -> top-k combine. The Humming
     announcement times MoE as gate_up plus Down (section "Results: kernel microbenchmarks").
-    tokens/s = T / (one layer's time); each stage is also timed on its own."""
+    tokens/s = T / (one layer's time); each stage is also timed on its own. w4a8: MXFP4 experts
+    with tokenwise FP8 activations (the announcement's end-to-end W4A8 setting): the tokens and
+    the SiLU output are quantized per row to e4m3 (two more timed stages) before the GEMMs."""
     import numpy as np
     import torch
 
@@ -580,7 +582,10 @@ def run_moe_layer(args):
 
     E, topk, H, I, Ts, cfg = (MOE_LAYER[k] for k in ("E", "topk", "H", "I", "Ts", "cfg"))
     dev = torch.device("cuda:0")
-    desc = hq.DESC_W4A16_SYM
+    desc = hq.DESC_W4A8_MXFP4 if w4a8 else hq.DESC_W4A16_SYM
+    name = MOE_LAYER["name"].replace("W4A16", "W4A8-MXFP4, tokenwise FP8 activations") if w4a8 else MOE_LAYER["name"]
+    gen = _random_mxfp4_expert if w4a8 else synth.random_int4_sym_expert
+    peak = "fp8" if w4a8 else "bf16"
     n_copies = 4                      # > 256 MB Infinity Cache between reuses even at T = 1
     g = synth.rng(cfg, 0)
     std = {}
@@ -590,14 +595,14 @@ def run_moe_layer(args):
         w0 = torch.empty(stride * E, dtype=torch.uint8, device=dev)
         host = np.zeros(stride, np.uint8)
         for e in range(E):
-            d = synth.random_int4_sym_expert(g, N, K)
+            d = gen(g, N, K)
             if e < 16:
                 std[(tag, e)] = d
             hq.hq_prepack_weights(desc, 1, N, K, d["wq"], d["scales"], None, host)
             w0[e * stride:(e + 1) * stride].copy_(torch.from_numpy(host))
         return [w0] + [w0.clone() for _ in range(n_copies - 1)], stride
 
-    log(f"[bench] {MOE_LAYER['name']}: preparing {E} gate_up and {E} Down experts (random INT4 codes)")
+    log(f"[bench] {name}: preparing {E} gate_up and {E} Down experts (random codes)")
     w_gu, st_gu = experts(2 * I, H, "gu")
     log("[bench] gate_up experts ready")
     w_dn, st_dn = experts(H, I, "dn")
@@ -619,6 +624,8 @@ def run_moe_layer(args):
             bexp=torch.empty(max(cap // bm, 1), dtype=torch.int32, device=dev),
             offs=torch.empty(E + 1, dtype=torch.int32, device=dev),
             npad=torch.empty(1, dtype=torch.int32, device=dev),
+            xq=torch.empty((T, H), dtype=torch.uint8, device=dev), xs=torch.empty(T, dtype=torch.float32, device=dev),
+            aq=torch.empty((R, I), dtype=torch.uint8, device=dev), as_=torch.empty(R, dtype=torch.float32, device=dev),
             gu=torch.empty((R, 2 * I), dtype=torch.int16, device=dev),
             act=torch.empty((R, I), dtype=torch.int16, device=dev),
             dn=torch.empty((R, H), dtype=torch.int16, device=dev),
@@ -633,11 +640,20 @@ def run_moe_layer(args):
         hq.hq_moe_align(s["ids"], T, topk, E, s["bm"], s["sorted"], s["bexp"], s["offs"], s["npad"],
                         None, 0, None)
 
+    def quant_x(T):
+        s = state[T]
+        hq.hq_quantize_activations(hq.HQ_ACT_FP8E4M3_PER_TOKEN, T, H, s["x"], s["xq"], s["xs"], None)
+
+    def quant_act(T):
+        s = state[T]
+        hq.hq_quantize_activations(hq.HQ_ACT_FP8E4M3_PER_TOKEN, T * topk, I, s["act"], s["aq"], s["as_"], None)
+
     def gate_up(T):
         s = state[T]
         w = w_gu[ctr[0] % n_copies]
         ctr[0] += 1
-        hq.hq_moe_grouped_gemm(desc, T, topk, E, 2 * I, H, s["x"], None, w, s["sorted"], s["bexp"],
+        a, sa = (s["xq"], s["xs"]) if w4a8 else (s["x"], None)
+        hq.hq_moe_grouped_gemm(desc, T, topk, E, 2 * I, H, a, sa, w, s["sorted"], s["bexp"],
                                s["npad"], s["bm"], None, s["gu"], s["ws"], s["ws1"], None)
 
     def silu(T):
@@ -648,14 +664,19 @@ def run_moe_layer(args):
         s = state[T]
         w = w_dn[ctr[1] % n_copies]
         ctr[1] += 1
-        hq.hq_moe_grouped_gemm(desc, T * topk, 1, E, H, I, s["act"], None, w, s["sorted"], s["bexp"],
+        a, sa = (s["aq"], s["as_"]) if w4a8 else (s["act"], None)
+        hq.hq_moe_grouped_gemm(desc, T * topk, 1, E, H, I, a, sa, w, s["sorted"], s["bexp"],
                                s["npad"], s["bm"], s["tw"], s["dn"], s["ws"], s["ws2"], None)
 
     def combine(T):
         s = state[T]
         hq.hq_moe_combine(T, topk, E, H, s["ids"], s["dn"], s["out"], None)
 
-    stages = {"align": align, "gate_up": gate_up, "silu_mul": silu, "down": down, "combine": combine}
+    if w4a8:
+        stages = {"align": align, "quant_x": quant_x, "gate_up": gate_up, "silu_mul": silu,
+                  "quant_act": quant_act, "down": down, "combine": combine}
+    else:
+        stages = {"align": align, "gate_up": gate_up, "silu_mul": silu, "down": down, "combine": combine}
 
     def layer(T):
         for f in stages.values():
@@ -699,9 +720,9 @@ def run_moe_layer(args):
         pt = {}
         for n, (N, K, st) in (("gate_up", (2 * I, H, st_gu)), ("down", (H, I, st_dn))):
             fl = 2.0 * R * N * K
-            by = s["active"] * st + R * K * 2 + R * N * 2
+            by = s["active"] * st + (R * (K + 4) if w4a8 else R * K * 2) + R * N * 2
             tf, gbs = fl / (us[n] * 1e-6) / 1e12, by / (us[n] * 1e-6) / 1e9
-            fc, fm = tf / PEAK_TFLOPS["bf16"], gbs / HBM_PEAK_GBS
+            fc, fm = tf / PEAK_TFLOPS[peak], gbs / HBM_PEAK_GBS
             pt[n] = {"us": round(us[n], 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
                      "bound": "hbm" if fm >= fc else "mfma", "frac": round(max(fc, fm), 4)}
         sweep.append({"T": T, "launches_per_graph": reps[T], "block_m": s["bm"], "active_experts": s["active"],
@@ -714,18 +735,19 @@ def run_moe_layer(args):
                        key=lambda k: next(r for r in sweep if r["T"] == k[0])["gemms"][k[1]]["us"])
     d = next(r for r in sweep if r["T"] == dom_T)["gemms"][dom_n]
     if d["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(d["tflops"] / PEAK_TFLOPS["bf16"], 4)}
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": PEAK_TFLOPS[peak], "unit": "TFLOP/s",
+                "frac": round(d["tflops"] / PEAK_TFLOPS[peak], 4)}
     else:
         roof = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(d["gbps"] / HBM_PEAK_GBS, 4)}
-    roof.update(traffic=measured_traffic("moe_layer", f"{dom_n} T={dom_T}"), kernel=f"{dom_n} grouped GEMM T={dom_T}")
+    roof.update(traffic=measured_traffic("moe_layer_w4a8" if w4a8 else "moe_layer", f"{dom_n} T={dom_T}"),
+                kernel=f"{dom_n} grouped GEMM T={dom_T}")
     line = {
         "metric": METRIC, "value": round(tot_tok / tot_t, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": peak,
         "data": "synthetic",
-        "config": {"workload": MOE_LAYER["name"], "E": E, "topk": topk, "H": H, "I": I, "T": Ts,
+        "config": {"workload": name, "E": E, "topk": topk, "H": H, "I": I, "T": Ts,
                    "routing": "N(0,1) logits + Zipf(1.1) log-prior, softmax top-8"},
         "roofline": roof, "sweep": sweep, "cpu_baseline": None,
     }
@@ -738,12 +760,16 @@ def run_moe_layer(args):
         gu_w, dn_w = {}, {}
         for tag, (N, K), dst in (("gu", (2 * I, H), gu_w), ("dn", (H, I), dn_w)):
             for e in range(E):           # regenerate the same random experts in order
-                dd = synth.random_int4_sym_expert(rg, N, K)
+                dd = gen(rg, N, K)
                 if e in need:
                     dst[e] = dd
         t0 = time.perf_counter()
-        oracle.ref_moe_layer(inp["x"], ids, inp["topk_weights"], lambda e: gu_w[e], lambda e: dn_w[e],
-                             I, H, E, 128)
+        if w4a8:
+            oracle.ref_moe_layer_w4a8(inp["x"], ids, inp["topk_weights"], lambda e: gu_w[e], lambda e: dn_w[e],
+                                      I, H, E)
+        else:
+            oracle.ref_moe_layer(inp["x"], ids, inp["topk_weights"], lambda e: gu_w[e], lambda e: dn_w[e],
+                                 I, H, E, 128)
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(),
                                 "kind": "oracle", "sample": f"T=1 ({len(need)} experts), {dt:.1f} s"}
@@ -755,7 +781,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_fp8b", "moe_layer"])
+    ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_fp8b", "moe_layer", "moe_layer_w4a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -770,6 +796,8 @@ def main():
         line = run_moe(args, mx="fp8b")
     elif args.config == "moe_layer":
         line = run_moe_layer(args)
+    elif args.config == "moe_layer_w4a8":
+        line = run_moe_layer(args, w4a8=True)
     else:
         line = run_dense(args, args.config)
     print(json.dumps(line), flush=True)

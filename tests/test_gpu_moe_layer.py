@@ -226,3 +226,89 @@ def test_layer_stage_calls_reject_bad_shapes_and_accept_empty():
         hq.hq_moe_combine(2, 2, 4, 12, buf, buf, buf)
     with pytest.raises(hq.HQError):
         hq.hq_moe_combine(2, 0, 4, 8, buf, buf, buf)
+
+
+class LayerW4A8:
+    """The layer with MXFP4 experts and tokenwise FP8 activations: per-token e4m3 quantization of
+    the tokens and of the SiLU output (hq_quantize_activations) before each grouped GEMM."""
+
+    def __init__(self, seed, T, topk, E, H, I):
+        inp = synth.make_moe_inputs(seed, T, H, E, topk)
+        self.T, self.topk, self.E, self.H, self.I = T, topk, E, H, I
+        self.x, self.ids, self.tw = inp["x"], inp["topk_ids"], inp["topk_weights"]
+        active = [int(e) for e in np.unique(self.ids)]
+        self.gu_w = {e: synth.make_moe_weights_expert_mx(seed, e, 2 * I, H) for e in active}
+        self.dn_w = {e: synth.make_moe_weights_expert_mx(seed + 1, e, H, I) for e in active}
+        self.desc = hq.DESC_W4A8_MXFP4
+        self.w_gu = self._pack(self.gu_w, 2 * I, H)
+        self.w_dn = self._pack(self.dn_w, H, I)
+        self.bm = hq.hq_moe_block_m(self.desc, T, topk, E, 2 * I, H)
+
+    def _pack(self, ws, N, K):
+        stride = hq.hq_prepacked_bytes(self.desc, 1, N, K)
+        w = torch.zeros(stride * self.E, dtype=torch.uint8, device=DEV)
+        for e, wd in ws.items():
+            w[e * stride:(e + 1) * stride] = prepack(self.desc, 1, N, K, wd["wq"], wd["scales"])
+        return w
+
+    def run(self):
+        T, topk, E, H, I, bm, D = self.T, self.topk, self.E, self.H, self.I, self.bm, self.desc
+        R = T * topk
+        cap = hq.hq_moe_align_capacity(T, topk, E, bm)
+        sorted_ids = torch.empty(cap, dtype=torch.int32, device=DEV)
+        block_expert = torch.empty(max(cap // bm, 1), dtype=torch.int32, device=DEV)
+        offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+        npad = torch.empty(1, dtype=torch.int32, device=DEV)
+        ids_d = to_dev(self.ids.astype(np.int32))
+        hq.hq_moe_align(ids_d, T, topk, E, bm, sorted_ids, block_expert, offs, npad)
+        xq = torch.empty((T, H), dtype=torch.uint8, device=DEV)
+        xs = torch.empty(T, dtype=torch.float32, device=DEV)
+        gu = torch.full((R, 2 * I), 0x7FC0, dtype=torch.int16, device=DEV)
+        act = torch.full((R, I), 0x7FC0, dtype=torch.int16, device=DEV)
+        aq = torch.empty((R, I), dtype=torch.uint8, device=DEV)
+        as_ = torch.empty(R, dtype=torch.float32, device=DEV)
+        dn = torch.full((R, H), 0x7FC0, dtype=torch.int16, device=DEV)
+        out = torch.full((T, H), 0x7FC0, dtype=torch.int16, device=DEV)
+        ws1 = hq.hq_moe_gemm_workspace_bytes(D, T, topk, E, 2 * I, H, bm)
+        ws2 = hq.hq_moe_gemm_workspace_bytes(D, R, 1, E, H, I, bm)
+        ws = torch.empty(max(ws1, ws2, 16), dtype=torch.uint8, device=DEV)
+        hq.hq_quantize_activations(hq.HQ_ACT_FP8E4M3_PER_TOKEN, T, H, to_dev(self.x), xq, xs)
+        hq.hq_moe_grouped_gemm(D, T, topk, E, 2 * I, H, xq, xs, self.w_gu, sorted_ids, block_expert, npad, bm,
+                               None, gu, ws, ws1)
+        hq.hq_moe_silu_mul(R, I, gu, act)
+        hq.hq_quantize_activations(hq.HQ_ACT_FP8E4M3_PER_TOKEN, R, I, act, aq, as_)
+        hq.hq_moe_grouped_gemm(D, R, 1, E, H, I, aq, as_, self.w_dn, sorted_ids, block_expert, npad, bm,
+                               to_dev(self.tw.reshape(-1).astype(np.float32)), dn, ws, ws2)
+        hq.hq_moe_combine(T, topk, E, H, ids_d, dn, out)
+        torch.cuda.synchronize()
+        res = {k: v.cpu().numpy().view(np.uint16) for k, v in
+               (("gate_up", gu), ("act", act), ("down", dn), ("out", out))}
+        res.update(xq=xq.cpu().numpy(), xs=xs.cpu().numpy(), aq=aq.cpu().numpy(), as_=as_.cpu().numpy())
+        return res
+
+
+@pytest.mark.parametrize("T,topk,E,H,I", [(7, 4, 8, 512, 256), (300, 8, 32, 1024, 256)])
+def test_moe_layer_w4a8(T, topk, E, H, I):
+    """Every stage against the oracle on the GPU's own input of that stage (the quantizations bit
+    for bit), then the layer's output against the oracle's layer: both chains quantize the same
+    way, so they differ only where a GEMM's last-bit difference moves an activation code, and the
+    float bar applies between them."""
+    L = LayerW4A8(60 + T, T, topk, E, H, I)
+    say(f"[moe layer w4a8] T={T} topk={topk} E={E} H={H} I={I} bm={L.bm}")
+    got = L.run()
+    xq, xs = oracle.quantize_per_token(L.x, "e4m3")
+    assert np.array_equal(got["xq"], xq) and np.array_equal(got["xs"], xs)
+    ref_gu, _, valid = oracle.ref_moe_gemm_q(xq, xs, L.ids, lambda e: L.gu_w[e], 2 * I, E, "e4m3")
+    assert valid.all()
+    check_float(got["gate_up"], ref_gu, "gate_up w4a8")
+    act64, delta = _silu_bound(got["gate_up"])
+    _check_rounded(got["act"], act64, delta, "silu_mul")
+    aq, as_ = oracle.quantize_per_token(got["act"], "e4m3")
+    assert np.array_equal(got["aq"], aq) and np.array_equal(got["as_"], as_)
+    ref_dn, _, _ = oracle.ref_moe_gemm_q(aq, as_, L.ids.reshape(-1, 1), lambda e: L.dn_w[e], H, E, "e4m3",
+                                         topk_weights=L.tw.reshape(-1, 1))
+    check_float(got["down"], ref_dn, "down w4a8")
+    out64, delta = _combine_bound(got["down"], L.ids, E)
+    _check_rounded(got["out"], out64, delta, "combine")
+    ref = oracle.ref_moe_layer_w4a8(L.x, L.ids, L.tw, lambda e: L.gu_w[e], lambda e: L.dn_w[e], I, H, E)
+    check_float(got["out"], bf16_to_f64(ref["out"]), "layer out w4a8 vs the oracle's layer")
