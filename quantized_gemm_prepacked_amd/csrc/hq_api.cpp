@@ -307,14 +307,6 @@ struct GroupedWs {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Formats with MoE / grouped kernels: all of them (activations in bf16, per token, per token and
-// 128-k block, or MX-scaled per 32 k).
-bool moe_family(const hq::Combo& c) {
-  return c.fam == hq::FAM_WNA16 || c.fam == hq::FAM_MXW4A16 || c.fam == hq::FAM_W8A8 || c.fam == hq::FAM_W4A8 ||
-         c.fam == hq::FAM_FP8B || c.fam == hq::FAM_W8A16 || c.fam == hq::FAM_F8A16 || c.fam == hq::FAM_W4A4 ||
-         c.fam == hq::FAM_W4A8MX || c.fam == hq::FAM_WNA2;
-}
-
 GroupedWs grouped_ws(const hq::Combo& c, int64_t R, int32_t E, int64_t N, int64_t K) {
   GroupedWs g{};
   g.bm = hq::moe_block_m(c, R, 1, E, N, K);
@@ -342,10 +334,7 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (!moe_family(c))
-    return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM: bf16 activations (INT4, MXFP4, INT8 or FP8 weights), "
-                                    "per-token INT8 / FP8 activations (INT8 or MXFP4 weights) or block-scaled FP8");
-  const bool per_token = !hq::family_bf16_act(c.fam);   // per token, or per token and 128-k block
+  const bool per_token = !hq::family_bf16_act(c.fam);   // activation scale rows, one per token
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (R < 0 || R > kMaxDim || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld E=%d out of range", (long long)R, E);
@@ -423,11 +412,8 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
-  if (!moe_family(c))
-    return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM: bf16 activations (INT4, MXFP4, INT8 or FP8 weights), "
-                                    "per-token INT8 / FP8 activations (INT8 or MXFP4 weights) or block-scaled FP8");
   if (c.out_i32) return fail(HQ_ERR_UNSUPPORTED, "MoE grouped GEMM writes bf16 only");
-  const bool per_token = !hq::family_bf16_act(c.fam);   // per token, or per token and 128-k block
+  const bool per_token = !hq::family_bf16_act(c.fam);   // activation scale rows, one per token
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (T < 0 || topk <= 0 || topk > 64 || E <= 0 || E > 512)
     return fail(HQ_ERR_INVALID_ARGUMENT, "T=%lld topk=%d E=%d out of range", (long long)T, topk, E);
