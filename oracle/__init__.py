@@ -25,12 +25,12 @@ torch's own dtype casts, the zero-exponent/symmetric-integer equivalence stated 
 triple loop, and special cases that reduce to a plain library matmul.
 """
 from .codecs import (  # noqa: F401
-    unpack_nibbles, unpack_crumbs, decode_int4_sym, decode_uint4, decode_int8, decode_e2m1, decode_e8m0,
+    unpack_nibbles, unpack_crumbs, unpack_triplets, decode_int4_sym, decode_uint4, decode_int8, decode_e2m1, decode_e8m0,
     decode_e4m3, decode_bf16, round_to_bf16, decode_sign_magnitude,
 )
 from .gemm import (  # noqa: F401
     dequant_wna16, dequant_mxfp4, ref_wna16, ref_w8a8, ref_w4a8, ref_w4a4, ref_w4a8_mx, ref_w4a16_mx, ref_w8a8_fp8_block,
-    ref_w8a16, dequant_wna2, ref_wna2,
+    ref_w8a16, dequant_wna2, ref_wna2, dequant_wna3, ref_wna3,
 )
 from .moe import (  # noqa: F401
     ref_moe_align, ref_moe_gemm, ref_moe_gemm_q, ref_moe_gemm_fp8_block, ref_moe_gemm_mx, ref_grouped_gemm, ref_silu_mul, ref_moe_combine, ref_moe_layer, ref_moe_layer_w4a8,

@@ -42,6 +42,15 @@ def unpack_crumbs(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+def unpack_triplets(packed: np.ndarray) -> np.ndarray:
+    """[..., 3K/8] bytes -> [..., K] 3-bit codes (uint8): the row is one little-endian bit string
+    and code k occupies its bits 3k .. 3k + 2 (lowest bit first)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    bits = np.unpackbits(p, axis=-1, bitorder="little")                  # [..., 3K]
+    b = bits.reshape(p.shape[:-1] + (-1, 3)).astype(np.uint8)
+    return b[..., 0] | (b[..., 1] << 1) | (b[..., 2] << 2)
+
+
 def decode_int4_sym(codes: np.ndarray) -> np.ndarray:
     c = np.asarray(codes).astype(np.int64) & 0xF
     return np.where(c >= 8, c - 16, c)

@@ -17,7 +17,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import (
-    unpack_nibbles, unpack_crumbs, decode_int4_sym, decode_uint4, decode_e2m1, decode_e8m0, decode_e4m3,
+    unpack_nibbles, unpack_crumbs, unpack_triplets, decode_int4_sym, decode_uint4, decode_e2m1, decode_e8m0, decode_e4m3,
     decode_bf16, round_to_bf16, decode_int8,
 )
 
@@ -53,6 +53,17 @@ def dequant_wna2(wq: np.ndarray, scales_bf16: np.ndarray, zeros: np.ndarray, g: 
     q = unpack_crumbs(_sel(wq, cols)).astype(np.int64)
     s = decode_bf16(_sel(scales_bf16, cols))
     z = np.asarray(_sel(zeros, cols)).astype(np.int64) & 0x3
+    grp = np.arange(q.shape[1]) // g
+    return (q - z[:, grp]).astype(np.float64) * s[:, grp]
+
+
+def dequant_wna3(wq: np.ndarray, scales_bf16: np.ndarray, zeros: np.ndarray, g: int, cols=None) -> np.ndarray:
+    """Group-wise asymmetric UINT3 weights -> float64 [N, K] (the page's WnA16 at a 3-bit width):
+        w[n, k] = (q[n, k] - z[n, k // g]) * s[n, k // g],    q, z in [0, 7]
+    wq packs each row as a little-endian bit string of 3-bit codes (3K/8 bytes)."""
+    q = unpack_triplets(_sel(wq, cols)).astype(np.int64)
+    s = decode_bf16(_sel(scales_bf16, cols))
+    z = np.asarray(_sel(zeros, cols)).astype(np.int64) & 0x7
     grp = np.arange(q.shape[1]) // g
     return (q - z[:, grp]).astype(np.float64) * s[:, grp]
 
@@ -182,5 +193,15 @@ def ref_wna2(x_bf16: np.ndarray, wq: np.ndarray, scales_bf16: np.ndarray, zeros:
     y = x . dequant_wna2(w)^T in float64, rounded once to bf16. Returns (y float64, y bf16 bits)."""
     x = decode_bf16(_sel(x_bf16, rows))
     w = dequant_wna2(wq, scales_bf16, zeros, g, cols)
+    y = x @ w.T
+    return y, round_to_bf16(y)
+
+
+def ref_wna3(x_bf16: np.ndarray, wq: np.ndarray, scales_bf16: np.ndarray, zeros: np.ndarray, g: int,
+             rows=None, cols=None):
+    """3-bit WnA16: bf16 activations times group-wise UINT3 weights with zero-points,
+    y = x . dequant_wna3(w)^T in float64, rounded once to bf16. Returns (y float64, y bf16 bits)."""
+    x = decode_bf16(_sel(x_bf16, rows))
+    w = dequant_wna3(wq, scales_bf16, zeros, g, cols)
     y = x @ w.T
     return y, round_to_bf16(y)

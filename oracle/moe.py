@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import decode_bf16, decode_e4m3, decode_e8m0, decode_int8, round_to_bf16
-from .gemm import dequant_mxfp4, dequant_wna16, dequant_wna2
+from .gemm import dequant_mxfp4, dequant_wna16, dequant_wna2, dequant_wna3
 
 
 def ref_moe_align(topk_ids: np.ndarray, E: int, block_m: int):
@@ -63,6 +63,8 @@ def _dequant_expert(wd, g: int, cols):
     scales and zero-points ({"wq", "scales", "zeros", "bits": 2})."""
     if wd.get("bits") == 2:
         return dequant_wna2(wd["wq"], wd["scales"], wd["zeros"], g, cols)
+    if wd.get("bits") == 3:
+        return dequant_wna3(wd["wq"], wd["scales"], wd["zeros"], g, cols)
     if "s_ch" in wd:
         c = np.asarray(wd["wq"]) if cols is None else np.asarray(wd["wq"])[np.asarray(cols)]
         q = decode_e4m3(c) if wd.get("fp8") else decode_int8(c).astype(np.float64)

@@ -135,6 +135,40 @@ def quantize_uint2_asym(w: np.ndarray, g: int):
     return {"wq": _pack_crumbs(q), "scales": s_bits, "zeros": z.astype(np.uint8)}
 
 
+def _pack_triplets(codes: np.ndarray) -> np.ndarray:
+    """[N, K] codes in 0..7 -> [N, 3K/8] bytes: the row as a little-endian bit string, code k in
+    bits 3k .. 3k + 2."""
+    c = codes.astype(np.uint8)
+    bits = np.stack([c & 1, (c >> 1) & 1, (c >> 2) & 1], axis=-1).reshape(c.shape[0], -1)
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def quantize_uint3_asym(w: np.ndarray, g: int):
+    """Asymmetric UINT3 with a uint3 zero-point per (n, group): s = bf16((max - min) / 7),
+    z = clamp(rne(-min / s), 0, 7), q = clamp(rne(w / s) + z, 0, 7) (a constant group: s = 1,
+    z = 0). Returns wq uint8 [N, 3K/8], scales bf16 bits [N, K/g], zeros uint8 [N, K/g]."""
+    N, K = w.shape
+    wg = w.reshape(N, K // g, g).astype(np.float32)
+    lo = wg.min(axis=2)
+    hi = wg.max(axis=2)
+    s_bits = bf16_bits((hi - lo) / np.float32(7.0))
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)
+    degenerate = s == 0
+    s_bits = np.where(degenerate, np.uint16(0x3F80), s_bits).astype(np.uint16)
+    s = np.where(degenerate, 1.0, s)
+    z = np.clip(_rne(-lo.astype(np.float64) / s), 0, 7)
+    z = np.where(degenerate, 0, z)
+    q = np.clip(_rne(wg / s[:, :, None]) + z[:, :, None], 0, 7).astype(np.uint8).reshape(N, K)
+    return {"wq": _pack_triplets(q), "scales": s_bits, "zeros": z.astype(np.uint8)}
+
+
+def make_wna3(config_id: int, M: int, N: int, K: int, g: int = 128):
+    """Dense 3-bit WnA16: bf16 N(0,1) activations, weights N(0, 0.02) quantized to UINT3 with a
+    zero-point per (channel, group of g)."""
+    w = rng(config_id, 0).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    return {"x": normal_bf16(rng(config_id, M), (M, K)), **quantize_uint3_asym(w, g)}
+
+
 def make_wna2(config_id: int, M: int, N: int, K: int, g: int = 128):
     """Dense 2-bit WnA16: bf16 N(0,1) activations, weights N(0, 0.02) quantized to UINT2 with a
     zero-point per (channel, group of g)."""
