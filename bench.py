@@ -4,7 +4,7 @@
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
 M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
---config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | w2a16 | moe | moe_mx | moe_fp8b |
+--config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | w2a16 | w3a16 | moe | moe_mx | moe_fp8b |
 moe_layer | moe_layer_w4a8.
 
 Timing follows the Humming announcement's microbenchmark protocol (section "Results: kernel
@@ -48,6 +48,8 @@ WORKLOADS = {
     "w8a16": dict(name="dense W8A16 INT8 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
                   dtype="bf16", peak="bf16"),
     "w2a16": dict(name="dense W2A16 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
+                  dtype="bf16", peak="bf16"),
+    "w3a16": dict(name="dense W3A16 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
                   dtype="bf16", peak="bf16"),
     "f8a16": dict(name="dense W8A16 FP8 e4m3 M-sweep", N=14336, K=4096, Ms=[1, 16, 128, 1024, 8192], cfg=2,
                   dtype="bf16", peak="bf16"),
@@ -109,6 +111,8 @@ def alg_bytes(wl: str, M: int, N: int, K: int) -> int:
         return N * K + N * 4 + M * K * 2 + M * N * 2
     if wl == "w2a16":
         return N * K // 4 + N * (K // 128) * 2 + N * (K // 128) // 2 + M * K * 2 + M * N * 2
+    if wl == "w3a16":
+        return N * K * 3 // 8 + N * (K // 128) * 2 + N * (K // 128) // 2 + M * K * 2 + M * N * 2
     return N * K // 2 + N * (K // 32) + M * K + M * 4 + M * N * 2
 
 
@@ -139,9 +143,9 @@ def make_inputs(wl: str, spec: dict):
         for M in spec["Ms"]:
             a = synth.make_w8a8_fp8_block(cfg, M, 128, K)          # activations only (N unused)
             acts[M] = (a["xq"], a["xs"])
-    elif wl == "w2a16":
-        d = synth.make_wna2(cfg, 1, N, K)
-        desc = hq.DESC_W2A16_ASYM
+    elif wl in ("w2a16", "w3a16"):
+        d = synth.make_wna2(cfg, 1, N, K) if wl == "w2a16" else synth.make_wna3(cfg, 1, N, K)
+        desc = hq.DESC_W2A16_ASYM if wl == "w2a16" else hq.DESC_W3A16_ASYM
         std = (d["wq"], d["scales"], d["zeros"])
         acts = {M: (synth.normal_bf16(synth.rng(cfg, M), (M, K)), None) for M in spec["Ms"]}
     elif wl in ("w8a16", "f8a16"):
@@ -206,6 +210,8 @@ def cpu_baseline(wl: str, spec: dict, std, acts):
             oracle.ref_w8a16(x, std[0], std[1], fp8=wl == "f8a16", rows=rows)
         elif wl == "w2a16":
             oracle.ref_wna2(x, std[0], std[1], std[2], 128, rows=rows)
+        elif wl == "w3a16":
+            oracle.ref_wna3(x, std[0], std[1], std[2], 128, rows=rows)
         elif wl == "fp8block":
             oracle.ref_w8a8_fp8_block(x, s, std[0], std[1], rows=rows)
         else:
@@ -371,7 +377,8 @@ def run_dense(args, wl: str):
                                "fp8block": "e4m3 + fp32 per 128x128 block, e4m3 act + fp32 per 1x128",
                                "w8a16": "int8 per-channel fp32 scale, bf16 act",
                                "f8a16": "fp8 e4m3 per-channel fp32 scale, bf16 act",
-                               "w2a16": "uint2 asym g128 bf16 scale + uint2 zero"}[wl]},
+                               "w2a16": "uint2 asym g128 bf16 scale + uint2 zero",
+                               "w3a16": "uint3 asym g128 bf16 scale + uint3 zero"}[wl]},
         "roofline": roof,
         "sweep": sweep,
     }

@@ -60,8 +60,10 @@ typedef enum {
   HQ_W_FP4_E2M1 = 3,   /* OCP MX e2m1, packed 2 per byte, low nibble = even k                      */
   HQ_W_FP8_E4M3 = 4,   /* OCP e4m3 [N, K]: one fp32 scale per 128 x 128 block (group_size 128) or,
                           with bf16 activations, per output channel (group_size 0)              */
-  HQ_W_UINT2_ASYM = 5  /* unsigned INT2 in [0, 3], packed 4 per byte (code k in bits 2 (k % 4)),
+  HQ_W_UINT2_ASYM = 5, /* unsigned INT2 in [0, 3], packed 4 per byte (code k in bits 2 (k % 4)),
                           with a uint2 zero-point per (n, group)                                  */
+  HQ_W_UINT3_ASYM = 6  /* unsigned INT3 in [0, 7], each row a little-endian bit string (code k in
+                          bits 3k .. 3k + 2), with a uint3 zero-point per (n, group)              */
 } hq_weight_fmt;
 
 typedef enum {
@@ -122,7 +124,8 @@ typedef struct {
  *   FP8_E4M3   + FP32 scale, group 0                  + ACT_BF16   (W8A16)    -> OUT_BF16
  *              (the 8-bit WnA16 widths; K % 128 == 0)
  *   UINT2_ASYM + BF16 scale, group 128, zero-point    + ACT_BF16   (W2A16)    -> OUT_BF16
- *              (the 2-bit WnA16 width; small-M kernel at every M)
+ *   UINT3_ASYM + BF16 scale, group 128, zero-point    + ACT_BF16   (W3A16)    -> OUT_BF16
+ *              (the 2- and 3-bit WnA16 widths; 3-bit weights on the small-M kernel at every M)
  * MoE grouped GEMM and grouped GEMM: every combination above with OUT_BF16 -- ACT_BF16 (INT4 sym /
  * asym, FP4, INT8, FP8 weights), per-token activations (INT8 W8A8, FP4 + ACT_FP8E4M3_PER_TOKEN
  * W4A8), block-scaled FP8 (a_scale = fp32 [T, K/128]) and MX activations (ACT_MXFP4, ACT_MXFP8:
@@ -164,11 +167,14 @@ hq_status hq_quantize_activations(int32_t act_fmt, int64_t M, int64_t K, const v
  * Weight prepack (host).  Standard-format inputs, all host memory, row-major:
  *   wq      INT4/FP4: uint8 [E, N, K/2] (two codes per byte, low nibble = even k)
  *           UINT2   : uint8 [E, N, K/4] (four codes per byte, code k in bits 2 (k % 4) .. +1)
+ *           UINT3   : uint8 [E, N, 3K/8] (each row a little-endian bit string, code k in bits
+ *                     3k .. 3k + 2)
  *           INT8    : int8  [E, N, K];  FP8: e4m3 bytes [E, N, K]
  *   scales  BF16: uint16 bf16 bits [E, N, K/group];  FP32: float [E, N] (per channel: INT8,
  *           and FP8 with group_size 0) or float [E, N/128, K/128] (FP8 block scales);
  *           E8M0: uint8 [E, N, K/32]
- *   zeros   UINT4_ASYM / UINT2_ASYM only: uint8 [E, N, K/group], values 0..15 / 0..3; NULL otherwise
+ *   zeros   UINT4_ASYM / UINT3_ASYM / UINT2_ASYM only: uint8 [E, N, K/group], values 0..15 / 0..7 /
+ *           0..3; NULL otherwise
  * E = 1 for a dense layer, E = number of experts for MoE (experts stacked).
  * Output: `out` (host, `hq_prepacked_bytes` bytes) receives the weights rearranged into the
  * MFMA operand order of the kernels. The layout is private to this library version; the caller

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # ---- enums (hq.h) -----------------------------------------------------------------------------
 HQ_OK, HQ_ERR_INVALID_ARGUMENT, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP = range(5)
-HQ_W_INT4_SYM, HQ_W_UINT4_ASYM, HQ_W_INT8_SYM, HQ_W_FP4_E2M1, HQ_W_FP8_E4M3, HQ_W_UINT2_ASYM = range(6)
+HQ_W_INT4_SYM, HQ_W_UINT4_ASYM, HQ_W_INT8_SYM, HQ_W_FP4_E2M1, HQ_W_FP8_E4M3, HQ_W_UINT2_ASYM, HQ_W_UINT3_ASYM = range(7)
 HQ_SCALE_BF16, HQ_SCALE_FP32, HQ_SCALE_E8M0 = range(3)
 HQ_ACT_BF16, HQ_ACT_INT8_PER_TOKEN, HQ_ACT_FP8E4M3_PER_TOKEN, HQ_ACT_MXFP4, HQ_ACT_MXFP8, HQ_ACT_FP8E4M3_BLOCK128 = range(6)
 HQ_OUT_BF16, HQ_OUT_INT32_ACC = range(2)
@@ -83,6 +83,7 @@ DESC_W8A8_FP8_BLOCK = make_desc(HQ_W_FP8_E4M3, 128, HQ_SCALE_FP32, 0, HQ_ACT_FP8
 DESC_W8A16_INT8 = make_desc(HQ_W_INT8_SYM, 0, HQ_SCALE_FP32, 0, HQ_ACT_BF16)
 DESC_W8A16_FP8 = make_desc(HQ_W_FP8_E4M3, 0, HQ_SCALE_FP32, 0, HQ_ACT_BF16)
 DESC_W2A16_ASYM = make_desc(HQ_W_UINT2_ASYM, 128, HQ_SCALE_BF16, 1, HQ_ACT_BF16)
+DESC_W3A16_ASYM = make_desc(HQ_W_UINT3_ASYM, 128, HQ_SCALE_BF16, 1, HQ_ACT_BF16)
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 from . import (DESC_W4A16_ASYM, DESC_W4A16_MXFP4, DESC_W4A16_SYM, DESC_W4A4_MXFP4, DESC_W4A8_MXFP4,
-               DESC_W4A8_MXFP8, DESC_W8A8, DESC_W8A8_FP8_BLOCK, DESC_W8A16_FP8, DESC_W8A16_INT8, DESC_W2A16_ASYM,
+               DESC_W4A8_MXFP8, DESC_W8A8, DESC_W8A8_FP8_BLOCK, DESC_W8A16_FP8, DESC_W8A16_INT8, DESC_W2A16_ASYM, DESC_W3A16_ASYM,
                HQError, hq_gemm, hq_gemm_plan, hq_gemm_workspace_bytes, hq_kernel_config_count,
                hq_load_tuning_table, hq_prepack_weights, hq_prepacked_bytes)
 
@@ -45,6 +45,7 @@ FORMATS = {
     "w8a16": (DESC_W8A16_INT8, "w8a16", 0),
     "f8a16": (DESC_W8A16_FP8, "f8a16", 0),
     "w2a16": (DESC_W2A16_ASYM, "wna2", 1),
+    "w3a16": (DESC_W3A16_ASYM, "wna3", 1),
 }
 INF_M = 1 << 40
 
@@ -57,10 +58,11 @@ def _weights(fmt: str, N: int, K: int, g: np.random.Generator):
         scales = (s.view(np.uint32) >> 16).astype(np.uint16)
         zeros = g.integers(0, 16, (N, K // 128), dtype=np.uint8) if fmt == "w4a16a" else None
         return wq, scales, zeros
-    if fmt == "w2a16":
+    if fmt in ("w2a16", "w3a16"):
         s = (0.01 * (1 + 0.1 * g.standard_normal((N, K // 128)))).astype(np.float32)
-        return (g.integers(0, 256, (N, K // 4), dtype=np.uint8), (s.view(np.uint32) >> 16).astype(np.uint16),
-                g.integers(0, 4, (N, K // 128), dtype=np.uint8))
+        b2 = fmt == "w2a16"
+        return (g.integers(0, 256, (N, K // 4 if b2 else 3 * K // 8), dtype=np.uint8),
+                (s.view(np.uint32) >> 16).astype(np.uint16), g.integers(0, 4 if b2 else 8, (N, K // 128), dtype=np.uint8))
     if fmt in ("w8a8", "w8a16"):
         return (g.integers(-127, 128, (N, K)).astype(np.int8),
                 (0.001 * (1 + g.random(N))).astype(np.float32), None)
@@ -76,7 +78,7 @@ def _weights(fmt: str, N: int, K: int, g: np.random.Generator):
 
 def _activations(fmt: str, M: int, K: int, g: np.random.Generator):
     """(a bytes, a_scale) in the format's activation layout."""
-    if fmt in ("w4a16", "w4a16a", "w4a16mx", "w8a16", "f8a16", "w2a16"):
+    if fmt in ("w4a16", "w4a16a", "w4a16mx", "w8a16", "f8a16", "w2a16", "w3a16"):
         x = g.standard_normal((M, K)).astype(np.float32)
         return (x.view(np.uint32) >> 16).astype(np.uint16).view(np.uint8), None
     if fmt == "w8a8":

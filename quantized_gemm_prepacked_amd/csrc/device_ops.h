@@ -31,6 +31,11 @@ __device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// 4 bytes (3-bit weights: a lane's high bits), streamed.
+__device__ __forceinline__ uint32_t ldg4_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 // 8 bytes (2-bit weights: a lane's half unit), streamed; returned in the low two dwords.
 __device__ __forceinline__ u32x4 ldg8_stream(const void* p) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -103,11 +108,27 @@ __device__ __forceinline__ bf16x8 dequant_uint2x8_offset128(uint32_t v, int h) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// 3-bit form (WNA3): low two bits of the 16 codes of dword `lo` as for 2-bit codes, high bits in
+// dword `hi` (code 2s + e of low dword h in bit 16 e + 8 h + s); returns (128 + u) for codes
+// 8 half .. 8 half + 7 of low dword h.
+__device__ __forceinline__ bf16x8 dequant_uint3x8_offset128(uint32_t lo, uint32_t hi, int h, int half) {
+  const uint32_t w = lo >> (8 * half);
+  const uint32_t v = hi >> (8 * h + 4 * half);
+  uint32_t p[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    p[s] = ((w >> (2 * s)) & 0x00030003u) | (((v >> s) & 0x00010001u) << 2) | 0x43004300u;
+  const u32x4 r = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // The offset-128 operand of MFMA d (0..3) of a 128-k group from a lane's packed codes: 4-bit
-// codes hold it in dword d, 2-bit codes in half d & 1 of dword d >> 1.
+// codes hold it in dword d, 2-bit codes in half d & 1 of dword d >> 1, 3-bit codes as 2-bit ones
+// plus their high bits in dword 2.
 template <int FAM>
 __device__ __forceinline__ bf16x8 dequant_offset128(const u32x4& q, int d) {
   if constexpr (FAM == FAM_WNA2) return dequant_uint2x8_offset128(q[d >> 1], d & 1);
+  else if constexpr (FAM == FAM_WNA3) return dequant_uint3x8_offset128(q[d >> 1], q[2], d >> 1, d & 1);
   else return dequant_int4x8_offset128(q[d]);
 }
 

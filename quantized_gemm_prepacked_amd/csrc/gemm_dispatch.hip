@@ -30,7 +30,7 @@ int k_unit(const Combo& c) {
 // instantiation).
 bool pp_only(const Combo& c) {
   return c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B ||
-         c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_WNA2;
+         c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_WNA2 || c.fam == FAM_WNA3;
 }
 
 // Activation bytes per 2 k (bf16: 4; 8-bit: 2; 4-bit: 1): the direct-to-LDS kernels address
@@ -51,7 +51,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
   };
   if (rows <= 16) {
-    if (c.fam == FAM_WNA2) return first_fit({28, 13, 0, 1, 2});
+    if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({28, 13, 0, 1, 2});
     // 8-bit weights with bf16 activations, N=14336 K=4096: 16 waves of 64 channels, two units in
     // flight (M=1 INT8 / FP8: 13.2 / 12.3 us; the 8-wave form 13.5 / 12.6)
     if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) return first_fit({27, 0, 1, 2});
@@ -63,7 +63,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     return first_fit({28, 13, 0, 1, 2});
   }
   if (rows <= 32) {
-    if (c.fam == FAM_WNA2) return first_fit({29, 22, 3, 7, 8});
+    if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({29, 22, 3, 7, 8});
     if (c.fam == FAM_W8A16) return first_fit({29, 22, 3, 7, 8});   // M=32: 16.0 us (next 18.9)
     if (c.fam == FAM_F8A16) return first_fit({22, 29, 3, 7, 8});   // M=32: 15.8 us (next 16.3)
     if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
@@ -74,7 +74,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   }
   // 2-bit weights: two 32-row blocks, double-buffered (N=14336, K=4096, M=64 / 128: 20.4 / 37.2
   // us against 22.4 / 39.2 with 64-row blocks)
-  if (c.fam == FAM_WNA2) return first_fit({22, 5, 4, 6});
+  if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({22, 5, 4, 6});
   if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
   if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
   if (c.fam == FAM_FP8B && rows <= 64) return first_fit({29, 15, 8});   // M=64: 31.9 us vs 40.6
@@ -133,6 +133,8 @@ hipError_t launch_splitk_reduce(const KParams& p, int fam, hipStream_t s) {
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_W8A16>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_WNA2)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_WNA2>, grid, dim3(256), 0, s, p);
+  else if (fam == FAM_WNA3)
+    hipLaunchKernelGGL(splitk_reduce_kernel<FAM_WNA3>, grid, dim3(256), 0, s, p);
   else if (fam == FAM_F8A16)
     hipLaunchKernelGGL(splitk_reduce_kernel<FAM_F8A16>, grid, dim3(256), 0, s, p);
   else
@@ -208,7 +210,7 @@ int tile_n_of(int kind, int cfg) {
 
 // (kind, cfg) from the table, or kind 0 for the skinny kernel.
 RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
-  if (K % 128 != 0) return {0, 0, 0};
+  if (K % 128 != 0 || c.fam == FAM_WNA3) return {0, 0, 0};   // 3-bit weights: the skinny kernel
   const RangeEntry* t;
   int n;
   if (c.fam == FAM_WNA16) {

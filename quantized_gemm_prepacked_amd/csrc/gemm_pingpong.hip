@@ -552,7 +552,8 @@ int pp_lds_table(int cfg, std::integer_sequence<int, I...>) {
 
 int pp_lds_bytes(int fam, int cfg) {
   constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
-  if (cfg < 0 || cfg >= n) return 1 << 30;
+  // (3-bit weights' 768-byte units do not split into the kernel's 1 KiB copies: no instantiation)
+  if (cfg < 0 || cfg >= n || fam == FAM_WNA3) return 1 << 30;
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_WNA2) return pp_lds_table<FAM_WNA2>(cfg, seq);

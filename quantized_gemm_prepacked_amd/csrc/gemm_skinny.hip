@@ -44,6 +44,10 @@ struct SkTraits<FAM_WNA16> {
   static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
 };
 template <>
+struct SkTraits<FAM_WNA3> {
+  static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
+};
+template <>
 struct SkTraits<FAM_WNA2> {
   static constexpr int kRowBytes = 256, kUnitK = 128, kScaleBytes = 32, kZeroBytes = 8, kAScaleBytes = 0;
 };
@@ -97,7 +101,8 @@ struct SkShape {
   static constexpr int RED = NW * MB * NTW * 4 * 64 * 4; // epilogue reduction (aliases the slots)
   static constexpr int LDS = (NW * WAVE_LDS > RED ? NW * WAVE_LDS : RED);
   static constexpr int WL = SkWLoads<FAM>::value;
-  static constexpr int UNIT_INSTR = A_INSTR + NTW * WL + META_INSTR;   // vector-memory ops per unit
+  static constexpr int WI = FAM == FAM_WNA3 ? 2 : WL;   // weight loads per tile and unit
+  static constexpr int UNIT_INSTR = A_INSTR + NTW * WI + META_INSTR;   // vector-memory ops per unit
   static_assert(A_UNIT % 1024 == 0, "whole-wave activation copies");
   static_assert(SC / 16 <= 64 && ZB / 4 <= 64 && ASC / 4 <= 64, "metadata copies fit one instruction each");
   static_assert(UNR * UNIT_INSTR < 64, "vmcnt range");
@@ -179,10 +184,14 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       const size_t unit = (size_t(nt0 + t) * k_units + u) * Sh::WL;
-      if constexpr (FAM == FAM_WNA2)
+      if constexpr (FAM == FAM_WNA2) {
         bw[buf][r][t] = ldg8_stream(w + unit * 512 + 8 * lane);
-      else
+      } else if constexpr (FAM == FAM_WNA3) {
+        bw[buf][r][t] = ldg8_stream(w + unit * 768 + 8 * lane);
+        bw[buf][r][t][2] = ldg4_stream(w + unit * 768 + 512 + 4 * lane);
+      } else {
         bw[buf][r][t] = ldg16_stream(w + unit * kUnitBytes + 16 * lane);
+      }
       if constexpr (Sh::WL == 2) bw2[buf][r][t] = ldg16_stream(w + (unit + 1) * kUnitBytes + 16 * lane);
     }
     if constexpr (Sh::SC > 0) {
@@ -245,9 +254,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
         f32x4 part[MB];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          bf16x8 bv;
-          if constexpr (FAM == FAM_WNA2) bv = dequant_uint2x8_offset128(bw[buf][r][t][d >> 1], d & 1);
-          else bv = dequant_int4x8_offset128(bw[buf][r][t][d]);
+          const bf16x8 bv = dequant_offset128<FAM>(bw[buf][r][t], d);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             part[mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv,
@@ -490,6 +497,7 @@ int skinny_lds_bytes(int fam, int cfg) {
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return skinny_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_WNA2) return skinny_lds_table<FAM_WNA2>(cfg, seq);
+  if (fam == FAM_WNA3) return skinny_lds_table<FAM_WNA3>(cfg, seq);
   if (fam == FAM_W8A8) return skinny_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return skinny_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return skinny_lds_table<FAM_W4A8MX>(cfg, seq);
@@ -536,6 +544,8 @@ hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid
                                    : launch_skinny_fam<FAM_WNA16, false>(p, cfg, grid, s);
   if (fam == FAM_WNA2) return moe ? launch_skinny_fam<FAM_WNA2, true>(p, cfg, grid, s)
                                   : launch_skinny_fam<FAM_WNA2, false>(p, cfg, grid, s);
+  if (fam == FAM_WNA3) return moe ? launch_skinny_fam<FAM_WNA3, true>(p, cfg, grid, s)
+                                  : launch_skinny_fam<FAM_WNA3, false>(p, cfg, grid, s);
   if (fam == FAM_MXW4A16) return moe ? launch_skinny_fam<FAM_MXW4A16, true>(p, cfg, grid, s)
                                      : launch_skinny_fam<FAM_MXW4A16, false>(p, cfg, grid, s);
   if (moe && fam == FAM_W8A8) return launch_skinny_fam<FAM_W8A8, true>(p, cfg, grid, s);

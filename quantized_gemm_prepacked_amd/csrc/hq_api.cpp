@@ -66,12 +66,13 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
       return HQ_OK;
     }
     case HQ_W_UINT2_ASYM:
+    case HQ_W_UINT3_ASYM:
       if (d->group_size != 128 || d->scale_dtype != HQ_SCALE_BF16 || d->has_zero_point != 1 ||
           d->act_fmt != HQ_ACT_BF16 || c->out_i32)
         return fail(HQ_ERR_UNSUPPORTED,
-                    "UINT2 weights need group_size 128, BF16 scales, has_zero_point 1, BF16 "
+                    "UINT2 / UINT3 weights need group_size 128, BF16 scales, has_zero_point 1, BF16 "
                     "activations and bf16 output");
-      c->fam = hq::FAM_WNA2;
+      c->fam = d->weight_fmt == HQ_W_UINT2_ASYM ? hq::FAM_WNA2 : hq::FAM_WNA3;
       c->asym = true;
       return HQ_OK;
     case HQ_W_INT8_SYM:
@@ -164,7 +165,7 @@ hq_status hq_prepack_weights(const hq_quant_desc* desc, int64_t E, int64_t N, in
   if (E <= 0 || E > 65536) return fail(HQ_ERR_INVALID_ARGUMENT, "E=%lld out of range", (long long)E);
   if ((s = check_shape(c, N, K)) != HQ_OK) return s;
   if (!wq || !scales || !out) return fail(HQ_ERR_INVALID_ARGUMENT, "wq, scales and out must be non-NULL");
-  if (c.asym && !zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for UINT4_ASYM / UINT2_ASYM");
+  if (c.asym && !zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for UINT4_ASYM / UINT3_ASYM / UINT2_ASYM");
   if (!c.asym && zeros) return fail(HQ_ERR_INVALID_ARGUMENT, "zeros must be NULL without zero-points");
   const size_t need = hq::prepacked_bytes(c, E, N, K);
   if (out_bytes < need)

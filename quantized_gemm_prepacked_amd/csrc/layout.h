@@ -30,6 +30,9 @@
 //   k = 128*kt + 32*(l>>4) + 16*h + c in dword h (0, 1), code c = 2s + e (s = 0..7, e = 0, 1) in
 //   bits 16*e + 2*s .. +1, so (dword >> 2s) & 0x00030003 yields the pair (k 2s, 2s+1) as two
 //   16-bit lanes. Scales and zeros as WNA16's (zeros 0..3 in the 4-bit slots).
+//   WNA3 (UINT3 with zero-points): a unit is 768 bytes, the low two bits of each code in WNA2's
+//   512-byte layout, then 256 bytes of high bits: lane l's dword at 512 + 4*l holds the high bit
+//   of code c = 2s + e of dword h in bit 16*e + 8*h + s.
 //
 // Regions per expert (each starts at a 256-byte aligned offset; experts are stacked with a
 // 256-byte aligned stride):
@@ -49,13 +52,14 @@ namespace hq {
 // FP8B: block-scaled FP8 W8A8 (e4m3 weights with an fp32 scale per 128 x 128 block, e4m3
 // activations with an fp32 scale per (row, 128 k)); its codes use W8A8's 64-k units.
 // W8A16 / F8A16: INT8 / FP8 e4m3 weights with a per-channel fp32 scale and bf16 activations.
-// WNA2: 2-bit WnA16 (UINT2 codes with zero-points, the WNA16 scale and zero layout).
+// WNA2 / WNA3: 2-bit / 3-bit WnA16 (UINT2 / UINT3 codes with zero-points, the WNA16 scale and
+// zero layout).
 enum Family { FAM_WNA16 = 0, FAM_W8A8 = 1, FAM_W4A8 = 2, FAM_W4A4 = 3, FAM_W4A8MX = 4, FAM_MXW4A16 = 5, FAM_FP8B = 6,
-              FAM_W8A16 = 7, FAM_F8A16 = 8, FAM_WNA2 = 9 };
+              FAM_W8A16 = 7, FAM_F8A16 = 8, FAM_WNA2 = 9, FAM_WNA3 = 10 };
 
 // Integer group-wise weights with bf16 activations: group scales and zero-points, the offset-128
 // operand (WNA16, WNA2).
-inline constexpr bool family_int_groups(int f) { return f == FAM_WNA16 || f == FAM_WNA2; }
+inline constexpr bool family_int_groups(int f) { return f == FAM_WNA16 || f == FAM_WNA2 || f == FAM_WNA3; }
 
 // 8-bit weight codes in 64-k units
 inline constexpr bool family_8bit_weights(int f) {
@@ -64,12 +68,12 @@ inline constexpr bool family_8bit_weights(int f) {
 
 // bf16 activations (2 bytes per k)
 inline constexpr bool family_bf16_act(int f) {
-  return f == FAM_WNA16 || f == FAM_MXW4A16 || f == FAM_W8A16 || f == FAM_F8A16 || f == FAM_WNA2;
+  return f == FAM_WNA16 || f == FAM_MXW4A16 || f == FAM_W8A16 || f == FAM_F8A16 || f == FAM_WNA2 || f == FAM_WNA3;
 }
 
 constexpr int kUnitBytes = 1024;
-// Bytes of one 16-channel unit of codes (WNA2: 128 k of 2-bit codes).
-inline constexpr int family_unit_bytes(int f) { return f == FAM_WNA2 ? 512 : kUnitBytes; }
+// Bytes of one 16-channel unit of codes (WNA2 / WNA3: 128 k of 2-bit / 3-bit codes).
+inline constexpr int family_unit_bytes(int f) { return f == FAM_WNA2 ? 512 : f == FAM_WNA3 ? 768 : kUnitBytes; }
 constexpr int kTileN = 16;
 
 inline int family_k_unit(Family f) { return family_8bit_weights(f) ? 64 : 128; }

@@ -110,6 +110,45 @@ void pack_wna2(const PackedLayout& L, const uint8_t* wq, const uint16_t* scales,
   });
 }
 
+// 3-bit codes (layout.h, WNA3): input wq [N, 3K/8], each row a little-endian bit string with
+// code k in bits 3k .. 3k + 2; scales and zeros as WNA16's.
+void pack_wna3(const PackedLayout& L, const uint8_t* wq, const uint16_t* scales, const uint8_t* zeros,
+               uint8_t* out) {
+  const int64_t K = L.K, G = K / 128;
+  parallel_for(L.n_tiles, [&](int64_t nt) {
+    for (int64_t kt = 0; kt < L.k_units; ++kt) {
+      uint8_t* unit = out + L.codes_off + (size_t(nt) * L.k_units + kt) * 768;
+      for (int l = 0; l < 64; ++l) {
+        const int64_t n = nt * 16 + (l & 15);
+        const uint8_t* row = wq + size_t(n) * (K / 8 * 3);
+        uint32_t lo[2] = {0, 0}, hi = 0;
+        for (int h = 0; h < 2; ++h)
+          for (int c = 0; c < 16; ++c) {
+            const int64_t k = kt * 128 + 32 * (l >> 4) + 16 * h + c;
+            uint32_t code = 0;
+            for (int b = 0; b < 3; ++b) {
+              const int64_t bit = 3 * k + b;
+              code |= uint32_t((row[bit >> 3] >> (bit & 7)) & 1u) << b;
+            }
+            const int s = c >> 1, e = c & 1;
+            lo[h] |= (code & 3u) << (16 * e + 2 * s);
+            hi |= (code >> 2) << (16 * e + 8 * h + s);
+          }
+        std::memcpy(unit + 8 * l, lo, 8);
+        std::memcpy(unit + 512 + 4 * l, &hi, 4);
+      }
+      uint16_t* sdst = reinterpret_cast<uint16_t*>(out + L.scales_off) + (size_t(nt) * L.k_units + kt) * 16;
+      for (int i = 0; i < 16; ++i) sdst[i] = scales[size_t(nt * 16 + i) * G + kt];
+      uint8_t* zdst = out + L.zeros_off + (size_t(nt) * L.k_units + kt) * 8;
+      for (int i = 0; i < 8; ++i) {
+        const uint8_t zlo = zeros[size_t(nt * 16 + 2 * i) * G + kt] & 0x7;
+        const uint8_t zhi = zeros[size_t(nt * 16 + 2 * i + 1) * G + kt] & 0x7;
+        zdst[i] = uint8_t(zlo | (zhi << 4));
+      }
+    }
+  });
+}
+
 void pack_w8a8(const PackedLayout& L, const int8_t* wq, const float* scales, uint8_t* out) {
   const int64_t K = L.K;
   parallel_for(L.n_tiles, [&](int64_t nt) {
@@ -192,6 +231,10 @@ void prepack(const Combo& c, int64_t E, int64_t N, int64_t K, const void* wq,
     } else if (c.fam == FAM_WNA2) {
       const size_t s_stride = size_t(N) * (K / 128);
       pack_wna2(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * (K / 4),
+                static_cast<const uint16_t*>(scales) + e * s_stride, static_cast<const uint8_t*>(zeros) + e * s_stride, o);
+    } else if (c.fam == FAM_WNA3) {
+      const size_t s_stride = size_t(N) * (K / 128);
+      pack_wna3(L, static_cast<const uint8_t*>(wq) + e * size_t(N) * (K / 8 * 3),
                 static_cast<const uint16_t*>(scales) + e * s_stride, static_cast<const uint8_t*>(zeros) + e * s_stride, o);
     } else if (c.fam == FAM_W8A8) {
       pack_w8a8(L, static_cast<const int8_t*>(wq) + e * size_t(N) * K,

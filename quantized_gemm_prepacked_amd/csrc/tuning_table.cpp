@@ -46,6 +46,7 @@ bool parse_family(const std::string& s, Family* f) {
   else if (s == "w8a16") *f = FAM_W8A16;
   else if (s == "f8a16") *f = FAM_F8A16;
   else if (s == "wna2") *f = FAM_WNA2;
+  else if (s == "wna3") *f = FAM_WNA3;
   else return false;
   return true;
 }

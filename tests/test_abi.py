@@ -175,3 +175,14 @@ def test_w2a16_descriptor():
     with pytest.raises(hq.HQError):
         hq.hq_prepack_weights(d, 1, 256, 512, np.zeros((256, 128), np.uint8), np.zeros((256, 4), np.uint16),
                               None, np.zeros(hq.hq_prepacked_bytes(d, 1, 256, 512), np.uint8))   # zeros missing
+
+
+def test_w3a16_descriptor():
+    d = hq.DESC_W3A16_ASYM
+    assert hq.hq_prepacked_bytes(d, 1, 256, 512) > 0
+    assert hq.hq_gemm_plan(d, 8192, 256, 512)[0] == 0            # the skinny kernel at every M
+    with pytest.raises(hq.HQError):                               # zeros missing
+        hq.hq_prepack_weights(d, 1, 256, 512, np.zeros((256, 192), np.uint8), np.zeros((256, 4), np.uint16),
+                              None, np.zeros(hq.hq_prepacked_bytes(d, 1, 256, 512), np.uint8))
+    bad = hq.make_desc(hq.HQ_W_UINT3_ASYM, 32, hq.HQ_SCALE_BF16, 1, hq.HQ_ACT_BF16)
+    assert hq.hq_prepacked_bytes(bad, 1, 256, 512) == 0

@@ -18,7 +18,7 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_records_are_well_formed():
     for wl in ("w4a16", "w8a8", "w4a8", "w4a4", "w4a16mx", "fp8block", "w8a16", "f8a16", "w2a16", "moe", "moe_mx",
-               "moe_fp8b", "moe_layer", "moe_layer_w4a8"):
+               "moe_fp8b", "moe_layer", "moe_layer_w4a8", "w3a16"):
         path = os.path.join(ROOT, "profiles", f"traffic_{wl}.json")
         rec = json.load(open(path))
         cal = rec["copy_calibration"]

@@ -37,6 +37,9 @@ def _inputs(fmt, M, N, K):
     if fmt == "w4a16mx":
         d = synth.make_w4a16mx(900, M, N, K)
         return hq.DESC_W4A16_MXFP4, (d["wq"], d["scales"], None), d["x"], None
+    if fmt == "w3a16":
+        d = synth.make_wna3(900, M, N, K)
+        return hq.DESC_W3A16_ASYM, (d["wq"], d["scales"], d["zeros"]), d["x"], None
     if fmt == "w2a16":
         d = synth.make_wna2(900, M, N, K)
         return hq.DESC_W2A16_ASYM, (d["wq"], d["scales"], d["zeros"]), d["x"], None
@@ -49,7 +52,7 @@ def _inputs(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["w4a16", "w4a16a", "w8a8", "w4a8", "w4a4", "w4a8mx", "w4a16mx", "fp8block",
-                                 "w8a16", "f8a16", "w2a16"])
+                                 "w8a16", "f8a16", "w2a16", "w3a16"])
 def test_rows_do_not_depend_on_the_batch(fmt):
     M, N, K = 300, 512, 1024
     desc, std, x, s = _inputs(fmt, M, N, K)
@@ -85,6 +88,8 @@ def test_rows_do_not_depend_on_the_batch(fmt):
         ref, _ = oracle.ref_w4a16_mx(x, std[0], std[1])
     elif fmt == "fp8block":
         ref, _ = oracle.ref_w8a8_fp8_block(x, s, std[0], std[1])
+    elif fmt == "w3a16":
+        ref, _ = oracle.ref_wna3(x, std[0], std[1], std[2], 128)
     elif fmt == "w2a16":
         ref, _ = oracle.ref_wna2(x, std[0], std[1], std[2], 128)
     elif fmt in ("w8a16", "f8a16"):

@@ -1,0 +1,146 @@
+"""GPU parity of 3-bit WnA16 (UINT3 codes with a uint3 zero-point and a bf16 scale per channel and
+group of 128, bf16 activations; the low two bits and the high bit of each code bit-selected into
+the offset-128 bf16 operand, bf16 MFMA, group scale on the fp32 partial; the small-M kernel at
+every M) against the CPU oracle, through the C ABI: dense, MoE and grouped calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_prepacked_amd as hq
+import synth
+
+from gpu_harness import DEV, check_float, gemm, prepack, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+D = hq.DESC_W3A16_ASYM
+
+
+def _run(d, M, N, K):
+    w = prepack(D, 1, N, K, d["wq"], d["scales"], d["zeros"])
+    return gemm(D, M, N, K, to_dev(d["x"]), None, w)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 512, 4096), (3, 272, 384), (16, 64, 128), (32, 256, 1024), (64, 512, 512),
+    (1, 64, 8192),      # 4 workgroups: K split across workgroups, then the reduction launch
+    (200, 256, 640),    # ragged M
+    (300, 512, 1024),
+    (1000, 400, 512),
+])
+def test_wna3_small(M, N, K):
+    say(f"[wna3] M={M} N={N} K={K}")
+    d = synth.make_wna3(1600, M, N, K)
+    y = _run(d, M, N, K)
+    ref, _ = oracle.ref_wna3(d["x"], d["wq"], d["scales"], d["zeros"], 128)
+    check_float(y, ref, "wna3")
+
+
+@pytest.mark.parametrize("M", [1, 16, 128, 8192])
+def test_wna3_full_size_sampled(M):
+    N, K = 14336, 4096
+    say(f"[wna3 full] M={M}")
+    d = synth.make_wna3(2, M, N, K)
+    y = _run(d, M, N, K)
+    g = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, 48)]))
+    cols = np.unique(np.concatenate([[0, N - 1], g.integers(0, N, 96)]))
+    ref, _ = oracle.ref_wna3(d["x"], d["wq"], d["scales"], d["zeros"], 128, rows=rows, cols=cols)
+    check_float(y[np.ix_(rows, cols)], ref, f"wna3 M={M}")
+
+
+def test_wna3_every_kernel_configuration(monkeypatch):
+    """Every skinny configuration that fits; the LDS-staged kernels have no 3-bit instantiation."""
+    M, N, K = 96, 512, 768
+    d = synth.make_wna3(1601, M, N, K)
+    w = prepack(D, 1, N, K, d["wq"], d["scales"], d["zeros"])
+    ref, _ = oracle.ref_wna3(d["x"], d["wq"], d["scales"], d["zeros"], 128)
+    ran = {0: 0, 3: 0}
+    for kind in (0, 3):
+        for cfg in range(hq.hq_kernel_config_count(kind)):
+            monkeypatch.setenv("HQ_TUNE", f"kind={kind},cfg={cfg},split=1")
+            try:
+                hq.hq_gemm_plan(D, M, N, K)
+            except hq.HQError:
+                continue
+            say(f"[wna3] kind={kind} cfg={cfg}")
+            y = gemm(D, M, N, K, to_dev(d["x"]), None, w)
+            check_float(y, ref, f"wna3 kind={kind} cfg={cfg}")
+            ran[kind] += 1
+    assert ran[0] >= 20 and ran[3] == 0
+    monkeypatch.setenv("HQ_TUNE", "kind=3,cfg=0,split=1")     # refused
+    with pytest.raises(hq.HQError):
+        hq.hq_gemm_plan(D, M, N, K)
+
+
+def test_wna3_extreme_codes_and_zeros():
+    """Codes from all-zero and all-one bytes (0 and 7, and mixed codes where a code straddles two
+    bytes) against zero-points 0 and 7 (the largest |q - z|), scales over 2^-20 .. 2^20."""
+    M, N, K = 24, 128, 512
+    g = np.random.default_rng(5)
+    x = synth.normal_bf16(g, (M, K))
+    wq = np.where(g.random((N, 3 * K // 8)) < 0.5, 0x00, 0xFF).astype(np.uint8)
+    zeros = np.where(g.random((N, K // 128)) < 0.5, 0, 7).astype(np.uint8)
+    scales = synth.bf16_bits((2.0 ** g.integers(-20, 21, (N, K // 128))).astype(np.float32))
+    y = _run({"x": x, "wq": wq, "scales": scales, "zeros": zeros}, M, N, K)
+    ref, _ = oracle.ref_wna3(x, wq, scales, zeros, 128)
+    check_float(y, ref, "wna3 extremes", rounding_floor=True)
+
+
+def _experts(seed, active, N, K):
+    return {int(e): dict(synth.make_wna3(seed * 1000 + int(e), 1, N, K), bits=3) for e in active}
+
+
+def _stack(E, N, K, experts):
+    stride = hq.hq_prepacked_bytes(D, 1, N, K)
+    w = torch.zeros(stride * E, dtype=torch.uint8, device=DEV)
+    for e, wd in experts.items():
+        w[e * stride:(e + 1) * stride] = prepack(D, 1, N, K, wd["wq"], wd["scales"], wd["zeros"])
+    return w
+
+
+@pytest.mark.parametrize("T,topk,E,N,K,bm", [
+    (5, 2, 4, 64, 256, 16), (64, 8, 16, 512, 1024, 16), (150, 8, 8, 512, 384, 32),
+    (400, 8, 16, 256, 768, 64),
+])
+def test_wna3_moe(T, topk, E, N, K, bm):
+    inp = synth.make_moe_inputs(1700 + T, T, K, E, topk)
+    ids = inp["topk_ids"]
+    experts = _experts(17, np.unique(ids), N, K)
+    w = _stack(E, N, K, experts)
+    cap = hq.hq_moe_align_capacity(T, topk, E, bm)
+    so = torch.empty(cap, dtype=torch.int32, device=DEV)
+    be = torch.empty(max(cap // bm, 1), dtype=torch.int32, device=DEV)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    npad = torch.empty(1, dtype=torch.int32, device=DEV)
+    hq.hq_moe_align(to_dev(ids.astype(np.int32)), T, topk, E, bm, so, be, offs, npad)
+    y = torch.full((T * topk, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    wsb = hq.hq_moe_gemm_workspace_bytes(D, T, topk, E, N, K, bm)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    say(f"[wna3 moe] T={T} topk={topk} E={E} N={N} K={K} bm={bm}")
+    hq.hq_moe_grouped_gemm(D, T, topk, E, N, K, to_dev(inp["x"]), None, w, so, be, npad, bm,
+                           to_dev(inp["topk_weights"].reshape(-1)), y, ws, wsb)
+    torch.cuda.synchronize()
+    ref, _, valid = oracle.ref_moe_gemm(inp["x"], ids, lambda e: experts[e], N, E, 128,
+                                        topk_weights=inp["topk_weights"])
+    assert valid.all()
+    check_float(y.cpu().numpy(), ref, f"wna3 moe T={T} bm={bm}")
+
+
+def test_wna3_grouped():
+    R, E, N, K = 300, 6, 512, 512
+    counts = [80, 0, 120, 40, 59, 1]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synth.normal_bf16(synth.rng(1800, R), (R, K))
+    experts = _experts(18, [e for e in range(E) if counts[e]], N, K)
+    w = _stack(E, N, K, experts)
+    wsb = hq.hq_grouped_gemm_workspace_bytes(D, R, E, N, K)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+    y = torch.empty((R, N), dtype=torch.int16, device=DEV)
+    say("[wna3 grouped]")
+    hq.hq_grouped_gemm(D, R, E, N, K, to_dev(x), None, w, to_dev(offs), y, ws, wsb)
+    torch.cuda.synchronize()
+    ref, _, valid = oracle.ref_grouped_gemm(x, offs, lambda e: experts[e], N, E, 128)
+    assert valid.all()
+    check_float(y.cpu().numpy(), ref, "wna3 grouped")

@@ -207,3 +207,36 @@ def test_wna2_roundtrip():
     hq.hq_prepack_weights(hq.DESC_W2A16_ASYM, 1, N, K, d["wq"], d["scales"], d["zeros"], out)
     wq, s, z = unpack_wna2(out, N, K)
     assert np.array_equal(wq, d["wq"]) and np.array_equal(s, d["scales"]) and np.array_equal(z, d["zeros"])
+
+
+def unpack_wna3(buf, N, K):
+    """3-bit units of 16 channels x 128 k in 768 bytes: the low two bits as 2-bit codes (512
+    bytes), then lane l's dword at 512 + 4 l holds the high bit of code c = 2s + e of dword h in
+    bit 16 e + 8 h + s; WNA16's scale and zero regions follow."""
+    nt_n, kt_n = N // 16, K // 128
+    units = buf[:nt_n * kt_n * 768].reshape(nt_n, kt_n, 768)
+    lo = np.ascontiguousarray(units[:, :, :512]).view(np.uint32).reshape(nt_n, kt_n, 4, 16, 2)   # nt, kt, g, ch, h
+    hi = np.ascontiguousarray(units[:, :, 512:]).view(np.uint32).reshape(nt_n, kt_n, 4, 16)
+    codes = np.zeros((N, K), np.uint8)
+    for h in range(2):
+        for c in range(16):
+            s, e = c >> 1, c & 1
+            v = ((lo[..., h] >> np.uint32(16 * e + 2 * s)) & np.uint32(3)) | \
+                (((hi >> np.uint32(16 * e + 8 * h + s)) & np.uint32(1)) << np.uint32(2))
+            codes.reshape(nt_n, 16, kt_n, 4, 2, 16)[:, :, :, :, h, c] = v.astype(np.uint8).transpose(0, 3, 1, 2)
+    s_off = _a256(nt_n * kt_n * 768)
+    sc = buf[s_off:s_off + nt_n * kt_n * 32].view(np.uint16).reshape(nt_n, kt_n, 16)
+    scales = sc.transpose(0, 2, 1).reshape(N, kt_n)
+    z_off = _a256(s_off + nt_n * kt_n * 32)
+    zb = buf[z_off:z_off + nt_n * kt_n * 8].reshape(nt_n, kt_n, 8)
+    z = np.stack([zb & 0xF, zb >> 4], axis=-1).reshape(nt_n, kt_n, 16).transpose(0, 2, 1).reshape(N, kt_n)
+    return synth._pack_triplets(codes), scales, z
+
+
+def test_wna3_roundtrip():
+    N, K = 48, 384
+    d = synth.make_wna3(915, 2, N, K)
+    out = np.zeros(hq.hq_prepacked_bytes(hq.DESC_W3A16_ASYM, 1, N, K), np.uint8)
+    hq.hq_prepack_weights(hq.DESC_W3A16_ASYM, 1, N, K, d["wq"], d["scales"], d["zeros"], out)
+    wq, s, z = unpack_wna3(out, N, K)
+    assert np.array_equal(wq, d["wq"]) and np.array_equal(s, d["scales"]) and np.array_equal(z, d["zeros"])
