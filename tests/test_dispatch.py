@@ -1,0 +1,58 @@
+"""The built-in per-M dispatch (host logic, no GPU): the kernel kind and configuration a dense call
+runs at the crossovers measured on MI355X and documented beside the tables in
+quantized_gemm_prepacked_amd/csrc/gemm_dispatch.hip. Kinds: 0 small-M (skinny), 2 async-pipelined,
+3 ping-pong."""
+import pytest
+
+import quantized_gemm_prepacked_amd as hq
+
+# format: (descriptor, N, K, [(M, (kind, cfg))])
+TABLE = {
+    "w4a16": (hq.DESC_W4A16_ASYM, 14336, 4096,
+              [(1, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 2)), (128, (2, 2)), (129, (3, 3)),
+               (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
+    "w4a16mx": (hq.DESC_W4A16_MXFP4, 14336, 4096,
+                [(1, (0, 28)), (64, (0, 5)), (65, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
+    "w2a16": (hq.DESC_W2A16_ASYM, 14336, 4096,
+              [(1, (0, 28)), (128, (0, 22)), (129, (3, 13)), (512, (3, 13)), (513, (3, 0)), (8192, (3, 0))]),
+    "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096, [(1, (0, 28)), (32, (0, 29)), (8192, (0, 22))]),
+    "w8a16": (hq.DESC_W8A16_INT8, 14336, 4096,
+              [(1, (0, 27)), (32, (0, 29)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
+    "f8a16": (hq.DESC_W8A16_FP8, 14336, 4096,
+              [(1, (0, 27)), (32, (0, 22)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
+    "w8a8": (hq.DESC_W8A8, 8192, 8192,
+             [(1, (0, 1)), (32, (0, 23)), (33, (2, 3)), (256, (2, 3)), (257, (3, 11)), (512, (3, 11)),
+              (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
+    "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192, [(1, (0, 21)), (64, (0, 29)), (65, (3, 10)), (4096, (3, 10))]),
+    "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
+             [(1, (0, 21)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (640, (0, 4)), (641, (3, 10)), (4097, (3, 0))]),
+    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
+}
+
+
+@pytest.fixture(autouse=True)
+def _built_in_table(monkeypatch):
+    monkeypatch.delenv("HQ_TUNE", raising=False)
+    monkeypatch.delenv("HQ_TUNING_FILE", raising=False)
+    hq.hq_load_tuning_table(None)
+    yield
+    hq.hq_load_tuning_table(None)
+
+
+@pytest.mark.parametrize("fmt", sorted(TABLE))
+def test_built_in_dispatch(fmt):
+    desc, N, K, points = TABLE[fmt]
+    for M, (kind, cfg) in points:
+        k, c, split = hq.hq_gemm_plan(desc, M, N, K)
+        assert (k, c) == (kind, cfg), (fmt, M, (k, c))
+        assert split == 1
+
+
+def test_fallbacks_when_no_tile_divides_n():
+    # 2-bit weights on the ping-pong kernel need 256-wide tiles; 8-bit bf16-activation formats
+    # take 128 x 128; with N = 400 neither divides and the skinny kernel runs
+    for desc in (hq.DESC_W2A16_ASYM, hq.DESC_W8A16_INT8, hq.DESC_W4A16_MXFP4):
+        assert hq.hq_gemm_plan(desc, 4096, 400, 4096)[0] == 0
+    assert hq.hq_gemm_plan(hq.DESC_W2A16_ASYM, 4096, 384, 4096)[0] == 0
+    assert hq.hq_gemm_plan(hq.DESC_W8A16_INT8, 4096, 384, 4096)[0] == 3
