@@ -580,7 +580,8 @@ def run_moe_layer(args, w4a8=False):
     announcement times MoE as gate_up plus Down (section "Results: kernel microbenchmarks").
     tokens/s = T / (one layer's time); each stage is also timed on its own. w4a8: MXFP4 experts
     with tokenwise FP8 activations (the announcement's end-to-end W4A8 setting): the tokens and
-    the SiLU output are quantized per row to e4m3 (two more timed stages) before the GEMMs."""
+    the SiLU output are quantized per row to e4m3 before the GEMMs (the latter fused with the
+    gated activation: hq_moe_silu_mul_quantize)."""
     import numpy as np
     import torch
 
@@ -651,9 +652,9 @@ def run_moe_layer(args, w4a8=False):
         s = state[T]
         hq.hq_quantize_activations(hq.HQ_ACT_FP8E4M3_PER_TOKEN, T, H, s["x"], s["xq"], s["xs"], None)
 
-    def quant_act(T):
+    def silu_quant(T):     # the gated activation and its per-row e4m3 quantization in one launch
         s = state[T]
-        hq.hq_quantize_activations(hq.HQ_ACT_FP8E4M3_PER_TOKEN, T * topk, I, s["act"], s["aq"], s["as_"], None)
+        hq.hq_moe_silu_mul_quantize(hq.HQ_ACT_FP8E4M3_PER_TOKEN, T * topk, I, s["gu"], s["aq"], s["as_"], None)
 
     def gate_up(T):
         s = state[T]
@@ -680,8 +681,8 @@ def run_moe_layer(args, w4a8=False):
         hq.hq_moe_combine(T, topk, E, H, s["ids"], s["dn"], s["out"], None)
 
     if w4a8:
-        stages = {"align": align, "quant_x": quant_x, "gate_up": gate_up, "silu_mul": silu,
-                  "quant_act": quant_act, "down": down, "combine": combine}
+        stages = {"align": align, "quant_x": quant_x, "gate_up": gate_up, "silu_quant": silu_quant,
+                  "down": down, "combine": combine}
     else:
         stages = {"align": align, "gate_up": gate_up, "silu_mul": silu, "down": down, "combine": combine}
 

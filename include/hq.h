@@ -354,8 +354,16 @@ int32_t hq_version(void);
  * hq_moe_combine: out[t, n] = bf16(sum_k y[t*topk + k, n]) over the k with topk_ids[t, k] in
  *   [0, E), summed in fp32 in k order; a token with no valid k gets zeros. y bf16 [T*topk, N],
  *   out bf16 [T, N], 16-byte aligned; N % 8 == 0; topk_ids int32 [T, topk] (device).
+ * hq_moe_silu_mul_quantize: the gated activation quantized per row for a Down GEMM with 8-bit
+ *   activations (the page's tokenwise FP8 activations, section "End-to-end inference
+ *   performance"), in one launch: bit for bit hq_moe_silu_mul(R, I, gate_up, act) followed by
+ *   hq_quantize_activations(act_fmt, R, I, act, act_q, act_scale), without the bf16 act tensor.
+ *   act_fmt HQ_ACT_FP8E4M3_PER_TOKEN or HQ_ACT_INT8_PER_TOKEN; gate_up bf16 [R, 2I] (16-byte
+ *   aligned), act_q e4m3 / int8 [R, I] (16-byte aligned), act_scale fp32 [R]; I % 8 == 0.
  * ------------------------------------------------------------------------------------------- */
 hq_status hq_moe_silu_mul(int64_t R, int64_t I, const void* gate_up, void* act, hq_stream_t stream);
+hq_status hq_moe_silu_mul_quantize(int32_t act_fmt, int64_t R, int64_t I, const void* gate_up, void* act_q,
+                                   float* act_scale, hq_stream_t stream);
 hq_status hq_moe_combine(int64_t T, int32_t topk, int32_t E, int64_t N, const int32_t* topk_ids,
                          const void* y, void* out, hq_stream_t stream);
 

@@ -36,7 +36,8 @@ EXPORTED = (
     "hq_prepacked_bytes", "hq_prepack_weights", "hq_gemm_workspace_bytes", "hq_gemm",
     "hq_moe_align_capacity", "hq_moe_align_workspace_bytes", "hq_moe_align", "hq_moe_block_m",
     "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_quantize_activations",
-    "hq_moe_silu_mul", "hq_moe_combine", "hq_grouped_gemm_workspace_bytes", "hq_grouped_gemm",
+    "hq_moe_silu_mul", "hq_moe_silu_mul_quantize", "hq_moe_combine", "hq_grouped_gemm_workspace_bytes",
+    "hq_grouped_gemm",
     "hq_load_tuning_table", "hq_gemm_plan", "hq_kernel_config_count",
     "hq_last_error", "hq_version",
 )
@@ -120,6 +121,7 @@ _c = {
     "hq_gemm_plan": _sig("hq_gemm_plan", ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P),
     "hq_kernel_config_count": _sig("hq_kernel_config_count", _I32, _I32),
     "hq_moe_silu_mul": _sig("hq_moe_silu_mul", ctypes.c_int, _I64, _I64, _P, _P, _P),
+    "hq_moe_silu_mul_quantize": _sig("hq_moe_silu_mul_quantize", ctypes.c_int, _I32, _I64, _I64, _P, _P, _P, _P),
     "hq_moe_combine": _sig("hq_moe_combine", ctypes.c_int, _I64, _I32, _I32, _I64, _P, _P, _P, _P),
     "hq_last_error": _sig("hq_last_error", ctypes.c_char_p),
     "hq_version": _sig("hq_version", _I32),
@@ -254,6 +256,11 @@ def hq_quantize_activations(act_fmt, M, K, x, xq, s_tok, stream=None):
 
 def hq_moe_silu_mul(R, I, gate_up, act, stream=None):
     _check(_c["hq_moe_silu_mul"](R, I, _ptr(gate_up), _ptr(act), _stream(stream)))
+
+
+def hq_moe_silu_mul_quantize(act_fmt, R, I, gate_up, act_q, act_scale, stream=None):
+    _check(_c["hq_moe_silu_mul_quantize"](act_fmt, R, I, _ptr(gate_up), _ptr(act_q), _ptr(act_scale),
+                                          _stream(stream)))
 
 
 def hq_moe_combine(T, topk, E, N, topk_ids, y, out, stream=None):

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_ops.h"
+#include "elementwise_ops.h"
 #include "internal.h"
 
 namespace hq {
@@ -50,23 +51,37 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return sign | code;
 }
 
+// The eight codes of eight bf16 inputs (four packed pairs) at scale s, as two dwords.
 template <int ACT>
-__global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x,
-                                                             uint8_t* __restrict__ xq,
-                                                             float* __restrict__ s_tok, int K) {
-  const int row = blockIdx.x;
-  const uint16_t* xr = x + size_t(row) * K;
-  uint8_t* qr = xq + size_t(row) * K;
-
-  float amax = 0.0f;
-  for (int i = threadIdx.x * 8; i < K; i += kThreads * 8) {
-    const u32x4 v = ldg16(xr + i);
+__device__ __forceinline__ uint2 quant8(const u32x4& v, float s) {
+  uint32_t out[2] = {0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t bits = (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
+    const float q = __uint_as_float(bits) / s;
+    uint32_t code;
+    if constexpr (ACT == HQ_ACT_INT8_PER_TOKEN) {
+      code = uint32_t(int(fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f))) & 0xFFu;
+    } else {
+      code = e4m3_rne(fminf(fmaxf(q, -448.0f), 448.0f));
     }
+    out[j >> 2] |= code << (8 * (j & 3));
   }
+  return make_uint2(out[0], out[1]);
+}
+
+__device__ __forceinline__ float absmax8(float amax, const u32x4& v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(v[j] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(v[j] & 0xFFFF0000u)));
+  }
+  return amax;
+}
+
+// The row maximum over the workgroup (wave shuffles, then LDS), and the row's scale.
+template <int ACT>
+__device__ __forceinline__ float row_scale(float amax) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   __shared__ float wmax[kThreads / 64];
@@ -75,28 +90,71 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __r
   amax = wmax[0];
 #pragma unroll
   for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
-
   float s = amax / (ACT == HQ_ACT_INT8_PER_TOKEN ? 127.0f : 448.0f);
-  if (s == 0.0f) s = 1.0f;
-  if (threadIdx.x == 0) s_tok[row] = s;
+  return s == 0.0f ? 1.0f : s;
+}
 
-  for (int i = threadIdx.x * 8; i < K; i += kThreads * 8) {
-    const u32x4 v = ldg16(xr + i);
-    uint32_t out[2] = {0u, 0u};
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ xq,
+                                                             float* __restrict__ s_tok, int K) {
+  const int row = blockIdx.x;
+  const uint16_t* xr = x + size_t(row) * K;
+  uint8_t* qr = xq + size_t(row) * K;
+  float amax = 0.0f;
+  for (int i = threadIdx.x * 8; i < K; i += kThreads * 8) amax = absmax8(amax, ldg16(xr + i));
+  const float s = row_scale<ACT>(amax);
+  if (threadIdx.x == 0) s_tok[row] = s;
+  for (int i = threadIdx.x * 8; i < K; i += kThreads * 8)
+    *reinterpret_cast<uint2*>(qr + i) = quant8<ACT>(ldg16(xr + i), s);
+}
+
+// Eight gated activations bf16(silu(g) * u) of a gate_up row [g (I) | u (I)] at column i,
+// computed exactly as the SiLU-gated activation kernel of the MoE layer does.
+__device__ __forceinline__ u32x4 gated8(const uint16_t* gr, int I, int i) {
+  const u32x4 g = ldg16(gr + i);
+  const u32x4 u = ldg16(gr + I + i);
+  u32x4 out;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t bits = (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
-      const float q = __uint_as_float(bits) / s;
-      uint32_t code;
-      if constexpr (ACT == HQ_ACT_INT8_PER_TOKEN) {
-        code = uint32_t(int(fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f))) & 0xFFu;
-      } else {
-        code = e4m3_rne(fminf(fmaxf(q, -448.0f), 448.0f));
-      }
-      out[j >> 2] |= code << (8 * (j & 3));
-    }
-    *reinterpret_cast<uint2*>(qr + i) = make_uint2(out[0], out[1]);
+  for (int j = 0; j < 4; ++j) {
+    const float a0 = silu(__uint_as_float(g[j] << 16)) * __uint_as_float(u[j] << 16);
+    const float a1 = silu(__uint_as_float(g[j] & 0xFFFF0000u)) * __uint_as_float(u[j] & 0xFFFF0000u);
+    out[j] = uint32_t(f32_to_bf16_rne(a0)) | (uint32_t(f32_to_bf16_rne(a1)) << 16);
   }
+  return out;
+}
+
+// The gated activation of a row quantized per row: the same chunks per thread as act_quant_kernel
+// (column tid * 8 + c * 2048), the first kKeep chunks computed once and kept in registers between
+// the maximum and the quantization, any further ones (I > 8192) computed again.
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void silu_quant_kernel(const uint16_t* __restrict__ gu,
+                                                              uint8_t* __restrict__ aq,
+                                                              float* __restrict__ s_out, int I) {
+  constexpr int kKeep = 4;
+  const int row = blockIdx.x;
+  const uint16_t* gr = gu + size_t(row) * 2 * I;
+  uint8_t* qr = aq + size_t(row) * I;
+  u32x4 a[kKeep];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kKeep; ++c) {
+    const int i = (c * kThreads + threadIdx.x) * 8;
+    if (i < I) {
+      a[c] = gated8(gr, I, i);
+      amax = absmax8(amax, a[c]);
+    }
+  }
+  for (int i = (kKeep * kThreads + threadIdx.x) * 8; i < I; i += kThreads * 8) amax = absmax8(amax, gated8(gr, I, i));
+  const float s = row_scale<ACT>(amax);
+  if (threadIdx.x == 0) s_out[row] = s;
+#pragma unroll
+  for (int c = 0; c < kKeep; ++c) {
+    const int i = (c * kThreads + threadIdx.x) * 8;
+    if (i < I) *reinterpret_cast<uint2*>(qr + i) = quant8<ACT>(a[c], s);
+  }
+  for (int i = (kKeep * kThreads + threadIdx.x) * 8; i < I; i += kThreads * 8)
+    *reinterpret_cast<uint2*>(qr + i) = quant8<ACT>(gated8(gr, I, i), s);
 }
 
 // e2m1 magnitude code of a >= 0 (exact binary32), ties to the even code, saturating at 6.
@@ -251,6 +309,20 @@ hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, vo
     hipLaunchKernelGGL(act_quant_kernel<HQ_ACT_INT8_PER_TOKEN>, grid, dim3(kThreads), 0, stream, xin, out, s_tok, int(K));
   else
     hipLaunchKernelGGL(act_quant_kernel<HQ_ACT_FP8E4M3_PER_TOKEN>, grid, dim3(kThreads), 0, stream, xin, out, s_tok, int(K));
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(int act_fmt, int64_t R, int64_t I, const void* gate_up, void* act_q,
+                                 float* act_scale, hipStream_t stream) {
+  const dim3 grid{static_cast<unsigned>(R)};
+  const auto* gu = static_cast<const uint16_t*>(gate_up);
+  auto* out = static_cast<uint8_t*>(act_q);
+  if (act_fmt == HQ_ACT_INT8_PER_TOKEN)
+    hipLaunchKernelGGL(silu_quant_kernel<HQ_ACT_INT8_PER_TOKEN>, grid, dim3(kThreads), 0, stream, gu, out,
+                       act_scale, int(I));
+  else
+    hipLaunchKernelGGL(silu_quant_kernel<HQ_ACT_FP8E4M3_PER_TOKEN>, grid, dim3(kThreads), 0, stream, gu, out,
+                       act_scale, int(I));
   return hipGetLastError();
 }
 

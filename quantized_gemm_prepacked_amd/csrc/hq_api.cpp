@@ -376,6 +376,23 @@ hq_status hq_moe_silu_mul(int64_t R, int64_t I, const void* gate_up, void* act, 
                    "hq_moe_silu_mul launch");
 }
 
+hq_status hq_moe_silu_mul_quantize(int32_t act_fmt, int64_t R, int64_t I, const void* gate_up, void* act_q,
+                                   float* act_scale, hq_stream_t stream) {
+  if (act_fmt != HQ_ACT_INT8_PER_TOKEN && act_fmt != HQ_ACT_FP8E4M3_PER_TOKEN)
+    return fail(HQ_ERR_UNSUPPORTED, "act_fmt=%d: INT8 or FP8 e4m3 per token", act_fmt);
+  if (R < 0 || R > kMaxDim || I <= 0 || I > kMaxDim)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "R=%lld I=%lld out of range", (long long)R, (long long)I);
+  if (I % 8 != 0) return fail(HQ_ERR_UNSUPPORTED, "I=%lld must be a multiple of 8", (long long)I);
+  if (R * I > (int64_t(1) << 40)) return fail(HQ_ERR_UNSUPPORTED, "R*I must stay below 2^40");
+  if (R == 0) return ok();
+  if (!gate_up || !act_q || !act_scale)
+    return fail(HQ_ERR_INVALID_ARGUMENT, "gate_up, act_q and act_scale must be non-NULL");
+  if (!aligned16(gate_up) || !aligned16(act_q) || (reinterpret_cast<uintptr_t>(act_scale) & 3u))
+    return fail(HQ_ERR_INVALID_ARGUMENT, "gate_up and act_q must be 16-byte aligned, act_scale 4-byte aligned");
+  return check_hip(hq::launch_silu_mul_quant(act_fmt, R, I, gate_up, act_q, act_scale, static_cast<hipStream_t>(stream)),
+                   "hq_moe_silu_mul_quantize launch");
+}
+
 hq_status hq_moe_combine(int64_t T, int32_t topk, int32_t E, int64_t N, const int32_t* topk_ids,
                          const void* y, void* out, hq_stream_t stream) {
   if (T < 0 || T > kMaxDim || topk <= 0 || topk > 64 || E <= 0 || N <= 0 || N > kMaxDim)

@@ -74,6 +74,8 @@ hipError_t launch_moe_combine(int64_t T, int32_t topk, int32_t E, int64_t N, con
                               const void* y, void* out, hipStream_t s);
 hipError_t launch_act_quant(int act_fmt, int64_t M, int64_t K, const void* x, void* xq, float* s_tok,
                             hipStream_t stream);
+hipError_t launch_silu_mul_quant(int act_fmt, int64_t R, int64_t I, const void* gate_up, void* act_q,
+                                 float* act_scale, hipStream_t stream);
 hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
                             int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                             int32_t* expert_offsets, int32_t* num_padded, void* ws,

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_ops.h"
+#include "elementwise_ops.h"
 #include "internal.h"
 
 namespace hq {
@@ -19,14 +20,6 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// silu(g) = g * sigmoid(g), with sigmoid(g) = 1 / (1 + e) for g >= 0 and e / (1 + e) for g < 0,
-// e = exp(-|g|): e never overflows, so a very negative gate keeps its tiny product instead of
-// dividing by an infinite exp(-g).
-__device__ __forceinline__ float silu(float g) {
-  const float e = expf(-fabsf(g));
-  return g * ((g >= 0.0f ? 1.0f : e) / (1.0f + e));
-}
 
 // act[r, i] = bf16(silu(g) * u), g = gu[r, i], u = gu[r, I + i]; 8 outputs per thread.
 __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const uint16_t* __restrict__ gu,

@@ -312,3 +312,39 @@ def test_moe_layer_w4a8(T, topk, E, H, I):
     _check_rounded(got["out"], out64, delta, "combine")
     ref = oracle.ref_moe_layer_w4a8(L.x, L.ids, L.tw, lambda e: L.gu_w[e], lambda e: L.dn_w[e], I, H, E)
     check_float(got["out"], bf16_to_f64(ref["out"]), "layer out w4a8 vs the oracle's layer")
+
+
+@pytest.mark.parametrize("R,I", [(37, 256), (5, 2048), (300, 1024)])
+@pytest.mark.parametrize("act_fmt", [hq.HQ_ACT_FP8E4M3_PER_TOKEN, hq.HQ_ACT_INT8_PER_TOKEN])
+def test_silu_mul_quantize_is_the_two_calls(R, I, act_fmt):
+    """The fused gated activation + per-row quantization equals hq_moe_silu_mul followed by
+    hq_quantize_activations bit for bit (codes and scales), and its codes are the oracle's
+    quantizer applied to that gated activation. Gates include large magnitudes of both signs and a
+    zero row."""
+    g = synth.rng(70 + R, I)
+    gu32 = g.standard_normal((R, 2 * I)).astype(np.float32) * np.float32(3.0)
+    gu32[0, :8] = [-100.0, -30.0, 30.0, 100.0, 0.0, -0.0, 1e-30, -1e-30]
+    gu32[R - 1] = 0.0                                           # an all-zero row: scale 1, codes 0
+    gu = to_dev(synth.bf16_bits(gu32))
+    act = torch.empty((R, I), dtype=torch.int16, device=DEV)
+    q2 = torch.empty((R, I), dtype=torch.uint8, device=DEV)
+    s2 = torch.empty(R, dtype=torch.float32, device=DEV)
+    q1 = torch.full((R, I), 0xAB, dtype=torch.uint8, device=DEV)
+    s1 = torch.full((R,), -1.0, dtype=torch.float32, device=DEV)
+    say(f"[silu_mul_quantize] R={R} I={I} act_fmt={act_fmt}")
+    hq.hq_moe_silu_mul(R, I, gu, act)
+    hq.hq_quantize_activations(act_fmt, R, I, act, q2, s2)
+    hq.hq_moe_silu_mul_quantize(act_fmt, R, I, gu, q1, s1)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+    kind = "e4m3" if act_fmt == hq.HQ_ACT_FP8E4M3_PER_TOKEN else "int8"
+    qo, so = oracle.quantize_per_token(act.cpu().numpy().view(np.uint16), kind)
+    assert np.array_equal(q1.cpu().numpy(), qo.view(np.uint8)) and np.array_equal(s1.cpu().numpy(), so)
+
+
+def test_silu_mul_quantize_rejections():
+    with pytest.raises(hq.HQError):
+        hq.hq_moe_silu_mul_quantize(hq.HQ_ACT_MXFP4, 4, 64, 16, 16, 16)        # per-token formats only
+    with pytest.raises(hq.HQError):
+        hq.hq_moe_silu_mul_quantize(hq.HQ_ACT_FP8E4M3_PER_TOKEN, 4, 60, 16, 16, 16)   # I % 8
+    hq.hq_moe_silu_mul_quantize(hq.HQ_ACT_FP8E4M3_PER_TOKEN, 0, 64, 0, 0, 0)   # R = 0: no-op
