@@ -6,11 +6,15 @@
 // multiple of block_m with sentinel T*topk) is the library's (hq.h).
 //
 // One workgroup of 1024 threads: (1) per-expert histogram with LDS atomics (order-free),
-// (2) block-wide scan of the padded counts, (3) stable scatter in tiles of 1024 entries: inside a
-// wave, entries of the same expert are found with ballots over the expert id bits and ranked by
-// lane; across the 16 waves of a tile, per-wave counts are prefix-summed in wave order; across
-// tiles a running count per expert carries on. Every position is therefore a pure function of
-// the input, independent of scheduling.
+// (2) block-wide scan of the padded counts (wave shuffles, then over the wave totals),
+// (3) stable scatter in tiles of 1024 entries: inside a wave, entries of the same expert are
+// found with ballots over the expert id bits and ranked by lane; across the 16 waves of a tile,
+// per-wave counts are prefix-summed in wave order; across tiles a running count per expert
+// carries on. Every position is therefore a pure function of the input, independent of
+// scheduling. The ids are read in chunks of 8 tiles, each thread issuing its 8 loads together
+// and keeping them in registers, so a chunk costs one memory latency rather than eight; the first
+// chunk (8192 entries, e.g. 1024 tokens at top-8) is read once for both the histogram and the
+// scatter.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -24,6 +28,43 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kIdBits = 11;  // expert ids < 2048; id E marks an unrouted entry
+constexpr int kPer = 8;      // ids each thread holds in registers: one chunk = kPer tiles of kThreads
+
+// Entries [c0, c0 + kPer * kThreads) of the flat id list, thread tid holding c0 + j * kThreads + tid
+// in e[j] (-1 past the end); all loads issued before any is used.
+__device__ void load_chunk(const int32_t* __restrict__ ids, int n_flat, int c0, int (&e)[kPer]) {
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = c0 + j * kThreads + int(threadIdx.x);
+    e[j] = i < n_flat ? ids[i] : -1;
+  }
+}
+
+// Inclusive prefix sum of v over the kThreads threads of the workgroup, in thread order:
+// shuffles inside each wave, then over the kWaves wave totals in wave 0. tmp: 2 * kWaves ints of
+// LDS, not touched by the caller between the call and its return. Two barriers.
+__device__ int block_inclusive_scan(int v, int* tmp) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) tmp[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kWaves ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWaves; off <<= 1) {
+      const int t = __shfl_up(w, off, 64);
+      if (lane >= off) w += t;
+    }
+    if (lane < kWaves) tmp[kWaves + lane] = w;   // total of waves 0 .. lane
+  }
+  __syncthreads();
+  return wave > 0 ? v + tmp[kWaves + wave - 1] : v;
+}
 
 __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __restrict__ ids,
                                                              int n_flat, int E, int bm,
@@ -36,8 +77,8 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
   int* cnt = sm;               // [E]
   int* offs = cnt + E;         // [E + 1]
   int* run = offs + E + 1;     // [E]
-  int* scan = run + E;         // [kThreads]
-  int* wc = scan + kThreads;   // [kWaves][E]
+  int* scan = run + E;         // [2 * kWaves], the scan's wave totals
+  int* wc = scan + 2 * kWaves; // [kWaves][E]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -46,25 +87,28 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
     cnt[e] = 0;
     run[e] = 0;
   }
+  for (int j = tid; j < kWaves * E; j += kThreads) wc[j] = 0;
+  // The first chunk stays in registers for the scatter (one chunk covers n_flat <= 8192).
+  int ec[kPer];
+  load_chunk(ids, n_flat, 0, ec);
   __syncthreads();
-  for (int i = tid; i < n_flat; i += kThreads) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (ec[j] >= 0 && ec[j] < E) atomicAdd(&cnt[ec[j]], 1);
+  for (int c0 = kPer * kThreads; c0 < n_flat; c0 += kPer * kThreads) {
+    int e[kPer];
+    load_chunk(ids, n_flat, c0, e);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (e[j] >= 0 && e[j] < E) atomicAdd(&cnt[e[j]], 1);
   }
   __syncthreads();
 
   // Exclusive scan of padded counts; E <= kThreads is checked on the host, E may be < kThreads.
   const int padded = tid < E ? (cnt[tid] + bm - 1) / bm * bm : 0;
-  scan[tid] = padded;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int t = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += t;
-    __syncthreads();
-  }
-  if (tid < E) offs[tid] = scan[tid] - padded;
-  if (tid == E - 1) offs[E] = scan[tid];
+  const int incl = block_inclusive_scan(padded, scan);
+  if (tid < E) offs[tid] = incl - padded;
+  if (tid == E - 1) offs[E] = incl;
   __syncthreads();
   const int total = offs[E];
   for (int e = tid; e <= E; e += kThreads) offsets_out[e] = offs[e];
@@ -85,37 +129,45 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
   // blocks past the sorted rows (up to the capacity) get no expert
   for (int b = (total + bm - 1) / bm + tid; b < max_blocks; b += kThreads) block_expert[b] = -1;
 
-  // Stable scatter.
+  // Stable scatter, one tile of kThreads entries at a time. wc is zero at the start of every tile:
+  // zeroed above, then by the running-count update that reads it.
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int t0 = 0; t0 < n_flat; t0 += kThreads) {
-    for (int j = tid; j < kWaves * E; j += kThreads) wc[j] = 0;
-    __syncthreads();
-    const int i = t0 + tid;
-    int e = i < n_flat ? ids[i] : -1;
-    const bool valid = e >= 0 && e < E;
-    const int key = valid ? e : E;
-    uint64_t same = ~0ull;
+  for (int c0 = 0; c0 < n_flat; c0 += kPer * kThreads) {
+    if (c0 > 0) load_chunk(ids, n_flat, c0, ec);
 #pragma unroll
-    for (int b = 0; b < kIdBits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      same &= bit ? bal : ~bal;
+    for (int jt = 0; jt < kPer; ++jt) {
+      const int t0 = c0 + jt * kThreads;
+      if (t0 >= n_flat) break;  // the same for every thread
+      const int i = t0 + tid;
+      const int e = ec[jt];
+      const bool valid = e >= 0 && e < E;
+      const int key = valid ? e : E;
+      uint64_t same = ~0ull;
+#pragma unroll
+      for (int b = 0; b < kIdBits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+      }
+      const int rank = __popcll(same & below);
+      if (valid && rank == 0) wc[wave * E + e] = __popcll(same);
+      __syncthreads();
+      if (valid) {
+        int base = run[e];
+        for (int w = 0; w < wave; ++w) base += wc[w * E + e];
+        sorted[offs[e] + base + rank] = i;
+      }
+      __syncthreads();
+      for (int x = tid; x < E; x += kThreads) {
+        int sum = 0;
+        for (int w = 0; w < kWaves; ++w) {
+          sum += wc[w * E + x];
+          wc[w * E + x] = 0;
+        }
+        run[x] += sum;
+      }
+      __syncthreads();
     }
-    const int rank = __popcll(same & below);
-    if (valid && rank == 0) wc[wave * E + e] = __popcll(same);
-    __syncthreads();
-    if (valid) {
-      int base = run[e];
-      for (int w = 0; w < wave; ++w) base += wc[w * E + e];
-      sorted[offs[e] + base + rank] = i;
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += kThreads) {
-      int s = 0;
-      for (int w = 0; w < kWaves; ++w) s += wc[w * E + x];
-      run[x] += s;
-    }
-    __syncthreads();
   }
 }
 
@@ -131,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void grouped_index_kernel(const int32_t* 
                                                                  int32_t* __restrict__ sorted,
                                                                  int32_t* __restrict__ block_expert,
                                                                  int32_t* __restrict__ num_padded) {
-  __shared__ int lo_s[kThreads], cnt_s[kThreads], scan[kThreads];
+  __shared__ int lo_s[kThreads], cnt_s[kThreads], scan[kThreads], wtot[2 * kWaves];
   const int tid = threadIdx.x;
   int padded = 0;
   if (tid < E) {
@@ -141,14 +193,8 @@ __global__ __launch_bounds__(kThreads) void grouped_index_kernel(const int32_t* 
     cnt_s[tid] = max(hi - lo, 0);
     padded = (cnt_s[tid] + bm - 1) / bm * bm;
   }
-  scan[tid] = padded;
+  scan[tid] = block_inclusive_scan(padded, wtot);
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int t = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += t;
-    __syncthreads();
-  }
   const int total = min(scan[E - 1], cap);   // inclusive scan: scan[e] = end of expert e's range
   if (blockIdx.x == 0 && tid == 0) *num_padded = total;
   for (int pos = blockIdx.x * kThreads + tid; pos < cap; pos += gridDim.x * kThreads) {
@@ -185,7 +231,7 @@ hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, in
                             int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                             int32_t* expert_offsets, int32_t* num_padded, void*,
                             hipStream_t stream) {
-  const size_t smem = sizeof(int) * (size_t(E) * 3 + 1 + kThreads + size_t(kWaves) * E);
+  const size_t smem = sizeof(int) * (size_t(E) * 3 + 1 + 2 * kWaves + size_t(kWaves) * E);
   hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kThreads), smem, stream, topk_ids,
                      int(T * topk), int(E), int(block_m), sorted_ids, block_expert,
                      expert_offsets, num_padded,

@@ -61,12 +61,21 @@ def test_moe_align_hand_case():
     assert got["block_expert"].tolist() == [0, 2, 3]
 
 
-@pytest.mark.parametrize("T", [1, 3, 32, 512, 4096])
+@pytest.mark.parametrize("T", [1, 3, 32, 512, 1100, 4096])
 @pytest.mark.parametrize("bm", [16, 64])
 def test_moe_align_skewed_routing(T, bm):
+    # 1100 x 8 = 8800 entries: a second chunk of 8192 entries that ends inside its first tile
     say(f"[moe_align] T={T} bm={bm}")
     ids = synth.make_moe_inputs(5, T, 64)["topk_ids"]
     _check_align(ids, 256, bm)
+
+
+@pytest.mark.parametrize("T,topk", [(5, 8), (2600, 4)])
+def test_moe_align_512_experts(T, topk):
+    # the largest expert count the sort takes; 2600 x 4 = 10400 entries span two chunks
+    ids = np.random.default_rng(T).integers(0, 512, (T, topk)).astype(np.int32)
+    say(f"[moe_align] E=512 T={T} topk={topk}")
+    _check_align(ids, 512, 16)
 
 
 def test_moe_align_out_of_range_ids_and_small_E():
