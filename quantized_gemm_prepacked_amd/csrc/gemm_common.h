@@ -93,10 +93,14 @@ __device__ __forceinline__ void store_result(const KParams& p, const uint8_t* w,
 
 // A skinny-kernel instantiation: MB row blocks of 16, NTW channel tiles of 16, NW waves that
 // split K, UNR units per batch; pp = 1 double-buffers batches (next batch in flight while the
-// current one is computed).
+// current one is computed); few = 1 (MB = 1, dense only, M <= kFewRows): only the first rows of
+// the block are copied and reduced -- one 1 KiB activation copy per unit, the other MFMA rows
+// repeating them and never stored.
 struct SkinnyCfg {
   int mb, ntw, nw, unr, pp;
+  int few = 0;
 };
+constexpr int kFewRows = 4;
 const SkinnyCfg* skinny_configs(int* count);
 int skinny_lds_bytes(int fam, int cfg);
 

@@ -47,9 +47,22 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
   auto first_fit = [&](std::initializer_list<int> cands) {
     for (int i : cands)
-      if (nt % cfgs[i].ntw == 0 && skinny_lds_bytes(c.fam, i) <= 160 * 1024) return i;
+      if (nt % cfgs[i].ntw == 0 && skinny_lds_bytes(c.fam, i) <= 160 * 1024 &&
+          (!cfgs[i].few || rows <= kFewRows))
+        return i;
     return 2;  // NTW = 1 always fits (same rows as the candidates' fallback)
   };
+  if (rows <= kFewRows) {
+    // bf16 activations: the few-row forms (one activation copy per unit instead of four).
+    // N=14336 K=4096 M=1, few-row form against the best whole-block one: INT4 9.25 / 9.60 us,
+    // MXFP4 8.53 / 8.88, UINT2 8.00 / 8.78, UINT3 10.80 / 11.49, INT8 13.00 / 13.10, FP8 12.07 /
+    // 12.32.
+    if (c.fam == FAM_WNA16) return first_fit({30, 28, 13, 0, 1, 2});
+    if (c.fam == FAM_MXW4A16) return first_fit({32, 30, 28, 13, 0, 1, 2});
+    if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({31, 30, 28, 13, 0, 1, 2});
+    if (c.fam == FAM_W8A16) return first_fit({33, 31, 27, 0, 1, 2});
+    if (c.fam == FAM_F8A16) return first_fit({30, 31, 27, 0, 1, 2});
+  }
   if (rows <= 16) {
     if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({28, 13, 0, 1, 2});
     // 8-bit weights with bf16 activations, N=14336 K=4096: 16 waves of 64 channels, two units in
@@ -272,7 +285,8 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
   if (o.kind == 0) {
     const SkinnyCfg* cfgs = skinny_configs(&n);
     return o.cfg < 0 || (o.cfg < n && (N / 16) % cfgs[o.cfg].ntw == 0 &&
-                         skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024);
+                         skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024 &&
+                         (!cfgs[o.cfg].few || M <= kFewRows));
   }
   if (pp_only(c) && (o.kind == 1 || o.kind == 2)) return false;
   if (o.kind == 1) {
@@ -378,7 +392,7 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   int n_cfg = 0;
   const SkinnyCfg* cfgs = skinny_configs(&n_cfg);
   if (tov.kind == 0 && tov.cfg >= 0 && tov.cfg < n_cfg && (N / 16) % cfgs[tov.cfg].ntw == 0 &&
-      skinny_lds_bytes(c.fam, tov.cfg) <= 160 * 1024)
+      skinny_lds_bytes(c.fam, tov.cfg) <= 160 * 1024 && (!cfgs[tov.cfg].few || M <= kFewRows))
     pl.cfg = tov.cfg;
   const SkinnyCfg& sc = cfgs[pl.cfg];
   const int64_t units = K / k_unit(c);
@@ -409,7 +423,7 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   if (tov.kind == 0) {
     int n_s = 0;
     const SkinnyCfg* sc = skinny_configs(&n_s);
-    const bool fits = tov.cfg >= 0 && tov.cfg < n_s && 16 * sc[tov.cfg].mb == block_m &&
+    const bool fits = tov.cfg >= 0 && tov.cfg < n_s && 16 * sc[tov.cfg].mb == block_m && !sc[tov.cfg].few &&
                       (N / 16) % sc[tov.cfg].ntw == 0 && skinny_lds_bytes(c.fam, tov.cfg) <= 160 * 1024;
     pl.kind = fits ? 0 : -1;
     pl.cfg = tov.cfg;

@@ -84,12 +84,14 @@ struct SkTraits<FAM_W4A4> {
   static constexpr int kRowBytes = 64, kUnitK = 128, kScaleBytes = 64, kZeroBytes = 0, kAScaleBytes = 4;
 };
 
-template <int FAM, int MB, int NTW, int NW, int UNR, bool PP>
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool FEW = false>
 struct SkShape {
   using T = SkTraits<FAM>;
   static constexpr int ROWB = T::kRowBytes;              // activation bytes per row per unit
   static constexpr int CPR = ROWB / 16;
-  static constexpr int A_UNIT = 16 * MB * ROWB;
+  // FEW: the rows one 1 KiB copy holds (4 .. 16) are the live ones
+  static constexpr int LIVE = FEW ? (1024 / ROWB < 16 ? 1024 / ROWB : 16) : 16 * MB;
+  static constexpr int A_UNIT = LIVE * ROWB;
   static constexpr int A_INSTR = A_UNIT / 1024;         // copies of a unit's activation rows
   static constexpr int SC = NTW * T::kScaleBytes;       // per unit, all tiles
   static constexpr int ZB = NTW * T::kZeroBytes;
@@ -106,11 +108,12 @@ struct SkShape {
   static_assert(A_UNIT % 1024 == 0, "whole-wave activation copies");
   static_assert(SC / 16 <= 64 && ZB / 4 <= 64 && ASC / 4 <= 64, "metadata copies fit one instruction each");
   static_assert(UNR * UNIT_INSTR < 64, "vmcnt range");
+  static_assert(!FEW || (MB == 1 && LIVE >= kFewRows), "few-row form: one 16-row block");
 };
 
-template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE>
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE, bool FEW>
 __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
-  using Sh = SkShape<FAM, MB, NTW, NW, UNR, PP>;
+  using Sh = SkShape<FAM, MB, NTW, NW, UNR, PP, FEW>;
   using Acc = typename AccType<FAM>::type;
   using Elem = typename AccType<FAM>::elem;
   using T = SkTraits<FAM>;
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   auto compute_unit = [&](int buf, int r) __attribute__((always_inline)) {
     const uint8_t* slot = wlds + (buf * UNR + r) * Sh::UNIT_LDS;
     auto read_a = [&](int mb, int chunk) __attribute__((always_inline)) -> u32x4 {
-      const int row = 16 * mb + (lane & 15);
+      const int row = FEW ? (lane & (Sh::LIVE - 1)) : 16 * mb + (lane & 15);
       return *reinterpret_cast<const u32x4*>(slot + row * ROWB + 16 * lds_chunk_swizzle(row, chunk, CPR));
     };
     if constexpr (family_int_groups(FAM)) {
@@ -414,19 +417,24 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 
   // Sum the waves' tiles through LDS (fixed order: wave 0, 1, ...), then the epilogue. The
   // reduction buffer aliases the unit slots: every wave has finished with its slot first.
+  // Output rows 4 (lane >> 4) + j: in the few-row form only lane groups below LIVE / 4 hold live
+  // rows.
   constexpr int kVals = MB * NTW * 4;
   Elem(*red)[kVals][64] = reinterpret_cast<Elem(*)[kVals][64]>(smem);
   __syncthreads();
+  if (!FEW || (lane >> 4) < Sh::LIVE / 4) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red[wave][(mb * NTW + t) * 4 + j][lane] = acc[mb][t][j];
+        for (int j = 0; j < 4; ++j) red[wave][(mb * NTW + t) * 4 + j][lane] = acc[mb][t][j];
+  }
   __syncthreads();
   static_assert(NW > 1, "the epilogue reads the waves' tiles from LDS");
   for (int v = threadIdx.x; v < kVals * 64; v += NW * 64) {
     const int le = v & 63;
+    if (FEW && (le >> 4) >= Sh::LIVE / 4) continue;
     const int q = v >> 6;
     const int j = q & 3;
     const int t = (q >> 2) % NTW;
@@ -477,6 +485,11 @@ static constexpr SkinnyCfg kSkinny[] = {
     {1, 4, 16, 2, 0},  // 27: M <= 16, 16 waves
     {1, 4, 16, 1, 1},  // 28
     {2, 4, 8, 2, 0},   // 29: M <= 32, 8 waves
+    {1, 4, 16, 1, 1, 1},  // 30: M <= 4, the few-row forms of 28, 27, 13, 0, 20
+    {1, 4, 16, 2, 0, 1},  // 31
+    {1, 4, 8, 1, 1, 1},   // 32
+    {1, 4, 8, 2, 0, 1},   // 33
+    {1, 2, 16, 1, 1, 1},  // 34
 };
 
 const SkinnyCfg* skinny_configs(int* count) {
@@ -487,7 +500,7 @@ const SkinnyCfg* skinny_configs(int* count) {
 template <int FAM, int... I>
 static int skinny_lds_table(int cfg, std::integer_sequence<int, I...>) {
   static const int t[] = {SkShape<FAM, kSkinny[I].mb, kSkinny[I].ntw, kSkinny[I].nw, kSkinny[I].unr,
-                                  kSkinny[I].pp != 0>::LDS...};
+                                  kSkinny[I].pp != 0, kSkinny[I].few != 0>::LDS...};
   return t[cfg];
 }
 
@@ -508,13 +521,14 @@ int skinny_lds_bytes(int fam, int cfg) {
   return skinny_lds_table<FAM_W4A8>(cfg, seq);
 }
 
-template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE>
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE, bool FEW>
 static hipError_t launch_skinny_one(const KParams& p, dim3 grid, hipStream_t s) {
-  constexpr int lds = SkShape<FAM, MB, NTW, NW, UNR, PP>::LDS;
-  if constexpr (lds > 160 * 1024) {
+  constexpr int lds = SkShape<FAM, MB, NTW, NW, UNR, PP, FEW>::LDS;
+  if constexpr (lds > 160 * 1024 || (MOE && FEW)) {   // MoE row blocks are always whole
     return hipErrorInvalidValue;
   } else {
-    auto kern = skinny_gemm_kernel<FAM, MB, NTW, NW, UNR, PP, MOE>;
+    if (FEW && p.M > kFewRows) return hipErrorInvalidValue;
+    auto kern = skinny_gemm_kernel<FAM, MB, NTW, NW, UNR, PP, MOE, FEW>;
     if (lds > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, p);
@@ -527,11 +541,12 @@ static hipError_t launch_skinny_fam(const KParams& p, int cfg, dim3 grid, hipStr
 #define HQ_SK(I)                                                                           \
   case I:                                                                                  \
     return launch_skinny_one<FAM, kSkinny[I].mb, kSkinny[I].ntw, kSkinny[I].nw,            \
-                             kSkinny[I].unr, kSkinny[I].pp != 0, MOE>(p, grid, s);
+                             kSkinny[I].unr, kSkinny[I].pp != 0, MOE, kSkinny[I].few != 0>(p, grid, s);
   switch (cfg) {
     HQ_SK(0) HQ_SK(1) HQ_SK(2) HQ_SK(3) HQ_SK(4) HQ_SK(5) HQ_SK(6) HQ_SK(7) HQ_SK(8) HQ_SK(9)
     HQ_SK(10) HQ_SK(11) HQ_SK(12) HQ_SK(13) HQ_SK(14) HQ_SK(15) HQ_SK(16) HQ_SK(17) HQ_SK(18)
     HQ_SK(19) HQ_SK(20) HQ_SK(21) HQ_SK(22) HQ_SK(23) HQ_SK(24) HQ_SK(25) HQ_SK(26) HQ_SK(27) HQ_SK(28) HQ_SK(29)
+    HQ_SK(30) HQ_SK(31) HQ_SK(32) HQ_SK(33) HQ_SK(34)
     default:
       return hipErrorInvalidValue;
   }

@@ -9,17 +9,17 @@ import quantized_gemm_prepacked_amd as hq
 # format: (descriptor, N, K, [(M, (kind, cfg))])
 TABLE = {
     "w4a16": (hq.DESC_W4A16_ASYM, 14336, 4096,
-              [(1, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 2)), (128, (2, 2)), (129, (3, 3)),
+              [(1, (0, 30)), (4, (0, 30)), (5, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 2)), (128, (2, 2)), (129, (3, 3)),
                (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w4a16mx": (hq.DESC_W4A16_MXFP4, 14336, 4096,
-                [(1, (0, 28)), (64, (0, 5)), (65, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
+                [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 5)), (65, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w2a16": (hq.DESC_W2A16_ASYM, 14336, 4096,
-              [(1, (0, 28)), (128, (0, 22)), (129, (3, 13)), (512, (3, 13)), (513, (3, 0)), (8192, (3, 0))]),
-    "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096, [(1, (0, 28)), (32, (0, 29)), (8192, (0, 22))]),
+              [(1, (0, 31)), (4, (0, 31)), (5, (0, 28)), (128, (0, 22)), (129, (3, 13)), (512, (3, 13)), (513, (3, 0)), (8192, (3, 0))]),
+    "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096, [(1, (0, 31)), (5, (0, 28)), (32, (0, 29)), (8192, (0, 22))]),
     "w8a16": (hq.DESC_W8A16_INT8, 14336, 4096,
-              [(1, (0, 27)), (32, (0, 29)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
+              [(1, (0, 33)), (4, (0, 33)), (5, (0, 27)), (32, (0, 29)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
     "f8a16": (hq.DESC_W8A16_FP8, 14336, 4096,
-              [(1, (0, 27)), (32, (0, 22)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
+              [(1, (0, 30)), (5, (0, 27)), (32, (0, 22)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
     "w8a8": (hq.DESC_W8A8, 8192, 8192,
              [(1, (0, 1)), (32, (0, 23)), (33, (2, 3)), (256, (2, 3)), (257, (3, 11)), (512, (3, 11)),
               (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
