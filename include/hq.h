@@ -312,11 +312,12 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
  * `python -m quantized_gemm_prepacked_amd.autotune` (the roadmap's autotune, run offline) takes
  * precedence for the shapes it lists. Text, one entry per line ('#' comments):
  *     <family> <asym 0|1> <N> <K> <max_m> <kind> <cfg> <split>
- * family wna16 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16 | fp8b; kind 0 skinny, 1 LDS-tiled, 2 async-pipelined,
- * 3 ping-pong; cfg indexes that kind's configurations (hq_kernel_config_count); split = K splits
- * of the skinny kernel, -1 = the heuristic's. A dense call uses the first entry of its family,
- * asym, N and K whose max_m >= M, if that configuration fits the shape; otherwise the built-in
- * choice. The table is process-wide:
+ * family wna16 | wna2 | wna3 | w8a8 | w4a8 | w4a4 | w4a8mx | mxw4a16 | fp8b | w8a16 | f8a16; kind 0
+ * skinny, 1 LDS-tiled, 2 async-pipelined, 3 ping-pong; cfg indexes that kind's configurations
+ * (hq_kernel_config_count); split = K splits of the skinny kernel, -1 = the heuristic's. A dense
+ * call uses the first entry of its family, asym, N and K whose max_m >= M, if that configuration
+ * fits the shape (the skinny kernel's few-row configurations fit only M <= 4); otherwise the
+ * built-in choice. The table is process-wide:
  *   hq_load_tuning_table(path)  replaces it (NULL clears it); a malformed line fails with
  *                               HQ_ERR_INVALID_ARGUMENT and leaves the table unchanged.
  *   Without a call, the file named by the environment variable HQ_TUNING_FILE (if any) is read
