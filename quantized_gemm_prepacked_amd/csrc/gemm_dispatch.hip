@@ -62,6 +62,7 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({31, 30, 28, 13, 0, 1, 2});
     if (c.fam == FAM_W8A16) return first_fit({33, 31, 27, 0, 1, 2});
     if (c.fam == FAM_F8A16) return first_fit({30, 31, 27, 0, 1, 2});
+    if (c.fam == FAM_FP8B) return first_fit({21, 2});
   }
   if (rows <= 16) {
     if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({28, 13, 0, 1, 2});
@@ -69,8 +70,10 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     // flight (M=1 INT8 / FP8: 13.2 / 12.3 us; the 8-wave form 13.5 / 12.6)
     if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) return first_fit({27, 0, 1, 2});
     if (c.fam == FAM_MXW4A16) return first_fit({28, 13, 0, 1, 2});
-    if (c.fam == FAM_FP8B) return first_fit({21, 2});
-    if (c.fam == FAM_W8A8) return first_fit({1, 11, 2});
+    // 8-bit activations, N=K=8192: block-scaled FP8 M=8 / 16 12.65 / 13.16 us (the form taken
+    // below 5 rows: 13.01 / 14.87); W8A8 M=8 12.23 us (the 16-row choice: 13.26)
+    if (c.fam == FAM_FP8B) return first_fit({20, 21, 2});
+    if (c.fam == FAM_W8A8) return rows <= 8 ? first_fit({2}) : first_fit({1, 11, 2});
     if (c.fam == FAM_W4A8) return first_fit({21, 2});
     if (c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({21, 2});
     return first_fit({28, 13, 0, 1, 2});
@@ -80,8 +83,11 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
     if (c.fam == FAM_W8A16) return first_fit({29, 22, 3, 7, 8});   // M=32: 16.0 us (next 18.9)
     if (c.fam == FAM_F8A16) return first_fit({22, 29, 3, 7, 8});   // M=32: 15.8 us (next 16.3)
     if (c.fam == FAM_MXW4A16) return first_fit({29, 22, 3, 7, 8});
-    if (c.fam == FAM_FP8B) return first_fit({29, 15, 8});
-    if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({16, 8});
+    // M=32: block-scaled FP8 (N=K=8192) 16.0 us against 22.8 for the 32-row 4-tile form; the
+    // MXFP4-weight formats (N=4096, K=7168) on two 16-row blocks of 32 channels: W4A8 7.24,
+    // W4A4 7.04, MXFP8 activations 7.52 us against 8.50 / 8.25 / 9.35 for one 32-row block
+    if (c.fam == FAM_FP8B) return first_fit({23, 15, 8});
+    if (c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) return first_fit({18, 16, 8});
     if (c.fam == FAM_W8A8) return first_fit({23, 15, 8});
     return first_fit({29, 22, 3, 7, 8});
   }
@@ -89,7 +95,12 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   // us against 22.4 / 39.2 with 64-row blocks)
   if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({22, 5, 4, 6});
   if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
-  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
+  // M=64 (N=4096, K=7168): W4A8 8.96 us against 16.3 for the 64-row form with a K split, W4A4
+  // 8.76, MXFP8 activations 9.36 on four 16-row blocks (9.87 on two 32-row ones); W8A8 (N=K=8192)
+  // 21.96 us on two 32-row blocks against 25.6 for the pipelined kernel
+  if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
+  if (c.fam == FAM_W4A8MX && rows <= 64) return first_fit({28, 23, 15, 8});
+  if (c.fam == FAM_W8A8 && rows <= 64) return first_fit({29, 15, 8});
   if (c.fam == FAM_FP8B && rows <= 64) return first_fit({29, 15, 8});   // M=64: 31.9 us vs 40.6
   return first_fit({4, 5, 6});
 }
@@ -176,7 +187,7 @@ struct RangeEntry {
 constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
 // (M in (256, 512]: ping-pong 128 x 128 with four LDS slots, 57.7 vs 61.3 us with three)
-constexpr RangeEntry kW8a8Table[] = {{32, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
+constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
 constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
 // W4A4 and W4A8 with MXFP8 activations run on the skinny and ping-pong kernels only. W4A4,
 // measured at N=4096, K=7168: skinny 64-row blocks to M=512 (34 vs 49 us), then ping-pong

@@ -21,13 +21,16 @@ TABLE = {
     "f8a16": (hq.DESC_W8A16_FP8, 14336, 4096,
               [(1, (0, 30)), (5, (0, 27)), (32, (0, 22)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
     "w8a8": (hq.DESC_W8A8, 8192, 8192,
-             [(1, (0, 1)), (32, (0, 23)), (33, (2, 3)), (256, (2, 3)), (257, (3, 11)), (512, (3, 11)),
+             [(1, (0, 2)), (8, (0, 2)), (9, (0, 1)), (16, (0, 1)), (32, (0, 23)), (33, (0, 29)),
+              (64, (0, 29)), (65, (2, 3)), (256, (2, 3)), (257, (3, 11)), (512, (3, 11)),
               (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
-    "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192, [(1, (0, 21)), (64, (0, 29)), (65, (3, 10)), (4096, (3, 10))]),
+    "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192,
+                 [(1, (0, 21)), (4, (0, 21)), (5, (0, 20)), (16, (0, 20)), (32, (0, 23)), (64, (0, 29)),
+                  (65, (3, 10)), (4096, (3, 10))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
-             [(1, (0, 21)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
-    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (640, (0, 4)), (641, (3, 10)), (4097, (3, 0))]),
-    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
+             [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (640, (0, 4)), (641, (3, 10)), (4097, (3, 0))]),
+    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
 }
 
 
