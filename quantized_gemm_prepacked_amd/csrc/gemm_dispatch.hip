@@ -94,13 +94,22 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   // 2-bit weights: two 32-row blocks, double-buffered (N=14336, K=4096, M=64 / 128: 20.4 / 37.2
   // us against 22.4 / 39.2 with 64-row blocks)
   if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({22, 5, 4, 6});
-  if (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) return first_fit({5, 4, 6});
+  if (c.fam == FAM_WNA16) return first_fit({5, 4, 6});
+  // MXFP4 weights with bf16 activations, M=64: two 32-row blocks of 64 channels 18.7 us (the
+  // 64-row form 20.2); M=128: the 64-row form
+  if (c.fam == FAM_MXW4A16) return rows <= 64 ? first_fit({3, 5, 4, 6}) : first_fit({4, 5, 6});
   // M=64 (N=4096, K=7168): W4A8 8.96 us against 16.3 for the 64-row form with a K split, W4A4
   // 8.76, MXFP8 activations 9.36 on four 16-row blocks (9.87 on two 32-row ones); W8A8 (N=K=8192)
   // 21.96 us on two 32-row blocks against 25.6 for the pipelined kernel
   if ((c.fam == FAM_W4A4 || c.fam == FAM_W4A8) && rows <= 64) return first_fit({23, 15, 8});   // two 32-row blocks
   if (c.fam == FAM_W4A8MX && rows <= 64) return first_fit({28, 23, 15, 8});
   if (c.fam == FAM_W8A8 && rows <= 64) return first_fit({29, 15, 8});
+  // M=128 (N=4096, K=7168): four 32-row blocks of 64 channels, W4A8 / W4A4 / MXFP8 activations
+  // 12.4 / 12.0 / 13.6 us against 21.5 / 20.0 / 21.2 for the 64-row form; W4A8 M=256: 32-row
+  // blocks of 64 channels, double-buffered, 19.5 against 21.3
+  if ((c.fam == FAM_W4A8 || c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX) && rows <= 128)
+    return first_fit({29, 4, 5, 6});
+  if (c.fam == FAM_W4A8 && rows <= 256) return first_fit({22, 4, 5, 6});
   if (c.fam == FAM_FP8B && rows <= 64) return first_fit({29, 15, 8});   // M=64: 31.9 us vs 40.6
   return first_fit({4, 5, 6});
 }
@@ -200,12 +209,14 @@ constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {4096, 3, 10}, {kInf, 3, 0}};
 // slots from M=2048 (M=2048 / 4096 / 8192: 74.9 / 136.9 / 256.0 us, against 84.8 / 154.4 / 364.8).
 constexpr RangeEntry kW4a8mxTable[] = {{576, 0, 0}, {1536, 3, 13}, {kInf, 3, 8}};
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
-constexpr RangeEntry kMxW4a16Table[] = {{64, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
+// (M = 128, N=14336 K=4096: the small-M kernel 25.7 us against 35.0 for ping-pong 128 x 128)
+constexpr RangeEntry kMxW4a16Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
 // Block-scaled FP8 W8A8: skinny and ping-pong only (measured at N=K=8192: skinny to M=64, then
 // ping-pong 128 x 128 with four LDS slots: M=128 / 512 / 1024 / 2048 / 4096 at 66.3 / 75.4 / 138.0
 // / 272.9 / 517.0 us, against 91.7 / 101.6 / 194.0 / 304.2 / 610.4 for the three-slot 64 x 256 and
 // 256 x 128 tiles)
-constexpr RangeEntry kFp8bTable[] = {{64, 0, 0}, {kInf, 3, 10}};
+// (M = 128 / 256, N=K=8192: the small-M kernel 34.1 / 53.5 us against 58.4 / 57.4 for ping-pong)
+constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {kInf, 3, 10}};
 // INT8 / FP8 weights with bf16 activations (the 128 x 256 tiles' three-slot ring of 64 KiB steps
 // exceeds the LDS). Measured at N=14336, K=4096 (INT8 / FP8): skinny 64-row blocks to M=128
 // (34.5 / 32.5 us; ping-pong 41.7 / 32.1), then ping-pong 128 x 128 with waves of 64 x 32:

@@ -12,7 +12,7 @@ TABLE = {
               [(1, (0, 30)), (4, (0, 30)), (5, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 2)), (128, (2, 2)), (129, (3, 3)),
                (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w4a16mx": (hq.DESC_W4A16_MXFP4, 14336, 4096,
-                [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 5)), (65, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
+                [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 3)), (65, (0, 4)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w2a16": (hq.DESC_W2A16_ASYM, 14336, 4096,
               [(1, (0, 31)), (4, (0, 31)), (5, (0, 28)), (128, (0, 22)), (129, (3, 13)), (512, (3, 13)), (513, (3, 0)), (8192, (3, 0))]),
     "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096, [(1, (0, 31)), (5, (0, 28)), (32, (0, 29)), (8192, (0, 22))]),
@@ -26,11 +26,12 @@ TABLE = {
               (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
     "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192,
                  [(1, (0, 21)), (4, (0, 21)), (5, (0, 20)), (16, (0, 20)), (32, (0, 23)), (64, (0, 29)),
-                  (65, (3, 10)), (4096, (3, 10))]),
+                  (65, (0, 4)), (256, (0, 4)), (257, (3, 10)), (4096, (3, 10))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
-             [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
-    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (640, (0, 4)), (641, (3, 10)), (4097, (3, 0))]),
-    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
+             [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 29)), (128, (0, 29)), (129, (0, 22)),
+              (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (3, 10)), (4097, (3, 0))]),
+    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
 }
 
 
