@@ -203,7 +203,8 @@ constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {k
 // 128 x 128 with four LDS slots (M=768 / 1024 / 2048 / 4096: 50.7 / 51.2 / 67.3 / 121.9 us,
 // against 66.9 skinny and 60.2 / 74.1 / 135.5 with three slots), 128 x 256 with three at M=8192
 // (187 us; four or five slots: 235 / 243).
-constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {4096, 3, 10}, {kInf, 3, 0}};
+// (M = 4096: configuration 0 82.0 us against 99.3 for 10; M = 2048: 68.2 against 55.8)
+constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {2048, 3, 10}, {kInf, 3, 0}};
 // W4A8-MXFP8 at the same shape: skinny to M=512 (45.5 vs 50.9 us), ping-pong 64 x 256 with four
 // slots at M=768 / 1024 (52.6 / 52.9 us; 75.3 / 70.1 with the W4A4 choices), 128 x 256 with four
 // slots from M=2048 (M=2048 / 4096 / 8192: 74.9 / 136.9 / 256.0 us, against 84.8 / 154.4 / 364.8).
@@ -216,7 +217,8 @@ constexpr RangeEntry kMxW4a16Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
 // / 272.9 / 517.0 us, against 91.7 / 101.6 / 194.0 / 304.2 / 610.4 for the three-slot 64 x 256 and
 // 256 x 128 tiles)
 // (M = 128 / 256, N=K=8192: the small-M kernel 34.1 / 53.5 us against 58.4 / 57.4 for ping-pong)
-constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {kInf, 3, 10}};
+// (M = 4096: ping-pong configuration 0 412.6 us against 426.5 for 10; M = 2048: 236.4 against 231.1)
+constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {2048, 3, 10}, {kInf, 3, 0}};
 // INT8 / FP8 weights with bf16 activations (the 128 x 256 tiles' three-slot ring of 64 KiB steps
 // exceeds the LDS). Measured at N=14336, K=4096 (INT8 / FP8): skinny 64-row blocks to M=128
 // (34.5 / 32.5 us; ping-pong 41.7 / 32.1), then ping-pong 128 x 128 with waves of 64 x 32:

@@ -26,11 +26,12 @@ TABLE = {
               (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
     "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192,
                  [(1, (0, 21)), (4, (0, 21)), (5, (0, 20)), (16, (0, 20)), (32, (0, 23)), (64, (0, 29)),
-                  (65, (0, 4)), (256, (0, 4)), (257, (3, 10)), (4096, (3, 10))]),
+                  (65, (0, 4)), (256, (0, 4)), (257, (3, 10)), (2048, (3, 10)), (2049, (3, 0)),
+                  (4096, (3, 0))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
              [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 29)), (128, (0, 29)), (129, (0, 22)),
               (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
-    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (3, 10)), (4097, (3, 0))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (3, 10)), (2048, (3, 10)), (2049, (3, 0))]),
     "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
 }
 
