@@ -3,7 +3,10 @@
 
 Default workload: dense W4A16 M-sweep, N=14336, K=4096, asymmetric UINT4 weights with a bf16
 scale and a uint4 zero-point per (channel, group of 128), bf16 N(0,1) activations, bf16 output,
-M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. Other workloads:
+M in {1, 16, 128, 1024, 8192}. One step = one GEMM at every M of the sweep. The default run then
+times the MoE gate_up workload (E=256, top-8, N=4096, K=7168, T in {1, 32, 512, 4096}: token sort
++ grouped GEMM, tokens/s) the same way and reports it under "moe" (--no-moe leaves it out). Other
+workloads:
 --config w8a8 | w4a8 | w4a4 | w4a16mx | fp8block | w8a16 | f8a16 | w2a16 | w3a16 | moe | moe_mx | moe_fp8b |
 moe_layer | moe_layer_w4a8.
 
@@ -58,6 +61,14 @@ WORKLOADS = {
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def per_launch_stats(ms_per_replay, reps: int) -> dict:
+    """Per-launch microseconds from the replays' event times: median (the reported time), min and
+    90th percentile over the timed replays."""
+    import numpy as np
+    us = np.asarray(ms_per_replay, dtype=np.float64) * 1e3 / reps
+    return {"median": float(np.median(us)), "min": float(us.min()), "p90": float(np.percentile(us, 90))}
 
 
 def kernel_sources_sha(files=None) -> str:
@@ -315,14 +326,16 @@ def run_dense(args, wl: str):
     tot_flops = 0.0
     tot_s = 0.0
     for M in Ms:
-        us = float(np.mean([a.elapsed_time(b) for a, b in evs[M]])) * 1e3 / reps[M]
+        st = per_launch_stats([a.elapsed_time(b) for a, b in evs[M]], reps[M])
+        us = st["median"]
         fl = 2.0 * M * N * K
         by = alg_bytes(wl, M, N, K)
         tf = fl / (us * 1e-6) / 1e12
         gbs = by / (us * 1e-6) / 1e9
         peak = PEAK_TFLOPS[spec["peak"]]
         frac_c, frac_m = tf / peak, gbs / HBM_PEAK_GBS
-        sweep.append({"M": M, "launches_per_graph": reps[M], "us": round(us, 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
+        sweep.append({"M": M, "launches_per_graph": reps[M], "us": round(us, 3), "us_min": round(st["min"], 3),
+                      "us_p90": round(st["p90"], 3), "tflops": round(tf, 3), "gbps": round(gbs, 1),
                       "bound": "hbm" if frac_m >= frac_c else "mfma",
                       "frac": round(max(frac_c, frac_m), 4), "bytes": by, "flops": fl})
         tot_flops += fl
@@ -353,7 +366,7 @@ def run_dense(args, wl: str):
                 b.record(stream)
                 qe.append((a, b))
             torch.cuda.synchronize()
-            row["act_quant_us"] = round(float(np.mean([a.elapsed_time(b) for a, b in qe])) * 1e3 / r, 3)
+            row["act_quant_us"] = round(per_launch_stats([a.elapsed_time(b) for a, b in qe], r)["median"], 3)
     dom = max(sweep, key=lambda r: r["us"])
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_TFLOPS[spec["peak"]],
@@ -515,8 +528,9 @@ def run_moe(args, mx=False):
     tot_t = 0.0
     tot_tok = 0
     for T in Ts:
-        ta = float(np.mean([e[0].elapsed_time(e[1]) for e in rec[T]])) * 1e3 / reps[T]
-        tg = float(np.mean([e[1].elapsed_time(e[2]) for e in rec[T]])) * 1e3 / reps[T]
+        sa = per_launch_stats([e[0].elapsed_time(e[1]) for e in rec[T]], reps[T])
+        sg = per_launch_stats([e[1].elapsed_time(e[2]) for e in rec[T]], reps[T])
+        ta, tg = sa["median"], sg["median"]
         s = state[T]
         fl = 2.0 * T * topk * N * K
         by = s["active"] * stride + (T * K + T * (K // 128) * 4 if fp8b else T * K * 2) + T * topk * N * 2
@@ -524,7 +538,8 @@ def run_moe(args, mx=False):
         gbs = by / (tg * 1e-6) / 1e9
         fc, fm = tf / PEAK_TFLOPS[peak], gbs / HBM_PEAK_GBS
         sweep.append({"T": T, "launches_per_graph": reps[T], "block_m": s["bm"], "active_experts": s["active"], "top_expert_rows": s["top"],
-                      "align_us": round(ta, 3), "gemm_us": round(tg, 3),
+                      "align_us": round(ta, 3), "gemm_us": round(tg, 3), "gemm_us_min": round(sg["min"], 3),
+                      "gemm_us_p90": round(sg["p90"], 3),
                       "tokens_per_s": round(T / ((ta + tg) * 1e-6), 1), "tflops": round(tf, 3),
                       "gbps": round(gbs, 1), "bound": "hbm" if fm >= fc else "mfma",
                       "frac": round(max(fc, fm), 4)})
@@ -722,7 +737,7 @@ def run_moe_layer(args, w4a8=False):
     wall = time.perf_counter() - t0
     sweep, tot_t, tot_tok = [], 0.0, 0
     for T in Ts:
-        us = {n: float(np.mean([a.elapsed_time(b) for a, b in rec[(T, n)]])) * 1e3 / reps[T] for n in names}
+        us = {n: per_launch_stats([a.elapsed_time(b) for a, b in rec[(T, n)]], reps[T])["median"] for n in names}
         s = state[T]
         R = T * topk
         pt = {}
@@ -791,6 +806,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_fp8b", "moe_layer", "moe_layer_w4a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="default workload only: leave out the MoE gate_up sweep that follows the dense one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -808,6 +825,12 @@ def main():
         line = run_moe_layer(args, w4a8=True)
     else:
         line = run_dense(args, args.config)
+        if args.config == "w4a16" and not args.no_moe:
+            # The metric's second half: MoE tokens/s on the DeepSeek-V3-shaped gate_up (token sort +
+            # grouped GEMM per T), timed the same way in the same run. `value` stays the dense
+            # sweep's TFLOP/s; the MoE line rides along under "moe".
+            moe = run_moe(argparse.Namespace(**{**vars(args), "no_cpu_baseline": True}))
+            line["moe"] = {k: moe[k] for k in ("value", "unit", "ms_per_step", "config", "roofline", "sweep")}
     print(json.dumps(line), flush=True)
 
 

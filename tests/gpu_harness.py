@@ -39,8 +39,15 @@ def workspace(nbytes: int):
     return torch.empty(nbytes, dtype=torch.uint8, device=DEV), nbytes
 
 
+# Sentinels an output keeps when the library never writes it: a bf16 NaN (check_float's finite
+# check catches it) or, for int32 outputs, INT32_MIN (outside every W8A8 accumulator's range).
+BF16_NAN_BITS = 0x7FC0
+I32_SENTINEL = -(2 ** 31)
+
+
 def gemm(desc, M, N, K, a, a_scale, w_dev, out_dtype=torch.int16):
-    y = torch.empty((max(M, 1), N), dtype=out_dtype, device=DEV)
+    fill = BF16_NAN_BITS if out_dtype == torch.int16 else I32_SENTINEL
+    y = torch.full((max(M, 1), N), fill, dtype=out_dtype, device=DEV)
     ws, wsb = workspace(hq.hq_gemm_workspace_bytes(desc, M, N, K))
     hq.hq_gemm(desc, M, N, K, a, a_scale, w_dev, y, ws, wsb)
     torch.cuda.synchronize()

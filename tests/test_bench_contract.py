@@ -46,3 +46,27 @@ def test_kernel_sources_sha_covers_the_named_files_only(tmp_path):
     part = bench.kernel_sources_sha(["gemm_pingpong.hip", "device_ops.h"])
     assert len(full) == len(part) == 64 and full != part
     assert part == bench.kernel_sources_sha(["device_ops.h", "gemm_pingpong.hip"])   # order-free
+
+
+def test_traffic_records_reach_the_gpu_box():
+    """bench.py resolves `roofline.traffic` from profiles/traffic_*.json on the machine it runs on,
+    so no line of .gpurunignore may keep those records from being shipped with the tree."""
+    import fnmatch
+    lines = [ln.strip() for ln in open(os.path.join(ROOT, ".gpurunignore")) if ln.strip() and not ln.startswith("#")]
+    for rec in ("./profiles/traffic_w4a16.json", "./profiles/traffic_moe.json"):
+        for pat in lines:
+            anchored = pat.startswith("./")
+            name = rec if anchored else os.path.basename(rec)
+            assert not fnmatch.fnmatch(name, pat) and not rec.startswith(pat.rstrip("/") + "/"), (pat, rec)
+
+
+def test_current_records_resolve():
+    """A record whose kernel sources are unchanged must give a number: a null traffic field in the
+    measured line then means the kernel changed, never that the record was not found."""
+    for path in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if not (path.startswith("traffic_") and path.endswith(".json")):
+            continue
+        rec = json.load(open(os.path.join(ROOT, "profiles", path)))
+        if rec["kernel_sources_sha256"] != bench.kernel_sources_sha(rec["kernel_files"]):
+            continue
+        assert bench.measured_traffic(rec["workload"], rec["point"]) == rec["hbm_bytes_per_launch"], path

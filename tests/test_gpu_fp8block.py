@@ -25,8 +25,11 @@ def _gemm(d, M, N, K):
     (300, 256, 640),     # ping-pong, ragged M, 5 K steps
     (1000, 384, 512),    # N not a multiple of 256
     (700, 512, 1024),
-    (200, 256, 128),     # ping-pong with four LDS slots, one K step
-    (150, 128, 256),     # two K steps
+    (300, 256, 128),     # ping-pong 128 x 128 with four LDS slots, one K step
+    (480, 128, 256),     # ping-pong, four slots, two K steps
+    (200, 256, 128),     # small-M kernel (M <= 256), one K step
+    (150, 128, 256),     # small-M kernel, two K steps
+    (2100, 256, 256),    # above 2048 rows: ping-pong 128 x 256, three slots, ragged last tile
 ])
 def test_fp8block_small(M, N, K):
     say(f"[fp8block] M={M} N={N} K={K}")

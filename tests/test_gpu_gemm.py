@@ -133,7 +133,11 @@ W4A8_SMALL = [(1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (13
               (700, 256, 1024),    # 64 x 128 pipelined tiles
               (1200, 512, 768),    # 64 x 128 pipelined tiles
               (1600, 512, 384),    # 128 x 128 pipelined tiles, ragged M
-              (3200, 256, 384)]    # 256 x 256 pipelined tiles, ragged M
+              (3200, 256, 384),    # 256 x 256 pipelined tiles, ragged M
+              (48, 256, 1024),     # 33..64 rows: two 32-row skinny blocks of 32 channels
+              (64, 512, 2048),
+              (100, 512, 1024),    # 65..128 rows: four 32-row blocks of 64 channels, ragged M
+              (128, 256, 1536)]
 
 
 @pytest.mark.parametrize("M,N,K", W4A8_SMALL)
@@ -146,7 +150,7 @@ def test_w4a8_small(M, N, K):
     check_float(y, ref, "w4a8")
 
 
-@pytest.mark.parametrize("M", [1, 32, 256, 2048, 8192])
+@pytest.mark.parametrize("M", [1, 32, 64, 128, 256, 2048, 8192])
 def test_w4a8_full_size_sampled(M):
     N, K = 4096, 7168
     say(f"[w4a8 full] M={M}")

@@ -130,9 +130,11 @@ def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
     check_float(y, ref, "moe gemm")
 
 
-@pytest.mark.parametrize("T", [1, 8, 512, 2048])
+@pytest.mark.parametrize("T", [1, 8, 32, 512, 2048, 4096])
 def test_moe_gemm_full_size_sampled(T):
-    """DeepSeek-V3-shaped layer: 256 experts, top-8, K=7168, fused gate_up N=4096."""
+    """DeepSeek-V3-shaped layer: 256 experts, top-8, K=7168, fused gate_up N=4096, at every token
+    count of the MoE workload (1, 32, 512, 4096) and two between them; skewed routing, so at
+    T=4096 one expert takes nearly every token and many take a handful."""
     E, topk, N, K = 256, 8, 4096, 7168
     bm = hq.hq_moe_block_m(hq.DESC_W4A16_SYM, T, topk, E, N, K)
     inp, experts, y = _moe_case(T, topk, E, N, K, bm, False, 5, random_codes=T > 8)

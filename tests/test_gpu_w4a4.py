@@ -24,6 +24,9 @@ def _gemm(d, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024),
+    (100, 512, 1024),    # 65..128 rows: four 32-row skinny blocks of 64 channels, ragged M
+    (128, 256, 1536),
+    (64, 256, 1024),     # 33..64 rows: two 32-row blocks
     (300, 256, 512),     # skinny, 64-row blocks, ragged M
     (700, 384, 640),     # ping-pong 128 x 128, four LDS slots, 5 K steps
     (1000, 256, 128),    # four slots, one K step

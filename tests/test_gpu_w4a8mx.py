@@ -22,6 +22,9 @@ def _gemm(d, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (64, 256, 512), (300, 256, 512),
+    (100, 512, 1024),    # 65..128 rows: four 32-row skinny blocks of 64 channels, ragged M
+    (128, 256, 1536),
+    (48, 256, 1024),     # 33..64 rows
     (1100, 384, 640),    # ping-pong 128 x 128 fallback (four LDS slots), 5 K steps
     (700, 512, 640),     # ping-pong 64 x 256, four slots
     (1600, 256, 1024),   # ping-pong 128 x 256, four slots, ragged M
