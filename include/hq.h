@@ -22,7 +22,8 @@
  * General conventions
  *   - Ownership: the caller allocates every buffer. Host buffers for the prepack; device
  *     buffers (e.g. from PyTorch) for everything else. The library keeps no pointer after a
- *     call returns and allocates no device memory.
+ *     call returns and allocates no device memory (hq_gemm_noalloc's scratch is a static device
+ *     array of the library, not an allocation).
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream). Device calls only enqueue
  *     work and never synchronize. `hq_moe_grouped_gemm` reads the padded row count on the
  *     device, so no host round trip is needed between the two MoE calls.
@@ -221,6 +222,25 @@ size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, 
 hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K,
                   const void* a, const float* a_scale, const void* w_packed,
                   void* y, void* ws, size_t ws_bytes, hq_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * hq_gemm without a workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (minus ws / ws_bytes), kernels, results and errors as hq_gemm, bit for bit. The
+ * split-K partials and activation group sums that hq_gemm keeps in the caller's workspace live in
+ * a library-owned device array of HQ_NOALLOC_SCRATCH_BYTES per GPU instead, held until the
+ * process ends. Nothing is allocated by the call.
+ *   - A call whose workspace (hq_gemm_workspace_bytes) exceeds HQ_NOALLOC_SCRATCH_BYTES fails
+ *     with HQ_ERR_WORKSPACE before any launch.
+ *   - The array keeps the last call's contents; no call depends on them (every byte a launch
+ *     reads from it was written by the same call).
+ *   - Calls on one GPU share its array: calls that overlap in time on one GPU (different
+ *     streams or threads) race and give unspecified results. Serialize them.
+ * ------------------------------------------------------------------------------------------- */
+#define HQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+hq_status hq_gemm_noalloc(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K,
+                          const void* a, const float* a_scale, const void* w_packed,
+                          void* y, hq_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * MoE token sort / expert offsets (device).

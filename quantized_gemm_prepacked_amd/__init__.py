@@ -33,7 +33,7 @@ HQ_ACT_BF16, HQ_ACT_INT8_PER_TOKEN, HQ_ACT_FP8E4M3_PER_TOKEN, HQ_ACT_MXFP4, HQ_A
 HQ_OUT_BF16, HQ_OUT_INT32_ACC = range(2)
 
 EXPORTED = (
-    "hq_prepacked_bytes", "hq_prepack_weights", "hq_gemm_workspace_bytes", "hq_gemm",
+    "hq_prepacked_bytes", "hq_prepack_weights", "hq_gemm_workspace_bytes", "hq_gemm", "hq_gemm_noalloc",
     "hq_moe_align_capacity", "hq_moe_align_workspace_bytes", "hq_moe_align", "hq_moe_block_m",
     "hq_moe_gemm_workspace_bytes", "hq_moe_grouped_gemm", "hq_quantize_activations",
     "hq_moe_silu_mul", "hq_moe_silu_mul_quantize", "hq_moe_combine", "hq_grouped_gemm_workspace_bytes",
@@ -105,6 +105,7 @@ _c = {
     "hq_prepack_weights": _sig("hq_prepack_weights", ctypes.c_int, _D, _I64, _I64, _I64, _P, _P, _P, _P, _SZ),
     "hq_gemm_workspace_bytes": _sig("hq_gemm_workspace_bytes", _SZ, _D, _I64, _I64, _I64),
     "hq_gemm": _sig("hq_gemm", ctypes.c_int, _D, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P),
+    "hq_gemm_noalloc": _sig("hq_gemm_noalloc", ctypes.c_int, _D, _I64, _I64, _I64, _P, _P, _P, _P, _P),
     "hq_moe_align_capacity": _sig("hq_moe_align_capacity", _SZ, _I64, _I32, _I32, _I32),
     "hq_moe_align_workspace_bytes": _sig("hq_moe_align_workspace_bytes", _SZ, _I64, _I32, _I32, _I32),
     "hq_moe_align": _sig("hq_moe_align", ctypes.c_int, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P),
@@ -192,6 +193,15 @@ def hq_gemm_workspace_bytes(desc, M, N, K) -> int:
 def hq_gemm(desc, M, N, K, a, a_scale, w_packed, y, ws=None, ws_bytes=0, stream=None):
     _check(_c["hq_gemm"](_d(desc), M, N, K, _ptr(a), _ptr(a_scale), _ptr(w_packed), _ptr(y),
                          _ptr(ws), ws_bytes, _stream(stream)))
+
+
+HQ_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def hq_gemm_noalloc(desc, M, N, K, a, a_scale, w_packed, y, stream=None):
+    """hq_gemm with the library's own per-GPU scratch instead of a workspace (allocates nothing)."""
+    _check(_c["hq_gemm_noalloc"](_d(desc), M, N, K, _ptr(a), _ptr(a_scale), _ptr(w_packed), _ptr(y),
+                                 _stream(stream)))
 
 
 def hq_moe_align_capacity(T, topk, E, block_m) -> int:

@@ -11,6 +11,7 @@
 #include <initializer_list>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "gemm_common.h"
 #include "internal.h"
@@ -648,6 +649,34 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   hipError_t e = launch_skinny(p, c.fam, false, plan.cfg, grid, call.stream);
   if (e != hipSuccess || plan.split == 1) return e;
   return launch_splitk_reduce(p, c.fam, call.stream);
+}
+
+// ---- library-owned scratch for hq_gemm_noalloc --------------------------------------------------
+// One array per GPU (each device holds its own copy of a __device__ variable), alive until the
+// process ends. Host code never passes `scratch` itself to a kernel or a copy: on the host that
+// name is only a stand-in symbol, not a device address. The device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and is what the kernels
+// receive, exactly as they receive a caller's workspace in hq_gemm.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace hq

@@ -203,9 +203,15 @@ size_t hq_gemm_workspace_bytes(const hq_quant_desc* desc, int64_t M, int64_t N, 
   return hq::plan_dense(c, M, N, K).ws_bytes;
 }
 
-hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, const void* a,
-                  const float* a_scale, const void* w_packed, void* y, void* ws, size_t ws_bytes,
-                  hq_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// hq_gemm and hq_gemm_noalloc: validation, plan, launch. noalloc: the workspace is the
+// library-owned scratch array of the current device instead of (ws, ws_bytes).
+hq_status gemm_entry(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, const void* a,
+                     const float* a_scale, const void* w_packed, void* y, void* ws, size_t ws_bytes,
+                     hq_stream_t stream, bool noalloc) {
   hq::Combo c{};
   hq_status s = resolve(desc, &c);
   if (s != HQ_OK) return s;
@@ -224,9 +230,23 @@ hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, co
   if (M == 0) return ok();
   const hq::Plan plan = hq::plan_dense(c, M, N, K);
   if (plan.kind < 0) return fail(HQ_ERR_INVALID_ARGUMENT, "the HQ_TUNE override does not fit this shape");
-  if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
-    return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
-  if (ws && !aligned16(ws)) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 16-byte aligned");
+  if (noalloc) {
+    if (plan.ws_bytes > hq::kNoAllocScratchBytes)
+      return fail(HQ_ERR_WORKSPACE,
+                  "hq_gemm_noalloc: this call needs %zu bytes of scratch, more than the %zu bytes the "
+                  "library holds per GPU (use hq_gemm with a workspace)",
+                  plan.ws_bytes, hq::kNoAllocScratchBytes);
+    ws_bytes = hq::kNoAllocScratchBytes;
+    ws = nullptr;
+    if (plan.ws_bytes) {
+      const hipError_t e = hq::noalloc_scratch(&ws);
+      if (e != hipSuccess) return fail(HQ_ERR_HIP, "hq_gemm_noalloc: scratch address: %s", hipGetErrorString(e));
+    }
+  } else {
+    if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
+      return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
+    if (ws && !aligned16(ws)) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 16-byte aligned");
+  }
   hq::GemmCall call{};
   call.c = c;
   call.M = M;
@@ -239,7 +259,22 @@ hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, co
   call.ws = ws;
   call.ws_bytes = ws_bytes;
   call.stream = static_cast<hipStream_t>(stream);
-  return check_hip(hq::launch_gemm(call, plan), "hq_gemm launch");
+  return check_hip(hq::launch_gemm(call, plan), noalloc ? "hq_gemm_noalloc launch" : "hq_gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_gemm(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, const void* a,
+                  const float* a_scale, const void* w_packed, void* y, void* ws, size_t ws_bytes,
+                  hq_stream_t stream) {
+  return gemm_entry(desc, M, N, K, a, a_scale, w_packed, y, ws, ws_bytes, stream, false);
+}
+
+hq_status hq_gemm_noalloc(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, const void* a,
+                          const float* a_scale, const void* w_packed, void* y, hq_stream_t stream) {
+  return gemm_entry(desc, M, N, K, a, a_scale, w_packed, y, nullptr, 0, stream, true);
 }
 
 size_t hq_moe_align_capacity(int64_t T, int32_t topk, int32_t E, int32_t block_m) {

@@ -64,6 +64,10 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int
 int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K);
 bool moe_block_m_supported(int32_t block_m);
 hipError_t launch_gemm(const GemmCall& call, const Plan& plan);
+// hq_gemm_noalloc's workspace: a library-owned device array of kNoAllocScratchBytes per GPU; the
+// device address of the current device's copy (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(HQ_NOALLOC_SCRATCH_BYTES);
+hipError_t noalloc_scratch(void** ptr);
 
 size_t moe_align_ws_bytes(int64_t T, int32_t topk, int32_t E, int32_t block_m);
 hipError_t launch_grouped_index(const int32_t* offsets, int64_t R, int32_t E, int32_t bm, int64_t cap,
