@@ -55,6 +55,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return uint16_t(u >> 16);
 }
 
+// Two fp32 -> two bf16 bit patterns (round to nearest even), low half from a: gfx950's paired
+// conversion instruction, one VALU operation for both (finite values and infinities round exactly
+// as f32_to_bf16_rne does; a NaN stays a NaN).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // ---- WNA16 dequantization -------------------------------------------------------------------
 // One dword holds 8 unsigned 4-bit codes u of consecutive k in the slot order k0 k2 k4 k6 k1 k3
 // k5 k7 (layout.h). Returns the 8 values (u - z), exactly representable in bf16 since

@@ -23,6 +23,7 @@
 // with the router weight. Blocks past the sorted rows carry expert -1 and exit at once.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "device_ops.h"
@@ -194,10 +195,21 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   const int nt_wg = ntile * NT;
   const int nt0 = nt_wg + wn * NTW;
   const uint8_t* w = p.w;
+  // MoE: this wave's 16-row blocks up to the last one holding a routed row. The token sort puts
+  // an expert's routed rows first in its blocks and the padding after them, so in a lightly
+  // loaded expert's block the later row blocks are padding only: their MFMAs (and operand
+  // reads) are skipped, their rows are never stored.
+  int nlive = MW;
   if constexpr (MOE) {
     const int e = p.block_expert[mt];
     if (e < 0 || e >= p.E) return;     // the whole workgroup, before any barrier
     w += size_t(e) * p.expert_stride;
+    nlive = 0;
+#pragma unroll
+    for (int mb = 0; mb < MW; ++mb) {
+      const int id = p.sorted_ids[row0 + wm * 16 * MW + 16 * mb + (lane & 15)];
+      if (__builtin_amdgcn_ballot_w64(id < p.M) != 0) nlive = mb + 1;
+    }
   }
 
   // ---- per-lane sources of the stage copies (constant over K) ----
@@ -301,11 +313,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   int asf[MW];   // MXFP4 activations: this lane's row block scale
   float asr[MW][4];   // block-scaled FP8: the activation scale of each output row of the lane
 
-  auto memory_phase = [&](int ks) {
+  auto memory_phase = [&](int ks, auto nmb) {
+    constexpr int NMB = decltype(nmb)::value;   // row blocks with routed rows (MoE) or MW
     const uint8_t* st = smem + (ks % S) * Sh::STAGE;
     const uint8_t* sm = st + Sh::A_BYTES + Sh::B_BYTES;
 #pragma unroll
-    for (int mb = 0; mb < MW; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int d = 0; d < NA; ++d) {
         // WNA16: lane group g holds k 32g..32g+31 of the step (chunks 4g..4g+3); 8-bit
@@ -316,13 +329,13 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     if constexpr (FAM == FAM_FP8B) {
       const float* sa = reinterpret_cast<const float*>(sm + Sh::META_BYTES);
 #pragma unroll
-      for (int mb = 0; mb < MW; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) asr[mb][i] = sa[wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i];
     } else if constexpr (Sh::ASC_BYTES > 0) {
       const uint8_t* sa = sm + Sh::META_BYTES;
 #pragma unroll
-      for (int mb = 0; mb < MW; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
         asf[mb] = sa[(wm * 16 * MW + 16 * mb + (lane & 15)) * 4 + (lane >> 4)];
     }
 #pragma unroll
@@ -339,7 +352,8 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     }
   };
 
-  auto compute_phase = [&]() {
+  auto compute_phase = [&](auto nmb) {
+    constexpr int NMB = decltype(nmb)::value;
     if constexpr (family_int_groups(FAM)) {
       // Software-pipelined over the channel tiles: while the MFMAs of tile t run, the VALU
       // dequantizes tile t + 1 and applies the group scale to tile t - 1's partial sums.
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 #pragma unroll
         for (int d = 0; d < 4; ++d)
 #pragma unroll
-          for (int mb = 0; mb < MW; ++mb)
+          for (int mb = 0; mb < NMB; ++mb)
             part[cur][mb] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bw[cur][d],
                                       d == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : part[cur][mb]);
         if (t + 1 < NTW) {
@@ -363,17 +377,17 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         if (t > 0) {
           const float s = __uint_as_float(meta[t - 1] << 16);
 #pragma unroll
-          for (int mb = 0; mb < MW; ++mb) acc[mb][t - 1] += part[cur ^ 1][mb] * s;
+          for (int mb = 0; mb < NMB; ++mb) acc[mb][t - 1] += part[cur ^ 1][mb] * s;
         }
       }
       {
         const float s = __uint_as_float(meta[NTW - 1] << 16);
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb) acc[mb][NTW - 1] += part[(NTW - 1) & 1][mb] * s;
+        for (int mb = 0; mb < NMB; ++mb) acc[mb][NTW - 1] += part[(NTW - 1) & 1][mb] * s;
       }
       // issue order: one MFMA, then up to three VALU instructions
 #pragma unroll
-      for (int i = 0; i < 4 * MW * NTW; ++i) {
+      for (int i = 0; i < 4 * NMB * NTW; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         for (int d = 0; d < 4; ++d) {
           const bf16x8 bv = dequant_fp4x8_scaled(bq[t][0][d], s);
 #pragma unroll
-          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+          for (int mb = 0; mb < NMB; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
         }
       }
     } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         for (int d = 0; d < 4; ++d) {
           const bf16x8 bv = dequant_w8_step<FAM == FAM_F8A16>(bq[t][0], bq[t][NB - 1], d);
 #pragma unroll
-          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
+          for (int mb = 0; mb < NMB; ++mb) acc[mb][t] = mfma_bf16(__builtin_bit_cast(bf16x8, af[mb][d]), bv, acc[mb][t]);
         }
     } else if constexpr (FAM == FAM_FP8B) {
       // A wave's NTW tiles (NTW divides 8, first tile a multiple of NTW) lie in one 128-channel
@@ -408,19 +422,19 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       const float sw = __uint_as_float(meta[0]);
       float c[MW][4];
 #pragma unroll
-      for (int mb = 0; mb < MW; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[mb][i] = asr[mb][i] * sw;
       f32x4 part[MW][NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
           part[mb][t] = mfma_fp8_fp8(af[mb][0], af[mb][1], bq[t][0], bq[t][1], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[mb][t][i] * c[mb][i];
     } else if constexpr (FAM == FAM_W8A8) {
@@ -429,24 +443,24 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
-          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_i8(af[mb][q], bq[t][q], acc[mb][t]);
+          for (int mb = 0; mb < NMB; ++mb) acc[mb][t] = mfma_i8(af[mb][q], bq[t][q], acc[mb][t]);
     } else if constexpr (FAM == FAM_W4A4) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
           acc[mb][t] = mfma_fp4_fp4(af[mb][0], asf[mb], bq[t][0], int(meta[t]), acc[mb][t]);
     } else if constexpr (FAM == FAM_W4A8MX) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
           acc[mb][t] = mfma_fp8_fp4(af[mb][0], af[mb][1], bq[t][0], int(meta[t]), acc[mb][t], asf[mb]);
     } else {
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int mb = 0; mb < MW; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
           acc[mb][t] = mfma_fp8_fp4(af[mb][0], af[mb][1], bq[t][0], int(meta[t]), acc[mb][t]);
     }
   };
@@ -469,17 +483,28 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   phase_barrier();
   if (group == 1) phase_barrier();   // group 1 runs one phase behind
 
-  for (int ks = 0; ks < nks; ++ks) {
-    // memory phase of step ks: the slot of step ks + S - 1 held step ks - 1, which both groups
-    // finished reading before the barrier that opened this phase
-    if (ks + S - 1 < nks) issue_stage(ks + S - 1);
-    memory_phase(ks);
-    wait_step(ks + 1);   // own copies of step ks + 1 have landed
-    wait_lgkm0();
-    phase_barrier();
-    compute_phase();
-    // group 1's last compute phase needs no closing barrier; the counts of the groups match
-    if (!(group == 1 && ks == nks - 1)) phase_barrier();
+  // The main loop over row blocks 0 .. NMB - 1 (MoE: all of them, only the first, or none; each
+  // count a loop of its own so that each keeps its own register allocation).
+  auto main_loop = [&](auto nmb) {
+    for (int ks = 0; ks < nks; ++ks) {
+      // memory phase of step ks: the slot of step ks + S - 1 held step ks - 1, which both groups
+      // finished reading before the barrier that opened this phase
+      if (ks + S - 1 < nks) issue_stage(ks + S - 1);
+      if constexpr (decltype(nmb)::value > 0) memory_phase(ks, nmb);
+      wait_step(ks + 1);   // own copies of step ks + 1 have landed
+      wait_lgkm0();
+      phase_barrier();
+      if constexpr (decltype(nmb)::value > 0) compute_phase(nmb);
+      // group 1's last compute phase needs no closing barrier; the counts of the groups match
+      if (!(group == 1 && ks == nks - 1)) phase_barrier();
+    }
+  };
+  if constexpr (!MOE) {
+    main_loop(std::integral_constant<int, MW>{});
+  } else {
+    if (nlive == MW || nlive > 1) main_loop(std::integral_constant<int, MW>{});
+    else if (nlive == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
   }
 
   const int row_base = row0 + wm * 16 * MW;

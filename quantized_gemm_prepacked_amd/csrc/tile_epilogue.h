@@ -16,7 +16,8 @@ namespace hq {
 //   acc[m][n] -= sum_g s[n,g] * (128 + z[n,g]) * S[m][g]      (S: group sums of row m of X)
 // a K' = K/128 contraction, run on the bf16 MFMA over operands split into high and low bf16
 // halves: hi*hi + hi*lo + lo*hi keeps ~16 significant bits of each product (the fp32 sums in the
-// workspace and the fp32 -s*(128+z) are each exact to ~2^-17 relative). Lane l supplies
+// workspace are split to ~2^-17 relative; -s*(128+z) has 16 significant bits and splits
+// exactly). Lane l supplies
 // row / channel l&15 and groups 32*gb + 8*(l>>4) .. +7 of block gb; groups past G are zero.
 // Workspace: per activation row, Gp = ceil(G/32)*32 bf16 high halves then Gp low halves
 // (group_sums_split_kernel).
@@ -47,32 +48,31 @@ __device__ __forceinline__ void wna16_offset_contraction(const KParams& p, const
       sh[mb] = *reinterpret_cast<const u32x4*>(src);
       sl[mb] = *reinterpret_cast<const u32x4*>(src + Gp);
     }
-    float sc[NTW][8];
-    uint32_t zc[NTW][8];
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int g = min(32 * gb + 8 * h + j, G - 1);
-        const size_t unit = size_t(nt0 + t) * p.k_units + g;
-        sc[t][j] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(w + p.scales_off + unit * 32 + 2 * (lane & 15)));
-        zc[t][j] = p.asym ? uint32_t(w[p.zeros_off + unit * 8 + ((lane & 15) >> 1)]) : 0x88u;
-      }
+    // -s * (128 + z) of the lane's channel and 8 groups, exact in fp32 (8 x 8 significant
+    // bits), split as hi = the value truncated to bf16 and lo = the exact rest (at most 8
+    // significant bits, so its fp32 pattern has a zero low half): hi + lo is the value exactly
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
+      const size_t tile_unit = size_t(nt0 + t) * p.k_units;
+      const uint8_t* sbase = w + p.scales_off + tile_unit * 32 + 2 * (lane & 15);
+      const uint8_t* zbase = w + p.zeros_off + tile_unit * 8 + ((lane & 15) >> 1);
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t z = (lane & 1) ? (zc[t][j] >> 4) : (zc[t][j] & 0xFu);
-        const float b = (32 * gb + 8 * h + j < G) ? -sc[t][j] * float(128u + z) : 0.0f;
-        const uint32_t hi = f32_to_bf16_rne(b);
-        const uint32_t lo = f32_to_bf16_rne(b - __uint_as_float(hi << 16));
+        const int gj = 32 * gb + 8 * h + j;
+        const int g = min(gj, G - 1);
+        const float s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sbase + g * 32));
+        const uint32_t zb = p.asym ? uint32_t(zbase[g * 8]) : 0x88u;
+        const uint32_t z = (lane & 1) ? (zb >> 4) : (zb & 0xFu);
+        const float b = gj < G ? -s * float(128u + z) : 0.0f;
+        const uint32_t hi = __float_as_uint(b) & 0xFFFF0000u;
+        const uint32_t lo = __float_as_uint(b - __uint_as_float(hi));
         if (j & 1) {
-          bh[j >> 1] |= hi << 16;
-          bl[j >> 1] |= lo << 16;
+          bh[j >> 1] |= hi;
+          bl[j >> 1] |= lo & 0xFFFF0000u;
         } else {
-          bh[j >> 1] = hi;
-          bl[j >> 1] = lo;
+          bh[j >> 1] = hi >> 16;
+          bl[j >> 1] = lo >> 16;
         }
       }
       const bf16x8 bhv = __builtin_bit_cast(bf16x8, u32x4{bh[0], bh[1], bh[2], bh[3]});
@@ -126,27 +126,39 @@ __device__ __forceinline__ void store_tile(const KParams& p, const uint8_t* w,
     constexpr bool kChannelScale = FAM == FAM_W8A8 || FAM == FAM_W8A16 || FAM == FAM_F8A16;
     cs[t] = (kChannelScale && !p.out_i32) ? reinterpret_cast<const float*>(w + p.scales_off)[n] : 1.0f;
   }
+  // One row pointer per output row (the lane's column of the wave's first tile); the tiles of the
+  // row are 16 columns apart. bf16 results are rounded two at a time (tiles t, t + 1).
 #pragma unroll
   for (int mb = 0; mb < MW; ++mb)
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+    for (int i = 0; i < 4; ++i) {
+      const int o = orow[mb][i];
+      if (o < 0) continue;
+      const size_t row_off = size_t(o) * p.N + size_t(nt0) * 16 + (lane & 15);
+      if constexpr (FAM == FAM_W8A8) {
+        if (p.out_i32) {
+          int* yr = reinterpret_cast<int*>(p.y) + row_off;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = orow[mb][i];
-        if (o < 0) continue;
-        const size_t idx = size_t(o) * p.N + (nt0 + t) * 16 + (lane & 15);
-        const auto v = acc[mb][t][i];
-        if constexpr (family_int_groups(FAM)) {
-          reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * tw[mb][i]);
-        } else if constexpr (FAM == FAM_W8A8) {
-          if (p.out_i32) reinterpret_cast<int*>(p.y)[idx] = v;
-          else reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(float(v) * rs[mb][i] * cs[t] * tw[mb][i]);
-        } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
-          reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * cs[t] * tw[mb][i]);
-        } else {
-          reinterpret_cast<uint16_t*>(p.y)[idx] = f32_to_bf16_rne(v * rs[mb][i] * tw[mb][i]);
+          for (int t = 0; t < NTW; ++t) yr[16 * t] = acc[mb][t][i];
+          continue;
         }
       }
+      auto value = [&](int t) -> float {
+        const auto v = acc[mb][t][i];
+        if constexpr (family_int_groups(FAM)) return v * tw[mb][i];
+        else if constexpr (FAM == FAM_W8A8) return float(v) * rs[mb][i] * cs[t] * tw[mb][i];
+        else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) return v * cs[t] * tw[mb][i];
+        else return v * rs[mb][i] * tw[mb][i];
+      };
+      uint16_t* yr = reinterpret_cast<uint16_t*>(p.y) + row_off;
+#pragma unroll
+      for (int t = 0; t + 1 < NTW; t += 2) {
+        const uint32_t pk = f32x2_to_bf16x2_rne(value(t), value(t + 1));
+        yr[16 * t] = uint16_t(pk);
+        yr[16 * (t + 1)] = uint16_t(pk >> 16);
+      }
+      if constexpr (NTW % 2 == 1) yr[16 * (NTW - 1)] = uint16_t(f32x2_to_bf16x2_rne(value(NTW - 1), 0.0f));
+    }
 }
 
 }  // namespace hq
