@@ -249,6 +249,8 @@ def run_dense(args, wl: str):
     dev = torch.device("cuda:0")
     log(f"[bench] {spec['name']} N={N} K={K} M={Ms}: generating inputs")
     desc, std, packed, acts = make_inputs(wl, spec)
+    if args.stream_k:
+        desc = hq.with_flags(desc, hq.HQ_COMPUTE_STREAM_K)
     w0 = torch.from_numpy(packed).to(dev)
     n_copies = max(2, int(np.ceil(768e6 / packed.nbytes)))
     weights = [w0] + [w0.clone() for _ in range(n_copies - 1)]
@@ -382,6 +384,7 @@ def run_dense(args, wl: str):
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": spec["dtype"], "data": "synthetic",
         "config": {"workload": spec["name"], "N": N, "K": K, "M": Ms,
+                   **({"compute": "stream_k"} if args.stream_k else {}),
                    "weights": {"w4a16": "uint4 asym g128 bf16 scale + uint4 zero",
                                "w8a8": "int8 per-channel fp32 scale, int8 per-token act",
                                "w4a8": "mxfp4 e2m1 + e8m0 per 32, fp8 e4m3 per-token act",
@@ -806,6 +809,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="w4a16", choices=sorted(WORKLOADS) + ["moe", "moe_mx", "moe_fp8b", "moe_layer", "moe_layer_w4a8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-k", action="store_true",
+                    help="dense workloads: set HQ_COMPUTE_STREAM_K (small-M calls balanced over the CUs)")
     ap.add_argument("--no-moe", action="store_true",
                     help="default workload only: leave out the MoE gate_up sweep that follows the dense one")
     args = ap.parse_args()

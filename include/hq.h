@@ -110,6 +110,25 @@ typedef struct {
  * is the tuned kernels' speed at large M (measured about 2x slower for W4A16 at M = 8192). */
 #define HQ_COMPUTE_BATCH_INVARIANT 1
 
+/* Stream-K (the announcement's section "Device-specific performance tuning" names Stream-K
+ * scheduling among its tuning controls): for a dense call whose rows fit one row block of the
+ * small-M kernel (M <= 16 for most formats), the (16-channel tile group, K unit) work items are cut
+ * into one equal contiguous range per workgroup, about one workgroup per CU, instead of one
+ * workgroup per tile group -- so no CU idles when the tile groups do not divide evenly over the
+ * CUs. A tile group split between workgroups is summed by the last of them to finish (a per-group
+ * arrival counter in library-owned device memory, reset by that workgroup), in a fixed order: the
+ * result is deterministic, but not bit-identical to a call without the flag. The workspace holds
+ * the partial tiles (hq_gemm_workspace_bytes with the flag). The counters are kept per stream (up
+ * to 16 streams per GPU; calls on further streams run without Stream-K), so calls on one stream
+ * never share them with calls on another. Two things must not run at the same time: two replays
+ * of one captured HIP graph holding such a call, or such a replay and other work of the stream it
+ * was captured on. Other calls, other shapes and MoE ignore the flag. Ignored with
+ * HQ_COMPUTE_BATCH_INVARIANT. Measured on MI355X it is slower at the dense W4A16 decode shape
+ * (N=14336, K=4096, M=1: 17.1 us against 9.6 us without it): a workgroup then works through its
+ * two pieces one after the other, and decode time is set by load latency and total bytes, not by
+ * the per-CU share -- so it is off unless asked for. */
+#define HQ_COMPUTE_STREAM_K 2
+
 /*
  * Supported combinations (others return HQ_ERR_UNSUPPORTED):
  *   INT4_SYM   + BF16 scale, group 128, no zero-point + ACT_BF16              -> OUT_BF16
@@ -342,7 +361,9 @@ hq_status hq_grouped_gemm(const hq_quant_desc* desc, int64_t R, int32_t E, int64
  *                               HQ_ERR_INVALID_ARGUMENT and leaves the table unchanged.
  *   Without a call, the file named by the environment variable HQ_TUNING_FILE (if any) is read
  *   at the first dense plan. Loading while other threads launch GEMMs is safe (locked).
- * hq_gemm_plan reports the (kind, cfg, split) a dense call of that shape would run.
+ * hq_gemm_plan reports the (kind, cfg, split) a dense call of that shape would run; with
+ * HQ_COMPUTE_STREAM_K it may report kind 4 (the small-M kernel's configuration cfg in Stream-K
+ * form) with split = the number of workgroups.
  * ------------------------------------------------------------------------------------------- */
 hq_status hq_load_tuning_table(const char* path);
 hq_status hq_gemm_plan(const hq_quant_desc* desc, int64_t M, int64_t N, int64_t K, int32_t* kind,

@@ -57,6 +57,7 @@ class hq_quant_desc(ctypes.Structure):
 
 
 HQ_COMPUTE_BATCH_INVARIANT = 1
+HQ_COMPUTE_STREAM_K = 2
 
 
 def make_desc(weight_fmt, group_size, scale_dtype, has_zero_point, act_fmt, out_fmt=HQ_OUT_BF16,

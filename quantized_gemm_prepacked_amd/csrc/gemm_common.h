@@ -32,6 +32,11 @@ struct KParams {
   const float* topk_weights;
   int topk;
   int E;                    // MoE experts (block_expert entries outside [0, E) are skipped)
+  // Stream-K (skinny kernel, one row block): (tile group, K unit) items in all, partial-tile
+  // slots per tile group in the workspace, and the per-group arrival counters (zero between calls)
+  long long sk_items;
+  int sk_slots;
+  uint32_t* sk_counters;
 };
 
 template <int FAM>
@@ -103,6 +108,9 @@ struct SkinnyCfg {
 constexpr int kFewRows = 4;
 const SkinnyCfg* skinny_configs(int* count);
 int skinny_lds_bytes(int fam, int cfg);
+// Stream-K instantiations exist for these skinny configurations (the ones chosen at M <= 16).
+bool skinny_stream_k_cfg(int cfg);
+hipError_t launch_skinny_stream_k(const KParams& p, int fam, int cfg, int wgs, hipStream_t s);
 
 // A tiled-kernel instantiation: waves own (16*MW) x (16*NTW) sub-tiles, WM x WN waves per
 // workgroup; the workgroup tile is (16*MW*WM) x (16*NTW*WN).

@@ -21,6 +21,9 @@ namespace hq {
 namespace {
 
 constexpr int kCUs = 256;
+// Stream-K arrival counters: up to kSkStreams streams per GPU, kSkMaxGroups tile groups per call.
+constexpr int kSkStreams = 16;
+constexpr int kSkMaxGroups = 8192;
 
 // K per skinny unit (8-bit weights other than W8A8's step over two 64-k layout units at a time)
 int k_unit(const Combo& c) {
@@ -430,6 +433,24 @@ Plan plan_dense(const Combo& c, int64_t M, int64_t N, int64_t K) {
   if (tov.kind == 0 && tov.split >= 1 && tov.split <= units) split = tov.split;
   pl.split = split;
   pl.ws_bytes = split > 1 ? size_t(split) * M * N * acc_elem_bytes() : 0;
+  // Stream-K: one row block, a configuration with a Stream-K form, fewer tile groups than the
+  // workgroups the chip runs at once (one per CU; two for workgroups of at most eight waves), so
+  // that a plain launch would leave CUs idle; at least one K unit per wave
+  const long long res_wgs = (long long)kCUs * (sc.nw <= 8 ? 2 : 1);
+  if (c.stream_k && tov.kind < 0 && M <= 16 * sc.mb && skinny_stream_k_cfg(pl.cfg) &&
+      N / 16 / sc.ntw < res_wgs && N / 16 / sc.ntw <= kSkMaxGroups) {
+    const long long items = (long long)(N / 16 / sc.ntw) * units;
+    const long long wgs = std::min<long long>(res_wgs, items / sc.nw);
+    if (wgs >= 1) {
+      const long long per = items / wgs;                 // every workgroup gets per or per + 1
+      const int slots = int((units + per - 1) / per) + 1;  // pieces a tile group can be cut into
+      pl.kind = 4;
+      pl.split = int(wgs);
+      pl.sk_items = items;
+      pl.sk_slots = slots;
+      pl.ws_bytes = size_t(N / 16 / sc.ntw) * slots * size_t(sc.mb * sc.ntw * 4 * 64) * acc_elem_bytes();
+    }
+  }
   return pl;
 }
 
@@ -526,6 +547,45 @@ int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t,
   if (rows_per_expert < 2) return 16;
   if (rows_per_expert < 32) return 32;
   return 64;
+}
+
+// Stream-K arrival counters: library-owned, zero from load time, and left at zero by every call
+// (the workgroup that sums a tile group resets its counter). Each stream that runs a Stream-K
+// call gets its own set, so calls ordered on one stream reuse it safely and calls on different
+// streams never share one. The kernels get the device address of the current device's copy
+// (taken once per device), never the array's name.
+static __device__ uint32_t sk_counter_sets[kSkStreams * kSkMaxGroups];
+
+static hipError_t stream_k_counters(hipStream_t stream, uint32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint32_t* base[kMaxDevices] = {};
+  static hipStream_t owner[kMaxDevices][kSkStreams] = {};
+  static int used[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(sk_counter_sets));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    base[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = nullptr;
+  for (int i = 0; i < used[dev]; ++i)
+    if (owner[dev][i] == stream) {
+      *out = base[dev] + size_t(i) * kSkMaxGroups;
+      return hipSuccess;
+    }
+  if (used[dev] < kSkStreams) {
+    owner[dev][used[dev]] = stream;
+    *out = base[dev] + size_t(used[dev]) * kSkMaxGroups;
+    ++used[dev];
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
@@ -626,6 +686,21 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
   int n_cfg = 0;
   const SkinnyCfg& sc = skinny_configs(&n_cfg)[plan.cfg];
   const int rows_per_block = 16 * sc.mb;
+  if (plan.kind == 4 && !moe) {
+    uint32_t* counters = nullptr;
+    hipError_t e = stream_k_counters(call.stream, &counters);
+    if (e != hipSuccess) return e;
+    if (counters) {
+      p.M = int(call.M);
+      p.split = 1;
+      p.units_per_split = p.k_units;
+      p.sk_items = plan.sk_items;
+      p.sk_slots = plan.sk_slots;
+      p.sk_counters = counters;
+      return launch_skinny_stream_k(p, c.fam, plan.cfg, plan.split, call.stream);
+    }
+    // every counter set is held by other streams: the plain small-M launch (no K split)
+  }
   if (moe) {
     if (rows_per_block != call.block_m) return hipErrorInvalidValue;   // one row block = one block
     p.M = int(call.T * call.topk);
@@ -641,13 +716,13 @@ hipError_t launch_gemm(const GemmCall& call, const Plan& plan) {
     return launch_skinny(p, c.fam, true, plan.cfg, grid, call.stream);
   }
   p.M = int(call.M);
-  p.split = plan.split;
+  p.split = plan.kind == 4 ? 1 : plan.split;
   const int sk_units = int(call.K / k_unit(c));   // skinny units (128-k steps for block-scaled FP8)
-  p.units_per_split = (sk_units + plan.split - 1) / plan.split;
+  p.units_per_split = (sk_units + p.split - 1) / p.split;
   dim3 grid(unsigned(call.N / 16 / sc.ntw), unsigned((call.M + rows_per_block - 1) / rows_per_block),
-            unsigned(plan.split));
+            unsigned(p.split));
   hipError_t e = launch_skinny(p, c.fam, false, plan.cfg, grid, call.stream);
-  if (e != hipSuccess || plan.split == 1) return e;
+  if (e != hipSuccess || p.split == 1) return e;
   return launch_splitk_reduce(p, c.fam, call.stream);
 }
 

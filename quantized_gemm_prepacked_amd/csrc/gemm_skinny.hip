@@ -111,7 +111,7 @@ struct SkShape {
   static_assert(!FEW || (MB == 1 && LIVE >= kFewRows), "few-row form: one 16-row block");
 };
 
-template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE, bool FEW>
+template <int FAM, int MB, int NTW, int NW, int UNR, bool PP, bool MOE, bool FEW, bool SK = false>
 __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   using Sh = SkShape<FAM, MB, NTW, NW, UNR, PP, FEW>;
   using Acc = typename AccType<FAM>::type;
@@ -122,8 +122,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nt0 = blockIdx.x * NTW;
-  const int rb = blockIdx.y;
+  int nt0 = SK ? 0 : blockIdx.x * NTW;   // Stream-K: the tile group of the current segment
+  const int rb = SK ? 0 : blockIdx.y;
   const int row0 = rb * 16 * MB;
 
   const uint8_t* w = p.w;
@@ -168,6 +168,36 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     ascale_src = reinterpret_cast<const uint8_t*>(p.a_scale) + size_t(src_row) * (p.K / 32);
   }
 
+  // Stream-K (one row block): the (tile group, K unit) items, tile groups outermost, are cut into
+  // gridDim.x equal contiguous ranges, one per workgroup, so every workgroup streams the same
+  // number of weight units. A range covers whole tile groups and at most two partial ones; each
+  // piece of a group is a segment. A whole group is stored directly; the pieces of a split group
+  // leave fp32 (int32) partial tiles in the workspace, and the workgroup that contributes last
+  // (an arrival counter per group) sums them in piece order and stores the result, then sets the
+  // counter back to zero for the next call. No workgroup waits for another, and no fence writes
+  // back or invalidates a whole cache: the partial tiles and the counters are accessed at device
+  // scope, item by item.
+  const int k_units = p.k_units / Sh::WL;             // kernel units (steps of kUnitK k)
+  long long sk_item = 0, sk_end = 0;
+  if constexpr (SK) {
+    sk_item = (long long)blockIdx.x * p.sk_items / gridDim.x;
+    sk_end = (long long)(blockIdx.x + 1) * p.sk_items / gridDim.x;
+  }
+  for (;;) {
+  int ubeg, uend, sk_g = 0;
+  if constexpr (SK) {
+    if (sk_item >= sk_end) break;
+    sk_g = int(sk_item / k_units);
+    ubeg = int(sk_item - (long long)sk_g * k_units);
+    uend = int(sk_end - (long long)sk_g * k_units < k_units ? sk_end - (long long)sk_g * k_units : k_units);
+    sk_item += uend - ubeg;
+    nt0 = sk_g * NTW;
+    __syncthreads();   // the previous segment's reads of the reduction buffer are done
+  } else {
+    ubeg = blockIdx.z * p.units_per_split;
+    uend = min(k_units, ubeg + p.units_per_split);
+  }
+
   Acc acc[MB][NTW];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -177,7 +207,6 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
   uint8_t* wlds = smem + wave * Sh::WAVE_LDS;
   u32x4 bw[Sh::NBUF][UNR][NTW];   // packed weights of the batches in flight
   u32x4 bw2[Sh::NBUF][UNR][Sh::WL == 2 ? NTW : 1];   // block-scaled FP8: the step's second unit
-  const int k_units = p.k_units / Sh::WL;             // kernel units (steps of kUnitK k)
 
   // Issue every copy and load of unit u into slot (buf, r).
   auto issue_unit = [&](int buf, int r, int u) __attribute__((always_inline)) {
@@ -363,8 +392,6 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
 
   // This wave's units are u0, u0 + NW, ... < uend, in batches of UNR; a remainder below UNR is
   // taken one unit at a time.
-  const int ubeg = blockIdx.z * p.units_per_split;
-  const int uend = min(k_units, ubeg + p.units_per_split);
   const int u0 = ubeg + wave;
   const int nunits = u0 < uend ? (uend - u0 + NW - 1) / NW : 0;
   const int nbatch = nunits / UNR;
@@ -444,8 +471,56 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(KParams p) {
     for (int ww = 1; ww < NW; ++ww) sum += red[ww][q][le];
     const int ib = 16 * mb + 4 * (le >> 4) + j;
     const int n = (nt0 + t) * 16 + (le & 15);
-    store_result<FAM, MOE>(p, w, row0 + ib, n, sum, blockIdx.z);
+    if (!SK || (ubeg == 0 && uend == k_units)) {
+      store_result<FAM, MOE>(p, w, row0 + ib, n, sum, blockIdx.z);
+    } else {
+      // partial tile of this piece: slot = this workgroup's place among the group's contributors
+      const long long first = ((long long)sk_g * k_units + 1) * gridDim.x - 1;
+      const int slot = int(blockIdx.x - first / p.sk_items);
+      // written at device (agent) scope: through to the point where every CU's loads see it
+      __hip_atomic_store(reinterpret_cast<Elem*>(p.ws) + (size_t(sk_g) * p.sk_slots + slot) * (kVals * 64) + v,
+                         sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+  if constexpr (SK) {
+    if (!(ubeg == 0 && uend == k_units)) {
+      const long long gi = (long long)sk_g * k_units;
+      const int w_first = int(((gi + 1) * gridDim.x - 1) / p.sk_items);
+      const int w_last = int(((gi + k_units) * gridDim.x - 1) / p.sk_items);
+      // Ordering without whole-cache fences: every partial store above has completed (its wait
+      // count is zero) before the workgroup barrier, and the arrival is counted after the barrier;
+      // the partial tiles are read back below with device-scope loads, which bypass the
+      // non-coherent cache path.
+      wait_vmcnt<0>();
+      __syncthreads();   // every thread's partial stores are complete; the reduction buffer is free
+      int* flag = reinterpret_cast<int*>(smem);
+      if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(p.sk_counters + sk_g, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        *flag = int(old) + 1 == w_last - w_first + 1;
+      }
+      __syncthreads();
+      if (*flag) {
+        Elem* part = reinterpret_cast<Elem*>(p.ws) + size_t(sk_g) * p.sk_slots * (kVals * 64);
+        for (int v = threadIdx.x; v < kVals * 64; v += NW * 64) {
+          const int le = v & 63;
+          if (FEW && (le >> 4) >= Sh::LIVE / 4) continue;
+          Elem sum = __hip_atomic_load(part + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int sl = 1; sl <= w_last - w_first; ++sl)
+            sum += __hip_atomic_load(part + size_t(sl) * (kVals * 64) + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int q = v >> 6;
+          const int j = q & 3;
+          const int t = (q >> 2) % NTW;
+          const int mb = (q >> 2) / NTW;
+          store_result<FAM, MOE>(p, w, row0 + 16 * mb + 4 * (le >> 4) + j, (nt0 + t) * 16 + (le & 15), sum, 0);
+        }
+        if (threadIdx.x == 0)   // ready for the next call
+          __hip_atomic_store(p.sk_counters + sk_g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if constexpr (!SK) break;
+  }   // segments
 }
 
 }  // namespace
@@ -551,6 +626,69 @@ static hipError_t launch_skinny_fam(const KParams& p, int cfg, dim3 grid, hipStr
       return hipErrorInvalidValue;
   }
 #undef HQ_SK
+}
+
+// ---- Stream-K launches (dense, one row block) ------------------------------------------------
+static constexpr int kSkCfgs[] = {0, 1, 2, 11, 12, 13, 20, 21, 27, 28, 30, 31, 32, 33};
+
+bool skinny_stream_k_cfg(int cfg) {
+  for (int c : kSkCfgs)
+    if (c == cfg) return true;
+  return false;
+}
+
+template <int FAM, int I>
+static hipError_t launch_sk_one(const KParams& p, int wgs, hipStream_t s) {
+  constexpr SkinnyCfg C = kSkinny[I];
+  constexpr int lds = SkShape<FAM, C.mb, C.ntw, C.nw, C.unr, C.pp != 0, C.few != 0>::LDS;
+  if constexpr (lds > 160 * 1024) {
+    return hipErrorInvalidValue;
+  } else {
+    if (C.few && p.M > kFewRows) return hipErrorInvalidValue;
+    auto kern = skinny_gemm_kernel<FAM, C.mb, C.ntw, C.nw, C.unr, C.pp != 0, false, C.few != 0, true>;
+    if (lds > 65536)
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipLaunchKernelGGL(kern, dim3(unsigned(wgs)), dim3(C.nw * 64), lds, s, p);
+    return hipGetLastError();
+  }
+}
+
+template <int FAM>
+static hipError_t launch_sk_fam(const KParams& p, int cfg, int wgs, hipStream_t s) {
+  switch (cfg) {
+    case 0: return launch_sk_one<FAM, 0>(p, wgs, s);
+    case 1: return launch_sk_one<FAM, 1>(p, wgs, s);
+    case 2: return launch_sk_one<FAM, 2>(p, wgs, s);
+    case 11: return launch_sk_one<FAM, 11>(p, wgs, s);
+    case 12: return launch_sk_one<FAM, 12>(p, wgs, s);
+    case 13: return launch_sk_one<FAM, 13>(p, wgs, s);
+    case 20: return launch_sk_one<FAM, 20>(p, wgs, s);
+    case 21: return launch_sk_one<FAM, 21>(p, wgs, s);
+    case 27: return launch_sk_one<FAM, 27>(p, wgs, s);
+    case 28: return launch_sk_one<FAM, 28>(p, wgs, s);
+    case 30: return launch_sk_one<FAM, 30>(p, wgs, s);
+    case 31: return launch_sk_one<FAM, 31>(p, wgs, s);
+    case 32: return launch_sk_one<FAM, 32>(p, wgs, s);
+    case 33: return launch_sk_one<FAM, 33>(p, wgs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_skinny_stream_k(const KParams& p, int fam, int cfg, int wgs, hipStream_t s) {
+  switch (fam) {
+    case FAM_WNA16: return launch_sk_fam<FAM_WNA16>(p, cfg, wgs, s);
+    case FAM_WNA2: return launch_sk_fam<FAM_WNA2>(p, cfg, wgs, s);
+    case FAM_WNA3: return launch_sk_fam<FAM_WNA3>(p, cfg, wgs, s);
+    case FAM_MXW4A16: return launch_sk_fam<FAM_MXW4A16>(p, cfg, wgs, s);
+    case FAM_W8A8: return launch_sk_fam<FAM_W8A8>(p, cfg, wgs, s);
+    case FAM_W4A8: return launch_sk_fam<FAM_W4A8>(p, cfg, wgs, s);
+    case FAM_W4A4: return launch_sk_fam<FAM_W4A4>(p, cfg, wgs, s);
+    case FAM_W4A8MX: return launch_sk_fam<FAM_W4A8MX>(p, cfg, wgs, s);
+    case FAM_FP8B: return launch_sk_fam<FAM_FP8B>(p, cfg, wgs, s);
+    case FAM_W8A16: return launch_sk_fam<FAM_W8A16>(p, cfg, wgs, s);
+    case FAM_F8A16: return launch_sk_fam<FAM_F8A16>(p, cfg, wgs, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_skinny(const KParams& p, int fam, bool moe, int cfg, dim3 grid,

@@ -48,9 +48,10 @@ hq_status resolve(const hq_quant_desc* d, hq::Combo* c) {
     return fail(HQ_ERR_INVALID_ARGUMENT, "unknown out_fmt %d", d->out_fmt);
   c->out_i32 = d->out_fmt == HQ_OUT_INT32_ACC;
   c->asym = false;
-  if (d->compute_flags & ~int32_t(HQ_COMPUTE_BATCH_INVARIANT))
+  if (d->compute_flags & ~int32_t(HQ_COMPUTE_BATCH_INVARIANT | HQ_COMPUTE_STREAM_K))
     return fail(HQ_ERR_INVALID_ARGUMENT, "unknown compute_flags bits 0x%x", unsigned(d->compute_flags));
   c->invariant = (d->compute_flags & HQ_COMPUTE_BATCH_INVARIANT) != 0;
+  c->stream_k = !c->invariant && (d->compute_flags & HQ_COMPUTE_STREAM_K) != 0;
   switch (d->weight_fmt) {
     case HQ_W_INT4_SYM:
     case HQ_W_UINT4_ASYM: {

@@ -18,6 +18,7 @@ struct Combo {
   bool asym;     // WNA16 with zero-points
   bool out_i32;  // W8A8 raw accumulator output
   bool invariant;  // HQ_COMPUTE_BATCH_INVARIANT: one fixed kernel configuration for every M
+  bool stream_k;   // HQ_COMPUTE_STREAM_K: small-M calls balanced over the CUs (Stream-K)
 };
 
 size_t prepacked_bytes(const Combo& c, int64_t E, int64_t N, int64_t K);
@@ -26,10 +27,14 @@ void prepack(const Combo& c, int64_t E, int64_t N, int64_t K, const void* wq, co
 
 // Kernel choice for one call (see dispatch in gemm_kernels.hip).
 struct Plan {
-  int kind;    // 0 = skinny (waves split K), 1 = tiled (LDS-staged activations)
+  int kind;    // 0 = skinny (waves split K), 1 = tiled (LDS-staged activations), 2 = pipelined,
+               // 3 = ping-pong, 4 = skinny Stream-K (one row block, `split` workgroups)
   int cfg;     // index into the kind's instantiation table
-  int split;   // K splits across workgroups (partials in the workspace, then a reduction)
+  int split;   // K splits across workgroups (partials in the workspace, then a reduction);
+               // Stream-K: the number of workgroups
   size_t ws_bytes;
+  long long sk_items = 0;   // Stream-K: (tile group, K unit) items
+  int sk_slots = 0;         // Stream-K: partial-tile slots per tile group
 };
 
 struct GemmCall {
