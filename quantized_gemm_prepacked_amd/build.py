@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libhq.so")
+PROBE_OUT = os.path.join(PKG, "libhq_probe.so")
 BUILD = os.path.join(PKG, "_build")
 
 SOURCES = ["hq_api.cpp", "prepack.cpp", "gemm_dispatch.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gemm_pipe.hip", "gemm_pingpong.hip", "moe_align.hip", "moe_layer.hip", "act_quant.hip", "tuning_table.cpp"]
@@ -88,6 +89,16 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")
+    # the streaming-read probe of ceilings.py: its own small library, not part of libhq.so
+    pobj = _compile("read_probe.hip")
+    ptmp = PROBE_OUT + ".tmp"
+    r = subprocess.run(["g++", "-shared", "-fPIC", "-o", ptmp, pobj, f"-L{rt}", "-l:libamdhip64.so",
+                        f"-Wl,-rpath,{rt}", "-Wl,--no-undefined"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe link failed:\n" + r.stdout + r.stderr)
+    os.replace(ptmp, PROBE_OUT)
+    if verbose:
+        print(f"built {PROBE_OUT}")
     return OUT
 
 
