@@ -308,6 +308,8 @@ int32_t hq_moe_block_m(const hq_quant_desc* desc, int64_t T, int32_t topk, int32
  *   w_packed      prepacked weights of all E experts (hq_prepack_weights with E experts)
  *   sorted_ids, block_expert, num_padded: outputs of hq_moe_align with the same T, topk, E,
  *                 block_m (device)
+ *   block_m       16, 32, 64 or 128 (HQ_ERR_UNSUPPORTED otherwise); 128 needs K % 128 == 0 and
+ *                 N % 128 == 0 (HQ_ERR_UNSUPPORTED otherwise)
  *   topk_weights  fp32 [T*topk] or NULL (device)
  *   y             bf16 [T*topk, N] row-major (device)
  *   ws            hq_moe_gemm_workspace_bytes(...) bytes (may be 0 / NULL)

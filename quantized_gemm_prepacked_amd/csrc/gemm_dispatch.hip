@@ -234,6 +234,12 @@ constexpr RangeEntry kW8a16Table[] = {{128, 0, 0}, {kInf, 3, 3}};
 // 52.1), 64 x 256 with four slots to 512 (M=256: 49.5 us against 53.1 with three), 128 x 256
 // beyond (M=1024 / 8192: 133 / 916 us; the skinny kernel 242 / 1834)
 constexpr RangeEntry kWna2Table[] = {{128, 0, 0}, {512, 3, 13}, {kInf, 3, 0}};
+// 3-bit WnA16 (each tile's 768-byte unit of a step lands in a 1 KiB LDS slot, three 4-byte-per-lane
+// copies, so every ping-pong tile whose ring fits the LDS works), measured at N=14336, K=4096:
+// skinny to M=128 (46.6 us), ping-pong 128 x 128 to 256 (M=192 / 256: 55.2 / 55.6 us against 69.9
+// for 64 x 256 with four slots), 128 x 256 beyond (M=512 / 1024 / 2048 / 8192: 89.8 / 172.6 / 337.8
+// / 1154.8 us; the best skinny configuration 2342 us at M=8192)
+constexpr RangeEntry kWna3Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
 
 int tile_n_of(int kind, int cfg) {
   int n = 0;
@@ -251,7 +257,7 @@ int tile_n_of(int kind, int cfg) {
 
 // (kind, cfg) from the table, or kind 0 for the skinny kernel.
 RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
-  if (K % 128 != 0 || c.fam == FAM_WNA3) return {0, 0, 0};   // 3-bit weights: the skinny kernel
+  if (K % 128 != 0) return {0, 0, 0};
   const RangeEntry* t;
   int n;
   if (c.fam == FAM_WNA16) {
@@ -269,6 +275,9 @@ RangeEntry pick_range(const Combo& c, int64_t M, int64_t N, int64_t K) {
   } else if (c.fam == FAM_WNA2) {
     t = kWna2Table;
     n = int(sizeof(kWna2Table) / sizeof(kWna2Table[0]));
+  } else if (c.fam == FAM_WNA3) {
+    t = kWna3Table;
+    n = int(sizeof(kWna3Table) / sizeof(kWna3Table[0]));
   } else if (c.fam == FAM_W8A16 || c.fam == FAM_F8A16) {
     t = kW8a16Table;
     n = int(sizeof(kW8a16Table) / sizeof(kW8a16Table[0]));
@@ -491,10 +500,10 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   // T = 32..4096: 32 x 256 and 64 x 512 beat the LDS-tiled and skinny kernels from two routed
   // rows per expert up); otherwise the LDS-tiled 64 x 128 tile, then the skinny kernel.
   const bool a32 = uint64_t(T) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);   // 32-bit row offsets
-  if (K % 128 == 0 && a32 && (block_m == 32 || block_m == 64)) {
+  if (K % 128 == 0 && a32 && (block_m == 32 || block_m == 64 || block_m == 128)) {
     // (the 8-bit-activation formats' 32-row tiles do not split into whole-wave copies: skinny)
-    static const int pp32[1] = {7}, pp64[2] = {5, 4};
-    const int* cands = block_m == 32 ? pp32 : pp64;
+    static const int pp32[1] = {7}, pp64[2] = {5, 4}, pp128[2] = {0, 3};
+    const int* cands = block_m == 32 ? pp32 : block_m == 64 ? pp64 : pp128;
     const int n_c = block_m == 32 ? 1 : 2;
     int n_p = 0;
     const PPCfg* pc = pp_configs(&n_p);
@@ -508,6 +517,10 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
         return pl;
       }
     }
+  }
+  if (block_m == 128) {   // only the ping-pong kernel has 128-row tiles
+    pl.kind = -1;
+    return pl;
   }
   if (c.fam == FAM_WNA16 && block_m == 64 && N % 128 == 0 && K % 128 == 0) {
     pl.kind = 1;       // LDS-tiled, 64 x 128 tiles: one expert block per tile row
@@ -535,18 +548,30 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
   return pl;
 }
 
-bool moe_block_m_supported(int32_t block_m) { return block_m == 16 || block_m == 32 || block_m == 64; }
+bool moe_block_m_supported(int32_t block_m) {
+  return block_m == 16 || block_m == 32 || block_m == 64 || block_m == 128;
+}
 
 // Measured on MI355X (gate_up 4096 x 7168 and Down 7168 x 2048, 256 experts, top-8, skewed
-// routing): 16-row blocks below 2 routed rows per expert, 32-row blocks (ping-pong 32 x 256)
-// from 2, 64-row blocks (ping-pong 64 x 512) from 32 -- the two tie at 16 rows per expert and the
-// wider tile wins by ~11% at 64, where the padding of the small experts costs less than it gains.
-int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t, int64_t) {
+// routing): 16-row blocks below 2 routed rows per expert, 32-row blocks from 2, 64-row blocks
+// (ping-pong 64 x 512 / 64 x 256) from 8 -- at 8 and 16 rows per expert (T = 256 / 512) they beat
+// 32-row blocks in every format measured (INT4 gate_up 375 / 566 us against 399 / 636; MXFP4 315 /
+// 478 against 325 / 515; block-scaled FP8 463 / 620 against 569 / 928; the INT4 and W4A8 layers at
+// T = 512 942 / 612 us against 1026 / 894). 128-row blocks (ping-pong 128 x 256): for bf16
+// activations with 4-bit weights from 64 rows per expert (INT4 gate_up T = 2048 / 4096: 1423 / 2504
+// us against 1528 / 2713; MXFP4 1201 / 2079 against 1277 / 2295; the INT4 layer 2254 / 4021 against
+// 2330 / 4235; a tie at 32 rows), for block-scaled FP8 from 8 (T = 256 / 1024 / 4096: 454 / 816 /
+// 2064 us against 463 / 939 / 2591). The other 8-bit-activation formats keep 64-row blocks (the
+// W4A8 layer at T = 4096: 2707 us with 128 against 2509).
+int32_t moe_block_m(const Combo& c, int64_t T, int32_t topk, int32_t E, int64_t N, int64_t K) {
   if (c.invariant) return 32;
   const double rows_per_expert = double(T) * topk / std::max(1, E);
   if (rows_per_expert < 2) return 16;
-  if (rows_per_expert < 32) return 32;
-  return 64;
+  if (rows_per_expert < 8) return 32;
+  const bool fits128 = K % 128 == 0 && N % 128 == 0 &&
+                       uint64_t(T) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);
+  const bool wide = (c.fam == FAM_WNA16 || c.fam == FAM_MXW4A16) ? rows_per_expert >= 64 : c.fam == FAM_FP8B;
+  return wide && fits128 ? 128 : 64;
 }
 
 // Stream-K arrival counters: library-owned, zero from load time, and left at zero by every call

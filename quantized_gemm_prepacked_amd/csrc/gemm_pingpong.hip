@@ -54,6 +54,13 @@ struct PPTraits<FAM_WNA2> {   // 2-bit codes: 512 bytes per tile and step (half 
   static constexpr int kAScaleBytes = 0;
 };
 template <>
+struct PPTraits<FAM_WNA3> {   // 3-bit codes: 768 bytes per tile and step, three 4-byte-per-lane copies
+  static constexpr int kRowBytes = 256;
+  static constexpr int kUnitsPerStep = 1;
+  static constexpr int kMetaPerTile = 32;   // 16 bf16 group scales
+  static constexpr int kAScaleBytes = 0;
+};
+template <>
 struct PPTraits<FAM_W8A8> {
   static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 2;
@@ -131,7 +138,9 @@ struct PPShape {
   static constexpr int NT = BN / 16;
   static constexpr int UPS = PPTraits<FAM>::kUnitsPerStep;
   static constexpr int TILE_STEP_BYTES = UPS * family_unit_bytes(FAM);   // weight bytes per tile and step
-  static constexpr int B_BYTES = NT * TILE_STEP_BYTES;
+  // LDS bytes per tile and step: 3-bit units (768 bytes) each take a 1 KiB slot
+  static constexpr int B_SLOT = FAM == FAM_WNA3 ? 1024 : TILE_STEP_BYTES;
+  static constexpr int B_BYTES = NT * B_SLOT;
   static constexpr int MPT = PPTraits<FAM>::kMetaPerTile;
   static constexpr int META_BYTES = NT * MPT;
   static constexpr int META_PER_WAVE = META_BYTES / 8;
@@ -141,7 +150,7 @@ struct PPShape {
   static constexpr int STAGE = (A_BYTES + B_BYTES + META_BYTES + ASC_BYTES + 1023) / 1024 * 1024;
   static constexpr int LDS = kStages * STAGE;
   static constexpr int A_INSTR = A_BYTES / 1024 / 8;
-  static constexpr int B_INSTR = B_BYTES / 1024 / 8;
+  static constexpr int B_INSTR = FAM == FAM_WNA3 ? 3 * NT / 8 : B_BYTES / 1024 / 8;
   static constexpr int INSTR = A_INSTR + B_INSTR + (META_BYTES ? 1 : 0) + (ASC_BYTES ? 1 : 0);
   // the copies split evenly over the eight waves (shapes that do not are never launched)
   // the copies split evenly over the eight waves (shapes that do not are never launched), and
@@ -264,6 +273,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
         // one copy moves the step's 512 bytes of tiles 2u (lanes 0-31) and 2u + 1 (lanes 32-63)
         const size_t unit = size_t(nt_wg + 2 * u + (lane >> 5)) * p.k_units + size_t(ks);
         lds_dma16(w + unit * 512 + 16 * (lane & 31), sb + u * 1024);
+      } else if constexpr (FAM == FAM_WNA3) {
+        // tile tl's 768-byte unit of the step in three 256-byte pieces (4 bytes per lane), an
+        // exact image at the start of the tile's 1 KiB slot
+        const int tl = wave * (Sh::NT / 8) + j / 3, c = j % 3;
+        const size_t unit = size_t(nt_wg + tl) * p.k_units + size_t(ks);
+        lds_dma4(w + unit * 768 + 256 * c + 4 * lane, sb + tl * 1024 + 256 * c);
       } else {
         const size_t unit = size_t(nt_wg + u / UPS) * p.k_units + size_t(ks) * UPS + (u % UPS);
         lds_dma16(w + unit * kUnitBytes + 16 * lane, sb + u * 1024);
@@ -291,6 +306,11 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 v = *reinterpret_cast<const u32x2*>(st + Sh::A_BYTES + (wn * NTW + t) * 512 + 8 * lane);
       return u32x4{v[0], v[1], 0u, 0u};
+    } else if constexpr (FAM == FAM_WNA3) {   // low bits: 8 bytes per lane; high bits: 4
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const uint8_t* b = st + Sh::A_BYTES + (wn * NTW + t) * 1024;
+      const u32x2 v = *reinterpret_cast<const u32x2*>(b + 8 * lane);
+      return u32x4{v[0], v[1], *reinterpret_cast<const uint32_t*>(b + 512 + 4 * lane), 0u};
     } else {
       const int u = (wn * NTW + t) * UPS + q;
       return *reinterpret_cast<const u32x4*>(st + Sh::A_BYTES + u * 1024 + 16 * lane);
@@ -483,8 +503,9 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   phase_barrier();
   if (group == 1) phase_barrier();   // group 1 runs one phase behind
 
-  // The main loop over row blocks 0 .. NMB - 1 (MoE: all of them, only the first, or none; each
-  // count a loop of its own so that each keeps its own register allocation).
+  // The main loop over row blocks 0 .. NMB - 1 (MoE: all of them, only the first, or none, and
+  // with four row blocks per wave every count; each count a loop of its own so that each keeps
+  // its own register allocation).
   auto main_loop = [&](auto nmb) {
     for (int ks = 0; ks < nks; ++ks) {
       // memory phase of step ks: the slot of step ks + S - 1 held step ks - 1, which both groups
@@ -501,6 +522,12 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
   };
   if constexpr (!MOE) {
     main_loop(std::integral_constant<int, MW>{});
+  } else if constexpr (MW == 4) {   // 128-row blocks: every count of live row blocks
+    if (nlive == 4) main_loop(std::integral_constant<int, 4>{});
+    else if (nlive == 3) main_loop(std::integral_constant<int, 3>{});
+    else if (nlive == 2) main_loop(std::integral_constant<int, 2>{});
+    else if (nlive == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
   } else {
     if (nlive == MW || nlive > 1) main_loop(std::integral_constant<int, MW>{});
     else if (nlive == 1) main_loop(std::integral_constant<int, 1>{});
@@ -577,11 +604,11 @@ int pp_lds_table(int cfg, std::integer_sequence<int, I...>) {
 
 int pp_lds_bytes(int fam, int cfg) {
   constexpr int n = int(sizeof(kPP) / sizeof(kPP[0]));
-  // (3-bit weights' 768-byte units do not split into the kernel's 1 KiB copies: no instantiation)
-  if (cfg < 0 || cfg >= n || fam == FAM_WNA3) return 1 << 30;
+  if (cfg < 0 || cfg >= n) return 1 << 30;
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return pp_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_WNA2) return pp_lds_table<FAM_WNA2>(cfg, seq);
+  if (fam == FAM_WNA3) return pp_lds_table<FAM_WNA3>(cfg, seq);
   if (fam == FAM_W8A8) return pp_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A4) return pp_lds_table<FAM_W4A4>(cfg, seq);
   if (fam == FAM_W4A8MX) return pp_lds_table<FAM_W4A8MX>(cfg, seq);
@@ -625,6 +652,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   if (moe) {
     if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_WNA2) return launch_pp_fam<FAM_WNA2, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+    if (fam == FAM_WNA3) return launch_pp_fam<FAM_WNA3, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_MXW4A16) return launch_pp_fam<FAM_MXW4A16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
     if (fam == FAM_W4A8) return launch_pp_fam<FAM_W4A8, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
@@ -637,6 +665,7 @@ hipError_t launch_pingpong(const KParams& p, int fam, bool moe, int cfg, dim3 gr
   }
   if (fam == FAM_WNA16) return launch_pp_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_WNA2) return launch_pp_fam<FAM_WNA2, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_WNA3) return launch_pp_fam<FAM_WNA3, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W8A8) return launch_pp_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A4) return launch_pp_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A8MX) return launch_pp_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);

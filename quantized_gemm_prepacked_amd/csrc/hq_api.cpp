@@ -474,7 +474,7 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
   if (T * topk * N >= (int64_t(1) << 31))
     return fail(HQ_ERR_UNSUPPORTED, "T*topk*N must stay below 2^31");
   if (!hq::moe_block_m_supported(block_m))
-    return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: supported values are 16, 32, 64", block_m);
+    return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: supported values are 16, 32, 64, 128", block_m);
   if (c.invariant && block_m != 32)
     return fail(HQ_ERR_INVALID_ARGUMENT, "block_m=%d: batch-invariant MoE calls use block_m 32", block_m);
   if (per_token && !a_scale)
@@ -486,7 +486,9 @@ hq_status hq_moe_grouped_gemm(const hq_quant_desc* desc, int64_t T, int32_t topk
     return fail(HQ_ERR_INVALID_ARGUMENT, "a, w_packed and y must be 16-byte aligned");
   if (T == 0) return ok();
   const hq::Plan plan = hq::plan_moe(c, T, topk, E, N, K, block_m);
-  if (plan.kind < 0) return fail(HQ_ERR_INVALID_ARGUMENT, "the HQ_TUNE override does not fit this shape");
+  if (plan.kind < 0)
+    return fail(HQ_ERR_UNSUPPORTED, "block_m=%d: no kernel configuration fits N=%lld K=%lld (128-row blocks need K %% 128 == 0 and N %% 128 == 0), or the HQ_TUNE override does not fit",
+                block_m, (long long)N, (long long)K);
   if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
     return fail(HQ_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, plan.ws_bytes);
   if (ws && !aligned16(ws)) return fail(HQ_ERR_INVALID_ARGUMENT, "ws must be 16-byte aligned");

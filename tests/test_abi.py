@@ -104,6 +104,9 @@ def test_moe_rejections():
     with pytest.raises(hq.HQError) as ei:
         hq.hq_moe_grouped_gemm(d, 4, 8, 256, 256, 512, 16, None, 16, 16, 16, 16, 48, None, 16, stream=0)
     assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
+    with pytest.raises(hq.HQError) as ei:      # 128-row blocks need N % 128 == 0
+        hq.hq_moe_grouped_gemm(d, 4, 8, 256, 272, 512, 16, None, 16, 16, 16, 16, 128, None, 16, stream=0)
+    assert ei.value.status == hq.HQ_ERR_UNSUPPORTED
 
 
 def test_moe_capacity_bounds_padding():

@@ -121,6 +121,8 @@ def _moe_case(T, topk, E, N, K, bm, with_weights, seed, random_codes=False):
     (400, 8, 16, 1024, 768, 64, True),    # ping-pong 64 x 512 tiles
     (150, 8, 8, 512, 384, 32, True),      # ping-pong 32 x 256 tiles
     (90, 8, 24, 768, 1152, 32, False),    # 32 x 256 tiles, 9 groups, sparse experts
+    (600, 8, 16, 512, 512, 128, True),    # 128-row blocks: ping-pong 128 x 256
+    (300, 8, 64, 384, 640, 128, False),   # 128 x 128 tiles, 5 groups, every count of live row blocks
 ])
 def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
     inp, experts, y = _moe_case(T, topk, E, N, K, bm, tw, 500 + T)

@@ -101,6 +101,8 @@ MOE_CASES = [
     (200, 8, 32, 272, 384, 64, True),     # N = 17 channel tiles: skinny kernel, 64-row blocks
     (300, 8, 16, 256, 640, 64, True),     # ping-pong 64 x 256, K/128 = 5
     (400, 8, 16, 1024, 768, 64, True),    # ping-pong 64 x 512 (W4A8) / 64 x 256 (W8A8)
+    (600, 8, 16, 512, 512, 128, True),    # 128-row blocks: ping-pong 128 x 256
+    (300, 8, 64, 256, 640, 128, False),   # 128-row blocks, mostly padding, K/128 = 5
 ]
 
 
@@ -116,7 +118,8 @@ def test_moe_q_small(fmt, T, topk, E, N, K, bm, tw):
 @pytest.mark.parametrize("T", [8, 128, 1024])
 def test_moe_q_full_size_sampled(fmt, T):
     """DeepSeek-V3 gate_up shape (256 experts, top-8, K = 7168, N = 4096) at the block size the
-    library recommends (16, 32, 64 rows for T = 8, 128, 1024), sampled output columns."""
+    library recommends (16, 32, 64 rows for T = 8, 128, 1024; 128 rows at T = 1024 for block-scaled
+    FP8), sampled output columns."""
     E, topk, N, K = 256, 8, 4096, 7168
     desc = FORMATS[fmt][0]
     bm = hq.hq_moe_block_m(desc, T, topk, E, N, K)

@@ -1,7 +1,8 @@
 """GPU parity of 3-bit WnA16 (UINT3 codes with a uint3 zero-point and a bf16 scale per channel and
 group of 128, bf16 activations; the low two bits and the high bit of each code bit-selected into
-the offset-128 bf16 operand, bf16 MFMA, group scale on the fp32 partial; the small-M kernel at
-every M) against the CPU oracle, through the C ABI: dense, MoE and grouped calls."""
+the offset-128 bf16 operand, bf16 MFMA, group scale on the fp32 partial; the small-M kernel to
+M = 128, the LDS-staged ping-pong kernel beyond) against the CPU oracle, through the C ABI: dense,
+MoE and grouped calls."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +27,10 @@ def _run(d, M, N, K):
     (1, 512, 4096), (3, 272, 384), (16, 64, 128), (32, 256, 1024), (64, 512, 512),
     (1, 64, 8192),      # 4 workgroups: K split across workgroups, then the reduction launch
     (200, 256, 640),    # ragged M
-    (300, 512, 1024),
-    (1000, 400, 512),
+    (300, 512, 1024),   # ping-pong 64 x 256, four LDS slots
+    (1000, 400, 512),   # N = 25 channel tiles: no ping-pong tile divides it, the small-M kernel
+    (600, 384, 640),    # ping-pong 128 x 128 (N % 256 != 0), 5 K steps
+    (2100, 256, 512),   # ping-pong 128 x 256, ragged last row tile
 ])
 def test_wna3_small(M, N, K):
     say(f"[wna3] M={M} N={N} K={K}")
@@ -51,7 +54,8 @@ def test_wna3_full_size_sampled(M):
 
 
 def test_wna3_every_kernel_configuration(monkeypatch):
-    """Every skinny configuration that fits; the LDS-staged kernels have no 3-bit instantiation."""
+    """Every skinny and ping-pong configuration that fits; a ping-pong tile whose LDS ring does not
+    fit is refused."""
     M, N, K = 96, 512, 768
     d = synth.make_wna3(1601, M, N, K)
     w = prepack(D, 1, N, K, d["wq"], d["scales"], d["zeros"])
@@ -68,8 +72,8 @@ def test_wna3_every_kernel_configuration(monkeypatch):
             y = gemm(D, M, N, K, to_dev(d["x"]), None, w)
             check_float(y, ref, f"wna3 kind={kind} cfg={cfg}")
             ran[kind] += 1
-    assert ran[0] >= 20 and ran[3] == 0
-    monkeypatch.setenv("HQ_TUNE", "kind=3,cfg=0,split=1")     # refused
+    assert ran[0] >= 20 and ran[3] >= 8
+    monkeypatch.setenv("HQ_TUNE", "kind=3,cfg=1,split=1")     # 256 x 128: 217 KiB of LDS, refused
     with pytest.raises(hq.HQError):
         hq.hq_gemm_plan(D, M, N, K)
 
@@ -101,8 +105,11 @@ def _stack(E, N, K, experts):
 
 
 @pytest.mark.parametrize("T,topk,E,N,K,bm", [
-    (5, 2, 4, 64, 256, 16), (64, 8, 16, 512, 1024, 16), (150, 8, 8, 512, 384, 32),
-    (400, 8, 16, 256, 768, 64),
+    (5, 2, 4, 64, 256, 16), (64, 8, 16, 512, 1024, 16),
+    (150, 8, 8, 512, 384, 32),    # ping-pong 32 x 256
+    (400, 8, 16, 256, 768, 64),   # ping-pong 64 x 256
+    (600, 8, 16, 512, 512, 64),   # ping-pong 64 x 512
+    (600, 8, 16, 512, 640, 128),  # ping-pong 128 x 256, 5 K steps
 ])
 def test_wna3_moe(T, topk, E, N, K, bm):
     inp = synth.make_moe_inputs(1700 + T, T, K, E, topk)
