@@ -183,7 +183,9 @@ def test_w2a16_descriptor():
 def test_w3a16_descriptor():
     d = hq.DESC_W3A16_ASYM
     assert hq.hq_prepacked_bytes(d, 1, 256, 512) > 0
-    assert hq.hq_gemm_plan(d, 8192, 256, 512)[0] == 0            # the skinny kernel at every M
+    assert hq.hq_gemm_plan(d, 128, 256, 512)[0] == 0             # the small-M kernel to M = 128
+    assert hq.hq_gemm_plan(d, 8192, 256, 512)[:2] == (3, 0)      # ping-pong 128 x 256 beyond
+    assert hq.hq_gemm_plan(d, 8192, 400, 512)[0] == 0            # no ping-pong tile divides N
     with pytest.raises(hq.HQError):                               # zeros missing
         hq.hq_prepack_weights(d, 1, 256, 512, np.zeros((256, 192), np.uint8), np.zeros((256, 4), np.uint16),
                               None, np.zeros(hq.hq_prepacked_bytes(d, 1, 256, 512), np.uint8))

@@ -15,7 +15,8 @@ TABLE = {
                 [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 3)), (65, (0, 4)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w2a16": (hq.DESC_W2A16_ASYM, 14336, 4096,
               [(1, (0, 31)), (4, (0, 31)), (5, (0, 28)), (128, (0, 22)), (129, (3, 13)), (512, (3, 13)), (513, (3, 0)), (8192, (3, 0))]),
-    "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096, [(1, (0, 31)), (5, (0, 28)), (32, (0, 29)), (8192, (0, 22))]),
+    "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096,
+              [(1, (0, 31)), (5, (0, 28)), (32, (0, 29)), (128, (0, 22)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w8a16": (hq.DESC_W8A16_INT8, 14336, 4096,
               [(1, (0, 33)), (4, (0, 33)), (5, (0, 27)), (32, (0, 29)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
     "f8a16": (hq.DESC_W8A16_FP8, 14336, 4096,
