@@ -237,6 +237,16 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
     }
     a_off[j] = uint32_t(src_row) * uint32_t(p.K / 128 * RB) + uint32_t(c * 16);
   }
+  // MoE: wave w copies rows [w * RPW, (w + 1) * RPW) of the block's activations. A block holds its
+  // routed rows first and its padding after them, so when the first of these rows is padding all
+  // of them are: the wave then issues no activation copies at all (lightly loaded experts' blocks
+  // move only their routed rows). Nothing reads those rows: the row blocks after the last routed
+  // row are never computed. Such a wave's stages have INSTR - A_INSTR copies each.
+  bool a_skip = false;
+  if constexpr (MOE) {
+    constexpr int RPW = Sh::A_INSTR * 64 / CPR;   // rows per wave
+    a_skip = __builtin_amdgcn_readfirstlane(p.sorted_ids[row0 + wave * RPW]) >= p.M;   // wave-uniform
+  }
   // MXFP4 activations: lane i < BM / 8 of wave w copies the step's 4 scale bytes of row
   // w * BM / 8 + i
   const uint8_t* asc_src = nullptr;
@@ -262,9 +272,11 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 
   auto issue_stage = [&](int ks) {
     uint8_t* st = smem + (ks % S) * Sh::STAGE;
+    if (!a_skip) {
 #pragma unroll
-    for (int j = 0; j < Sh::A_INSTR; ++j)
-      lds_dma16(p.a + a_off[j] + size_t(ks) * RB, st + (wave * Sh::A_INSTR + j) * 1024);
+      for (int j = 0; j < Sh::A_INSTR; ++j)
+        lds_dma16(p.a + a_off[j] + size_t(ks) * RB, st + (wave * Sh::A_INSTR + j) * 1024);
+    }
     uint8_t* sb = st + Sh::A_BYTES;
 #pragma unroll
     for (int j = 0; j < Sh::B_INSTR; ++j) {
@@ -487,13 +499,19 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 
   const int nks = p.K / 128;
   // Wait until this wave's copies of every step up to `step` have landed, given that the copies
-  // of the steps after it, up to min(step + S - 2, nks - 1), may still be in flight.
-  auto wait_step = [&](int step) __attribute__((always_inline)) {
+  // of the steps after it, up to min(step + S - 2, nks - 1), may still be in flight (I copies per
+  // stage: INSTR, or INSTR - A_INSTR for a wave that skips its activation copies).
+  auto wait_step_n = [&](int step, auto instr) __attribute__((always_inline)) {
+    constexpr int I = decltype(instr)::value;
     const int after = min(S - 2, nks - 1 - step);
-    if (after >= 3) wait_vmcnt<(S >= 5 ? 3 : 0) * Sh::INSTR>();
-    else if (after == 2) wait_vmcnt<(S >= 4 ? 2 : 0) * Sh::INSTR>();
-    else if (after == 1) wait_vmcnt<Sh::INSTR>();
+    if (after >= 3) wait_vmcnt<(S >= 5 ? 3 : 0) * I>();
+    else if (after == 2) wait_vmcnt<(S >= 4 ? 2 : 0) * I>();
+    else if (after == 1) wait_vmcnt<I>();
     else wait_vmcnt<0>();
+  };
+  auto wait_step = [&](int step) __attribute__((always_inline)) {
+    if (MOE && a_skip) wait_step_n(step, std::integral_constant<int, Sh::INSTR - Sh::A_INSTR>{});
+    else wait_step_n(step, std::integral_constant<int, Sh::INSTR>{});
   };
 
 #pragma unroll
