@@ -145,6 +145,10 @@ def _check_layer(L: Layer, stages=True):
     mx = np.abs(out - exact).max() / np.abs(exact).max()
     say(f"  layer out: rel_l2 to the exact chain {e_gpu:.3e} (oracle's bf16 chain {e_round:.3e}), "
         f"max_abs/max_ref={mx:.3e}, rel_l2 to the oracle's chain {np.linalg.norm(out - ref) / norm:.3e}")
+    # (The GPU chain is not held to the float bar against the oracle's bf16 chain itself: the
+    # gated activation is within a bound of its exact value, not correctly rounded, so many of its
+    # bf16 values sit one ulp from the oracle's, and the two chains measured up to 2.8e-3 apart --
+    # as far apart as each is from the exact chain. Every stage is held to its own bar above.)
     assert e_gpu <= 2 * e_round, f"layer out: {e_gpu:.3e} > 2 x {e_round:.3e}"
     assert mx <= 2e-2
     return got
@@ -171,8 +175,9 @@ def test_moe_layer_unrouted_entries():
 
 
 def test_moe_layer_full_size_one_token():
-    """DeepSeek-V3 expert shapes: H = 7168, I = 2048 (gate_up N = 4096), 256 experts, top-8."""
-    _check_layer(Layer(7, 1, 8, 256, 7168, 2048), stages=False)
+    """DeepSeek-V3 expert shapes: H = 7168, I = 2048 (gate_up N = 4096), 256 experts, top-8; every
+    stage against the oracle on the GPU's own input of that stage, then the layer end to end."""
+    _check_layer(Layer(7, 1, 8, 256, 7168, 2048))
 
 
 def test_silu_mul_edge_values():
