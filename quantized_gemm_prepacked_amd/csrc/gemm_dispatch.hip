@@ -201,14 +201,19 @@ constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
 // (M in (256, 512]: ping-pong 128 x 128 with four LDS slots, 57.7 vs 61.3 us with three)
 constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
-constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 2, 0}, {kInf, 2, 11}};
+// (M in (1536, 3072]: ping-pong 128 x 256 with four slots, 52.3 us at M=2048, N=4096, K=7168,
+// against 54.4 for pipelined 128 x 128; the 256 x 256 ping-pong tile 102.9)
+constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 3, 8}, {kInf, 2, 11}};
 // W4A4 and W4A8 with MXFP8 activations run on the skinny and ping-pong kernels only. W4A4,
 // measured at N=4096, K=7168: skinny 64-row blocks to M=512 (34 vs 49 us), then ping-pong
 // 128 x 128 with four LDS slots (M=768 / 1024 / 2048 / 4096: 50.7 / 51.2 / 67.3 / 121.9 us,
 // against 66.9 skinny and 60.2 / 74.1 / 135.5 with three slots), 128 x 256 with three at M=8192
 // (187 us; four or five slots: 235 / 243).
 // (M = 4096: configuration 0 82.0 us against 99.3 for 10; M = 2048: 68.2 against 55.8)
-constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {2048, 3, 10}, {kInf, 3, 0}};
+// Above M=2048: 256 x 256 tiles with waves of 64 x 128 and four slots (a quarter fewer LDS bytes
+// per MFMA), M = 4096 / 8192 at 74.6 / 147.3 us against 81.1 / 157.9 for 128 x 256; 65.8 against
+// 51.5 at M = 2048, and with three slots 90.1 / 177.7.
+constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {2048, 3, 10}, {kInf, 3, 15}};
 // W4A8-MXFP8 at the same shape: skinny to M=512 (45.5 vs 50.9 us), ping-pong 64 x 256 with four
 // slots at M=768 / 1024 (52.6 / 52.9 us; 75.3 / 70.1 with the W4A4 choices), 128 x 256 with four
 // slots from M=2048 (M=2048 / 4096 / 8192: 74.9 / 136.9 / 256.0 us, against 84.8 / 154.4 / 364.8).

@@ -602,6 +602,9 @@ static constexpr PPCfg kPP[] = {
     {4, 2, 2, 4, 4},  // 11: as 3, four slots
     {4, 4, 4, 2, 4},  // 12: as 1, four slots
     {2, 4, 2, 4, 4},  // 13: as 4, four slots
+    // 256 x 256 tiles, waves of 64 x 128 (fewer LDS bytes per MFMA; 4- and 8-bit operands only)
+    {4, 8, 4, 2, 3},  // 14: three slots
+    {4, 8, 4, 2, 4},  // 15: four slots
 };
 
 const PPCfg* pp_configs(int* count) {
@@ -643,7 +646,8 @@ static hipError_t launch_pp_one(const KParams& p, dim3 grid, int tiles_m, int ti
   using Sh = PPShape<FAM, C.mw, C.ntw, C.wm, C.wn, C.stages>;
   // (MoE instantiations exist for every format: activation scales, where there are any, are
   // gathered per routed row from its token's row)
-  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024) {
+  // (MoE blocks have at most 128 rows: no MoE instantiation of the 256-row tiles)
+  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024 && !(MOE && Sh::BM > 128)) {
     auto kern = pp_gemm_kernel<FAM, MOE, C.mw, C.ntw, C.wm, C.wn, C.stages>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);

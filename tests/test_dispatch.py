@@ -31,8 +31,8 @@ TABLE = {
                   (4096, (3, 0))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
              [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 29)), (128, (0, 29)), (129, (0, 22)),
-              (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (2, 0)), (3073, (2, 11))]),
-    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (3, 10)), (2048, (3, 10)), (2049, (3, 0))]),
+              (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (3, 8)), (3072, (3, 8)), (3073, (2, 11))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (3, 10)), (2048, (3, 10)), (2049, (3, 15))]),
     "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
 }
 

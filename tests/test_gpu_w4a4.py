@@ -31,7 +31,8 @@ def _gemm(d, M, N, K):
     (700, 384, 640),     # ping-pong 128 x 128, four LDS slots, 5 K steps
     (1000, 256, 128),    # four slots, one K step
     (900, 128, 256),     # four slots, two K steps
-    (4200, 256, 512),    # ping-pong 128 x 256, three slots, ragged M
+    (4200, 256, 512),    # ping-pong 256 x 256 (waves of 64 x 128), four slots, ragged M
+    (2300, 512, 384),    # 256 x 256, three K steps (fewer than the four slots)
     (257, 128, 256),
 ])
 def test_w4a4_small(M, N, K):
