@@ -265,6 +265,14 @@ def make_wna16(config_id: int, M: int, N: int, K: int, asym: bool, g: int = 128)
     return {"x": x, **qw}
 
 
+def periodic_rows(block: np.ndarray, M: int) -> np.ndarray:
+    """Rows 0..M-1 taken from `block` in turn (row r = block[r % len(block)]): a large activation
+    matrix from a small random one. With a block length that divides no power of two (a prime),
+    a row read at an offset wrapped by any power of two of bytes holds other values."""
+    reps = -(-M // block.shape[0])
+    return np.ascontiguousarray(np.tile(block, (reps,) + (1,) * (block.ndim - 1))[:M])
+
+
 def make_w8a8_activations(config_id: int, M: int, K: int):
     """Per-token INT8 activations quantized from bf16 N(0,1)."""
     x = bf16_bits_to_f32(normal_bf16(rng(config_id, M), (M, K)))

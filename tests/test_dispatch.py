@@ -62,3 +62,14 @@ def test_fallbacks_when_no_tile_divides_n():
         assert hq.hq_gemm_plan(desc, 4096, 400, 4096)[0] == 0
     assert hq.hq_gemm_plan(hq.DESC_W2A16_ASYM, 4096, 384, 4096)[0] == 0
     assert hq.hq_gemm_plan(hq.DESC_W8A16_INT8, 4096, 384, 4096)[0] == 3
+
+
+def test_activation_offsets_past_32_bits_leave_the_lds_kernels():
+    """The direct-to-LDS kernels address activation rows with 32-bit offsets: a call whose
+    activations reach 4 GiB runs on the LDS-tiled kernel (WNA16) or the small-M kernel (formats
+    without a tiled form), both of which address rows with 64 bits."""
+    K = 8192
+    assert hq.hq_gemm_plan(hq.DESC_W4A16_ASYM, 262143, 256, K)[0] == 3      # 4 GiB - 16 KiB of bf16
+    assert hq.hq_gemm_plan(hq.DESC_W4A16_ASYM, 262144, 256, K)[0] == 1
+    assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20 - 1, 256, K)[0] == 3  # 4-bit codes
+    assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20, 256, K)[0] == 0

@@ -86,6 +86,25 @@ def test_wna16_full_size_sampled(cfg2_weights, M):
     ref, _ = oracle.ref_wna16(x, d["wq"], d["scales"], d["zeros"], 128, rows=rows, cols=cols)
     check_float(y[np.ix_(rows, cols)], ref, f"wna16 M={M}")
 
+def test_wna16_past_32bit_activation_offsets():
+    """M x K bf16 activations past 4 GiB: the direct-to-LDS kernels address activation rows with
+    32-bit offsets, so the dispatcher moves such a call to the LDS-tiled kernel (64-bit row
+    addresses). Rows repeat with a prime period, so a row read at a wrapped offset would hold other
+    values; sampled rows on both sides of the 4 GiB mark against the oracle."""
+    M, N, K = 262144 + 300, 256, 8192
+    desc = hq.DESC_W4A16_ASYM
+    assert hq.hq_gemm_plan(desc, M, N, K)[0] == 1
+    d = synth.make_wna16(1700, 997, N, K, asym=True)
+    x = synth.periodic_rows(d["x"], M)
+    say(f"[wna16 past 4 GiB] M={M} N={N} K={K}: {x.nbytes / 2**30:.2f} GiB of activations")
+    w = prepack(desc, 1, N, K, d["wq"], d["scales"], d["zeros"])
+    y = gemm(desc, M, N, K, to_dev(x), None, w)
+    rows = np.unique(np.concatenate([[0, 262143, 262144, 262145, M - 1],
+                                     np.random.default_rng(3).integers(0, M, 40)]))
+    ref, _ = oracle.ref_wna16(x, d["wq"], d["scales"], d["zeros"], 128, rows=rows)
+    del x
+    check_float(y[rows], ref, "wna16 past 4 GiB")
+
 
 # ---- W8A8 -------------------------------------------------------------------------------------
 W8A8_SMALL = [(1, 256, 8192), (64, 512, 1024), (7, 272, 320), (16, 256, 64), (200, 512, 2048),

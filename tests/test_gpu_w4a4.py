@@ -56,6 +56,21 @@ def test_w4a4_full_size_sampled(M):
     check_float(y[np.ix_(rows, cols)], ref, f"w4a4 M={M}")
 
 
+def test_w4a4_past_32bit_activation_offsets():
+    """MXFP4 activation codes past 4 GiB: the call leaves the direct-to-LDS kernels (32-bit row
+    offsets) for the small-M kernel (64-bit row addresses); rows repeat with a prime period, so a
+    wrapped row would hold other values; sampled rows around the 4 GiB mark against the oracle."""
+    M, N, K = 2 ** 20 + 100, 128, 8192
+    assert hq.hq_gemm_plan(D, M, N, K)[0] == 0
+    d = synth.make_w4a4(1701, 997, N, K)
+    d = dict(d, xq=synth.periodic_rows(d["xq"], M), xs=synth.periodic_rows(d["xs"], M))
+    say(f"[w4a4 past 4 GiB] M={M} N={N} K={K}: {d['xq'].nbytes / 2**30:.2f} GiB of codes")
+    y = _gemm(d, M, N, K)
+    rows = np.unique(np.concatenate([[0, 2 ** 20 - 1, 2 ** 20, M - 1], np.random.default_rng(4).integers(0, M, 40)]))
+    ref, _ = oracle.ref_w4a4(d["xq"], d["xs"], d["wq"], d["scales"], rows=rows)
+    check_float(y[rows], ref, "w4a4 past 4 GiB")
+
+
 def test_w4a4_block_scale_extremes():
     """Activation and weight block scales spread over 2^-40 .. 2^40 per block (products stay in
     fp32 range): every block scale must reach its own 32 k."""
