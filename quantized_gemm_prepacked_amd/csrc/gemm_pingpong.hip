@@ -559,29 +559,33 @@ __global__ __launch_bounds__(512) void pp_gemm_kernel(KParams p, int tiles_m, in
 
 // Group sums of bf16 activation rows over 128-k groups, split into bf16 high and low halves:
 // ws[row][0][g] = hi, ws[row][1][g] = lo with hi + lo = the fp32 sum to about 16 bits; groups
-// G..Gp-1 are zero. One thread per (row, group), groups fastest.
+// G..Gp-1 are zero. One wave per (row, four groups): lane l loads 16 bytes (8 values) of group
+// 4 q + (l >> 4), the 16 lanes of a group add their partial sums in a fixed butterfly, and the
+// group's first lane writes it. One load per lane, so the pass is a single memory round trip.
 __global__ __launch_bounds__(256) void group_sums_split_kernel(const uint8_t* __restrict__ a, int rows,
                                                                int K, uint16_t* __restrict__ ws) {
   const int G = K / 128;
   const int Gp = (G + 31) / 32 * 32;
-  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= long(rows) * Gp) return;
-  const int g = int(idx % Gp);
-  const long r = idx / Gp;
+  const int per_row = Gp / 4;   // waves per row
+  const long wid = (long(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wid >= long(rows) * per_row) return;   // whole waves
+  const long r = wid / per_row;
+  const int g = int(wid % per_row) * 4 + (lane >> 4);
   float sum = 0.0f;
   if (g < G) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a + (size_t(r) * K + size_t(g) * 128) * 2);
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const u32x4 v = src[i];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a + (size_t(r) * K + size_t(g) * 128) * 2 + 16 * (lane & 15));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sum += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xFFFF0000u);
-    }
+    for (int j = 0; j < 4; ++j) sum += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xFFFF0000u);
   }
-  const uint16_t hi = f32_to_bf16_rne(sum);
-  const uint16_t lo = f32_to_bf16_rne(sum - __uint_as_float(uint32_t(hi) << 16));
-  ws[size_t(r) * 2 * Gp + g] = hi;
-  ws[size_t(r) * 2 * Gp + Gp + g] = lo;
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  if ((lane & 15) == 0) {
+    const uint16_t hi = f32_to_bf16_rne(sum);
+    const uint16_t lo = f32_to_bf16_rne(sum - __uint_as_float(uint32_t(hi) << 16));
+    ws[size_t(r) * 2 * Gp + g] = hi;
+    ws[size_t(r) * 2 * Gp + Gp + g] = lo;
+  }
 }
 
 }  // namespace
@@ -705,8 +709,8 @@ size_t group_sums_split_bytes(int64_t rows, int64_t K) {
 
 hipError_t launch_group_sums_split(const uint8_t* a, int rows, int K, void* ws, hipStream_t s) {
   const int G = K / 128;
-  const long total = long(rows) * ((G + 31) / 32 * 32);
-  hipLaunchKernelGGL(group_sums_split_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, a,
+  const long waves = long(rows) * ((G + 31) / 32 * 32 / 4);   // four waves per 256-thread block
+  hipLaunchKernelGGL(group_sums_split_kernel, dim3(unsigned((waves + 3) / 4)), dim3(256), 0, s, a,
                      rows, K, static_cast<uint16_t*>(ws));
   return hipGetLastError();
 }
