@@ -103,6 +103,7 @@ MOE_CASES = [
     (400, 8, 16, 1024, 768, 64, True),    # ping-pong 64 x 512 (W4A8) / 64 x 256 (W8A8)
     (600, 8, 16, 512, 512, 128, True),    # 128-row blocks: ping-pong 128 x 256
     (300, 8, 64, 256, 640, 128, False),   # 128-row blocks, mostly padding, K/128 = 5
+    (300, 8, 64, 384, 640, 128, False),   # 128-row blocks on 128 x 128 tiles (N % 256 != 0)
 ]
 
 
