@@ -164,6 +164,7 @@ def _moe(fp8, T, topk, E, N, K, bm, seed, tw=True, random_codes=False, cols=None
 @pytest.mark.parametrize("T,topk,E,N,K,bm", [
     (5, 2, 4, 64, 256, 16), (64, 8, 16, 512, 1024, 16), (150, 8, 8, 512, 384, 32),
     (400, 8, 16, 1024, 768, 64), (200, 8, 32, 272, 384, 64), (600, 8, 16, 512, 512, 128),
+    (300, 8, 64, 384, 640, 128),   # 128-row blocks on 128 x 128 tiles
 ])
 def test_w8a16_moe(fp8, T, topk, E, N, K, bm):
     _moe(fp8, T, topk, E, N, K, bm, 1400 + T)
