@@ -30,12 +30,18 @@ int k_unit(const Combo& c) {
   return (c.fam == FAM_FP8B || c.fam == FAM_W8A16 || c.fam == FAM_F8A16) ? 128 : family_k_unit(c.fam);
 }
 
-// Families that run on the skinny and ping-pong kernels only (no LDS-tiled or pipelined
-// instantiation).
+// Families with no LDS-tiled instantiation: the skinny and ping-pong kernels (and, for
+// block-scaled FP8, the pipelined one) cover every shape they take.
 bool pp_only(const Combo& c) {
   return c.fam == FAM_W4A4 || c.fam == FAM_W4A8MX || c.fam == FAM_MXW4A16 || c.fam == FAM_FP8B ||
          c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_WNA2 || c.fam == FAM_WNA3;
 }
+
+// Families with a pipelined-kernel instantiation, dense and MoE.
+bool has_pipe(const Combo& c) {
+  return c.fam == FAM_WNA16 || c.fam == FAM_W8A8 || c.fam == FAM_W4A8 || c.fam == FAM_FP8B;
+}
+bool has_pipe_moe(const Combo& c) { return c.fam == FAM_WNA16 || c.fam == FAM_FP8B; }
 
 // Activation bytes per 2 k (bf16: 4; 8-bit: 2; 4-bit: 1): the direct-to-LDS kernels address
 // activation rows with 32-bit offsets, so M * K * this / 2 must stay below 2^32.
@@ -221,13 +227,16 @@ constexpr RangeEntry kW4a8mxTable[] = {{576, 0, 0}, {1536, 3, 13}, {kInf, 3, 8}}
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
 // (M = 128, N=14336 K=4096: the small-M kernel 25.7 us against 35.0 for ping-pong 128 x 128)
 constexpr RangeEntry kMxW4a16Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
-// Block-scaled FP8 W8A8: skinny and ping-pong only (measured at N=K=8192: skinny to M=64, then
-// ping-pong 128 x 128 with four LDS slots: M=128 / 512 / 1024 / 2048 / 4096 at 66.3 / 75.4 / 138.0
-// / 272.9 / 517.0 us, against 91.7 / 101.6 / 194.0 / 304.2 / 610.4 for the three-slot 64 x 256 and
-// 256 x 128 tiles)
-// (M = 128 / 256, N=K=8192: the small-M kernel 34.1 / 53.5 us against 58.4 / 57.4 for ping-pong)
-// (M = 4096: ping-pong configuration 0 412.6 us against 426.5 for 10; M = 2048: 236.4 against 231.1)
-constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {2048, 3, 10}, {kInf, 3, 0}};
+// Block-scaled FP8 W8A8, measured at N=K=8192: the small-M kernel to M=256 (M = 128 / 256: 34.1 /
+// 53.5 us against 58.4 / 57.4 for ping-pong), ping-pong 128 x 128 with four LDS slots at M=512
+// (56.5 us; pipelined 128 x 256 86.9), then the pipelined kernel, whose eight waves compute
+// together so that one wave's per-step scaling runs beside the other's MFMAs (ping-pong at
+// M = 768 / 1024 / 2048 / 4096: 106.2 / 107.9 / 214.9 / 408.9 us). Its two tiles alternate with
+// how evenly they fill the 256 CUs: 128 x 256 (waves of 32 x 128) at M = 768 / 1024 / 3072
+// (88.4 / 94.1 / 253.8 us; 256 x 256: 146.4 at 1024, 293.4 at 3072), 256 x 256 (waves of
+// 64 x 128) at M = 1536 / 2048 / 4096 (149.9 / 153.6 / 303.2 us; 128 x 256: 162.7 / 169.4 / 338.8).
+constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {640, 3, 10}, {1280, 2, 14}, {2048, 2, 11},
+                                     {3072, 2, 14}, {kInf, 2, 11}};
 // INT8 / FP8 weights with bf16 activations (the 128 x 256 tiles' three-slot ring of 64 KiB steps
 // exceeds the LDS). Measured at N=14336, K=4096 (INT8 / FP8): skinny 64-row blocks to M=128
 // (34.5 / 32.5 us; ping-pong 41.7 / 32.1), then ping-pong 128 x 128 with waves of 64 x 32:
@@ -330,7 +339,7 @@ bool override_fits(const Combo& c, const TuneOverride& o, int64_t M, int64_t N, 
                          skinny_lds_bytes(c.fam, o.cfg) <= 160 * 1024 &&
                          (!cfgs[o.cfg].few || M <= kFewRows));
   }
-  if (pp_only(c) && (o.kind == 1 || o.kind == 2)) return false;
+  if ((o.kind == 1 && pp_only(c)) || (o.kind == 2 && !has_pipe(c))) return false;
   if (o.kind == 1) {
     const TiledCfg* cfgs = tiled_configs(&n);
     return pick_tiled(c, N, K) >= 0 && o.cfg >= 0 && o.cfg < n && N % (16 * cfgs[o.cfg].ntw * cfgs[o.cfg].wn) == 0;
@@ -477,8 +486,9 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
     pl.cfg = invariant_skinny_cfg(c, N);
     return pl;
   }
-  // Sweep overrides (HQ_TUNE="kind=3,cfg=<i>" or "kind=0,cfg=<i>"): a ping-pong or skinny
-  // configuration whose tile rows equal block_m; one that does not fit is refused (kind -1).
+  // Sweep overrides (HQ_TUNE="kind=3,cfg=<i>", "kind=2,cfg=<i>" or "kind=0,cfg=<i>"): a
+  // ping-pong, pipelined (WNA16 and block-scaled FP8) or skinny configuration whose tile rows
+  // equal block_m; one that does not fit is refused (kind -1).
   const TuneOverride tov = tune_override();
   if (tov.kind == 0) {
     int n_s = 0;
@@ -487,6 +497,19 @@ Plan plan_moe(const Combo& c, int64_t T, int32_t, int32_t, int64_t N, int64_t K,
                       (N / 16) % sc[tov.cfg].ntw == 0 && skinny_lds_bytes(c.fam, tov.cfg) <= 160 * 1024;
     pl.kind = fits ? 0 : -1;
     pl.cfg = tov.cfg;
+    return pl;
+  }
+  if (tov.kind == 2) {
+    int n_p = 0;
+    const PipeCfg* pc = pipe_configs(&n_p);
+    const bool fits = has_pipe_moe(c) && tov.cfg >= 0 && tov.cfg < n_p &&
+                      16 * pc[tov.cfg].mw * pc[tov.cfg].wm == block_m && K % 128 == 0 &&
+                      N % (16 * pc[tov.cfg].ntw * pc[tov.cfg].wn) == 0 &&
+                      pipe_lds_bytes(c.fam, tov.cfg) <= 160 * 1024 &&
+                      uint64_t(T) * uint64_t(K) * act_bytes_2k(c) / 2 < (uint64_t(1) << 32);
+    pl.kind = fits ? 2 : -1;
+    pl.cfg = tov.cfg;
+    pl.ws_bytes = family_int_groups(c.fam) ? group_sums_split_bytes(T, K) : 0;
     return pl;
   }
   if (tov.kind == 3) {

@@ -43,6 +43,11 @@ struct PipeTraits<FAM_W4A8> {
   static constexpr int kABytes = 1;
   static constexpr int kUnitsPerStep = 1;
 };
+template <>
+struct PipeTraits<FAM_FP8B> {
+  static constexpr int kABytes = 1;
+  static constexpr int kUnitsPerStep = 2;
+};
 
 __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_s_barrier();
@@ -61,19 +66,30 @@ struct PipeShape {
   static constexpr int NT = BN / 16;               // channel tiles per workgroup
   static constexpr int UPS = PipeTraits<FAM>::kUnitsPerStep;
   static constexpr int B_BYTES = NT * UPS * kUnitBytes;
-  static constexpr int SC_BYTES = FAM == FAM_WNA16 ? NT * 32 : (FAM == FAM_W4A8 ? NT * 64 : 0);
+  // weight scales per tile and step: WNA16 16 bf16 group scales, W4A8 64 e8m0 block scales,
+  // block-scaled FP8 the 128 x 128 block's fp32 scale four times
+  static constexpr int SC_BYTES =
+      FAM == FAM_WNA16 ? NT * 32 : (FAM == FAM_W4A8 ? NT * 64 : (FAM == FAM_FP8B ? NT * 16 : 0));
   static constexpr int Z_BYTES = FAM == FAM_WNA16 ? NT * 8 : 0;
-  static constexpr int META_BYTES = (SC_BYTES || Z_BYTES) ? 2048 : 0;  // scales @0, zeros @1024
+  // block-scaled FP8: the fp32 activation scale of each row's 128-k block
+  static constexpr int ASC_BYTES = FAM == FAM_FP8B ? BM * 4 : 0;
+  static constexpr int ASC_ROWS = ASC_BYTES ? BM / kWaves : 0;   // rows whose scales a wave copies
+  // scales @0, zeros or activation scales @1024
+  static constexpr int META_BYTES = (SC_BYTES || Z_BYTES || ASC_BYTES) ? 2048 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + META_BYTES;
   static constexpr int LDS = STAGES * STAGE;
   // wave-wide 16-byte loads per stage, per wave
   static constexpr int A_INSTR = A_BYTES / 1024 / kWaves;
   static constexpr int B_INSTR = (NT * UPS) / kWaves;
-  static constexpr int META_INSTR = (SC_BYTES ? 1 : 0) + (Z_BYTES ? 1 : 0);
+  static constexpr int META_INSTR = (SC_BYTES ? 1 : 0) + (Z_BYTES ? 1 : 0) + (ASC_BYTES ? 1 : 0);
   static constexpr int INSTR = A_INSTR + B_INSTR + META_INSTR;
   static_assert(A_BYTES % (1024 * kWaves) == 0, "activation tile must split into wave loads");
   static_assert((NT * UPS) % kWaves == 0, "weight units must split over the waves");
   static_assert(SC_BYTES <= 1024 && Z_BYTES <= 256, "metadata fits one masked load");
+  static_assert(ASC_BYTES <= 1024 && (ASC_BYTES == 0 || (BM % kWaves == 0 && ASC_ROWS <= 64)),
+                "activation scales: one masked load per wave");
+  // block-scaled FP8: a wave's NTW tiles lie in one 128-channel scale block
+  static_assert(FAM != FAM_FP8B || 8 % NTW == 0, "a wave's tiles share one weight scale block");
 };
 
 template <int FAM, int MW, int NTW, int WM, int WN, int STAGES, bool MOE>
@@ -133,6 +149,21 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
     }
     a_off[j] = uint32_t(src_row) * uint32_t(p.K * Sh::AB) + uint32_t(c * 16);
   }
+  // Block-scaled FP8: lane i < ASC_ROWS of wave w copies the step's fp32 scale of row
+  // w * ASC_ROWS + i (MoE: of the row's token; rows past M and padding rows read a valid row's
+  // and are never stored).
+  const uint8_t* asc_src = nullptr;
+  if constexpr (Sh::ASC_BYTES > 0) {
+    const int r = wave * Sh::ASC_ROWS + min(lane, Sh::ASC_ROWS - 1);
+    int src_row;
+    if constexpr (MOE) {
+      const int id = p.sorted_ids[row0 + r];
+      src_row = id < p.M ? id / p.topk : 0;
+    } else {
+      src_row = min(row0 + r, p.M - 1);
+    }
+    asc_src = reinterpret_cast<const uint8_t*>(p.a_scale) + size_t(src_row) * (p.K / 32);
+  }
 
   auto issue_stage = [&](int ks) {
     uint8_t* st = smem + (ks % STAGES) * Sh::STAGE;
@@ -162,6 +193,12 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
       const int t = lane >> 2;
       const size_t unit = size_t(nt_wg + min(t, NT - 1)) * p.k_units + ks;
       if (lane < 4 * NT) lds_dma16(w + p.scales_off + unit * 64 + 16 * (lane & 3), sm);
+    } else if constexpr (FAM == FAM_FP8B) {
+      // weight scales: lane t < NT copies tile t's 16-byte granule of the step (two 64-k units
+      // per step, one granule per step); activation scales: this wave's rows
+      const size_t unit = size_t(nt_wg + min(lane, NT - 1)) * (p.k_units / UPS) + ks;
+      if (lane < NT) lds_dma16(w + p.scales_off + unit * 16, sm);
+      if (lane < Sh::ASC_ROWS) lds_dma4(asc_src + 4 * ks, sm + 1024 + wave * Sh::ASC_ROWS * 4);
     }
   };
 
@@ -235,6 +272,31 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
           for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_i8(af[mb], bq, acc[mb][t]);
         }
       }
+    } else if constexpr (FAM == FAM_FP8B) {
+      // One 128-k step is one scale block: each tile's fp8 partial of the step, times (row
+      // scale x the wave's weight block scale), is added to the tile in fp32. The row scale is
+      // per output row (rows 4 (lane >> 4) + i of each 16-row block).
+      const float* sa = reinterpret_cast<const float*>(sm + 1024);
+      const float sw = *reinterpret_cast<const float*>(sm + wn * NTW * 16);
+      u32x4 alo[MW], ahi[MW];
+      float c[MW][4];
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        alo[mb] = read_a(st, mb, lane >> 4);
+        ahi[mb] = read_a(st, mb, 4 + (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[mb][i] = sa[wm * 16 * MW + 16 * mb + 4 * (lane >> 4) + i] * sw;
+      }
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const u32x4 b0 = read_b(st, t, 0), b1 = read_b(st, t, 1);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) {
+          const f32x4 part = mfma_fp8_fp8(alo[mb], ahi[mb], b0, b1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[i] * c[mb][i];
+        }
+      }
     } else {
       u32x4 alo[MW], ahi[MW];
 #pragma unroll
@@ -273,6 +335,9 @@ static constexpr PipeCfg kPipe[] = {
     {8, 4, 2, 4, 3},  // 9: as 8, 3 stages (fp4 weights)
     {4, 4, 4, 2, 3},  // 10: as 7, 3 stages (8-bit activations)
     {4, 8, 4, 2, 2},  // 11: 256 x 256, 8 waves of 64 x 128
+    {4, 4, 2, 4, 2},  // 12: 128 x 256, 8 waves of 64 x 64, 2 stages
+    {4, 4, 2, 4, 3},  // 13: as 12, 3 stages
+    {2, 8, 4, 2, 3},  // 14: 128 x 256, 8 waves of 32 x 128, 3 stages
 };
 
 const PipeCfg* pipe_configs(int* count) {
@@ -298,7 +363,8 @@ int pipe_lds_bytes(int fam, int cfg) {
   if (fam == FAM_WNA16) return pipe_lds_table<FAM_WNA16>(cfg, seq);
   if (fam == FAM_W8A8) return pipe_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A8) return pipe_lds_table<FAM_W4A8>(cfg, seq);
-  return 1 << 30;   // no W4A4 instantiation
+  if (fam == FAM_FP8B) return pipe_lds_table<FAM_FP8B>(cfg, seq);
+  return 1 << 30;   // no instantiation for the other families
 }
 
 template <int FAM, bool MOE, int I>
@@ -331,9 +397,11 @@ hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, 
   auto seq = std::make_integer_sequence<int, n>{};
   if (fam == FAM_WNA16) return moe ? launch_pipe_fam<FAM_WNA16, true>(p, cfg, grid, tiles_m, tiles_n, s, seq)
                                    : launch_pipe_fam<FAM_WNA16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_FP8B && moe) return launch_pipe_fam<FAM_FP8B, true>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (moe) return hipErrorInvalidValue;
   if (fam == FAM_W8A8) return launch_pipe_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A8) return launch_pipe_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_FP8B) return launch_pipe_fam<FAM_FP8B, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return hipErrorInvalidValue;
 }
 

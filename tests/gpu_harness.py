@@ -91,3 +91,23 @@ def check_ulp(y_bits: np.ndarray, ref_bits: np.ndarray, what: str, max_ulp: int 
     d = np.abs(bf16_ordered(y_bits.view(np.uint16)) - bf16_ordered(ref_bits))
     say(f"  {what}: max ulp {d.max()}, exact {np.mean(d == 0) * 100:.2f}%")
     assert d.max() <= max_ulp, f"{what}: bf16 differs by {d.max()} ulp"
+
+
+def every_configuration(desc, M, N, K, run, check, monkeypatch):
+    """Run every configuration of every kernel kind that fits the shape (the tuning table may
+    name any of them) and check each output; returns {kind: configurations run}."""
+    ran = {}
+    for kind in (0, 1, 2, 3):
+        for cfg in range(hq.hq_kernel_config_count(kind)):
+            monkeypatch.setenv("HQ_TUNE", f"kind={kind},cfg={cfg},split=1")
+            try:
+                plan = hq.hq_gemm_plan(desc, M, N, K)
+            except hq.HQError:
+                continue            # the configuration does not fit this shape
+            assert plan[:2] == (kind, cfg), f"forced kind={kind} cfg={cfg}, planned {plan}"
+            say(f"[every configuration] kind={kind} cfg={cfg} plan={plan}")
+            check(run(), f"kind={kind} cfg={cfg}")
+            ran[kind] = ran.get(kind, 0) + 1
+    monkeypatch.delenv("HQ_TUNE")
+    say(f"[every configuration] configurations run per kind: {ran}")
+    return ran

@@ -27,8 +27,9 @@ TABLE = {
               (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
     "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192,
                  [(1, (0, 21)), (4, (0, 21)), (5, (0, 20)), (16, (0, 20)), (32, (0, 23)), (64, (0, 29)),
-                  (65, (0, 4)), (256, (0, 4)), (257, (3, 10)), (2048, (3, 10)), (2049, (3, 0)),
-                  (4096, (3, 0))]),
+                  (65, (0, 4)), (256, (0, 4)), (257, (3, 10)), (640, (3, 10)), (641, (2, 14)),
+                  (1280, (2, 14)), (1281, (2, 11)), (2048, (2, 11)), (2049, (2, 14)), (3072, (2, 14)),
+                  (3073, (2, 11)), (8192, (2, 11))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
              [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 29)), (128, (0, 29)), (129, (0, 22)),
               (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (3, 8)), (3072, (3, 8)), (3073, (2, 11))]),

@@ -8,7 +8,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, gemm, prepack, say, to_dev
+from gpu_harness import DEV, check_float, every_configuration, gemm, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -24,12 +24,16 @@ def _gemm(d, M, N, K):
     (1, 512, 7168), (3, 384, 384), (16, 128, 128), (32, 256, 1024), (64, 512, 512),
     (300, 256, 640),     # ping-pong, ragged M, 5 K steps
     (1000, 384, 512),    # N not a multiple of 256
-    (700, 512, 1024),
+    (700, 512, 1024),    # ping-pong 128 x 128, four LDS slots
+    (1100, 512, 640),    # pipelined 128 x 256 (waves of 32 x 128), ragged M, 5 K steps
+    (1000, 256, 128),    # pipelined 128 x 256, one K step (fewer than the three stages)
+    (2600, 256, 256),    # pipelined 128 x 256 between 2048 and 3072 rows, ragged M
     (300, 256, 128),     # ping-pong 128 x 128 with four LDS slots, one K step
     (480, 128, 256),     # ping-pong, four slots, two K steps
     (200, 256, 128),     # small-M kernel (M <= 256), one K step
     (150, 128, 256),     # small-M kernel, two K steps
-    (2100, 256, 256),    # above 2048 rows: ping-pong 128 x 256, three slots, ragged last tile
+    (2100, 256, 256),    # pipelined 256 x 256 (two stages), two K steps, ragged last tile
+    (3000, 512, 384),    # pipelined 256 x 256, three K steps
 ])
 def test_fp8block_small(M, N, K):
     say(f"[fp8block] M={M} N={N} K={K}")
@@ -39,7 +43,17 @@ def test_fp8block_small(M, N, K):
     check_float(y, ref, "fp8block")
 
 
-@pytest.mark.parametrize("M", [1, 512, 4096])
+def test_fp8block_every_kernel_configuration(monkeypatch):
+    """Ragged M over 256 rows, N = 512, six K steps, in every configuration that fits."""
+    M, N, K = 600, 512, 768
+    d = synth.make_w8a8_fp8_block(1308, M, N, K)
+    ref, _ = oracle.ref_w8a8_fp8_block(d["xq"], d["xs"], d["wq"], d["ws"])
+    ran = every_configuration(D, M, N, K, lambda: _gemm(d, M, N, K),
+                              lambda y, what: check_float(y, ref, f"fp8block {what}"), monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 2, 3))
+
+
+@pytest.mark.parametrize("M", [1, 512, 1024, 4096])
 def test_fp8block_full_size_sampled(M):
     N = K = 8192
     say(f"[fp8block full] M={M}")

@@ -12,7 +12,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import check_float, check_ulp, gemm, prepack, say, to_dev
+from gpu_harness import check_float, check_ulp, every_configuration, gemm, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +55,20 @@ def test_wna16_small(M, N, K, asym):
     y = gemm(desc, M, N, K, to_dev(d["x"]), None, w)
     ref, _ = oracle.ref_wna16(d["x"], d["wq"], d["scales"], d.get("zeros"), 128)
     check_float(y, ref, "wna16")
+
+
+@pytest.mark.parametrize("asym", [True, False])
+def test_wna16_every_kernel_configuration(asym, monkeypatch):
+    """INT4 W4A16 at a ragged M over 256 rows, N = 512, six groups, in every configuration."""
+    M, N, K = 600, 512, 768
+    d = synth.make_wna16(1304 + asym, M, N, K, asym=asym)
+    desc = hq.DESC_W4A16_ASYM if asym else hq.DESC_W4A16_SYM
+    w = prepack(desc, 1, N, K, d["wq"], d["scales"], d.get("zeros"))
+    x = to_dev(d["x"])
+    ref, _ = oracle.ref_wna16(d["x"], d["wq"], d["scales"], d.get("zeros"), 128)
+    ran = every_configuration(desc, M, N, K, lambda: gemm(desc, M, N, K, x, None, w),
+                              lambda y, what: check_float(y, ref, f"wna16 asym={asym} {what}"), monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 1, 2, 3))
 
 
 def test_wna16_deterministic():
@@ -146,6 +160,24 @@ def test_w8a8_full_size_sampled(M):
     check_ulp(y[np.ix_(rows, cols)], ref_bits, f"w8a8 M={M}")
 
 
+def test_w8a8_every_kernel_configuration(monkeypatch):
+    """W8A8 at a ragged M over 256 rows, N = 512, six K steps: int32 accumulator bit-exact in
+    every configuration."""
+    M, N, K = 600, 512, 768
+    d = synth.make_w8a8(1302, M, N, K)
+    w = prepack(hq.DESC_W8A8, 1, N, K, d["wq"], d["s_ch"])
+    xq, st = to_dev(d["xq"]), to_dev(d["s_tok"])
+    ref_acc, _, _ = oracle.ref_w8a8(d["xq"], d["s_tok"], d["wq"], d["s_ch"])
+
+    def check(acc, what):
+        assert np.array_equal(acc.astype(np.int64), ref_acc), f"w8a8 {what}: accumulator not bit-exact"
+
+    ran = every_configuration(hq.DESC_W8A8_I32, M, N, K,
+                               lambda: gemm(hq.DESC_W8A8_I32, M, N, K, xq, st, w, out_dtype=torch.int32),
+                               check, monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 1, 2, 3))
+
+
 # ---- W4A8-MXFP4 -------------------------------------------------------------------------------
 W4A8_SMALL = [(1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024),
               (600, 256, 1024),    # skinny, four 16-row blocks per workgroup
@@ -168,6 +200,19 @@ def test_w4a8_small(M, N, K):
     y = gemm(hq.DESC_W4A8_MXFP4, M, N, K, to_dev(d["xq"]), to_dev(d["s_tok"]), w)
     ref, _ = oracle.ref_w4a8(d["xq"], d["s_tok"], d["wq"], d["scales"])
     check_float(y, ref, "w4a8")
+
+
+def test_w4a8_every_kernel_configuration(monkeypatch):
+    """W4A8-MXFP4 at a ragged M over 256 rows, N = 512, six K steps, in every configuration."""
+    M, N, K = 600, 512, 768
+    d = synth.make_w4a8(1303, M, N, K)
+    w = prepack(hq.DESC_W4A8_MXFP4, 1, N, K, d["wq"], d["scales"])
+    xq, st = to_dev(d["xq"]), to_dev(d["s_tok"])
+    ref, _ = oracle.ref_w4a8(d["xq"], d["s_tok"], d["wq"], d["scales"])
+    ran = every_configuration(hq.DESC_W4A8_MXFP4, M, N, K,
+                               lambda: gemm(hq.DESC_W4A8_MXFP4, M, N, K, xq, st, w),
+                               lambda y, what: check_float(y, ref, f"w4a8 {what}"), monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 1, 2, 3))
 
 
 @pytest.mark.parametrize("M", [1, 32, 64, 128, 256, 2048, 8192])

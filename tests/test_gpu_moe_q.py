@@ -115,6 +115,27 @@ def test_moe_q_small(fmt, T, topk, E, N, K, bm, tw):
     _moe(fmt, T, topk, E, N, K, bm, tw, 600 + T)
 
 
+@pytest.mark.parametrize("T,topk,E,N,K,bm,tw", [
+    (600, 8, 16, 512, 512, 128, True),     # 128-row blocks: 128 x 256 / 128 x 128 tiles
+    (300, 8, 64, 256, 640, 128, False),    # 128-row blocks, mostly padding, K/128 = 5
+    (400, 8, 16, 512, 768, 64, True),      # 64-row blocks: 64 x 128 / 64 x 64 tiles
+])
+def test_moe_fp8b_pipelined_configurations(T, topk, E, N, K, bm, tw, monkeypatch):
+    """Block-scaled FP8 experts on every pipelined configuration whose tile rows equal the block
+    size (the tuning override may name any of them); the others are refused before any launch."""
+    ran = 0
+    for cfg in range(hq.hq_kernel_config_count(2)):
+        monkeypatch.setenv("HQ_TUNE", f"kind=2,cfg={cfg},split=1")
+        try:
+            _moe("fp8b", T, topk, E, N, K, bm, tw, 900 + T)
+        except hq.HQError as e:
+            assert e.status == hq.HQ_ERR_UNSUPPORTED, str(e)
+            continue
+        ran += 1
+    monkeypatch.delenv("HQ_TUNE")
+    assert ran >= 2
+
+
 @pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("T", [8, 128, 1024])
 def test_moe_q_full_size_sampled(fmt, T):

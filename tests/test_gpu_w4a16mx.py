@@ -8,7 +8,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, gemm, prepack, say, to_dev
+from gpu_harness import DEV, check_float, every_configuration, gemm, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,18 @@ def test_w4a16mx_small(M, N, K):
     y = gemm(D, M, N, K, to_dev(d["x"]), None, w)
     ref, _ = oracle.ref_w4a16_mx(d["x"], d["wq"], d["scales"])
     check_float(y, ref, "w4a16mx")
+
+
+def test_w4a16mx_every_kernel_configuration(monkeypatch):
+    """Ragged M over 256 rows, N = 512, six K steps, in every configuration that fits."""
+    M, N, K = 600, 512, 768
+    d = synth.make_w4a16mx(1309, M, N, K)
+    w = prepack(D, 1, N, K, d["wq"], d["scales"])
+    x = to_dev(d["x"])
+    ref, _ = oracle.ref_w4a16_mx(d["x"], d["wq"], d["scales"])
+    ran = every_configuration(D, M, N, K, lambda: gemm(D, M, N, K, x, None, w),
+                              lambda y, what: check_float(y, ref, f"w4a16mx {what}"), monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 3))
 
 
 @pytest.mark.parametrize("M", [1, 128, 8192])

@@ -8,7 +8,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, gemm, prepack, say, to_dev
+from gpu_harness import DEV, check_float, every_configuration, gemm, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,16 @@ def test_w4a4_small(M, N, K):
     y = _gemm(d, M, N, K)
     ref, _ = oracle.ref_w4a4(d["xq"], d["xs"], d["wq"], d["scales"])
     check_float(y, ref, "w4a4")
+
+
+def test_w4a4_every_kernel_configuration(monkeypatch):
+    """Ragged M over 256 rows, N = 512, six K steps, in every configuration that fits."""
+    M, N, K = 600, 512, 768
+    d = synth.make_w4a4(1306, M, N, K)
+    ref, _ = oracle.ref_w4a4(d["xq"], d["xs"], d["wq"], d["scales"])
+    ran = every_configuration(D, M, N, K, lambda: _gemm(d, M, N, K),
+                              lambda y, what: check_float(y, ref, f"w4a4 {what}"), monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 3))
 
 
 @pytest.mark.parametrize("M", [1, 32, 256, 2048, 8192])
