@@ -39,7 +39,8 @@ bool pp_only(const Combo& c) {
 
 // Families with a pipelined-kernel instantiation, dense and MoE.
 bool has_pipe(const Combo& c) {
-  return c.fam == FAM_WNA16 || c.fam == FAM_W8A8 || c.fam == FAM_W4A8 || c.fam == FAM_FP8B;
+  return c.fam == FAM_WNA16 || c.fam == FAM_W8A8 || c.fam == FAM_W4A8 || c.fam == FAM_FP8B ||
+         c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_MXW4A16;
 }
 bool has_pipe_moe(const Combo& c) { return c.fam == FAM_WNA16 || c.fam == FAM_FP8B; }
 
@@ -237,12 +238,15 @@ constexpr RangeEntry kMxW4a16Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
 // 64 x 128) at M = 1536 / 2048 / 4096 (149.9 / 153.6 / 303.2 us; 128 x 256: 162.7 / 169.4 / 338.8).
 constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {640, 3, 10}, {1280, 2, 14}, {2048, 2, 11},
                                      {3072, 2, 14}, {kInf, 2, 11}};
-// INT8 / FP8 weights with bf16 activations (the 128 x 256 tiles' three-slot ring of 64 KiB steps
-// exceeds the LDS). Measured at N=14336, K=4096 (INT8 / FP8): skinny 64-row blocks to M=128
-// (34.5 / 32.5 us; ping-pong 41.7 / 32.1), then ping-pong 128 x 128 with waves of 64 x 32:
-// M=256 / 1024 / 8192 at 45.7 / 171.7 / 1161 us and 40.4 / 155.0 / 1067 us, against 55.2 / 210.9
-// / 1364 and 41.9 / 158.9 / 1133 for waves of 32 x 64.
-constexpr RangeEntry kW8a16Table[] = {{128, 0, 0}, {kInf, 3, 3}};
+// INT8 / FP8 weights with bf16 activations, measured at N=14336, K=4096 (INT8 / FP8): skinny
+// 64-row blocks to M=128 (34.5 / 32.5 us; ping-pong 41.7 / 32.1), ping-pong 128 x 128 with waves
+// of 64 x 32 at M=256 (38.3 / 35.0 us; the ping-pong 128 x 256 tile's three-slot ring of 64 KiB
+// steps exceeds the LDS), then the pipelined 128 x 256 tile with eight waves of 64 x 64 and two
+// stages (the dequantization of one wave issues beside the other's MFMAs): M = 384 / 512 / 1024 /
+// 8192 at 66.7 / 67.6 / 130.3 / 934.9 and 58.0 / 57.7 / 112.1 / 816.0 us, against 73.6 / 74.8 /
+// 145.7 / 1038.9 and 67.6 / 69.4 / 132.2 / 961.5 for ping-pong 128 x 128 — except around M = 768,
+// where its 336 tiles fill the CUs unevenly (127.9 / 109.5 us against 112.0 / 102.2).
+constexpr RangeEntry kW8a16Table[] = {{128, 0, 0}, {256, 3, 3}, {640, 2, 12}, {896, 3, 3}, {kInf, 2, 12}};
 // 2-bit WnA16 on the ping-pong kernel's 256-wide tiles (the only ones whose half-unit weight copies
 // split over the eight waves), measured at N=14336, K=4096: skinny to M=128 (36.8 us; ping-pong
 // 52.1), 64 x 256 with four slots to 512 (M=256: 49.5 us against 53.1 with three), 128 x 256

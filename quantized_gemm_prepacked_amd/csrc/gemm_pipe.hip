@@ -48,6 +48,21 @@ struct PipeTraits<FAM_FP8B> {
   static constexpr int kABytes = 1;
   static constexpr int kUnitsPerStep = 2;
 };
+template <>
+struct PipeTraits<FAM_MXW4A16> {
+  static constexpr int kABytes = 2;
+  static constexpr int kUnitsPerStep = 1;
+};
+template <>
+struct PipeTraits<FAM_W8A16> {
+  static constexpr int kABytes = 2;
+  static constexpr int kUnitsPerStep = 2;
+};
+template <>
+struct PipeTraits<FAM_F8A16> {
+  static constexpr int kABytes = 2;
+  static constexpr int kUnitsPerStep = 2;
+};
 
 __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_s_barrier();
@@ -66,10 +81,11 @@ struct PipeShape {
   static constexpr int NT = BN / 16;               // channel tiles per workgroup
   static constexpr int UPS = PipeTraits<FAM>::kUnitsPerStep;
   static constexpr int B_BYTES = NT * UPS * kUnitBytes;
-  // weight scales per tile and step: WNA16 16 bf16 group scales, W4A8 64 e8m0 block scales,
-  // block-scaled FP8 the 128 x 128 block's fp32 scale four times
+  // weight scales per tile and step: WNA16 16 bf16 group scales, MXFP4 weights (W4A8,
+  // W4A16-MXFP4) 64 e8m0 block scales, block-scaled FP8 the 128 x 128 block's fp32 scale four times
   static constexpr int SC_BYTES =
-      FAM == FAM_WNA16 ? NT * 32 : (FAM == FAM_W4A8 ? NT * 64 : (FAM == FAM_FP8B ? NT * 16 : 0));
+      FAM == FAM_WNA16 ? NT * 32
+                       : ((FAM == FAM_W4A8 || FAM == FAM_MXW4A16) ? NT * 64 : (FAM == FAM_FP8B ? NT * 16 : 0));
   static constexpr int Z_BYTES = FAM == FAM_WNA16 ? NT * 8 : 0;
   // block-scaled FP8: the fp32 activation scale of each row's 128-k block
   static constexpr int ASC_BYTES = FAM == FAM_FP8B ? BM * 4 : 0;
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
       const uint8_t* zsrc = p.asym ? w + p.zeros_off + unit * 8 + 4 * (lane & 1)
                                    : w + p.scales_off + unit * 32;   // unused for symmetric weights
       if (lane < 2 * NT) lds_dma4(zsrc, sm + 1024);
-    } else if constexpr (FAM == FAM_W4A8) {
+    } else if constexpr (FAM == FAM_W4A8 || FAM == FAM_MXW4A16) {
       const int t = lane >> 2;
       const size_t unit = size_t(nt_wg + min(t, NT - 1)) * p.k_units + ks;
       if (lane < 4 * NT) lds_dma16(w + p.scales_off + unit * 64 + 16 * (lane & 3), sm);
@@ -270,6 +286,45 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
           const u32x4 bq = read_b(st, t, q);
 #pragma unroll
           for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_i8(af[mb], bq, acc[mb][t]);
+        }
+      }
+    } else if constexpr (FAM == FAM_MXW4A16) {
+      // the lane's 32 weights of a tile share k block (lane >> 4): its e8m0 scale is folded into
+      // the conversion to bf16, and the MFMAs accumulate straight into the tile
+      bf16x8 af[MW][4];
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          af[mb][d] = __builtin_bit_cast(bf16x8, read_a(st, mb, 4 * (lane >> 4) + d));
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float sc = e8m0_to_f32(sm[(wn * NTW + t) * 64 + lane]);
+        const u32x4 bq = read_b(st, t, 0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_fp4x8_scaled(bq[d], sc);
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(af[mb][d], bv, acc[mb][t]);
+        }
+      }
+    } else if constexpr (FAM == FAM_W8A16 || FAM == FAM_F8A16) {
+      // 8-bit codes of the step's two units -> bf16, MFMA d taking unit d >> 1; the per-channel
+      // scale is applied in the epilogue
+      bf16x8 af[MW][4];
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          af[mb][d] = __builtin_bit_cast(bf16x8, read_a(st, mb, 4 * (lane >> 4) + d));
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const u32x4 b0 = read_b(st, t, 0), b1 = read_b(st, t, 1);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bf16x8 bv = dequant_w8_step<FAM == FAM_F8A16>(b0, b1, d);
+#pragma unroll
+          for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_bf16(af[mb][d], bv, acc[mb][t]);
         }
       }
     } else if constexpr (FAM == FAM_FP8B) {
@@ -364,6 +419,9 @@ int pipe_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W8A8) return pipe_lds_table<FAM_W8A8>(cfg, seq);
   if (fam == FAM_W4A8) return pipe_lds_table<FAM_W4A8>(cfg, seq);
   if (fam == FAM_FP8B) return pipe_lds_table<FAM_FP8B>(cfg, seq);
+  if (fam == FAM_MXW4A16) return pipe_lds_table<FAM_MXW4A16>(cfg, seq);
+  if (fam == FAM_W8A16) return pipe_lds_table<FAM_W8A16>(cfg, seq);
+  if (fam == FAM_F8A16) return pipe_lds_table<FAM_F8A16>(cfg, seq);
   return 1 << 30;   // no instantiation for the other families
 }
 
@@ -402,6 +460,9 @@ hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, 
   if (fam == FAM_W8A8) return launch_pipe_fam<FAM_W8A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W4A8) return launch_pipe_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_FP8B) return launch_pipe_fam<FAM_FP8B, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_MXW4A16) return launch_pipe_fam<FAM_MXW4A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W8A16) return launch_pipe_fam<FAM_W8A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_F8A16) return launch_pipe_fam<FAM_F8A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return hipErrorInvalidValue;
 }
 

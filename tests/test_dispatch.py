@@ -18,9 +18,11 @@ TABLE = {
     "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096,
               [(1, (0, 31)), (5, (0, 28)), (32, (0, 29)), (128, (0, 22)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w8a16": (hq.DESC_W8A16_INT8, 14336, 4096,
-              [(1, (0, 33)), (4, (0, 33)), (5, (0, 27)), (32, (0, 29)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
+              [(1, (0, 33)), (4, (0, 33)), (5, (0, 27)), (32, (0, 29)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)),
+               (257, (2, 12)), (640, (2, 12)), (641, (3, 3)), (896, (3, 3)), (897, (2, 12)), (8192, (2, 12))]),
     "f8a16": (hq.DESC_W8A16_FP8, 14336, 4096,
-              [(1, (0, 30)), (5, (0, 27)), (32, (0, 22)), (128, (0, 4)), (129, (3, 3)), (8192, (3, 3))]),
+              [(1, (0, 30)), (5, (0, 27)), (32, (0, 22)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)),
+               (257, (2, 12)), (768, (3, 3)), (1024, (2, 12)), (8192, (2, 12))]),
     "w8a8": (hq.DESC_W8A8, 8192, 8192,
              [(1, (0, 2)), (8, (0, 2)), (9, (0, 1)), (16, (0, 1)), (32, (0, 23)), (33, (0, 29)),
               (64, (0, 29)), (65, (2, 3)), (256, (2, 3)), (257, (3, 11)), (512, (3, 11)),

@@ -9,7 +9,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, gemm, prepack, say, to_dev
+from gpu_harness import DEV, check_float, every_configuration, gemm, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +30,11 @@ def _run(d, M, N, K, fp8):
     (1, 512, 4096), (3, 272, 384), (16, 64, 128), (32, 256, 1024), (64, 512, 512),
     (1, 64, 8192),      # 4 workgroups: K split across workgroups, then the reduction launch
     (200, 256, 640),    # ping-pong 128 x 128, 5 K steps
-    (300, 512, 1024),   # ragged M
+    (300, 512, 1024),   # pipelined 128 x 256 (eight waves of 64 x 64), ragged M
+    (700, 256, 640),    # ping-pong 128 x 128 around M = 768, 5 K steps
+    (1100, 256, 128),   # pipelined 128 x 256, one K step
     (1000, 400, 512),   # N not a multiple of the 128-wide tile: skinny fallback
+    (1000, 384, 512),   # N % 256 != 0: ping-pong 128 x 128 fallback
 ])
 def test_w8a16_small(M, N, K, fp8):
     say(f"[w8a16 fp8={fp8}] M={M} N={N} K={K}")
@@ -57,25 +60,17 @@ def test_w8a16_full_size_sampled(M, fp8):
 
 @pytest.mark.parametrize("fp8", FMTS)
 def test_w8a16_every_kernel_configuration(fp8, monkeypatch):
-    """Every skinny and ping-pong configuration that fits the shape (the tuner may pick any)."""
-    M, N, K = 96, 512, 768
+    """Every skinny, pipelined and ping-pong configuration that fits the shape (the tuner may pick
+    any), at a ragged M over 256 rows."""
+    M, N, K = 600, 512, 768
     d = synth.make_w8a16(1301, M, N, K, fp8=fp8)
     desc = _desc(fp8)
     w = prepack(desc, 1, N, K, d["wq"], d["s_ch"])
+    x = to_dev(d["x"])
     ref, _ = oracle.ref_w8a16(d["x"], d["wq"], d["s_ch"], fp8=fp8)
-    ran = 0
-    for kind in (0, 3):
-        for cfg in range(hq.hq_kernel_config_count(kind)):
-            monkeypatch.setenv("HQ_TUNE", f"kind={kind},cfg={cfg},split=1")
-            try:
-                plan = hq.hq_gemm_plan(desc, M, N, K)
-            except hq.HQError:
-                continue            # the configuration does not fit this shape
-            say(f"[w8a16 fp8={fp8}] kind={kind} cfg={cfg} plan={plan}")
-            y = gemm(desc, M, N, K, to_dev(d["x"]), None, w)
-            check_float(y, ref, f"w8a16 fp8={fp8} kind={kind} cfg={cfg}")
-            ran += 1
-    assert ran >= 20
+    ran = every_configuration(desc, M, N, K, lambda: gemm(desc, M, N, K, x, None, w),
+                              lambda y, what: check_float(y, ref, f"w8a16 fp8={fp8} {what}"), monkeypatch)
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 2, 3))
 
 
 def test_w8a16_code_and_scale_extremes():
