@@ -249,9 +249,10 @@ constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {640, 3, 10}, {1280, 2, 14}, {
 constexpr RangeEntry kW8a16Table[] = {{128, 0, 0}, {256, 3, 3}, {640, 2, 12}, {896, 3, 3}, {kInf, 2, 12}};
 // 2-bit WnA16 on the ping-pong kernel's 256-wide tiles (the only ones whose half-unit weight copies
 // split over the eight waves), measured at N=14336, K=4096: skinny to M=128 (36.8 us; ping-pong
-// 52.1), 64 x 256 with four slots to 512 (M=256: 49.5 us against 53.1 with three), 128 x 256
-// beyond (M=1024 / 8192: 133 / 916 us; the skinny kernel 242 / 1834)
-constexpr RangeEntry kWna2Table[] = {{128, 0, 0}, {512, 3, 13}, {kInf, 3, 0}};
+// 52.1), 64 x 256 with four slots to 256 (44.2 us; 128 x 256 71.2), 128 x 256 beyond (M = 320 /
+// 384 / 512: 65.4 / 66.1 / 68.0 us against 83.2 / 83.4 / 84.8 for 64 x 256; M=1024 / 8192: 133 /
+// 916 us, the skinny kernel 242 / 1834)
+constexpr RangeEntry kWna2Table[] = {{128, 0, 0}, {256, 3, 13}, {kInf, 3, 0}};
 // 3-bit WnA16 (each tile's 768-byte unit of a step lands in a 1 KiB LDS slot, three 4-byte-per-lane
 // copies, so every ping-pong tile whose ring fits the LDS works), measured at N=14336, K=4096:
 // skinny to M=128 (46.6 us), ping-pong 128 x 128 to 256 (M=192 / 256: 55.2 / 55.6 us against 69.9

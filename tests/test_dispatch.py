@@ -14,7 +14,7 @@ TABLE = {
     "w4a16mx": (hq.DESC_W4A16_MXFP4, 14336, 4096,
                 [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 3)), (65, (0, 4)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w2a16": (hq.DESC_W2A16_ASYM, 14336, 4096,
-              [(1, (0, 31)), (4, (0, 31)), (5, (0, 28)), (128, (0, 22)), (129, (3, 13)), (512, (3, 13)), (513, (3, 0)), (8192, (3, 0))]),
+              [(1, (0, 31)), (4, (0, 31)), (5, (0, 28)), (128, (0, 22)), (129, (3, 13)), (256, (3, 13)), (257, (3, 0)), (512, (3, 0)), (8192, (3, 0))]),
     "w3a16": (hq.DESC_W3A16_ASYM, 14336, 4096,
               [(1, (0, 31)), (5, (0, 28)), (32, (0, 29)), (128, (0, 22)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w8a16": (hq.DESC_W8A16_INT8, 14336, 4096,

@@ -10,7 +10,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, gemm, prepack, say, to_dev
+from gpu_harness import DEV, check_float, every_configuration, gemm, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -51,25 +51,17 @@ def test_wna2_full_size_sampled(M):
 
 
 def test_wna2_every_kernel_configuration(monkeypatch):
-    """Every skinny and ping-pong configuration that fits (the ping-pong kernel's 128-wide tiles
-    do not: their half-unit copies do not split over eight waves)."""
-    M, N, K = 96, 512, 768
+    """Every skinny and ping-pong configuration that fits, at a ragged M over 256 rows
+    (the ping-pong kernel's 128-wide tiles do not: their half-unit copies do not split over eight
+    waves)."""
+    M, N, K = 600, 512, 768
     d = synth.make_wna2(1601, M, N, K)
     w = prepack(D, 1, N, K, d["wq"], d["scales"], d["zeros"])
+    x = to_dev(d["x"])
     ref, _ = oracle.ref_wna2(d["x"], d["wq"], d["scales"], d["zeros"], 128)
-    ran = {0: 0, 3: 0}
-    for kind in (0, 3):
-        for cfg in range(hq.hq_kernel_config_count(kind)):
-            monkeypatch.setenv("HQ_TUNE", f"kind={kind},cfg={cfg},split=1")
-            try:
-                hq.hq_gemm_plan(D, M, N, K)
-            except hq.HQError:
-                continue
-            say(f"[wna2] kind={kind} cfg={cfg}")
-            y = gemm(D, M, N, K, to_dev(d["x"]), None, w)
-            check_float(y, ref, f"wna2 kind={kind} cfg={cfg}")
-            ran[kind] += 1
-    assert ran[0] >= 20 and ran[3] >= 4
+    ran = every_configuration(D, M, N, K, lambda: gemm(D, M, N, K, x, None, w),
+                              lambda y, what: check_float(y, ref, f"wna2 {what}"), monkeypatch)
+    assert ran.get(0, 0) >= 20 and ran.get(3, 0) >= 4
     monkeypatch.setenv("HQ_TUNE", "kind=3,cfg=2,split=1")     # 128 x 128: refused
     with pytest.raises(hq.HQError):
         hq.hq_gemm_plan(D, M, N, K)
