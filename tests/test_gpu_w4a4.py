@@ -28,11 +28,13 @@ def _gemm(d, M, N, K):
     (128, 256, 1536),
     (64, 256, 1024),     # 33..64 rows: two 32-row blocks
     (300, 256, 512),     # skinny, 64-row blocks, ragged M
-    (700, 384, 640),     # ping-pong 128 x 128, four LDS slots, 5 K steps
-    (1000, 256, 128),    # four slots, one K step
-    (900, 128, 256),     # four slots, two K steps
-    (4200, 256, 512),    # ping-pong 256 x 256 (waves of 64 x 128), four slots, ragged M
-    (2300, 512, 384),    # 256 x 256, three K steps (fewer than the four slots)
+    (700, 384, 640),     # pipelined 64 x 128 (four stages), 5 K steps
+    (1000, 256, 128),    # pipelined 64 x 128, one K step
+    (900, 128, 256),     # pipelined 64 x 128, two K steps
+    (1500, 256, 640),    # pipelined 128 x 256, eight waves of 64 x 64, ragged M, 5 K steps
+    (1200, 384, 512),    # N % 256 != 0 above 1024 rows: ping-pong 128 x 128 fallback
+    (4200, 256, 512),    # pipelined 128 x 256 (four waves of 64 x 128, three stages), ragged M
+    (2300, 512, 384),    # pipelined 128 x 256, three K steps
     (257, 128, 256),
 ])
 def test_w4a4_small(M, N, K):
@@ -50,7 +52,7 @@ def test_w4a4_every_kernel_configuration(monkeypatch):
     ref, _ = oracle.ref_w4a4(d["xq"], d["xs"], d["wq"], d["scales"])
     ran = every_configuration(D, M, N, K, lambda: _gemm(d, M, N, K),
                               lambda y, what: check_float(y, ref, f"w4a4 {what}"), monkeypatch)
-    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 3))
+    assert sum(ran.values()) >= 20 and all(ran.get(k, 0) > 0 for k in (0, 2, 3))
 
 
 @pytest.mark.parametrize("M", [1, 32, 256, 2048, 8192])
