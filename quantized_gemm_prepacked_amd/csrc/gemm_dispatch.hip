@@ -206,7 +206,10 @@ struct RangeEntry {
   int kind, cfg;
 };
 constexpr int64_t kInf = int64_t(1) << 40;
-constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 2}, {256, 3, 3}, {kInf, 3, 0}};
+// WNA16 at N=14336, K=4096: pipelined 64 x 128 with four waves of 64 x 32 at M = 65..128 (every wave
+// spans the tile's 64 rows, so each dequantized weight feeds four row blocks: M=128 32.9 us against
+// 35.4 for waves of 32 x 64 and 36.1 for eight waves of 32 x 32)
+constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 15}, {256, 3, 3}, {kInf, 3, 0}};
 // (M in (256, 512]: ping-pong 128 x 128 with four LDS slots, 57.7 vs 61.3 us with three)
 constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
 // The MXFP4-weight formats with 8- or 4-bit activations, measured at N=4096, K=7168 (one sweep

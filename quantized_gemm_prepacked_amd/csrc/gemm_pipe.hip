@@ -109,11 +109,12 @@ struct PipeShape {
   static constexpr int B_INSTR = (NT * UPS) / kWaves;
   static constexpr int META_INSTR = (SC_BYTES ? 1 : 0) + (Z_BYTES ? 1 : 0) + (ASC_BYTES ? 1 : 0);
   static constexpr int INSTR = A_INSTR + B_INSTR + META_INSTR;
-  static_assert(A_BYTES % (1024 * kWaves) == 0, "activation tile must split into wave loads");
-  static_assert((NT * UPS) % kWaves == 0, "weight units must split over the waves");
+  // the copies split evenly over the waves (shapes that do not are never launched)
+  static constexpr bool kValid = A_BYTES % (1024 * kWaves) == 0 && (NT * UPS) % kWaves == 0 &&
+                                 (ASC_BYTES == 0 || BM % kWaves == 0);
+  static constexpr int LDS_OR_NONE = kValid ? LDS : 1 << 30;
   static_assert(SC_BYTES <= 1024 && Z_BYTES <= 256, "metadata fits one masked load");
-  static_assert(ASC_BYTES <= 1024 && (ASC_BYTES == 0 || (BM % kWaves == 0 && ASC_ROWS <= 64)),
-                "activation scales: one masked load per wave");
+  static_assert(ASC_BYTES <= 1024 && ASC_ROWS <= 64, "activation scales: one masked load per wave");
   // block-scaled FP8: a wave's NTW tiles lie in one 128-channel scale block
   static_assert(FAM != FAM_FP8B || 8 % NTW == 0, "a wave's tiles share one weight scale block");
 };
@@ -121,6 +122,7 @@ struct PipeShape {
 template <int FAM, int MW, int NTW, int WM, int WN, int STAGES, bool MOE>
 __global__ __launch_bounds__(64 * WM * WN) void pipe_gemm_kernel(KParams p, int tiles_m, int tiles_n) {
   using Sh = PipeShape<FAM, MW, NTW, WM, WN, STAGES, MOE>;
+  static_assert(Sh::kValid, "copies must split over the waves");
   using Acc = typename AccType<FAM>::type;
   constexpr int BM = Sh::BM, RB = Sh::RB, CPR = Sh::CPR, NT = Sh::NT, UPS = Sh::UPS;
   extern __shared__ __align__(1024) uint8_t smem[];
@@ -440,6 +442,7 @@ static constexpr PipeCfg kPipe[] = {
     {4, 4, 2, 4, 2},  // 12: 128 x 256, 8 waves of 64 x 64, 2 stages
     {4, 4, 2, 4, 3},  // 13: as 12, 3 stages
     {2, 8, 4, 2, 3},  // 14: 128 x 256, 8 waves of 32 x 128, 3 stages
+    {4, 2, 1, 4, 4},  // 15: 64 x 128, 4 waves of 64 x 32 (every wave on all rows), 4 stages
 };
 
 const PipeCfg* pipe_configs(int* count) {
@@ -449,7 +452,7 @@ const PipeCfg* pipe_configs(int* count) {
 
 template <int FAM, int I>
 constexpr int pipe_lds_of() {
-  return PipeShape<FAM, kPipe[I].mw, kPipe[I].ntw, kPipe[I].wm, kPipe[I].wn, kPipe[I].stages, false>::LDS;
+  return PipeShape<FAM, kPipe[I].mw, kPipe[I].ntw, kPipe[I].wm, kPipe[I].wn, kPipe[I].stages, false>::LDS_OR_NONE;
 }
 
 template <int FAM, int... I>
@@ -478,7 +481,7 @@ template <int FAM, bool MOE, int I>
 static hipError_t launch_pipe_one(const KParams& p, dim3 grid, int tiles_m, int tiles_n, hipStream_t s) {
   constexpr PipeCfg C = kPipe[I];
   using Sh = PipeShape<FAM, C.mw, C.ntw, C.wm, C.wn, C.stages, MOE>;
-  if constexpr (Sh::LDS <= 160 * 1024) {
+  if constexpr (Sh::kValid && Sh::LDS <= 160 * 1024) {
     auto kern = pipe_gemm_kernel<FAM, C.mw, C.ntw, C.wm, C.wn, C.stages, MOE>;
     if (Sh::LDS > 65536)
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);

@@ -9,7 +9,7 @@ import quantized_gemm_prepacked_amd as hq
 # format: (descriptor, N, K, [(M, (kind, cfg))])
 TABLE = {
     "w4a16": (hq.DESC_W4A16_ASYM, 14336, 4096,
-              [(1, (0, 30)), (4, (0, 30)), (5, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 2)), (128, (2, 2)), (129, (3, 3)),
+              [(1, (0, 30)), (4, (0, 30)), (5, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 15)), (128, (2, 15)), (129, (3, 3)),
                (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w4a16mx": (hq.DESC_W4A16_MXFP4, 14336, 4096,
                 [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 3)), (65, (0, 4)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
