@@ -106,7 +106,9 @@ int pick_skinny(const Combo& c, int64_t rows, int64_t N) {
   // 2-bit weights: two 32-row blocks, double-buffered (N=14336, K=4096, M=64 / 128: 20.4 / 37.2
   // us against 22.4 / 39.2 with 64-row blocks)
   if (c.fam == FAM_WNA2 || c.fam == FAM_WNA3) return first_fit({22, 5, 4, 6});
-  if (c.fam == FAM_WNA16) return first_fit({5, 4, 6});
+  // INT4 at 33..64 rows: two 32-row blocks of 64 channels, double-buffered (M = 48 / 64: 20.6 /
+  // 21.4 us against 21.4 / 21.9 for one 64-row block)
+  if (c.fam == FAM_WNA16) return first_fit({22, 5, 4, 6});
   // MXFP4 weights with bf16 activations, M=64: two 32-row blocks of 64 channels 18.7 us (the
   // 64-row form 20.2); M=128: the 64-row form
   if (c.fam == FAM_MXW4A16) return rows <= 64 ? first_fit({3, 5, 4, 6}) : first_fit({4, 5, 6});
@@ -211,37 +213,44 @@ constexpr int64_t kInf = int64_t(1) << 40;
 // 35.4 for waves of 32 x 64 and 36.1 for eight waves of 32 x 32)
 constexpr RangeEntry kWna16Table[] = {{64, 0, 0}, {128, 2, 15}, {256, 3, 3}, {kInf, 3, 0}};
 // (M in (256, 512]: ping-pong 128 x 128 with four LDS slots, 57.7 vs 61.3 us with three)
-constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {256, 2, 3}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
+// W8A8 at N=K=8192: pipelined 64 x 64 to M=128 (M = 96 / 128: 23.6 / 24.3 us), then 64 x 128 with
+// four waves of 64 x 32 to 256 (M = 160 / 192 / 256: 36.1 / 36.5 / 37.7 us against 36.5 / 38.4 /
+// 38.7 for 64 x 64)
+constexpr RangeEntry kW8a8Table[] = {{64, 0, 0}, {128, 2, 3}, {256, 2, 15}, {512, 3, 11}, {1024, 3, 1}, {kInf, 2, 8}};
 // The MXFP4-weight formats with 8- or 4-bit activations, measured at N=4096, K=7168 (one sweep
 // of every pipelined and ping-pong configuration; us at the M values named, the choice's time
 // first, the ping-pong kernel's best after the semicolon). Above the skinny range the pipelined
 // kernel wins nearly everywhere (one barrier per step, all waves computing); which tile depends
 // on how evenly it fills the CUs at this N.
-// W4A8 (FP8 activations), M = 768 / 1024 / 1536 / 2048 / 3072 / 4096 / 8192: 64 x 128 to 1024
-// (34.4 / 33.2; 38.8 / 39.3), 128 x 128 to 2048 (45.5 / 52.4; 48.7 / 52.1), 128 x 256 with eight
-// waves of 64 x 64 at 3072 (82.5; 95.0), 256 x 256 beyond (91.1 / 176.2; 100.9 / 197.1).
-constexpr RangeEntry kW4a8Table[] = {{512, 0, 0}, {1024, 2, 2}, {2048, 2, 0}, {3072, 2, 12}, {kInf, 2, 11}};
-// W4A4 (MXFP4 activations): skinny 64-row blocks to 640 (M=512: 34 us against 49 for ping-pong),
-// 64 x 128 to 1024 (32.4 / 30.7; 38.4 / 39.1), 128 x 256 with eight waves of 64 x 64 and three
+// W4A8 (FP8 activations): skinny to M=256 (19.4 us), pipelined 64 x 64 to 512 (M = 320 / 448 /
+// 512: 24.6 / 25.5 / 26.0 us against 27.1 / 26.6 / 27.4 skinny); then, at M = 768 / 1024 / 1536 /
+// 2048 / 3072 / 4096 / 8192: 64 x 128 to 1024 (34.4 / 33.2; 38.8 / 39.3), 128 x 128 to 2048
+// (45.5 / 52.4; 48.7 / 52.1), 128 x 256 with eight waves of 64 x 64 at 3072 (82.5; 95.0),
+// 256 x 256 beyond (91.1 / 176.2; 100.9 / 197.1).
+constexpr RangeEntry kW4a8Table[] = {{256, 0, 0}, {512, 2, 3}, {1024, 2, 2}, {2048, 2, 0}, {3072, 2, 12}, {kInf, 2, 11}};
+// W4A4 (MXFP4 activations): skinny to M=160 (M=128: 11.9 us), pipelined 64 x 64 to 640 (M = 192 /
+// 256 / 320 / 384 / 512: 18.5 / 18.9 / 23.2 / 23.8 / 23.0 us against 19.8 / 19.3 / 32.9 / 31.1 /
+// 29.7 for skinny 64-row blocks), 64 x 128 to 1024 (32.4 / 30.7; 38.4 / 39.1), 128 x 256 with eight waves of 64 x 64 and three
 // stages to 2048 (45.6 / 47.0; 50.2 / 51.9), 128 x 256 with four waves of 64 x 128 beyond
 // (63.8 / 73.3 / 141.1; 69.2 / 75.1 / 146.9).
-constexpr RangeEntry kW4a4Table[] = {{640, 0, 0}, {1024, 2, 2}, {2048, 2, 13}, {kInf, 2, 6}};
-// W4A8-MXFP8: skinny to M=576 (M=512: 45.5 us against 50.9), pipelined 64 x 128 to 1024 (37.5 /
-// 36.2; 41.6 / 43.0), ping-pong 128 x 256 with four slots to 2048 (52.5 / 56.1), pipelined
+constexpr RangeEntry kW4a4Table[] = {{160, 0, 0}, {640, 2, 3}, {1024, 2, 2}, {2048, 2, 13}, {kInf, 2, 6}};
+// W4A8-MXFP8: skinny to M=256 (21.1 us), pipelined 64 x 64 to 512 (M = 320 / 384 / 512: 25.0 /
+// 25.6 / 27.4 us against 35.3 / 33.9 / 35.3 skinny), 64 x 128 to 1024 (37.5 / 36.2; 41.6 / 43.0), ping-pong 128 x 256 with four slots to 2048 (52.5 / 56.1), pipelined
 // 256 x 256 beyond (92.1 / 99.5 / 192.2; 104.2 / 110.4 / 214.3).
-constexpr RangeEntry kW4a8mxTable[] = {{576, 0, 0}, {1024, 2, 2}, {2048, 3, 8}, {kInf, 2, 11}};
+constexpr RangeEntry kW4a8mxTable[] = {{256, 0, 0}, {512, 2, 3}, {1024, 2, 2}, {2048, 3, 8}, {kInf, 2, 11}};
 // MXFP4 weights with bf16 activations: the W4A16 crossovers, ping-pong instead of async-pipelined
 // (M = 128, N=14336 K=4096: the small-M kernel 25.7 us against 35.0 for ping-pong 128 x 128)
 constexpr RangeEntry kMxW4a16Table[] = {{128, 0, 0}, {256, 3, 3}, {kInf, 3, 0}};
-// Block-scaled FP8 W8A8, measured at N=K=8192: the small-M kernel to M=256 (M = 128 / 256: 34.1 /
-// 53.5 us against 58.4 / 57.4 for ping-pong), ping-pong 128 x 128 with four LDS slots at M=512
+// Block-scaled FP8 W8A8, measured at N=K=8192: the small-M kernel to M=128 (33.1 us; ping-pong
+// 58.4), pipelined 64 x 128 to 256 (M = 160 / 192 / 224 / 256: 41.4 / 42.7 / 42.2 / 43.4 us against
+// 48.9 / 54.0 / 53.6 / 53.5 for the small-M kernel), ping-pong 128 x 128 with four LDS slots at M=512
 // (56.5 us; pipelined 128 x 256 86.9), then the pipelined kernel, whose eight waves compute
 // together so that one wave's per-step scaling runs beside the other's MFMAs (ping-pong at
 // M = 768 / 1024 / 2048 / 4096: 106.2 / 107.9 / 214.9 / 408.9 us). Its two tiles alternate with
 // how evenly they fill the 256 CUs: 128 x 256 (waves of 32 x 128) at M = 768 / 1024 / 3072
 // (88.4 / 94.1 / 253.8 us; 256 x 256: 146.4 at 1024, 293.4 at 3072), 256 x 256 (waves of
 // 64 x 128) at M = 1536 / 2048 / 4096 (149.9 / 153.6 / 303.2 us; 128 x 256: 162.7 / 169.4 / 338.8).
-constexpr RangeEntry kFp8bTable[] = {{256, 0, 0}, {640, 3, 10}, {1280, 2, 14}, {2048, 2, 11},
+constexpr RangeEntry kFp8bTable[] = {{128, 0, 0}, {256, 2, 2}, {640, 3, 10}, {1280, 2, 14}, {2048, 2, 11},
                                      {3072, 2, 14}, {kInf, 2, 11}};
 // INT8 / FP8 weights with bf16 activations, measured at N=14336, K=4096 (INT8 / FP8): skinny
 // 64-row blocks to M=128 (34.5 / 32.5 us; ping-pong 41.7 / 32.1), ping-pong 128 x 128 with waves

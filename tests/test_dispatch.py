@@ -9,7 +9,7 @@ import quantized_gemm_prepacked_amd as hq
 # format: (descriptor, N, K, [(M, (kind, cfg))])
 TABLE = {
     "w4a16": (hq.DESC_W4A16_ASYM, 14336, 4096,
-              [(1, (0, 30)), (4, (0, 30)), (5, (0, 28)), (16, (0, 28)), (64, (0, 5)), (65, (2, 15)), (128, (2, 15)), (129, (3, 3)),
+              [(1, (0, 30)), (4, (0, 30)), (5, (0, 28)), (16, (0, 28)), (33, (0, 22)), (64, (0, 22)), (65, (2, 15)), (128, (2, 15)), (129, (3, 3)),
                (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
     "w4a16mx": (hq.DESC_W4A16_MXFP4, 14336, 4096,
                 [(1, (0, 32)), (4, (0, 32)), (5, (0, 28)), (64, (0, 3)), (65, (0, 4)), (128, (0, 4)), (129, (3, 3)), (256, (3, 3)), (257, (3, 0)), (8192, (3, 0))]),
@@ -25,19 +25,19 @@ TABLE = {
                (257, (2, 12)), (768, (3, 3)), (1024, (2, 12)), (8192, (2, 12))]),
     "w8a8": (hq.DESC_W8A8, 8192, 8192,
              [(1, (0, 2)), (8, (0, 2)), (9, (0, 1)), (16, (0, 1)), (32, (0, 23)), (33, (0, 29)),
-              (64, (0, 29)), (65, (2, 3)), (256, (2, 3)), (257, (3, 11)), (512, (3, 11)),
+              (64, (0, 29)), (65, (2, 3)), (128, (2, 3)), (129, (2, 15)), (256, (2, 15)), (257, (3, 11)), (512, (3, 11)),
               (513, (3, 1)), (1024, (3, 1)), (1025, (2, 8))]),
     "fp8block": (hq.DESC_W8A8_FP8_BLOCK, 8192, 8192,
                  [(1, (0, 21)), (4, (0, 21)), (5, (0, 20)), (16, (0, 20)), (32, (0, 23)), (64, (0, 29)),
-                  (65, (0, 4)), (256, (0, 4)), (257, (3, 10)), (640, (3, 10)), (641, (2, 14)),
+                  (65, (0, 4)), (128, (0, 4)), (129, (2, 2)), (256, (2, 2)), (257, (3, 10)), (640, (3, 10)), (641, (2, 14)),
                   (1280, (2, 14)), (1281, (2, 11)), (2048, (2, 11)), (2049, (2, 14)), (3072, (2, 14)),
                   (3073, (2, 11)), (8192, (2, 11))]),
     "w4a8": (hq.DESC_W4A8_MXFP4, 4096, 7168,
              [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (65, (0, 29)), (128, (0, 29)), (129, (0, 22)),
-              (256, (0, 22)), (257, (0, 4)), (512, (0, 4)), (513, (2, 2)), (1024, (2, 2)), (1025, (2, 0)),
+              (256, (0, 22)), (257, (2, 3)), (512, (2, 3)), (513, (2, 2)), (1024, (2, 2)), (1025, (2, 0)),
               (2048, (2, 0)), (2049, (2, 12)), (3072, (2, 12)), (3073, (2, 11))]),
-    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (640, (0, 4)), (641, (2, 2)), (1024, (2, 2)), (1025, (2, 13)), (2048, (2, 13)), (2049, (2, 6)), (8192, (2, 6))]),
-    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (576, (0, 4)), (577, (2, 2)), (1024, (2, 2)), (1025, (3, 8)), (2048, (3, 8)), (2049, (2, 11)), (8192, (2, 11))]),
+    "w4a4": (hq.DESC_W4A4_MXFP4, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 23)), (128, (0, 29)), (129, (0, 4)), (160, (0, 4)), (161, (2, 3)), (640, (2, 3)), (641, (2, 2)), (1024, (2, 2)), (1025, (2, 13)), (2048, (2, 13)), (2049, (2, 6)), (8192, (2, 6))]),
+    "w4a8mx": (hq.DESC_W4A8_MXFP8, 4096, 7168, [(1, (0, 21)), (32, (0, 18)), (64, (0, 28)), (128, (0, 29)), (129, (0, 4)), (256, (0, 4)), (257, (2, 3)), (512, (2, 3)), (513, (2, 2)), (1024, (2, 2)), (1025, (3, 8)), (2048, (3, 8)), (2049, (2, 11)), (8192, (2, 11))]),
 }
 
 

@@ -30,8 +30,10 @@ def _gemm(d, M, N, K):
     (2600, 256, 256),    # pipelined 128 x 256 between 2048 and 3072 rows, ragged M
     (300, 256, 128),     # ping-pong 128 x 128 with four LDS slots, one K step
     (480, 128, 256),     # ping-pong, four slots, two K steps
-    (200, 256, 128),     # small-M kernel (M <= 256), one K step
-    (150, 128, 256),     # small-M kernel, two K steps
+    (200, 256, 128),     # pipelined 64 x 128 (129..256 rows), one K step
+    (100, 256, 128),     # small-M kernel (M <= 128), one K step
+    (150, 128, 256),     # pipelined 64 x 128, two K steps
+    (90, 128, 256),      # small-M kernel, two K steps
     (2100, 256, 256),    # pipelined 256 x 256 (two stages), two K steps, ragged last tile
     (3000, 512, 384),    # pipelined 256 x 256, three K steps
 ])

@@ -121,7 +121,9 @@ def test_wna16_past_32bit_activation_offsets():
 
 
 # ---- W8A8 -------------------------------------------------------------------------------------
-W8A8_SMALL = [(1, 256, 8192), (64, 512, 1024), (7, 272, 320), (16, 256, 64), (200, 512, 2048),
+W8A8_SMALL = [(1, 256, 8192), (64, 512, 1024), (7, 272, 320), (16, 256, 64),
+              (200, 512, 2048),    # 64 x 128 pipelined tiles, four waves of 64 x 32
+              (100, 512, 1024),    # 64 x 64 pipelined tiles, ragged M
               (20, 512, 1024),     # two 16-row blocks per skinny workgroup
               (700, 384, 1024),    # 256 x 128 ping-pong tiles
               (400, 256, 640),     # 128 x 128 ping-pong tiles, four LDS slots
@@ -180,7 +182,7 @@ def test_w8a8_every_kernel_configuration(monkeypatch):
 
 # ---- W4A8-MXFP4 -------------------------------------------------------------------------------
 W4A8_SMALL = [(1, 512, 7168), (32, 256, 1024), (3, 272, 384), (16, 64, 128), (130, 512, 1024),
-              (500, 256, 1024),    # skinny, four 16-row blocks per workgroup
+              (500, 256, 1024),    # 64 x 64 pipelined tiles, ragged M
               (700, 256, 1024),    # 64 x 128 pipelined tiles
               (1200, 512, 768),    # 128 x 128 pipelined tiles
               (1600, 512, 384),    # 128 x 128 pipelined tiles, ragged M, 3 K steps

@@ -27,7 +27,8 @@ def _gemm(d, M, N, K):
     (100, 512, 1024),    # 65..128 rows: four 32-row skinny blocks of 64 channels, ragged M
     (128, 256, 1536),
     (64, 256, 1024),     # 33..64 rows: two 32-row blocks
-    (300, 256, 512),     # skinny, 64-row blocks, ragged M
+    (300, 256, 512),     # pipelined 64 x 64 (four stages), ragged M
+    (150, 256, 512),     # skinny, 64-row blocks, ragged M
     (700, 384, 640),     # pipelined 64 x 128 (four stages), 5 K steps
     (1000, 256, 128),    # pipelined 64 x 128, one K step
     (900, 128, 256),     # pipelined 64 x 128, two K steps

@@ -21,7 +21,9 @@ def _gemm(d, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (64, 256, 512), (300, 256, 512),
+    (1, 512, 7168), (32, 256, 1024), (3, 272, 384), (64, 256, 512),
+    (300, 256, 512),     # pipelined 64 x 64, ragged M
+    (200, 256, 1024),    # skinny, 64-row blocks
     (100, 512, 1024),    # 65..128 rows: four 32-row skinny blocks of 64 channels, ragged M
     (128, 256, 1536),
     (48, 256, 1024),     # 33..64 rows
