@@ -111,3 +111,22 @@ def every_configuration(desc, M, N, K, run, check, monkeypatch):
     monkeypatch.delenv("HQ_TUNE")
     say(f"[every configuration] configurations run per kind: {ran}")
     return ran
+
+
+def moe_random_shapes(seed: int, n: int, n_multiple: int = 16):
+    """n seeded MoE problems (T, topk, E, N, K, block_m, with_router_weights) over few-token,
+    mid and large T, every top-k up to 8 and block size 16..128 (128-row blocks only where N
+    allows them), small enough for the fp64 oracle."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(g.choice([g.integers(1, 16), g.integers(16, 200), g.integers(200, 700)]))
+        topk = int(g.choice([1, 2, 4, 8]))
+        E = int(g.integers(max(2, topk), 65))
+        N = int(n_multiple * g.integers(1, 768 // n_multiple + 1))
+        K = int(128 * g.integers(1, 13))
+        bm = int(g.choice([16, 32, 64, 128]))
+        if (bm == 128 and N % 128) or T * topk * N * K > 2e8:
+            continue
+        out.append((T, topk, E, N, K, bm, bool(g.integers(0, 2))))
+    return out

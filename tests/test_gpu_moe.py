@@ -10,7 +10,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, prepack, say, to_dev
+from gpu_harness import DEV, check_float, moe_random_shapes, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -130,6 +130,17 @@ def test_moe_gemm_small(T, topk, E, N, K, bm, tw):
                                         topk_weights=inp["topk_weights"] if tw else None)
     assert valid.all()
     check_float(y, ref, "moe gemm")
+
+
+def test_moe_gemm_random_shapes():
+    """INT4 experts on eight seeded random problems (T up to 700, top-k 1..8, E up to 64, every
+    block size; `moe_random_shapes`), the sort and the grouped GEMM against the oracle."""
+    for i, (T, topk, E, N, K, bm, tw) in enumerate(moe_random_shapes(31, 8)):
+        inp, experts, y = _moe_case(T, topk, E, N, K, bm, tw, 1500 + i)
+        ref, _, valid = oracle.ref_moe_gemm(inp["x"], inp["topk_ids"], lambda e: experts[e], N, E, 128,
+                                            topk_weights=inp["topk_weights"] if tw else None)
+        assert valid.all()
+        check_float(y, ref, f"moe gemm random {i}")
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 512, 2048, 4096])

@@ -11,7 +11,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, check_ulp, prepack, say, to_dev
+from gpu_harness import DEV, check_float, check_ulp, moe_random_shapes, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,14 @@ def test_moe_q_small(fmt, T, topk, E, N, K, bm, tw):
     if fmt == "fp8b" and N % 128:
         pytest.skip("block-scaled FP8 weights need N % 128 == 0 (128 x 128 scale blocks)")
     _moe(fmt, T, topk, E, N, K, bm, tw, 600 + T)
+
+
+@pytest.mark.parametrize("fmt", ALL)
+def test_moe_q_random_shapes(fmt):
+    """Six seeded random MoE problems per format (`moe_random_shapes`; block-scaled FP8 with N a
+    multiple of 128)."""
+    for i, case in enumerate(moe_random_shapes(33 + ALL.index(fmt), 6, 128 if fmt == "fp8b" else 16)):
+        _moe(fmt, *case, 1700 + i)
 
 
 @pytest.mark.parametrize("T,topk,E,N,K,bm,tw", [

@@ -8,7 +8,7 @@ import oracle
 import quantized_gemm_prepacked_amd as hq
 import synth
 
-from gpu_harness import DEV, check_float, every_configuration, gemm, prepack, say, to_dev
+from gpu_harness import DEV, check_float, every_configuration, gemm, moe_random_shapes, prepack, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -102,6 +102,16 @@ def test_w4a16mx_moe(T, topk, E, N, K, bm):
                                         topk_weights=inp["topk_weights"])
     assert valid.all()
     check_float(y, ref, "w4a16mx moe")
+
+
+def test_w4a16mx_moe_random_shapes():
+    """MXFP4 experts with bf16 activations on six seeded random MoE problems."""
+    for i, (T, topk, E, N, K, bm, tw) in enumerate(moe_random_shapes(32, 6)):
+        inp, experts, y = _moe(T, topk, E, N, K, bm, 1600 + i, tw=tw)
+        ref, _, valid = oracle.ref_moe_gemm(inp["x"], inp["topk_ids"], lambda e: experts[e], N, E, 128,
+                                            topk_weights=inp["topk_weights"] if tw else None)
+        assert valid.all()
+        check_float(y, ref, f"w4a16mx moe random {i}")
 
 
 @pytest.mark.parametrize("T", [8, 512])
