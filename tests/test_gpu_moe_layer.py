@@ -133,7 +133,10 @@ def _check_layer(L: Layer, stages=True):
     # End to end, against the layer with no rounding between stages. The GPU rounds to bf16 at
     # the same four boundaries as the oracle's layer, so both sit at about the same distance from
     # the exact chain -- the rounding noise -- and only that: the kernels' own fp32 error is far
-    # smaller. The bar is twice the oracle's own distance (plus the usual max-abs bar).
+    # smaller. Measured, the two distances agree to 1 % (ratio 1.000-1.010 over every case here).
+    # The bar is 1.1x the oracle's own distance (plus the usual max-abs bar): an extra error of
+    # its own in the GPU chain, independent of the rounding noise, then passes only below
+    # sqrt(1.1^2 - 1) = 0.46 of that distance (~1.7e-3 relative L2), under the float bar.
     args = (L.x, L.ids, L.tw, lambda e: L.gu_w[e], lambda e: L.dn_w[e], L.I, L.H, L.E, 128)
     ref = bf16_to_f64(oracle.ref_moe_layer(*args)["out"])
     exact = oracle.ref_moe_layer(*args, exact=True)["out"]
@@ -149,7 +152,7 @@ def _check_layer(L: Layer, stages=True):
     # gated activation is within a bound of its exact value, not correctly rounded, so many of its
     # bf16 values sit one ulp from the oracle's, and the two chains measured up to 2.8e-3 apart --
     # as far apart as each is from the exact chain. Every stage is held to its own bar above.)
-    assert e_gpu <= 2 * e_round, f"layer out: {e_gpu:.3e} > 2 x {e_round:.3e}"
+    assert e_gpu <= 1.1 * e_round, f"layer out: {e_gpu:.3e} > 1.1 x {e_round:.3e}"
     assert mx <= 2e-2
     return got
 
