@@ -5,8 +5,10 @@ back-to-back launches, each launch reading a different copy of its operands, cyc
 than the MI355X's 256 MB Infinity Cache, so the bytes come from HBM):
 
   read ceiling   the fastest one streaming-read kernel (csrc/read_probe.hip: 16-byte non-temporal
-                 loads, grid-stride, best of a few grid sizes) reads a fresh buffer of the sizes the
-                 decode calls stream, all of it in flight at once: 15.6 MB (the W4A8-MXFP4 weights), 30.5 MB (W4A16, N=14336
+                 loads, grid-stride or a contiguous share per workgroup, 1, 4 or 16 loads in flight
+                 per thread, workgroups of 256 or 1024 threads, best of these and of a few grid
+                 sizes)
+                 reads a fresh buffer of the sizes the decode calls stream: 15.6 MB (the W4A8-MXFP4 weights), 30.5 MB (W4A16, N=14336
                  K=4096), 67 MB (W8A8, N=K=8192) -- the practical bound of an M=1 call, below the
                  8 TB/s data-sheet figure; torch's copy (read + write) beside it.
   vendor GEMMs   torch's unquantized GEMMs (hipBLASLt) at the large-M shapes (bf16 at M=8192
@@ -65,13 +67,14 @@ def _probe_lib():
     lib = ctypes.CDLL(path)
     f = lib.hqp_stream_read
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p]
     return f
 
 
-def read_ceilings(sizes_mb=(15.6, 30.5, 67.1), wgs_list=(512, 1024, 2048, 4096, 8192)):
-    """Best time of the streaming-read probe over a few grid sizes, and torch's copy (read + write)
-    for comparison."""
+def read_ceilings(sizes_mb=(15.6, 30.5, 67.1), wgs_list=(224, 256, 512, 1024, 2048, 4096, 8192)):
+    """Best time of the streaming-read probe over a few grid sizes, both ways of dealing the buffer
+    to the workgroups and three load depths, and torch's copy (read + write) for comparison."""
     probe = _probe_lib()
     out = []
     for mb in sizes_mb:
@@ -80,16 +83,21 @@ def read_ceilings(sizes_mb=(15.6, 30.5, 67.1), wgs_list=(512, 1024, 2048, 4096, 
         src = [torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda") for _ in range(k)]
         sink = torch.empty(max(wgs_list), dtype=torch.int32, device="cuda")
         best = None
-        for wgs in wgs_list:
-            def rd(s, wgs=wgs):
-                assert probe(s.data_ptr(), n, sink.data_ptr(), wgs, torch.cuda.current_stream().cuda_stream) == 0
-            us = _graph_time([lambda s=s: rd(s) for s in src], reps=2 * k)
-            if best is None or us < best[0]:
-                best = (us, wgs)
+        for threads in (256, 1024):
+            for blocked in (0, 1):
+                for loads in (1, 4, 16):
+                    for wgs in wgs_list:
+                        def rd(s, wgs=wgs, threads=threads, blocked=blocked, loads=loads):
+                            assert probe(s.data_ptr(), n, sink.data_ptr(), wgs, threads, blocked, loads,
+                                         torch.cuda.current_stream().cuda_stream) == 0
+                        us = _graph_time([lambda s=s: rd(s) for s in src], reps=2 * k)
+                        if best is None or us < best[0]:
+                            best = (us, wgs, blocked, loads, threads)
         dst = torch.empty(n, dtype=torch.uint8, device="cuda")
         cp = _graph_time([lambda s=s: dst.copy_(s) for s in src], reps=2 * k)
         out.append({"MB": mb, "read_us": round(best[0], 2), "read_GBps": round(n / best[0] / 1e3, 1),
-                    "read_workgroups": best[1],
+                    "read_workgroups": best[1], "read_layout": "blocked" if best[2] else "grid-stride",
+                    "read_loads_in_flight_per_thread": best[3], "read_threads_per_workgroup": best[4],
                     "torch_copy_us": round(cp, 2), "torch_copy_traffic_GBps": round(2 * n / cp / 1e3, 1)})
         del src
     return out
