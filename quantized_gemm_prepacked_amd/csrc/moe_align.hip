@@ -1,20 +1,25 @@
-// moe_align.hip -- MoE token sort / expert offsets on the device, one workgroup, no host sync.
+// moe_align.hip -- MoE token sort / expert offsets on the device, one launch, no host sync.
 //
 // Feeds the "Indexed" MoE path (rows gathered through a sorted index) of the Humming
 // announcement's section "Results: kernel microbenchmarks". The token sort itself is not
 // described there; the contract (stable ascending order per expert, per-expert padding to a
 // multiple of block_m with sentinel T*topk) is the library's (hq.h).
 //
-// One workgroup of 1024 threads: (1) per-expert histogram with LDS atomics (order-free),
-// (2) block-wide scan of the padded counts (wave shuffles, then over the wave totals),
-// (3) stable scatter in tiles of 1024 entries: inside a wave, entries of the same expert are
-// found with ballots over the expert id bits and ranked by lane; across the 16 waves of a tile,
-// per-wave counts are prefix-summed in wave order; across tiles a running count per expert
-// carries on. Every position is therefore a pure function of the input, independent of
-// scheduling. The ids are read in chunks of 8 tiles, each thread issuing its 8 loads together
-// and keeping them in registers, so a chunk costs one memory latency rather than eight; the first
-// chunk (8192 entries, e.g. 1024 tokens at top-8) is read once for both the histogram and the
-// scatter.
+// Workgroups of 1024 threads, each owning a contiguous range of whole tiles of 1024 entries of the
+// flat id list (up to 128 workgroups, so the scatter is spread over the GPU). Every workgroup
+// (1) builds the per-expert histogram of the whole list with LDS atomics (order-free), counting
+// apart the entries before its own range, (2) scans the padded counts block-wide (wave shuffles,
+// then over the wave totals) -- the same offsets in every workgroup, from the same counts --
+// (3) scatters its own range stably, one tile at a time: inside a wave, entries of the same
+// expert are found with ballots over the expert id bits and ranked by lane; across the 16 waves
+// of a tile, per-wave counts are prefix-summed in wave order; across tiles a running count per
+// expert carries on, starting from the expert's count before the range. Every position is
+// therefore a pure function of the input, independent of scheduling, and the workgroups write
+// disjoint positions; the padding slots, the block -> expert table and the offsets are dealt
+// out between them the same way. The ids are read in chunks of 8 tiles, each thread issuing its
+// 8 loads together and keeping them in registers, so a chunk costs one memory latency rather
+// than eight; when the first workgroup's range holds the whole first chunk (8192 entries, e.g.
+// 1024 tokens at top-8) it reuses the histogram's registers for its scatter.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -72,35 +77,47 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
                                                              int32_t* __restrict__ block_expert,
                                                              int32_t* __restrict__ offsets_out,
                                                              int32_t* __restrict__ num_padded,
-                                                             int max_blocks) {
+                                                             int max_blocks, int range) {
   extern __shared__ int sm[];
   int* cnt = sm;               // [E]
   int* offs = cnt + E;         // [E + 1]
-  int* run = offs + E + 1;     // [E]
+  int* run = offs + E + 1;     // [E] entries of expert e before the current tile
   int* scan = run + E;         // [2 * kWaves], the scan's wave totals
   int* wc = scan + 2 * kWaves; // [kWaves][E]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  // this workgroup's entries: [r0, r1), whole tiles (range is a multiple of kThreads)
+  const int r0 = min(n_flat, wg * range);
+  const int r1 = min(n_flat, r0 + range);
 
   for (int e = tid; e < E; e += kThreads) {
     cnt[e] = 0;
     run[e] = 0;
   }
   for (int j = tid; j < kWaves * E; j += kThreads) wc[j] = 0;
-  // The first chunk stays in registers for the scatter (one chunk covers n_flat <= 8192).
+  // The first chunk stays in registers for the scatter of the first workgroup when its range
+  // holds all of the chunk's entries.
+  const bool reuse_first = wg == 0 && r1 >= min(n_flat, kPer * kThreads);
   int ec[kPer];
   load_chunk(ids, n_flat, 0, ec);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
-    if (ec[j] >= 0 && ec[j] < E) atomicAdd(&cnt[ec[j]], 1);
+    if (ec[j] >= 0 && ec[j] < E) {
+      atomicAdd(&cnt[ec[j]], 1);
+      if (j * kThreads + tid < r0) atomicAdd(&run[ec[j]], 1);
+    }
   for (int c0 = kPer * kThreads; c0 < n_flat; c0 += kPer * kThreads) {
     int e[kPer];
     load_chunk(ids, n_flat, c0, e);
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (e[j] >= 0 && e[j] < E) atomicAdd(&cnt[e[j]], 1);
+      if (e[j] >= 0 && e[j] < E) {
+        atomicAdd(&cnt[e[j]], 1);
+        if (c0 + j * kThreads + tid < r0) atomicAdd(&run[e[j]], 1);
+      }
   }
   __syncthreads();
 
@@ -111,13 +128,16 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
   if (tid == E - 1) offs[E] = incl;
   __syncthreads();
   const int total = offs[E];
-  for (int e = tid; e <= E; e += kThreads) offsets_out[e] = offs[e];
-  if (tid == 0) *num_padded = total;
+  if (wg == 0) {
+    for (int e = tid; e <= E; e += kThreads) offsets_out[e] = offs[e];
+    if (tid == 0) *num_padded = total;
+  }
 
-  // Padding slots and the block -> expert table.
-  for (int e = tid; e < E; e += kThreads)
+  // Padding slots (expert e's by workgroup e mod nwg) and the block -> expert table (blocks dealt
+  // out round robin).
+  for (int e = wg + nwg * tid; e < E; e += nwg * kThreads)
     for (int s = offs[e] + cnt[e]; s < offs[e + 1]; ++s) sorted[s] = n_flat;
-  for (int b = tid; b * bm < total; b += kThreads) {
+  for (int b = wg * kThreads + tid; b * bm < total; b += nwg * kThreads) {
     const int row = b * bm;
     int lo = 0, hi = E - 1;  // last e with offs[e] <= row (offs is non-decreasing)
     while (lo < hi) {
@@ -127,17 +147,18 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
     block_expert[b] = lo;
   }
   // blocks past the sorted rows (up to the capacity) get no expert
-  for (int b = (total + bm - 1) / bm + tid; b < max_blocks; b += kThreads) block_expert[b] = -1;
+  for (int b = (total + bm - 1) / bm + wg * kThreads + tid; b < max_blocks; b += nwg * kThreads)
+    block_expert[b] = -1;
 
-  // Stable scatter, one tile of kThreads entries at a time. wc is zero at the start of every tile:
-  // zeroed above, then by the running-count update that reads it.
+  // Stable scatter of [r0, r1), one tile of kThreads entries at a time. wc is zero at the start of
+  // every tile: zeroed above, then by the running-count update that reads it.
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < n_flat; c0 += kPer * kThreads) {
-    if (c0 > 0) load_chunk(ids, n_flat, c0, ec);
+  for (int c0 = r0; c0 < r1; c0 += kPer * kThreads) {
+    if (!(c0 == 0 && reuse_first)) load_chunk(ids, r1, c0, ec);
 #pragma unroll
     for (int jt = 0; jt < kPer; ++jt) {
       const int t0 = c0 + jt * kThreads;
-      if (t0 >= n_flat) break;  // the same for every thread
+      if (t0 >= r1) break;  // the same for every thread
       const int i = t0 + tid;
       const int e = ec[jt];
       const bool valid = e >= 0 && e < E;
@@ -232,10 +253,16 @@ hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, in
                             int32_t* expert_offsets, int32_t* num_padded, void*,
                             hipStream_t stream) {
   const size_t smem = sizeof(int) * (size_t(E) * 3 + 1 + 2 * kWaves + size_t(kWaves) * E);
-  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kThreads), smem, stream, topk_ids,
-                     int(T * topk), int(E), int(block_m), sorted_ids, block_expert,
+  // up to 128 workgroups of whole tiles: each counts the whole list, then scatters its own range
+  const int64_t n_flat = T * topk;
+  const int64_t tiles = std::max<int64_t>(1, (n_flat + kThreads - 1) / kThreads);
+  const int64_t tiles_per_wg = (tiles + 127) / 128;
+  const int64_t wgs = (tiles + tiles_per_wg - 1) / tiles_per_wg;
+  hipLaunchKernelGGL(moe_align_kernel, dim3(unsigned(wgs)), dim3(kThreads), smem, stream, topk_ids,
+                     int(n_flat), int(E), int(block_m), sorted_ids, block_expert,
                      expert_offsets, num_padded,
-                     int(hq_moe_align_capacity(T, topk, E, block_m) / size_t(block_m)));
+                     int(hq_moe_align_capacity(T, topk, E, block_m) / size_t(block_m)),
+                     int(tiles_per_wg * kThreads));
   return hipGetLastError();
 }
 

@@ -61,10 +61,12 @@ def test_moe_align_hand_case():
     assert got["block_expert"].tolist() == [0, 2, 3]
 
 
-@pytest.mark.parametrize("T", [1, 3, 32, 512, 1100, 4096])
+@pytest.mark.parametrize("T", [1, 3, 32, 512, 1100, 4096, 20000])
 @pytest.mark.parametrize("bm", [16, 64])
 def test_moe_align_skewed_routing(T, bm):
-    # 1100 x 8 = 8800 entries: a second chunk of 8192 entries that ends inside its first tile
+    # 1100 x 8 = 8800 entries: nine workgroups, the last with a ragged tile; 4096 x 8: 32
+    # workgroups of one tile; 20000 x 8 = 160000 entries: 79 workgroups of two tiles, each range
+    # starting inside an 8192-entry chunk of the histogram pass, the last one ragged
     say(f"[moe_align] T={T} bm={bm}")
     ids = synth.make_moe_inputs(5, T, 64)["topk_ids"]
     _check_align(ids, 256, bm)
