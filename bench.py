@@ -715,12 +715,12 @@ def run_moe_layer(args, w4a8=False):
     torch.cuda.synchronize()
     graphs = {}
     for T in Ts:
-        for name, f in [("layer", layer)] + list(stages.items()):
+        for stage, f in [("layer", layer)] + list(stages.items()):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 for _ in range(reps[T]):
                     f(T)
-            graphs[(T, name)] = gr
+            graphs[(T, stage)] = gr
     names = ["layer"] + list(stages)
     for _ in range(args.warmup):
         for gr in graphs.values():
@@ -730,12 +730,12 @@ def run_moe_layer(args, w4a8=False):
     t0 = time.perf_counter()
     for _ in range(args.steps):
         for T in Ts:
-            for name in names:
+            for stage in names:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                graphs[(T, name)].replay()
+                graphs[(T, stage)].replay()
                 b.record(stream)
-                rec[(T, name)].append((a, b))
+                rec[(T, stage)].append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sweep, tot_t, tot_tok = [], 0.0, 0
