@@ -418,6 +418,19 @@ def _random_mxfp4_expert(g, N: int, K: int):
             "scales": g.integers(119, 123, (N, K // 32)).astype(np.uint8)}
 
 
+def workload_name(config: str) -> str:
+    """The `config.workload` label of a --config value's bench line."""
+    if config in WORKLOADS:
+        return WORKLOADS[config]["name"]
+    return {
+        "moe": MOE["name"],
+        "moe_mx": MOE["name"].replace("W4A16", "W4A16-MXFP4"),
+        "moe_fp8b": MOE["name"].replace("W4A16", "FP8 W8A8 block-scaled (128x128 weights, 1x128 tokens)"),
+        "moe_layer": MOE_LAYER["name"],
+        "moe_layer_w4a8": MOE_LAYER["name"].replace("W4A16", "W4A8-MXFP4, tokenwise FP8 activations"),
+    }[config]
+
+
 def run_moe(args, mx=False):
     """Token sort + grouped GEMM per T. tokens/s = T / (t_align + t_gemm). mx: True for MXFP4
     experts (W4A16-MXFP4) instead of INT4 group-128, "fp8b" for block-scaled FP8 experts and
@@ -431,12 +444,11 @@ def run_moe(args, mx=False):
     E, topk, N, K, Ts, cfg = (MOE[k] for k in ("E", "topk", "N", "K", "Ts", "cfg"))
     dev = torch.device("cuda:0")
     fp8b = mx == "fp8b"
+    name = workload_name("moe_fp8b" if fp8b else "moe_mx" if mx else "moe")
     if fp8b:
-        desc, name, expert_gen = hq.DESC_W8A8_FP8_BLOCK, MOE["name"].replace(
-            "W4A16", "FP8 W8A8 block-scaled (128x128 weights, 1x128 tokens)"), synth.random_fp8b_expert
+        desc, expert_gen = hq.DESC_W8A8_FP8_BLOCK, synth.random_fp8b_expert
     else:
         desc = hq.DESC_W4A16_MXFP4 if mx else hq.DESC_W4A16_SYM
-        name = MOE["name"].replace("W4A16", "W4A16-MXFP4") if mx else MOE["name"]
         expert_gen = _random_mxfp4_expert if mx else synth.random_int4_sym_expert
     peak = "fp8" if fp8b else "bf16"
     stride = hq.hq_prepacked_bytes(desc, 1, N, K)
@@ -609,7 +621,7 @@ def run_moe_layer(args, w4a8=False):
     E, topk, H, I, Ts, cfg = (MOE_LAYER[k] for k in ("E", "topk", "H", "I", "Ts", "cfg"))
     dev = torch.device("cuda:0")
     desc = hq.DESC_W4A8_MXFP4 if w4a8 else hq.DESC_W4A16_SYM
-    name = MOE_LAYER["name"].replace("W4A16", "W4A8-MXFP4, tokenwise FP8 activations") if w4a8 else MOE_LAYER["name"]
+    name = workload_name("moe_layer_w4a8" if w4a8 else "moe_layer")
     gen = _random_mxfp4_expert if w4a8 else synth.random_int4_sym_expert
     peak = "fp8" if w4a8 else "bf16"
     n_copies = 4                      # > 256 MB Infinity Cache between reuses even at T = 1

@@ -28,6 +28,16 @@ def test_traffic_records_are_well_formed():
         assert len(rec["kernel_sources_sha256"]) == 64 and rec["kernel_files"]
 
 
+def test_committed_bench_lines_name_their_workload():
+    """Every committed bench line's config.workload is the label bench.py gives that workload."""
+    configs = list(bench.WORKLOADS) + ["moe", "moe_mx", "moe_fp8b", "moe_layer", "moe_layer_w4a8"]
+    for wl in configs:
+        path = os.path.join(ROOT, "profiles", f"bench_{wl}.json")
+        line = json.load(open(path))
+        assert line["config"]["workload"] == bench.workload_name(wl), path
+    assert len({bench.workload_name(wl) for wl in configs}) == len(configs)
+
+
 def test_traffic_is_dropped_when_sources_change(monkeypatch):
     rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_w4a16.json")))
     monkeypatch.setattr(bench, "kernel_sources_sha", lambda files=None: rec["kernel_sources_sha256"])
