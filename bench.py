@@ -190,16 +190,21 @@ def make_inputs(wl: str, spec: dict):
     return desc, std, packed, acts
 
 
+def oracle_threads() -> int:
+    """Threads the CPU oracle's numpy calls run on (its BLAS pool), for cpu_baseline.cores."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(wl: str, spec: dict, std, acts):
     """The CPU oracle, untuned, on a bounded sample of the same workload."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = oracle_threads()
     N, K = spec["N"], spec["K"]
     flops = 0.0
     secs = 0.0
@@ -595,7 +600,7 @@ def run_moe(args, mx=False):
         else:
             oracle.ref_moe_gemm(inp["x"], ids, lambda e: ws[e], N, E, 128)
         dt = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(),
+        line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": oracle_threads(),
                                 "kind": "oracle", "sample": f"T=1 ({len(need)} experts), {dt:.1f} s"}
     return line
 
@@ -809,7 +814,7 @@ def run_moe_layer(args, w4a8=False):
             oracle.ref_moe_layer(inp["x"], ids, inp["topk_weights"], lambda e: gu_w[e], lambda e: dn_w[e],
                                  I, H, E, 128)
         dt = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": os.cpu_count(),
+        line["cpu_baseline"] = {"value": round(1 / dt, 3), "unit": "tokens/s", "cores": oracle_threads(),
                                 "kind": "oracle", "sample": f"T=1 ({len(need)} experts), {dt:.1f} s"}
     return line
 
