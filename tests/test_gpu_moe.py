@@ -86,6 +86,29 @@ def test_moe_align_out_of_range_ids_and_small_E():
     _check_align(ids, 7, 32)
 
 
+def test_moe_align_and_grouped_gemm_with_no_tokens():
+    """T = 0: the sort writes zero offsets and num_padded = 0 and nothing else (the capacity is 0);
+    the grouped GEMM returns without a launch and leaves its output as it was."""
+    E, bm, N, K = 16, 16, 256, 256
+    assert hq.hq_moe_align_capacity(0, 8, E, bm) == 0
+    ids = torch.zeros(8, dtype=torch.int32, device=DEV)
+    so = torch.full((16,), -7, dtype=torch.int32, device=DEV)
+    be = torch.full((16,), -7, dtype=torch.int32, device=DEV)
+    offs = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    npad = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    hq.hq_moe_align(ids, 0, 8, E, bm, so, be, offs, npad)
+    torch.cuda.synchronize()
+    assert int(npad.item()) == 0 and (offs.cpu().numpy() == 0).all()
+    assert (so.cpu().numpy() == -7).all() and (be.cpu().numpy() == -7).all()
+    desc = hq.DESC_W4A16_SYM
+    w = torch.zeros(hq.hq_prepacked_bytes(desc, E, N, K), dtype=torch.uint8, device=DEV)
+    x = torch.zeros((1, K), dtype=torch.int16, device=DEV)
+    y = torch.full((8, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    hq.hq_moe_grouped_gemm(desc, 0, 8, E, N, K, x, None, w, so, be, npad, bm, None, y)
+    torch.cuda.synchronize()
+    assert (y.cpu().numpy() == 0x7FC0).all()
+
+
 def _moe_case(T, topk, E, N, K, bm, with_weights, seed, random_codes=False):
     inp = synth.make_moe_inputs(seed, T, K, E, topk)
     ids = inp["topk_ids"]
