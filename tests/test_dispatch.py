@@ -77,3 +77,17 @@ def test_activation_offsets_past_32_bits_leave_the_lds_kernels():
     assert hq.hq_gemm_plan(hq.DESC_W4A16_ASYM, 262144, 256, K)[0] == 1
     assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20 - 1, 256, K)[0] in (2, 3)  # 4-bit codes
     assert hq.hq_gemm_plan(hq.DESC_W4A4_MXFP4, 2 ** 20, 256, K)[0] == 0
+
+
+def test_moe_block_sizes_follow_the_measured_crossovers():
+    """hq_moe_block_m at the DeepSeek-V3 gate_up shape (top-8 of 256 experts): 16-row blocks below
+    2 routed rows per expert, 32 from 2, 64 from 8, 128 for INT4 / MXFP4 experts with bf16
+    activations from 24 (block-scaled FP8 from 8); 8-bit per-token activations stay at 64."""
+    N, K, E, topk = 4096, 7168, 256, 8
+    want = [(hq.DESC_W4A16_SYM, {32: 16, 64: 32, 256: 64, 512: 64, 767: 64, 768: 128, 4096: 128}),
+            (hq.DESC_W4A16_MXFP4, {512: 64, 768: 128}),
+            (hq.DESC_W8A8_FP8_BLOCK, {64: 32, 256: 128, 4096: 128}),
+            (hq.DESC_W4A8_MXFP4, {256: 64, 4096: 64})]
+    for desc, pts in want:
+        for T, bm in pts.items():
+            assert hq.hq_moe_block_m(desc, T, topk, E, N, K) == bm, (T, bm)
