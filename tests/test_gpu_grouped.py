@@ -59,6 +59,28 @@ def test_grouped_gemm(R, E, N, K, counts):
     _case(R, E, N, K, counts, 40 + R)
 
 
+def test_grouped_gemm_random_shapes():
+    """Eight seeded random problems: up to 64 experts with Zipf-like row counts (empty experts
+    included, so the block size the library picks varies), rows before the first and after the
+    last range, N a multiple of 16 up to 768, K a multiple of 128 up to 1536."""
+    g = np.random.default_rng(41)
+    done = 0
+    while done < 8:
+        E = int(g.integers(1, 65))
+        N = int(16 * g.integers(1, 49))
+        K = int(128 * g.integers(1, 13))
+        counts = np.floor(g.pareto(1.2, E) * g.choice([1, 8, 40])).astype(np.int64)
+        counts[g.random(E) < 0.2] = 0
+        R_used = int(counts.sum())
+        lead, tail = int(g.integers(0, 5)), int(g.integers(0, 5))
+        R = R_used + lead + tail
+        if R == 0 or R * N * K > 3e8:
+            continue
+        y = _case(R, E, N, K, counts.tolist(), 900 + done, lead=lead, random_codes=True)
+        assert (y[:lead] == NAN_BF16).all() and (y[lead + R_used:] == NAN_BF16).all()
+        done += 1
+
+
 def test_grouped_gemm_rows_outside_the_ranges():
     """offsets[0] > 0 and offsets[E] < R: the leading and trailing rows are left untouched."""
     R, E, N, K = 120, 6, 256, 384
