@@ -192,6 +192,81 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(const int32_t* __re
   }
 }
 
+// The same sort for at most 64 entries (a few tokens): one wave, one entry per lane. Lanes with the
+// same expert are found with ballots over the expert id bits and ranked by lane (stable); the
+// padded counts go to an LDS table indexed by expert and are prefix-summed by the wave (each lane
+// a contiguous run of experts, then shuffles over the run totals); each entry's position is its
+// expert's offset plus its rank, the first lane of each expert writes that expert's padding, and
+// the block -> expert table is searched in the offsets. A few hundred instructions where the
+// workgroup kernel above needs its LDS clears and about ten workgroup barriers.
+__global__ __launch_bounds__(64) void moe_align_small_kernel(const int32_t* __restrict__ ids, int n_flat,
+                                                              int E, int bm, int32_t* __restrict__ sorted,
+                                                              int32_t* __restrict__ block_expert,
+                                                              int32_t* __restrict__ offsets_out,
+                                                              int32_t* __restrict__ num_padded, int max_blocks) {
+  __shared__ int offs[513];   // padded count, then exclusive offset, per expert; offs[E] = total
+  const int lane = threadIdx.x;
+  const int e = lane < n_flat ? ids[lane] : -1;
+  const bool valid = e >= 0 && e < E;
+  const int key = valid ? e : E;
+  uint64_t same = ~0ull;
+#pragma unroll
+  for (int b = 0; b < kIdBits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & below);
+  const int cnt = __popcll(same);
+  for (int x = lane; x <= E; x += 64) offs[x] = 0;
+  __syncthreads();
+  if (valid && rank == 0) offs[e] = (cnt + bm - 1) / bm * bm;
+  __syncthreads();
+  // exclusive scan of offs[0..E): lane l owns experts [l * per, (l + 1) * per)
+  const int per = (E + 63) / 64;
+  const int lo = min(E, lane * per), hi = min(E, lo + per);
+  int run = 0;
+  for (int x = lo; x < hi; ++x) run += offs[x];
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  const int total = __shfl(incl, 63, 64);
+  __syncthreads();
+  int acc = incl - run;
+  for (int x = lo; x < hi; ++x) {
+    const int padded = offs[x];
+    offs[x] = acc;
+    acc += padded;
+  }
+  if (lane == 0) offs[E] = total;
+  __syncthreads();
+  for (int x = lane; x <= E; x += 64) offsets_out[x] = offs[x];
+  if (lane == 0) *num_padded = total;
+  if (valid) {
+    const int base = offs[e];
+    sorted[base + rank] = lane;
+    if (rank == 0)
+      for (int s = base + cnt; s < offs[e + 1]; ++s) sorted[s] = n_flat;
+  }
+  for (int b = lane; b < max_blocks; b += 64) {
+    const int row = b * bm;
+    int v = -1;
+    if (row < total) {
+      int l = 0, h = E - 1;  // last expert with offs <= row (offs is non-decreasing)
+      while (l < h) {
+        const int mid = (l + h + 1) >> 1;
+        if (offs[mid] <= row) l = mid; else h = mid - 1;
+      }
+      v = l;
+    }
+    block_expert[b] = v;
+  }
+}
+
 // Row index of the "Grouped" path (rows already grouped by expert): expert e owns rows
 // [offsets[e], offsets[e+1]) clipped to [0, R). The same outputs as the token sort -- each
 // expert's rows padded to a multiple of bm with the sentinel R, the block -> expert table, -1
@@ -252,17 +327,21 @@ hipError_t launch_moe_align(const int32_t* topk_ids, int64_t T, int32_t topk, in
                             int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                             int32_t* expert_offsets, int32_t* num_padded, void*,
                             hipStream_t stream) {
+  const int64_t n_flat = T * topk;
+  const int max_blocks = int(hq_moe_align_capacity(T, topk, E, block_m) / size_t(block_m));
+  if (n_flat <= 64) {   // a few tokens: one wave
+    hipLaunchKernelGGL(moe_align_small_kernel, dim3(1), dim3(64), 0, stream, topk_ids, int(n_flat), int(E),
+                       int(block_m), sorted_ids, block_expert, expert_offsets, num_padded, max_blocks);
+    return hipGetLastError();
+  }
   const size_t smem = sizeof(int) * (size_t(E) * 3 + 1 + 2 * kWaves + size_t(kWaves) * E);
   // up to 128 workgroups of whole tiles: each counts the whole list, then scatters its own range
-  const int64_t n_flat = T * topk;
   const int64_t tiles = std::max<int64_t>(1, (n_flat + kThreads - 1) / kThreads);
   const int64_t tiles_per_wg = (tiles + 127) / 128;
   const int64_t wgs = (tiles + tiles_per_wg - 1) / tiles_per_wg;
   hipLaunchKernelGGL(moe_align_kernel, dim3(unsigned(wgs)), dim3(kThreads), smem, stream, topk_ids,
                      int(n_flat), int(E), int(block_m), sorted_ids, block_expert,
-                     expert_offsets, num_padded,
-                     int(hq_moe_align_capacity(T, topk, E, block_m) / size_t(block_m)),
-                     int(tiles_per_wg * kThreads));
+                     expert_offsets, num_padded, max_blocks, int(tiles_per_wg * kThreads));
   return hipGetLastError();
 }
 

@@ -80,10 +80,21 @@ def test_moe_align_512_experts(T, topk):
     _check_align(ids, 512, 16)
 
 
-def test_moe_align_out_of_range_ids_and_small_E():
-    ids = np.random.default_rng(3).integers(-2, 9, (700, 4)).astype(np.int32)
-    say("[moe_align] invalid ids")
+@pytest.mark.parametrize("T,topk", [(700, 4), (10, 4), (16, 4)])
+def test_moe_align_out_of_range_ids_and_small_E(T, topk):
+    # 2800 entries over three workgroups; 40 and 64 entries on the one-wave form
+    ids = np.random.default_rng(3).integers(-2, 9, (T, topk)).astype(np.int32)
+    say(f"[moe_align] invalid ids T={T} topk={topk}")
     _check_align(ids, 7, 32)
+
+
+@pytest.mark.parametrize("T,topk,E,bm", [(1, 8, 256, 16), (8, 8, 512, 16), (16, 4, 3, 64), (65, 1, 64, 32),
+                                         (2, 8, 1, 128)])
+def test_moe_align_few_entries(T, topk, E, bm):
+    """The one-wave form (at most 64 entries) and the first size past it, against the oracle."""
+    ids = np.random.default_rng(T * 100 + E).integers(0, E, (T, topk)).astype(np.int32)
+    say(f"[moe_align] few entries T={T} topk={topk} E={E} bm={bm}")
+    _check_align(ids, E, bm)
 
 
 def test_moe_align_and_grouped_gemm_with_no_tokens():
